@@ -1,0 +1,387 @@
+"""Pins of the fp64 oracle against things other than itself: brute force on
+tiny inputs, closed forms, textbook values and invariants the method fixes.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term,
+a wrong sign or index, a transposed operand) fails it."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import esm_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+def _tiny_weights(H, F, rng, scale=0.05, random_ln=True):
+    w = {
+        "w_qkv": rng.standard_normal((3 * H, H)) * scale,
+        "b_qkv": rng.standard_normal(3 * H) * scale,
+        "w_out": rng.standard_normal((H, H)) * scale,
+        "b_out": rng.standard_normal(H) * scale,
+        "w_fc1": rng.standard_normal((F, H)) * scale,
+        "b_fc1": rng.standard_normal(F) * scale,
+        "w_fc2": rng.standard_normal((H, F)) * scale,
+        "b_fc2": rng.standard_normal(H) * scale,
+    }
+    if random_ln:
+        w["ln1_gamma"] = 1 + 0.2 * rng.standard_normal(H)
+        w["ln1_beta"] = 0.2 * rng.standard_normal(H)
+        w["ln2_gamma"] = 1 + 0.2 * rng.standard_normal(H)
+        w["ln2_beta"] = 0.2 * rng.standard_normal(H)
+    else:
+        w["ln1_gamma"] = np.ones(H); w["ln1_beta"] = np.zeros(H)
+        w["ln2_gamma"] = np.ones(H); w["ln2_beta"] = np.zeros(H)
+    return w
+
+
+# ---------------------------------------------------------------- attention
+
+def _brute_attention(q, k, v, cu):
+    """Scalar loops straight from softmax(q k^T / 8) v, per segment and head."""
+    T, nh, d = q.shape
+    out = np.zeros((T, nh * d))
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        for n in range(nh):
+            for i in range(a, b):
+                scores = []
+                for j in range(a, b):
+                    scores.append(sum(float(q[i, n, e]) * float(k[j, n, e]) for e in range(d)) / 8.0)
+                m = max(scores)
+                ex = [math.exp(x - m) for x in scores]
+                z = sum(ex)
+                for e in range(d):
+                    out[i, n * d + e] = sum(ex[j - a] / z * float(v[j, n, e]) for j in range(a, b))
+    return out
+
+
+def test_attention_matches_brute_force():
+    r = _rng(1)
+    cu = np.array([0, 1, 4, 9])
+    q, k, v = (r.standard_normal((9, 2, 64)) * 2 for _ in range(3))
+    got = O.attention(q, k, v, cu)
+    ref = _brute_attention(q, k, v, cu)
+    assert np.abs(got - ref).max() < 1e-12
+
+
+def test_softmax_rows_sum_to_one_and_nonnegative():
+    r = _rng(2)
+    P = O.attention_probs(r.standard_normal((37, 64)) * 5, r.standard_normal((37, 64)) * 5)
+    assert (P >= 0).all()
+    assert np.abs(P.sum(axis=1) - 1).max() < 1e-13
+
+
+def test_zero_query_gives_segment_mean_of_values():
+    # q = 0 => uniform weights over exactly the own segment: pins segment bounds.
+    r = _rng(3)
+    cu = np.array([0, 5, 6, 20, 20, 33])
+    T = 33
+    q = np.zeros((T, 3, 64))
+    k = r.standard_normal((T, 3, 64))
+    v = r.standard_normal((T, 3, 64))
+    ctx = O.attention(q, k, v, cu).reshape(T, 3, 64)
+    for a, b in O.segments(cu):
+        if b > a:
+            assert np.abs(ctx[a:b] - v[a:b].mean(axis=0)).max() < 1e-13
+
+
+def test_length_one_segment_returns_its_value_and_identical_keys_are_uniform():
+    r = _rng(4)
+    q = r.standard_normal((1, 1, 64)) * 10
+    v = r.standard_normal((1, 1, 64))
+    assert np.abs(O.attention(q, r.standard_normal((1, 1, 64)), v, [0, 1]).ravel() - v.ravel()).max() < 1e-15
+    L = 11
+    q = r.standard_normal((L, 1, 64))
+    k = np.repeat(r.standard_normal((1, 1, 64)), L, axis=0)
+    v = r.standard_normal((L, 1, 64))
+    ctx = O.attention(q, k, v, [0, L])
+    assert np.abs(ctx - v.mean(axis=0).ravel()).max() < 1e-13
+
+
+def test_softmax_scale_is_one_over_sqrt_head_dim():
+    # Two keys with scores s1, s2: weight ratio exp((s1 - s2) / 8).
+    q = np.zeros((1, 64)); q[0, 0] = 1.0
+    k = np.zeros((2, 64)); k[0, 0] = 8.0; k[1, 0] = 0.0
+    P = O.attention_probs(q, k)
+    assert abs(P[0, 0] / P[0, 1] - math.e) < 1e-12
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_equals_complex_rotation():
+    # RoFormer rotation of pair (u_i, u_{i+32}) read as the complex number
+    # u_i + i*u_{i+32}, multiplied by exp(i * p * 10000^(-i/32)).
+    r = _rng(5)
+    u = r.standard_normal((50, 3, 64))
+    pos = r.integers(0, 1026, 50)
+    got = O.apply_rope(u, pos)
+    z = u[..., :32] + 1j * u[..., 32:]
+    ang = pos[:, None, None] * (10000.0 ** (-np.arange(32) / 32.0))[None, None, :]
+    w = z * np.exp(1j * ang)
+    assert np.abs(got[..., :32] - w.real).max() < 1e-12
+    assert np.abs(got[..., 32:] - w.imag).max() < 1e-12
+
+
+def test_rope_position_zero_is_identity_and_preserves_pair_norms():
+    r = _rng(6)
+    u = r.standard_normal((40, 64))
+    assert np.abs(O.apply_rope(u[:1], [0]) - u[:1]).max() == 0
+    pos = np.arange(40) * 25
+    v = O.apply_rope(u, pos)
+    n0 = u[:, :32] ** 2 + u[:, 32:] ** 2
+    n1 = v[:, :32] ** 2 + v[:, 32:] ** 2
+    assert np.abs(n0 - n1).max() < 1e-12
+
+
+def test_rope_scores_depend_only_on_relative_position():
+    r = _rng(7)
+    q = r.standard_normal((1, 64))
+    k = r.standard_normal((1, 64))
+    for (pq, pk), c in [((3, 17), 100), ((500, 2), 7), ((0, 1021), 3)]:
+        s0 = (O.apply_rope(q, [pq]) @ O.apply_rope(k, [pk]).T).item()
+        s1 = (O.apply_rope(q, [pq + c]) @ O.apply_rope(k, [pk + c]).T).item()
+        assert abs(s0 - s1) < 1e-11
+    # ... and really do depend on it.
+    sa = (O.apply_rope(q, [5]) @ O.apply_rope(k, [3]).T).item()
+    sb = (O.apply_rope(q, [3]) @ O.apply_rope(k, [5]).T).item()
+    assert abs(sa - sb) > 1e-3
+
+
+def test_positions_restart_per_sequence():
+    assert O.positions([0, 3, 3, 5]).tolist() == [0, 1, 2, 0, 1]
+
+
+# ---------------------------------------------------------------- LayerNorm, GELU
+
+def test_layernorm_closed_forms():
+    r = _rng(8)
+    x = r.standard_normal((20, 320)) * 3 + 1.5
+    h = O.layer_norm(x, np.ones(320), np.zeros(320), 1e-5)
+    var = x.var(axis=1)
+    assert np.abs(h.mean(axis=1)).max() < 1e-13
+    assert np.abs(h.var(axis=1) - var / (var + 1e-5)).max() < 1e-12
+    # constant row -> beta
+    beta = r.standard_normal(320)
+    c = O.layer_norm(np.full((1, 320), 7.25), r.standard_normal(320), beta, 1e-5)
+    assert np.abs(c - beta).max() < 1e-12
+    # with eps = 0: invariant to row scale and shift, and gamma/beta act per column
+    g, b = r.standard_normal(320), r.standard_normal(320)
+    h0 = O.layer_norm(x, g, b, 0.0)
+    h1 = O.layer_norm(4.0 * x - 9.0, g, b, 0.0)
+    assert np.abs(h0 - h1).max() < 1e-11
+    z = (x[0] - x[0].mean()) / math.sqrt(((x[0] - x[0].mean()) ** 2).sum() / 320)
+    assert np.abs(h0[0] - (z * g + b)).max() < 1e-12
+
+
+def test_gelu_textbook_values_and_identities():
+    # GELU(1) = Phi(1) = 0.8413447460685429 (standard normal CDF at 1).
+    assert abs(O.gelu(1.0) - 0.8413447460685429) < 1e-15
+    assert O.gelu(0.0) == 0.0
+    z = np.linspace(-6, 6, 241)
+    assert np.abs(O.gelu(z) - O.gelu(-z) - z).max() < 1e-14
+    for t in [-3.3, -0.7, 0.2, 1.9, 4.4]:
+        ref = 0.5 * t * (1 + math.erf(t / math.sqrt(2)))
+        assert abs(O.gelu(t) - ref) < 1e-15
+    assert abs(O.gelu(10.0) - 10.0) < 1e-15
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _scalar_layer(x, cu, w, heads):
+    """An independent scalar-loop evaluation of the layer definition (tiny sizes)."""
+    T, H = x.shape
+    F = w["w_fc1"].shape[0]
+
+    def ln(row, g, b):
+        mu = sum(row) / H
+        var = sum((t - mu) ** 2 for t in row) / H
+        return [(row[i] - mu) / math.sqrt(var + 1e-5) * g[i] + b[i] for i in range(H)]
+
+    def lin(row, W, bias):
+        return [sum(W[o][i] * row[i] for i in range(len(row))) + bias[o] for o in range(len(W))]
+
+    seg_of = {}
+    for s in range(len(cu) - 1):
+        for t in range(cu[s], cu[s + 1]):
+            seg_of[t] = s
+    qs, ks, vs = {}, {}, {}
+    for t in range(T):
+        y = lin(ln(list(x[t]), w["ln1_gamma"], w["ln1_beta"]), w["w_qkv"], w["b_qkv"])
+        p = t - cu[seg_of[t]]
+        for n in range(heads):
+            q = y[192 * n: 192 * n + 64]
+            k = y[192 * n + 64: 192 * n + 128]
+            v = y[192 * n + 128: 192 * n + 192]
+            qr, kr = [0.0] * 64, [0.0] * 64
+            for i in range(32):
+                th = p * 10000.0 ** (-i / 32.0)
+                c, s_ = math.cos(th), math.sin(th)
+                qr[i], qr[i + 32] = q[i] * c - q[i + 32] * s_, q[i + 32] * c + q[i] * s_
+                kr[i], kr[i + 32] = k[i] * c - k[i + 32] * s_, k[i + 32] * c + k[i] * s_
+            qs[t, n], ks[t, n], vs[t, n] = qr, kr, v
+    out = np.zeros((T, H))
+    for t in range(T):
+        s = seg_of[t]
+        keys = range(cu[s], cu[s + 1])
+        ctx = []
+        for n in range(heads):
+            sc = [sum(a * b for a, b in zip(qs[t, n], ks[j, n])) / 8.0 for j in keys]
+            m = max(sc)
+            e = [math.exp(z - m) for z in sc]
+            Z = sum(e)
+            ctx += [sum(e[jj] / Z * vs[j, n][d] for jj, j in enumerate(keys)) for d in range(64)]
+        x1 = [a + b for a, b in zip(x[t], lin(ctx, w["w_out"], w["b_out"]))]
+        hid = lin(ln(x1, w["ln2_gamma"], w["ln2_beta"]), w["w_fc1"], w["b_fc1"])
+        act = [0.5 * z * (1 + math.erf(z / math.sqrt(2))) for z in hid]
+        out[t] = [a + b for a, b in zip(x1, lin(act, w["w_fc2"], w["b_fc2"]))]
+    assert F == len(hid)
+    return out
+
+
+@pytest.mark.slow
+def test_layer_matches_scalar_evaluation():
+    r = _rng(9)
+    H, F, heads = 128, 512, 2
+    w = _tiny_weights(H, F, r)
+    cu = [0, 3, 7]
+    x = r.standard_normal((7, H))
+    got = O.layer_forward(x, cu, w, heads)
+    ref = _scalar_layer(x, cu, w, heads)
+    assert np.abs(got - ref).max() < 1e-11
+
+
+def test_zero_output_projections_make_the_layer_the_identity():
+    r = _rng(10)
+    H, F = 128, 512
+    w = _tiny_weights(H, F, r)
+    for k in ("w_out", "b_out", "w_fc2", "b_fc2"):
+        w[k] = np.zeros_like(w[k])
+    x = r.standard_normal((12, H))
+    assert np.array_equal(O.layer_forward(x, [0, 5, 12], w, 2), x)
+
+
+def test_one_hot_out_projection_routes_one_context_column():
+    # W_out[n, j] = 1 only: x1[:, n] - x[:, n] = ctx[:, j] (nn.Linear [out, in] layout).
+    r = _rng(11)
+    H, F = 128, 512
+    w = _tiny_weights(H, F, r)
+    w["w_out"] = np.zeros((H, H)); w["w_out"][5, 70] = 1.0
+    w["b_out"] = np.zeros(H)
+    x = r.standard_normal((9, H))
+    _, it = O.layer_forward(x, [0, 9], w, 2, return_intermediates=True)
+    d = it["x1"] - x
+    assert np.abs(d[:, 5] - it["ctx"][:, 70]).max() < 1e-14
+    assert np.abs(np.delete(d, 5, axis=1)).max() == 0
+
+
+def test_fc1_is_not_transposed():
+    # W_fc1 has shape [F, H]: with F != H a transposed operand cannot even run.
+    r = _rng(12)
+    H, F = 128, 384
+    w = _tiny_weights(H, F, r)
+    x = r.standard_normal((4, H))
+    _, it = O.layer_forward(x, [0, 4], w, 2, return_intermediates=True)
+    assert it["a"].shape == (4, F)
+
+
+def test_packed_equals_each_sequence_alone_and_permutation():
+    r = _rng(13)
+    H, F, heads = 128, 512, 2
+    w = _tiny_weights(H, F, r)
+    lens = [5, 1, 17, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = r.standard_normal((cu[-1], H))
+    full = O.layer_forward(x, cu, w, heads)
+    for s, L in enumerate(lens):
+        a = cu[s]
+        alone = O.layer_forward(x[a:a + L], [0, L], w, heads)
+        assert np.abs(full[a:a + L] - alone).max() < 1e-12
+    perm = [2, 0, 3, 1]
+    xp = np.concatenate([x[cu[s]:cu[s + 1]] for s in perm])
+    cup = np.concatenate([[0], np.cumsum([lens[s] for s in perm])])
+    fp = O.layer_forward(xp, cup, w, heads)
+    for i, s in enumerate(perm):
+        assert np.abs(fp[cup[i]:cup[i + 1]] - full[cu[s]:cu[s + 1]]).max() < 1e-12
+
+
+def test_bshd_valid_rows_equal_thd():
+    r = _rng(14)
+    H, F, heads = 128, 512, 2
+    w = _tiny_weights(H, F, r)
+    lens = [3, 8, 0, 6]
+    S = 8
+    xb = r.standard_normal((4, S, H))
+    xb[0, 3:] = np.nan  # padding content must not matter
+    out = O.layer_forward_bshd(xb, lens, w, heads)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = np.concatenate([xb[b, :L] for b, L in enumerate(lens)])
+    thd = O.layer_forward(x, cu, w, heads)
+    for b, L in enumerate(lens):
+        if L:
+            assert np.abs(out[b, :L] - thd[cu[b]:cu[b] + L]).max() < 1e-12
+        assert np.isnan(out[b, L:]).all()
+
+
+def test_interleaved_qkv_layout_round_trip_and_head_permutation():
+    r = _rng(15)
+    H, F, heads = 192, 768, 3
+    wq, wk, wv = (r.standard_normal((H, H)) * 0.05 for _ in range(3))
+    wqkv = O.pack_qkv_weight(wq, wk, wv, heads)
+    h = r.standard_normal((6, H))
+    q, k, v = O.split_qkv(h @ wqkv.T, heads)
+    assert np.abs(q.reshape(6, H) - h @ wq.T).max() < 1e-13
+    assert np.abs(k.reshape(6, H) - h @ wk.T).max() < 1e-13
+    assert np.abs(v.reshape(6, H) - h @ wv.T).max() < 1e-13
+    # Relabelling heads (in q, k, v rows and the matching out-projection
+    # columns) leaves the layer output unchanged.
+    w = _tiny_weights(H, F, r)
+    w["w_qkv"] = wqkv
+    x = r.standard_normal((10, H))
+    base = O.layer_forward(x, [0, 4, 10], w, heads)
+    perm = [2, 0, 1]
+    rows = np.concatenate([np.arange(192 * p, 192 * p + 192) for p in perm])
+    cols = np.concatenate([np.arange(64 * p, 64 * p + 64) for p in perm])
+    w2 = dict(w)
+    w2["w_qkv"] = w["w_qkv"][rows]
+    w2["b_qkv"] = w["b_qkv"][rows]
+    w2["w_out"] = w["w_out"][:, cols]
+    assert np.abs(O.layer_forward(x, [0, 4, 10], w2, heads) - base).max() < 1e-12
+
+
+def test_architecture_matches_the_pages():
+    g = json.load(open(os.path.join(GOLDEN, "esm2_architecture.json")))
+    from protein_language_model_amd.datagen import ESM2_650M, ESM2_3B
+    for key, m in (("650M", ESM2_650M), ("3B", ESM2_3B)):
+        assert (m.layers, m.hidden, m.heads) == (g[key]["layers"], g[key]["hidden"], g[key]["heads"])
+        assert m.hidden // m.heads == O.HEAD_DIM
+        n = O.param_count(m.hidden, m.ffn, m.layers, g["vocab_size"])
+        # The layer definition (4 linears with biases, FFN = 4H, two LayerNorms)
+        # lands in the parameter class the model names give.
+        assert abs(n / g[key]["params_class"] - 1) < 0.06, (key, n)
+    assert ESM2_650M.vocab == g["vocab_size"]
+    assert ESM2_650M.max_positions == g["max_position_embeddings"]
+
+
+def test_query_tiles_cover_each_row_once_longest_first():
+    lens = [5, 300, 0, 129, 300, 64]
+    tiles = O.query_tiles(lens, 128)
+    seen = {}
+    for s, q0 in tiles:
+        for t in range(q0, min(q0 + 128, lens[s])):
+            seen[(s, t)] = seen.get((s, t), 0) + 1
+    assert all(seen.get((s, t)) == 1 for s, L in enumerate(lens) for t in range(L))
+    assert len(seen) == sum(lens)
+    L_order = [lens[s] for s, _ in tiles]
+    assert L_order == sorted(L_order, reverse=True)
+
+
+def test_rel_max_err():
+    assert O.rel_max_err([1.0, 2.0], [1.0, 4.0]) == 0.5
+    assert O.rel_max_err([1.0, 5.0], [1.0, np.nan]) == 0.0
