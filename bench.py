@@ -1,0 +1,219 @@
+"""Throughput of the ESM-2 encoder forward on one MI355X.
+
+One step = one esm_stack_fwd call: embedding lookup plus all layers of the
+650M (33-layer, bf16) encoder over one packed THD batch of ~32768 residues
+(87 sequences, lognormal lengths, seed 0), inputs already resident in HBM.
+Timing follows the TransformerEngine tutorial's protocol: warm-up steps, then
+timed steps bracketed by device synchronisation, HIP events on the library
+stream.  Prints one JSON line.
+
+    python bench.py [--steps 30] [--warmup 10] [--workload 650m] [--no-cpu-baseline] [--padded]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (vendor figure)
+PEAK_HBM_GBS = 8000.0
+
+
+def layer_flops(H: int, F: int, T: int, sum_L2: int) -> dict:
+    """Algorithmic flops per launch of each kernel class for one layer."""
+    return {
+        "gemm_qkv": 2.0 * T * H * 3 * H,
+        "gemm_out": 2.0 * T * H * H,
+        "gemm_fc1": 2.0 * T * H * F,
+        "gemm_fc2": 2.0 * T * F * H,
+        "attention": 4.0 * H * sum_L2,   # q k^T and p v, 2 flops per multiply-add
+    }
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="650m", choices=["650m", "3b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--padded", action="store_true", help="also time the padded bshd layout of the same batch")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, batch, emb_bits, weights_dev, budget_residues: int = 2048, layers: int = 2) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    the first sequences of the batch up to `budget_residues` residues, through
+    `layers` layers; scaled to residues/s of the full-depth forward."""
+    from oracle import esm_oracle as O
+    from protein_language_model_amd import datagen as D
+    m = wl.model
+    n, tot = 0, 0
+    while n < batch.B and tot + int(batch.lengths[n]) <= budget_residues:
+        tot += int(batch.lengths[n])
+        n += 1
+    n = max(n, 1)
+    seqs = list(range(n))
+    tot = int(sum(batch.lengths[:n]))
+    cu = D.cu_from_lengths(batch.lengths[:n])
+    x = D.bf16_bits_to_f64(emb_bits)[batch.ids[:tot]]
+    ws = [O.weights_to_f64({k: D.tensor_bits(v) for k, v in weights_dev[l].items()}) for l in range(layers)]
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    for l in range(layers):
+        x = O.layer_forward(x, cu, ws[l], m.heads)
+    dt = time.perf_counter() - t0
+    per_layer = dt / layers
+    return {
+        "value": tot / (per_layer * m.layers),
+        "unit": "residues/s",
+        "cores": threads or os.cpu_count(),
+        "kind": "oracle",
+        "sample": f"first {n} sequences ({tot} residues) of the batch through {layers} of {m.layers} layers "
+                  f"(fp64 numpy/scipy), {dt:.1f} s; scaled to the {m.layers}-layer forward",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the forward needs no "
+              "cross-GPU exchange: a batch would be split by whole sequences, one process per GPU)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from protein_language_model_amd import datagen as D
+    from protein_language_model_amd import esm
+
+    wl = D.WORKLOADS[args.workload]
+    m = wl.model
+    batch = D.make_batch(wl)
+    dev = "cuda:0"
+    emb = D.make_embedding(m.vocab, m.hidden)
+    weights = [D.make_layer_weights_device(m.hidden, m.ffn, l) for l in range(m.layers)]
+
+    def up_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    enc = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn,
+                      num_hidden_layers=m.layers)
+    T, B = batch.T, batch.B
+    cu = torch.from_numpy(batch.cu_seqlens).to(dev)
+    ids = torch.from_numpy(batch.ids).to(dev)
+    emb_d = up_bf16(emb)
+    ws = enc.workspace(T, B)
+    out = torch.empty((T, m.hidden), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        enc.stack_fwd(weights, cu, B, T, batch.max_seqlen, token_ids=ids, embedding=emb_d, x_out=out,
+                      workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kernel_timing = not args.no_kernel_timing
+    if kernel_timing:
+        enc.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    prof = enc.profile_read() if kernel_timing else None
+    enc.profile_enable(False)
+
+    sum_L2 = int((batch.lengths.astype(np.int64) ** 2).sum())
+    fl = layer_flops(m.hidden, m.ffn, T, sum_L2)
+    total_flops = m.layers * sum(fl.values())
+    tflops = total_flops / (ms * 1e-3) / 1e12
+    value = T / (ms * 1e-3)
+
+    roofline = None
+    kernels = None
+    if prof:
+        kernels = {k: {"ms_per_launch": (v[0] / v[1]) if v[1] else None, "launches_per_step": v[1] / args.steps,
+                       "ms_per_step": v[0] / args.steps} for k, v in prof.items() if v[1]}
+        cand = {k: v for k, v in prof.items() if k in fl and v[1]}
+        dom = max(cand, key=lambda k: cand[k][0])
+        avg_ms = cand[dom][0] / cand[dom][1]
+        achieved = fl[dom] / (avg_ms * 1e-3) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": fl[dom]}
+
+    padded = None
+    if args.padded:
+        S = 1024
+        sl = torch.from_numpy(batch.lengths).to(dev)
+        ids_p = np.zeros((B, S), np.int32)
+        for i in range(B):
+            ids_p[i, :batch.lengths[i]] = batch.ids[batch.cu_seqlens[i]:batch.cu_seqlens[i + 1]]
+        ids_pd = torch.from_numpy(ids_p).to(dev)
+        ws_p = enc.workspace(B * S, B)
+        out_p = torch.empty((B, S, m.hidden), dtype=torch.bfloat16, device=dev)
+        for _ in range(2):
+            enc.stack_fwd_bshd(weights, sl, B, S, token_ids=ids_pd, embedding=emb_d, x_out=out_p, workspace=ws_p)
+        n_p = max(3, args.steps // 6)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n_p):
+            enc.stack_fwd_bshd(weights, sl, B, S, token_ids=ids_pd, embedding=emb_d, x_out=out_p, workspace=ws_p,
+                               stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_p = e0.elapsed_time(e1) / n_p
+        padded = {"layout": f"bshd [{B}, {S}]", "ms_per_step": round(ms_p, 3), "steps": n_p,
+                  "valid_fraction": round(T / (B * S), 4), "packing_gain": round(ms_p / ms, 3)}
+        del ws_p, out_p
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, batch, emb, weights)
+
+    rec = {
+        "metric": "packed residues/s, ESM-2 650M 33-layer fwd bf16; % of MFMA peak" if args.workload == "650m"
+        else "packed residues/s, ESM-2 3B-shaped 36-layer fwd bf16; % of MFMA peak",
+        "value": round(value, 1),
+        "unit": "residues/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"ESM-2 {m.hidden}x{m.layers} ({args.workload}) packed THD forward",
+                   "sequences": B, "residues": T, "max_seqlen": batch.max_seqlen, "sum_L2": sum_L2,
+                   "hidden": m.hidden, "heads": m.heads, "ffn": m.ffn, "layers": m.layers},
+        "tflops": round(tflops, 1),
+        "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "kernel_timing_in_timed_region": kernel_timing,
+        "padded": padded,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,272 @@
+/*
+ * esm_encoder.h -- C ABI of the MI355X (gfx950) ESM-2 encoder forward.
+ *
+ * The library runs the forward pass of the ESM-2 BERT-style encoder layer
+ * stack over variable-length protein sequences, either packed by cu_seqlens
+ * (THD layout, no padding) or padded (bshd layout with per-row valid
+ * lengths).  Every step runs in the library's own HIP kernels.
+ *
+ * Pages that define the operations (title, section):
+ *   [TE-ESM2] "深入源码NVIDIA ESM-2 TransformerEngine优化的实现原理与技术细节":
+ *             核心技术架构设计 (NVEsmEncoder: a stack of Transformer layers;
+ *             config.json 33 layers / hidden 1280 / 20 heads), 旋转位置编码集成
+ *             (rotary embedding of size hidden/heads), 注意力掩码优化 (padding mask,
+ *             bshd input format), 权重融合技术 (fused, interleaved QKV weight),
+ *             序列长度优化 (max_position_embeddings 1026, vocab 33),
+ *             自动混合精度训练 (per-layer forward loop).
+ *   [BIO-ACC] "生物大模型训练加速实战：基于PyTorch与NVIDIA BioNeMo的Transformer优化指南":
+ *             3.1 (EsmLayer: self-attention, LayerNorm, fc1, fc2; TransformerLayer
+ *             with hidden / ffn / heads, encoder type, padding mask, bshd or thd),
+ *             3.2 (collate_fn: cu_seqlens = cumsum([0] + lengths), max_seqlen =
+ *             max(lengths); PackedEsm.forward(input_ids, cu_seqlens, max_seqlen)
+ *             = embedding then every layer), 4.1 (DelayedScaling recipe).
+ *   [CARD]    "ESM-2" (BioNeMo framework model card): 描述 (bidirectional BERT-style
+ *             encoder; 650M and 3B shapes), 输入 (at most 1022 residues), 输出 (one
+ *             embedding vector per residue).
+ *   [TE-RU]   TransformerEngine tutorial summary (aikraft.ru): fused modules
+ *             LayerNormLinear / LayerNormMLP / TransformerLayer; FP8 DelayedScaling
+ *             with amax_history_len 16 and the "max" algorithm.
+ *
+ * Conventions for every call
+ *   - All tensors are device pointers to bfloat16 unless stated, row-major,
+ *     16-byte aligned.  Linear weights use the [out, in] layout.
+ *   - Calls are asynchronous on the given stream (hipStream_t, NULL = the
+ *     default stream): they enqueue kernels and return.  The caller keeps every
+ *     buffer alive until the stream has passed the call.
+ *   - All argument checks happen on the host before anything is enqueued; on
+ *     failure nothing is enqueued and esm_last_error() describes the problem.
+ *   - One handle must not be used from two host threads or two streams at once.
+ *   - The caller owns every tensor passed in, the workspace and the stream.  The
+ *     library owns the handle and the rotary table it builds at create time.
+ */
+#ifndef ESM_ENCODER_H
+#define ESM_ENCODER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ESM_ABI_VERSION 1
+
+typedef struct esm_encoder esm_encoder;
+typedef void* esm_stream_t; /* a hipStream_t */
+
+typedef enum {
+  ESM_OK = 0,
+  ESM_ERR_NULL = 1,        /* a required pointer is NULL */
+  ESM_ERR_SHAPE = 2,       /* bad hidden / heads / ffn / layers / vocab / T / B / S */
+  ESM_ERR_SEQLENS = 3,     /* host copy of cu_seqlens / seqlens inconsistent */
+  ESM_ERR_UNSUPPORTED = 4, /* head_dim != 64, misaligned pointer, unknown option */
+  ESM_ERR_WORKSPACE = 5,   /* workspace NULL or too small */
+  ESM_ERR_ARCH = 6,        /* device is not gfx950 */
+  ESM_ERR_HIP = 7,         /* HIP runtime error */
+  ESM_ERR_STATE = 8        /* call not valid in the handle's current state */
+} esm_status;
+
+typedef enum { ESM_PRECISION_BF16 = 0, ESM_PRECISION_FP8_DELAYED = 1 } esm_precision;
+typedef enum { ESM_LAYOUT_THD = 0, ESM_LAYOUT_BSHD = 1 } esm_layout;
+
+/* Model configuration.  Key names follow the config.json keys of [TE-ESM2]. */
+typedef struct {
+  int32_t hidden_size;          /* H, multiple of 64 */
+  int32_t num_attention_heads;  /* H / 64 (head_dim 64 is the only one built) */
+  int32_t intermediate_size;    /* F, FFN width, multiple of 64 */
+  int32_t num_hidden_layers;    /* layers in a stack call */
+  int32_t vocab_size;           /* rows of the embedding table */
+  int32_t max_position_embeddings; /* rotary table rows; longest allowed sequence */
+  float layer_norm_eps;         /* LayerNorm epsilon (biased variance) */
+  float rope_base;              /* rotary base; theta_i = p * base^(-i/32) */
+  int32_t precision;            /* esm_precision */
+  int32_t amax_history_len;     /* FP8 delayed-scaling history, 1..1024 */
+} esm_config;
+
+/* Fills the ESM-2 650M configuration: H 1280, 20 heads, F 5120, 33 layers,
+ * vocab 33, 1026 positions, eps 1e-5, base 10000, bf16, history 16. */
+void esm_config_default(esm_config* cfg);
+
+/* One layer's tensors (bfloat16, device).  Rows of w_qkv [3H, H] are grouped
+ * per head as in [TE-ESM2] 权重融合技术 with the interleaved flag: row
+ * 192*n + 64*c + j is component c (0 query, 1 key, 2 value) of head n, dim j.
+ * Bias pointers may be NULL (treated as zero); gamma/beta may not. */
+typedef struct {
+  const void* ln1_gamma; /* [H] */
+  const void* ln1_beta;  /* [H] */
+  const void* w_qkv;     /* [3H, H] */
+  const void* b_qkv;     /* [3H] */
+  const void* w_out;     /* [H, H] */
+  const void* b_out;     /* [H] */
+  const void* ln2_gamma; /* [H] */
+  const void* ln2_beta;  /* [H] */
+  const void* w_fc1;     /* [F, H] */
+  const void* b_fc1;     /* [F] */
+  const void* w_fc2;     /* [H, F] */
+  const void* b_fc2;     /* [H] */
+} esm_layer_weights;
+
+/* ---------------------------------------------------------------- lifetime */
+
+/* Validates cfg, checks that `device` is a gfx950 GPU (ESM_ERR_ARCH otherwise),
+ * makes it current and builds the rotary cos/sin table [max_positions, 32]
+ * (fp32, computed in fp64 on the host).  *out receives the new handle. */
+esm_status esm_encoder_create(const esm_config* cfg, int device, esm_encoder** out);
+
+/* Frees the handle and everything it owns.  NULL is a no-op. */
+esm_status esm_encoder_destroy(esm_encoder* enc);
+
+/* ---------------------------------------------------------------- workspace */
+
+/* Bytes of device workspace a forward call needs for up to max_tokens rows
+ * (T for THD, B*S for bshd) and max_seqs sequences.  The workspace is
+ * caller-allocated, 256-byte aligned, and may be reused between calls once the
+ * stream has passed the previous one.  Its contents after a layer call hold
+ * that layer's intermediates (see esm_workspace_region). */
+esm_status esm_workspace_size(const esm_encoder* enc, int64_t max_tokens, int32_t max_seqs,
+                              size_t* bytes);
+
+typedef enum {
+  ESM_WS_LN1 = 0,   /* bf16 [T, H]  LayerNorm-1 output */
+  ESM_WS_QKV = 1,   /* bf16 [3, heads, T, 64]  rotated q, rotated k, v (planar) */
+  ESM_WS_CTX = 2,   /* bf16 [T, H]  attention output, head-major columns */
+  ESM_WS_X1 = 3,    /* bf16 [T, H]  after the attention residual */
+  ESM_WS_LN2 = 4,   /* bf16 [T, H]  LayerNorm-2 output */
+  ESM_WS_ACT = 5,   /* bf16 [T, F]  GELU(fc1) */
+  ESM_WS_POS = 6,   /* int32 [T]    position of each row in its sequence, -1 = padding */
+  ESM_WS_TILES = 7, /* int32 [n, 2] attention query tiles (sequence, first row) */
+  ESM_WS_NTILES = 8,/* int32 [1]    number of valid tiles */
+  ESM_WS_SEGS = 9   /* int32 [B, 2] (first row, length) of every sequence */
+} esm_ws_region;
+
+/* Byte offset and size of one region inside a workspace sized for
+ * (max_tokens, max_seqs).  Row strides use T = max_tokens. */
+esm_status esm_workspace_region(const esm_encoder* enc, int64_t max_tokens, int32_t max_seqs,
+                                int32_t region, size_t* offset, size_t* bytes);
+
+/* ---------------------------------------------------------------- forward */
+
+/* One pre-LN encoder layer on a packed batch ([BIO-ACC] 3.1, 3.2):
+ *   X1 = X + Attn(RoPE(LN1(X) W_qkv^T + b_qkv)) W_out^T + b_out
+ *   Y  = X1 + GELU(LN2(X1) W_fc1^T + b_fc1) W_fc2^T + b_fc2
+ * Attention is non-causal and stays inside each sequence; positions restart at
+ * 0 in every sequence.
+ *   x_in, x_out      [T, H]; x_out may equal x_in (in-place)
+ *   cu_seqlens_dev   int32 [B+1] on the device: sequence s owns rows
+ *                    cu[s] .. cu[s+1]-1; zero-length sequences allowed
+ *   cu_seqlens_host  optional host copy; when given it is checked (cu[0] = 0,
+ *                    non-decreasing, cu[B] = T, every length <= max_seqlen <=
+ *                    max_positions) and ESM_ERR_SEQLENS returned on failure.
+ *                    When NULL the device array is trusted; kernels clamp every
+ *                    index, so bad values give wrong numbers, never an
+ *                    out-of-bounds access.
+ *   max_seqlen       host upper bound on the sequence lengths
+ *   layer_idx        0-based index of the layer (FP8 state slot)
+ * T = 0 or B = 0 returns ESM_OK without a launch. */
+esm_status esm_layer_fwd(esm_encoder* enc, const esm_layer_weights* w, int32_t layer_idx,
+                         const void* x_in, void* x_out,
+                         const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                         int32_t B, int64_t T, int32_t max_seqlen,
+                         void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* Embedding lookup (when token_ids != NULL: X0 = E[ids], ids clamped into
+ * [0, vocab)) or the given hidden states x_in, then all num_hidden_layers
+ * layers in order ([BIO-ACC] 3.2 PackedEsm.forward; [TE-ESM2] 自动混合精度训练).
+ * No final LayerNorm.  `w` is a HOST array of num_hidden_layers structs. */
+esm_status esm_stack_fwd(esm_encoder* enc, const esm_layer_weights* w,
+                         const int32_t* token_ids, const void* embedding,
+                         const void* x_in, void* x_out,
+                         const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                         int32_t B, int64_t T, int32_t max_seqlen,
+                         void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* Padded (bshd) variants ([TE-ESM2] 注意力掩码优化; [BIO-ACC] 3.1 bshd format).
+ * x_in / x_out are [B, S, H]; row b holds a valid prefix of seqlens[b] <= S
+ * tokens (the padding mask, 1 = valid, as lengths).  Keys beyond the prefix
+ * are never read; output rows beyond it are written as 0.  The dense layers run
+ * over all B*S rows, as padded execution does.  Workspace is sized with
+ * max_tokens = B*S, max_seqs = B. */
+esm_status esm_layer_fwd_bshd(esm_encoder* enc, const esm_layer_weights* w, int32_t layer_idx,
+                              const void* x_in, void* x_out,
+                              const int32_t* seqlens_dev, const int32_t* seqlens_host,
+                              int32_t B, int32_t S,
+                              void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+esm_status esm_stack_fwd_bshd(esm_encoder* enc, const esm_layer_weights* w,
+                              const int32_t* token_ids, const void* embedding,
+                              const void* x_in, void* x_out,
+                              const int32_t* seqlens_dev, const int32_t* seqlens_host,
+                              int32_t B, int32_t S,
+                              void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* ---------------------------------------------------------------- kernel-level entries */
+
+/* Segment table ([BIO-ACC] 3.2 cu_seqlens contract): writes into the workspace
+ * the per-row positions (ESM_WS_POS), the sequence extents (ESM_WS_SEGS) and the
+ * attention query tiles of `tile_rows` = 128 rows, longest sequence first
+ * (ESM_WS_TILES, count in ESM_WS_NTILES).  layout selects cu_seqlens (THD,
+ * `lens` = cu [B+1], S ignored) or seqlens (bshd, `lens` = [B], rows b*S + p). */
+esm_status esm_segment_table(esm_encoder* enc, int32_t layout, const int32_t* lens_dev,
+                             int32_t B, int64_t T, int32_t S,
+                             void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* Attention alone on a packed batch: qkv is [3, heads, T, 64] (q and k
+ * already rotated), ctx is [T, H].  Runs the segment table first. */
+esm_status esm_attention_fwd(esm_encoder* enc, const void* qkv, void* ctx,
+                             const int32_t* cu_seqlens_dev, int32_t B, int64_t T,
+                             void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+typedef enum {
+  ESM_EPI_BIAS = 0,          /* y = x W^T + b */
+  ESM_EPI_BIAS_GELU = 1,     /* y = GELU(x W^T + b) */
+  ESM_EPI_BIAS_RESIDUAL = 2  /* y = r + x W^T + b */
+} esm_epilogue;
+
+/* y[M, N] = epilogue(x[M, K] W[N, K]^T + b) on the library's MFMA GEMM.
+ * N and K must be multiples of 64; residual r is [M, N] (may equal y). */
+esm_status esm_linear_fwd(esm_encoder* enc, const void* x, const void* w, const void* b,
+                          const void* residual, void* y, int64_t M, int32_t N, int32_t K,
+                          int32_t epilogue, esm_stream_t stream);
+
+/* Row LayerNorm y = (x - mean) / sqrt(var + eps) * gamma + beta over [M, H]. */
+esm_status esm_layernorm_fwd(esm_encoder* enc, const void* x, const void* gamma,
+                             const void* beta, void* y, int64_t M, esm_stream_t stream);
+
+/* ---------------------------------------------------------------- timing */
+
+/* Kernel classes timed when profiling is on. */
+typedef enum {
+  ESM_K_SEGMENT = 0, ESM_K_EMBED = 1, ESM_K_LAYERNORM = 2, ESM_K_GEMM_QKV = 3,
+  ESM_K_ATTENTION = 4, ESM_K_GEMM_OUT = 5, ESM_K_GEMM_FC1 = 6, ESM_K_GEMM_FC2 = 7,
+  ESM_K_OTHER = 8, ESM_K_COUNT = 9
+} esm_kernel_class;
+
+/* When on, every launch is bracketed by HIP events recorded on the launch
+ * stream, and durations are summed per kernel class.  Turning it on clears the
+ * sums.  Adds two event records per launch. */
+esm_status esm_profile_enable(esm_encoder* enc, int32_t on);
+
+/* Waits for the recorded events and returns, per class, the summed kernel time
+ * in milliseconds and the number of launches (arrays of ESM_K_COUNT). */
+esm_status esm_profile_read(esm_encoder* enc, double* ms_out, int64_t* launches_out);
+
+/* ---------------------------------------------------------------- host-only helpers */
+
+/* Host check of a cu_seqlens array (no device work): cu[0] = 0, non-decreasing,
+ * cu[B] = T, every length <= max_seqlen, max_seqlen <= max_positions. */
+esm_status esm_check_cu_seqlens(const int32_t* cu_host, int32_t B, int64_t T,
+                                int32_t max_seqlen, int32_t max_positions);
+
+/* Host check of padded lengths: 0 <= seqlens[b] <= S <= max_positions. */
+esm_status esm_check_seqlens(const int32_t* seqlens_host, int32_t B, int32_t S,
+                             int32_t max_positions);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char* esm_last_error(void);
+const char* esm_status_str(esm_status s);
+int32_t esm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ESM_ENCODER_H */

@@ -1,0 +1,229 @@
+// Memory-bound pieces of the encoder forward on gfx950:
+//   * segment table: per-sequence extents, per-row positions and the attention
+//     query-tile list, built on the device from cu_seqlens (no host sync),
+//   * embedding gather X0 = E[ids],
+//   * row LayerNorm.
+#include "common.h"
+
+namespace esm {
+
+namespace {
+
+constexpr int kSegThreads = 1024;
+
+// Sequence extents and the list of 128-row query tiles, longest sequence
+// first ([BIO-ACC] 3.2: cu_seqlens = cumsum([0] + lengths); sequence s owns
+// rows cu[s] .. cu[s+1]-1).  One workgroup: a counting sort of the tiles by
+// sequence length (bucket = max_positions - length, so long sequences come
+// first); tiles of equal-length sequences may come in any order.  Every value
+// read from the device array is clamped, so inconsistent input cannot lead to
+// an out-of-range row.
+__global__ __launch_bounds__(kSegThreads) void k_segment_table(int layout, const int32_t* __restrict__ lens,
+                                                               int32_t B, int64_t rows, int32_t S, int32_t nbins,
+                                                               SegOut out) {
+  extern __shared__ int32_t sh[];
+  int32_t* hist = sh;           // [nbins]
+  int32_t* part = sh + nbins;   // [kSegThreads]
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nbins; i += kSegThreads) hist[i] = 0;
+  __syncthreads();
+  for (int s = tid; s < B; s += kSegThreads) {
+    int64_t start, len;
+    if (layout == 0) {
+      int64_t a = lens[s], b = lens[s + 1];
+      a = a < 0 ? 0 : (a > rows ? rows : a);
+      b = b < a ? a : (b > rows ? rows : b);
+      start = a;
+      len = b - a;
+    } else {
+      int64_t l = lens[s];
+      l = l < 0 ? 0 : (l > S ? S : l);
+      start = (int64_t)s * S;
+      len = l;
+    }
+    out.segs[2 * s] = (int32_t)start;
+    out.segs[2 * s + 1] = (int32_t)len;
+    const int64_t nt = (len + kAttnTileRows - 1) / kAttnTileRows;
+    if (nt) atomicAdd(&hist[nbins - 1 - (int)(len < nbins - 1 ? len : nbins - 1)], (int32_t)nt);
+  }
+  __syncthreads();
+  // Exclusive scan of the histogram: per-thread serial chunk, then a block scan.
+  const int per = (nbins + kSegThreads - 1) / kSegThreads;
+  const int b0 = tid * per;
+  const int b1 = b0 + per < nbins ? b0 + per : nbins;
+  int32_t local = 0;
+  for (int i = b0; i < b1; ++i) local += hist[i];
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kSegThreads; off <<= 1) {
+    const int32_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - local;
+  for (int i = b0; i < b1; ++i) {
+    const int32_t c = hist[i];
+    hist[i] = run;
+    run += c;
+  }
+  const int32_t total = part[kSegThreads - 1];
+  __syncthreads();
+  for (int s = tid; s < B; s += kSegThreads) {
+    const int32_t len = out.segs[2 * s + 1];
+    const int32_t nt = (len + kAttnTileRows - 1) / kAttnTileRows;
+    if (!nt) continue;
+    const int32_t base = atomicAdd(&hist[nbins - 1 - (len < nbins - 1 ? len : nbins - 1)], nt);
+    for (int32_t i = 0; i < nt; ++i) {
+      const int64_t idx = (int64_t)base + i;
+      if (idx < out.tile_cap) {
+        out.tiles[2 * idx] = s;
+        out.tiles[2 * idx + 1] = i * kAttnTileRows;
+      }
+    }
+  }
+  if (tid == 0) *out.ntiles = (int32_t)(total < out.tile_cap ? total : out.tile_cap);
+}
+
+// Position of every row inside its sequence (rotary positions restart at 0 in
+// each sequence); -1 marks padding rows of a bshd batch.
+__global__ void k_positions(int layout, const int32_t* __restrict__ lens, int32_t B, int64_t rows, int32_t S,
+                            int32_t* __restrict__ pos) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= rows) return;
+  if (B <= 0) {
+    pos[t] = -1;
+    return;
+  }
+  if (layout == 0) {
+    // last s in [0, B) with cu[s] <= t
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int64_t)lens[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int64_t a = lens[lo], b = lens[lo + 1];
+    pos[t] = (a <= t && t < b) ? (int32_t)(t - a) : -1;
+  } else {
+    const int64_t b = t / S, p = t % S;
+    int64_t l = lens[b];
+    l = l < 0 ? 0 : (l > S ? S : l);
+    pos[t] = p < l ? (int32_t)p : -1;
+  }
+}
+
+// X0 = E[ids] ([BIO-ACC] 3.2 PackedEsm.forward: embedding of the packed ids).
+__global__ void k_embed(const int32_t* __restrict__ ids, const bf16_t* __restrict__ table, int32_t vocab,
+                        bf16_t* __restrict__ x, int64_t T, int32_t H) {
+  const int chunks = H / 8;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * chunks) return;
+  const int64_t t = i / chunks;
+  const int c = (int)(i % chunks);
+  int id = ids[t];
+  id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+  *(u32x4*)(x + t * H + c * 8) = *(const u32x4*)(table + (int64_t)id * H + c * 8);
+}
+
+// Row LayerNorm, one wave per row: mean, then the biased variance from the
+// centred values held in registers, y = (x - mean) * rsqrt(var + eps) * g + b
+// ([BIO-ACC] 3.1 layernorm; [TE-RU] LayerNormLinear / LayerNormMLP).
+template <int CH>
+__global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
+                                                   const bf16_t* __restrict__ beta, bf16_t* __restrict__ y,
+                                                   int64_t M, int32_t H, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int chunks = H / 8;
+  const bf16_t* xr = x + row * H;
+  float v[CH][8];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+      const u32x4 w = *(const u32x4*)(xr + c * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[i][2 * e] = bflo(w[e]);
+        v[i][2 * e + 1] = bfhi(w[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += v[i][e];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  const float mean = sum / (float)H;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[i][e] -= mean;
+        sq += v[i][e] * v[i][e];
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+  const float rstd = 1.0f / sqrtf(sq / (float)H + eps);
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+      const u32x4 g = *(const u32x4*)(gamma + c * 8);
+      const u32x4 b = *(const u32x4*)(beta + c * 8);
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float y0 = v[i][2 * e] * rstd * bflo(g[e]) + bflo(b[e]);
+        const float y1 = v[i][2 * e + 1] * rstd * bfhi(g[e]) + bfhi(b[e]);
+        o[e] = pack_bf2(y0, y1);
+      }
+      *(u32x4*)(y + row * H + c * 8) = o;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_segment_table(int layout, const int32_t* lens, int32_t B, int64_t rows, int32_t S,
+                                int32_t max_positions, const SegOut& out, hipStream_t st) {
+  // Lengths above the last bin share it (they still sort first).
+  const int32_t nbins = (max_positions < 8192 ? max_positions : 8192) + 1;
+  const size_t shmem = sizeof(int32_t) * ((size_t)nbins + kSegThreads);
+  hipLaunchKernelGGL(k_segment_table, dim3(1), dim3(kSegThreads), shmem, st, layout, lens, B, rows, S, nbins, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || rows <= 0) return e;
+  hipLaunchKernelGGL(k_positions, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, layout, lens, B, rows, S,
+                     out.pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const int32_t* ids, const bf16_t* table, int32_t vocab, bf16_t* x, int64_t T, int32_t H,
+                        hipStream_t st) {
+  const int64_t n = T * (H / 8);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_embed, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids, table, vocab, x, T, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y, int64_t M,
+                            int32_t H, float eps, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((M + 3) / 4);
+  const int ch = (H / 8 + 63) / 64;
+  if (ch <= 1) hipLaunchKernelGGL(k_layernorm<1>, dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps);
+  else if (ch <= 2) hipLaunchKernelGGL(k_layernorm<2>, dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps);
+  else if (ch <= 3) hipLaunchKernelGGL(k_layernorm<3>, dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps);
+  else if (ch <= 5) hipLaunchKernelGGL(k_layernorm<5>, dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps);
+  else if (ch <= 8) hipLaunchKernelGGL(k_layernorm<8>, dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace esm

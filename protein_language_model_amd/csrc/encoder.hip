@@ -1,0 +1,634 @@
+// Host side of the C ABI declared in include/esm_encoder.h: argument checks,
+// workspace planning, the launch sequence of one encoder layer and of the
+// stack, and per-kernel-class timing with HIP events.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/esm_encoder.h"
+#include "common.h"
+
+using namespace esm;
+
+struct esm_encoder {
+  esm_config cfg;
+  int device = 0;
+  float2* rope = nullptr;  // [max_positions, 32]
+  bool profiling = false;
+  std::vector<hipEvent_t> pool;
+  size_t pool_used = 0;
+  std::vector<std::pair<int, size_t>> recs;  // (class, index of start event)
+  double ms[ESM_K_COUNT] = {0};
+  int64_t launches[ESM_K_COUNT] = {0};
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+esm_status fail(esm_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+esm_status ok() { return ESM_OK; }
+
+esm_status hip_fail(hipError_t e, const char* what) {
+  return fail(ESM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                      \
+  do {                                           \
+    hipError_t _e = (expr);                      \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+esm_status check_config(const esm_config* c) {
+  if (!c) return fail(ESM_ERR_NULL, "config is NULL");
+  if (c->hidden_size <= 0 || c->hidden_size % 64 != 0)
+    return fail(ESM_ERR_SHAPE, "hidden_size %d must be a positive multiple of 64", c->hidden_size);
+  if (c->num_attention_heads <= 0 || c->hidden_size / c->num_attention_heads * c->num_attention_heads != c->hidden_size)
+    return fail(ESM_ERR_SHAPE, "num_attention_heads %d does not divide hidden_size %d", c->num_attention_heads,
+                c->hidden_size);
+  if (c->hidden_size / c->num_attention_heads != kHeadDim)
+    return fail(ESM_ERR_UNSUPPORTED, "head_dim %d: only 64 is built", c->hidden_size / c->num_attention_heads);
+  if (c->hidden_size > 4096) return fail(ESM_ERR_UNSUPPORTED, "hidden_size %d above 4096", c->hidden_size);
+  if (c->intermediate_size <= 0 || c->intermediate_size % 64 != 0)
+    return fail(ESM_ERR_SHAPE, "intermediate_size %d must be a positive multiple of 64", c->intermediate_size);
+  if (c->num_hidden_layers < 0) return fail(ESM_ERR_SHAPE, "num_hidden_layers %d < 0", c->num_hidden_layers);
+  if (c->vocab_size <= 0) return fail(ESM_ERR_SHAPE, "vocab_size %d <= 0", c->vocab_size);
+  if (c->max_position_embeddings <= 0 || c->max_position_embeddings > 65536)
+    return fail(ESM_ERR_SHAPE, "max_position_embeddings %d outside [1, 65536]", c->max_position_embeddings);
+  if (!(c->layer_norm_eps > 0.f) || !isfinite(c->layer_norm_eps))
+    return fail(ESM_ERR_SHAPE, "layer_norm_eps must be positive and finite");
+  if (!(c->rope_base > 1.f) || !isfinite(c->rope_base)) return fail(ESM_ERR_SHAPE, "rope_base must be > 1");
+  if (c->precision != ESM_PRECISION_BF16 && c->precision != ESM_PRECISION_FP8_DELAYED)
+    return fail(ESM_ERR_UNSUPPORTED, "unknown precision %d", c->precision);
+  if (c->precision == ESM_PRECISION_FP8_DELAYED)
+    return fail(ESM_ERR_UNSUPPORTED, "FP8 delayed scaling is not built in this library version");
+  if (c->amax_history_len < 1 || c->amax_history_len > 1024)
+    return fail(ESM_ERR_SHAPE, "amax_history_len %d outside [1, 1024]", c->amax_history_len);
+  return ok();
+}
+
+// ---------------------------------------------------------------- workspace plan
+
+struct Plan {
+  size_t off[10];
+  size_t size[10];
+  size_t total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t tile_cap(int64_t rows, int32_t seqs) { return rows / kAttnTileRows + seqs + 1; }
+
+Plan make_plan(const esm_config& c, int64_t T, int32_t B) {
+  Plan p;
+  const size_t H = (size_t)c.hidden_size, F = (size_t)c.intermediate_size;
+  const size_t t = (size_t)(T > 0 ? T : 0), b = (size_t)(B > 0 ? B : 0);
+  size_t sizes[10];
+  sizes[ESM_WS_LN1] = t * H * 2;
+  sizes[ESM_WS_QKV] = 3 * t * H * 2;
+  sizes[ESM_WS_CTX] = t * H * 2;
+  sizes[ESM_WS_X1] = t * H * 2;
+  sizes[ESM_WS_LN2] = t * H * 2;
+  sizes[ESM_WS_ACT] = t * F * 2;
+  sizes[ESM_WS_POS] = t * 4;
+  sizes[ESM_WS_TILES] = (size_t)tile_cap((int64_t)t, (int32_t)b) * 8;
+  sizes[ESM_WS_NTILES] = 4;
+  sizes[ESM_WS_SEGS] = b * 8;
+  size_t o = 0;
+  for (int i = 0; i < 10; ++i) {
+    p.off[i] = o;
+    p.size[i] = sizes[i];
+    o += align256(sizes[i]);
+  }
+  p.total = o;
+  return p;
+}
+
+template <class T>
+T* region(void* ws, const Plan& p, int r) {
+  return (T*)((char*)ws + p.off[r]);
+}
+
+// ---------------------------------------------------------------- timing
+
+esm_status grow_pool(esm_encoder* e) {
+  for (int i = 0; i < 256; ++i) {
+    hipEvent_t ev;
+    HIP_TRY(hipEventCreate(&ev), "hipEventCreate");
+    e->pool.push_back(ev);
+  }
+  return ok();
+}
+
+template <class F>
+esm_status timed(esm_encoder* e, int cls, hipStream_t st, const char* what, F&& launch) {
+  if (!e->profiling) {
+    hipError_t err = launch();
+    if (err != hipSuccess) return hip_fail(err, what);
+    return ok();
+  }
+  if (e->pool_used + 2 > e->pool.size()) {
+    esm_status s = grow_pool(e);
+    if (s != ESM_OK) return s;
+  }
+  const size_t i0 = e->pool_used;
+  e->pool_used += 2;
+  HIP_TRY(hipEventRecord(e->pool[i0], st), "hipEventRecord");
+  hipError_t err = launch();
+  if (err != hipSuccess) return hip_fail(err, what);
+  HIP_TRY(hipEventRecord(e->pool[i0 + 1], st), "hipEventRecord");
+  e->recs.push_back({cls, i0});
+  return ok();
+}
+
+// ---------------------------------------------------------------- argument checks
+
+esm_status check_weights(const esm_layer_weights* w, int idx) {
+  if (!w) return fail(ESM_ERR_NULL, "layer %d: weights struct is NULL", idx);
+  const void* req[] = {w->ln1_gamma, w->ln1_beta, w->w_qkv, w->w_out, w->ln2_gamma, w->ln2_beta, w->w_fc1, w->w_fc2};
+  const char* names[] = {"ln1_gamma", "ln1_beta", "w_qkv", "w_out", "ln2_gamma", "ln2_beta", "w_fc1", "w_fc2"};
+  for (int i = 0; i < 8; ++i) {
+    if (!req[i]) return fail(ESM_ERR_NULL, "layer %d: %s is NULL", idx, names[i]);
+    if (!aligned16(req[i])) return fail(ESM_ERR_UNSUPPORTED, "layer %d: %s not 16-byte aligned", idx, names[i]);
+  }
+  const void* opt[] = {w->b_qkv, w->b_out, w->b_fc1, w->b_fc2};
+  for (int i = 0; i < 4; ++i)
+    if (opt[i] && ((uintptr_t)opt[i] & 7u)) return fail(ESM_ERR_UNSUPPORTED, "layer %d: bias not 8-byte aligned", idx);
+  return ok();
+}
+
+esm_status check_rows(const esm_encoder* e, int64_t rows, int32_t B) {
+  if (rows < 0 || B < 0) return fail(ESM_ERR_SHAPE, "negative T (%lld) or B (%d)", (long long)rows, B);
+  if (rows > (int64_t)INT32_MAX - 1024) return fail(ESM_ERR_SHAPE, "T = %lld rows too large", (long long)rows);
+  (void)e;
+  return ok();
+}
+
+esm_status check_ws(const esm_encoder* e, void* ws, size_t ws_bytes, int64_t rows, int32_t B, Plan* p) {
+  *p = make_plan(e->cfg, rows, B);
+  if (!ws) return fail(ESM_ERR_WORKSPACE, "workspace is NULL");
+  if ((uintptr_t)ws & 255u) return fail(ESM_ERR_WORKSPACE, "workspace not 256-byte aligned");
+  if (ws_bytes < p->total)
+    return fail(ESM_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", ws_bytes, p->total);
+  return ok();
+}
+
+// ---------------------------------------------------------------- launch sequence
+
+esm_status run_segments(esm_encoder* e, int layout, const int32_t* lens, int32_t B, int64_t rows, int32_t S,
+                        void* ws, const Plan& p, hipStream_t st) {
+  SegOut so;
+  so.pos = region<int32_t>(ws, p, ESM_WS_POS);
+  so.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
+  so.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
+  so.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
+  so.tile_cap = tile_cap(rows, B);
+  return timed(e, ESM_K_SEGMENT, st, "segment table", [&] {
+    return launch_segment_table(layout, lens, B, rows, S, e->cfg.max_position_embeddings, so, st);
+  });
+}
+
+// One pre-LN layer on rows already described by the segment table in ws.
+esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, const bf16_t* x_in, bf16_t* x_out, int64_t rows,
+                     int32_t B, bool zero_pad_rows, void* ws, const Plan& p, hipStream_t st) {
+  const esm_config& c = e->cfg;
+  const int H = c.hidden_size, F = c.intermediate_size, heads = c.num_attention_heads;
+  bf16_t* ln1 = region<bf16_t>(ws, p, ESM_WS_LN1);
+  bf16_t* qkv = region<bf16_t>(ws, p, ESM_WS_QKV);
+  bf16_t* ctx = region<bf16_t>(ws, p, ESM_WS_CTX);
+  bf16_t* x1 = region<bf16_t>(ws, p, ESM_WS_X1);
+  bf16_t* ln2 = region<bf16_t>(ws, p, ESM_WS_LN2);
+  bf16_t* act = region<bf16_t>(ws, p, ESM_WS_ACT);
+  const int32_t* pos = region<int32_t>(ws, p, ESM_WS_POS);
+  esm_status s;
+
+  s = timed(e, ESM_K_LAYERNORM, st, "layernorm 1", [&] {
+    return launch_layernorm(x_in, (const bf16_t*)w->ln1_gamma, (const bf16_t*)w->ln1_beta, ln1, rows, H,
+                            c.layer_norm_eps, st);
+  });
+  if (s) return s;
+
+  GemmArgs g{};
+  g.M = rows;
+  g.pos = pos;
+  g.rope = e->rope;
+  g.max_positions = c.max_position_embeddings;
+  g.zero_pad_rows = zero_pad_rows ? 1 : 0;
+
+  g.x = ln1; g.w = (const bf16_t*)w->w_qkv; g.bias = (const bf16_t*)w->b_qkv; g.res = nullptr; g.y = qkv;
+  g.N = 3 * H; g.K = H;
+  s = timed(e, ESM_K_GEMM_QKV, st, "qkv gemm", [&] { return launch_gemm(EPI_QKV_ROPE, g, st); });
+  if (s) return s;
+
+  AttnArgs aa{};
+  aa.qkv = qkv; aa.ctx = ctx;
+  aa.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
+  aa.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
+  aa.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
+  aa.tile_cap = tile_cap(rows, B);
+  aa.T = rows; aa.heads = heads;
+  s = timed(e, ESM_K_ATTENTION, st, "attention", [&] { return launch_attention(aa, st); });
+  if (s) return s;
+
+  g.x = ctx; g.w = (const bf16_t*)w->w_out; g.bias = (const bf16_t*)w->b_out; g.res = x_in; g.y = x1;
+  g.N = H; g.K = H;
+  s = timed(e, ESM_K_GEMM_OUT, st, "out-proj gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
+  if (s) return s;
+
+  s = timed(e, ESM_K_LAYERNORM, st, "layernorm 2", [&] {
+    return launch_layernorm(x1, (const bf16_t*)w->ln2_gamma, (const bf16_t*)w->ln2_beta, ln2, rows, H,
+                            c.layer_norm_eps, st);
+  });
+  if (s) return s;
+
+  g.x = ln2; g.w = (const bf16_t*)w->w_fc1; g.bias = (const bf16_t*)w->b_fc1; g.res = nullptr; g.y = act;
+  g.N = F; g.K = H;
+  s = timed(e, ESM_K_GEMM_FC1, st, "fc1 gemm", [&] { return launch_gemm(EPI_BIAS_GELU, g, st); });
+  if (s) return s;
+
+  g.x = act; g.w = (const bf16_t*)w->w_fc2; g.bias = (const bf16_t*)w->b_fc2; g.res = x1; g.y = x_out;
+  g.N = H; g.K = F;
+  return timed(e, ESM_K_GEMM_FC2, st, "fc2 gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
+}
+
+esm_status check_cu_host(const esm_encoder* e, const int32_t* cu, int32_t B, int64_t T, int32_t max_seqlen) {
+  if (max_seqlen < 0 || max_seqlen > e->cfg.max_position_embeddings)
+    return fail(ESM_ERR_SEQLENS, "max_seqlen %d outside [0, max_position_embeddings = %d]", max_seqlen,
+                e->cfg.max_position_embeddings);
+  if (cu) return esm_check_cu_seqlens(cu, B, T, max_seqlen, e->cfg.max_position_embeddings);
+  return ok();
+}
+
+esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, int32_t layer_idx,
+                       const int32_t* ids, const void* emb, const void* x_in, void* x_out, const int32_t* cu_dev,
+                       const int32_t* cu_host, int32_t B, int64_t T, int32_t max_seqlen, void* ws, size_t ws_bytes,
+                       esm_stream_t stream) {
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  esm_status s = check_rows(e, T, B);
+  if (s) return s;
+  if (T == 0 || B == 0) return ok();
+  if (!x_out) return fail(ESM_ERR_NULL, "x_out is NULL");
+  if (!aligned16(x_out)) return fail(ESM_ERR_UNSUPPORTED, "x_out not 16-byte aligned");
+  if (ids) {
+    if (!emb) return fail(ESM_ERR_NULL, "token_ids given without an embedding table");
+    if (!aligned16(emb)) return fail(ESM_ERR_UNSUPPORTED, "embedding not 16-byte aligned");
+  } else {
+    if (!x_in) return fail(ESM_ERR_NULL, "x_in is NULL (and no token ids)");
+    if (!aligned16(x_in)) return fail(ESM_ERR_UNSUPPORTED, "x_in not 16-byte aligned");
+  }
+  if (!cu_dev) return fail(ESM_ERR_NULL, "cu_seqlens_dev is NULL");
+  if (!w && nlayers > 0) return fail(ESM_ERR_NULL, "weights are NULL");
+  for (int l = 0; l < nlayers; ++l)
+    if ((s = check_weights(&w[l], layer_idx >= 0 ? layer_idx : l))) return s;
+  if ((s = check_cu_host(e, cu_host, B, T, max_seqlen))) return s;
+  if (T == 0 || B == 0) return ok();
+  Plan p;
+  if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  if ((s = run_segments(e, 0, cu_dev, B, T, 0, ws, p, st))) return s;
+  const bf16_t* cur = (const bf16_t*)x_in;
+  if (ids) {
+    s = timed(e, ESM_K_EMBED, st, "embedding", [&] {
+      return launch_embed(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, T, e->cfg.hidden_size, st);
+    });
+    if (s) return s;
+    cur = (const bf16_t*)x_out;
+  }
+  for (int l = 0; l < nlayers; ++l) {
+    if ((s = run_layer(e, &w[l], cur, (bf16_t*)x_out, T, B, false, ws, p, st))) return s;
+    cur = (const bf16_t*)x_out;
+  }
+  return ok();
+}
+
+esm_status forward_bshd(esm_encoder* e, const esm_layer_weights* w, int nlayers, int32_t layer_idx,
+                        const int32_t* ids, const void* emb, const void* x_in, void* x_out, const int32_t* sl_dev,
+                        const int32_t* sl_host, int32_t B, int32_t S, void* ws, size_t ws_bytes, esm_stream_t stream) {
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  if (B < 0 || S < 0) return fail(ESM_ERR_SHAPE, "negative B (%d) or S (%d)", B, S);
+  const int64_t rows = (int64_t)B * S;
+  esm_status s = check_rows(e, rows, B);
+  if (s) return s;
+  if (rows == 0) return ok();
+  if (S > e->cfg.max_position_embeddings)
+    return fail(ESM_ERR_SEQLENS, "S = %d above max_position_embeddings %d", S, e->cfg.max_position_embeddings);
+  if (!x_out) return fail(ESM_ERR_NULL, "x_out is NULL");
+  if (!aligned16(x_out)) return fail(ESM_ERR_UNSUPPORTED, "x_out not 16-byte aligned");
+  if (ids) {
+    if (!emb) return fail(ESM_ERR_NULL, "token_ids given without an embedding table");
+    if (!aligned16(emb)) return fail(ESM_ERR_UNSUPPORTED, "embedding not 16-byte aligned");
+  } else {
+    if (!x_in) return fail(ESM_ERR_NULL, "x_in is NULL (and no token ids)");
+    if (!aligned16(x_in)) return fail(ESM_ERR_UNSUPPORTED, "x_in not 16-byte aligned");
+  }
+  if (!sl_dev) return fail(ESM_ERR_NULL, "seqlens_dev is NULL");
+  if (!w && nlayers > 0) return fail(ESM_ERR_NULL, "weights are NULL");
+  for (int l = 0; l < nlayers; ++l)
+    if ((s = check_weights(&w[l], layer_idx >= 0 ? layer_idx : l))) return s;
+  if (sl_host && (s = esm_check_seqlens(sl_host, B, S, e->cfg.max_position_embeddings))) return s;
+  if (rows == 0) return ok();
+  Plan p;
+  if ((s = check_ws(e, ws, ws_bytes, rows, B, &p))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  if ((s = run_segments(e, 1, sl_dev, B, rows, S, ws, p, st))) return s;
+  const bf16_t* cur = (const bf16_t*)x_in;
+  if (ids) {
+    s = timed(e, ESM_K_EMBED, st, "embedding", [&] {
+      return launch_embed(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, rows, e->cfg.hidden_size, st);
+    });
+    if (s) return s;
+    cur = (const bf16_t*)x_out;
+  }
+  for (int l = 0; l < nlayers; ++l) {
+    if ((s = run_layer(e, &w[l], cur, (bf16_t*)x_out, rows, B, true, ws, p, st))) return s;
+    cur = (const bf16_t*)x_out;
+  }
+  return ok();
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+void esm_config_default(esm_config* c) {
+  if (!c) return;
+  c->hidden_size = 1280;
+  c->num_attention_heads = 20;
+  c->intermediate_size = 5120;
+  c->num_hidden_layers = 33;
+  c->vocab_size = 33;
+  c->max_position_embeddings = 1026;
+  c->layer_norm_eps = 1e-5f;
+  c->rope_base = 10000.f;
+  c->precision = ESM_PRECISION_BF16;
+  c->amax_history_len = 16;
+}
+
+esm_status esm_encoder_create(const esm_config* cfg, int device, esm_encoder** out) {
+  g_last_error.clear();
+  if (!out) return fail(ESM_ERR_NULL, "out is NULL");
+  *out = nullptr;
+  esm_status s = check_config(cfg);
+  if (s) return s;
+  int n = 0;
+  HIP_TRY(hipGetDeviceCount(&n), "hipGetDeviceCount");
+  if (device < 0 || device >= n) return fail(ESM_ERR_ARCH, "device %d not present (%d devices)", device, n);
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, device), "hipGetDeviceProperties");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(ESM_ERR_ARCH, "device %d is %s; this library is built for gfx950 only", device, prop.gcnArchName);
+  HIP_TRY(hipSetDevice(device), "hipSetDevice");
+  esm_encoder* e = new esm_encoder();
+  e->cfg = *cfg;
+  e->device = device;
+  // Rotary table: theta = p * base^(-i/32), i < 32, in fp64 then rounded
+  // ([TE-ESM2] 旋转位置编码集成).
+  const int P = cfg->max_position_embeddings;
+  std::vector<float2> tab((size_t)P * 32);
+  for (int p = 0; p < P; ++p)
+    for (int i = 0; i < 32; ++i) {
+      const double th = (double)p * pow((double)cfg->rope_base, -(double)i / 32.0);
+      tab[(size_t)p * 32 + i] = make_float2((float)cos(th), (float)sin(th));
+    }
+  hipError_t err = hipMalloc((void**)&e->rope, tab.size() * sizeof(float2));
+  if (err == hipSuccess) err = hipMemcpy(e->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice);
+  if (err != hipSuccess) {
+    if (e->rope) (void)hipFree(e->rope);
+    delete e;
+    return hip_fail(err, "rotary table");
+  }
+  *out = e;
+  return ok();
+}
+
+esm_status esm_encoder_destroy(esm_encoder* e) {
+  if (!e) return ESM_OK;
+  (void)hipSetDevice(e->device);
+  if (e->rope) (void)hipFree(e->rope);
+  for (hipEvent_t ev : e->pool) (void)hipEventDestroy(ev);
+  delete e;
+  return ESM_OK;
+}
+
+esm_status esm_workspace_size(const esm_encoder* e, int64_t max_tokens, int32_t max_seqs, size_t* bytes) {
+  if (!e || !bytes) return fail(ESM_ERR_NULL, "encoder or bytes is NULL");
+  if (max_tokens < 0 || max_seqs < 0) return fail(ESM_ERR_SHAPE, "negative sizes");
+  *bytes = make_plan(e->cfg, max_tokens, max_seqs).total;
+  return ok();
+}
+
+esm_status esm_workspace_region(const esm_encoder* e, int64_t max_tokens, int32_t max_seqs, int32_t r,
+                                size_t* offset, size_t* bytes) {
+  if (!e || !offset || !bytes) return fail(ESM_ERR_NULL, "NULL argument");
+  if (r < 0 || r > ESM_WS_SEGS) return fail(ESM_ERR_UNSUPPORTED, "unknown region %d", r);
+  const Plan p = make_plan(e->cfg, max_tokens, max_seqs);
+  *offset = p.off[r];
+  *bytes = p.size[r];
+  return ok();
+}
+
+esm_status esm_layer_fwd(esm_encoder* e, const esm_layer_weights* w, int32_t layer_idx, const void* x_in, void* x_out,
+                         const int32_t* cu_dev, const int32_t* cu_host, int32_t B, int64_t T, int32_t max_seqlen,
+                         void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  return forward_thd(e, w, 1, layer_idx, nullptr, nullptr, x_in, x_out, cu_dev, cu_host, B, T, max_seqlen, ws,
+                     ws_bytes, stream);
+}
+
+esm_status esm_stack_fwd(esm_encoder* e, const esm_layer_weights* w, const int32_t* ids, const void* emb,
+                         const void* x_in, void* x_out, const int32_t* cu_dev, const int32_t* cu_host, int32_t B,
+                         int64_t T, int32_t max_seqlen, void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  return forward_thd(e, w, e->cfg.num_hidden_layers, -1, ids, emb, x_in, x_out, cu_dev, cu_host, B, T, max_seqlen,
+                     ws, ws_bytes, stream);
+}
+
+esm_status esm_layer_fwd_bshd(esm_encoder* e, const esm_layer_weights* w, int32_t layer_idx, const void* x_in,
+                              void* x_out, const int32_t* sl_dev, const int32_t* sl_host, int32_t B, int32_t S,
+                              void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  return forward_bshd(e, w, 1, layer_idx, nullptr, nullptr, x_in, x_out, sl_dev, sl_host, B, S, ws, ws_bytes, stream);
+}
+
+esm_status esm_stack_fwd_bshd(esm_encoder* e, const esm_layer_weights* w, const int32_t* ids, const void* emb,
+                              const void* x_in, void* x_out, const int32_t* sl_dev, const int32_t* sl_host, int32_t B,
+                              int32_t S, void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  return forward_bshd(e, w, e->cfg.num_hidden_layers, -1, ids, emb, x_in, x_out, sl_dev, sl_host, B, S, ws, ws_bytes,
+                      stream);
+}
+
+esm_status esm_segment_table(esm_encoder* e, int32_t layout, const int32_t* lens_dev, int32_t B, int64_t T, int32_t S,
+                             void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !lens_dev) return fail(ESM_ERR_NULL, "encoder or lengths NULL");
+  if (layout != ESM_LAYOUT_THD && layout != ESM_LAYOUT_BSHD) return fail(ESM_ERR_UNSUPPORTED, "layout %d", layout);
+  if (layout == ESM_LAYOUT_BSHD) {
+    if (S < 0 || B < 0) return fail(ESM_ERR_SHAPE, "negative B or S");
+    T = (int64_t)B * S;
+  }
+  esm_status s = check_rows(e, T, B);
+  if (s) return s;
+  if (T == 0 && B == 0) return ok();
+  Plan p;
+  if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  return run_segments(e, layout, lens_dev, B, T, S, ws, p, (hipStream_t)stream);
+}
+
+esm_status esm_attention_fwd(esm_encoder* e, const void* qkv, void* ctx, const int32_t* cu_dev, int32_t B, int64_t T,
+                             void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !qkv || !ctx || !cu_dev) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!aligned16(qkv) || !aligned16(ctx)) return fail(ESM_ERR_UNSUPPORTED, "qkv/ctx not 16-byte aligned");
+  esm_status s = check_rows(e, T, B);
+  if (s) return s;
+  if (T == 0 || B == 0) return ok();
+  Plan p;
+  if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  if ((s = run_segments(e, 0, cu_dev, B, T, 0, ws, p, st))) return s;
+  AttnArgs aa{};
+  aa.qkv = (const bf16_t*)qkv; aa.ctx = (bf16_t*)ctx;
+  aa.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
+  aa.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
+  aa.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
+  aa.tile_cap = tile_cap(T, B);
+  aa.T = T; aa.heads = e->cfg.num_attention_heads;
+  return timed(e, ESM_K_ATTENTION, st, "attention", [&] { return launch_attention(aa, st); });
+}
+
+esm_status esm_linear_fwd(esm_encoder* e, const void* x, const void* w, const void* b, const void* res, void* y,
+                          int64_t M, int32_t N, int32_t K, int32_t epi, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !x || !w || !y) return fail(ESM_ERR_NULL, "NULL argument");
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64)
+    return fail(ESM_ERR_SHAPE, "M %lld N %d K %d: N and K must be positive multiples of 64", (long long)M, N, K);
+  if (epi < ESM_EPI_BIAS || epi > ESM_EPI_BIAS_RESIDUAL) return fail(ESM_ERR_UNSUPPORTED, "epilogue %d", epi);
+  if (epi == ESM_EPI_BIAS_RESIDUAL && !res) return fail(ESM_ERR_NULL, "residual is NULL");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (res && !aligned16(res)) || (b && ((uintptr_t)b & 7u)))
+    return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer");
+  if (M == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  GemmArgs g{};
+  g.x = (const bf16_t*)x; g.w = (const bf16_t*)w; g.bias = (const bf16_t*)b; g.res = (const bf16_t*)res;
+  g.y = (bf16_t*)y; g.M = M; g.N = N; g.K = K;
+  const int kind = epi == ESM_EPI_BIAS ? EPI_BIAS : (epi == ESM_EPI_BIAS_GELU ? EPI_BIAS_GELU : EPI_BIAS_RESIDUAL);
+  return timed(e, ESM_K_OTHER, (hipStream_t)stream, "linear", [&] { return launch_gemm(kind, g, (hipStream_t)stream); });
+}
+
+esm_status esm_layernorm_fwd(esm_encoder* e, const void* x, const void* gamma, const void* beta, void* y, int64_t M,
+                             esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !x || !gamma || !beta || !y) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(beta) || !aligned16(y))
+    return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer");
+  if (M < 0) return fail(ESM_ERR_SHAPE, "M < 0");
+  if (M == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  return timed(e, ESM_K_LAYERNORM, (hipStream_t)stream, "layernorm", [&] {
+    return launch_layernorm((const bf16_t*)x, (const bf16_t*)gamma, (const bf16_t*)beta, (bf16_t*)y, M,
+                            e->cfg.hidden_size, e->cfg.layer_norm_eps, (hipStream_t)stream);
+  });
+}
+
+esm_status esm_profile_enable(esm_encoder* e, int32_t on) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  e->profiling = on != 0;
+  e->recs.clear();
+  e->pool_used = 0;
+  for (int i = 0; i < ESM_K_COUNT; ++i) {
+    e->ms[i] = 0;
+    e->launches[i] = 0;
+  }
+  return ok();
+}
+
+esm_status esm_profile_read(esm_encoder* e, double* ms_out, int64_t* launches_out) {
+  g_last_error.clear();
+  if (!e || !ms_out || !launches_out) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!e->recs.empty()) {
+    HIP_TRY(hipEventSynchronize(e->pool[e->recs.back().second + 1]), "hipEventSynchronize");
+    for (auto& r : e->recs) {
+      float ms = 0.f;
+      HIP_TRY(hipEventElapsedTime(&ms, e->pool[r.second], e->pool[r.second + 1]), "hipEventElapsedTime");
+      e->ms[r.first] += ms;
+      e->launches[r.first] += 1;
+    }
+    e->recs.clear();
+    e->pool_used = 0;
+  }
+  for (int i = 0; i < ESM_K_COUNT; ++i) {
+    ms_out[i] = e->ms[i];
+    launches_out[i] = e->launches[i];
+  }
+  return ok();
+}
+
+esm_status esm_check_cu_seqlens(const int32_t* cu, int32_t B, int64_t T, int32_t max_seqlen, int32_t max_positions) {
+  if (!cu) return fail(ESM_ERR_NULL, "cu_seqlens is NULL");
+  if (B < 0 || T < 0) return fail(ESM_ERR_SHAPE, "negative B or T");
+  if (max_seqlen < 0 || max_seqlen > max_positions)
+    return fail(ESM_ERR_SEQLENS, "max_seqlen %d outside [0, %d]", max_seqlen, max_positions);
+  if (cu[0] != 0) return fail(ESM_ERR_SEQLENS, "cu_seqlens[0] = %d, expected 0", cu[0]);
+  for (int32_t s = 0; s < B; ++s) {
+    const int64_t L = (int64_t)cu[s + 1] - cu[s];
+    if (L < 0) return fail(ESM_ERR_SEQLENS, "cu_seqlens decreases at %d (%d -> %d)", s, cu[s], cu[s + 1]);
+    if (L > max_seqlen) return fail(ESM_ERR_SEQLENS, "sequence %d has length %lld > max_seqlen %d", s, (long long)L, max_seqlen);
+  }
+  if ((int64_t)cu[B] != T) return fail(ESM_ERR_SEQLENS, "cu_seqlens[B] = %d, expected T = %lld", cu[B], (long long)T);
+  return ESM_OK;
+}
+
+esm_status esm_check_seqlens(const int32_t* sl, int32_t B, int32_t S, int32_t max_positions) {
+  if (!sl) return fail(ESM_ERR_NULL, "seqlens is NULL");
+  if (B < 0 || S < 0) return fail(ESM_ERR_SHAPE, "negative B or S");
+  if (S > max_positions) return fail(ESM_ERR_SEQLENS, "S = %d above max positions %d", S, max_positions);
+  for (int32_t b = 0; b < B; ++b)
+    if (sl[b] < 0 || sl[b] > S) return fail(ESM_ERR_SEQLENS, "seqlens[%d] = %d outside [0, S = %d]", b, sl[b], S);
+  return ESM_OK;
+}
+
+const char* esm_last_error(void) { return g_last_error.c_str(); }
+
+const char* esm_status_str(esm_status s) {
+  switch (s) {
+    case ESM_OK: return "ESM_OK";
+    case ESM_ERR_NULL: return "ESM_ERR_NULL";
+    case ESM_ERR_SHAPE: return "ESM_ERR_SHAPE";
+    case ESM_ERR_SEQLENS: return "ESM_ERR_SEQLENS";
+    case ESM_ERR_UNSUPPORTED: return "ESM_ERR_UNSUPPORTED";
+    case ESM_ERR_WORKSPACE: return "ESM_ERR_WORKSPACE";
+    case ESM_ERR_ARCH: return "ESM_ERR_ARCH";
+    case ESM_ERR_HIP: return "ESM_ERR_HIP";
+    case ESM_ERR_STATE: return "ESM_ERR_STATE";
+  }
+  return "unknown status";
+}
+
+int32_t esm_abi_version(void) { return ESM_ABI_VERSION; }
+
+}  // extern "C"

@@ -23,6 +23,12 @@ Recipe (seed s, stream k):  numpy Generator over SeedSequence([s, k]).
   stream 1000+l weights of layer l in the order W_qkv, b_qkv, W_o, b_o, W_1,
                 b_1, W_2, b_2, each N(0, 0.02); LayerNorm gamma = 1, beta = 0
 All float draws are float64 -> float32 -> bfloat16 (round to nearest even).
+
+Deep stacks (33 or 36 layers, 0.65 or 2.8 billion weights) use a second,
+faster weight recipe that draws on the device with torch's generator:
+  layer l: torch.Generator(device).manual_seed(seed * 1_000_003 + 1000 + l),
+  then randn(float32) * 0.02 -> bfloat16 (round to nearest even), in the same
+  tensor order as above.  Weights for the oracle are copied back to the host.
 """
 from __future__ import annotations
 
@@ -206,6 +212,38 @@ def make_layer_weights(H: int, F: int, layer: int, seed: int = 0) -> Dict[str, n
     out["ln1_gamma"], out["ln1_beta"] = one.copy(), zero.copy()
     out["ln2_gamma"], out["ln2_beta"] = one.copy(), zero.copy()
     return out
+
+
+def make_layer_weights_device(H: int, F: int, layer: int, seed: int = 0, device: str = "cuda:0"):
+    """Same tensors as make_layer_weights, drawn on the device (torch generator).
+
+    Returns torch bfloat16 tensors; gamma = 1 and beta = 0."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 1_000_003 + 1000 + layer)
+
+    def draw(shape):
+        return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+
+    out = {}
+    out["w_qkv"] = draw((3 * H, H))
+    out["b_qkv"] = draw((3 * H,))
+    out["w_out"] = draw((H, H))
+    out["b_out"] = draw((H,))
+    out["w_fc1"] = draw((F, H))
+    out["b_fc1"] = draw((F,))
+    out["w_fc2"] = draw((H, F))
+    out["b_fc2"] = draw((H,))
+    out["ln1_gamma"] = torch.ones(H, dtype=torch.bfloat16, device=device)
+    out["ln1_beta"] = torch.zeros(H, dtype=torch.bfloat16, device=device)
+    out["ln2_gamma"] = torch.ones(H, dtype=torch.bfloat16, device=device)
+    out["ln2_beta"] = torch.zeros(H, dtype=torch.bfloat16, device=device)
+    return out
+
+
+def tensor_bits(t) -> np.ndarray:
+    """torch bfloat16 tensor (any device) -> uint16 bit patterns on the host."""
+    return t.detach().contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16)
 
 
 def random_layernorm_params(H: int, seed: int, stream: int = 5) -> Dict[str, np.ndarray]:

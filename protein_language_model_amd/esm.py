@@ -1,0 +1,322 @@
+"""Python binding of the C ABI in include/esm_encoder.h (ctypes).
+
+Argument marshalling only: torch tensors become device pointers and the
+current torch stream becomes the hipStream_t.  Every step of the forward runs
+in the library's HIP kernels; there is no other code path.  If libesmenc.so is
+missing, loading raises instead of falling back to anything else."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Iterable, List, Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libesmenc.so")
+
+ESM_OK = 0
+STATUS_NAMES = {0: "ESM_OK", 1: "ESM_ERR_NULL", 2: "ESM_ERR_SHAPE", 3: "ESM_ERR_SEQLENS", 4: "ESM_ERR_UNSUPPORTED",
+                5: "ESM_ERR_WORKSPACE", 6: "ESM_ERR_ARCH", 7: "ESM_ERR_HIP", 8: "ESM_ERR_STATE"}
+PRECISION = {"bf16": 0, "fp8": 1}
+LAYOUT_THD, LAYOUT_BSHD = 0, 1
+EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL = 0, 1, 2
+WS_REGIONS = {"ln1": 0, "qkv": 1, "ctx": 2, "x1": 3, "ln2": 4, "act": 5, "pos": 6, "tiles": 7, "ntiles": 8, "segs": 9}
+KERNEL_CLASSES = ("segment", "embed", "layernorm", "gemm_qkv", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
+                  "other")
+LAYER_WEIGHT_NAMES = ("ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_out", "b_out",
+                      "ln2_gamma", "ln2_beta", "w_fc1", "b_fc1", "w_fc2", "b_fc2")
+
+# Every function the header declares, with its ctypes signature.
+_i32, _i64, _p, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+
+
+class EsmConfig(ctypes.Structure):
+    _fields_ = [
+        ("hidden_size", ctypes.c_int32), ("num_attention_heads", ctypes.c_int32),
+        ("intermediate_size", ctypes.c_int32), ("num_hidden_layers", ctypes.c_int32),
+        ("vocab_size", ctypes.c_int32), ("max_position_embeddings", ctypes.c_int32),
+        ("layer_norm_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
+        ("precision", ctypes.c_int32), ("amax_history_len", ctypes.c_int32),
+    ]
+
+
+class EsmLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHT_NAMES]
+
+
+SIGNATURES = {
+    "esm_config_default": (None, [ctypes.POINTER(EsmConfig)]),
+    "esm_encoder_create": (_i32, [ctypes.POINTER(EsmConfig), ctypes.c_int, ctypes.POINTER(_p)]),
+    "esm_encoder_destroy": (_i32, [_p]),
+    "esm_workspace_size": (_i32, [_p, _i64, _i32, ctypes.POINTER(_sz)]),
+    "esm_workspace_region": (_i32, [_p, _i64, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "esm_layer_fwd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _i32, _p, _p, _p, _p, _i32, _i64, _i32, _p, _sz,
+                             _p]),
+    "esm_stack_fwd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _p, _p, _p, _p, _p, _p, _i32, _i64, _i32, _p, _sz,
+                             _p]),
+    "esm_layer_fwd_bshd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _i32, _p, _p, _p, _p, _i32, _i32, _p, _sz,
+                                  _p]),
+    "esm_stack_fwd_bshd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _p, _p, _p, _p, _p, _p, _i32, _i32, _p, _sz,
+                                  _p]),
+    "esm_segment_table": (_i32, [_p, _i32, _p, _i32, _i64, _i32, _p, _sz, _p]),
+    "esm_attention_fwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
+    "esm_linear_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
+    "esm_layernorm_fwd": (_i32, [_p, _p, _p, _p, _p, _i64, _p]),
+    "esm_profile_enable": (_i32, [_p, _i32]),
+    "esm_profile_read": (_i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
+    "esm_check_cu_seqlens": (_i32, [_p, _i32, _i64, _i32, _i32]),
+    "esm_check_seqlens": (_i32, [_p, _i32, _i32, _i32]),
+    "esm_last_error": (ctypes.c_char_p, []),
+    "esm_status_str": (ctypes.c_char_p, [_i32]),
+    "esm_abi_version": (_i32, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class EsmError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+        self.fn = fn
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m protein_language_model_amd.build` "
+                          "(the encoder has no other implementation)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _call(name: str, *args) -> None:
+    lib = load_library()
+    st = getattr(lib, name)(*args)
+    if st != ESM_OK:
+        raise EsmError(name, st, lib.esm_last_error().decode())
+
+
+def check_cu_seqlens(cu, T: int, max_seqlen: int, max_positions: int = 1026) -> None:
+    """Host-only validation of a cu_seqlens array (raises EsmError)."""
+    a = np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
+    _call("esm_check_cu_seqlens", a.ctypes.data_as(ctypes.c_void_p), int(a.size - 1), int(T), int(max_seqlen),
+          int(max_positions))
+
+
+def check_seqlens(seqlens, S: int, max_positions: int = 1026) -> None:
+    a = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int32))
+    _call("esm_check_seqlens", a.ctypes.data_as(ctypes.c_void_p), int(a.size), int(S), int(max_positions))
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _host_i32(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    import torch
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def layer_weights_struct(w: Dict[str, "object"]) -> EsmLayerWeights:
+    s = EsmLayerWeights()
+    for n in LAYER_WEIGHT_NAMES:
+        t = w.get(n)
+        setattr(s, n, _ptr(t) if t is not None else None)
+    return s
+
+
+class Encoder:
+    """Handle of the C library (esm_encoder_create / esm_encoder_destroy)."""
+
+    def __init__(self, hidden_size: int = 1280, num_attention_heads: int = 20, intermediate_size: int = 5120,
+                 num_hidden_layers: int = 33, vocab_size: int = 33, max_position_embeddings: int = 1026,
+                 layer_norm_eps: float = 1e-5, rope_base: float = 10000.0, precision: str = "bf16",
+                 amax_history_len: int = 16, device: int = 0):
+        lib = load_library()
+        cfg = EsmConfig()
+        lib.esm_config_default(ctypes.byref(cfg))
+        cfg.hidden_size, cfg.num_attention_heads = hidden_size, num_attention_heads
+        cfg.intermediate_size, cfg.num_hidden_layers = intermediate_size, num_hidden_layers
+        cfg.vocab_size, cfg.max_position_embeddings = vocab_size, max_position_embeddings
+        cfg.layer_norm_eps, cfg.rope_base = layer_norm_eps, rope_base
+        cfg.precision, cfg.amax_history_len = PRECISION[precision], amax_history_len
+        self.cfg = cfg
+        self.device = device
+        h = ctypes.c_void_p()
+        _call("esm_encoder_create", ctypes.byref(cfg), device, ctypes.byref(h))
+        self._h = h
+
+    # -- lifetime
+    def close(self) -> None:
+        if getattr(self, "_h", None) and self._h.value:
+            load_library().esm_encoder_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def hidden(self) -> int:
+        return self.cfg.hidden_size
+
+    # -- workspace
+    def workspace_size(self, max_tokens: int, max_seqs: int) -> int:
+        n = ctypes.c_size_t()
+        _call("esm_workspace_size", self._h, int(max_tokens), int(max_seqs), ctypes.byref(n))
+        return n.value
+
+    def workspace(self, max_tokens: int, max_seqs: int):
+        import torch
+        n = self.workspace_size(max_tokens, max_seqs)
+        ws = torch.empty(max(n, 256), dtype=torch.uint8, device=f"cuda:{self.device}")
+        assert ws.data_ptr() % 256 == 0
+        return ws
+
+    def workspace_region(self, ws, max_tokens: int, max_seqs: int, name: str):
+        """A view of one named region of a workspace used by a call with (T, B)."""
+        import torch
+        off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+        _call("esm_workspace_region", self._h, int(max_tokens), int(max_seqs), WS_REGIONS[name], ctypes.byref(off),
+              ctypes.byref(nb))
+        raw = ws[off.value: off.value + nb.value]
+        if name in ("pos", "tiles", "ntiles", "segs"):
+            return raw.view(torch.int32)
+        return raw.view(torch.bfloat16)
+
+    # -- forward
+    def layer_fwd(self, weights, x_in, cu_seqlens, B: int, T: int, max_seqlen: int, *, x_out=None,
+                  layer_idx: int = 0, cu_seqlens_host=None, workspace=None, stream=None):
+        import torch
+        if x_out is None:
+            x_out = torch.empty_like(x_in)
+        if workspace is None:
+            workspace = self.workspace(T, B)
+        w = layer_weights_struct(weights)
+        cuh = _host_i32(cu_seqlens_host)
+        _call("esm_layer_fwd", self._h, ctypes.byref(w), int(layer_idx), _ptr(x_in), _ptr(x_out), _ptr(cu_seqlens),
+              cuh.ctypes.data_as(ctypes.c_void_p) if cuh is not None else None, int(B), int(T), int(max_seqlen),
+              _ptr(workspace), workspace.numel(), _stream(stream))
+        return x_out
+
+    def stack_fwd(self, weights: Sequence[Dict], cu_seqlens, B: int, T: int, max_seqlen: int, *, token_ids=None,
+                  embedding=None, x_in=None, x_out=None, cu_seqlens_host=None, workspace=None, stream=None):
+        import torch
+        if len(weights) != self.cfg.num_hidden_layers:
+            raise ValueError(f"{len(weights)} layer weight sets for {self.cfg.num_hidden_layers} layers")
+        if x_out is None:
+            x_out = torch.empty((T, self.hidden), dtype=torch.bfloat16, device=f"cuda:{self.device}")
+        if workspace is None:
+            workspace = self.workspace(T, B)
+        arr = (EsmLayerWeights * max(len(weights), 1))(*[layer_weights_struct(w) for w in weights])
+        cuh = _host_i32(cu_seqlens_host)
+        _call("esm_stack_fwd", self._h, arr, _ptr(token_ids), _ptr(embedding), _ptr(x_in), _ptr(x_out),
+              _ptr(cu_seqlens), cuh.ctypes.data_as(ctypes.c_void_p) if cuh is not None else None, int(B), int(T),
+              int(max_seqlen), _ptr(workspace), workspace.numel(), _stream(stream))
+        return x_out
+
+    def layer_fwd_bshd(self, weights, x_in, seqlens, B: int, S: int, *, x_out=None, layer_idx: int = 0,
+                       seqlens_host=None, workspace=None, stream=None):
+        import torch
+        if x_out is None:
+            x_out = torch.empty_like(x_in)
+        if workspace is None:
+            workspace = self.workspace(B * S, B)
+        w = layer_weights_struct(weights)
+        slh = _host_i32(seqlens_host)
+        _call("esm_layer_fwd_bshd", self._h, ctypes.byref(w), int(layer_idx), _ptr(x_in), _ptr(x_out), _ptr(seqlens),
+              slh.ctypes.data_as(ctypes.c_void_p) if slh is not None else None, int(B), int(S), _ptr(workspace),
+              workspace.numel(), _stream(stream))
+        return x_out
+
+    def stack_fwd_bshd(self, weights: Sequence[Dict], seqlens, B: int, S: int, *, token_ids=None, embedding=None,
+                       x_in=None, x_out=None, seqlens_host=None, workspace=None, stream=None):
+        import torch
+        if len(weights) != self.cfg.num_hidden_layers:
+            raise ValueError(f"{len(weights)} layer weight sets for {self.cfg.num_hidden_layers} layers")
+        if x_out is None:
+            x_out = torch.empty((B, S, self.hidden), dtype=torch.bfloat16, device=f"cuda:{self.device}")
+        if workspace is None:
+            workspace = self.workspace(B * S, B)
+        arr = (EsmLayerWeights * max(len(weights), 1))(*[layer_weights_struct(w) for w in weights])
+        slh = _host_i32(seqlens_host)
+        _call("esm_stack_fwd_bshd", self._h, arr, _ptr(token_ids), _ptr(embedding), _ptr(x_in), _ptr(x_out),
+              _ptr(seqlens), slh.ctypes.data_as(ctypes.c_void_p) if slh is not None else None, int(B), int(S),
+              _ptr(workspace), workspace.numel(), _stream(stream))
+        return x_out
+
+    # -- kernel-level entries
+    def segment_table(self, layout: int, lens, B: int, T: int, S: int = 0, *, workspace=None, stream=None):
+        if workspace is None:
+            workspace = self.workspace(T if layout == LAYOUT_THD else B * S, B)
+        _call("esm_segment_table", self._h, int(layout), _ptr(lens), int(B), int(T), int(S), _ptr(workspace),
+              workspace.numel(), _stream(stream))
+        return workspace
+
+    def attention_fwd(self, qkv, cu_seqlens, B: int, T: int, *, ctx=None, workspace=None, stream=None):
+        import torch
+        if ctx is None:
+            ctx = torch.empty((T, self.hidden), dtype=torch.bfloat16, device=qkv.device)
+        if workspace is None:
+            workspace = self.workspace(T, B)
+        _call("esm_attention_fwd", self._h, _ptr(qkv), _ptr(ctx), _ptr(cu_seqlens), int(B), int(T), _ptr(workspace),
+              workspace.numel(), _stream(stream))
+        return ctx
+
+    def linear_fwd(self, x, w, b=None, *, residual=None, epilogue: int = EPI_BIAS, y=None, stream=None):
+        import torch
+        M, K = x.shape
+        N = w.shape[0]
+        if y is None:
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+        _call("esm_linear_fwd", self._h, _ptr(x), _ptr(w), _ptr(b), _ptr(residual), _ptr(y), int(M), int(N), int(K),
+              int(epilogue), _stream(stream))
+        return y
+
+    def layernorm_fwd(self, x, gamma, beta, *, y=None, stream=None):
+        import torch
+        if y is None:
+            y = torch.empty_like(x)
+        _call("esm_layernorm_fwd", self._h, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), int(x.shape[0]),
+              _stream(stream))
+        return y
+
+    # -- timing
+    def profile_enable(self, on: bool = True) -> None:
+        _call("esm_profile_enable", self._h, 1 if on else 0)
+
+    def profile_read(self) -> Dict[str, tuple]:
+        n = len(KERNEL_CLASSES)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        _call("esm_profile_read", self._h, ms, cnt)
+        return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_CLASSES)}
