@@ -16,9 +16,14 @@
 //    lane and register of two adjacent blocks, which is what the rotary
 //    epilogue needs ([TE-ESM2] 旋转位置编码集成: rotate-half pairs (i, i+32)).
 //  * K step 64; tiles live in LDS twice (double buffer) with a 16-byte-chunk XOR
-//    swizzle (chunk c of row r stored at c ^ (r & 7)); the next K step is
-//    fetched from global memory into registers while the current one is
-//    multiplied, so one barrier per K step suffices.
+//    swizzle (chunk c of row r stored at c ^ ((r >> 1) & 7)): the 16 lanes that
+//    one LDS cycle serves read 16 rows of one column and hit 16 distinct
+//    16-byte bank groups of the 64-bank LDS.  The next K step is
+//    fetched straight into the other LDS buffer (global_load_lds, no staging
+//    registers) while the current one is multiplied.  MFMA fragments are
+//    double-buffered in registers across the four 16-wide k sub-steps, and the
+//    single barrier per K step sits before the last sub-step, so the next
+//    tile's first fragments load under MFMAs.
 //  * Rows beyond M and weight rows beyond N are clamped on load (never read out
 //    of bounds) and skipped on store.
 //  * Workgroup ids are remapped so consecutive tiles land on one XCD (ids are
@@ -34,10 +39,38 @@ constexpr int kBK = 64;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
+// Direct-to-LDS 16-byte load: lane i's 16 bytes from g land at LDS byte
+// lds_base + 16 i (lds_base must be wave-uniform; it goes through M0).  Issued
+// as inline assembly so the compiler keeps exact LDS wait counts for the
+// fragment reads; the caller waits with vm_wait_all() before the barrier that
+// publishes the tile.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// GELU(z) = z * Phi(z) = z/2 * (1 + erf(z / sqrt 2)).  The pages name a
+// fused activation only; the erf form is the definition used here.  erf comes
+// from Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: erf(x) = 1 - (a1 t + ... + a5 t^5) exp(-x^2), t = 1 / (1 + p x),
+// x >= 0, |error| <= 1.5e-7 (odd extension for x < 0).
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+  return copysignf(fmaf(-poly, e, 1.0f), x);
+}
 __device__ __forceinline__ float gelu_erf(float z) {
-  // Exact GELU z * Phi(z) ([BIO-ACC] 2.1 names the fused activation; the erf
-  // form is the definition of GELU).
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+  return 0.5f * z * (1.0f + erf_as7126(z * 0.70710678118654752f));
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
@@ -46,12 +79,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
   constexpr int WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32;
   constexpr int FN = WTN / 32;
-  constexpr int XCH = BM * 8 / 256;  // 16-byte chunks of x per thread per K step
-  constexpr int WCH = BN * 8 / 256;
+  constexpr int XRB = BM / 32;  // 8-row blocks of the x tile per wave
+  constexpr int WRB = BN / 32;
+  constexpr int kStage = (BM + BN) * kBK;
   static_assert(WAVES_M * WAVES_N == 4, "4 waves");
   static_assert(EPI != EPI_QKV_ROPE || (FN % 2 == 0 && WTN % 64 == 0), "rotary pairs need 64-wide wave columns");
 
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2][(BM + BN) * kBK];
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * kStage];
 
   const int64_t M = a.M;
   const int N = a.N, K = a.K;
@@ -76,39 +110,51 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int lrow = lane & 31, lhalf = lane >> 5;
 
-  const bf16_t* __restrict__ X = a.x;
-  const bf16_t* __restrict__ W = a.w;
-
-  u32x4 xr[XCH], wr[WCH];
-  const int crow = tid >> 3, cchk = tid & 7;
-  auto gload = [&](int k0) {
+  // Direct-to-LDS tile loads.  One global_load_lds_dwordx4 fills 1 KB of LDS
+  // (8 rows of 64 bf16), lane i writing bytes [16 i, 16 i + 16).  Lane i of a
+  // wave therefore fetches row r = 8*rb + i/8 at the logical chunk that the
+  // swizzle stores in physical chunk i%8: c = (i%8) ^ ((r >> 1) & 7), where
+  // (r >> 1) & 7 = 4*(rb & 1) + i/16 and rb & 1 = wave & 1.
+  const int lr8 = lane >> 3;
+  const int lchunk = ((lane & 7) ^ (((wave & 1) << 2) | (lane >> 4))) * 8;
+  const bf16_t* xsrc[XRB];
+  const bf16_t* wsrc[WRB];
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      int64_t r = m0 + crow + 32 * i;
-      r = r < M ? r : M - 1;
-      xr[i] = *(const u32x4*)(X + r * K + k0 + cchk * 8);
-    }
+  for (int i = 0; i < XRB; ++i) {
+    int64_t r = m0 + (int64_t)(wave + 4 * i) * 8 + lr8;
+    r = r < M ? r : M - 1;
+    xsrc[i] = a.x + r * K + lchunk;
+  }
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      int r = n0 + crow + 32 * i;
-      r = r < N ? r : N - 1;
-      wr[i] = *(const u32x4*)(W + (int64_t)r * K + k0 + cchk * 8);
-    }
+  for (int i = 0; i < WRB; ++i) {
+    int r = n0 + (wave + 4 * i) * 8 + lr8;
+    r = r < N ? r : N - 1;
+    wsrc[i] = a.w + (int64_t)r * K + lchunk;
+  }
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue_tile = [&](int k0, int buf) {
+    const uint32_t base = lds0 + (uint32_t)(buf * kStage) * 2u;
+#pragma unroll
+    for (int i = 0; i < XRB; ++i) lds_dma16(xsrc[i] + k0, base + (uint32_t)((wave_u + 4 * i) * 8 * kBK) * 2u);
+#pragma unroll
+    for (int i = 0; i < WRB; ++i) lds_dma16(wsrc[i] + k0, base + (uint32_t)((BM + (wave_u + 4 * i) * 8) * kBK) * 2u);
   };
-  auto sstore = [&](int buf) {
-    bf16_t* sx = smem[buf];
-    bf16_t* sw = smem[buf] + BM * kBK;
+
+  // Fragment reads: row r of the tile, logical 16-byte chunk ch, stored at
+  // physical chunk ch ^ ((r >> 1) & 7); every row this lane reads has
+  // (r >> 1) & 7 = (lane % 32) / 2.
+  const int swz = (lrow >> 1) & 7;
+  auto load_frags = [&](bf16x8 (&xf)[FM], bf16x8 (&wf)[FN], int buf, int kk) {
+    const bf16_t* sx = smem + buf * kStage;
+    const bf16_t* sw = sx + BM * kBK;
+    const int ch = ((kk * 2 + lhalf) ^ swz) * 8;
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      int r = crow + 32 * i;
-      *(u32x4*)(sx + r * kBK + ((cchk ^ (r & 7)) * 8)) = xr[i];
-    }
+    for (int i = 0; i < FM; ++i) xf[i] = *(const bf16x8*)(sx + (wm * WTM + i * 32 + lrow) * kBK + ch);
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      int r = crow + 32 * i;
-      *(u32x4*)(sw + r * kBK + ((cchk ^ (r & 7)) * 8)) = wr[i];
-    }
+    for (int j = 0; j < FN; ++j) wf[j] = *(const bf16x8*)(sw + (wn * WTN + j * 32 + lrow) * kBK + ch);
   };
 
   f32x16 acc[FM][FN];
@@ -119,70 +165,105 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  auto mfma_step = [&](const bf16x8 (&xf)[FM], const bf16x8 (&wf)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+  };
+
   const int nk = K / kBK;
-  gload(0);
-  sstore(0);
+  bf16x8 xa[FM], wa[FN], xb[FM], wb[FN];
+  issue_tile(0, 0);
+  vm_wait_all();
   __syncthreads();
-  const int lrow = lane & 31, lhalf = lane >> 5;
+  load_frags(xa, wa, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
-    const bf16_t* sx = smem[cur];
-    const bf16_t* sw = smem[cur] + BM * kBK;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int ch = kk * 2 + lhalf;
-      bf16x8 xf[FM], wf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        int r = wm * WTM + i * 32 + lrow;
-        xf[i] = *(const bf16x8*)(sx + r * kBK + ((ch ^ (r & 7)) * 8));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        int r = wn * WTN + j * 32 + lrow;
-        wf[j] = *(const bf16x8*)(sw + r * kBK + ((ch ^ (r & 7)) * 8));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+    const bool more = kt + 1 < nk;
+    if (more) issue_tile((kt + 1) * kBK, cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(xb, wb, cur, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(xa, wa, cur, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags(xb, wb, cur, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(xa, wa);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) {
+      // Next tile landed for every wave, and every wave is done with this
+      // tile's first three k-steps; its first fragments load under the last
+      // k-step's MFMAs.
+      vm_wait_all();
+      __syncthreads();
+      load_frags(xa, wa, cur ^ 1, 0);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(xb, wb);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ------------------------------------------------------------ epilogue
+  // Each wave stages its (WTM x WTN) bf16 result tile in LDS (free once every
+  // wave is past the K loop), so that global memory is written (and, for the
+  // residual, read) in full rows with 16-byte lanes.  Staged rows hold CPR
+  // 16-byte chunks, chunk c of row r stored at c ^ ((r / (16 / CPR)) % CPR),
+  // which spreads the row-per-lane accesses of the MFMA layout over the banks.
+  constexpr int CPR = WTN / 8;
+  constexpr int RPW = 16 / CPR;           // staged rows per 256-byte bank window
+  constexpr int PASSES = WTM * CPR / 64;  // 16-byte transfers per lane
+  __syncthreads();
+  bf16_t* stage = smem + wave * (WTM * WTN);
+  auto soff = [&](int row, int chunk) { return row * WTN + ((chunk ^ ((row / RPW) & (CPR - 1))) * 8); };
+  const int64_t mw = m0 + wm * WTM;
+  const int nw = n0 + wn * WTN;
   const bf16_t* __restrict__ bias = a.bias;
+
+  if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+#pragma unroll 4
+    for (int p = 0; p < PASSES; ++p) {
+      const int idx = p * 64 + lane, row = idx / CPR, ch = idx % CPR;
+      const int64_t m = mw + row;
+      const int n = nw + ch * 8;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (m < M && n < N) v = *(const u32x4*)(a.res + m * N + n);
+      *(u32x4*)(stage + soff(row, ch)) = v;
+    }
+    __syncthreads();
+  }
+
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int64_t m = m0 + wm * WTM + i * 32 + lrow;
-    if (m >= M) continue;
+    const int row = i * 32 + lrow;
+    const int64_t m = mw + row;
+    const int64_t mc = m < M ? m : M - 1;
     if constexpr (EPI == EPI_QKV_ROPE) {
-      int p = a.pos[m];
-      if (p < 0) continue;  // padding row of a bshd batch: never attended
-      p = p < a.max_positions ? p : a.max_positions - 1;
-      const int heads = N / 192;
+      int p = a.pos[mc];
+      p = p < 0 ? 0 : (p < a.max_positions ? p : a.max_positions - 1);
 #pragma unroll
       for (int j = 0; j < FN; j += 2) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int nlo = n0 + wn * WTN + j * 32 + 8 * gq + 4 * lhalf;
-          if (nlo >= N) continue;
-          const int head = nlo / 192, c = (nlo % 192) / 64, d = nlo % 64;  // d < 32
+          const int cl = j * 32 + 8 * gq + 4 * lhalf;  // local column of the low half
+          const int nlo = nw + cl;
+          const int c = (nlo % 192) / 64, d = nlo % 64;  // d < 32
           float lo[4], hi[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             lo[e] = acc[i][j][4 * gq + e];
             hi[e] = acc[i][j + 1][4 * gq + e];
           }
-          if (bias) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              lo[e] += bf2f(bias[nlo + e]);
-              hi[e] += bf2f(bias[nlo + 32 + e]);
-            }
+          if (bias && nlo < N) {
+            const u32x2 bl = *(const u32x2*)(bias + nlo);
+            const u32x2 bh = *(const u32x2*)(bias + nlo + 32);
+            lo[0] += bflo(bl[0]); lo[1] += bfhi(bl[0]); lo[2] += bflo(bl[1]); lo[3] += bfhi(bl[1]);
+            hi[0] += bflo(bh[0]); hi[1] += bfhi(bh[0]); hi[2] += bflo(bh[1]); hi[3] += bfhi(bh[1]);
           }
           if (c < 2) {
             const float2* cs = a.rope + (int64_t)p * 32 + d;
@@ -194,39 +275,57 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
               hi[e] = x1 * t.x + x0 * t.y;
             }
           }
-          bf16_t* dst = a.y + (((int64_t)c * heads + head) * M + m) * kHeadDim + d;
-          *(u32x2*)dst = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
-          *(u32x2*)(dst + 32) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
+          *(u32x2*)(stage + soff(row, cl / 8) + 4 * lhalf) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
+          *(u32x2*)(stage + soff(row, cl / 8 + 4) + 4 * lhalf) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
         }
       }
     } else {
       bool zero_row = false;
-      if constexpr (EPI == EPI_BIAS_RESIDUAL) zero_row = a.zero_pad_rows && a.pos[m] < 0;
+      if constexpr (EPI == EPI_BIAS_RESIDUAL) zero_row = a.zero_pad_rows && a.pos[mc] < 0;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int n = n0 + wn * WTN + j * 32 + 8 * gq + 4 * lhalf;
-          if (n >= N) continue;
+          const int cl = j * 32 + 8 * gq + 4 * lhalf;
+          const int n = nw + cl;
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e];
-          if (bias) {
+          if (bias && n < N) {
             const u32x2 bb = *(const u32x2*)(bias + n);
             v[0] += bflo(bb[0]); v[1] += bfhi(bb[0]); v[2] += bflo(bb[1]); v[3] += bfhi(bb[1]);
           }
+          bf16_t* sp = stage + soff(row, cl / 8) + 4 * lhalf;
           if constexpr (EPI == EPI_BIAS_GELU) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
           }
           if constexpr (EPI == EPI_BIAS_RESIDUAL) {
-            const u32x2 rr = *(const u32x2*)(a.res + m * N + n);
+            const u32x2 rr = *(const u32x2*)sp;
             v[0] += bflo(rr[0]); v[1] += bfhi(rr[0]); v[2] += bflo(rr[1]); v[3] += bfhi(rr[1]);
             if (zero_row) v[0] = v[1] = v[2] = v[3] = 0.f;
           }
-          *(u32x2*)(a.y + m * N + n) = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+          *(u32x2*)sp = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
         }
       }
+    }
+  }
+  __syncthreads();
+
+#pragma unroll 4
+  for (int p = 0; p < PASSES; ++p) {
+    const int idx = p * 64 + lane, row = idx / CPR, ch = idx % CPR;
+    const int64_t m = mw + row;
+    const int n = nw + ch * 8;
+    if (m >= M || n >= N) continue;
+    const u32x4 v = *(const u32x4*)(stage + soff(row, ch));
+    if constexpr (EPI == EPI_QKV_ROPE) {
+      if (a.pos[m] < 0) continue;  // padding row of a bshd batch: never attended
+      const int heads = N / 192;
+      const int head = n / 192, c = (n % 192) / 64, d = n % 64;
+      *(u32x4*)(a.y + (((int64_t)c * heads + head) * M + m) * kHeadDim + d) = v;
+    } else {
+      *(u32x4*)(a.y + m * N + n) = v;
     }
   }
 }
