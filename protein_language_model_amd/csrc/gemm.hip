@@ -6,9 +6,10 @@
 // from LDS as 16-byte runs along K.
 //
 // Design (CDNA4):
-//  * 256 threads = 4 waves in a WAVES_M x WAVES_N grid; each wave owns a
-//    (BM/WAVES_M) x (BN/WAVES_N) tile built from 32x32 blocks of
-//    v_mfma_f32_32x32x16_bf16 with fp32 accumulators.
+//  * WAVES_M x WAVES_N waves (8 = two per SIMD: one wave's LDS reads and
+//    waits overlap the other's MFMAs); each wave owns a (BM/WAVES_M) x
+//    (BN/WAVES_N) tile built from 32x32 blocks of v_mfma_f32_32x32x16_bf16
+//    with fp32 accumulators.
 //  * The weight is MFMA operand A and the activations operand B, so lane l of
 //    a 32x32 block holds output row m = l%32 and columns
 //    n = 8*(r/4) + 4*(l/32) + r%4 (r = 0..15): four consecutive columns per
@@ -74,15 +75,17 @@ __device__ __forceinline__ float gelu_erf(float z) {
 }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) {
+  constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WTM = BM / WAVES_M;
   constexpr int WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32;
   constexpr int FN = WTN / 32;
-  constexpr int XRB = BM / 32;  // 8-row blocks of the x tile per wave
-  constexpr int WRB = BN / 32;
+  constexpr int XRB = BM / (8 * NW);  // 8-row blocks of the x tile per wave
+  constexpr int WRB = BN / (8 * NW);
   constexpr int kStage = (BM + BN) * kBK;
-  static_assert(WAVES_M * WAVES_N == 4, "4 waves");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(XRB * 8 * NW == BM && WRB * 8 * NW == BN, "tile rows must split evenly over the waves");
   static_assert(EPI != EPI_QKV_ROPE || (FN % 2 == 0 && WTN % 64 == 0), "rotary pairs need 64-wide wave columns");
 
   __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * kStage];
@@ -123,13 +126,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
   const bf16_t* wsrc[WRB];
 #pragma unroll
   for (int i = 0; i < XRB; ++i) {
-    int64_t r = m0 + (int64_t)(wave + 4 * i) * 8 + lr8;
+    int64_t r = m0 + (int64_t)(wave + NW * i) * 8 + lr8;
     r = r < M ? r : M - 1;
     xsrc[i] = a.x + r * K + lchunk;
   }
 #pragma unroll
   for (int i = 0; i < WRB; ++i) {
-    int r = n0 + (wave + 4 * i) * 8 + lr8;
+    int r = n0 + (wave + NW * i) * 8 + lr8;
     r = r < N ? r : N - 1;
     wsrc[i] = a.w + (int64_t)r * K + lchunk;
   }
@@ -138,9 +141,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmArgs a) {
   auto issue_tile = [&](int k0, int buf) {
     const uint32_t base = lds0 + (uint32_t)(buf * kStage) * 2u;
 #pragma unroll
-    for (int i = 0; i < XRB; ++i) lds_dma16(xsrc[i] + k0, base + (uint32_t)((wave_u + 4 * i) * 8 * kBK) * 2u);
+    for (int i = 0; i < XRB; ++i) lds_dma16(xsrc[i] + k0, base + (uint32_t)((wave_u + NW * i) * 8 * kBK) * 2u);
 #pragma unroll
-    for (int i = 0; i < WRB; ++i) lds_dma16(wsrc[i] + k0, base + (uint32_t)((BM + (wave_u + 4 * i) * 8) * kBK) * 2u);
+    for (int i = 0; i < WRB; ++i) lds_dma16(wsrc[i] + k0, base + (uint32_t)((BM + (wave_u + NW * i) * 8) * kBK) * 2u);
   };
 
   // Fragment reads: row r of the tile, logical 16-byte chunk ch, stored at
@@ -335,21 +338,15 @@ hipError_t run(const GemmArgs& a, hipStream_t st) {
   const int64_t tilesM = (a.M + BM - 1) / BM;
   const int64_t tilesN = (a.N + BN - 1) / BN;
   const int64_t nb = tilesM * tilesN;
-  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI>), dim3((unsigned)nb), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI>), dim3((unsigned)nb), dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
 
 template <int EPI>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
-  // 256x256 tiles when they give at least ~4 waves of workgroups over the 256
-  // CUs; otherwise 256x128 tiles halve the wave-quantisation loss.
-  const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  if constexpr (EPI == EPI_QKV_ROPE) {
-    return run<256, 256, 2, 2, EPI>(a, st);
-  } else {
-    if (t256 >= 4 * 256) return run<256, 256, 2, 2, EPI>(a, st);
-    return run<256, 128, 2, 2, EPI>(a, st);
-  }
+  // 256x256 tiles, 8 waves (two per SIMD, so one wave's LDS reads overlap the
+  // other's MFMAs) of 128x64 each.
+  return run<256, 256, 2, 4, EPI>(a, st);
 }
 
 }  // namespace
