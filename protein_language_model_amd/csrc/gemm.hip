@@ -36,7 +36,6 @@ namespace esm {
 
 namespace {
 
-constexpr int kBK = 64;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 
@@ -74,21 +73,28 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erf_as7126(z * 0.70710678118654752f));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) {
+template <int BM, int BN, int WAVES_M, int WAVES_N, int kBK, int MINB, int EPI>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void k_gemm(GemmArgs a) {
   constexpr int NW = WAVES_M * WAVES_N;
+  constexpr int KK = kBK / 16;         // 16-wide k sub-steps per K step
+  constexpr int CR = kBK / 8;          // 16-byte chunks per LDS row
+  constexpr int RW = 256 / (kBK * 2);  // LDS rows per 256-byte bank window
+  constexpr int RPI = 1024 / (kBK * 2);  // rows filled by one 1 KB direct load
   constexpr int WTM = BM / WAVES_M;
   constexpr int WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32;
   constexpr int FN = WTN / 32;
-  constexpr int XRB = BM / (8 * NW);  // 8-row blocks of the x tile per wave
-  constexpr int WRB = BN / (8 * NW);
+  constexpr int XRB = BM / (RPI * NW);  // RPI-row blocks of the x tile per wave
+  constexpr int WRB = BN / (RPI * NW);
   constexpr int kStage = (BM + BN) * kBK;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  static_assert(XRB * 8 * NW == BM && WRB * 8 * NW == BN, "tile rows must split evenly over the waves");
+  static_assert(XRB * RPI * NW == BM && WRB * RPI * NW == BN, "tile rows must split evenly over the waves");
+  static_assert(KK % 2 == 0, "fragment double buffering alternates over an even number of sub-steps");
   static_assert(EPI != EPI_QKV_ROPE || (FN % 2 == 0 && WTN % 64 == 0), "rotary pairs need 64-wide wave columns");
 
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * kStage];
+  // Two K-step stages; after the K loop the same memory stages the output tile.
+  constexpr int kSmem = 2 * kStage > BM * BN ? 2 * kStage : BM * BN;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmem];
 
   const int64_t M = a.M;
   const int N = a.N, K = a.K;
@@ -116,23 +122,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   const int lrow = lane & 31, lhalf = lane >> 5;
 
   // Direct-to-LDS tile loads.  One global_load_lds_dwordx4 fills 1 KB of LDS
-  // (8 rows of 64 bf16), lane i writing bytes [16 i, 16 i + 16).  Lane i of a
-  // wave therefore fetches row r = 8*rb + i/8 at the logical chunk that the
-  // swizzle stores in physical chunk i%8: c = (i%8) ^ ((r >> 1) & 7), where
-  // (r >> 1) & 7 = 4*(rb & 1) + i/16 and rb & 1 = wave & 1.
-  const int lr8 = lane >> 3;
-  const int lchunk = ((lane & 7) ^ (((wave & 1) << 2) | (lane >> 4))) * 8;
+  // (RPI rows of kBK bf16), lane i writing bytes [16 i, 16 i + 16).  Lane i of
+  // a wave therefore fetches row r = RPI*rb + i/CR at the logical chunk that
+  // the swizzle stores in physical chunk i%CR: c = (i%CR) ^ ((r / RW) % CR).
+  // With rb = wave + NW*i (NW even), (r / RW) % CR depends on the lane and on
+  // wave & 1 only.
+  const int lr8 = lane / CR;
+  const int lchunk = ((lane % CR) ^ (((((wave & 1) * RPI) + lr8) / RW) % CR)) * 8;
   const bf16_t* xsrc[XRB];
   const bf16_t* wsrc[WRB];
 #pragma unroll
   for (int i = 0; i < XRB; ++i) {
-    int64_t r = m0 + (int64_t)(wave + NW * i) * 8 + lr8;
+    int64_t r = m0 + (int64_t)(wave + NW * i) * RPI + lr8;
     r = r < M ? r : M - 1;
     xsrc[i] = a.x + r * K + lchunk;
   }
 #pragma unroll
   for (int i = 0; i < WRB; ++i) {
-    int r = n0 + (wave + NW * i) * 8 + lr8;
+    int r = n0 + (wave + NW * i) * RPI + lr8;
     r = r < N ? r : N - 1;
     wsrc[i] = a.w + (int64_t)r * K + lchunk;
   }
@@ -141,15 +148,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   auto issue_tile = [&](int k0, int buf) {
     const uint32_t base = lds0 + (uint32_t)(buf * kStage) * 2u;
 #pragma unroll
-    for (int i = 0; i < XRB; ++i) lds_dma16(xsrc[i] + k0, base + (uint32_t)((wave_u + NW * i) * 8 * kBK) * 2u);
+    for (int i = 0; i < XRB; ++i) lds_dma16(xsrc[i] + k0, base + (uint32_t)((wave_u + NW * i) * RPI * kBK) * 2u);
 #pragma unroll
-    for (int i = 0; i < WRB; ++i) lds_dma16(wsrc[i] + k0, base + (uint32_t)((BM + (wave_u + NW * i) * 8) * kBK) * 2u);
+    for (int i = 0; i < WRB; ++i) lds_dma16(wsrc[i] + k0, base + (uint32_t)((BM + (wave_u + NW * i) * RPI) * kBK) * 2u);
   };
 
   // Fragment reads: row r of the tile, logical 16-byte chunk ch, stored at
-  // physical chunk ch ^ ((r >> 1) & 7); every row this lane reads has
-  // (r >> 1) & 7 = (lane % 32) / 2.
-  const int swz = (lrow >> 1) & 7;
+  // physical chunk ch ^ ((r / RW) % CR); every row this lane reads has
+  // (r / RW) % CR = ((lane % 32) / RW) % CR.
+  const int swz = (lrow / RW) % CR;
   auto load_frags = [&](bf16x8 (&xf)[FM], bf16x8 (&wf)[FN], int buf, int kk) {
     const bf16_t* sx = smem + buf * kStage;
     const bf16_t* sw = sx + BM * kBK;
@@ -177,38 +184,30 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   };
 
   const int nk = K / kBK;
-  bf16x8 xa[FM], wa[FN], xb[FM], wb[FN];
+  bf16x8 xf[2][FM], wf[2][FN];
   issue_tile(0, 0);
   vm_wait_all();
   __syncthreads();
-  load_frags(xa, wa, 0, 0);
+  load_frags(xf[0], wf[0], 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) issue_tile((kt + 1) * kBK, cur ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(xb, wb, cur, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(xa, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(xa, wa, cur, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(xb, wb);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags(xb, wb, cur, 3);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(xa, wa);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) {
-      // Next tile landed for every wave, and every wave is done with this
-      // tile's first three k-steps; its first fragments load under the last
-      // k-step's MFMAs.
-      vm_wait_all();
-      __syncthreads();
-      load_frags(xa, wa, cur ^ 1, 0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 1 < KK) {
+        load_frags(xf[(kk + 1) & 1], wf[(kk + 1) & 1], cur, kk + 1);
+      } else if (more) {
+        // Next tile landed for every wave, and every wave is done reading this
+        // one; its first fragments load under the last sub-step's MFMAs.
+        vm_wait_all();
+        __syncthreads();
+        load_frags(xf[0], wf[0], cur ^ 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(xf[kk & 1], wf[kk & 1]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_step(xb, wb);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -333,12 +332,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int BK, int MINB, int EPI>
 hipError_t run(const GemmArgs& a, hipStream_t st) {
   const int64_t tilesM = (a.M + BM - 1) / BM;
   const int64_t tilesN = (a.N + BN - 1) / BN;
   const int64_t nb = tilesM * tilesN;
-  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI>), dim3((unsigned)nb), dim3(64 * WM * WN), 0, st, a);
+  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, BK, MINB, EPI>), dim3((unsigned)nb), dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
 
@@ -346,7 +345,7 @@ template <int EPI>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   // 256x256 tiles, 8 waves (two per SIMD, so one wave's LDS reads overlap the
   // other's MFMAs) of 128x64 each.
-  return run<256, 256, 2, 4, EPI>(a, st);
+  return run<256, 256, 2, 4, 64, 1, EPI>(a, st);
 }
 
 }  // namespace

@@ -13,7 +13,8 @@ from typing import Dict, Iterable, List, Optional, Sequence
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libesmenc.so")
+# ESM_LIBRARY may point at another build of the same library.
+LIB_PATH = os.environ.get("ESM_LIBRARY") or os.path.join(_PKG, "libesmenc.so")
 
 ESM_OK = 0
 STATUS_NAMES = {0: "ESM_OK", 1: "ESM_ERR_NULL", 2: "ESM_ERR_SHAPE", 3: "ESM_ERR_SEQLENS", 4: "ESM_ERR_UNSUPPORTED",
