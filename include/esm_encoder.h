@@ -37,7 +37,9 @@
  *     failure nothing is enqueued and esm_last_error() describes the problem.
  *   - One handle must not be used from two host threads or two streams at once.
  *   - The caller owns every tensor passed in, the workspace and the stream.  The
- *     library owns the handle and the rotary table it builds at create time.
+ *     library owns the handle and the rotary table it builds at create time,
+ *     and, for the FP8 precision, the delayed-scaling state and the E4M3
+ *     copies of the weights.
  */
 #ifndef ESM_ENCODER_H
 #define ESM_ENCODER_H
@@ -49,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 1
+#define ESM_ABI_VERSION 2
 
 typedef struct esm_encoder esm_encoder;
 typedef void* esm_stream_t; /* a hipStream_t */
@@ -79,7 +81,7 @@ typedef struct {
   int32_t max_position_embeddings; /* rotary table rows; longest allowed sequence */
   float layer_norm_eps;         /* LayerNorm epsilon (biased variance) */
   float rope_base;              /* rotary base; theta_i = p * base^(-i/32) */
-  int32_t precision;            /* esm_precision */
+  int32_t precision;            /* esm_precision; FP8 needs H and F multiples of 128 */
   int32_t amax_history_len;     /* FP8 delayed-scaling history, 1..1024 */
 } esm_config;
 
@@ -126,6 +128,9 @@ esm_status esm_encoder_destroy(esm_encoder* enc);
 esm_status esm_workspace_size(const esm_encoder* enc, int64_t max_tokens, int32_t max_seqs,
                               size_t* bytes);
 
+/* With the FP8 precision the four GEMM inputs (LN1, CTX, LN2, ACT) hold E4M3
+ * bytes with the same row counts ([T, H] or [T, F] bytes, the region keeps its
+ * bf16 size); the code of value v is cast(v * scale) of that tensor. */
 typedef enum {
   ESM_WS_LN1 = 0,   /* bf16 [T, H]  LayerNorm-1 output */
   ESM_WS_QKV = 1,   /* bf16 [3, heads, T, 64]  rotated q, rotated k, v (planar) */
@@ -162,7 +167,18 @@ esm_status esm_workspace_region(const esm_encoder* enc, int64_t max_tokens, int3
  *                    out-of-bounds access.
  *   max_seqlen       host upper bound on the sequence lengths
  *   layer_idx        0-based index of the layer (FP8 state slot)
- * T = 0 or B = 0 returns ESM_OK without a launch. */
+ * T = 0 or B = 0 returns ESM_OK without a launch.
+ *
+ * FP8 precision (ESM_PRECISION_FP8_DELAYED; [BIO-ACC] 2.1 and 4.1, [TE-RU] FP8
+ * recipe): each of the four linears computes (Q(a s_a) Q(W s_w)^T) / (s_a s_w)
+ * + b, Q = cast to E4M3 (round to nearest even, saturating at +-448), with the
+ * per-tensor scales of layer layer_idx; LayerNorm, attention, the residuals and
+ * every GEMM output stay in bf16/fp32.  The layer's E4M3 weights come from
+ * esm_fp8_prepare_layer (ESM_ERR_STATE if it was never called for layer_idx);
+ * the bf16 weight pointers in w must still be valid, LN parameters and biases
+ * are read from w.  The call is one delayed-scaling step for that layer: it
+ * uses the scales fixed by earlier steps, records this step's amax of the four
+ * activations and, at its end, rolls the history and sets the next scales. */
 esm_status esm_layer_fwd(esm_encoder* enc, const esm_layer_weights* w, int32_t layer_idx,
                          const void* x_in, void* x_out,
                          const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -172,7 +188,8 @@ esm_status esm_layer_fwd(esm_encoder* enc, const esm_layer_weights* w, int32_t l
 /* Embedding lookup (when token_ids != NULL: X0 = E[ids], ids clamped into
  * [0, vocab)) or the given hidden states x_in, then all num_hidden_layers
  * layers in order ([BIO-ACC] 3.2 PackedEsm.forward; [TE-ESM2] 自动混合精度训练).
- * No final LayerNorm.  `w` is a HOST array of num_hidden_layers structs. */
+ * No final LayerNorm.  `w` is a HOST array of num_hidden_layers structs.
+ * FP8: layer l uses state slot l; the call is one step for every layer. */
 esm_status esm_stack_fwd(esm_encoder* enc, const esm_layer_weights* w,
                          const int32_t* token_ids, const void* embedding,
                          const void* x_in, void* x_out,
@@ -219,7 +236,8 @@ esm_status esm_attention_fwd(esm_encoder* enc, const void* qkv, void* ctx,
 typedef enum {
   ESM_EPI_BIAS = 0,          /* y = x W^T + b */
   ESM_EPI_BIAS_GELU = 1,     /* y = GELU(x W^T + b) */
-  ESM_EPI_BIAS_RESIDUAL = 2  /* y = r + x W^T + b */
+  ESM_EPI_BIAS_RESIDUAL = 2, /* y = r + x W^T + b */
+  ESM_EPI_BIAS_GELU_E4M3 = 3 /* y = cast(GELU(x W^T + b) * s_y) to E4M3, amax recorded (E4M3 GEMM only) */
 } esm_epilogue;
 
 /* y[M, N] = epilogue(x[M, K] W[N, K]^T + b) on the library's MFMA GEMM.
@@ -228,9 +246,69 @@ esm_status esm_linear_fwd(esm_encoder* enc, const void* x, const void* w, const 
                           const void* residual, void* y, int64_t M, int32_t N, int32_t K,
                           int32_t epilogue, esm_stream_t stream);
 
+/* E4M3 GEMM of the FP8 path ([BIO-ACC] 4.1, [TE-RU] FP8 recipe):
+ *   z = (x8 . w8^T) / (x_scale[0] * w_scale[0]) + b,  then the epilogue on z.
+ *   x8 [M, K], w8 [N, K]: E4M3 codes (uint8); x_scale, w_scale: device float[1]
+ *   y: bf16 [M, N], or E4M3 [M, N] for ESM_EPI_BIAS_GELU_E4M3, which casts
+ *      GELU(z) * y_scale[0] and atomically maxes max|GELU(z)| into *y_amax
+ *      (device uint32 holding float bits; the caller clears it).
+ * N must be a multiple of 64 and K of 128. */
+esm_status esm_linear_e4m3_fwd(esm_encoder* enc, const void* x8, const float* x_scale,
+                               const void* w8, const float* w_scale, const void* b,
+                               const void* residual, void* y, const float* y_scale,
+                               uint32_t* y_amax, int64_t M, int32_t N, int32_t K,
+                               int32_t epilogue, esm_stream_t stream);
+
 /* Row LayerNorm y = (x - mean) / sqrt(var + eps) * gamma + beta over [M, H]. */
 esm_status esm_layernorm_fwd(esm_encoder* enc, const void* x, const void* gamma,
                              const void* beta, void* y, int64_t M, esm_stream_t stream);
+
+/* ---------------------------------------------------------------- FP8 delayed scaling */
+
+/* Per-tensor delayed scaling ([BIO-ACC] 2.1 and 4.1: DelayedScaling, amax
+ * history, "max" algorithm; [TE-RU] FP8 recipe: history length 16).  Per layer
+ * four activation tensors are tracked, in this order: LN1 output, attention
+ * context, LN2 output, GELU output.  Each has a scale s (initially 1) and a
+ * ring buffer of the amax (max |value| before the cast) of the last
+ * amax_history_len steps (initially 0).  At the end of every step the step's
+ * amax enters slot steps % history_len, steps increases, and
+ * s = 448 / max(history) when that maximum is positive and finite (otherwise s
+ * is kept and, if the step's amax was Inf or NaN, the sticky nonfinite flag is
+ * set).  Weight scales are 448 / amax(W), fixed when the layer is prepared
+ * (1 for an all-zero or non-finite weight). */
+typedef struct {
+  int32_t num_layers;    /* must equal the config's num_hidden_layers */
+  int32_t history_len;   /* must equal the config's amax_history_len */
+  float* act_scale;      /* host [num_layers, 4] */
+  float* amax_history;   /* host [num_layers, 4, history_len] */
+  int64_t* steps;        /* host [num_layers] */
+  float* weight_scale;   /* host [num_layers, 4] (qkv, out, fc1, fc2); read by get, ignored by set */
+  uint32_t nonfinite;    /* sticky flag */
+} esm_fp8_state;
+
+/* Casts layer layer_idx's four linear weights (bf16 in w) to E4M3 copies owned
+ * by the library, each with scale 448 / amax(W) computed on the device.
+ * Enqueued on stream; call again whenever the weights change.
+ * ESM_ERR_STATE for a bf16 encoder. */
+esm_status esm_fp8_prepare_layer(esm_encoder* enc, int32_t layer_idx, const esm_layer_weights* w,
+                                 esm_stream_t stream);
+
+/* Copies the state into the caller's host arrays after waiting for stream. */
+esm_status esm_fp8_get_state(esm_encoder* enc, esm_fp8_state* state, esm_stream_t stream);
+
+/* Replaces the state (scales must be positive and finite; steps >= 0) after
+ * waiting for stream, and clears the amax of the current step. */
+esm_status esm_fp8_set_state(esm_encoder* enc, const esm_fp8_state* state, esm_stream_t stream);
+
+/* Back to the initial state (scales 1, empty histories, steps 0, flag clear);
+ * prepared weights are kept. */
+esm_status esm_fp8_reset(esm_encoder* enc, esm_stream_t stream);
+
+/* The E4M3 cast the producers use, as a test entry: y[i] = cast(x[i] *
+ * scale[0]) for fp32 x (device, n values), y uint8 codes; max |x| is
+ * atomically maxed into *amax (device uint32, float bits, caller-cleared). */
+esm_status esm_fp8_quantize(esm_encoder* enc, const float* x, int64_t n, const float* scale,
+                            void* y, uint32_t* amax, esm_stream_t stream);
 
 /* ---------------------------------------------------------------- timing */
 
@@ -238,7 +316,7 @@ esm_status esm_layernorm_fwd(esm_encoder* enc, const void* x, const void* gamma,
 typedef enum {
   ESM_K_SEGMENT = 0, ESM_K_EMBED = 1, ESM_K_LAYERNORM = 2, ESM_K_GEMM_QKV = 3,
   ESM_K_ATTENTION = 4, ESM_K_GEMM_OUT = 5, ESM_K_GEMM_FC1 = 6, ESM_K_GEMM_FC2 = 7,
-  ESM_K_OTHER = 8, ESM_K_COUNT = 9
+  ESM_K_OTHER = 8, ESM_K_FP8 = 9 /* weight casts, scale updates */, ESM_K_COUNT = 10
 } esm_kernel_class;
 
 /* When on, every launch is bracketed by HIP events recorded on the launch

@@ -188,10 +188,32 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
     __syncthreads();
   }
 
-  if (qrow >= L) return;
   const float lt = l_i + __shfl_xor(l_i, 32);
   const float inv = 1.0f / lt;
   const int H = heads * kHeadDim;
+  if (a.ctx8.y) {
+    // E4M3 context for the FP8 out-projection: cast with the tensor's delayed
+    // scale, amax over the valid rows recorded by every lane of the wave.
+    const float s8 = a.ctx8.scale[0];
+    float amax = 0.f;
+    if (qrow < L) {
+      uint8_t* dst = a.ctx8.y + (start + qrow) * H + head * kHeadDim;
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int dim = d * 32 + 8 * gq + 4 * lhalf;
+          const float v[4] = {o[d][4 * gq] * inv, o[d][4 * gq + 1] * inv, o[d][4 * gq + 2] * inv,
+                              o[d][4 * gq + 3] * inv};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(v[e]));
+          *(uint32_t*)(dst + dim) = pack_e4m3x4(v, s8);
+        }
+    }
+    record_amax(a.ctx8.amax, amax);
+    return;
+  }
+  if (qrow >= L) return;
   bf16_t* dst = a.ctx + (start + qrow) * H + head * kHeadDim;
 #pragma unroll
   for (int d = 0; d < 2; ++d)

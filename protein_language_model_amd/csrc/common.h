@@ -31,6 +31,41 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }
 
+// Operand element types of the GEMM.
+constexpr int kBF16 = 0;
+constexpr int kE4M3 = 1;
+constexpr float kE4M3Max = 448.0f;
+
+// Four values v * s cast to OCP E4M3 (1.4.3, bias 7, no infinity, 0x7F = NaN,
+// largest finite 448), packed little-endian into one word.  The gfx950
+// converter rounds to nearest even; out-of-range inputs are clamped to +-448
+// first (saturating cast, as the delayed-scaling recipe requires) and NaN is
+// written as 0x7F.
+__device__ __forceinline__ uint32_t pack_e4m3x4(const float (&v)[4], float s) {
+  float c[4];
+  uint32_t nan_mask = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float t = v[e] * s;
+    nan_mask |= (t != t) ? (0xFFu << (8 * e)) : 0u;
+    c[e] = fminf(fmaxf(t, -kE4M3Max), kE4M3Max);
+  }
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
+  return ((uint32_t)w & ~nan_mask) | (0x7F7F7F7Fu & nan_mask);
+}
+
+// Record a non-negative per-lane maximum into *amax (float bits as uint32):
+// the wave reduces with fmaxf (which drops NaN), lane 0 issues one
+// atomicMax.  Non-negative floats order like their bit patterns, so the result
+// is exact and independent of the order of the atomics.  Every lane of the
+// wave must call this.
+__device__ __forceinline__ void record_amax(uint32_t* amax, float m) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0 && m > 0.f) atomicMax(amax, __float_as_uint(m));
+}
+
 // Launch context handed from the host library to each launcher.
 struct Launch {
   hipStream_t stream;
@@ -56,14 +91,26 @@ hipError_t launch_segment_table(int layout, const int32_t* lens, int32_t B, int6
 hipError_t launch_embed(const int32_t* ids, const bf16_t* table, int32_t vocab, bf16_t* x,
                         int64_t T, int32_t H, hipStream_t st);
 
-hipError_t launch_layernorm(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y,
-                            int64_t M, int32_t H, float eps, hipStream_t st);
+// E4M3 output of a producer kernel: y = cast(v * scale[0]), amax of v
+// recorded into *amax.  y == nullptr selects the bf16 output instead.
+struct E4m3Out {
+  uint8_t* y;
+  const float* scale;  // device
+  uint32_t* amax;      // device, float bits
+  const int32_t* pos;  // optional [rows]: rows with pos < 0 (padding) stay out of the amax
+};
 
-enum GemmEpi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_QKV_ROPE = 3 };
+hipError_t launch_layernorm(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y,
+                            int64_t M, int32_t H, float eps, const E4m3Out& q, hipStream_t st);
+
+enum GemmEpi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_QKV_ROPE = 3, EPI_BIAS_GELU_E4M3 = 4 };
 
 struct GemmArgs {
-  const bf16_t* x;     // [M, K]
-  const bf16_t* w;     // [N, K]
+  int32_t dtype;       // kBF16 or kE4M3 operands
+  const void* x;       // [M, K]
+  const void* w;       // [N, K]
+  const float* x_scale;  // E4M3: device scales; the product is divided by x_scale[0] * w_scale[0]
+  const float* w_scale;
   const bf16_t* bias;  // [N] or null
   const bf16_t* res;   // [M, N] residual or null
   bf16_t* y;           // [M, N] (EPI_QKV_ROPE: planar [3, heads, M, 64])
@@ -75,6 +122,10 @@ struct GemmArgs {
   int32_t max_positions;
   // residual epilogue: rows whose pos < 0 are written as zero when zero_pad_rows
   int32_t zero_pad_rows;
+  // EPI_BIAS_GELU_E4M3: y8 = cast(gelu(.) * y8_scale[0]), amax into *y8_amax
+  uint8_t* y8;
+  const float* y8_scale;
+  uint32_t* y8_amax;
 };
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st);
@@ -82,6 +133,7 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st);
 struct AttnArgs {
   const bf16_t* qkv;      // [3, heads, T, 64]
   bf16_t* ctx;            // [T, heads*64]
+  E4m3Out ctx8;           // when ctx8.y is set: E4M3 context instead of ctx
   const int32_t* segs;    // [B, 2]
   const int32_t* tiles;   // [cap, 2]
   const int32_t* ntiles;  // [1]
@@ -91,5 +143,29 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
+// Delayed-scaling bookkeeping (fp8.hip).
+struct Fp8State {
+  float* act_scale;    // [layers, 4] scale used by the current step (ln1, ctx, ln2, act)
+  uint32_t* act_amax;  // [layers, 4] amax of the current step, float bits
+  float* history;      // [layers, 4, history_len] ring buffer
+  int64_t* steps;      // [layers] recorded steps (ring position = steps % history_len)
+  uint32_t* flags;     // [1] bit 0: a non-finite amax was recorded
+  float* w_scale;      // [layers, 4] weight scales (qkv, out, fc1, fc2)
+  uint32_t* w_amax;    // [layers, 4]
+  int32_t history_len;
+};
+
+// amax of n bf16 values into *amax (which must start at 0).
+hipError_t launch_amax_bf16(const bf16_t* x, int64_t n, uint32_t* amax, hipStream_t st);
+// y = cast(x * s), s = 448 / amax (1 when amax is 0 or not finite); writes s to *scale_out.
+hipError_t launch_quantize_weight(const bf16_t* x, int64_t n, const uint32_t* amax, uint8_t* y, float* scale_out,
+                                  hipStream_t st);
+// y = cast(x * scale[0]) with x fp32 (test hook of the cast); amax of x into *amax.
+hipError_t launch_quantize_f32(const float* x, int64_t n, const float* scale, uint8_t* y, uint32_t* amax,
+                               hipStream_t st);
+// End of a step for layers [l0, l0 + nl): push amax into the history, new scale
+// = 448 / max(history) when that is positive and finite, clear amax.
+hipError_t launch_scale_update(const Fp8State& s, int32_t l0, int32_t nl, hipStream_t st);
 
 }  // namespace esm

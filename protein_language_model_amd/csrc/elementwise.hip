@@ -127,14 +127,16 @@ __global__ void k_embed(const int32_t* __restrict__ ids, const bf16_t* __restric
 
 // Row LayerNorm, one wave per row: mean, then the biased variance from the
 // centred values held in registers, y = (x - mean) * rsqrt(var + eps) * g + b
-// ([BIO-ACC] 3.1 layernorm; [TE-RU] LayerNormLinear / LayerNormMLP).
-template <int CH>
+// ([BIO-ACC] 3.1 layernorm; [TE-RU] LayerNormLinear / LayerNormMLP).  With
+// OUT8 the normalised row is cast to E4M3 with the tensor's delayed scale and
+// its amax recorded, the quantiser that feeds an FP8 GEMM ([BIO-ACC] 2.1).
+template <int CH, bool OUT8>
 __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
                                                    const bf16_t* __restrict__ beta, bf16_t* __restrict__ y,
-                                                   int64_t M, int32_t H, float eps) {
+                                                   int64_t M, int32_t H, float eps, E4m3Out q) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
+  if (row >= M) return;  // wave-uniform: the amax reduction below stays wave-complete
   const int chunks = H / 8;
   const bf16_t* xr = x + row * H;
   float v[CH][8];
@@ -171,22 +173,37 @@ __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x,
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
   const float rstd = 1.0f / sqrtf(sq / (float)H + eps);
+  float s8 = 1.0f, amax = 0.0f;
+  bool count = true;
+  if constexpr (OUT8) {
+    s8 = q.scale[0];
+    count = q.pos == nullptr || q.pos[row] >= 0;
+  }
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = lane + 64 * i;
     if (c < chunks) {
       const u32x4 g = *(const u32x4*)(gamma + c * 8);
       const u32x4 b = *(const u32x4*)(beta + c * 8);
-      u32x4 o;
+      float o[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float y0 = v[i][2 * e] * rstd * bflo(g[e]) + bflo(b[e]);
-        const float y1 = v[i][2 * e + 1] * rstd * bfhi(g[e]) + bfhi(b[e]);
-        o[e] = pack_bf2(y0, y1);
+        o[2 * e] = v[i][2 * e] * rstd * bflo(g[e]) + bflo(b[e]);
+        o[2 * e + 1] = v[i][2 * e + 1] * rstd * bfhi(g[e]) + bfhi(b[e]);
       }
-      *(u32x4*)(y + row * H + c * 8) = o;
+      if constexpr (OUT8) {
+        const float lo[4] = {o[0], o[1], o[2], o[3]}, hi[4] = {o[4], o[5], o[6], o[7]};
+        if (count)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(o[e]));
+        *(u32x2*)(q.y + row * H + c * 8) = u32x2{pack_e4m3x4(lo, s8), pack_e4m3x4(hi, s8)};
+      } else {
+        *(u32x4*)(y + row * H + c * 8) =
+            u32x4{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7])};
+      }
     }
   }
+  if constexpr (OUT8) record_amax(q.amax, amax);
 }
 
 }  // namespace
@@ -212,18 +229,25 @@ hipError_t launch_embed(const int32_t* ids, const bf16_t* table, int32_t vocab, 
   return hipGetLastError();
 }
 
-hipError_t launch_layernorm(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y, int64_t M,
-                            int32_t H, float eps, hipStream_t st) {
-  if (M <= 0) return hipSuccess;
+template <bool OUT8>
+hipError_t layernorm_ch(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y, int64_t M, int32_t H,
+                        float eps, const E4m3Out& q, hipStream_t st) {
   const unsigned grid = (unsigned)((M + 3) / 4);
   const int ch = (H / 8 + 63) / 64;
-  if (ch <= 1) hipLaunchKernelGGL(k_layernorm<1>, dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps);
-  else if (ch <= 2) hipLaunchKernelGGL(k_layernorm<2>, dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps);
-  else if (ch <= 3) hipLaunchKernelGGL(k_layernorm<3>, dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps);
-  else if (ch <= 5) hipLaunchKernelGGL(k_layernorm<5>, dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps);
-  else if (ch <= 8) hipLaunchKernelGGL(k_layernorm<8>, dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps);
+  if (ch <= 1) hipLaunchKernelGGL((k_layernorm<1, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
+  else if (ch <= 2) hipLaunchKernelGGL((k_layernorm<2, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
+  else if (ch <= 3) hipLaunchKernelGGL((k_layernorm<3, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
+  else if (ch <= 5) hipLaunchKernelGGL((k_layernorm<5, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
+  else if (ch <= 8) hipLaunchKernelGGL((k_layernorm<8, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
   else return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_layernorm(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y, int64_t M,
+                            int32_t H, float eps, const E4m3Out& q, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (q.y) return layernorm_ch<true>(x, gamma, beta, y, M, H, eps, q, st);
+  return layernorm_ch<false>(x, gamma, beta, y, M, H, eps, q, st);
 }
 
 }  // namespace esm

@@ -24,6 +24,12 @@ struct esm_encoder {
   std::vector<std::pair<int, size_t>> recs;  // (class, index of start event)
   double ms[ESM_K_COUNT] = {0};
   int64_t launches[ESM_K_COUNT] = {0};
+  // FP8 delayed scaling (precision ESM_PRECISION_FP8_DELAYED only)
+  void* fp8_mem = nullptr;         // state arrays of f8
+  Fp8State f8{};
+  uint8_t* w8 = nullptr;           // per layer: E4M3 w_qkv | w_out | w_fc1 | w_fc2
+  size_t w8_layer = 0;             // bytes per layer
+  std::vector<char> prepared;      // layer weights cast since create
 };
 
 namespace {
@@ -75,8 +81,10 @@ esm_status check_config(const esm_config* c) {
   if (!(c->rope_base > 1.f) || !isfinite(c->rope_base)) return fail(ESM_ERR_SHAPE, "rope_base must be > 1");
   if (c->precision != ESM_PRECISION_BF16 && c->precision != ESM_PRECISION_FP8_DELAYED)
     return fail(ESM_ERR_UNSUPPORTED, "unknown precision %d", c->precision);
-  if (c->precision == ESM_PRECISION_FP8_DELAYED)
-    return fail(ESM_ERR_UNSUPPORTED, "FP8 delayed scaling is not built in this library version");
+  if (c->precision == ESM_PRECISION_FP8_DELAYED && (c->hidden_size % 128 != 0 || c->intermediate_size % 128 != 0))
+    return fail(ESM_ERR_UNSUPPORTED,
+                "FP8 needs hidden_size (%d) and intermediate_size (%d) to be multiples of 128 (E4M3 K step)",
+                c->hidden_size, c->intermediate_size);
   if (c->amax_history_len < 1 || c->amax_history_len > 1024)
     return fail(ESM_ERR_SHAPE, "amax_history_len %d outside [1, 1024]", c->amax_history_len);
   return ok();
@@ -188,6 +196,92 @@ esm_status check_ws(const esm_encoder* e, void* ws, size_t ws_bytes, int64_t row
   return ok();
 }
 
+// ---------------------------------------------------------------- FP8 state
+
+bool is_fp8(const esm_encoder* e) { return e->cfg.precision == ESM_PRECISION_FP8_DELAYED; }
+
+// Byte offsets of the four E4M3 weights inside one layer's block.
+struct W8Off {
+  size_t qkv, out, fc1, fc2, total;
+};
+W8Off w8_offsets(const esm_config& c) {
+  const size_t H = (size_t)c.hidden_size, F = (size_t)c.intermediate_size;
+  W8Off o;
+  o.qkv = 0;
+  o.out = 3 * H * H;
+  o.fc1 = o.out + H * H;
+  o.fc2 = o.fc1 + F * H;
+  o.total = o.fc2 + H * F;
+  return o;
+}
+
+// Device layout of the delayed-scaling state: one allocation, 256-byte
+// aligned arrays.
+struct Fp8Layout {
+  size_t act_scale, act_amax, history, steps, flags, w_scale, w_amax, total;
+};
+Fp8Layout fp8_layout(const esm_config& c) {
+  const size_t L = (size_t)(c.num_hidden_layers > 0 ? c.num_hidden_layers : 1), HL = (size_t)c.amax_history_len;
+  Fp8Layout f;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  f.act_scale = take(L * 4 * sizeof(float));
+  f.act_amax = take(L * 4 * sizeof(uint32_t));
+  f.history = take(L * 4 * HL * sizeof(float));
+  f.steps = take(L * sizeof(int64_t));
+  f.flags = take(sizeof(uint32_t));
+  f.w_scale = take(L * 4 * sizeof(float));
+  f.w_amax = take(L * 4 * sizeof(uint32_t));
+  f.total = o;
+  return f;
+}
+
+// Scales 1, empty histories, no steps, no flags, amax cleared (synchronous).
+esm_status fp8_reset_state(esm_encoder* e) {
+  const esm_config& c = e->cfg;
+  const size_t L = (size_t)(c.num_hidden_layers > 0 ? c.num_hidden_layers : 1), HL = (size_t)c.amax_history_len;
+  std::vector<float> ones(L * 4, 1.0f);
+  HIP_TRY(hipMemcpy(e->f8.act_scale, ones.data(), ones.size() * sizeof(float), hipMemcpyHostToDevice), "fp8 reset");
+  HIP_TRY(hipMemset(e->f8.act_amax, 0, L * 4 * sizeof(uint32_t)), "fp8 reset");
+  HIP_TRY(hipMemset(e->f8.history, 0, L * 4 * HL * sizeof(float)), "fp8 reset");
+  HIP_TRY(hipMemset(e->f8.steps, 0, L * sizeof(int64_t)), "fp8 reset");
+  HIP_TRY(hipMemset(e->f8.flags, 0, sizeof(uint32_t)), "fp8 reset");
+  return ok();
+}
+
+esm_status fp8_create(esm_encoder* e) {
+  const esm_config& c = e->cfg;
+  const Fp8Layout f = fp8_layout(c);
+  HIP_TRY(hipMalloc(&e->fp8_mem, f.total), "fp8 state");
+  char* b = (char*)e->fp8_mem;
+  e->f8.act_scale = (float*)(b + f.act_scale);
+  e->f8.act_amax = (uint32_t*)(b + f.act_amax);
+  e->f8.history = (float*)(b + f.history);
+  e->f8.steps = (int64_t*)(b + f.steps);
+  e->f8.flags = (uint32_t*)(b + f.flags);
+  e->f8.w_scale = (float*)(b + f.w_scale);
+  e->f8.w_amax = (uint32_t*)(b + f.w_amax);
+  e->f8.history_len = c.amax_history_len;
+  HIP_TRY(hipMemset(e->f8.w_scale, 0, f.total - f.w_scale), "fp8 state");
+  e->w8_layer = align256(w8_offsets(c).total);
+  const size_t L = (size_t)(c.num_hidden_layers > 0 ? c.num_hidden_layers : 1);
+  HIP_TRY(hipMalloc((void**)&e->w8, L * e->w8_layer), "fp8 weights");
+  e->prepared.assign(L, 0);
+  return fp8_reset_state(e);
+}
+
+esm_status check_fp8_layer(const esm_encoder* e, int32_t l) {
+  if (l < 0 || l >= e->cfg.num_hidden_layers)
+    return fail(ESM_ERR_SHAPE, "layer_idx %d outside [0, num_hidden_layers = %d)", l, e->cfg.num_hidden_layers);
+  if (!e->prepared[(size_t)l])
+    return fail(ESM_ERR_STATE, "FP8 weights of layer %d not prepared (esm_fp8_prepare_layer)", l);
+  return ok();
+}
+
 // ---------------------------------------------------------------- launch sequence
 
 esm_status run_segments(esm_encoder* e, int layout, const int32_t* lens, int32_t B, int64_t rows, int32_t S,
@@ -204,8 +298,11 @@ esm_status run_segments(esm_encoder* e, int layout, const int32_t* lens, int32_t
 }
 
 // One pre-LN layer on rows already described by the segment table in ws.
-esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, const bf16_t* x_in, bf16_t* x_out, int64_t rows,
-                     int32_t B, bool zero_pad_rows, void* ws, const Plan& p, hipStream_t st) {
+// FP8: the four GEMM inputs are produced in E4M3 by their producers (LN1, the
+// attention epilogue, LN2, the fc1 epilogue) with layer li's delayed scales,
+// and the GEMMs read layer li's E4M3 weights.
+esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, int32_t li, const bf16_t* x_in, bf16_t* x_out,
+                     int64_t rows, int32_t B, bool zero_pad_rows, void* ws, const Plan& p, hipStream_t st) {
   const esm_config& c = e->cfg;
   const int H = c.hidden_size, F = c.intermediate_size, heads = c.num_attention_heads;
   bf16_t* ln1 = region<bf16_t>(ws, p, ESM_WS_LN1);
@@ -215,28 +312,52 @@ esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, const bf16_t* x
   bf16_t* ln2 = region<bf16_t>(ws, p, ESM_WS_LN2);
   bf16_t* act = region<bf16_t>(ws, p, ESM_WS_ACT);
   const int32_t* pos = region<int32_t>(ws, p, ESM_WS_POS);
+  const bool fp8 = is_fp8(e);
+  float* as = nullptr;                 // activation scales: ln1, ctx, ln2, act
+  uint32_t* am = nullptr;              // their amax slots
+  const float* wsc = nullptr;          // weight scales: qkv, out, fc1, fc2
+  const uint8_t* w8 = nullptr;
+  const W8Off wo = w8_offsets(c);
+  if (fp8) {
+    as = e->f8.act_scale + 4 * li;
+    am = e->f8.act_amax + 4 * li;
+    wsc = e->f8.w_scale + 4 * li;
+    w8 = e->w8 + (size_t)li * e->w8_layer;
+  }
+  auto q8 = [&](void* y, int t, const int32_t* rows_pos) {
+    return fp8 ? E4m3Out{(uint8_t*)y, as + t, am + t, rows_pos} : E4m3Out{nullptr, nullptr, nullptr, nullptr};
+  };
   esm_status s;
 
   s = timed(e, ESM_K_LAYERNORM, st, "layernorm 1", [&] {
     return launch_layernorm(x_in, (const bf16_t*)w->ln1_gamma, (const bf16_t*)w->ln1_beta, ln1, rows, H,
-                            c.layer_norm_eps, st);
+                            c.layer_norm_eps, q8(ln1, 0, pos), st);
   });
   if (s) return s;
 
   GemmArgs g{};
+  g.dtype = fp8 ? kE4M3 : kBF16;
   g.M = rows;
   g.pos = pos;
   g.rope = e->rope;
   g.max_positions = c.max_position_embeddings;
   g.zero_pad_rows = zero_pad_rows ? 1 : 0;
+  auto operands = [&](const void* x, const void* wbf, size_t off8, int t) {
+    g.x = x;
+    g.w = fp8 ? (const void*)(w8 + off8) : wbf;
+    g.x_scale = fp8 ? as + t : nullptr;
+    g.w_scale = fp8 ? wsc + t : nullptr;
+  };
 
-  g.x = ln1; g.w = (const bf16_t*)w->w_qkv; g.bias = (const bf16_t*)w->b_qkv; g.res = nullptr; g.y = qkv;
+  operands(ln1, w->w_qkv, wo.qkv, 0);
+  g.bias = (const bf16_t*)w->b_qkv; g.res = nullptr; g.y = qkv;
   g.N = 3 * H; g.K = H;
   s = timed(e, ESM_K_GEMM_QKV, st, "qkv gemm", [&] { return launch_gemm(EPI_QKV_ROPE, g, st); });
   if (s) return s;
 
   AttnArgs aa{};
   aa.qkv = qkv; aa.ctx = ctx;
+  aa.ctx8 = q8(ctx, 1, nullptr);
   aa.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
   aa.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
   aa.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
@@ -245,25 +366,41 @@ esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, const bf16_t* x
   s = timed(e, ESM_K_ATTENTION, st, "attention", [&] { return launch_attention(aa, st); });
   if (s) return s;
 
-  g.x = ctx; g.w = (const bf16_t*)w->w_out; g.bias = (const bf16_t*)w->b_out; g.res = x_in; g.y = x1;
+  operands(ctx, w->w_out, wo.out, 1);
+  g.bias = (const bf16_t*)w->b_out; g.res = x_in; g.y = x1;
   g.N = H; g.K = H;
   s = timed(e, ESM_K_GEMM_OUT, st, "out-proj gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
   if (s) return s;
 
   s = timed(e, ESM_K_LAYERNORM, st, "layernorm 2", [&] {
     return launch_layernorm(x1, (const bf16_t*)w->ln2_gamma, (const bf16_t*)w->ln2_beta, ln2, rows, H,
-                            c.layer_norm_eps, st);
+                            c.layer_norm_eps, q8(ln2, 2, pos), st);
   });
   if (s) return s;
 
-  g.x = ln2; g.w = (const bf16_t*)w->w_fc1; g.bias = (const bf16_t*)w->b_fc1; g.res = nullptr; g.y = act;
+  operands(ln2, w->w_fc1, wo.fc1, 2);
+  g.bias = (const bf16_t*)w->b_fc1; g.res = nullptr; g.y = act;
+  if (fp8) {
+    g.y8 = (uint8_t*)act;
+    g.y8_scale = as + 3;
+    g.y8_amax = am + 3;
+  }
   g.N = F; g.K = H;
-  s = timed(e, ESM_K_GEMM_FC1, st, "fc1 gemm", [&] { return launch_gemm(EPI_BIAS_GELU, g, st); });
+  s = timed(e, ESM_K_GEMM_FC1, st, "fc1 gemm",
+            [&] { return launch_gemm(fp8 ? EPI_BIAS_GELU_E4M3 : EPI_BIAS_GELU, g, st); });
   if (s) return s;
 
-  g.x = act; g.w = (const bf16_t*)w->w_fc2; g.bias = (const bf16_t*)w->b_fc2; g.res = x1; g.y = x_out;
+  operands(act, w->w_fc2, wo.fc2, 3);
+  g.bias = (const bf16_t*)w->b_fc2; g.res = x1; g.y = x_out;
   g.N = H; g.K = F;
   return timed(e, ESM_K_GEMM_FC2, st, "fc2 gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
+}
+
+// FP8: the call was one step for the layers it ran; roll their histories.
+esm_status end_of_step(esm_encoder* e, int nlayers, int32_t layer_idx, hipStream_t st) {
+  if (!is_fp8(e) || nlayers == 0) return ok();
+  const int32_t l0 = layer_idx >= 0 ? layer_idx : 0;
+  return timed(e, ESM_K_FP8, st, "fp8 scale update", [&] { return launch_scale_update(e->f8, l0, nlayers, st); });
 }
 
 esm_status check_cu_host(const esm_encoder* e, const int32_t* cu, int32_t B, int64_t T, int32_t max_seqlen) {
@@ -293,8 +430,10 @@ esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, 
   }
   if (!cu_dev) return fail(ESM_ERR_NULL, "cu_seqlens_dev is NULL");
   if (!w && nlayers > 0) return fail(ESM_ERR_NULL, "weights are NULL");
-  for (int l = 0; l < nlayers; ++l)
+  for (int l = 0; l < nlayers; ++l) {
     if ((s = check_weights(&w[l], layer_idx >= 0 ? layer_idx : l))) return s;
+    if (is_fp8(e) && (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l))) return s;
+  }
   if ((s = check_cu_host(e, cu_host, B, T, max_seqlen))) return s;
   if (T == 0 || B == 0) return ok();
   Plan p;
@@ -311,10 +450,11 @@ esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, 
     cur = (const bf16_t*)x_out;
   }
   for (int l = 0; l < nlayers; ++l) {
-    if ((s = run_layer(e, &w[l], cur, (bf16_t*)x_out, T, B, false, ws, p, st))) return s;
+    if ((s = run_layer(e, &w[l], layer_idx >= 0 ? layer_idx : l, cur, (bf16_t*)x_out, T, B, false, ws, p, st)))
+      return s;
     cur = (const bf16_t*)x_out;
   }
-  return ok();
+  return end_of_step(e, nlayers, layer_idx, st);
 }
 
 esm_status forward_bshd(esm_encoder* e, const esm_layer_weights* w, int nlayers, int32_t layer_idx,
@@ -339,8 +479,10 @@ esm_status forward_bshd(esm_encoder* e, const esm_layer_weights* w, int nlayers,
   }
   if (!sl_dev) return fail(ESM_ERR_NULL, "seqlens_dev is NULL");
   if (!w && nlayers > 0) return fail(ESM_ERR_NULL, "weights are NULL");
-  for (int l = 0; l < nlayers; ++l)
+  for (int l = 0; l < nlayers; ++l) {
     if ((s = check_weights(&w[l], layer_idx >= 0 ? layer_idx : l))) return s;
+    if (is_fp8(e) && (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l))) return s;
+  }
   if (sl_host && (s = esm_check_seqlens(sl_host, B, S, e->cfg.max_position_embeddings))) return s;
   if (rows == 0) return ok();
   Plan p;
@@ -357,10 +499,11 @@ esm_status forward_bshd(esm_encoder* e, const esm_layer_weights* w, int nlayers,
     cur = (const bf16_t*)x_out;
   }
   for (int l = 0; l < nlayers; ++l) {
-    if ((s = run_layer(e, &w[l], cur, (bf16_t*)x_out, rows, B, true, ws, p, st))) return s;
+    if ((s = run_layer(e, &w[l], layer_idx >= 0 ? layer_idx : l, cur, (bf16_t*)x_out, rows, B, true, ws, p, st)))
+      return s;
     cur = (const bf16_t*)x_out;
   }
-  return ok();
+  return end_of_step(e, nlayers, layer_idx, st);
 }
 
 }  // namespace
@@ -416,6 +559,10 @@ esm_status esm_encoder_create(const esm_config* cfg, int device, esm_encoder** o
     delete e;
     return hip_fail(err, "rotary table");
   }
+  if (is_fp8(e) && (s = fp8_create(e)) != ESM_OK) {
+    esm_encoder_destroy(e);
+    return s;
+  }
   *out = e;
   return ok();
 }
@@ -424,6 +571,8 @@ esm_status esm_encoder_destroy(esm_encoder* e) {
   if (!e) return ESM_OK;
   (void)hipSetDevice(e->device);
   if (e->rope) (void)hipFree(e->rope);
+  if (e->fp8_mem) (void)hipFree(e->fp8_mem);
+  if (e->w8) (void)hipFree(e->w8);
   for (hipEvent_t ev : e->pool) (void)hipEventDestroy(ev);
   delete e;
   return ESM_OK;
@@ -533,7 +682,8 @@ esm_status esm_linear_fwd(esm_encoder* e, const void* x, const void* w, const vo
   if (M == 0) return ok();
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
   GemmArgs g{};
-  g.x = (const bf16_t*)x; g.w = (const bf16_t*)w; g.bias = (const bf16_t*)b; g.res = (const bf16_t*)res;
+  g.dtype = kBF16;
+  g.x = x; g.w = w; g.bias = (const bf16_t*)b; g.res = (const bf16_t*)res;
   g.y = (bf16_t*)y; g.M = M; g.N = N; g.K = K;
   const int kind = epi == ESM_EPI_BIAS ? EPI_BIAS : (epi == ESM_EPI_BIAS_GELU ? EPI_BIAS_GELU : EPI_BIAS_RESIDUAL);
   return timed(e, ESM_K_OTHER, (hipStream_t)stream, "linear", [&] { return launch_gemm(kind, g, (hipStream_t)stream); });
@@ -550,8 +700,146 @@ esm_status esm_layernorm_fwd(esm_encoder* e, const void* x, const void* gamma, c
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
   return timed(e, ESM_K_LAYERNORM, (hipStream_t)stream, "layernorm", [&] {
     return launch_layernorm((const bf16_t*)x, (const bf16_t*)gamma, (const bf16_t*)beta, (bf16_t*)y, M,
-                            e->cfg.hidden_size, e->cfg.layer_norm_eps, (hipStream_t)stream);
+                            e->cfg.hidden_size, e->cfg.layer_norm_eps, E4m3Out{nullptr, nullptr, nullptr, nullptr},
+                            (hipStream_t)stream);
   });
+}
+
+esm_status esm_linear_e4m3_fwd(esm_encoder* e, const void* x8, const float* x_scale, const void* w8,
+                               const float* w_scale, const void* b, const void* res, void* y, const float* y_scale,
+                               uint32_t* y_amax, int64_t M, int32_t N, int32_t K, int32_t epi, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !x8 || !w8 || !y || !x_scale || !w_scale) return fail(ESM_ERR_NULL, "NULL argument");
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 128)
+    return fail(ESM_ERR_SHAPE, "M %lld N %d K %d: N must be a positive multiple of 64, K of 128", (long long)M, N, K);
+  if (epi < ESM_EPI_BIAS || epi > ESM_EPI_BIAS_GELU_E4M3) return fail(ESM_ERR_UNSUPPORTED, "epilogue %d", epi);
+  if (epi == ESM_EPI_BIAS_RESIDUAL && !res) return fail(ESM_ERR_NULL, "residual is NULL");
+  if (epi == ESM_EPI_BIAS_GELU_E4M3 && (!y_scale || !y_amax)) return fail(ESM_ERR_NULL, "output scale or amax NULL");
+  if (!aligned16(x8) || !aligned16(w8) || !aligned16(y) || (res && !aligned16(res)) || (b && ((uintptr_t)b & 7u)))
+    return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer");
+  if (M == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  GemmArgs g{};
+  g.dtype = kE4M3;
+  g.x = x8; g.w = w8; g.x_scale = x_scale; g.w_scale = w_scale;
+  g.bias = (const bf16_t*)b; g.res = (const bf16_t*)res;
+  g.M = M; g.N = N; g.K = K;
+  int kind = EPI_BIAS;
+  if (epi == ESM_EPI_BIAS_GELU) kind = EPI_BIAS_GELU;
+  if (epi == ESM_EPI_BIAS_RESIDUAL) kind = EPI_BIAS_RESIDUAL;
+  if (epi == ESM_EPI_BIAS_GELU_E4M3) {
+    kind = EPI_BIAS_GELU_E4M3;
+    g.y8 = (uint8_t*)y; g.y8_scale = y_scale; g.y8_amax = y_amax;
+  } else {
+    g.y = (bf16_t*)y;
+  }
+  return timed(e, ESM_K_OTHER, (hipStream_t)stream, "linear e4m3", [&] { return launch_gemm(kind, g, (hipStream_t)stream); });
+}
+
+esm_status esm_fp8_prepare_layer(esm_encoder* e, int32_t layer_idx, const esm_layer_weights* w, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  if (!is_fp8(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
+  if (layer_idx < 0 || layer_idx >= e->cfg.num_hidden_layers)
+    return fail(ESM_ERR_SHAPE, "layer_idx %d outside [0, %d)", layer_idx, e->cfg.num_hidden_layers);
+  esm_status s = check_weights(w, layer_idx);
+  if (s) return s;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  const esm_config& c = e->cfg;
+  const int64_t H = c.hidden_size, F = c.intermediate_size;
+  const W8Off wo = w8_offsets(c);
+  uint8_t* w8 = e->w8 + (size_t)layer_idx * e->w8_layer;
+  uint32_t* wam = e->f8.w_amax + 4 * layer_idx;
+  float* wsc = e->f8.w_scale + 4 * layer_idx;
+  const bf16_t* src[4] = {(const bf16_t*)w->w_qkv, (const bf16_t*)w->w_out, (const bf16_t*)w->w_fc1,
+                          (const bf16_t*)w->w_fc2};
+  const int64_t n[4] = {3 * H * H, H * H, F * H, H * F};
+  const size_t off[4] = {wo.qkv, wo.out, wo.fc1, wo.fc2};
+  HIP_TRY(hipMemsetAsync(wam, 0, 4 * sizeof(uint32_t), st), "hipMemsetAsync");
+  for (int i = 0; i < 4; ++i) {
+    s = timed(e, ESM_K_FP8, st, "weight amax", [&] { return launch_amax_bf16(src[i], n[i], wam + i, st); });
+    if (s) return s;
+    s = timed(e, ESM_K_FP8, st, "weight cast",
+              [&] { return launch_quantize_weight(src[i], n[i], wam + i, w8 + off[i], wsc + i, st); });
+    if (s) return s;
+  }
+  e->prepared[(size_t)layer_idx] = 1;
+  return ok();
+}
+
+static esm_status check_state_arg(const esm_encoder* e, const esm_fp8_state* st) {
+  if (!e || !st) return fail(ESM_ERR_NULL, "encoder or state is NULL");
+  if (!is_fp8(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
+  if (st->num_layers != e->cfg.num_hidden_layers || st->history_len != e->cfg.amax_history_len)
+    return fail(ESM_ERR_SHAPE, "state is for %d layers x history %d; the encoder has %d x %d", st->num_layers,
+                st->history_len, e->cfg.num_hidden_layers, e->cfg.amax_history_len);
+  return ok();
+}
+
+esm_status esm_fp8_get_state(esm_encoder* e, esm_fp8_state* st, esm_stream_t stream) {
+  g_last_error.clear();
+  esm_status s = check_state_arg(e, st);
+  if (s) return s;
+  if (!st->act_scale || !st->amax_history || !st->steps || !st->weight_scale)
+    return fail(ESM_ERR_NULL, "state arrays are NULL");
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  const size_t L = (size_t)st->num_layers, HL = (size_t)st->history_len;
+  if (L > 0) {
+    HIP_TRY(hipMemcpy(st->act_scale, e->f8.act_scale, L * 4 * sizeof(float), hipMemcpyDeviceToHost), "fp8 state");
+    HIP_TRY(hipMemcpy(st->amax_history, e->f8.history, L * 4 * HL * sizeof(float), hipMemcpyDeviceToHost), "fp8 state");
+    HIP_TRY(hipMemcpy(st->steps, e->f8.steps, L * sizeof(int64_t), hipMemcpyDeviceToHost), "fp8 state");
+    HIP_TRY(hipMemcpy(st->weight_scale, e->f8.w_scale, L * 4 * sizeof(float), hipMemcpyDeviceToHost), "fp8 state");
+  }
+  uint32_t flags = 0;
+  HIP_TRY(hipMemcpy(&flags, e->f8.flags, sizeof flags, hipMemcpyDeviceToHost), "fp8 state");
+  st->nonfinite = flags & 1u;
+  return ok();
+}
+
+esm_status esm_fp8_set_state(esm_encoder* e, const esm_fp8_state* st, esm_stream_t stream) {
+  g_last_error.clear();
+  esm_status s = check_state_arg(e, st);
+  if (s) return s;
+  if (!st->act_scale || !st->amax_history || !st->steps) return fail(ESM_ERR_NULL, "state arrays are NULL");
+  const size_t L = (size_t)st->num_layers, HL = (size_t)st->history_len;
+  for (size_t i = 0; i < L * 4; ++i)
+    if (!(st->act_scale[i] > 0.f) || !isfinite(st->act_scale[i]))
+      return fail(ESM_ERR_SHAPE, "act_scale[%zu] = %g is not positive and finite", i, (double)st->act_scale[i]);
+  for (size_t i = 0; i < L; ++i)
+    if (st->steps[i] < 0) return fail(ESM_ERR_SHAPE, "steps[%zu] < 0", i);
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  if (L > 0) {
+    HIP_TRY(hipMemcpy(e->f8.act_scale, st->act_scale, L * 4 * sizeof(float), hipMemcpyHostToDevice), "fp8 state");
+    HIP_TRY(hipMemcpy(e->f8.history, st->amax_history, L * 4 * HL * sizeof(float), hipMemcpyHostToDevice), "fp8 state");
+    HIP_TRY(hipMemcpy(e->f8.steps, st->steps, L * sizeof(int64_t), hipMemcpyHostToDevice), "fp8 state");
+    HIP_TRY(hipMemset(e->f8.act_amax, 0, L * 4 * sizeof(uint32_t)), "fp8 state");
+  }
+  const uint32_t flags = st->nonfinite ? 1u : 0u;
+  HIP_TRY(hipMemcpy(e->f8.flags, &flags, sizeof flags, hipMemcpyHostToDevice), "fp8 state");
+  return ok();
+}
+
+esm_status esm_fp8_reset(esm_encoder* e, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  if (!is_fp8(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  return fp8_reset_state(e);
+}
+
+esm_status esm_fp8_quantize(esm_encoder* e, const float* x, int64_t n, const float* scale, void* y, uint32_t* amax,
+                            esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !x || !scale || !y || !amax) return fail(ESM_ERR_NULL, "NULL argument");
+  if (n < 0) return fail(ESM_ERR_SHAPE, "n < 0");
+  if (n == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  return timed(e, ESM_K_FP8, (hipStream_t)stream, "e4m3 cast",
+               [&] { return launch_quantize_f32(x, n, scale, (uint8_t*)y, amax, (hipStream_t)stream); });
 }
 
 esm_status esm_profile_enable(esm_encoder* e, int32_t on) {

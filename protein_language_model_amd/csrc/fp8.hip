@@ -1,0 +1,117 @@
+// Delayed-scaling FP8 bookkeeping for gfx950: weight casts, the cast test
+// hook and the end-of-step scale update.
+//
+// Per-tensor delayed scaling ([BIO-ACC] 2.1 and 4.1; [TE-RU] FP8 recipe
+// section: amax history of 16 steps, "max" algorithm): every FP8 tensor has a
+// scale s; a step casts x * s to E4M3 with the scale fixed before the step,
+// records amax = max |x| on the side, and at the end of the step the amax
+// enters a ring buffer of the last history_len steps and s becomes
+// 448 / max(history).  A maximum that is zero or not finite keeps the previous
+// scale (initially 1).  Weights are cast once with s_w = 448 / amax(W).
+#include "common.h"
+
+namespace esm {
+
+namespace {
+
+__device__ __forceinline__ bool finite_pos(float v) { return v > 0.f && v < __builtin_inff(); }
+
+__global__ __launch_bounds__(256) void k_amax_bf16(const bf16_t* __restrict__ x, int64_t n8, uint32_t* amax) {
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4 w = *(const u32x4*)(x + i * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bflo(w[e])), fabsf(bfhi(w[e]))));
+  }
+  record_amax(amax, m);
+}
+
+__global__ __launch_bounds__(256) void k_quantize_weight(const bf16_t* __restrict__ x, int64_t n8,
+                                                         const uint32_t* __restrict__ amax, uint8_t* __restrict__ y,
+                                                         float* scale_out) {
+  const float am = __uint_as_float(*amax);
+  const float s = finite_pos(am) ? kE4M3Max / am : 1.0f;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) *scale_out = s;
+  if (i >= n8) return;
+  const u32x4 w = *(const u32x4*)(x + i * 8);
+  const float lo[4] = {bflo(w[0]), bfhi(w[0]), bflo(w[1]), bfhi(w[1])};
+  const float hi[4] = {bflo(w[2]), bfhi(w[2]), bflo(w[3]), bfhi(w[3])};
+  *(u32x2*)(y + i * 8) = u32x2{pack_e4m3x4(lo, s), pack_e4m3x4(hi, s)};
+}
+
+__global__ __launch_bounds__(256) void k_quantize_f32(const float* __restrict__ x, int64_t n,
+                                                      const float* __restrict__ scale, uint8_t* __restrict__ y,
+                                                      uint32_t* amax) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float m = 0.f;
+  if (i < n) {
+    const float v[4] = {x[i], 0.f, 0.f, 0.f};
+    y[i] = (uint8_t)(pack_e4m3x4(v, scale[0]) & 0xFFu);
+    m = fabsf(x[i]);
+  }
+  record_amax(amax, m);
+}
+
+// One thread per layer: its four activation tensors share the step counter.
+__global__ void k_scale_update(Fp8State s, int32_t l0, int32_t nl) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= nl) return;
+  const int l = l0 + idx;
+  const int HL = s.history_len;
+  const int slot = (int)(s.steps[l] % HL);
+  bool nonfinite = false;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int k = 4 * l + t;
+    const float am = __uint_as_float(s.act_amax[k]);
+    if (!(am < __builtin_inff())) nonfinite = true;  // Inf or NaN bits
+    float* h = s.history + (int64_t)k * HL;
+    h[slot] = am;
+    float mx = 0.f;
+    bool ok = true;
+    for (int j = 0; j < HL; ++j) {
+      const float v = h[j];
+      ok = ok && v < __builtin_inff() && v == v;
+      mx = fmaxf(mx, v);
+    }
+    if (ok && mx > 0.f) s.act_scale[k] = kE4M3Max / mx;
+    s.act_amax[k] = 0u;
+  }
+  s.steps[l] += 1;
+  if (nonfinite) atomicOr(s.flags, 1u);
+}
+
+}  // namespace
+
+hipError_t launch_amax_bf16(const bf16_t* x, int64_t n, uint32_t* amax, hipStream_t st) {
+  const int64_t n8 = n / 8;
+  if (n8 <= 0) return hipSuccess;
+  int64_t blocks = (n8 + 255) / 256;
+  blocks = blocks < 2048 ? blocks : 2048;
+  hipLaunchKernelGGL(k_amax_bf16, dim3((unsigned)blocks), dim3(256), 0, st, x, n8, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight(const bf16_t* x, int64_t n, const uint32_t* amax, uint8_t* y, float* scale_out,
+                                  hipStream_t st) {
+  const int64_t n8 = n / 8;
+  const int64_t blocks = n8 > 0 ? (n8 + 255) / 256 : 1;
+  hipLaunchKernelGGL(k_quantize_weight, dim3((unsigned)blocks), dim3(256), 0, st, x, n8, amax, y, scale_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_f32(const float* x, int64_t n, const float* scale, uint8_t* y, uint32_t* amax,
+                               hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_quantize_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, n, scale, y, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_update(const Fp8State& s, int32_t l0, int32_t nl, hipStream_t st) {
+  if (nl <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_scale_update, dim3((unsigned)((nl + 63) / 64)), dim3(64), 0, st, s, l0, nl);
+  return hipGetLastError();
+}
+
+}  // namespace esm

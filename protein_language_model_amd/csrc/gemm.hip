@@ -1,28 +1,31 @@
-// bf16 MFMA GEMM for gfx950 with fused epilogues:  y = epi(x[M,K] . w[N,K]^T + b)
+// MFMA GEMM for gfx950 with fused epilogues:  y = epi(x[M,K] . w[N,K]^T + b)
 //
 // The four linears of a pre-LN encoder layer ([BIO-ACC] 3.1: QKV projection,
 // attention output projection, fc1, fc2; [TE-RU] LayerNormLinear / LayerNormMLP)
 // are all "both operands K-contiguous" products, so both MFMA operands are read
-// from LDS as 16-byte runs along K.
+// from LDS as 16-byte runs along K.  Operands are bf16, or OCP E4M3 with one
+// scale per tensor for the delayed-scaling FP8 recipe ([BIO-ACC] 2.1 and 4.1;
+// [TE-RU] FP8 recipe section): y = (qx . qw^T) / (s_x s_w) + b.
 //
 // Design (CDNA4):
 //  * WAVES_M x WAVES_N waves (8 = two per SIMD: one wave's LDS reads and
 //    waits overlap the other's MFMAs); each wave owns a (BM/WAVES_M) x
-//    (BN/WAVES_N) tile built from 32x32 blocks of v_mfma_f32_32x32x16_bf16
-//    with fp32 accumulators.
+//    (BN/WAVES_N) tile built from 32x32 blocks, v_mfma_f32_32x32x16_bf16 for
+//    bf16 and v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, unit block
+//    scales) for FP8, with fp32 accumulators.
 //  * The weight is MFMA operand A and the activations operand B, so lane l of
 //    a 32x32 block holds output row m = l%32 and columns
 //    n = 8*(r/4) + 4*(l/32) + r%4 (r = 0..15): four consecutive columns per
 //    register group.  Columns j and j+32 of a 64-wide group sit in the same
 //    lane and register of two adjacent blocks, which is what the rotary
 //    epilogue needs ([TE-ESM2] 旋转位置编码集成: rotate-half pairs (i, i+32)).
-//  * K step 64; tiles live in LDS twice (double buffer) with a 16-byte-chunk XOR
-//    swizzle (chunk c of row r stored at c ^ ((r >> 1) & 7)): the 16 lanes that
+//  * A K step is 128 bytes of each row (64 bf16 or 128 E4M3 values); tiles
+//    live in LDS twice (double buffer) with a 16-byte-chunk XOR swizzle (chunk c of row r stored at c ^ ((r >> 1) & 7)): the 16 lanes that
 //    one LDS cycle serves read 16 rows of one column and hit 16 distinct
 //    16-byte bank groups of the 64-bank LDS.  The next K step is
 //    fetched straight into the other LDS buffer (global_load_lds, no staging
 //    registers) while the current one is multiplied.  MFMA fragments are
-//    double-buffered in registers across the four 16-wide k sub-steps, and the
+//    double-buffered in registers across the k sub-steps, and the
 //    single barrier per K step sits before the last sub-step, so the next
 //    tile's first fragments load under MFMAs.
 //  * Rows beyond M and weight rows beyond N are clamped on load (never read out
@@ -38,6 +41,9 @@ namespace {
 
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
+constexpr int kRowBytes = 128;  // bytes of each tile row per K step
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Direct-to-LDS 16-byte load: lane i's 16 bytes from g land at LDS byte
 // lds_base + 16 i (lds_base must be wave-uniform; it goes through M0).  Issued
@@ -73,28 +79,44 @@ __device__ __forceinline__ float gelu_erf(float z) {
   return 0.5f * z * (1.0f + erf_as7126(z * 0.70710678118654752f));
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int kBK, int MINB, int EPI>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void k_gemm(GemmArgs a) {
+template <int DT>
+struct Frag;
+template <>
+struct Frag<kBF16> {
+  typedef bf16x8 T;  // 8 bf16 along K: one 16-wide sub-step
+  static constexpr int kSub = 16;
+};
+template <>
+struct Frag<kE4M3> {
+  typedef i32x8 T;  // 32 E4M3 along K: one 64-wide sub-step
+  static constexpr int kSub = 64;
+};
+
+template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int DT>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) {
+  typedef typename Frag<DT>::T frag_t;
+  constexpr int ES = DT == kE4M3 ? 1 : 2;       // operand bytes per element
+  constexpr int kBK = kRowBytes / ES;           // K per step, in elements
+  constexpr int KK = kBK / Frag<DT>::kSub;      // k sub-steps per K step
+  constexpr int FB = Frag<DT>::kSub * ES / 32;  // 16-byte chunks per lane per fragment
   constexpr int NW = WAVES_M * WAVES_N;
-  constexpr int KK = kBK / 16;         // 16-wide k sub-steps per K step
-  constexpr int CR = kBK / 8;          // 16-byte chunks per LDS row
-  constexpr int RW = 256 / (kBK * 2);  // LDS rows per 256-byte bank window
-  constexpr int RPI = 1024 / (kBK * 2);  // rows filled by one 1 KB direct load
   constexpr int WTM = BM / WAVES_M;
   constexpr int WTN = BN / WAVES_N;
   constexpr int FM = WTM / 32;
   constexpr int FN = WTN / 32;
-  constexpr int XRB = BM / (RPI * NW);  // RPI-row blocks of the x tile per wave
+  constexpr int RPI = 1024 / kRowBytes;         // tile rows filled by one 1 KB direct load
+  constexpr int XRB = BM / (RPI * NW);          // such row blocks of the x tile per wave
   constexpr int WRB = BN / (RPI * NW);
-  constexpr int kStage = (BM + BN) * kBK;
+  constexpr int kStage = (BM + BN) * kRowBytes;  // bytes per K-step stage
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(XRB * RPI * NW == BM && WRB * RPI * NW == BN, "tile rows must split evenly over the waves");
-  static_assert(KK % 2 == 0, "fragment double buffering alternates over an even number of sub-steps");
+  static_assert(DT == kE4M3 || KK % 2 == 0, "fragment double buffering alternates over an even number of sub-steps");
   static_assert(EPI != EPI_QKV_ROPE || (FN % 2 == 0 && WTN % 64 == 0), "rotary pairs need 64-wide wave columns");
+  static_assert(EPI != EPI_BIAS_GELU_E4M3 || DT == kE4M3, "E4M3 output is built for E4M3 operands");
 
   // Two K-step stages; after the K loop the same memory stages the output tile.
-  constexpr int kSmem = 2 * kStage > BM * BN ? 2 * kStage : BM * BN;
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[kSmem];
+  constexpr int kSmem = 2 * kStage > BM * BN * 2 ? 2 * kStage : BM * BN * 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem];
 
   const int64_t M = a.M;
   const int N = a.N, K = a.K;
@@ -122,49 +144,61 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void k_gemm(GemmArgs 
   const int lrow = lane & 31, lhalf = lane >> 5;
 
   // Direct-to-LDS tile loads.  One global_load_lds_dwordx4 fills 1 KB of LDS
-  // (RPI rows of kBK bf16), lane i writing bytes [16 i, 16 i + 16).  Lane i of
-  // a wave therefore fetches row r = RPI*rb + i/CR at the logical chunk that
-  // the swizzle stores in physical chunk i%CR: c = (i%CR) ^ ((r / RW) % CR).
-  // With rb = wave + NW*i (NW even), (r / RW) % CR depends on the lane and on
-  // wave & 1 only.
-  const int lr8 = lane / CR;
-  const int lchunk = ((lane % CR) ^ (((((wave & 1) * RPI) + lr8) / RW) % CR)) * 8;
-  const bf16_t* xsrc[XRB];
-  const bf16_t* wsrc[WRB];
+  // (8 rows of 128 bytes), lane i writing bytes [16 i, 16 i + 16).  Lane i of
+  // a wave therefore fetches row r = 8*rb + i/8 at the logical chunk that the
+  // swizzle stores in physical chunk i%8: c = (i%8) ^ ((r >> 1) & 7), and
+  // (r >> 1) & 7 = 4*(rb & 1) + i/16 with rb & 1 = wave & 1 (rb = wave + NW*j,
+  // NW even).
+  const int lr8 = lane >> 3;
+  const int lchunk = ((lane & 7) ^ (((wave & 1) << 2) | (lane >> 4))) * 16;  // bytes
+  const unsigned char* xsrc[XRB];
+  const unsigned char* wsrc[WRB];
 #pragma unroll
   for (int i = 0; i < XRB; ++i) {
     int64_t r = m0 + (int64_t)(wave + NW * i) * RPI + lr8;
     r = r < M ? r : M - 1;
-    xsrc[i] = a.x + r * K + lchunk;
+    xsrc[i] = (const unsigned char*)a.x + r * K * ES + lchunk;
   }
 #pragma unroll
   for (int i = 0; i < WRB; ++i) {
     int r = n0 + (wave + NW * i) * RPI + lr8;
     r = r < N ? r : N - 1;
-    wsrc[i] = a.w + (int64_t)r * K + lchunk;
+    wsrc[i] = (const unsigned char*)a.w + (int64_t)r * K * ES + lchunk;
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
-  auto issue_tile = [&](int k0, int buf) {
-    const uint32_t base = lds0 + (uint32_t)(buf * kStage) * 2u;
+  auto issue_tile = [&](int kbyte, int buf) {
+    const uint32_t base = lds0 + (uint32_t)(buf * kStage);
 #pragma unroll
-    for (int i = 0; i < XRB; ++i) lds_dma16(xsrc[i] + k0, base + (uint32_t)((wave_u + NW * i) * RPI * kBK) * 2u);
+    for (int i = 0; i < XRB; ++i) lds_dma16(xsrc[i] + kbyte, base + (uint32_t)((wave_u + NW * i) * RPI * kRowBytes));
 #pragma unroll
-    for (int i = 0; i < WRB; ++i) lds_dma16(wsrc[i] + k0, base + (uint32_t)((BM + (wave_u + NW * i) * RPI) * kBK) * 2u);
+    for (int i = 0; i < WRB; ++i)
+      lds_dma16(wsrc[i] + kbyte, base + (uint32_t)((BM + (wave_u + NW * i) * RPI) * kRowBytes));
   };
 
   // Fragment reads: row r of the tile, logical 16-byte chunk ch, stored at
-  // physical chunk ch ^ ((r / RW) % CR); every row this lane reads has
-  // (r / RW) % CR = ((lane % 32) / RW) % CR.
-  const int swz = (lrow / RW) % CR;
-  auto load_frags = [&](bf16x8 (&xf)[FM], bf16x8 (&wf)[FN], int buf, int kk) {
-    const bf16_t* sx = smem + buf * kStage;
-    const bf16_t* sw = sx + BM * kBK;
-    const int ch = ((kk * 2 + lhalf) ^ swz) * 8;
+  // physical chunk ch ^ ((r >> 1) & 7); every row this lane reads has
+  // (r >> 1) & 7 = ((lane % 32) >> 1) & 7.  Sub-step kk covers the chunks
+  // [2 FB kk, 2 FB (kk + 1)); lane half h takes FB consecutive ones.  A and B
+  // fragments use the same chunk-to-k assignment, so the MFMA contracts
+  // matching k.
+  const int swz = (lrow >> 1) & 7;
+  auto read_frag = [&](const unsigned char* rowp, int kk) -> frag_t {
+    if constexpr (FB == 1) {
+      return *(const frag_t*)(rowp + (((kk * 2 + lhalf) ^ swz) * 16));
+    } else {
+      const u32x4 lo = *(const u32x4*)(rowp + (((kk * 4 + lhalf * 2) ^ swz) * 16));
+      const u32x4 hi = *(const u32x4*)(rowp + (((kk * 4 + lhalf * 2 + 1) ^ swz) * 16));
+      return __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto load_frags = [&](frag_t (&xf)[FM], frag_t (&wf)[FN], int buf, int kk) {
+    const unsigned char* sx = smem + buf * kStage;
+    const unsigned char* sw = sx + BM * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) xf[i] = *(const bf16x8*)(sx + (wm * WTM + i * 32 + lrow) * kBK + ch);
+    for (int i = 0; i < FM; ++i) xf[i] = read_frag(sx + (wm * WTM + i * 32 + lrow) * kRowBytes, kk);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) wf[j] = *(const bf16x8*)(sw + (wn * WTN + j * 32 + lrow) * kBK + ch);
+    for (int j = 0; j < FN; ++j) wf[j] = read_frag(sw + (wn * WTN + j * 32 + lrow) * kRowBytes, kk);
   };
 
   f32x16 acc[FM][FN];
@@ -175,24 +209,50 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void k_gemm(GemmArgs 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto mfma_step = [&](const bf16x8 (&xf)[FM], const bf16x8 (&wf)[FN]) {
+  auto mfma_step = [&](const frag_t (&xf)[FM], const frag_t (&wf)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (DT == kE4M3)
+          // cbsz = blgp = 0: both operands E4M3; block scales 127 = 2^0.
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 0, 0, 0, 127, 0, 127);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+      }
   };
 
   const int nk = K / kBK;
-  bf16x8 xf[2][FM], wf[2][FN];
   issue_tile(0, 0);
   vm_wait_all();
   __syncthreads();
+  if constexpr (DT == kE4M3) {
+    // One fragment set (8 registers per 32-byte fragment; a second set would
+    // not fit beside the 128 accumulators at two waves per SIMD): the other
+    // wave on the SIMD multiplies while this one waits for its LDS reads.
+    frag_t xf[FM], wf[FN];
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) issue_tile((kt + 1) * kRowBytes, cur ^ 1);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(xf, wf, cur, kk);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(xf, wf);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // Next tile landed for every wave; every wave is done reading this one.
+      vm_wait_all();
+      __syncthreads();
+    }
+  } else {
+  frag_t xf[2][FM], wf[2][FN];
   load_frags(xf[0], wf[0], 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
-    if (more) issue_tile((kt + 1) * kBK, cur ^ 1);
+    if (more) issue_tile((kt + 1) * kRowBytes, cur ^ 1);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
@@ -210,22 +270,33 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void k_gemm(GemmArgs 
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  }
 
   // ------------------------------------------------------------ epilogue
-  // Each wave stages its (WTM x WTN) bf16 result tile in LDS (free once every
-  // wave is past the K loop), so that global memory is written (and, for the
+  // Each wave stages its (WTM x WTN) result tile in LDS (free once every wave
+  // is past the K loop), so that global memory is written (and, for the
   // residual, read) in full rows with 16-byte lanes.  Staged rows hold CPR
-  // 16-byte chunks, chunk c of row r stored at c ^ ((r / (16 / CPR)) % CPR),
-  // which spreads the row-per-lane accesses of the MFMA layout over the banks.
-  constexpr int CPR = WTN / 8;
-  constexpr int RPW = 16 / CPR;           // staged rows per 256-byte bank window
-  constexpr int PASSES = WTM * CPR / 64;  // 16-byte transfers per lane
+  // 16-byte chunks, chunk c of row r stored at c ^ ((r / RPW) % CPR), which
+  // spreads the row-per-lane accesses of the MFMA layout over the banks.
+  // E4M3 operands: the accumulators are first divided by s_x s_w.  E4M3
+  // output: the GELU values are cast with the output's scale, and their amax
+  // (before the cast) is recorded.
+  constexpr bool OUT8 = EPI == EPI_BIAS_GELU_E4M3;
+  constexpr int OES = OUT8 ? 1 : 2;               // output bytes per element
+  constexpr int CPR = WTN * OES / 16;             // 16-byte chunks per staged row
+  constexpr int RPW = CPR >= 16 ? 1 : 16 / CPR;   // staged rows per 256-byte bank window
+  constexpr int PASSES = WTM * CPR / 64;          // 16-byte transfers per lane
+  constexpr int EPC = 16 / OES;                   // output elements per chunk
   __syncthreads();
-  bf16_t* stage = smem + wave * (WTM * WTN);
-  auto soff = [&](int row, int chunk) { return row * WTN + ((chunk ^ ((row / RPW) & (CPR - 1))) * 8); };
+  unsigned char* stage = smem + wave * (WTM * WTN * OES);
+  auto soff = [&](int row, int chunk) { return row * (WTN * OES) + ((chunk ^ ((row / RPW) & (CPR - 1))) * 16); };
   const int64_t mw = m0 + wm * WTM;
   const int nw = n0 + wn * WTN;
   const bf16_t* __restrict__ bias = a.bias;
+  float dq = 1.0f;
+  if constexpr (DT == kE4M3) dq = 1.0f / (a.x_scale[0] * a.w_scale[0]);
+  float oscale = 1.0f, amax = 0.0f;
+  if constexpr (OUT8) oscale = a.y8_scale[0];
 
   if constexpr (EPI == EPI_BIAS_RESIDUAL) {
 #pragma unroll 4
@@ -258,8 +329,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void k_gemm(GemmArgs 
           float lo[4], hi[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            lo[e] = acc[i][j][4 * gq + e];
-            hi[e] = acc[i][j + 1][4 * gq + e];
+            lo[e] = acc[i][j][4 * gq + e] * dq;
+            hi[e] = acc[i][j + 1][4 * gq + e] * dq;
           }
           if (bias && nlo < N) {
             const u32x2 bl = *(const u32x2*)(bias + nlo);
@@ -277,8 +348,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void k_gemm(GemmArgs 
               hi[e] = x1 * t.x + x0 * t.y;
             }
           }
-          *(u32x2*)(stage + soff(row, cl / 8) + 4 * lhalf) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
-          *(u32x2*)(stage + soff(row, cl / 8 + 4) + 4 * lhalf) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
+          *(u32x2*)(stage + soff(row, cl / 8) + 8 * lhalf) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
+          *(u32x2*)(stage + soff(row, cl / 8 + 4) + 8 * lhalf) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
         }
       }
     } else {
@@ -292,33 +363,42 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void k_gemm(GemmArgs 
           const int n = nw + cl;
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e];
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e] * dq;
           if (bias && n < N) {
             const u32x2 bb = *(const u32x2*)(bias + n);
             v[0] += bflo(bb[0]); v[1] += bfhi(bb[0]); v[2] += bflo(bb[1]); v[3] += bfhi(bb[1]);
           }
-          bf16_t* sp = stage + soff(row, cl / 8) + 4 * lhalf;
-          if constexpr (EPI == EPI_BIAS_GELU) {
+          if constexpr (EPI == EPI_BIAS_GELU || OUT8) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
           }
-          if constexpr (EPI == EPI_BIAS_RESIDUAL) {
-            const u32x2 rr = *(const u32x2*)sp;
-            v[0] += bflo(rr[0]); v[1] += bfhi(rr[0]); v[2] += bflo(rr[1]); v[3] += bfhi(rr[1]);
-            if (zero_row) v[0] = v[1] = v[2] = v[3] = 0.f;
+          if constexpr (OUT8) {
+            if (m < M && n < N && (a.pos == nullptr || a.pos[mc] >= 0))
+#pragma unroll
+              for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(v[e]));
+            // four consecutive E4M3 bytes at byte cl of the staged row
+            *(uint32_t*)(stage + soff(row, cl / 16) + (cl % 16)) = pack_e4m3x4(v, oscale);
+          } else {
+            unsigned char* sp = stage + soff(row, cl / 8) + 8 * lhalf;
+            if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+              const u32x2 rr = *(const u32x2*)sp;
+              v[0] += bflo(rr[0]); v[1] += bfhi(rr[0]); v[2] += bflo(rr[1]); v[3] += bfhi(rr[1]);
+              if (zero_row) v[0] = v[1] = v[2] = v[3] = 0.f;
+            }
+            *(u32x2*)sp = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
           }
-          *(u32x2*)sp = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
         }
       }
     }
   }
+  if constexpr (OUT8) record_amax(a.y8_amax, amax);
   __syncthreads();
 
 #pragma unroll 4
   for (int p = 0; p < PASSES; ++p) {
     const int idx = p * 64 + lane, row = idx / CPR, ch = idx % CPR;
     const int64_t m = mw + row;
-    const int n = nw + ch * 8;
+    const int n = nw + ch * EPC;
     if (m >= M || n >= N) continue;
     const u32x4 v = *(const u32x4*)(stage + soff(row, ch));
     if constexpr (EPI == EPI_QKV_ROPE) {
@@ -326,18 +406,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, MINB) void k_gemm(GemmArgs 
       const int heads = N / 192;
       const int head = n / 192, c = (n % 192) / 64, d = n % 64;
       *(u32x4*)(a.y + (((int64_t)c * heads + head) * M + m) * kHeadDim + d) = v;
+    } else if constexpr (OUT8) {
+      *(u32x4*)(a.y8 + m * N + n) = v;
     } else {
       *(u32x4*)(a.y + m * N + n) = v;
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int MINB, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, int DT>
 hipError_t run(const GemmArgs& a, hipStream_t st) {
   const int64_t tilesM = (a.M + BM - 1) / BM;
   const int64_t tilesN = (a.N + BN - 1) / BN;
   const int64_t nb = tilesM * tilesN;
-  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, BK, MINB, EPI>), dim3((unsigned)nb), dim3(64 * WM * WN), 0, st, a);
+  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI, DT>), dim3((unsigned)nb), dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
 
@@ -345,18 +427,23 @@ template <int EPI>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   // 256x256 tiles, 8 waves (two per SIMD, so one wave's LDS reads overlap the
   // other's MFMAs) of 128x64 each.
-  return run<256, 256, 2, 4, 64, 1, EPI>(a, st);
+  if (a.dtype == kE4M3) return run<256, 256, 2, 4, EPI, kE4M3>(a, st);
+  if constexpr (EPI == EPI_BIAS_GELU_E4M3) return hipErrorInvalidValue;
+  else return run<256, 256, 2, 4, EPI, kBF16>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
+  const int kb = a.dtype == kE4M3 ? kRowBytes : kRowBytes / 2;
+  if (a.K % kb != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_BIAS: return dispatch<EPI_BIAS>(a, st);
     case EPI_BIAS_GELU: return dispatch<EPI_BIAS_GELU>(a, st);
     case EPI_BIAS_RESIDUAL: return dispatch<EPI_BIAS_RESIDUAL>(a, st);
     case EPI_QKV_ROPE: return dispatch<EPI_QKV_ROPE>(a, st);
+    case EPI_BIAS_GELU_E4M3: return dispatch<EPI_BIAS_GELU_E4M3>(a, st);
   }
   return hipErrorInvalidValue;
 }

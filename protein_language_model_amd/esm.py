@@ -21,10 +21,12 @@ STATUS_NAMES = {0: "ESM_OK", 1: "ESM_ERR_NULL", 2: "ESM_ERR_SHAPE", 3: "ESM_ERR_
                 5: "ESM_ERR_WORKSPACE", 6: "ESM_ERR_ARCH", 7: "ESM_ERR_HIP", 8: "ESM_ERR_STATE"}
 PRECISION = {"bf16": 0, "fp8": 1}
 LAYOUT_THD, LAYOUT_BSHD = 0, 1
-EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL = 0, 1, 2
+EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_E4M3 = 0, 1, 2, 3
 WS_REGIONS = {"ln1": 0, "qkv": 1, "ctx": 2, "x1": 3, "ln2": 4, "act": 5, "pos": 6, "tiles": 7, "ntiles": 8, "segs": 9}
 KERNEL_CLASSES = ("segment", "embed", "layernorm", "gemm_qkv", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
-                  "other")
+                  "other", "fp8")
+FP8_ACT_NAMES = ("ln1", "ctx", "ln2", "act")      # activation tensors tracked per layer, in state order
+FP8_WEIGHT_NAMES = ("w_qkv", "w_out", "w_fc1", "w_fc2")
 LAYER_WEIGHT_NAMES = ("ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_out", "b_out",
                       "ln2_gamma", "ln2_beta", "w_fc1", "b_fc1", "w_fc2", "b_fc2")
 
@@ -46,6 +48,14 @@ class EsmLayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHT_NAMES]
 
 
+class EsmFp8State(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32), ("history_len", ctypes.c_int32),
+        ("act_scale", ctypes.c_void_p), ("amax_history", ctypes.c_void_p), ("steps", ctypes.c_void_p),
+        ("weight_scale", ctypes.c_void_p), ("nonfinite", ctypes.c_uint32),
+    ]
+
+
 SIGNATURES = {
     "esm_config_default": (None, [ctypes.POINTER(EsmConfig)]),
     "esm_encoder_create": (_i32, [ctypes.POINTER(EsmConfig), ctypes.c_int, ctypes.POINTER(_p)]),
@@ -64,6 +74,12 @@ SIGNATURES = {
     "esm_attention_fwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_linear_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
     "esm_layernorm_fwd": (_i32, [_p, _p, _p, _p, _p, _i64, _p]),
+    "esm_linear_e4m3_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
+    "esm_fp8_prepare_layer": (_i32, [_p, _i32, ctypes.POINTER(EsmLayerWeights), _p]),
+    "esm_fp8_get_state": (_i32, [_p, ctypes.POINTER(EsmFp8State), _p]),
+    "esm_fp8_set_state": (_i32, [_p, ctypes.POINTER(EsmFp8State), _p]),
+    "esm_fp8_reset": (_i32, [_p, _p]),
+    "esm_fp8_quantize": (_i32, [_p, _p, _i64, _p, _p, _p, _p]),
     "esm_profile_enable": (_i32, [_p, _i32]),
     "esm_profile_read": (_i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "esm_check_cu_seqlens": (_i32, [_p, _i32, _i64, _i32, _i32]),
@@ -212,6 +228,8 @@ class Encoder:
         raw = ws[off.value: off.value + nb.value]
         if name in ("pos", "tiles", "ntiles", "segs"):
             return raw.view(torch.int32)
+        if self.cfg.precision == PRECISION["fp8"] and name in ("ln1", "ctx", "ln2", "act"):
+            return raw  # E4M3 codes, row-major with the bf16 row count
         return raw.view(torch.bfloat16)
 
     # -- forward
@@ -310,6 +328,65 @@ class Encoder:
         _call("esm_layernorm_fwd", self._h, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), int(x.shape[0]),
               _stream(stream))
         return y
+
+    def linear_e4m3_fwd(self, x8, x_scale, w8, w_scale, b=None, *, residual=None, epilogue: int = EPI_BIAS, y=None,
+                        y_scale=None, y_amax=None, stream=None):
+        """E4M3 GEMM: x8 [M, K] and w8 [N, K] uint8 codes, scales as device float32[1] tensors."""
+        import torch
+        M, K = x8.shape
+        N = w8.shape[0]
+        if y is None:
+            dt = torch.uint8 if epilogue == EPI_BIAS_GELU_E4M3 else torch.bfloat16
+            y = torch.empty((M, N), dtype=dt, device=x8.device)
+        _call("esm_linear_e4m3_fwd", self._h, _ptr(x8), _ptr(x_scale), _ptr(w8), _ptr(w_scale), _ptr(b),
+              _ptr(residual), _ptr(y), _ptr(y_scale), _ptr(y_amax), int(M), int(N), int(K), int(epilogue),
+              _stream(stream))
+        return y
+
+    # -- FP8 delayed scaling
+    def fp8_prepare_layer(self, layer_idx: int, weights, stream=None) -> None:
+        w = layer_weights_struct(weights)
+        _call("esm_fp8_prepare_layer", self._h, int(layer_idx), ctypes.byref(w), _stream(stream))
+
+    def fp8_prepare(self, weights: Sequence[Dict], stream=None) -> None:
+        for l, w in enumerate(weights):
+            self.fp8_prepare_layer(l, w, stream)
+
+    def fp8_get_state(self, stream=None) -> Dict[str, np.ndarray]:
+        L, HL = self.cfg.num_hidden_layers, self.cfg.amax_history_len
+        out = {"act_scale": np.zeros((L, 4), np.float32), "amax_history": np.zeros((L, 4, HL), np.float32),
+               "steps": np.zeros(L, np.int64), "weight_scale": np.zeros((L, 4), np.float32)}
+        st = EsmFp8State(num_layers=L, history_len=HL)
+        for k, a in out.items():
+            setattr(st, k, a.ctypes.data_as(ctypes.c_void_p))
+        _call("esm_fp8_get_state", self._h, ctypes.byref(st), _stream(stream))
+        out["nonfinite"] = bool(st.nonfinite)
+        return out
+
+    def fp8_set_state(self, state: Dict, stream=None) -> None:
+        L, HL = self.cfg.num_hidden_layers, self.cfg.amax_history_len
+        arrs = {"act_scale": np.ascontiguousarray(state["act_scale"], np.float32).reshape(L, 4),
+                "amax_history": np.ascontiguousarray(state["amax_history"], np.float32).reshape(L, 4, HL),
+                "steps": np.ascontiguousarray(state["steps"], np.int64).reshape(L),
+                "weight_scale": np.zeros((L, 4), np.float32)}
+        st = EsmFp8State(num_layers=L, history_len=HL, nonfinite=1 if state.get("nonfinite") else 0)
+        for k, a in arrs.items():
+            setattr(st, k, a.ctypes.data_as(ctypes.c_void_p))
+        _call("esm_fp8_set_state", self._h, ctypes.byref(st), _stream(stream))
+
+    def fp8_reset(self, stream=None) -> None:
+        _call("esm_fp8_reset", self._h, _stream(stream))
+
+    def fp8_quantize(self, x, scale, *, y=None, amax=None, stream=None):
+        """E4M3 codes of x * scale[0] (x float32 on the device); returns (codes, amax tensor)."""
+        import torch
+        if y is None:
+            y = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        if amax is None:
+            amax = torch.zeros(1, dtype=torch.int32, device=x.device)
+        _call("esm_fp8_quantize", self._h, _ptr(x), int(x.numel()), _ptr(scale), _ptr(y), _ptr(amax),
+              _stream(stream))
+        return y, amax
 
     # -- timing
     def profile_enable(self, on: bool = True) -> None:

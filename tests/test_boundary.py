@@ -27,7 +27,15 @@ def test_library_exports_every_declared_symbol():
     assert not missing, missing
     # and the binding knows the signature of each
     assert set(names) == set(esm.SIGNATURES), set(names) ^ set(esm.SIGNATURES)
-    assert lib.esm_abi_version() == 1
+    src = open(HEADER).read()
+    assert lib.esm_abi_version() == int(re.search(r"#define ESM_ABI_VERSION (\d+)", src).group(1))
+    assert len(esm.KERNEL_CLASSES) == int(re.search(r"ESM_K_COUNT = (\d+)", src).group(1))
+
+
+def test_fp8_state_struct_layout_matches_the_header():
+    # two int32, four pointers, one uint32 (padded to the pointer alignment)
+    assert ctypes.sizeof(esm.EsmFp8State) == 48
+    assert esm.EsmFp8State.act_scale.offset == 8 and esm.EsmFp8State.nonfinite.offset == 40
 
 
 def test_status_strings():
@@ -101,6 +109,9 @@ def test_config_default_is_esm2_650m():
     (dict(layer_norm_eps=0.0), 2),
     (dict(precision=7), 4),
     (dict(amax_history_len=0), 2),
+    (dict(amax_history_len=1025), 2),
+    (dict(precision=1, hidden_size=320, num_attention_heads=5, intermediate_size=1280), 4),  # FP8 K step 128
+    (dict(precision=1, intermediate_size=5120 + 64), 4),
 ])
 def test_create_rejects_bad_config_before_touching_a_device(kw, code):
     c = _cfg(**kw)
@@ -108,6 +119,20 @@ def test_create_rejects_bad_config_before_touching_a_device(kw, code):
     st, msg = _status("esm_encoder_create", ctypes.byref(c), 0, ctypes.byref(h))
     assert st == code, msg
     assert not h.value
+
+
+def test_fp8_calls_fail_cleanly_without_a_handle():
+    st, _ = _status("esm_fp8_reset", None, None)
+    assert st == 1
+    st, _ = _status("esm_fp8_prepare_layer", None, 0, None, None)
+    assert st == 1
+    st, _ = _status("esm_fp8_get_state", None, None, None)
+    assert st == 1
+    st, _ = _status("esm_fp8_quantize", None, None, 4, None, None, None, None)
+    assert st == 1
+    st, _ = _status("esm_linear_e4m3_fwd", None, None, None, None, None, None, None, None, None, None, 1, 64, 128,
+                    0, None)
+    assert st == 1
 
 
 def test_null_handle_calls_fail_cleanly():
