@@ -6,9 +6,12 @@ One step = one esm_stack_fwd call: embedding lookup plus all layers of the
 Timing follows the TransformerEngine tutorial's protocol: warm-up steps, then
 timed steps bracketed by device synchronisation, HIP events on the library
 stream; a second pass over the same steps times every kernel launch with HIP
-events for the roofline of the dominant kernel.  Prints one JSON line.
+events for the roofline of the dominant kernel.  The same batch is then run
+through the FP8 (E4M3, delayed scaling) encoder, whose scales come from at
+least 10 warm-up steps, and reported under "fp8".  Prints one JSON line.
 
-    python bench.py [--steps 30] [--warmup 10] [--workload 650m] [--no-cpu-baseline] [--padded]
+    python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
+                    [--padded] [--no-fp8]
 """
 from __future__ import annotations
 
@@ -24,6 +27,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (vendor figure)
+PEAK_FP8_TFLOPS = 5033.2     # MI355X dense fp8 MFMA (vendor figure)
+FP8_MIN_WARMUP = 10          # delayed scales settle over the warm-up steps
 PEAK_HBM_GBS = 8000.0
 
 
@@ -43,7 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="650m", choices=["650m", "3b"])
+    ap.add_argument("--workload", default="650m", choices=["650m", "3b", "650m_fp8"])
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 leg of a bf16 workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--padded", action="store_true", help="also time the padded bshd layout of the same batch")
     ap.add_argument("--no-kernel-timing", action="store_true")
@@ -92,9 +98,16 @@ def cpu_baseline(wl, batch, emb_bits, weights_dev, budget_residues: int = 12288,
         threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
     except Exception:
         pass
+    fp8 = wl.precision == "fp8"
+    if fp8:
+        from oracle import fp8_ref as F8
+        unit_scales = {n: 1.0 for n in F8.ACT_NAMES}   # the cost does not depend on the scale values
     t0 = time.perf_counter()
     for l in range(layers):
-        x = O.layer_forward(x, cu, ws[l], m.heads)
+        if fp8:
+            x = F8.layer_forward_fp8(x, cu, ws[l], m.heads, unit_scales)
+        else:
+            x = O.layer_forward(x, cu, ws[l], m.heads)
     dt = time.perf_counter() - t0
     per_layer = dt / layers
     return {
@@ -103,8 +116,21 @@ def cpu_baseline(wl, batch, emb_bits, weights_dev, budget_residues: int = 12288,
         "cores": threads or os.cpu_count(),
         "kind": "oracle",
         "sample": f"first {n} sequences ({tot} residues) of the batch through {layers} of {m.layers} layers "
-                  f"(fp64 numpy/scipy), {dt:.1f} s; scaled to the {m.layers}-layer forward",
+                  f"({'FP8-emulating ' if fp8 else ''}fp64 numpy/scipy), {dt:.1f} s; scaled to the "
+                  f"{m.layers}-layer forward",
     }
+
+
+def roofline_of(prof, fl, peaks):
+    """Roofline record of the kernel class with the largest total time."""
+    cand = {k: v for k, v in prof.items() if k in fl and v[1]}
+    dom = max(cand, key=lambda k: cand[k][0])
+    avg_ms = cand[dom][0] / cand[dom][1]
+    achieved = fl[dom] / (avg_ms * 1e-3) / 1e12
+    peak = peaks.get(dom, PEAK_BF16_TFLOPS)
+    return {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None, "avg_launch_ms": round(avg_ms, 4),
+            "flops_per_launch": fl[dom]}
 
 
 def main():
@@ -128,19 +154,13 @@ def main():
     def up_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    enc = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn,
-                      num_hidden_layers=m.layers)
     T, B = batch.T, batch.B
     cu = torch.from_numpy(batch.cu_seqlens).to(dev)
     ids = torch.from_numpy(batch.ids).to(dev)
     emb_d = up_bf16(emb)
-    ws = enc.workspace(T, B)
     out = torch.empty((T, m.hidden), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
-
-    def step():
-        enc.stack_fwd(weights, cu, B, T, batch.max_seqlen, token_ids=ids, embedding=emb_d, x_out=out,
-                      workspace=ws, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     if args.copy_calibration:
         src_c = torch.ones(128 * 1024 * 1024, dtype=torch.bfloat16, device=dev)
@@ -148,50 +168,61 @@ def main():
         dst_c.copy_(src_c)
         torch.cuda.synchronize()
         del src_c, dst_c
-    for _ in range(args.warmup):
-        step()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def timed_steps(n: int) -> float:
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(n):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    # Timed region 1: the throughput.  Timed region 2: the same steps again with
-    # every launch bracketed by HIP events on the library stream, for the
-    # per-kernel durations (the events add a few percent, so they stay out of 1).
-    ms = timed_steps(args.steps)
-    kernel_timing = not args.no_kernel_timing
-    prof = None
-    ms_instrumented = None
-    if kernel_timing:
-        enc.profile_enable(True)
-        ms_instrumented = timed_steps(args.steps)
-        prof = enc.profile_read()
-        enc.profile_enable(False)
 
     sum_L2 = int((batch.lengths.astype(np.int64) ** 2).sum())
     fl = layer_flops(m.hidden, m.ffn, T, sum_L2)
     total_flops = m.layers * sum(fl.values())
+
+    def measure(precision: str, warmup: int):
+        """Clean timed region (the throughput), then the same steps with every
+        launch bracketed by HIP events (per-kernel durations)."""
+        enc = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn,
+                          num_hidden_layers=m.layers, precision=precision)
+        if precision == "fp8":
+            enc.fp8_prepare(weights, stream=stream)
+        ws = enc.workspace(T, B)
+
+        def step():
+            enc.stack_fwd(weights, cu, B, T, batch.max_seqlen, token_ids=ids, embedding=emb_d, x_out=out,
+                          workspace=ws, stream=stream)
+
+        def timed_steps(n: int) -> float:
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        for _ in range(warmup):
+            step()
+        ms = timed_steps(args.steps)
+        prof = ms_instr = None
+        if not args.no_kernel_timing:
+            enc.profile_enable(True)
+            ms_instr = timed_steps(args.steps)
+            prof = enc.profile_read()
+            enc.profile_enable(False)
+        return enc, ws, ms, prof, ms_instr
+
+    def kernel_table(prof):
+        return {k: {"ms_per_launch": (v[0] / v[1]) if v[1] else None, "launches_per_step": v[1] / args.steps,
+                    "ms_per_step": v[0] / args.steps} for k, v in prof.items() if v[1]}
+
+    fp8_main = wl.precision == "fp8"
+    gemm_peak = PEAK_FP8_TFLOPS if fp8_main else PEAK_BF16_TFLOPS
+    peaks = {k: gemm_peak for k in fl if k.startswith("gemm")}
+    enc, ws, ms, prof, ms_instrumented = measure(wl.precision, max(args.warmup, FP8_MIN_WARMUP) if fp8_main
+                                                 else args.warmup)
     tflops = total_flops / (ms * 1e-3) / 1e12
     value = T / (ms * 1e-3)
-
-    roofline = None
-    kernels = None
+    roofline = kernels = None
     if prof:
-        kernels = {k: {"ms_per_launch": (v[0] / v[1]) if v[1] else None, "launches_per_step": v[1] / args.steps,
-                       "ms_per_step": v[0] / args.steps} for k, v in prof.items() if v[1]}
-        cand = {k: v for k, v in prof.items() if k in fl and v[1]}
-        dom = max(cand, key=lambda k: cand[k][0])
-        avg_ms = cand[dom][0] / cand[dom][1]
-        achieved = fl[dom] / (avg_ms * 1e-3) / 1e12
-        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_record(dom),
-                    "avg_launch_ms": round(avg_ms, 4), "flops_per_launch": fl[dom]}
+        kernels = kernel_table(prof)
+        roofline = roofline_of(prof, fl, peaks)
+        if not fp8_main:
+            roofline["traffic"] = traffic_record(roofline["kernel"])
 
     padded = None
     if args.padded:
@@ -217,24 +248,40 @@ def main():
         padded = {"layout": f"bshd [{B}, {S}]", "ms_per_step": round(ms_p, 3), "steps": n_p,
                   "valid_fraction": round(T / (B * S), 4), "packing_gain": round(ms_p / ms, 3)}
         del ws_p, out_p
+    enc.close()
+    del ws
+
+    fp8 = None
+    if not fp8_main and not args.no_fp8 and m.hidden % 128 == 0 and m.ffn % 128 == 0:
+        enc8, ws8, ms8, prof8, _ = measure("fp8", max(args.warmup, FP8_MIN_WARMUP))
+        fp8 = {"ms_per_step": round(ms8, 4), "value": round(T / (ms8 * 1e-3), 1), "unit": "residues/s",
+               "tflops": round(total_flops / (ms8 * 1e-3) / 1e12, 1), "speedup_vs_bf16": round(ms / ms8, 3),
+               "warmup": max(args.warmup, FP8_MIN_WARMUP),
+               "recipe": "E4M3 QKV/out/fc1/fc2 GEMMs, per-tensor delayed scaling, amax history 16, max"}
+        if prof8:
+            fp8["kernels"] = kernel_table(prof8)
+            fp8["roofline"] = roofline_of(prof8, fl, {k: PEAK_FP8_TFLOPS for k in fl if k.startswith("gemm")})
+        enc8.close()
+        del ws8
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, batch, emb, weights)
 
+    prec = "FP8 E4M3 delayed scaling" if fp8_main else "bf16"
+    shape = "650M 33-layer" if m.layers == 33 else "3B-shaped 36-layer"
     rec = {
-        "metric": "packed residues/s, ESM-2 650M 33-layer fwd bf16; % of MFMA peak" if args.workload == "650m"
-        else "packed residues/s, ESM-2 3B-shaped 36-layer fwd bf16; % of MFMA peak",
+        "metric": f"packed residues/s, ESM-2 {shape} fwd {prec}; % of MFMA peak",
         "value": round(value, 1),
         "unit": "residues/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": max(args.warmup, FP8_MIN_WARMUP) if fp8_main else args.warmup,
         "ms_per_step": round(ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3" if fp8_main else "bf16",
         "data": "synthetic",
         "config": {"workload": f"ESM-2 {m.hidden}x{m.layers} ({args.workload}) packed THD forward",
                    "sequences": B, "residues": T, "max_seqlen": batch.max_seqlen, "sum_L2": sum_L2,
@@ -246,6 +293,7 @@ def main():
         "kernels": kernels,
         "ms_per_step_with_kernel_events": round(ms_instrumented, 4) if ms_instrumented else None,
         "padded": padded,
+        "fp8": fp8,
     }
     print(json.dumps(rec))
 

@@ -210,7 +210,8 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
           *(uint32_t*)(dst + dim) = pack_e4m3x4(v, s8);
         }
     }
-    record_amax(a.ctx8.amax, amax);
+    __shared__ float red[4];
+    record_amax_block<4>(a.ctx8.amax, amax, red);
     return;
   }
   if (qrow >= L) return;

@@ -55,15 +55,37 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(const float (&v)[4], float s) {
   return ((uint32_t)w & ~nan_mask) | (0x7F7F7F7Fu & nan_mask);
 }
 
-// Record a non-negative per-lane maximum into *amax (float bits as uint32):
-// the wave reduces with fmaxf (which drops NaN), lane 0 issues one
-// atomicMax.  Non-negative floats order like their bit patterns, so the result
-// is exact and independent of the order of the atomics.  Every lane of the
-// wave must call this.
-__device__ __forceinline__ void record_amax(uint32_t* amax, float m) {
+// Maximum of a non-negative per-lane value over the wave (fmaxf drops NaN).
+__device__ __forceinline__ float wave_max(float m) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0 && m > 0.f) atomicMax(amax, __float_as_uint(m));
+  return m;
+}
+
+// Fold a non-negative maximum into *amax (float bits as uint32).  Non-negative
+// floats order like their bit patterns, so atomicMax is exact and independent
+// of the order of the updates.  A relaxed read first skips the atomic when the
+// recorded value is already as large (it only grows, so a stale read can only
+// cause an unneeded atomic): after the first workgroups almost all skip it.
+__device__ __forceinline__ void fold_amax(uint32_t* amax, float m) {
+  if (!(m > 0.f)) return;
+  const uint32_t v = __float_as_uint(m);
+  if (v > __hip_atomic_load(amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(amax, v);
+}
+
+// Block-wide amax: every thread of the workgroup calls this with its value
+// (0 when it has none), NW = waves per workgroup; one lane folds the result.
+template <int NW>
+__device__ __forceinline__ void record_amax_block(uint32_t* amax, float m, float* red) {
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) b = fmaxf(b, red[w]);
+    fold_amax(amax, b);
+  }
 }
 
 // Launch context handed from the host library to each launcher.

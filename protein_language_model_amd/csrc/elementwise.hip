@@ -135,8 +135,14 @@ __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x,
                                                    const bf16_t* __restrict__ beta, bf16_t* __restrict__ y,
                                                    int64_t M, int32_t H, float eps, E4m3Out q) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;  // wave-uniform: the amax reduction below stays wave-complete
+  const int64_t row_ = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if constexpr (!OUT8) {
+    if (row_ >= M) return;
+  }
+  // E4M3 output: every wave reaches the block amax reduction; a wave past the
+  // last row works on the last row and stores nothing.
+  const bool active = row_ < M;
+  const int64_t row = active ? row_ : M - 1;
   const int chunks = H / 8;
   const bf16_t* xr = x + row * H;
   float v[CH][8];
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x,
   bool count = true;
   if constexpr (OUT8) {
     s8 = q.scale[0];
-    count = q.pos == nullptr || q.pos[row] >= 0;
+    count = active && (q.pos == nullptr || q.pos[row] >= 0);
   }
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
@@ -196,14 +202,17 @@ __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x,
         if (count)
 #pragma unroll
           for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(o[e]));
-        *(u32x2*)(q.y + row * H + c * 8) = u32x2{pack_e4m3x4(lo, s8), pack_e4m3x4(hi, s8)};
+        if (active) *(u32x2*)(q.y + row * H + c * 8) = u32x2{pack_e4m3x4(lo, s8), pack_e4m3x4(hi, s8)};
       } else {
         *(u32x4*)(y + row * H + c * 8) =
             u32x4{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7])};
       }
     }
   }
-  if constexpr (OUT8) record_amax(q.amax, amax);
+  if constexpr (OUT8) {
+    __shared__ float red[4];
+    record_amax_block<4>(q.amax, amax, red);
+  }
 }
 
 }  // namespace

@@ -23,7 +23,8 @@ __global__ __launch_bounds__(256) void k_amax_bf16(const bf16_t* __restrict__ x,
 #pragma unroll
     for (int e = 0; e < 4; ++e) m = fmaxf(m, fmaxf(fabsf(bflo(w[e])), fabsf(bfhi(w[e]))));
   }
-  record_amax(amax, m);
+  __shared__ float red[4];
+  record_amax_block<4>(amax, m, red);
 }
 
 __global__ __launch_bounds__(256) void k_quantize_weight(const bf16_t* __restrict__ x, int64_t n8,
@@ -50,7 +51,8 @@ __global__ __launch_bounds__(256) void k_quantize_f32(const float* __restrict__ 
     y[i] = (uint8_t)(pack_e4m3x4(v, scale[0]) & 0xFFu);
     m = fabsf(x[i]);
   }
-  record_amax(amax, m);
+  __shared__ float red[4];
+  record_amax_block<4>(amax, m, red);
 }
 
 // One thread per layer: its four activation tensors share the step counter.

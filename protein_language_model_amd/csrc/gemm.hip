@@ -391,8 +391,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       }
     }
   }
-  if constexpr (OUT8) record_amax(a.y8_amax, amax);
-  __syncthreads();
+  if constexpr (OUT8) {
+    __shared__ float red[NW];
+    record_amax_block<NW>(a.y8_amax, amax, red);   // includes the barrier that publishes the staged tile
+  } else {
+    __syncthreads();
+  }
 
 #pragma unroll 4
   for (int p = 0; p < PASSES; ++p) {
