@@ -75,7 +75,7 @@ def traffic_record(kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, batch, emb_bits, weights_dev, budget_residues: int = 12288, layers: int = 3) -> dict:
+def cpu_baseline(wl, batch, emb_bits, weights_dev, budget_residues: int = 12288, layers: int = 8) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     the first sequences of the batch up to `budget_residues` residues, through
     `layers` layers; scaled to residues/s of the full-depth forward."""
@@ -221,8 +221,7 @@ def main():
     if prof:
         kernels = kernel_table(prof)
         roofline = roofline_of(prof, fl, peaks)
-        if not fp8_main:
-            roofline["traffic"] = traffic_record(roofline["kernel"])
+        roofline["traffic"] = traffic_record(("fp8_" if fp8_main else "") + roofline["kernel"])
 
     padded = None
     if args.padded:
@@ -261,6 +260,7 @@ def main():
         if prof8:
             fp8["kernels"] = kernel_table(prof8)
             fp8["roofline"] = roofline_of(prof8, fl, {k: PEAK_FP8_TFLOPS for k in fl if k.startswith("gemm")})
+            fp8["roofline"]["traffic"] = traffic_record("fp8_" + fp8["roofline"]["kernel"])
         enc8.close()
         del ws8
 

@@ -107,7 +107,8 @@ def _codes(rng, shape, sd):
     return F8.e4m3_encode(rng.standard_normal(shape) * sd)
 
 
-@pytest.mark.parametrize("M,N,K", [(600, 384, 384), (300, 1280, 1280), (77, 5120, 1280), (513, 1280, 5120)])
+@pytest.mark.parametrize("M,N,K", [(600, 384, 384), (300, 1280, 1280), (77, 5120, 1280), (513, 1280, 5120),
+                                   (5, 64, 128)])
 @pytest.mark.parametrize("epi", ["bias", "gelu", "residual", "gelu_e4m3"])
 def test_e4m3_gemm_contracts_exact_products(gu, M, N, K, epi):
     rng = np.random.default_rng(M * 7 + N + K)
