@@ -114,8 +114,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   static_assert(EPI != EPI_QKV_ROPE || (FN % 2 == 0 && WTN % 64 == 0), "rotary pairs need 64-wide wave columns");
   static_assert(EPI != EPI_BIAS_GELU_E4M3 || DT == kE4M3, "E4M3 output is built for E4M3 operands");
 
-  // Two K-step stages; after the K loop the same memory stages the output tile.
-  constexpr int kSmem = 2 * kStage > BM * BN * 2 ? 2 * kStage : BM * BN * 2;
+  // Two K-step stages; after the K loop the same memory stages the output,
+  // the whole tile at once when it fits, else 32-row chunks of every wave's
+  // tile (see the epilogue).
+  constexpr bool OUT8 = EPI == EPI_BIAS_GELU_E4M3;
+  constexpr int OES = OUT8 ? 1 : 2;               // output bytes per element
+  constexpr int ECH = BM * BN * OES <= 2 * kStage ? WTM : 32;  // staged rows per wave per chunk
+  static_assert(WTM % ECH == 0, "whole chunks");
+  constexpr int kSmem = 2 * kStage > NW * ECH * WTN * OES ? 2 * kStage : NW * ECH * WTN * OES;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem];
 
   const int64_t M = a.M;
@@ -246,6 +252,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       vm_wait_all();
       __syncthreads();
     }
+  } else if constexpr (FM * FN > 8) {
+    // Large wave tiles (160 x 64: 160 accumulator registers): one fragment
+    // set, as for E4M3.
+    frag_t xf[FM], wf[FN];
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) issue_tile((kt + 1) * kRowBytes, cur ^ 1);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(xf, wf, cur, kk);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step(xf, wf);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      vm_wait_all();
+      __syncthreads();
+    }
   } else {
   frag_t xf[2][FM], wf[2][FN];
   load_frags(xf[0], wf[0], 0, 0);
@@ -274,21 +298,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 
   // ------------------------------------------------------------ epilogue
   // Each wave stages its (WTM x WTN) result tile in LDS (free once every wave
-  // is past the K loop), so that global memory is written (and, for the
-  // residual, read) in full rows with 16-byte lanes.  Staged rows hold CPR
-  // 16-byte chunks, chunk c of row r stored at c ^ ((r / RPW) % CPR), which
-  // spreads the row-per-lane accesses of the MFMA layout over the banks.
-  // E4M3 operands: the accumulators are first divided by s_x s_w.  E4M3
-  // output: the GELU values are cast with the output's scale, and their amax
-  // (before the cast) is recorded.
-  constexpr bool OUT8 = EPI == EPI_BIAS_GELU_E4M3;
-  constexpr int OES = OUT8 ? 1 : 2;               // output bytes per element
+  // is past the K loop) -- all of it, or ECH-row chunks when the whole tile
+  // does not fit -- so that global memory is written (and, for the residual,
+  // read) in full rows with 16-byte lanes.  Staged rows hold CPR 16-byte
+  // chunks, chunk c of row r stored at c ^ ((r / RPW) % CPR), which spreads
+  // the row-per-lane accesses of the MFMA layout over the banks.  E4M3
+  // operands: the accumulators are first divided by s_x s_w.  E4M3 output:
+  // the GELU values are cast with the output's scale, and their amax (before
+  // the cast) is recorded.
   constexpr int CPR = WTN * OES / 16;             // 16-byte chunks per staged row
   constexpr int RPW = CPR >= 16 ? 1 : 16 / CPR;   // staged rows per 256-byte bank window
-  constexpr int PASSES = WTM * CPR / 64;          // 16-byte transfers per lane
+  constexpr int PASSES = ECH * CPR / 64;          // 16-byte transfers per lane per chunk
   constexpr int EPC = 16 / OES;                   // output elements per chunk
   __syncthreads();
-  unsigned char* stage = smem + wave * (WTM * WTN * OES);
+  unsigned char* stage = smem + wave * (ECH * WTN * OES);
   auto soff = [&](int row, int chunk) { return row * (WTN * OES) + ((chunk ^ ((row / RPW) & (CPR - 1))) * 16); };
   const int64_t mw = m0 + wm * WTM;
   const int nw = n0 + wn * WTN;
@@ -298,11 +321,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   float oscale = 1.0f, amax = 0.0f;
   if constexpr (OUT8) oscale = a.y8_scale[0];
 
+#pragma unroll
+  for (int c0 = 0; c0 < WTM; c0 += ECH) {
   if constexpr (EPI == EPI_BIAS_RESIDUAL) {
 #pragma unroll 4
     for (int p = 0; p < PASSES; ++p) {
       const int idx = p * 64 + lane, row = idx / CPR, ch = idx % CPR;
-      const int64_t m = mw + row;
+      const int64_t m = mw + c0 + row;
       const int n = nw + ch * 8;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (m < M && n < N) v = *(const u32x4*)(a.res + m * N + n);
@@ -312,9 +337,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   }
 
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int row = i * 32 + lrow;
-    const int64_t m = mw + row;
+  for (int i = c0 / 32; i < (c0 + ECH) / 32; ++i) {
+    const int row = i * 32 - c0 + lrow;  // row within the staged chunk
+    const int64_t m = mw + i * 32 + lrow;
     const int64_t mc = m < M ? m : M - 1;
     if constexpr (EPI == EPI_QKV_ROPE) {
       int p = a.pos[mc];
@@ -391,17 +416,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       }
     }
   }
-  if constexpr (OUT8) {
-    __shared__ float red[NW];
-    record_amax_block<NW>(a.y8_amax, amax, red);   // includes the barrier that publishes the staged tile
-  } else {
-    __syncthreads();
-  }
+  __syncthreads();
 
 #pragma unroll 4
   for (int p = 0; p < PASSES; ++p) {
     const int idx = p * 64 + lane, row = idx / CPR, ch = idx % CPR;
-    const int64_t m = mw + row;
+    const int64_t m = mw + c0 + row;
     const int n = nw + ch * EPC;
     if (m >= M || n >= N) continue;
     const u32x4 v = *(const u32x4*)(stage + soff(row, ch));
@@ -416,6 +436,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       *(u32x4*)(a.y + m * N + n) = v;
     }
   }
+  if (c0 + ECH < WTM) __syncthreads();  // the next chunk reuses the staging region
+  }
+  if constexpr (OUT8) {
+    __shared__ float red[NW];
+    record_amax_block<NW>(a.y8_amax, amax, red);
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int EPI, int DT>
@@ -427,13 +453,36 @@ hipError_t run(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Compute units of the current device.
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <int EPI>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
-  // 256x256 tiles, 8 waves (two per SIMD, so one wave's LDS reads overlap the
-  // other's MFMAs) of 128x64 each.
-  if (a.dtype == kE4M3) return run<256, 256, 2, 4, EPI, kE4M3>(a, st);
+  // 8 waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs)
+  // over 256x256 tiles (128x64 per wave), or 320x256 tiles (160x64 per wave)
+  // when those need fewer rounds of workgroups over the compute units: time
+  // ~ rounds x tile rows (N = 1280 at T = 32293: 3 x 256 vs 2 x 320).  Each
+  // output element accumulates the same K order in either shape, so results
+  // do not depend on the choice.
+  const int64_t tilesN = (a.N + 255) / 256;
+  const int64_t cus = device_cus();
+  const int64_t r256 = ((a.M + 255) / 256 * tilesN + cus - 1) / cus;
+  const int64_t r320 = ((a.M + 319) / 320 * tilesN + cus - 1) / cus;
+  const bool tall = r320 * 320 < r256 * 256;
+  if (a.dtype == kE4M3)
+    return tall ? run<320, 256, 2, 4, EPI, kE4M3>(a, st) : run<256, 256, 2, 4, EPI, kE4M3>(a, st);
   if constexpr (EPI == EPI_BIAS_GELU_E4M3) return hipErrorInvalidValue;
-  else return run<256, 256, 2, 4, EPI, kBF16>(a, st);
+  else return tall ? run<320, 256, 2, 4, EPI, kBF16>(a, st) : run<256, 256, 2, 4, EPI, kBF16>(a, st);
 }
 
 }  // namespace

@@ -108,7 +108,7 @@ def _codes(rng, shape, sd):
 
 
 @pytest.mark.parametrize("M,N,K", [(600, 384, 384), (300, 1280, 1280), (77, 5120, 1280), (513, 1280, 5120),
-                                   (5, 64, 128)])
+                                   (5, 64, 128), (15530, 1280, 1280)])
 @pytest.mark.parametrize("epi", ["bias", "gelu", "residual", "gelu_e4m3"])
 def test_e4m3_gemm_contracts_exact_products(gu, M, N, K, epi):
     rng = np.random.default_rng(M * 7 + N + K)
@@ -162,6 +162,21 @@ def test_e4m3_gemm_contracts_exact_products(gu, M, N, K, epi):
         bound += 2e-7 * np.abs(z)
     excess = np.abs(got - ref) / bound
     assert excess.max() <= 1.0, (excess.max(), np.unravel_index(excess.argmax(), excess.shape))
+    enc.close()
+
+
+def test_e4m3_gemm_tile_shape_does_not_change_rows(gu):
+    """320-row tiles (M = 15530, N = 1280) and 256-row tiles (a 1000-row slice)
+    give the same rows bit for bit."""
+    M, N, K, Ms = 15530, 1280, 1280, 1000
+    rng = np.random.default_rng(5)
+    x8, w8 = _codes(rng, (M, K), 3.0), _codes(rng, (N, K), 0.08)
+    enc = esm.Encoder(hidden_size=128, num_attention_heads=2, intermediate_size=256, num_hidden_layers=1,
+                      precision="fp8")
+    one, half = _dev_f32([1.0]), _dev_f32([0.5])
+    y = gu.bits_of(enc.linear_e4m3_fwd(_dev_u8(x8), one, _dev_u8(w8), half))
+    ys = gu.bits_of(enc.linear_e4m3_fwd(_dev_u8(x8[:Ms]), one, _dev_u8(w8), half))
+    assert np.array_equal(y[:Ms], ys)
     enc.close()
 
 

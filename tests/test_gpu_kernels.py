@@ -63,6 +63,28 @@ def test_linear_large_tiles_and_in_place_residual(gu, enc_650m):
     assert gu.rel_err(gu.from_dev(y)[rows], z) < 4e-3
 
 
+@pytest.mark.parametrize("epi", [esm.EPI_BIAS, esm.EPI_BIAS_GELU, esm.EPI_BIAS_RESIDUAL])
+def test_linear_tile_shape_does_not_change_rows(gu, enc_650m, epi):
+    """At M = 15530, N = 1280 the 320-row tiles take fewer rounds and are used;
+    a 1000-row slice takes 256-row tiles.  Every row must come out bit for bit
+    the same, and match the fp64 product on a sample."""
+    M, N, K, Ms = 15530, 1280, 1280, 1000
+    xb, wb, bb, rb = _rand_bits((M, K), 11), _rand_bits((N, K), 12, 0.05), _rand_bits((N,), 13), _rand_bits((M, N), 14)
+    x, w, b, r = (gu.to_dev_bf16(a) for a in (xb, wb, bb, rb))
+    res = epi == esm.EPI_BIAS_RESIDUAL
+    y = gu.bits_of(enc_650m.linear_fwd(x, w, b, residual=r if res else None, epilogue=epi))
+    ys = gu.bits_of(enc_650m.linear_fwd(x[:Ms].contiguous(), w, b, residual=r[:Ms].contiguous() if res else None,
+                                        epilogue=epi))
+    assert np.array_equal(y[:Ms], ys)
+    rows = np.random.default_rng(1).choice(M, 96, replace=False)
+    z = D.bf16_bits_to_f64(xb[rows]) @ D.bf16_bits_to_f64(wb).T + D.bf16_bits_to_f64(bb)
+    if epi == esm.EPI_BIAS_GELU:
+        z = O.gelu(z)
+    if res:
+        z = z + D.bf16_bits_to_f64(rb[rows])
+    assert gu.rel_err(D.bf16_bits_to_f64(y[rows]), z) < 4e-3
+
+
 @pytest.mark.parametrize("H,M", [(320, 381), (1280, 1000), (2560, 77)])
 def test_layernorm(gu, H, M):
     e = esm.Encoder(hidden_size=H, num_attention_heads=H // 64, intermediate_size=4 * H, num_hidden_layers=1)
