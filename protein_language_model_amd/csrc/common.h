@@ -38,21 +38,24 @@ constexpr float kE4M3Max = 448.0f;
 
 // Four values v * s cast to OCP E4M3 (1.4.3, bias 7, no infinity, 0x7F = NaN,
 // largest finite 448), packed little-endian into one word.  The gfx950
-// converter rounds to nearest even; out-of-range inputs are clamped to +-448
-// first (saturating cast, as the delayed-scaling recipe requires) and NaN is
-// written as 0x7F.
+// converter rounds to nearest even; inputs are clamped to +-448 first
+// (saturating cast, as the delayed-scaling recipe requires; s is positive and
+// finite) and NaN is written as 0x7F.  NaN is detected once per four values:
+// their sum is NaN iff one of them is NaN or they hold both infinities.
 __device__ __forceinline__ uint32_t pack_e4m3x4(const float (&v)[4], float s) {
   float c[4];
-  uint32_t nan_mask = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float t = v[e] * s;
-    nan_mask |= (t != t) ? (0xFFu << (8 * e)) : 0u;
-    c[e] = fminf(fmaxf(t, -kE4M3Max), kE4M3Max);
-  }
+  for (int e = 0; e < 4; ++e) c[e] = __builtin_amdgcn_fmed3f(v[e] * s, -kE4M3Max, kE4M3Max);
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], w, true);
-  return ((uint32_t)w & ~nan_mask) | (0x7F7F7F7Fu & nan_mask);
+  uint32_t r = (uint32_t)w;
+  const float chk = (v[0] + v[1]) + (v[2] + v[3]);
+  if (chk != chk) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (v[e] != v[e]) r = (r & ~(0xFFu << (8 * e))) | (0x7Fu << (8 * e));
+  }
+  return r;
 }
 
 // Maximum of a non-negative per-lane value over the wave (fmaxf drops NaN).

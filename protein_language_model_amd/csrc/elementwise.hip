@@ -125,6 +125,8 @@ __global__ void k_embed(const int32_t* __restrict__ ids, const bf16_t* __restric
   *(u32x4*)(x + t * H + c * 8) = *(const u32x4*)(table + (int64_t)id * H + c * 8);
 }
 
+constexpr int kLnRows8 = 4;  // rows per wave of the E4M3-output LayerNorm
+
 // Row LayerNorm, one wave per row: mean, then the biased variance from the
 // centred values held in registers, y = (x - mean) * rsqrt(var + eps) * g + b
 // ([BIO-ACC] 3.1 layernorm; [TE-RU] LayerNormLinear / LayerNormMLP).  With
@@ -134,78 +136,83 @@ template <int CH, bool OUT8>
 __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
                                                    const bf16_t* __restrict__ beta, bf16_t* __restrict__ y,
                                                    int64_t M, int32_t H, float eps, E4m3Out q) {
+  // E4M3 output: each wave normalises kLnRows8 rows, so that fewer workgroups
+  // fold their amax into the tensor's one amax word.
+  constexpr int RW = OUT8 ? kLnRows8 : 1;
   const int lane = threadIdx.x & 63;
-  const int64_t row_ = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row0 = (int64_t)blockIdx.x * (4 * RW) + (threadIdx.x >> 6);
   if constexpr (!OUT8) {
-    if (row_ >= M) return;
+    if (row0 >= M) return;
   }
-  // E4M3 output: every wave reaches the block amax reduction; a wave past the
-  // last row works on the last row and stores nothing.
-  const bool active = row_ < M;
-  const int64_t row = active ? row_ : M - 1;
   const int chunks = H / 8;
-  const bf16_t* xr = x + row * H;
-  float v[CH][8];
-  float sum = 0.f;
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int c = lane + 64 * i;
-    if (c < chunks) {
-      const u32x4 w = *(const u32x4*)(xr + c * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[i][2 * e] = bflo(w[e]);
-        v[i][2 * e + 1] = bfhi(w[e]);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sum += v[i][e];
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-  const float mean = sum / (float)H;
-  float sq = 0.f;
-#pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int c = lane + 64 * i;
-    if (c < chunks) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v[i][e] -= mean;
-        sq += v[i][e] * v[i][e];
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
-  const float rstd = 1.0f / sqrtf(sq / (float)H + eps);
   float s8 = 1.0f, amax = 0.0f;
-  bool count = true;
-  if constexpr (OUT8) {
-    s8 = q.scale[0];
-    count = active && (q.pos == nullptr || q.pos[row] >= 0);
-  }
+  if constexpr (OUT8) s8 = q.scale[0];
+#pragma unroll 1
+  for (int r = 0; r < RW; ++r) {
+    // Every wave reaches the block amax reduction below; a wave past the last
+    // row works on the last row and stores nothing.
+    const int64_t row_ = row0 + 4 * r;
+    const bool active = row_ < M;
+    const int64_t row = active ? row_ : M - 1;
+    const bf16_t* xr = x + row * H;
+    float v[CH][8];
+    float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int c = lane + 64 * i;
-    if (c < chunks) {
-      const u32x4 g = *(const u32x4*)(gamma + c * 8);
-      const u32x4 b = *(const u32x4*)(beta + c * 8);
-      float o[8];
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) {
+        const u32x4 w = *(const u32x4*)(xr + c * 8);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[2 * e] = v[i][2 * e] * rstd * bflo(g[e]) + bflo(b[e]);
-        o[2 * e + 1] = v[i][2 * e + 1] * rstd * bfhi(g[e]) + bfhi(b[e]);
+        for (int e = 0; e < 4; ++e) {
+          v[i][2 * e] = bflo(w[e]);
+          v[i][2 * e + 1] = bfhi(w[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += v[i][e];
       }
-      if constexpr (OUT8) {
-        const float lo[4] = {o[0], o[1], o[2], o[3]}, hi[4] = {o[4], o[5], o[6], o[7]};
-        if (count)
+    }
 #pragma unroll
-          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(o[e]));
-        if (active) *(u32x2*)(q.y + row * H + c * 8) = u32x2{pack_e4m3x4(lo, s8), pack_e4m3x4(hi, s8)};
-      } else {
-        *(u32x4*)(y + row * H + c * 8) =
-            u32x4{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7])};
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    const float mean = sum / (float)H;
+    float sq = 0.f;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          v[i][e] -= mean;
+          sq += v[i][e] * v[i][e];
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
+    const float rstd = 1.0f / sqrtf(sq / (float)H + eps);
+    bool count = true;
+    if constexpr (OUT8) count = active && (q.pos == nullptr || q.pos[row] >= 0);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) {
+        const u32x4 g = *(const u32x4*)(gamma + c * 8);
+        const u32x4 b = *(const u32x4*)(beta + c * 8);
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[2 * e] = v[i][2 * e] * rstd * bflo(g[e]) + bflo(b[e]);
+          o[2 * e + 1] = v[i][2 * e + 1] * rstd * bfhi(g[e]) + bfhi(b[e]);
+        }
+        if constexpr (OUT8) {
+          const float lo[4] = {o[0], o[1], o[2], o[3]}, hi[4] = {o[4], o[5], o[6], o[7]};
+          if (count)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(o[e]));
+          if (active) *(u32x2*)(q.y + row * H + c * 8) = u32x2{pack_e4m3x4(lo, s8), pack_e4m3x4(hi, s8)};
+        } else {
+          *(u32x4*)(y + row * H + c * 8) =
+              u32x4{pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]), pack_bf2(o[4], o[5]), pack_bf2(o[6], o[7])};
+        }
       }
     }
   }
@@ -241,7 +248,8 @@ hipError_t launch_embed(const int32_t* ids, const bf16_t* table, int32_t vocab, 
 template <bool OUT8>
 hipError_t layernorm_ch(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y, int64_t M, int32_t H,
                         float eps, const E4m3Out& q, hipStream_t st) {
-  const unsigned grid = (unsigned)((M + 3) / 4);
+  const int rows = 4 * (OUT8 ? kLnRows8 : 1);  // rows per workgroup
+  const unsigned grid = (unsigned)((M + rows - 1) / rows);
   const int ch = (H / 8 + 63) / 64;
   if (ch <= 1) hipLaunchKernelGGL((k_layernorm<1, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
   else if (ch <= 2) hipLaunchKernelGGL((k_layernorm<2, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);

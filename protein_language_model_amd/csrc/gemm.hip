@@ -380,6 +380,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     } else {
       bool zero_row = false;
       if constexpr (EPI == EPI_BIAS_RESIDUAL) zero_row = a.zero_pad_rows && a.pos[mc] < 0;
+      bool count_row = false;  // E4M3 output: row enters the amax (in range, not padding)
+      if constexpr (OUT8) count_row = m < M && (a.pos == nullptr || a.pos[mc] >= 0);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
 #pragma unroll
@@ -398,9 +400,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
             for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
           }
           if constexpr (OUT8) {
-            if (m < M && n < N && (a.pos == nullptr || a.pos[mc] >= 0))
-#pragma unroll
-              for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(v[e]));
+            const float vm = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+            if (count_row && n < N) amax = fmaxf(amax, vm);
             // four consecutive E4M3 bytes at byte cl of the staged row
             *(uint32_t*)(stage + soff(row, cl / 16) + (cl % 16)) = pack_e4m3x4(v, oscale);
           } else {
