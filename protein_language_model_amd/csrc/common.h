@@ -27,8 +27,12 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(bf16_t, h);
 }
+// Two floats -> two bfloat16 (RNE) in one word, lo in bits 0..15: one
+// v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Operand element types of the GEMM.
