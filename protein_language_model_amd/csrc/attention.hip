@@ -65,8 +65,10 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const bf16x8*)(Qg + (start + qc) * kHeadDim + kk * 16 + 8 * lhalf);
 
-  u32x4 kr[2], vr[2];
-  auto gload = [&](int j) {
+  // K/V tiles travel global -> registers -> LDS.  Two register sets (A, B)
+  // keep the loads of the next two tiles in flight while a tile is used.
+  u32x4 krA[2], vrA[2], krB[2], vrB[2];
+  auto gload = [&](int j, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
       vr[i] = *(const u32x4*)(Vg + (start + key) * kHeadDim + ch * 8);
     }
   };
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
@@ -100,92 +102,102 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
   const int n0_lane = 16 * ((lane >> 4) & 1);
 
   const int ntk = (L + kKT - 1) / kKT;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int j = 0; j < ntk; ++j) {
+  // A wave whose 32 query rows all lie past the end of the sequence only helps
+  // to stage K/V (and meets the barriers); it skips the math.
+  const bool wave_active = q0 + 32 * wave < L;
+  // Tile j is in LDS buffer j & 1; its successor is in registers `nx` and the
+  // one after that is loaded into `nn` during tile j.
+  auto run_tile = [&](int j, const u32x4 (&nxk)[2], const u32x4 (&nxv)[2], u32x4 (&nnk)[2], u32x4 (&nnv)[2]) {
     const int cur = j & 1;
-    if (j + 1 < ntk) gload(j + 1);
-
-    // S^T for this tile: two 32-key blocks.
-    f32x16 st[2];
+    if (j + 2 < ntk) gload(j + 2, nnk, nnv);
+    if (wave_active) {
+      // S^T for this tile: two 32-key blocks.
+      f32x16 st[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 kf = *(const bf16x8*)(&sk[cur][(kb * 32 + lrow) * kLdsRow + kk * 16 + 8 * lhalf]);
-        st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], st[kb], 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 kf = *(const bf16x8*)(&sk[cur][(kb * 32 + lrow) * kLdsRow + kk * 16 + 8 * lhalf]);
+          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], st[kb], 0, 0, 0);
+        }
       }
-    }
-    if ((j + 1) * kKT > L) {
+      if ((j + 1) * kKT > L) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j * kKT + kb * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+            if (key >= L) st[kb][r] = -INFINITY;
+          }
+      }
+      float mx = st[0][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_i, mx);
+      const float alpha = exp2_fast((m_i - m_new) * kScaleLog2);
+      const float mc = m_new * kScaleLog2;
+      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = j * kKT + kb * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-          if (key >= L) st[kb][r] = -INFINITY;
+          const float p = exp2_fast(fmaf(st[kb][r], kScaleLog2, -mc));
+          st[kb][r] = p;
+          rs += p;
         }
-    }
-    float mx = st[0][0];
+      l_i = l_i * alpha + rs;
+      m_i = m_new;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_i, mx);
-    const float alpha = exp2_fast((m_i - m_new) * kScaleLog2);
-    const float mc = m_new * kScaleLog2;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_fast(fmaf(st[kb][r], kScaleLog2, -mc));
-        st[kb][r] = p;
-        rs += p;
-      }
-    l_i = l_i * alpha + rs;
-    m_i = m_new;
-#pragma unroll
-    for (int d = 0; d < 2; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
 
-    // P^T as bf16 operand B: block kb, step u covers registers 8u .. 8u+7.
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4 w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf2(st[kb][8 * u + 2 * e], st[kb][8 * u + 2 * e + 1]);
-        pb[kb][u] = __builtin_bit_cast(bf16x8, w);
-      }
-
-    const bf16_t* vb = sv[cur];
-#pragma unroll
-    for (int d = 0; d < 2; ++d) {
-      const int n0 = d * 32 + n0_lane;
+      // P^T as bf16 operand B: block kb, step u covers registers 8u .. 8u+7.
+      bf16x8 pb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int k0 = kb * 32 + 16 * u + 4 * lhalf;
-          const bf16_t* p0 = vb + (k0 + tr_row) * kLdsRow + n0 + tr_col;
-          const bf16_t* p1 = p0 + 8 * kLdsRow;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
-          const i16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[kb][u], o[d], 0, 0, 0);
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = pack_bf2(st[kb][8 * u + 2 * e], st[kb][8 * u + 2 * e + 1]);
+          pb[kb][u] = __builtin_bit_cast(bf16x8, w);
         }
-    }
 
-    if (j + 1 < ntk) sstore(cur ^ 1);
+      const bf16_t* vb = sv[cur];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const int n0 = d * 32 + n0_lane;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int k0 = kb * 32 + 16 * u + 4 * lhalf;
+            const bf16_t* p0 = vb + (k0 + tr_row) * kLdsRow + n0 + tr_col;
+            const bf16_t* p1 = p0 + 8 * kLdsRow;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            const i16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[kb][u], o[d], 0, 0, 0);
+          }
+      }
+    }
+    if (j + 1 < ntk) sstore(cur ^ 1, nxk, nxv);
     __syncthreads();
+  };
+  gload(0, krA, vrA);
+  sstore(0, krA, vrA);
+  if (ntk > 1) gload(1, krA, vrA);
+  __syncthreads();
+  for (int j = 0; j < ntk; j += 2) {
+    run_tile(j, krA, vrA, krB, vrB);
+    if (j + 1 < ntk) run_tile(j + 1, krB, vrB, krA, vrA);
   }
 
   const float lt = l_i + __shfl_xor(l_i, 32);
