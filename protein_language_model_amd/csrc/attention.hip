@@ -19,8 +19,11 @@
 //    the next MFMA (keys permuted within 16-key groups, bits 2 and 3 of the key
 //    index swapped), and V^T comes straight from a row-major V tile in LDS via
 //    ds_read_b64_tr_b16 with the same key permutation.
-//  * K/V tiles are double-buffered in LDS (rows padded to 72 elements); the
-//    next tile is fetched into registers during the current tile's math.
+//  * K/V tiles are double-buffered in LDS as 128-byte rows whose 16-byte
+//    chunks are XOR-swizzled by row (kSwz), so that the key fragment reads
+//    and the transposing V reads hit distinct banks.  The next tile is loaded
+//    straight into LDS (global_load_lds) during the current tile's math, which
+//    keeps no staging registers: 4 waves per SIMD fit.
 //  * Key rows past the end of the sequence are clamped to its last row (never a
 //    neighbour's row) and their scores set to -inf; query rows past the end are
 //    computed from a clamped row and not stored.
@@ -31,14 +34,22 @@ namespace esm {
 namespace {
 
 constexpr int kKT = 64;     // keys per tile
-constexpr int kLdsRow = 72; // padded LDS row (elements)
+constexpr int kLdsRow = 64; // LDS row (elements): one 128-byte row per key
 constexpr float kScaleLog2 = 0.18033688011112042f;  // log2(e) / sqrt(64)
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
+// Chunk swizzle of LDS row r (16-byte chunk c is stored at c ^ kSwz(r)).  Over
+// any 8 consecutive rows it is a permutation (key reads: eight rows, one chunk
+// each, per 128-byte bank sweep); rows 4i..4i+3 get distinct values of bit 1..2
+// and rows r, r+2 differ in bit 2 (transposing V reads: four rows, 32 or 64
+// bytes each); rows r and r+8 differ in bit 1, so the even (odd) rows of 16
+// are distinct too (key reads with a 256-byte bank sweep).
+__device__ __forceinline__ int kSwz(int r) { return (((r & 3) << 1) | ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1); }
+
+__global__ __launch_bounds__(256, 4) void k_attention(AttnArgs a) {
   const int heads = a.heads;
   const int tile = blockIdx.x / heads, head = blockIdx.x % heads;
   if (tile >= *a.ntiles) return;
@@ -47,8 +58,8 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
   const int L = a.segs[2 * s + 1];
   if (L <= 0) return;
 
-  __shared__ __attribute__((aligned(16))) bf16_t sk[2][kKT * kLdsRow];
-  __shared__ __attribute__((aligned(16))) bf16_t sv[2][kKT * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) bf16_t sk[2][kKT * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) bf16_t sv[2][kKT * kLdsRow];
 
   const int64_t T = a.T;
   const bf16_t* __restrict__ Qg = a.qkv + ((int64_t)(0 * heads + head) * T) * kHeadDim;
@@ -65,25 +76,29 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const bf16x8*)(Qg + (start + qc) * kHeadDim + kk * 16 + 8 * lhalf);
 
-  // K/V tiles travel global -> registers -> LDS.  Two register sets (A, B)
-  // keep the loads of the next two tiles in flight while a tile is used.
-  u32x4 krA[2], vrA[2], krB[2], vrB[2];
-  auto gload = [&](int j, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
+  // K/V tiles go straight from global memory into LDS (global_load_lds): the
+  // workgroup's 8 instructions per tensor fill 1 KB (8 rows) each; in
+  // instruction i of wave w, lane l writes physical chunk l % 8 of tile row
+  // 8 (w + 4 i) + l / 8 and so fetches that row's logical chunk
+  // (l % 8) ^ kSwz(row).  Key rows past the end of the sequence are clamped.
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sk[0][0];
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sv[0][0];
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int src_row[2], src_col[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    src_row[i] = 8 * (wave + 4 * i) + (lane >> 3);
+    src_col[i] = ((lane & 7) ^ kSwz(src_row[i])) * 8;
+  }
+  auto gload = [&](int j, int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      int key = j * kKT + row;
+      int key = j * kKT + src_row[i];
       key = key < L ? key : L - 1;
-      kr[i] = *(const u32x4*)(Kg + (start + key) * kHeadDim + ch * 8);
-      vr[i] = *(const u32x4*)(Vg + (start + key) * kHeadDim + ch * 8);
-    }
-  };
-  auto sstore = [&](int buf, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, ch = c & 7;
-      *(u32x4*)(&sk[buf][row * kLdsRow + ch * 8]) = kr[i];
-      *(u32x4*)(&sv[buf][row * kLdsRow + ch * 8]) = vr[i];
+      const int64_t at = (start + key) * kHeadDim + src_col[i];
+      const uint32_t dst = (uint32_t)(buf * kKT * kLdsRow * 2 + (wave_u + 4 * i) * 1024);
+      lds_dma16(Kg + at, lds_k + dst);
+      lds_dma16(Vg + at, lds_v + dst);
     }
   };
 
@@ -100,16 +115,32 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
   const int g16 = lane & 15;
   const int tr_row = g16 >> 2, tr_col = 4 * (g16 & 3);
   const int n0_lane = 16 * ((lane >> 4) & 1);
+  // Swizzled in-row offsets (elements).  Key reads: row kb*32 + lrow, chunk
+  // 2*kk + lhalf.  V reads: rows k0 + tr_row (+8), chunk of column n0 + tr_col;
+  // 16u and 32kb leave the swizzle unchanged.
+  int koff[4], voff[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = ((2 * kk + lhalf) ^ kSwz(lrow)) * 8;
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 4 * lhalf + tr_row + 8 * h, col = d * 32 + n0_lane + tr_col;
+      voff[d][h] = (((col >> 3) ^ kSwz(r)) * 8) + (col & 7);
+    }
 
   const int ntk = (L + kKT - 1) / kKT;
   // A wave whose 32 query rows all lie past the end of the sequence only helps
   // to stage K/V (and meets the barriers); it skips the math.
   const bool wave_active = q0 + 32 * wave < L;
-  // Tile j is in LDS buffer j & 1; its successor is in registers `nx` and the
-  // one after that is loaded into `nn` during tile j.
-  auto run_tile = [&](int j, const u32x4 (&nxk)[2], const u32x4 (&nxv)[2], u32x4 (&nnk)[2], u32x4 (&nnv)[2]) {
+  // Tile j is in LDS buffer j & 1; tile j + 1 is fetched into the other
+  // buffer during tile j's math and published by the barrier that ends it.
+  gload(0, 0);
+  vm_wait_all();
+  __syncthreads();
+  for (int j = 0; j < ntk; ++j) {
     const int cur = j & 1;
-    if (j + 2 < ntk) gload(j + 2, nnk, nnv);
+    if (j + 1 < ntk) gload(j + 1, cur ^ 1);
     if (wave_active) {
       // S^T for this tile: two 32-key blocks.
       f32x16 st[2];
@@ -119,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
         for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 kf = *(const bf16x8*)(&sk[cur][(kb * 32 + lrow) * kLdsRow + kk * 16 + 8 * lhalf]);
+          const bf16x8 kf = *(const bf16x8*)(&sk[cur][(kb * 32 + lrow) * kLdsRow + koff[kk]]);
           st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], st[kb], 0, 0, 0);
         }
       }
@@ -172,14 +203,13 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
       const bf16_t* vb = sv[cur];
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
-        const int n0 = d * 32 + n0_lane;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int k0 = kb * 32 + 16 * u + 4 * lhalf;
-            const bf16_t* p0 = vb + (k0 + tr_row) * kLdsRow + n0 + tr_col;
-            const bf16_t* p1 = p0 + 8 * kLdsRow;
+            const bf16_t* p0 = vb + (k0 + tr_row) * kLdsRow + voff[d][0];
+            const bf16_t* p1 = vb + (k0 + tr_row + 8) * kLdsRow + voff[d][1];
             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
             const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
             typedef short i16x8 __attribute__((ext_vector_type(8)));
@@ -188,16 +218,8 @@ __global__ __launch_bounds__(256, 2) void k_attention(AttnArgs a) {
           }
       }
     }
-    if (j + 1 < ntk) sstore(cur ^ 1, nxk, nxv);
+    vm_wait_all();
     __syncthreads();
-  };
-  gload(0, krA, vrA);
-  sstore(0, krA, vrA);
-  if (ntk > 1) gload(1, krA, vrA);
-  __syncthreads();
-  for (int j = 0; j < ntk; j += 2) {
-    run_tile(j, krA, vrA, krB, vrB);
-    if (j + 1 < ntk) run_tile(j + 1, krB, vrB, krA, vrA);
   }
 
   const float lt = l_i + __shfl_xor(l_i, 32);

@@ -63,6 +63,17 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(const float (&v)[4], float s) {
 }
 
 // Maximum of a non-negative per-lane value over the wave (fmaxf drops NaN).
+// Direct-to-LDS 16-byte load: lane i's 16 bytes from g land at LDS byte
+// lds_base + 16 i (lds_base must be wave-uniform; it goes through M0).  Issued
+// as inline assembly so the compiler keeps exact LDS wait counts for the
+// fragment reads; the caller waits with vm_wait_all() before the barrier that
+// publishes the tile.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ float wave_max(float m) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));

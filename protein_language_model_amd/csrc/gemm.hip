@@ -45,16 +45,6 @@ constexpr int kRowBytes = 128;  // bytes of each tile row per K step
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// Direct-to-LDS 16-byte load: lane i's 16 bytes from g land at LDS byte
-// lds_base + 16 i (lds_base must be wave-uniform; it goes through M0).  Issued
-// as inline assembly so the compiler keeps exact LDS wait counts for the
-// fragment reads; the caller waits with vm_wait_all() before the barrier that
-// publishes the tile.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
