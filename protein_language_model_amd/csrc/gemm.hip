@@ -49,24 +49,38 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// GELU(z) = z * Phi(z) = z/2 * (1 + erf(z / sqrt 2)).  The pages name a
-// fused activation only; the erf form is the definition used here.  erf comes
-// from Abramowitz & Stegun, Handbook of Mathematical Functions, formula
-// 7.1.26: erf(x) = 1 - (a1 t + ... + a5 t^5) exp(-x^2), t = 1 / (1 + p x),
-// x >= 0, |error| <= 1.5e-7 (odd extension for x < 0).
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
-  return copysignf(fmaf(-poly, e, 1.0f), x);
-}
-__device__ __forceinline__ float gelu_erf(float z) {
-  return 0.5f * z * (1.0f + erf_as7126(z * 0.70710678118654752f));
+// GELU(z) = z Phi(z), Phi the standard normal CDF (the exact, erf form; the
+// pages name a fused activation only).  With q = Phi(-|z|), GELU(z) is
+// z (1 - q) for z >= 0 and z q for z < 0, so the negative tail is a product
+// (no cancellation, sign kept).  q = 2^P(|z|) for |z| < 9, P a degree-9
+// polynomial fitted to log2 Phi(-a) on [0, 9] (gelu_tail_fit.py), and 0
+// beyond (Phi(-9) < 2^-62).  In fp32 |q - Phi(-|z|)| <= 6e-8, and relative to
+// Phi(-|z|) <= 3e-6 for |z| < 4 and <= 2.2e-4 for |z| < 5.  One exp2 and nine
+// FMAs replace the reciprocal, exp and polynomial of a rational erf formula.
+// GELU(+inf) = +inf, GELU(-inf) = NaN (as -inf * 0), NaN stays NaN.
+constexpr float kGeluP0 = -0.9999998807907104f;
+constexpr float kGeluP1 = -1.1511088609695435f;
+constexpr float kGeluP2 = -0.45918339490890503f;
+constexpr float kGeluP3 = -0.05255480110645294f;
+constexpr float kGeluP4 = 0.007119309157133102f;
+constexpr float kGeluP5 = -0.00014933945203665644f;
+constexpr float kGeluP6 = -0.00020084103744011372f;
+constexpr float kGeluP7 = 5.0493708840804175e-05f;
+constexpr float kGeluP8 = -5.732852514483966e-06f;
+constexpr float kGeluP9 = 2.664637577254325e-07f;
+__device__ __forceinline__ float gelu(float z) {
+  const float az = fabsf(z);
+  float p = fmaf(kGeluP9, az, kGeluP8);
+  p = fmaf(p, az, kGeluP7);
+  p = fmaf(p, az, kGeluP6);
+  p = fmaf(p, az, kGeluP5);
+  p = fmaf(p, az, kGeluP4);
+  p = fmaf(p, az, kGeluP3);
+  p = fmaf(p, az, kGeluP2);
+  p = fmaf(p, az, kGeluP1);
+  p = fmaf(p, az, kGeluP0);
+  const float q = az < 9.0f ? __builtin_amdgcn_exp2f(p) : 0.0f;  // P is only fitted below 9
+  return z * (z >= 0.0f ? 1.0f - q : q);
 }
 
 template <int DT>
@@ -310,6 +324,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   if constexpr (DT == kE4M3) dq = 1.0f / (a.x_scale[0] * a.w_scale[0]);
   float oscale = 1.0f, amax = 0.0f;
   if constexpr (OUT8) oscale = a.y8_scale[0];
+  // Bias of this lane's output columns nw + 32 j + 8 gq + 4 lhalf + 0..3,
+  // loaded once per tile (zeros without a bias or past N; N is a multiple of
+  // 64, so a wave's 64 columns are all in range or all out).
+  static_assert(FN == 2, "the epilogue assumes 64-column wave tiles");
+  u32x2 bcache[FN][4];
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int n = nw + j * 32 + 8 * gq + 4 * lhalf;
+      bcache[j][gq] = (bias && nw < N) ? *(const u32x2*)(bias + n) : u32x2{0u, 0u};
+    }
 
 #pragma unroll
   for (int c0 = 0; c0 < WTM; c0 += ECH) {
@@ -334,38 +360,43 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     if constexpr (EPI == EPI_QKV_ROPE) {
       int p = a.pos[mc];
       p = p < 0 ? 0 : (p < a.max_positions ? p : a.max_positions - 1);
-#pragma unroll
-      for (int j = 0; j < FN; j += 2) {
+      // The wave's 64 columns are one head's q, k or v (c = 0, 1, 2): dims
+      // d = 8 gq + 4 lhalf + e of this lane pair with d + 32.  Rotation
+      // factors (cos, sin) of row position p for those 16 dims, loaded at once.
+      const int c = (nw % 192) / 64;
+      float4 rc[4][2];
+      if (c < 2) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int cl = j * 32 + 8 * gq + 4 * lhalf;  // local column of the low half
-          const int nlo = nw + cl;
-          const int c = (nlo % 192) / 64, d = nlo % 64;  // d < 32
-          float lo[4], hi[4];
+          const float4* cs = (const float4*)(a.rope + (int64_t)p * 32 + 8 * gq + 4 * lhalf);
+          rc[gq][0] = cs[0];
+          rc[gq][1] = cs[1];
+        }
+      }
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int cl = 8 * gq + 4 * lhalf;  // local column of the low half
+        float lo[4], hi[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = acc[i][0][4 * gq + e] * dq;
+          hi[e] = acc[i][1][4 * gq + e] * dq;
+        }
+        const u32x2 bl = bcache[0][gq], bh = bcache[1][gq];
+        lo[0] += bflo(bl[0]); lo[1] += bfhi(bl[0]); lo[2] += bflo(bl[1]); lo[3] += bfhi(bl[1]);
+        hi[0] += bflo(bh[0]); hi[1] += bfhi(bh[0]); hi[2] += bflo(bh[1]); hi[3] += bfhi(bh[1]);
+        if (c < 2) {
+          const float cs_[4] = {rc[gq][0].x, rc[gq][0].z, rc[gq][1].x, rc[gq][1].z};
+          const float sn_[4] = {rc[gq][0].y, rc[gq][0].w, rc[gq][1].y, rc[gq][1].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            lo[e] = acc[i][j][4 * gq + e] * dq;
-            hi[e] = acc[i][j + 1][4 * gq + e] * dq;
+            const float x0 = lo[e], x1 = hi[e];
+            lo[e] = x0 * cs_[e] - x1 * sn_[e];
+            hi[e] = x1 * cs_[e] + x0 * sn_[e];
           }
-          if (bias && nlo < N) {
-            const u32x2 bl = *(const u32x2*)(bias + nlo);
-            const u32x2 bh = *(const u32x2*)(bias + nlo + 32);
-            lo[0] += bflo(bl[0]); lo[1] += bfhi(bl[0]); lo[2] += bflo(bl[1]); lo[3] += bfhi(bl[1]);
-            hi[0] += bflo(bh[0]); hi[1] += bfhi(bh[0]); hi[2] += bflo(bh[1]); hi[3] += bfhi(bh[1]);
-          }
-          if (c < 2) {
-            const float2* cs = a.rope + (int64_t)p * 32 + d;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float2 t = cs[e];
-              const float x0 = lo[e], x1 = hi[e];
-              lo[e] = x0 * t.x - x1 * t.y;
-              hi[e] = x1 * t.x + x0 * t.y;
-            }
-          }
-          *(u32x2*)(stage + soff(row, cl / 8) + 8 * lhalf) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
-          *(u32x2*)(stage + soff(row, cl / 8 + 4) + 8 * lhalf) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
         }
+        *(u32x2*)(stage + soff(row, cl / 8) + 8 * lhalf) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
+        *(u32x2*)(stage + soff(row, cl / 8 + 4) + 8 * lhalf) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
       }
     } else {
       bool zero_row = false;
@@ -381,13 +412,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e] * dq;
-          if (bias && n < N) {
-            const u32x2 bb = *(const u32x2*)(bias + n);
+          {
+            const u32x2 bb = bcache[j][gq];
             v[0] += bflo(bb[0]); v[1] += bfhi(bb[0]); v[2] += bflo(bb[1]); v[3] += bfhi(bb[1]);
           }
           if constexpr (EPI == EPI_BIAS_GELU || OUT8) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = gelu_erf(v[e]);
+            for (int e = 0; e < 4; ++e) v[e] = gelu(v[e]);
           }
           if constexpr (OUT8) {
             const float vm = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));

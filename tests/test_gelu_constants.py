@@ -1,0 +1,81 @@
+"""The GELU of the GEMM epilogue (gemm.hip): its fitted constants, evaluated in
+float32 as the kernel evaluates them, against the exact z * Phi(z).  Host-side
+check of the kernel's constants; the kernel itself is compared with the oracle
+in the GPU tests."""
+import os
+import re
+
+import numpy as np
+from scipy.special import ndtr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "protein_language_model_amd", "csrc", "gemm.hip")
+
+
+def kernel_coefficients():
+    found = dict(re.findall(r"constexpr float kGeluP(\d+) = ([-+0-9.e]+)f;", open(SRC).read()))
+    return np.array([float(found[str(k)]) for k in range(len(found))], np.float32)
+
+
+def f32(x):
+    return np.asarray(x, np.float64).astype(np.float32)
+
+
+def gelu_as_kernel(z):
+    """Horner in |z| with one rounding per FMA, exp2 below |z| = 9 (0 beyond),
+    then z (1 - q) or z q."""
+    z = f32(z)
+    co = kernel_coefficients()
+    a = np.abs(z)
+    with np.errstate(invalid="ignore", over="ignore"):
+        p = np.full_like(a, co[-1])
+        for ck in co[-2::-1]:
+            p = f32(p.astype(np.float64) * a + np.float64(ck))
+        q = np.where(a < 9, f32(np.exp2(p.astype(np.float64))), np.float32(0))
+    t = np.where(z >= 0, f32(np.float32(1.0) - q), q)
+    with np.errstate(invalid="ignore", over="ignore"):
+        return f32(z.astype(np.float64) * t)
+
+
+def test_tail_probability_bounds():
+    co = kernel_coefficients()
+    assert len(co) == 10
+    a = np.linspace(0.0, 9.0, 90001).astype(np.float32)
+    p = np.full_like(a, co[-1])
+    for ck in co[-2::-1]:
+        p = f32(p.astype(np.float64) * a + np.float64(ck))
+    q = np.exp2(p.astype(np.float64))
+    phi = ndtr(-a.astype(np.float64))
+    err = np.abs(q - phi)
+    assert err.max() <= 7e-8
+    assert (err / phi)[a < 4].max() <= 4e-6
+    assert (err / phi)[a < 5].max() <= 3e-4
+    assert q[-1] < 2.0 ** -57   # at |z| = 9, where the kernel switches to q = 0 (Phi(-9) ~ 1.1e-19)
+
+
+def test_gelu_against_exact():
+    z = np.concatenate([np.linspace(-12, 12, 240001), -np.logspace(-30, 1.1, 2000), np.logspace(-30, 1.1, 2000)])
+    g = gelu_as_kernel(z).astype(np.float64)
+    zz = f32(z).astype(np.float64)
+    exact = zz * ndtr(zz)
+    # q's error (absolute 7e-8, relative 4e-6 below |z| = 4) plus two fp32 roundings
+    bound = 7e-8 * np.abs(zz) + 2.0 ** -23 * np.abs(exact)
+    tail = np.abs(zz) < 4
+    assert np.all(np.abs(g - exact)[tail] <= np.maximum(bound, 4e-6 * np.abs(exact) + 2.0 ** -23 * np.abs(exact))[tail])
+    assert np.all(np.abs(g - exact) <= bound + 1e-30)
+    # the sign of the result is the sign of z (no cancellation to +0 in the
+    # tail); from z = -9 down the result is -0
+    inner = (zz != 0) & (np.abs(zz) < 9) & (np.abs(exact) > 1e-37)
+    assert np.all(np.sign(g[inner]) == np.sign(zz[inner]))
+    far = zz <= -9
+    assert np.all((g[far] == 0) & np.signbit(g[far]))
+
+
+def test_gelu_special_values():
+    g = gelu_as_kernel(np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e30, -1e30, -9.5, 9.5]))
+    assert g[0] == 0 and g[1] == 0 and np.signbit(g[1])
+    assert g[2] == np.inf
+    assert np.isnan(g[3]) and np.isnan(g[4])   # -inf * Phi(-inf) = -inf * 0
+    assert g[5] == np.float32(1e30)
+    assert g[6] == 0 and np.signbit(g[6])
+    assert g[7] == 0 and np.signbit(g[7]) and g[8] == np.float32(9.5)

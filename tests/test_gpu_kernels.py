@@ -52,6 +52,30 @@ def test_linear(gu, enc_tiny, M, N, K, epi):
     assert err < 4e-3, err
 
 
+def test_gelu_epilogue_elementwise(gu, enc_650m):
+    """GELU epilogue on pre-activations known exactly: W picks one input column
+    per output (z[m, n] = x[m, n % 64], no bias), so z spans [-12, 12] with no
+    GEMM rounding.  Each output must be the exact z Phi(z) up to one bf16
+    rounding (2^-8 relative) plus the epilogue's tail error (1e-7 |z|), and
+    carry the sign of z."""
+    M, N, K = 4096, 256, 64
+    rng = np.random.default_rng(21)
+    z = np.concatenate([rng.uniform(-12, 12, M * K // 2), rng.standard_normal(M * K // 2) * 3]).reshape(M, K)
+    xb = D.to_bf16_bits(z.astype(np.float32))
+    wf = np.zeros((N, K), np.float32)
+    wf[np.arange(N), np.arange(N) % K] = 1.0
+    y = enc_650m.linear_fwd(gu.to_dev_bf16(xb), gu.to_dev_bf16(D.to_bf16_bits(wf)), gu.to_dev_bf16(D.to_bf16_bits(np.zeros(N, np.float32))),
+                            epilogue=esm.EPI_BIAS_GELU)
+    got = gu.from_dev(y)
+    zz = D.bf16_bits_to_f64(xb)[:, np.arange(N) % K]
+    ref = O.gelu(zz)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-7 * np.abs(zz) + 1e-38
+    excess = np.abs(got - ref) / bound
+    assert excess.max() <= 1.0, (excess.max(), zz.flat[excess.argmax()])
+    neg = (zz < 0) & (np.abs(ref) > 1e-30)
+    assert np.all(np.signbit(got[zz < 0])) and np.all(got[neg] < 0)
+
+
 def test_linear_large_tiles_and_in_place_residual(gu, enc_650m):
     # Enough tiles for the 256x256 configuration; residual aliases the output.
     M, N, K = 4200, 5120, 1280
