@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 2
+#define ESM_ABI_VERSION 3
 
 typedef struct esm_encoder esm_encoder;
 typedef void* esm_stream_t; /* a hipStream_t */
@@ -262,6 +262,15 @@ esm_status esm_linear_e4m3_fwd(esm_encoder* enc, const void* x8, const float* x_
 /* Row LayerNorm y = (x - mean) / sqrt(var + eps) * gamma + beta over [M, H]. */
 esm_status esm_layernorm_fwd(esm_encoder* enc, const void* x, const void* gamma,
                              const void* beta, void* y, int64_t M, esm_stream_t stream);
+
+/* The same LayerNorm with the E4M3 output that feeds an FP8 GEMM ([BIO-ACC]
+ * 2.1: the LN output is an FP8 GEMM input), as a test entry: y8[m, h] =
+ * cast(LN(x)[m, h] * scale[0]) (uint8 codes, [M, H]); max |LN(x)| over all M
+ * rows, before the cast, is atomically maxed into *amax (device uint32, float
+ * bits, caller-cleared).  x, gamma, beta bf16 as above; scale device float. */
+esm_status esm_layernorm_e4m3_fwd(esm_encoder* enc, const void* x, const void* gamma,
+                                  const void* beta, const float* scale, void* y8, uint32_t* amax,
+                                  int64_t M, esm_stream_t stream);
 
 /* ---------------------------------------------------------------- FP8 delayed scaling */
 

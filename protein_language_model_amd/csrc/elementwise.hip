@@ -125,7 +125,12 @@ __global__ void k_embed(const int32_t* __restrict__ ids, const bf16_t* __restric
   *(u32x4*)(x + t * H + c * 8) = *(const u32x4*)(table + (int64_t)id * H + c * 8);
 }
 
-constexpr int kLnRows8 = 4;  // rows per wave of the E4M3-output LayerNorm
+// Rows per wave: the E4M3-output LayerNorm normalises several rows per wave,
+// so that fewer workgroups fold their amax into the tensor's one amax word;
+// all of a wave's rows are loaded before the first is reduced, so their
+// memory latencies overlap.
+template <int CH, bool OUT8>
+constexpr int ln_rows_per_wave() { return OUT8 && CH <= 5 ? 2 : 1; }
 
 // Row LayerNorm, one wave per row: mean, then the biased variance from the
 // centred values held in registers, y = (x - mean) * rsqrt(var + eps) * g + b
@@ -136,9 +141,7 @@ template <int CH, bool OUT8>
 __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
                                                    const bf16_t* __restrict__ beta, bf16_t* __restrict__ y,
                                                    int64_t M, int32_t H, float eps, E4m3Out q) {
-  // E4M3 output: each wave normalises kLnRows8 rows, so that fewer workgroups
-  // fold their amax into the tensor's one amax word.
-  constexpr int RW = OUT8 ? kLnRows8 : 1;
+  constexpr int RW = ln_rows_per_wave<CH, OUT8>();
   const int lane = threadIdx.x & 63;
   const int64_t row0 = (int64_t)blockIdx.x * (4 * RW) + (threadIdx.x >> 6);
   if constexpr (!OUT8) {
@@ -147,21 +150,48 @@ __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x,
   const int chunks = H / 8;
   float s8 = 1.0f, amax = 0.0f;
   if constexpr (OUT8) s8 = q.scale[0];
-#pragma unroll 1
+  // Every wave reaches the block amax reduction below; a wave past the last
+  // row works on the last row and stores nothing.
+  u32x4 raw[RW][CH], graw[CH], braw[CH];
+  bool count[RW];  // E4M3 output: the row enters the amax (in range, not padding)
+#pragma unroll
   for (int r = 0; r < RW; ++r) {
-    // Every wave reaches the block amax reduction below; a wave past the last
-    // row works on the last row and stores nothing.
+    const int64_t row_ = row0 + 4 * r;
+    const int64_t row = row_ < M ? row_ : M - 1;
+    const bf16_t* xr = x + row * H;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) raw[r][i] = *(const u32x4*)(xr + c * 8);
+    }
+    count[r] = true;
+    if constexpr (OUT8) count[r] = row_ < M && (q.pos == nullptr || q.pos[row] >= 0);
+  }
+  // gamma and beta: loaded with the rows when a wave has several of them,
+  // else at the output (fewer live registers)
+  auto load_gb = [&](int i) {
+    const int c = lane + 64 * i;
+    if (c < chunks) {
+      graw[i] = *(const u32x4*)(gamma + c * 8);
+      braw[i] = *(const u32x4*)(beta + c * 8);
+    }
+  };
+  if constexpr (RW > 1) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) load_gb(i);
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
     const int64_t row_ = row0 + 4 * r;
     const bool active = row_ < M;
     const int64_t row = active ? row_ : M - 1;
-    const bf16_t* xr = x + row * H;
     float v[CH][8];
     float sum = 0.f;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = lane + 64 * i;
       if (c < chunks) {
-        const u32x4 w = *(const u32x4*)(xr + c * 8);
+        const u32x4 w = raw[r][i];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           v[i][2 * e] = bflo(w[e]);
@@ -189,14 +219,13 @@ __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x,
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sq += __shfl_xor(sq, off);
     const float rstd = 1.0f / sqrtf(sq / (float)H + eps);
-    bool count = true;
-    if constexpr (OUT8) count = active && (q.pos == nullptr || q.pos[row] >= 0);
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
       const int c = lane + 64 * i;
       if (c < chunks) {
-        const u32x4 g = *(const u32x4*)(gamma + c * 8);
-        const u32x4 b = *(const u32x4*)(beta + c * 8);
+        if constexpr (RW == 1) load_gb(i);
+        const u32x4 g = graw[i];
+        const u32x4 b = braw[i];
         float o[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -205,7 +234,7 @@ __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x,
         }
         if constexpr (OUT8) {
           const float lo[4] = {o[0], o[1], o[2], o[3]}, hi[4] = {o[4], o[5], o[6], o[7]};
-          if (count)
+          if (count[r])
 #pragma unroll
             for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(o[e]));
           if (active) *(u32x2*)(q.y + row * H + c * 8) = u32x2{pack_e4m3x4(lo, s8), pack_e4m3x4(hi, s8)};
@@ -245,17 +274,23 @@ hipError_t launch_embed(const int32_t* ids, const bf16_t* table, int32_t vocab, 
   return hipGetLastError();
 }
 
+template <int CH, bool OUT8>
+void launch_ln(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y, int64_t M, int32_t H, float eps,
+               const E4m3Out& q, hipStream_t st) {
+  const int rows = 4 * ln_rows_per_wave<CH, OUT8>();  // rows per workgroup
+  const unsigned grid = (unsigned)((M + rows - 1) / rows);
+  hipLaunchKernelGGL((k_layernorm<CH, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
+}
+
 template <bool OUT8>
 hipError_t layernorm_ch(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y, int64_t M, int32_t H,
                         float eps, const E4m3Out& q, hipStream_t st) {
-  const int rows = 4 * (OUT8 ? kLnRows8 : 1);  // rows per workgroup
-  const unsigned grid = (unsigned)((M + rows - 1) / rows);
   const int ch = (H / 8 + 63) / 64;
-  if (ch <= 1) hipLaunchKernelGGL((k_layernorm<1, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
-  else if (ch <= 2) hipLaunchKernelGGL((k_layernorm<2, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
-  else if (ch <= 3) hipLaunchKernelGGL((k_layernorm<3, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
-  else if (ch <= 5) hipLaunchKernelGGL((k_layernorm<5, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
-  else if (ch <= 8) hipLaunchKernelGGL((k_layernorm<8, OUT8>), dim3(grid), dim3(256), 0, st, x, gamma, beta, y, M, H, eps, q);
+  if (ch <= 1) launch_ln<1, OUT8>(x, gamma, beta, y, M, H, eps, q, st);
+  else if (ch <= 2) launch_ln<2, OUT8>(x, gamma, beta, y, M, H, eps, q, st);
+  else if (ch <= 3) launch_ln<3, OUT8>(x, gamma, beta, y, M, H, eps, q, st);
+  else if (ch <= 5) launch_ln<5, OUT8>(x, gamma, beta, y, M, H, eps, q, st);
+  else if (ch <= 8) launch_ln<8, OUT8>(x, gamma, beta, y, M, H, eps, q, st);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -705,6 +705,22 @@ esm_status esm_layernorm_fwd(esm_encoder* e, const void* x, const void* gamma, c
   });
 }
 
+esm_status esm_layernorm_e4m3_fwd(esm_encoder* e, const void* x, const void* gamma, const void* beta,
+                                  const float* scale, void* y8, uint32_t* amax, int64_t M, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !x || !gamma || !beta || !scale || !y8 || !amax) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(beta) || ((uintptr_t)y8 & 7u))
+    return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer");
+  if (M < 0) return fail(ESM_ERR_SHAPE, "M < 0");
+  if (M == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  return timed(e, ESM_K_LAYERNORM, (hipStream_t)stream, "layernorm e4m3", [&] {
+    return launch_layernorm((const bf16_t*)x, (const bf16_t*)gamma, (const bf16_t*)beta, nullptr, M,
+                            e->cfg.hidden_size, e->cfg.layer_norm_eps, E4m3Out{(uint8_t*)y8, scale, amax, nullptr},
+                            (hipStream_t)stream);
+  });
+}
+
 esm_status esm_linear_e4m3_fwd(esm_encoder* e, const void* x8, const float* x_scale, const void* w8,
                                const float* w_scale, const void* b, const void* res, void* y, const float* y_scale,
                                uint32_t* y_amax, int64_t M, int32_t N, int32_t K, int32_t epi, esm_stream_t stream) {

@@ -493,14 +493,16 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   // 8 waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs)
   // over 256x256 tiles (128x64 per wave), or 320x256 tiles (160x64 per wave)
   // when those need fewer rounds of workgroups over the compute units: time
-  // ~ rounds x tile rows (N = 1280 at T = 32293: 3 x 256 vs 2 x 320).  Each
-  // output element accumulates the same K order in either shape, so results
-  // do not depend on the choice.
+  // ~ rounds x tile rows (N = 1280 at T = 32293: 3 x 256 vs 2 x 320); on a
+  // tie the 320-row tiles win (fewer tiles, so fewer prologues and
+  // epilogues: N = 5120, 8 x 320 vs 10 x 256).  Each output element
+  // accumulates the same K order in either shape, so results do not depend
+  // on the choice.
   const int64_t tilesN = (a.N + 255) / 256;
   const int64_t cus = device_cus();
   const int64_t r256 = ((a.M + 255) / 256 * tilesN + cus - 1) / cus;
   const int64_t r320 = ((a.M + 319) / 320 * tilesN + cus - 1) / cus;
-  const bool tall = r320 * 320 < r256 * 256;
+  const bool tall = r320 * 320 <= r256 * 256;
   if (a.dtype == kE4M3)
     return tall ? run<320, 256, 2, 4, EPI, kE4M3>(a, st) : run<256, 256, 2, 4, EPI, kE4M3>(a, st);
   if constexpr (EPI == EPI_BIAS_GELU_E4M3) return hipErrorInvalidValue;

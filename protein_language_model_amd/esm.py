@@ -74,6 +74,7 @@ SIGNATURES = {
     "esm_attention_fwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_linear_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
     "esm_layernorm_fwd": (_i32, [_p, _p, _p, _p, _p, _i64, _p]),
+    "esm_layernorm_e4m3_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _p]),
     "esm_linear_e4m3_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
     "esm_fp8_prepare_layer": (_i32, [_p, _i32, ctypes.POINTER(EsmLayerWeights), _p]),
     "esm_fp8_get_state": (_i32, [_p, ctypes.POINTER(EsmFp8State), _p]),
@@ -328,6 +329,17 @@ class Encoder:
         _call("esm_layernorm_fwd", self._h, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), int(x.shape[0]),
               _stream(stream))
         return y
+
+    def layernorm_e4m3_fwd(self, x, gamma, beta, scale, *, y8=None, amax=None, stream=None):
+        """LayerNorm of bf16 x [M, H] cast to E4M3 codes with scale[0]; returns (codes, amax tensor)."""
+        import torch
+        if y8 is None:
+            y8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        if amax is None:
+            amax = torch.zeros(1, dtype=torch.int32, device=x.device)
+        _call("esm_layernorm_e4m3_fwd", self._h, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(scale), _ptr(y8),
+              _ptr(amax), int(x.shape[0]), _stream(stream))
+        return y8, amax
 
     def linear_e4m3_fwd(self, x8, x_scale, w8, w_scale, b=None, *, residual=None, epilogue: int = EPI_BIAS, y=None,
                         y_scale=None, y_amax=None, stream=None):

@@ -168,6 +168,33 @@ def test_e4m3_gemm_contracts_exact_products(gu, M, N, K, epi):
     enc.close()
 
 
+@pytest.mark.parametrize("H,M", [(1280, 1), (1280, 17), (1280, 381), (1280, 32293), (2560, 77), (2560, 1030)])
+def test_layernorm_e4m3(gu, H, M):
+    """LayerNorm with E4M3 output (several rows per wave; M not a multiple of
+    a workgroup's rows) against the oracle's fp64 LayerNorm and cast: codes
+    differ only where fp32 and fp64 fall on two sides of a rounding boundary,
+    by one step; the amax is max |LN(x)| over all rows."""
+    rng = np.random.default_rng(H + M)
+    xb = D.to_bf16_bits((rng.standard_normal((M, H)) * 3 + 0.5).astype(np.float32))
+    ln = D.random_layernorm_params(H, 3)
+    enc = esm.Encoder(hidden_size=H, num_attention_heads=H // 64, intermediate_size=4 * H, num_hidden_layers=1,
+                      precision="fp8")
+    ys = 37.0
+    y8, amax = enc.layernorm_e4m3_fwd(gu.to_dev_bf16(xb), gu.to_dev_bf16(ln["ln2_gamma"]),
+                                      gu.to_dev_bf16(ln["ln2_beta"]), _dev_f32([ys]))
+    got = _host(y8)
+    ref = O.layer_norm(D.bf16_bits_to_f64(xb), D.bf16_bits_to_f64(ln["ln2_gamma"]), D.bf16_bits_to_f64(ln["ln2_beta"]),
+                       1e-5)
+    ref_codes = F8.e4m3_encode(ref * ys)
+    diff = got != ref_codes
+    assert diff.mean() < 2e-3, diff.mean()
+    step = np.abs(got[diff].astype(int) - ref_codes[diff].astype(int))
+    assert np.all((step == 1) | ((got[diff] & 0x7F) + (ref_codes[diff] & 0x7F) == 0)), step[:20]
+    am = _f32_bits_to_float(_host(amax))[0]
+    assert abs(am / np.max(np.abs(ref)) - 1) < 1e-5
+    enc.close()
+
+
 def test_e4m3_gemm_tile_shape_does_not_change_rows(gu):
     """320-row tiles (M = 15530, N = 1280) and 256-row tiles (a 1000-row slice)
     give the same rows bit for bit."""
