@@ -51,7 +51,10 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 3
+#define ESM_ABI_VERSION 4
+
+/* Query rows per attention workgroup (the segment table's tile size). */
+#define ESM_ATTN_TILE_ROWS 256
 
 typedef struct esm_encoder esm_encoder;
 typedef void* esm_stream_t; /* a hipStream_t */
@@ -220,7 +223,7 @@ esm_status esm_stack_fwd_bshd(esm_encoder* enc, const esm_layer_weights* w,
 
 /* Segment table ([BIO-ACC] 3.2 cu_seqlens contract): writes into the workspace
  * the per-row positions (ESM_WS_POS), the sequence extents (ESM_WS_SEGS) and the
- * attention query tiles of `tile_rows` = 128 rows, longest sequence first
+ * attention query tiles of ESM_ATTN_TILE_ROWS rows, longest sequence first
  * (ESM_WS_TILES, count in ESM_WS_NTILES).  layout selects cu_seqlens (THD,
  * `lens` = cu [B+1], S ignored) or seqlens (bshd, `lens` = [B], rows b*S + p). */
 esm_status esm_segment_table(esm_encoder* enc, int32_t layout, const int32_t* lens_dev,

@@ -3,11 +3,11 @@
 // For each (sequence s, head n): ctx = softmax(q k^T / 8) v over the rows of s
 // only ([CARD] 描述: bidirectional BERT-style encoder; [BIO-ACC] 3.2: packed
 // sequences delimited by cu_seqlens; [TE-ESM2] 注意力掩码优化).  No work is
-// done across sequences: a workgroup covers one 128-row query tile of one
+// done across sequences: a workgroup covers one 256-row query tile of one
 // sequence and one head, and streams that sequence's keys in 64-row tiles.
 //
 // Design (CDNA4):
-//  * 4 waves x 32 query rows.  Scores are formed transposed, S^T = K Q^T, with
+//  * 8 waves x 32 query rows.  Scores are formed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16 (operand A = keys from LDS, operand B = the
 //    wave's queries held in registers), so each lane owns one query row
 //    (lane % 32) and 32 of the 64 keys of a tile; the other 32 live in lane
@@ -23,7 +23,9 @@
 //    chunks are XOR-swizzled by row (kSwz), so that the key fragment reads
 //    and the transposing V reads hit distinct banks.  The next tile is loaded
 //    straight into LDS (global_load_lds) during the current tile's math, which
-//    keeps no staging registers: 4 waves per SIMD fit.
+//    keeps no staging registers: 4 waves per SIMD fit (two workgroups per
+//    CU).  Eight waves share each K/V tile: half the tile fills and barriers
+//    per query of four.
 //  * Key rows past the end of the sequence are clamped to its last row (never a
 //    neighbour's row) and their scores set to -inf; query rows past the end are
 //    computed from a clamped row and not stored.
@@ -34,6 +36,8 @@ namespace esm {
 namespace {
 
 constexpr int kKT = 64;     // keys per tile
+constexpr int kNW = kAttnTileRows / 32;  // waves per workgroup, 32 query rows each
+constexpr int kDmaPerWave = 8 / kNW;     // 1 KB direct loads per tensor per wave per tile
 constexpr int kLdsRow = 64; // LDS row (elements): one 128-byte row per key
 constexpr float kScaleLog2 = 0.18033688011112042f;  // log2(e) / sqrt(64)
 
@@ -49,7 +53,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // are distinct too (key reads with a 256-byte bank sweep).
 __device__ __forceinline__ int kSwz(int r) { return (((r & 3) << 1) | ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1); }
 
-__global__ __launch_bounds__(256, 4) void k_attention(AttnArgs a) {
+__global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
   const int heads = a.heads;
   const int tile = blockIdx.x / heads, head = blockIdx.x % heads;
   if (tile >= *a.ntiles) return;
@@ -79,24 +83,24 @@ __global__ __launch_bounds__(256, 4) void k_attention(AttnArgs a) {
   // K/V tiles go straight from global memory into LDS (global_load_lds): the
   // workgroup's 8 instructions per tensor fill 1 KB (8 rows) each; in
   // instruction i of wave w, lane l writes physical chunk l % 8 of tile row
-  // 8 (w + 4 i) + l / 8 and so fetches that row's logical chunk
+  // 8 (w + kNW i) + l / 8 and so fetches that row's logical chunk
   // (l % 8) ^ kSwz(row).  Key rows past the end of the sequence are clamped.
   const uint32_t lds_k = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sk[0][0];
   const uint32_t lds_v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sv[0][0];
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  int src_row[2], src_col[2];
+  int src_row[kDmaPerWave], src_col[kDmaPerWave];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    src_row[i] = 8 * (wave + 4 * i) + (lane >> 3);
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    src_row[i] = 8 * (wave + kNW * i) + (lane >> 3);
     src_col[i] = ((lane & 7) ^ kSwz(src_row[i])) * 8;
   }
   auto gload = [&](int j, int buf) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kDmaPerWave; ++i) {
       int key = j * kKT + src_row[i];
       key = key < L ? key : L - 1;
       const int64_t at = (start + key) * kHeadDim + src_col[i];
-      const uint32_t dst = (uint32_t)(buf * kKT * kLdsRow * 2 + (wave_u + 4 * i) * 1024);
+      const uint32_t dst = (uint32_t)(buf * kKT * kLdsRow * 2 + (wave_u + kNW * i) * 1024);
       lds_dma16(Kg + at, lds_k + dst);
       lds_dma16(Vg + at, lds_v + dst);
     }
@@ -244,8 +248,8 @@ __global__ __launch_bounds__(256, 4) void k_attention(AttnArgs a) {
           *(uint32_t*)(dst + dim) = pack_e4m3x4(v, s8);
         }
     }
-    __shared__ float red[4];
-    record_amax_block<4>(a.ctx8.amax, amax, red);
+    __shared__ float red[kNW];
+    record_amax_block<kNW>(a.ctx8.amax, amax, red);
     return;
   }
   if (qrow >= L) return;
@@ -265,7 +269,7 @@ __global__ __launch_bounds__(256, 4) void k_attention(AttnArgs a) {
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.tile_cap <= 0 || a.T <= 0) return hipSuccess;
   const int64_t nblk = a.tile_cap * a.heads;
-  hipLaunchKernelGGL(k_attention, dim3((unsigned)nblk), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_attention, dim3((unsigned)nblk), dim3(64 * kNW), 0, st, a);
   return hipGetLastError();
 }
 

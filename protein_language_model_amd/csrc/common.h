@@ -16,7 +16,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kHeadDim = 64;
-constexpr int kAttnTileRows = 128;  // query rows per attention workgroup
+constexpr int kAttnTileRows = 256;  // query rows per attention workgroup (8 waves x 32)
 
 __device__ __forceinline__ float bf2f(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 __device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -11,7 +11,7 @@ namespace {
 
 constexpr int kSegThreads = 1024;
 
-// Sequence extents and the list of 128-row query tiles, longest sequence
+// Sequence extents and the list of 256-row query tiles, longest sequence
 // first ([BIO-ACC] 3.2: cu_seqlens = cumsum([0] + lengths); sequence s owns
 // rows cu[s] .. cu[s+1]-1).  One workgroup: a counting sort of the tiles by
 // sequence length (bucket = max_positions - length, so long sequences come

@@ -12,6 +12,8 @@
 #include "../../include/esm_encoder.h"
 #include "common.h"
 
+static_assert(esm::kAttnTileRows == ESM_ATTN_TILE_ROWS, "attention tile rows");
+
 using namespace esm;
 
 struct esm_encoder {

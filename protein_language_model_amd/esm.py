@@ -23,6 +23,7 @@ PRECISION = {"bf16": 0, "fp8": 1}
 LAYOUT_THD, LAYOUT_BSHD = 0, 1
 EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_E4M3 = 0, 1, 2, 3
 WS_REGIONS = {"ln1": 0, "qkv": 1, "ctx": 2, "x1": 3, "ln2": 4, "act": 5, "pos": 6, "tiles": 7, "ntiles": 8, "segs": 9}
+ATTN_TILE_ROWS = 256  # ESM_ATTN_TILE_ROWS: query rows per attention workgroup
 KERNEL_CLASSES = ("segment", "embed", "layernorm", "gemm_qkv", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
                   "other", "fp8")
 FP8_ACT_NAMES = ("ln1", "ctx", "ln2", "act")      # activation tensors tracked per layer, in state order

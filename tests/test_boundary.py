@@ -30,6 +30,7 @@ def test_library_exports_every_declared_symbol():
     src = open(HEADER).read()
     assert lib.esm_abi_version() == int(re.search(r"#define ESM_ABI_VERSION (\d+)", src).group(1))
     assert len(esm.KERNEL_CLASSES) == int(re.search(r"ESM_K_COUNT = (\d+)", src).group(1))
+    assert esm.ATTN_TILE_ROWS == int(re.search(r"#define ESM_ATTN_TILE_ROWS (\d+)", src).group(1))
 
 
 def test_fp8_state_struct_layout_matches_the_header():

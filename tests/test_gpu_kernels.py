@@ -121,7 +121,8 @@ def test_layernorm(gu, H, M):
     e.close()
 
 
-@pytest.mark.parametrize("lens", [[17, 64, 100, 200], [0, 5, 0, 1026, 1, 128, 129, 0], [1], [300] * 40])
+@pytest.mark.parametrize("lens", [[17, 64, 100, 200], [0, 5, 0, 1026, 1, 128, 129, 0], [1], [300] * 40,
+                                  [255, 256, 257, 512, 513]])
 def test_segment_table_thd(gu, enc_tiny, lens):
     cu = D.cu_from_lengths(lens)
     T, B = int(cu[-1]), len(lens)
@@ -133,7 +134,7 @@ def test_segment_table_thd(gu, enc_tiny, lens):
     assert np.array_equal(segs[:, 0], cu[:-1]) and np.array_equal(segs[:, 1], lens)
     n = int(enc_tiny.workspace_region(ws, T, B, "ntiles").cpu().numpy()[0])
     tiles = enc_tiny.workspace_region(ws, T, B, "tiles").cpu().numpy().reshape(-1, 2)[:n]
-    ref = O.query_tiles(lens, 128)
+    ref = O.query_tiles(lens, esm.ATTN_TILE_ROWS)
     # unique: the set of tiles; valid: lengths non-increasing along the list
     assert sorted(map(tuple, tiles.tolist())) == sorted(ref)
     L = [lens[s] for s, _ in tiles]
@@ -164,7 +165,8 @@ def _attention_case(gu, enc, lens, seed, qscale=1.0):
     return gu.from_dev(ctx), ref
 
 
-@pytest.mark.parametrize("lens", [[17, 64, 100, 200], [1, 2, 63, 64, 65, 127, 128, 129], [1026, 0, 3], [700, 5]])
+@pytest.mark.parametrize("lens", [[17, 64, 100, 200], [1, 2, 63, 64, 65, 127, 128, 129], [1026, 0, 3], [700, 5],
+                                  [255, 256, 257, 31, 33, 224, 225]])
 def test_attention(gu, enc_tiny, lens):
     got, ref = _attention_case(gu, enc_tiny, lens, 11)
     assert gu.rel_err(got, ref) < TOL
