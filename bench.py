@@ -58,9 +58,10 @@ def parse():
     return ap.parse_args()
 
 
-def traffic_record(kernel: str):
+def traffic_record(kernel: str, rows: int, hidden: int, ffn: int):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None when the summary is missing or was taken on a different GEMM source."""
+    None when the summary is missing, was taken on a different GEMM source or
+    on another shape (rows x hidden x ffn) than the one being measured."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
     src = os.path.join(ROOT, "protein_language_model_amd", "csrc", "gemm.hip")
@@ -71,6 +72,8 @@ def traffic_record(kernel: str):
         return None
     ent = rec.get(kernel)
     if not ent or ent.get("gemm_source_sha256") != sha:
+        return None
+    if (ent.get("rows"), ent.get("hidden"), ent.get("ffn")) != (rows, hidden, ffn):
         return None
     return ent.get("bytes_per_launch")
 
@@ -221,7 +224,7 @@ def main():
     if prof:
         kernels = kernel_table(prof)
         roofline = roofline_of(prof, fl, peaks)
-        roofline["traffic"] = traffic_record(("fp8_" if fp8_main else "") + roofline["kernel"])
+        roofline["traffic"] = traffic_record(("fp8_" if fp8_main else "") + roofline["kernel"], T, m.hidden, m.ffn)
 
     padded = None
     if args.padded:
@@ -260,7 +263,7 @@ def main():
         if prof8:
             fp8["kernels"] = kernel_table(prof8)
             fp8["roofline"] = roofline_of(prof8, fl, {k: PEAK_FP8_TFLOPS for k in fl if k.startswith("gemm")})
-            fp8["roofline"]["traffic"] = traffic_record("fp8_" + fp8["roofline"]["kernel"])
+            fp8["roofline"]["traffic"] = traffic_record("fp8_" + fp8["roofline"]["kernel"], T, m.hidden, m.ffn)
         enc8.close()
         del ws8
 

@@ -1,0 +1,39 @@
+"""Host-side pieces of bench.py: the per-launch flop counts and the HBM
+traffic record, which is only reported for the GEMM source and the shape the
+counters were taken on."""
+import importlib.util
+import json
+import os
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_layer_flops_650m():
+    b = _bench()
+    fl = b.layer_flops(1280, 5120, 32293, 16024465)
+    assert fl["gemm_fc1"] == 2.0 * 32293 * 1280 * 5120 == fl["gemm_fc2"]
+    assert fl["gemm_qkv"] == 3 * fl["gemm_out"]
+    assert fl["attention"] == 4.0 * 1280 * 16024465
+
+
+def test_traffic_record_matches_source_and_shape():
+    b = _bench()
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    ent = rec["gemm_fc1"]
+    shape = (ent["rows"], ent["hidden"], ent["ffn"])
+    got = b.traffic_record("gemm_fc1", *shape)
+    import hashlib
+    sha = hashlib.sha256(open(os.path.join(ROOT, "protein_language_model_amd", "csrc", "gemm.hip"), "rb").read()).hexdigest()
+    if ent["gemm_source_sha256"] == sha:
+        assert got == ent["bytes_per_launch"]
+    else:
+        assert got is None
+    assert b.traffic_record("gemm_fc1", 16208, 2560, 10240) is None   # another shape: no record
+    assert b.traffic_record("no_such_kernel", *shape) is None
