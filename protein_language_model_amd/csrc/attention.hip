@@ -25,7 +25,8 @@
 //    straight into LDS (global_load_lds) during the current tile's math, which
 //    keeps no staging registers: 4 waves per SIMD fit (two workgroups per
 //    CU).  Eight waves share each K/V tile: half the tile fills and barriers
-//    per query of four.
+//    per query of four.  An LDS tile holds 128 keys, computed as two 64-key
+//    tiles between barriers (64 KB of LDS per workgroup).
 //  * Key rows past the end of the sequence are clamped to its last row (never a
 //    neighbour's row) and their scores set to -inf; query rows past the end are
 //    computed from a clamped row and not stored.
@@ -35,9 +36,11 @@ namespace esm {
 
 namespace {
 
-constexpr int kKT = 64;     // keys per tile
+constexpr int kKT = 64;     // keys per compute tile
+constexpr int kSub = 2;     // compute tiles per LDS tile (one fill and barrier)
+constexpr int kLT = kKT * kSub;  // keys per LDS tile
 constexpr int kNW = kAttnTileRows / 32;  // waves per workgroup, 32 query rows each
-constexpr int kDmaPerWave = 8 / kNW;     // 1 KB direct loads per tensor per wave per tile
+constexpr int kDmaPerWave = kLT / 8 / kNW;  // 1 KB direct loads per tensor per wave per LDS tile
 constexpr int kLdsRow = 64; // LDS row (elements): one 128-byte row per key
 constexpr float kScaleLog2 = 0.18033688011112042f;  // log2(e) / sqrt(64)
 
@@ -62,8 +65,8 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
   const int L = a.segs[2 * s + 1];
   if (L <= 0) return;
 
-  __shared__ __attribute__((aligned(1024))) bf16_t sk[2][kKT * kLdsRow];
-  __shared__ __attribute__((aligned(1024))) bf16_t sv[2][kKT * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) bf16_t sk[2][kLT * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) bf16_t sv[2][kLT * kLdsRow];
 
   const int64_t T = a.T;
   const bf16_t* __restrict__ Qg = a.qkv + ((int64_t)(0 * heads + head) * T) * kHeadDim;
@@ -97,10 +100,10 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
   auto gload = [&](int j, int buf) {
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-      int key = j * kKT + src_row[i];
+      int key = j * kLT + src_row[i];
       key = key < L ? key : L - 1;
       const int64_t at = (start + key) * kHeadDim + src_col[i];
-      const uint32_t dst = (uint32_t)(buf * kKT * kLdsRow * 2 + (wave_u + kNW * i) * 1024);
+      const uint32_t dst = (uint32_t)(buf * kLT * kLdsRow * 2 + (wave_u + kNW * i) * 1024);
       lds_dma16(Kg + at, lds_k + dst);
       lds_dma16(Vg + at, lds_v + dst);
     }
@@ -133,19 +136,24 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
       voff[d][h] = (((col >> 3) ^ kSwz(r)) * 8) + (col & 7);
     }
 
-  const int ntk = (L + kKT - 1) / kKT;
+  const int ntk = (L + kKT - 1) / kKT;   // compute tiles
+  const int ntl = (L + kLT - 1) / kLT;   // LDS tiles
   // A wave whose 32 query rows all lie past the end of the sequence only helps
   // to stage K/V (and meets the barriers); it skips the math.
   const bool wave_active = q0 + 32 * wave < L;
-  // Tile j is in LDS buffer j & 1; tile j + 1 is fetched into the other
-  // buffer during tile j's math and published by the barrier that ends it.
+  // LDS tile t is in buffer t & 1; tile t + 1 is fetched into the other
+  // buffer during tile t's math and published by the barrier that ends it.
   gload(0, 0);
   vm_wait_all();
   __syncthreads();
-  for (int j = 0; j < ntk; ++j) {
-    const int cur = j & 1;
-    if (j + 1 < ntk) gload(j + 1, cur ^ 1);
-    if (wave_active) {
+  for (int t = 0; t < ntl; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < ntl) gload(t + 1, cur ^ 1);
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) {
+    const int j = t * kSub + sub;   // compute tile: keys j*64 .. j*64+63, LDS rows sub*64 ..
+    if (wave_active && j < ntk) {
+      const bf16_t* kt = sk[cur] + sub * kKT * kLdsRow;
       // S^T for this tile: two 32-key blocks.
       f32x16 st[2];
 #pragma unroll
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
         for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 kf = *(const bf16x8*)(&sk[cur][(kb * 32 + lrow) * kLdsRow + koff[kk]]);
+          const bf16x8 kf = *(const bf16x8*)(&kt[(kb * 32 + lrow) * kLdsRow + koff[kk]]);
           st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], st[kb], 0, 0, 0);
         }
       }
@@ -204,7 +212,7 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
           pb[kb][u] = __builtin_bit_cast(bf16x8, w);
         }
 
-      const bf16_t* vb = sv[cur];
+      const bf16_t* vb = sv[cur] + sub * kKT * kLdsRow;
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
 #pragma unroll
@@ -221,6 +229,7 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
             o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[kb][u], o[d], 0, 0, 0);
           }
       }
+    }
     }
     vm_wait_all();
     __syncthreads();
