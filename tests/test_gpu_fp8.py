@@ -195,6 +195,34 @@ def test_layernorm_e4m3(gu, H, M):
     enc.close()
 
 
+def test_layernorm_e4m3_nonfinite_rows(gu):
+    """A row holding NaN or Inf gives NaN codes in that row only (mean and
+    variance are NaN); the other rows are cast as usual and the amax ignores
+    the NaN row."""
+    H, M = 1280, 40
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((M, H)) * 2).astype(np.float32)
+    x[3, 17] = np.nan
+    x[21, 5] = np.inf
+    xb = D.to_bf16_bits(x)
+    ln = D.random_layernorm_params(H, 4)
+    enc = esm.Encoder(hidden_size=H, num_attention_heads=H // 64, intermediate_size=4 * H, num_hidden_layers=1,
+                      precision="fp8")
+    y8, amax = enc.layernorm_e4m3_fwd(gu.to_dev_bf16(xb), gu.to_dev_bf16(ln["ln1_gamma"]),
+                                      gu.to_dev_bf16(ln["ln1_beta"]), _dev_f32([10.0]))
+    got = _host(y8)
+    bad = np.zeros(M, bool)
+    bad[[3, 21]] = True
+    assert np.all((got[bad] & 0x7F) == 0x7F)
+    ref = O.layer_norm(D.bf16_bits_to_f64(xb[~bad]), D.bf16_bits_to_f64(ln["ln1_gamma"]),
+                       D.bf16_bits_to_f64(ln["ln1_beta"]), 1e-5)
+    codes = F8.e4m3_encode(ref * 10.0)
+    assert (got[~bad] != codes).mean() < 2e-3
+    am = _f32_bits_to_float(_host(amax))[0]
+    assert abs(am / np.max(np.abs(ref)) - 1) < 1e-5
+    enc.close()
+
+
 def test_e4m3_gemm_tile_shape_does_not_change_rows(gu):
     """320-row tiles (M = 15530, N = 1280) and 256-row tiles (a 1000-row slice)
     give the same rows bit for bit."""
