@@ -35,7 +35,9 @@ Readings where the pages are silent (each is listed in the design notes):
   biases on all four linears; interleaved rows 192*n + 64*c + j (c = q, k, v);
   RoPE base 10000 with rotate-half pairing (i, i+32), applied after the QKV
   bias to q and k only; softmax scale 1/sqrt(64) = 1/8; exact-erf GELU; no
-  dropout; no final LayerNorm; X0 = E[ids].
+  dropout; no final LayerNorm inside the stack; X0 = E[ids].  After the
+  stack (head_forward): final LayerNorm, the ESM-2 masked-LM head with the
+  decoder tied to the embedding, and per-sequence mean embeddings.
 
 Everything is evaluated densely in float64 on bf16-valued inputs, per sequence
 and per head, with an exact max-subtracted softmax.
@@ -231,6 +233,44 @@ def stack_forward(cu_seqlens, layers: List[Dict[str, np.ndarray]], heads: int,
     for w in layers:
         h = layer_forward(h, cu_seqlens, w, heads, **kw)
     return h
+
+
+# --------------------------------------------------------------------------
+# After the stack: final LayerNorm, masked-LM head, sequence-level embedding
+# --------------------------------------------------------------------------
+# The model card lists per-residue and sequence-level embeddings as the outputs
+# ([CARD] 输出), and the usage section loads the model as a masked-LM
+# ([TE-ESM2] 快速开始使用).  The pages define neither head; the readings used
+# here are ESM-2's published ones: a final LayerNorm after the last layer; the
+# LM head dense(H -> H) + bias, exact GELU, LayerNorm, then a decoder whose
+# weight is the token embedding [vocab, H] plus a bias; the sequence-level
+# embedding is the mean of the sequence's final representations (zeros for an
+# empty sequence).
+
+def lm_head(x, w: Dict[str, np.ndarray], eps: float = LN_EPS) -> np.ndarray:
+    """Masked-LM logits [T, vocab] of final representations x [T, H]."""
+    x = np.asarray(x, np.float64)
+    h = gelu(x @ np.asarray(w["lm_dense_w"], np.float64).T + np.asarray(w["lm_dense_b"], np.float64))
+    h = layer_norm(h, w["lm_ln_gamma"], w["lm_ln_beta"], eps)
+    return h @ np.asarray(w["embedding"], np.float64).T + np.asarray(w["lm_decoder_b"], np.float64)
+
+
+def sequence_means(x, cu_seqlens) -> np.ndarray:
+    """Mean over each sequence's rows of x [T, H] -> [B, H]; zeros for an empty sequence."""
+    x = np.asarray(x, np.float64)
+    segs = segments(cu_seqlens)
+    out = np.zeros((len(segs), x.shape[1]))
+    for s, (a, b) in enumerate(segs):
+        if b > a:
+            out[s] = x[a:b].mean(axis=0)
+    return out
+
+
+def head_forward(x, cu_seqlens, w: Dict[str, np.ndarray], eps: float = LN_EPS):
+    """Stack output x [T, H] -> (final representations [T, H], logits [T, vocab],
+    sequence embeddings [B, H])."""
+    final = layer_norm(x, w["final_ln_gamma"], w["final_ln_beta"], eps)
+    return final, lm_head(final, w, eps), sequence_means(final, cu_seqlens)
 
 
 def layer_forward_bshd(x, seqlens, w, heads: int, **kw) -> np.ndarray:

@@ -385,3 +385,86 @@ def test_query_tiles_cover_each_row_once_longest_first():
 def test_rel_max_err():
     assert O.rel_max_err([1.0, 2.0], [1.0, 4.0]) == 0.5
     assert O.rel_max_err([1.0, 5.0], [1.0, np.nan]) == 0.0
+
+
+# ---------------------------------------------------------------- after the stack
+
+def _head_weights(H, V, rng):
+    return {
+        "final_ln_gamma": 1 + 0.2 * rng.standard_normal(H), "final_ln_beta": 0.2 * rng.standard_normal(H),
+        "lm_dense_w": rng.standard_normal((H, H)) * 0.1, "lm_dense_b": rng.standard_normal(H) * 0.1,
+        "lm_ln_gamma": 1 + 0.2 * rng.standard_normal(H), "lm_ln_beta": 0.2 * rng.standard_normal(H),
+        "embedding": rng.standard_normal((V, H)), "lm_decoder_b": rng.standard_normal(V) * 0.1,
+    }
+
+
+def _scalar_head_row(x, w):
+    """One row of the LM head by scalar loops: dense + bias, erf GELU, LayerNorm, tied decoder + bias."""
+    H = len(x)
+    z = [sum(w["lm_dense_w"][o][i] * x[i] for i in range(H)) + w["lm_dense_b"][o] for o in range(H)]
+    g = [0.5 * t * (1.0 + math.erf(t / math.sqrt(2.0))) for t in z]
+    mu = sum(g) / H
+    var = sum((t - mu) ** 2 for t in g) / H
+    n = [(t - mu) / math.sqrt(var + 1e-5) * w["lm_ln_gamma"][i] + w["lm_ln_beta"][i] for i, t in enumerate(g)]
+    return [sum(w["embedding"][v][i] * n[i] for i in range(H)) + w["lm_decoder_b"][v] for v in range(len(w["embedding"]))]
+
+
+def test_lm_head_matches_scalar_evaluation():
+    r = _rng(31)
+    H, V = 24, 7
+    w = _head_weights(H, V, r)
+    x = r.standard_normal((3, H))
+    got = O.lm_head(x, w)
+    for t in range(3):
+        assert np.abs(got[t] - np.array(_scalar_head_row(list(x[t]), w))).max() < 1e-12
+    assert got.shape == (3, V)
+
+
+def test_lm_head_closed_forms():
+    r = _rng(32)
+    H, V = 40, 33
+    w = _head_weights(H, V, r)
+    x = r.standard_normal((5, H))
+    # LM LayerNorm gamma = 0: every row's logits are beta_lm . E^T + b, whatever the input
+    w0 = dict(w, lm_ln_gamma=np.zeros(H))
+    ref = np.array([sum(w["lm_ln_beta"][i] * w["embedding"][v][i] for i in range(H)) + w["lm_decoder_b"][v]
+                    for v in range(V)])
+    assert np.abs(O.lm_head(x, w0) - ref).max() < 1e-12
+    # dense weight 0: the GELU output is the same for every row, so are the logits
+    wz = dict(w, lm_dense_w=np.zeros((H, H)))
+    lz = O.lm_head(x, wz)
+    assert np.abs(lz - lz[0]).max() < 1e-13
+    # the decoder is the embedding, not its transpose: a one-hot LN output picks one embedding column
+    wc = dict(w, lm_ln_gamma=np.zeros(H), lm_ln_beta=np.eye(H)[3], lm_decoder_b=np.zeros(V))
+    assert np.abs(O.lm_head(x, wc)[0] - w["embedding"][:, 3]).max() < 1e-15
+
+
+def test_sequence_means_brute_force_and_special_cases():
+    r = _rng(33)
+    lens = [3, 0, 5, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    x = r.standard_normal((int(cu[-1]), 6))
+    got = O.sequence_means(x, cu)
+    for s, L in enumerate(lens):
+        for c in range(6):
+            ref = sum(x[int(cu[s]) + i, c] for i in range(L)) / L if L else 0.0
+            assert abs(got[s, c] - ref) < 1e-15
+    # constant rows give that row; a sequence's mean does not depend on its neighbours
+    y = np.repeat(r.standard_normal((1, 6)), int(cu[-1]), axis=0)
+    assert np.abs(O.sequence_means(y, cu)[[0, 2, 3]] - y[0]).max() < 1e-15
+    alone = O.sequence_means(x[int(cu[2]):int(cu[3])], np.array([0, 5]))
+    assert np.abs(alone[0] - got[2]).max() < 1e-15
+
+
+def test_head_forward_composes_final_ln_head_and_means():
+    r = _rng(34)
+    H, V = 16, 5
+    w = _head_weights(H, V, r)
+    cu = np.array([0, 4, 9])
+    x = r.standard_normal((9, H)) * 2 + 0.3
+    final, logits, pooled = O.head_forward(x, cu, w)
+    # final LayerNorm: per row mean 0 and unit variance before the affine map
+    z = (final - w["final_ln_beta"]) / w["final_ln_gamma"]
+    assert np.abs(z.mean(axis=1)).max() < 1e-12
+    assert np.abs(logits - O.lm_head(final, w)).max() == 0
+    assert np.abs(pooled[1] - final[4:9].mean(axis=0)).max() < 1e-15
