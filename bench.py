@@ -8,7 +8,9 @@ timed steps bracketed by device synchronisation, HIP events on the library
 stream; a second pass over the same steps times every kernel launch with HIP
 events for the roofline of the dominant kernel.  The same batch is then run
 through the FP8 (E4M3, delayed scaling) encoder, whose scales come from at
-least 10 warm-up steps, and reported under "fp8".  Prints one JSON line.
+least 10 warm-up steps, and reported under "fp8"; what follows the stack
+(final LayerNorm, masked-LM logits, per-sequence means) is timed on its own
+under "head".  Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
                     [--padded] [--no-fp8]
@@ -53,6 +55,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--padded", action="store_true", help="also time the padded bshd layout of the same batch")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-head", action="store_true", help="skip timing the final LayerNorm / LM head / means")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference dispatch for HBM byte counters)")
     return ap.parse_args()
@@ -226,6 +229,35 @@ def main():
         roofline = roofline_of(prof, fl, peaks)
         roofline["traffic"] = traffic_record(("fp8_" if fp8_main else "") + roofline["kernel"], T, m.hidden, m.ffn)
 
+    # After the stack (final LayerNorm, masked-LM logits, per-sequence means):
+    # timed on its own, on the stack output of the last timed step.
+    head = None
+    if not args.no_head:
+        hw = {k: up_bf16(v) for k, v in D.make_head_weights(m.hidden, emb).items()}
+        xf = torch.empty_like(out)
+        lg = torch.empty((T, m.vocab), dtype=torch.bfloat16, device=dev)
+        pe = torch.empty((B, m.hidden), dtype=torch.float32, device=dev)
+
+        def head_call():
+            enc.head_fwd(hw, out, cu, B, T, batch.max_seqlen, x_final=xf, logits=lg, seq_emb=pe, workspace=ws,
+                         stream=stream)
+
+        for _ in range(3):
+            head_call()
+        n_h = max(5, args.steps)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n_h):
+            head_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_h = e0.elapsed_time(e1) / n_h
+        fl_h = 2.0 * T * m.hidden * (m.hidden + m.vocab)
+        head = {"ms_per_call": round(ms_h, 4), "calls": n_h, "tflops": round(fl_h / (ms_h * 1e-3) / 1e12, 1),
+                "outputs": f"final LayerNorm [T,{m.hidden}] bf16, logits [T,{m.vocab}] bf16, sequence means "
+                           f"[{B},{m.hidden}] fp32",
+                "share_of_step": round(ms_h / ms, 4)}
+
     padded = None
     if args.padded:
         S = 1024
@@ -296,6 +328,7 @@ def main():
         "kernels": kernels,
         "ms_per_step_with_kernel_events": round(ms_instrumented, 4) if ms_instrumented else None,
         "padded": padded,
+        "head": head,
         "fp8": fp8,
     }
     print(json.dumps(rec))

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 4
+#define ESM_ABI_VERSION 5
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -219,6 +219,40 @@ esm_status esm_stack_fwd_bshd(esm_encoder* enc, const esm_layer_weights* w,
                               int32_t B, int32_t S,
                               void* workspace, size_t workspace_bytes, esm_stream_t stream);
 
+/* ---------------------------------------------------------------- after the stack */
+
+/* Weights of the final LayerNorm and of the masked-LM head (device bf16,
+ * row-major [out, in] like the layer weights). */
+typedef struct {
+  const void* final_ln_gamma;  /* [H] LayerNorm after the last layer */
+  const void* final_ln_beta;   /* [H] */
+  const void* lm_dense_w;      /* [H, H] LM head dense layer */
+  const void* lm_dense_b;      /* [H] or NULL (zero) */
+  const void* lm_ln_gamma;     /* [H] LM head LayerNorm */
+  const void* lm_ln_beta;      /* [H] */
+  const void* lm_decoder_w;    /* [vocab, H] decoder weight: the token embedding (tied) */
+  const void* lm_decoder_b;    /* [vocab] or NULL (zero) */
+} esm_head_weights;
+
+/* The outputs after the stack ([CARD] 输出: per-residue and sequence-level
+ * embeddings; [TE-ESM2] 快速开始使用: the model as a masked LM; the layouts of
+ * the final LayerNorm and the head are ESM-2's, which the pages do not spell
+ * out):
+ *   x_final    = LayerNorm(x; final_ln)                  bf16 [T, H]; may alias x
+ *   logits     = LN(GELU(x_final W_d^T + b_d); lm_ln) E^T + b_e
+ *                                                         bf16 [T, vocab]; skipped when NULL
+ *   seq_emb[s] = mean of x_final over sequence s's rows   fp32 [B, H], 0 for an empty
+ *                                                         sequence; skipped when NULL
+ * x, cu_seqlens, B, T, max_seqlen and the workspace as for esm_stack_fwd (the
+ * workspace of esm_workspace_size(T, B) suffices); cu_seqlens_dev may be NULL
+ * when seq_emb is.  Runs in bf16 with fp32 accumulation for both precisions.
+ * x, x_final and the weights must be 16-byte aligned (x and x_final may be
+ * NULL when T = 0); the LM head takes vocab <= min(4096, 3 H). */
+esm_status esm_head_fwd(esm_encoder* enc, const esm_head_weights* w, const void* x, void* x_final,
+                        void* logits, float* seq_emb, const int32_t* cu_seqlens_dev,
+                        const int32_t* cu_seqlens_host, int32_t B, int64_t T, int32_t max_seqlen,
+                        void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
 /* ---------------------------------------------------------------- kernel-level entries */
 
 /* Segment table ([BIO-ACC] 3.2 cu_seqlens contract): writes into the workspace
@@ -328,7 +362,8 @@ esm_status esm_fp8_quantize(esm_encoder* enc, const float* x, int64_t n, const f
 typedef enum {
   ESM_K_SEGMENT = 0, ESM_K_EMBED = 1, ESM_K_LAYERNORM = 2, ESM_K_GEMM_QKV = 3,
   ESM_K_ATTENTION = 4, ESM_K_GEMM_OUT = 5, ESM_K_GEMM_FC1 = 6, ESM_K_GEMM_FC2 = 7,
-  ESM_K_OTHER = 8, ESM_K_FP8 = 9 /* weight casts, scale updates */, ESM_K_COUNT = 10
+  ESM_K_OTHER = 8, ESM_K_FP8 = 9 /* weight casts, scale updates */,
+  ESM_K_HEAD = 10 /* final LayerNorm, LM head, sequence means */, ESM_K_COUNT = 11
 } esm_kernel_class;
 
 /* When on, every launch is bracketed by HIP events recorded on the launch

@@ -140,6 +140,11 @@ struct E4m3Out {
   const int32_t* pos;  // optional [rows]: rows with pos < 0 (padding) stay out of the amax
 };
 
+hipError_t launch_pad_rows(const bf16_t* src, int32_t rows, int32_t cols, bf16_t* dst, int32_t rows_pad,
+                           hipStream_t st);
+hipError_t launch_take_cols(const bf16_t* src, int32_t ld_src, bf16_t* dst, int64_t T, int32_t cols, hipStream_t st);
+hipError_t launch_segment_mean(const bf16_t* x, const int32_t* segs, int32_t B, int32_t H, float* out,
+                               hipStream_t st);
 hipError_t launch_layernorm(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y,
                             int64_t M, int32_t H, float eps, const E4m3Out& q, hipStream_t st);
 

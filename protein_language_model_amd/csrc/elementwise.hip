@@ -251,6 +251,72 @@ __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x,
   }
 }
 
+// dst [rows_pad, cols] = src [rows, cols] followed by zero rows (src NULL:
+// all zero).  Pads the tied decoder weight and its bias to a GEMM-sized
+// number of output columns.
+__global__ void k_pad_rows(const bf16_t* __restrict__ src, int32_t rows, int32_t cols, bf16_t* __restrict__ dst,
+                           int32_t rows_pad) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)rows_pad * cols) return;
+  dst[i] = (src && i < (int64_t)rows * cols) ? src[i] : (bf16_t)0;
+}
+
+// dst [T, cols] = the first cols columns of src [T, ld_src].
+__global__ void k_take_cols(const bf16_t* __restrict__ src, int32_t ld_src, bf16_t* __restrict__ dst, int64_t T,
+                            int32_t cols) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * cols) return;
+  const int64_t t = i / cols;
+  dst[i] = src[t * ld_src + (i - t * cols)];
+}
+
+// Sequence-level embedding: out[s, :] = mean of x over the rows of sequence s
+// (segs[s] = first row, length), fp32; 0 for an empty sequence.  One
+// workgroup per sequence: wave w sums rows w, w + 4, ... in fp32 (lane l owns
+// the 8 columns of chunks l, l + 64, ...), then the four partial sums are
+// added in a fixed order, so the result does not depend on scheduling.
+template <int CH>
+__global__ __launch_bounds__(256) void k_segment_mean(const bf16_t* __restrict__ x, const int32_t* __restrict__ segs,
+                                                      int32_t H, float* __restrict__ out) {
+  extern __shared__ float part[];  // [4, H]
+  const int s = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t start = segs[2 * s];
+  const int L = segs[2 * s + 1];
+  const int chunks = H / 8;
+  float acc[CH][8];
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+#pragma unroll 2
+  for (int r = wave; r < L; r += 4) {
+    const bf16_t* xr = x + (start + r) * H;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < chunks) {
+        const u32x4 w = *(const u32x4*)(xr + c * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[i][2 * e] += bflo(w[e]);
+          acc[i][2 * e + 1] += bfhi(w[e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int c = lane + 64 * i;
+    if (c < chunks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[wave * H + c * 8 + e] = acc[i][e];
+  }
+  __syncthreads();
+  const float inv = L > 0 ? 1.0f / (float)L : 0.0f;
+  for (int col = threadIdx.x; col < H; col += 256)
+    out[(int64_t)s * H + col] = ((part[col] + part[H + col]) + (part[2 * H + col] + part[3 * H + col])) * inv;
+}
+
 }  // namespace
 
 hipError_t launch_segment_table(int layout, const int32_t* lens, int32_t B, int64_t rows, int32_t S,
@@ -300,6 +366,39 @@ hipError_t launch_layernorm(const bf16_t* x, const bf16_t* gamma, const bf16_t* 
   if (M <= 0) return hipSuccess;
   if (q.y) return layernorm_ch<true>(x, gamma, beta, y, M, H, eps, q, st);
   return layernorm_ch<false>(x, gamma, beta, y, M, H, eps, q, st);
+}
+
+}  // namespace esm
+
+namespace esm {
+
+hipError_t launch_pad_rows(const bf16_t* src, int32_t rows, int32_t cols, bf16_t* dst, int32_t rows_pad,
+                           hipStream_t st) {
+  const int64_t n = (int64_t)rows_pad * cols;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pad_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, rows, cols, dst, rows_pad);
+  return hipGetLastError();
+}
+
+hipError_t launch_take_cols(const bf16_t* src, int32_t ld_src, bf16_t* dst, int64_t T, int32_t cols, hipStream_t st) {
+  const int64_t n = T * cols;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_take_cols, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src, ld_src, dst, T, cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_mean(const bf16_t* x, const int32_t* segs, int32_t B, int32_t H, float* out,
+                               hipStream_t st) {
+  if (B <= 0) return hipSuccess;
+  const int ch = (H / 8 + 63) / 64;
+  const size_t shmem = sizeof(float) * 4 * (size_t)H;
+  if (ch <= 1) hipLaunchKernelGGL(k_segment_mean<1>, dim3(B), dim3(256), shmem, st, x, segs, H, out);
+  else if (ch <= 2) hipLaunchKernelGGL(k_segment_mean<2>, dim3(B), dim3(256), shmem, st, x, segs, H, out);
+  else if (ch <= 3) hipLaunchKernelGGL(k_segment_mean<3>, dim3(B), dim3(256), shmem, st, x, segs, H, out);
+  else if (ch <= 5) hipLaunchKernelGGL(k_segment_mean<5>, dim3(B), dim3(256), shmem, st, x, segs, H, out);
+  else if (ch <= 8) hipLaunchKernelGGL(k_segment_mean<8>, dim3(B), dim3(256), shmem, st, x, segs, H, out);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace esm

@@ -32,6 +32,10 @@ struct esm_encoder {
   uint8_t* w8 = nullptr;           // per layer: E4M3 w_qkv | w_out | w_fc1 | w_fc2
   size_t w8_layer = 0;             // bytes per layer
   std::vector<char> prepared;      // layer weights cast since create
+  // LM head: the tied decoder weight and its bias padded to vocab_pad rows
+  // (a multiple of 64 GEMM columns), refilled from the caller's on each call
+  bf16_t* head_w = nullptr;        // [vocab_pad, H] then [vocab_pad]
+  int32_t vocab_pad = 0;
 };
 
 namespace {
@@ -61,6 +65,8 @@ esm_status hip_fail(hipError_t e, const char* what) {
   } while (0)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+constexpr int32_t kHeadMaxVocab = 4096;  // LM head decoder rows supported
 
 esm_status check_config(const esm_config* c) {
   if (!c) return fail(ESM_ERR_NULL, "config is NULL");
@@ -565,6 +571,14 @@ esm_status esm_encoder_create(const esm_config* cfg, int device, esm_encoder** o
     esm_encoder_destroy(e);
     return s;
   }
+  if (cfg->vocab_size <= kHeadMaxVocab) {
+    e->vocab_pad = (cfg->vocab_size + 63) / 64 * 64;
+    err = hipMalloc((void**)&e->head_w, (size_t)e->vocab_pad * ((size_t)cfg->hidden_size + 1) * sizeof(bf16_t));
+    if (err != hipSuccess) {
+      esm_encoder_destroy(e);
+      return hip_fail(err, "LM head decoder buffer");
+    }
+  }
   *out = e;
   return ok();
 }
@@ -575,6 +589,7 @@ esm_status esm_encoder_destroy(esm_encoder* e) {
   if (e->rope) (void)hipFree(e->rope);
   if (e->fp8_mem) (void)hipFree(e->fp8_mem);
   if (e->w8) (void)hipFree(e->w8);
+  if (e->head_w) (void)hipFree(e->head_w);
   for (hipEvent_t ev : e->pool) (void)hipEventDestroy(ev);
   delete e;
   return ESM_OK;
@@ -612,6 +627,85 @@ esm_status esm_stack_fwd(esm_encoder* e, const esm_layer_weights* w, const int32
   if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
   return forward_thd(e, w, e->cfg.num_hidden_layers, -1, ids, emb, x_in, x_out, cu_dev, cu_host, B, T, max_seqlen,
                      ws, ws_bytes, stream);
+}
+
+esm_status esm_head_fwd(esm_encoder* e, const esm_head_weights* w, const void* x, void* x_final, void* logits,
+                        float* seq_emb, const int32_t* cu_dev, const int32_t* cu_host, int32_t B, int64_t T,
+                        int32_t max_seqlen, void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !w) return fail(ESM_ERR_NULL, "encoder or head weights NULL");
+  esm_status s = check_rows(e, T, B);
+  if (s) return s;
+  if (T > 0 && (!x || !x_final)) return fail(ESM_ERR_NULL, "x or x_final is NULL");
+  if (!aligned16(x) || !aligned16(x_final)) return fail(ESM_ERR_UNSUPPORTED, "x / x_final not 16-byte aligned");
+  if (!w->final_ln_gamma || !w->final_ln_beta) return fail(ESM_ERR_NULL, "final LayerNorm weights NULL");
+  if (!aligned16(w->final_ln_gamma) || !aligned16(w->final_ln_beta))
+    return fail(ESM_ERR_UNSUPPORTED, "final LayerNorm weights not 16-byte aligned");
+  if (logits) {
+    const void* req[] = {w->lm_dense_w, w->lm_ln_gamma, w->lm_ln_beta, w->lm_decoder_w};
+    for (const void* q : req) {
+      if (!q) return fail(ESM_ERR_NULL, "LM head weight NULL");
+      if (!aligned16(q)) return fail(ESM_ERR_UNSUPPORTED, "LM head weight not 16-byte aligned");
+    }
+    if (w->lm_dense_b && ((uintptr_t)w->lm_dense_b & 7u)) return fail(ESM_ERR_UNSUPPORTED, "lm_dense_b not 8-byte aligned");
+    if (!e->head_w || e->vocab_pad > 3 * e->cfg.hidden_size)
+      return fail(ESM_ERR_UNSUPPORTED, "vocab %d: the LM head takes up to min(%d, 3 * hidden) rows", e->cfg.vocab_size,
+                  kHeadMaxVocab);
+  }
+  if (seq_emb && !cu_dev) return fail(ESM_ERR_NULL, "seq_emb needs cu_seqlens_dev");
+  if ((s = check_cu_host(e, cu_host, B, T, max_seqlen))) return s;
+  if (T == 0 && (B == 0 || !seq_emb)) return ok();
+  Plan p;
+  if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  const esm_config& c = e->cfg;
+  const int H = c.hidden_size;
+  if (T > 0) {
+    s = timed(e, ESM_K_HEAD, st, "final layernorm", [&] {
+      return launch_layernorm((const bf16_t*)x, (const bf16_t*)w->final_ln_gamma, (const bf16_t*)w->final_ln_beta,
+                              (bf16_t*)x_final, T, H, c.layer_norm_eps, E4m3Out{nullptr, nullptr, nullptr, nullptr}, st);
+    });
+    if (s) return s;
+  }
+  if (seq_emb && B > 0) {
+    if ((s = run_segments(e, ESM_LAYOUT_THD, cu_dev, B, T, 0, ws, p, st))) return s;
+    s = timed(e, ESM_K_HEAD, st, "sequence means", [&] {
+      return launch_segment_mean((const bf16_t*)x_final, region<int32_t>(ws, p, ESM_WS_SEGS), B, H, seq_emb, st);
+    });
+    if (s) return s;
+  }
+  if (!logits || T == 0) return ok();
+  // LM head: dense + GELU into ACT, its LayerNorm into LN1, the decoder over
+  // vocab_pad columns into the QKV region ([T, vocab_pad] bf16 fits in
+  // [3, heads, T, 64]), then the first vocab columns into logits.
+  const int V = c.vocab_size, VP = e->vocab_pad;
+  bf16_t* dense = region<bf16_t>(ws, p, ESM_WS_ACT);
+  bf16_t* hn = region<bf16_t>(ws, p, ESM_WS_LN1);
+  bf16_t* padded = region<bf16_t>(ws, p, ESM_WS_QKV);
+  bf16_t* wdec = e->head_w;
+  bf16_t* bdec = e->head_w + (size_t)VP * H;
+  s = timed(e, ESM_K_HEAD, st, "pad decoder", [&] {
+    hipError_t r = launch_pad_rows((const bf16_t*)w->lm_decoder_w, V, H, wdec, VP, st);
+    return r != hipSuccess ? r : launch_pad_rows((const bf16_t*)w->lm_decoder_b, w->lm_decoder_b ? V : 0, 1, bdec, VP, st);
+  });
+  if (s) return s;
+  GemmArgs g{};
+  g.dtype = kBF16;
+  g.x = x_final; g.w = w->lm_dense_w; g.bias = (const bf16_t*)w->lm_dense_b; g.y = dense;
+  g.M = T; g.N = H; g.K = H;
+  s = timed(e, ESM_K_HEAD, st, "lm dense gemm", [&] { return launch_gemm(EPI_BIAS_GELU, g, st); });
+  if (s) return s;
+  s = timed(e, ESM_K_HEAD, st, "lm layernorm", [&] {
+    return launch_layernorm(dense, (const bf16_t*)w->lm_ln_gamma, (const bf16_t*)w->lm_ln_beta, hn, T, H,
+                            c.layer_norm_eps, E4m3Out{nullptr, nullptr, nullptr, nullptr}, st);
+  });
+  if (s) return s;
+  g.x = hn; g.w = wdec; g.bias = bdec; g.y = padded;
+  g.N = VP;
+  s = timed(e, ESM_K_HEAD, st, "lm decoder gemm", [&] { return launch_gemm(EPI_BIAS, g, st); });
+  if (s) return s;
+  return timed(e, ESM_K_HEAD, st, "logits", [&] { return launch_take_cols(padded, VP, (bf16_t*)logits, T, V, st); });
 }
 
 esm_status esm_layer_fwd_bshd(esm_encoder* e, const esm_layer_weights* w, int32_t layer_idx, const void* x_in,

@@ -214,6 +214,28 @@ def make_layer_weights(H: int, F: int, layer: int, seed: int = 0) -> Dict[str, n
     return out
 
 
+def make_head_weights(H: int, embedding_bits: np.ndarray, seed: int = 0, random_ln: bool = False) -> Dict[str, np.ndarray]:
+    """bf16 bit patterns of the final LayerNorm and the masked-LM head (stream
+    2000): dense [H, H] and biases N(0, 0.02); the decoder is the embedding
+    table itself (tied); LayerNorms gamma = 1, beta = 0 unless random_ln."""
+    r = rng(seed, 2000)
+
+    def draw(shape, scale=0.02):
+        return to_bf16_bits((r.standard_normal(shape) * scale).astype(np.float32))
+
+    out: Dict[str, np.ndarray] = {"lm_dense_w": draw((H, H)), "lm_dense_b": draw((H,)),
+                                  "lm_decoder_w": np.ascontiguousarray(embedding_bits),
+                                  "lm_decoder_b": draw((embedding_bits.shape[0],))}
+    for n in ("final_ln", "lm_ln"):
+        if random_ln:
+            out[n + "_gamma"] = to_bf16_bits((1 + 0.1 * r.standard_normal(H)).astype(np.float32))
+            out[n + "_beta"] = draw((H,), 0.1)
+        else:
+            out[n + "_gamma"] = to_bf16_bits(np.ones(H, np.float32))
+            out[n + "_beta"] = to_bf16_bits(np.zeros(H, np.float32))
+    return out
+
+
 def make_layer_weights_device(H: int, F: int, layer: int, seed: int = 0, device: str = "cuda:0"):
     """Same tensors as make_layer_weights, drawn on the device (torch generator).
 

@@ -25,7 +25,7 @@ EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_E4M3 = 0, 1, 2, 3
 WS_REGIONS = {"ln1": 0, "qkv": 1, "ctx": 2, "x1": 3, "ln2": 4, "act": 5, "pos": 6, "tiles": 7, "ntiles": 8, "segs": 9}
 ATTN_TILE_ROWS = 256  # ESM_ATTN_TILE_ROWS: query rows per attention workgroup
 KERNEL_CLASSES = ("segment", "embed", "layernorm", "gemm_qkv", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
-                  "other", "fp8")
+                  "other", "fp8", "head")
 FP8_ACT_NAMES = ("ln1", "ctx", "ln2", "act")      # activation tensors tracked per layer, in state order
 FP8_WEIGHT_NAMES = ("w_qkv", "w_out", "w_fc1", "w_fc2")
 LAYER_WEIGHT_NAMES = ("ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_out", "b_out",
@@ -49,6 +49,14 @@ class EsmLayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHT_NAMES]
 
 
+HEAD_WEIGHT_NAMES = ("final_ln_gamma", "final_ln_beta", "lm_dense_w", "lm_dense_b", "lm_ln_gamma", "lm_ln_beta",
+                     "lm_decoder_w", "lm_decoder_b")
+
+
+class EsmHeadWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in HEAD_WEIGHT_NAMES]
+
+
 class EsmFp8State(ctypes.Structure):
     _fields_ = [
         ("num_layers", ctypes.c_int32), ("history_len", ctypes.c_int32),
@@ -65,6 +73,8 @@ SIGNATURES = {
     "esm_workspace_region": (_i32, [_p, _i64, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     "esm_layer_fwd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _i32, _p, _p, _p, _p, _i32, _i64, _i32, _p, _sz,
                              _p]),
+    "esm_head_fwd": (_i32, [_p, ctypes.POINTER(EsmHeadWeights), _p, _p, _p, _p, _p, _p, _i32, _i64, _i32, _p, _sz,
+                            _p]),
     "esm_stack_fwd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _p, _p, _p, _p, _p, _p, _i32, _i64, _i32, _p, _sz,
                              _p]),
     "esm_layer_fwd_bshd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _i32, _p, _p, _p, _p, _i32, _i32, _p, _sz,
@@ -264,6 +274,33 @@ class Encoder:
               _ptr(cu_seqlens), cuh.ctypes.data_as(ctypes.c_void_p) if cuh is not None else None, int(B), int(T),
               int(max_seqlen), _ptr(workspace), workspace.numel(), _stream(stream))
         return x_out
+
+    def head_fwd(self, head_weights: Dict, x, cu_seqlens, B: int, T: int, max_seqlen: int, *, x_final=None,
+                 logits=True, seq_emb=True, cu_seqlens_host=None, workspace=None, stream=None):
+        """Final LayerNorm, masked-LM logits and per-sequence mean embeddings of
+        the stack output x [T, H]; returns (x_final, logits or None, seq_emb or None).
+        logits / seq_emb: True to allocate, a tensor to fill, or None / False to skip."""
+        import torch
+        dev = f"cuda:{self.device}"
+        if x_final is None:
+            x_final = torch.empty((T, self.hidden), dtype=torch.bfloat16, device=dev)
+        if logits is True:
+            logits = torch.empty((T, self.cfg.vocab_size), dtype=torch.bfloat16, device=dev)
+        if seq_emb is True:
+            seq_emb = torch.empty((B, self.hidden), dtype=torch.float32, device=dev)
+        logits = logits if logits is not False else None
+        seq_emb = seq_emb if seq_emb is not False else None
+        if workspace is None:
+            workspace = self.workspace(T, B)
+        hw = EsmHeadWeights()
+        for n in HEAD_WEIGHT_NAMES:
+            t = head_weights.get(n)
+            setattr(hw, n, _ptr(t) if t is not None else None)
+        cuh = _host_i32(cu_seqlens_host)
+        _call("esm_head_fwd", self._h, ctypes.byref(hw), _ptr(x), _ptr(x_final), _ptr(logits), _ptr(seq_emb),
+              _ptr(cu_seqlens), cuh.ctypes.data_as(ctypes.c_void_p) if cuh is not None else None, int(B), int(T),
+              int(max_seqlen), _ptr(workspace), workspace.numel(), _stream(stream))
+        return x_final, logits, seq_emb
 
     def layer_fwd_bshd(self, weights, x_in, seqlens, B: int, S: int, *, x_out=None, layer_idx: int = 0,
                        seqlens_host=None, workspace=None, stream=None):

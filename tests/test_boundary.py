@@ -33,6 +33,14 @@ def test_library_exports_every_declared_symbol():
     assert esm.ATTN_TILE_ROWS == int(re.search(r"#define ESM_ATTN_TILE_ROWS (\d+)", src).group(1))
 
 
+def test_head_weights_struct_has_eight_pointers():
+    assert ctypes.sizeof(esm.EsmHeadWeights) == 64
+    assert [f[0] for f in esm.EsmHeadWeights._fields_] == list(esm.HEAD_WEIGHT_NAMES)
+    src = open(HEADER).read()
+    body = src[src.index("const void* final_ln_gamma"):src.index("} esm_head_weights;")]
+    assert re.findall(r"const void\* (\w+);", body) == list(esm.HEAD_WEIGHT_NAMES)
+
+
 def test_fp8_state_struct_layout_matches_the_header():
     # two int32, four pointers, one uint32 (padded to the pointer alignment)
     assert ctypes.sizeof(esm.EsmFp8State) == 48
@@ -145,6 +153,8 @@ def test_null_handle_calls_fail_cleanly():
     st, _ = _status("esm_workspace_size", None, 10, 1, ctypes.byref(n))
     assert st == 1
     st, _ = _status("esm_layer_fwd", None, None, 0, None, None, None, None, 1, 1, 1, None, 0, None)
+    assert st == 1
+    st, _ = _status("esm_head_fwd", None, None, None, None, None, None, None, None, 1, 1, 1, None, 0, None)
     assert st == 1
 
 
