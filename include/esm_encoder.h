@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 5
+#define ESM_ABI_VERSION 6
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -347,8 +347,19 @@ esm_status esm_fp8_get_state(esm_encoder* enc, esm_fp8_state* state, esm_stream_
 esm_status esm_fp8_set_state(esm_encoder* enc, const esm_fp8_state* state, esm_stream_t stream);
 
 /* Back to the initial state (scales 1, empty histories, steps 0, flag clear);
- * prepared weights are kept. */
+ * prepared weights and per-layer precisions are kept. */
 esm_status esm_fp8_reset(esm_encoder* enc, esm_stream_t stream);
+
+/* Per-layer precision of an FP8 encoder ([TE-ESM2] FP8与FP4混合精度支持: a
+ * per-layer precision setting): precision[l] (host, num_layers entries) is
+ * ESM_PRECISION_FP8_DELAYED (every layer's default) or ESM_PRECISION_BF16.  A
+ * bf16 layer runs the bf16 kernels, needs no prepared FP8 weights, records no
+ * amax, and its FP8 state (scales, history, step count) stays as it is until
+ * the layer runs FP8 again.  Waits for stream.  ESM_ERR_STATE for an encoder
+ * created with bf16 precision; ESM_ERR_SHAPE when num_layers is not the
+ * config's; ESM_ERR_UNSUPPORTED for another precision code. */
+esm_status esm_set_layer_precision(esm_encoder* enc, const int32_t* precision, int32_t num_layers,
+                                   esm_stream_t stream);
 
 /* The E4M3 cast the producers use, as a test entry: y[i] = cast(x[i] *
  * scale[0]) for fp32 x (device, n values), y uint8 codes; max |x| is

@@ -198,6 +198,7 @@ struct Fp8State {
   uint32_t* flags;     // [1] bit 0: a non-finite amax was recorded
   float* w_scale;      // [layers, 4] weight scales (qkv, out, fc1, fc2)
   uint32_t* w_amax;    // [layers, 4]
+  int32_t* layer_on;   // [layers] 1 = the layer runs FP8 (its state is updated), 0 = bf16 (state frozen)
   int32_t history_len;
 };
 

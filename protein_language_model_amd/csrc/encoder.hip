@@ -32,6 +32,7 @@ struct esm_encoder {
   uint8_t* w8 = nullptr;           // per layer: E4M3 w_qkv | w_out | w_fc1 | w_fc2
   size_t w8_layer = 0;             // bytes per layer
   std::vector<char> prepared;      // layer weights cast since create
+  std::vector<int32_t> layer_prec; // FP8 encoder: per-layer precision (FP8 by default, or bf16)
   // LM head: the tied decoder weight and its bias padded to vocab_pad rows
   // (a multiple of 64 GEMM columns), refilled from the caller's on each call
   bf16_t* head_w = nullptr;        // [vocab_pad, H] then [vocab_pad]
@@ -207,6 +208,10 @@ esm_status check_ws(const esm_encoder* e, void* ws, size_t ws_bytes, int64_t row
 // ---------------------------------------------------------------- FP8 state
 
 bool is_fp8(const esm_encoder* e) { return e->cfg.precision == ESM_PRECISION_FP8_DELAYED; }
+// Layer l of an FP8 encoder runs FP8 unless esm_set_layer_precision chose bf16 for it.
+bool layer_fp8(const esm_encoder* e, int32_t l) {
+  return is_fp8(e) && l >= 0 && (size_t)l < e->layer_prec.size() && e->layer_prec[(size_t)l] == ESM_PRECISION_FP8_DELAYED;
+}
 
 // Byte offsets of the four E4M3 weights inside one layer's block.
 struct W8Off {
@@ -226,7 +231,7 @@ W8Off w8_offsets(const esm_config& c) {
 // Device layout of the delayed-scaling state: one allocation, 256-byte
 // aligned arrays.
 struct Fp8Layout {
-  size_t act_scale, act_amax, history, steps, flags, w_scale, w_amax, total;
+  size_t act_scale, act_amax, history, steps, flags, w_scale, w_amax, layer_on, total;
 };
 Fp8Layout fp8_layout(const esm_config& c) {
   const size_t L = (size_t)(c.num_hidden_layers > 0 ? c.num_hidden_layers : 1), HL = (size_t)c.amax_history_len;
@@ -244,6 +249,7 @@ Fp8Layout fp8_layout(const esm_config& c) {
   f.flags = take(sizeof(uint32_t));
   f.w_scale = take(L * 4 * sizeof(float));
   f.w_amax = take(L * 4 * sizeof(uint32_t));
+  f.layer_on = take(L * sizeof(int32_t));
   f.total = o;
   return f;
 }
@@ -273,12 +279,16 @@ esm_status fp8_create(esm_encoder* e) {
   e->f8.flags = (uint32_t*)(b + f.flags);
   e->f8.w_scale = (float*)(b + f.w_scale);
   e->f8.w_amax = (uint32_t*)(b + f.w_amax);
+  e->f8.layer_on = (int32_t*)(b + f.layer_on);
   e->f8.history_len = c.amax_history_len;
   HIP_TRY(hipMemset(e->f8.w_scale, 0, f.total - f.w_scale), "fp8 state");
   e->w8_layer = align256(w8_offsets(c).total);
   const size_t L = (size_t)(c.num_hidden_layers > 0 ? c.num_hidden_layers : 1);
   HIP_TRY(hipMalloc((void**)&e->w8, L * e->w8_layer), "fp8 weights");
   e->prepared.assign(L, 0);
+  e->layer_prec.assign(L, ESM_PRECISION_FP8_DELAYED);
+  std::vector<int32_t> on(L, 1);
+  HIP_TRY(hipMemcpy(e->f8.layer_on, on.data(), L * sizeof(int32_t), hipMemcpyHostToDevice), "fp8 layer flags");
   return fp8_reset_state(e);
 }
 
@@ -320,7 +330,7 @@ esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, int32_t li, con
   bf16_t* ln2 = region<bf16_t>(ws, p, ESM_WS_LN2);
   bf16_t* act = region<bf16_t>(ws, p, ESM_WS_ACT);
   const int32_t* pos = region<int32_t>(ws, p, ESM_WS_POS);
-  const bool fp8 = is_fp8(e);
+  const bool fp8 = layer_fp8(e, li);
   float* as = nullptr;                 // activation scales: ln1, ctx, ln2, act
   uint32_t* am = nullptr;              // their amax slots
   const float* wsc = nullptr;          // weight scales: qkv, out, fc1, fc2
@@ -440,7 +450,7 @@ esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, 
   if (!w && nlayers > 0) return fail(ESM_ERR_NULL, "weights are NULL");
   for (int l = 0; l < nlayers; ++l) {
     if ((s = check_weights(&w[l], layer_idx >= 0 ? layer_idx : l))) return s;
-    if (is_fp8(e) && (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l))) return s;
+    if (layer_fp8(e, layer_idx >= 0 ? layer_idx : l) && (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l))) return s;
   }
   if ((s = check_cu_host(e, cu_host, B, T, max_seqlen))) return s;
   if (T == 0 || B == 0) return ok();
@@ -489,7 +499,7 @@ esm_status forward_bshd(esm_encoder* e, const esm_layer_weights* w, int nlayers,
   if (!w && nlayers > 0) return fail(ESM_ERR_NULL, "weights are NULL");
   for (int l = 0; l < nlayers; ++l) {
     if ((s = check_weights(&w[l], layer_idx >= 0 ? layer_idx : l))) return s;
-    if (is_fp8(e) && (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l))) return s;
+    if (layer_fp8(e, layer_idx >= 0 ? layer_idx : l) && (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l))) return s;
   }
   if (sl_host && (s = esm_check_seqlens(sl_host, B, S, e->cfg.max_position_embeddings))) return s;
   if (rows == 0) return ok();
@@ -941,6 +951,25 @@ esm_status esm_fp8_reset(esm_encoder* e, esm_stream_t stream) {
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
   HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
   return fp8_reset_state(e);
+}
+
+esm_status esm_set_layer_precision(esm_encoder* e, const int32_t* prec, int32_t n, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !prec) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!is_fp8(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
+  if (n != e->cfg.num_hidden_layers)
+    return fail(ESM_ERR_SHAPE, "%d precisions for %d layers", n, e->cfg.num_hidden_layers);
+  std::vector<int32_t> on((size_t)n);
+  for (int32_t l = 0; l < n; ++l) {
+    if (prec[l] != ESM_PRECISION_BF16 && prec[l] != ESM_PRECISION_FP8_DELAYED)
+      return fail(ESM_ERR_UNSUPPORTED, "layer %d: precision %d", l, prec[l]);
+    on[(size_t)l] = prec[l] == ESM_PRECISION_FP8_DELAYED;
+  }
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  HIP_TRY(hipMemcpy(e->f8.layer_on, on.data(), on.size() * sizeof(int32_t), hipMemcpyHostToDevice), "layer flags");
+  e->layer_prec.assign(prec, prec + n);
+  return ok();
 }
 
 esm_status esm_fp8_quantize(esm_encoder* e, const float* x, int64_t n, const float* scale, void* y, uint32_t* amax,

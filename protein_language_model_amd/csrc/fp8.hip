@@ -60,6 +60,7 @@ __global__ void k_scale_update(Fp8State s, int32_t l0, int32_t nl) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= nl) return;
   const int l = l0 + idx;
+  if (!s.layer_on[l]) return;  // a bf16 layer: recorded nothing, its state stays as it is
   const int HL = s.history_len;
   const int slot = (int)(s.steps[l] % HL);
   bool nonfinite = false;

@@ -91,6 +91,7 @@ SIGNATURES = {
     "esm_fp8_get_state": (_i32, [_p, ctypes.POINTER(EsmFp8State), _p]),
     "esm_fp8_set_state": (_i32, [_p, ctypes.POINTER(EsmFp8State), _p]),
     "esm_fp8_reset": (_i32, [_p, _p]),
+    "esm_set_layer_precision": (_i32, [_p, _p, _i32, _p]),
     "esm_fp8_quantize": (_i32, [_p, _p, _i64, _p, _p, _p, _p]),
     "esm_profile_enable": (_i32, [_p, _i32]),
     "esm_profile_read": (_i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
@@ -426,6 +427,11 @@ class Encoder:
 
     def fp8_reset(self, stream=None) -> None:
         _call("esm_fp8_reset", self._h, _stream(stream))
+
+    def set_layer_precision(self, precisions: Sequence[str], stream=None) -> None:
+        """Per-layer precision of an FP8 encoder: "fp8" or "bf16" for every layer."""
+        arr = np.ascontiguousarray(np.array([PRECISION[p] for p in precisions], np.int32))
+        _call("esm_set_layer_precision", self._h, arr.ctypes.data_as(ctypes.c_void_p), len(arr), _stream(stream))
 
     def fp8_quantize(self, x, scale, *, y=None, amax=None, stream=None):
         """E4M3 codes of x * scale[0] (x float32 on the device); returns (codes, amax tensor)."""

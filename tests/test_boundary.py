@@ -141,6 +141,8 @@ def test_fp8_calls_fail_cleanly_without_a_handle():
     assert st == 1
     st, _ = _status("esm_layernorm_e4m3_fwd", None, None, None, None, None, None, None, 4, None)
     assert st == 1
+    st, _ = _status("esm_set_layer_precision", None, None, 1, None)
+    assert st == 1
     st, _ = _status("esm_linear_e4m3_fwd", None, None, None, None, None, None, None, None, None, None, 1, 64, 128,
                     0, None)
     assert st == 1

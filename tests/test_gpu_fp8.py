@@ -266,6 +266,71 @@ def test_forward_needs_prepared_weights(gu):
     enc.close()
 
 
+# ------------------------------------------------------------------ per-layer precision
+
+def _tiny8_stack_inputs(gu, layers):
+    m = TINY8
+    b = D.make_batch(D.WORKLOADS["tiny"])
+    ws = [gu.layer_weights(m.hidden, m.ffn, l)[0] for l in range(layers)]
+    x = gu.to_dev_bf16(D.make_hidden(b.T, m.hidden, 0, 2))
+    return m, b, ws, x
+
+
+def test_layer_precision_all_bf16_equals_the_bf16_encoder(gu):
+    """Every layer set to bf16: no FP8 weights needed, output bit-identical to
+    a bf16 encoder's, and the FP8 state untouched."""
+    m, b, ws, x = _tiny8_stack_inputs(gu, 3)
+    cu = gu.to_dev_i32(b.cu_seqlens)
+    enc8 = _encoder(m, layers=3)
+    enc8.set_layer_precision(["bf16"] * 3)
+    y8 = gu.bits_of(enc8.stack_fwd(ws, cu, b.B, b.T, b.max_seqlen, x_in=x))
+    enc = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn, num_hidden_layers=3)
+    y = gu.bits_of(enc.stack_fwd(ws, cu, b.B, b.T, b.max_seqlen, x_in=x))
+    assert np.array_equal(y8, y)
+    st = enc8.fp8_get_state()
+    assert np.all(st["steps"] == 0) and np.all(st["act_scale"] == 1)
+    enc8.close()
+    enc.close()
+
+
+def test_layer_precision_mixed_equals_layer_by_layer(gu):
+    """[fp8, bf16, fp8]: the stack equals layer 0 on an FP8 encoder, layer 1 on
+    a bf16 encoder and layer 2 on an FP8 encoder, each fresh (first step, all
+    scales 1), bit for bit; the bf16 layer's FP8 step count stays 0."""
+    m, b, ws, x = _tiny8_stack_inputs(gu, 3)
+    cu = gu.to_dev_i32(b.cu_seqlens)
+    enc = _encoder(m, layers=3)
+    enc.set_layer_precision(["fp8", "bf16", "fp8"])
+    enc.fp8_prepare_layer(0, ws[0])
+    enc.fp8_prepare_layer(2, ws[2])            # layer 1 needs no FP8 weights
+    got = gu.bits_of(enc.stack_fwd(ws, cu, b.B, b.T, b.max_seqlen, x_in=x))
+    assert list(enc.fp8_get_state()["steps"]) == [1, 0, 1]
+    ea, eb = _encoder(m, layers=3), _encoder(m, layers=3)
+    ea.fp8_prepare_layer(0, ws[0])
+    eb.fp8_prepare_layer(2, ws[2])
+    e16 = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn, num_hidden_layers=1)
+    y = ea.layer_fwd(ws[0], x, cu, b.B, b.T, b.max_seqlen, layer_idx=0)
+    y = e16.layer_fwd(ws[1], y, cu, b.B, b.T, b.max_seqlen)
+    y = eb.layer_fwd(ws[2], y, cu, b.B, b.T, b.max_seqlen, layer_idx=2)
+    assert np.array_equal(got, gu.bits_of(y))
+    for e in (enc, ea, eb, e16):
+        e.close()
+
+
+def test_layer_precision_rejects_bad_settings(gu):
+    m = TINY8
+    e16 = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn, num_hidden_layers=2)
+    with pytest.raises(esm.EsmError) as ei:
+        e16.set_layer_precision(["bf16", "bf16"])
+    assert ei.value.status == 8  # ESM_ERR_STATE: no FP8 state in a bf16 encoder
+    e8 = _encoder(m, layers=2)
+    with pytest.raises(esm.EsmError) as ei:
+        e8.set_layer_precision(["bf16"])
+    assert ei.value.status == 2  # ESM_ERR_SHAPE
+    e8.close()
+    e16.close()
+
+
 # ------------------------------------------------------------------ delayed scaling on one layer
 
 def _act_scales(st, l):
