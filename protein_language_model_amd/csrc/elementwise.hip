@@ -272,49 +272,44 @@ __global__ void k_take_cols(const bf16_t* __restrict__ src, int32_t ld_src, bf16
 
 // Sequence-level embedding: out[s, :] = mean of x over the rows of sequence s
 // (segs[s] = first row, length), fp32; 0 for an empty sequence.  One
-// workgroup per sequence: wave w sums rows w, w + 4, ... in fp32 (lane l owns
-// the 8 columns of chunks l, l + 64, ...), then the four partial sums are
-// added in a fixed order, so the result does not depend on scheduling.
-template <int CH>
+// workgroup per (sequence, 64-column slab), so that many workgroups share the
+// sequence's rows: lane l of wave w reads row 8 w + l / 8 (+ 32 i) at the
+// slab's 16-byte chunk l % 8 and sums in fp32; the 8 row lanes of a chunk are
+// added by lane exchange, then the four waves in a fixed order, so the
+// result does not depend on scheduling.
 __global__ __launch_bounds__(256) void k_segment_mean(const bf16_t* __restrict__ x, const int32_t* __restrict__ segs,
                                                       int32_t H, float* __restrict__ out) {
-  extern __shared__ float part[];  // [4, H]
-  const int s = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float part[4][64];
+  const int s = blockIdx.x, c0 = blockIdx.y * 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t start = segs[2 * s];
   const int L = segs[2 * s + 1];
-  const int chunks = H / 8;
-  float acc[CH][8];
+  const int ch = lane & 7;
+  float acc[8];
 #pragma unroll
-  for (int i = 0; i < CH; ++i)
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int r = wave * 8 + (lane >> 3); r < L; r += 32) {
+    const u32x4 w = *(const u32x4*)(x + (start + r) * H + c0 + ch * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
-#pragma unroll 2
-  for (int r = wave; r < L; r += 4) {
-    const bf16_t* xr = x + (start + r) * H;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = lane + 64 * i;
-      if (c < chunks) {
-        const u32x4 w = *(const u32x4*)(xr + c * 8);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[i][2 * e] += bflo(w[e]);
-          acc[i][2 * e + 1] += bfhi(w[e]);
-        }
-      }
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bflo(w[e]);
+      acc[2 * e + 1] += bfhi(w[e]);
     }
   }
 #pragma unroll
-  for (int i = 0; i < CH; ++i) {
-    const int c = lane + 64 * i;
-    if (c < chunks)
+  for (int off = 8; off < 64; off <<= 1)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part[wave * H + c * 8 + e] = acc[i][e];
-  }
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off);
+  if (lane < 8)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[wave][lane * 8 + e] = acc[e];
   __syncthreads();
-  const float inv = L > 0 ? 1.0f / (float)L : 0.0f;
-  for (int col = threadIdx.x; col < H; col += 256)
-    out[(int64_t)s * H + col] = ((part[col] + part[H + col]) + (part[2 * H + col] + part[3 * H + col])) * inv;
+  if (threadIdx.x < 64) {
+    const int col = threadIdx.x;
+    const float inv = L > 0 ? 1.0f / (float)L : 0.0f;
+    out[(int64_t)s * H + c0 + col] = ((part[0][col] + part[1][col]) + (part[2][col] + part[3][col])) * inv;
+  }
 }
 
 }  // namespace
@@ -390,14 +385,8 @@ hipError_t launch_take_cols(const bf16_t* src, int32_t ld_src, bf16_t* dst, int6
 hipError_t launch_segment_mean(const bf16_t* x, const int32_t* segs, int32_t B, int32_t H, float* out,
                                hipStream_t st) {
   if (B <= 0) return hipSuccess;
-  const int ch = (H / 8 + 63) / 64;
-  const size_t shmem = sizeof(float) * 4 * (size_t)H;
-  if (ch <= 1) hipLaunchKernelGGL(k_segment_mean<1>, dim3(B), dim3(256), shmem, st, x, segs, H, out);
-  else if (ch <= 2) hipLaunchKernelGGL(k_segment_mean<2>, dim3(B), dim3(256), shmem, st, x, segs, H, out);
-  else if (ch <= 3) hipLaunchKernelGGL(k_segment_mean<3>, dim3(B), dim3(256), shmem, st, x, segs, H, out);
-  else if (ch <= 5) hipLaunchKernelGGL(k_segment_mean<5>, dim3(B), dim3(256), shmem, st, x, segs, H, out);
-  else if (ch <= 8) hipLaunchKernelGGL(k_segment_mean<8>, dim3(B), dim3(256), shmem, st, x, segs, H, out);
-  else return hipErrorInvalidValue;
+  if (H % 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_segment_mean, dim3((unsigned)B, (unsigned)(H / 64)), dim3(256), 0, st, x, segs, H, out);
   return hipGetLastError();
 }
 
