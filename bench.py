@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--padded", action="store_true", help="also time the padded bshd layout of the same batch")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip timing the final LayerNorm / LM head / means")
+    ap.add_argument("--no-vendor-gemm", action="store_true", help="skip the hipBLASLt fc1-shape reference timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference dispatch for HBM byte counters)")
     return ap.parse_args()
@@ -192,24 +193,33 @@ def main():
             enc.stack_fwd(weights, cu, B, T, batch.max_seqlen, token_ids=ids, embedding=emb_d, x_out=out,
                           workspace=ws, stream=stream)
 
-        def timed_steps(n: int) -> float:
+        def timed_steps(n: int, per_step: list = None) -> float:
+            """Mean ms per step over n steps; per_step (if given) receives each
+            step's own duration from an event recorded after it."""
+            marks = [torch.cuda.Event(enable_timing=True) for _ in range(n)] if per_step is not None else None
             torch.cuda.synchronize()
             e0.record(stream)
-            for _ in range(n):
+            for i in range(n):
                 step()
+                if marks:
+                    marks[i].record(stream)
             e1.record(stream)
             torch.cuda.synchronize()
+            if marks:
+                per_step[:] = [e0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, n)]
             return e0.elapsed_time(e1) / n
 
         for _ in range(warmup):
             step()
-        ms = timed_steps(args.steps)
+        steps_ms = []
+        ms = timed_steps(args.steps, steps_ms)
         prof = ms_instr = None
         if not args.no_kernel_timing:
             enc.profile_enable(True)
             ms_instr = timed_steps(args.steps)
             prof = enc.profile_read()
             enc.profile_enable(False)
+        measure.steps_ms = steps_ms
         return enc, ws, ms, prof, ms_instr
 
     def kernel_table(prof):
@@ -223,11 +233,32 @@ def main():
                                                  else args.warmup)
     tflops = total_flops / (ms * 1e-3) / 1e12
     value = T / (ms * 1e-3)
+    sm = sorted(measure.steps_ms)
+    step_stats = {"median": round(sm[len(sm) // 2], 4), "min": round(sm[0], 4), "max": round(sm[-1], 4)} if sm else None
     roofline = kernels = None
     if prof:
         kernels = kernel_table(prof)
         roofline = roofline_of(prof, fl, peaks)
         roofline["traffic"] = traffic_record(("fp8_" if fp8_main else "") + roofline["kernel"], T, m.hidden, m.ffn)
+
+    # Context for the dominant kernel: the vendor GEMM library (hipBLASLt via
+    # torch.matmul, plain bf16, no epilogue) on the fc1 shape of this batch.
+    vendor = None
+    if not args.no_vendor_gemm:
+        xa = torch.randn((T, m.hidden), device=dev).to(torch.bfloat16)
+        wa = torch.randn((m.hidden, m.ffn), device=dev).to(torch.bfloat16)   # W^T, contiguous
+        for _ in range(3):
+            torch.matmul(xa, wa)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(20):
+            torch.matmul(xa, wa)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_v = e0.elapsed_time(e1) / 20
+        vendor = {"what": "torch.matmul (hipBLASLt) bf16 [T,H] x [H,F], no bias/GELU epilogue",
+                  "us_per_call": round(ms_v * 1e3, 1), "tflops": round(fl["gemm_fc1"] / (ms_v * 1e-3) / 1e12, 1)}
+        del xa, wa
 
     # After the stack (final LayerNorm, masked-LM logits, per-sequence means):
     # timed on its own, on the stack output of the last timed step.
@@ -326,9 +357,11 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "step_ms": step_stats,
         "ms_per_step_with_kernel_events": round(ms_instrumented, 4) if ms_instrumented else None,
         "padded": padded,
         "head": head,
+        "vendor_gemm_fc1": vendor,
         "fp8": fp8,
     }
     print(json.dumps(rec))
