@@ -140,6 +140,30 @@ def roofline_of(prof, fl, peaks):
             "flops_per_launch": fl[dom]}
 
 
+def rooflines_all(prof, fl, peaks, T: int, H: int, fp8: bool) -> dict:
+    """Achieved rate of every kernel class against the bound that applies to it:
+    MFMA flops for the GEMMs and attention (attention also reports its exp rate),
+    HBM bytes for LayerNorm and the embedding gather (algorithmic bytes: each
+    input read once, each output written once)."""
+    out = {}
+    for k, (ms_tot, n) in prof.items():
+        if not n:
+            continue
+        avg_s = ms_tot / n * 1e-3
+        if k in fl:
+            peak = peaks.get(k, PEAK_BF16_TFLOPS)
+            a = fl[k] / avg_s / 1e12
+            out[k] = {"bound": "mfma", "achieved": round(a, 1), "peak": peak, "unit": "TFLOP/s",
+                      "frac": round(a / peak, 4)}
+        elif k in ("layernorm", "embed"):
+            # LN: x in (bf16) + y out (bf16, or E4M3 in an FP8 encoder); embed: y out (the table is tiny)
+            nbytes = (T * H * 2 + T * H * (1 if fp8 else 2)) if k == "layernorm" else T * H * 2
+            a = nbytes / avg_s / 1e9
+            out[k] = {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(a / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -235,11 +259,12 @@ def main():
     value = T / (ms * 1e-3)
     sm = sorted(measure.steps_ms)
     step_stats = {"median": round(sm[len(sm) // 2], 4), "min": round(sm[0], 4), "max": round(sm[-1], 4)} if sm else None
-    roofline = kernels = None
+    roofline = kernels = rooflines = None
     if prof:
         kernels = kernel_table(prof)
         roofline = roofline_of(prof, fl, peaks)
         roofline["traffic"] = traffic_record(("fp8_" if fp8_main else "") + roofline["kernel"], T, m.hidden, m.ffn)
+        rooflines = rooflines_all(prof, fl, peaks, T, m.hidden, fp8_main)
 
     # Context for the dominant kernel: the vendor GEMM library (hipBLASLt via
     # torch.matmul, plain bf16, no epilogue) on the fc1 shape of this batch.
@@ -327,6 +352,8 @@ def main():
             fp8["kernels"] = kernel_table(prof8)
             fp8["roofline"] = roofline_of(prof8, fl, {k: PEAK_FP8_TFLOPS for k in fl if k.startswith("gemm")})
             fp8["roofline"]["traffic"] = traffic_record("fp8_" + fp8["roofline"]["kernel"], T, m.hidden, m.ffn)
+            fp8["rooflines"] = rooflines_all(prof8, fl, {k: PEAK_FP8_TFLOPS for k in fl if k.startswith("gemm")}, T,
+                                             m.hidden, True)
         enc8.close()
         del ws8
 
@@ -355,6 +382,7 @@ def main():
         "tflops": round(tflops, 1),
         "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
+        "rooflines": rooflines,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "step_ms": step_stats,

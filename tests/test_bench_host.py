@@ -37,3 +37,16 @@ def test_traffic_record_matches_source_and_shape():
         assert got is None
     assert b.traffic_record("gemm_fc1", 16208, 2560, 10240) is None   # another shape: no record
     assert b.traffic_record("no_such_kernel", *shape) is None
+
+
+def test_rooflines_all_uses_each_kernels_bound():
+    b = _bench()
+    fl = b.layer_flops(1280, 5120, 32293, 16024465)
+    prof = {"gemm_fc1": (0.45 * 33, 33), "layernorm": (0.033 * 66, 66), "embed": (0.0237, 1), "attention": (0.135 * 33, 33),
+            "segment": (0.011, 1)}
+    r = b.rooflines_all(prof, fl, {"gemm_fc1": b.PEAK_BF16_TFLOPS, "attention": b.PEAK_BF16_TFLOPS}, 32293, 1280, False)
+    assert r["gemm_fc1"]["unit"] == "TFLOP/s" and abs(r["gemm_fc1"]["achieved"] - fl["gemm_fc1"] / 0.45e-3 / 1e12) < 0.1
+    assert r["layernorm"]["bound"] == "hbm" and r["layernorm"]["bytes_per_launch"] == 4 * 32293 * 1280
+    assert "segment" not in r
+    r8 = b.rooflines_all(prof, fl, {}, 32293, 1280, True)
+    assert r8["layernorm"]["bytes_per_launch"] == 3 * 32293 * 1280
