@@ -326,3 +326,27 @@ def param_count(hidden: int, ffn: int, layers: int, vocab: int = 33) -> int:
     H, F = hidden, ffn
     per_layer = (3 * H * H + 3 * H) + (H * H + H) + (F * H + F) + (H * F + H) + 4 * H
     return layers * per_layer + vocab * H
+
+
+# --------------------------------------------------------------------------
+# Biased attention (the Evoformer-style kernel of the DeepSpeed4Science page)
+# --------------------------------------------------------------------------
+# [DS4SCI] "DeepSpeed4Science 深度解读以 AI 系统优化技术驱动大规模科学发现"
+# (mhpn.cn), sections 3.2 and 5.3: Q, K, V are [B, N, L, H, D]; up to two
+# additive biases shaped [B, N, 1, 1, L] (a per-key mask bias) and
+# [B, 1, H, L, L] (a pair bias shared by the N rows) are added to the scores
+# before the softmax.  The page leaves the score scale unstated; the reading
+# used is 1/sqrt(D), as in the encoder.
+
+def biased_attention(q, k, v, biases=(), scale: Optional[float] = None) -> np.ndarray:
+    """softmax(q k^T * scale + sum(biases)) v per (b, n, h); q, k, v [B, N, L, H, D]."""
+    q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+    s = np.einsum("bnqhd,bnkhd->bnhqk", q, k) * scale
+    for b in biases:
+        s = s + np.asarray(b, np.float64)          # broadcast [B,N,1,1,L] or [B,1,H,L,L]
+    m = s.max(axis=-1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        p = np.exp(s - m)
+        p = p / p.sum(axis=-1, keepdims=True)
+    return np.einsum("bnhqk,bnkhd->bnqhd", p, v)

@@ -468,3 +468,65 @@ def test_head_forward_composes_final_ln_head_and_means():
     assert np.abs(z.mean(axis=1)).max() < 1e-12
     assert np.abs(logits - O.lm_head(final, w)).max() == 0
     assert np.abs(pooled[1] - final[4:9].mean(axis=0)).max() < 1e-15
+
+
+# ---------------------------------------------------------------- biased attention
+
+def _brute_biased(q, k, v, biases, scale):
+    B, N, L, H, D = q.shape
+    out = np.zeros(q.shape)
+    for b in range(B):
+        for n in range(N):
+            for h in range(H):
+                for i in range(L):
+                    s = []
+                    for j in range(L):
+                        t = sum(float(q[b, n, i, h, e]) * float(k[b, n, j, h, e]) for e in range(D)) * scale
+                        for bb in biases:
+                            t += float(bb[b, 0 if bb.shape[1] == 1 else n, 0 if bb.shape[2] == 1 else h,
+                                          0 if bb.shape[3] == 1 else i, j])
+                        s.append(t)
+                    m = max(s)
+                    ex = [math.exp(x - m) for x in s]
+                    z = sum(ex)
+                    for e in range(D):
+                        out[b, n, i, h, e] = sum(ex[j] / z * float(v[b, n, j, h, e]) for j in range(L))
+    return out
+
+
+def test_biased_attention_matches_brute_force():
+    r = _rng(41)
+    B, N, L, H, D = 2, 2, 5, 2, 4
+    q, k, v = (r.standard_normal((B, N, L, H, D)) for _ in range(3))
+    mask = r.standard_normal((B, N, 1, 1, L))
+    pair = r.standard_normal((B, 1, H, L, L))
+    got = O.biased_attention(q, k, v, [mask, pair])
+    assert np.abs(got - _brute_biased(q, k, v, [mask, pair], 0.5)).max() < 1e-12
+
+
+def test_biased_attention_special_cases():
+    r = _rng(42)
+    B, N, L, H, D = 1, 3, 6, 2, 64
+    q, k, v = (r.standard_normal((B, N, L, H, D)) for _ in range(3))
+    # no bias: each (b, n) row is the encoder's attention over one segment of length L
+    plain = O.biased_attention(q, k, v)
+    for n in range(N):
+        seg = O.attention(q[0, n], k[0, n], v[0, n], np.array([0, L]))
+        assert np.abs(plain[0, n].reshape(L, H * D) - seg).max() < 1e-12
+    # a bias constant along the keys changes nothing (softmax shift invariance)
+    c = np.repeat(r.standard_normal((B, 1, H, L, 1)), L, axis=-1)
+    assert np.abs(O.biased_attention(q, k, v, [c]) - plain).max() < 1e-12
+    # a -inf mask bias removes those keys: same as attention over the kept keys only
+    mask = np.zeros((B, N, 1, 1, L))
+    mask[..., [1, 4]] = -np.inf
+    keep = [0, 2, 3, 5]
+    ref = O.biased_attention(q, k[:, :, keep], v[:, :, keep])
+    assert np.abs(O.biased_attention(q, k, v, [mask]) - ref).max() < 1e-12
+    # the pair bias is shared by the N rows: with q = 0 the weights are softmax(pair) for every n
+    pair = r.standard_normal((B, 1, H, L, L))
+    out0 = O.biased_attention(np.zeros_like(q), k, v, [pair])
+    w = np.exp(pair[0, 0] - pair[0, 0].max(-1, keepdims=True))
+    w /= w.sum(-1, keepdims=True)
+    for n in range(N):
+        for h in range(H):
+            assert np.abs(out0[0, n, :, h] - w[h] @ v[0, n, :, h]).max() < 1e-12
