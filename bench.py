@@ -10,7 +10,9 @@ events for the roofline of the dominant kernel.  The same batch is then run
 through the FP8 (E4M3, delayed scaling) encoder, whose scales come from at
 least 10 warm-up steps, and reported under "fp8"; what follows the stack
 (final LayerNorm, masked-LM logits, per-sequence means) is timed on its own
-under "head".  Prints one JSON line.
+under "head".  The biased attention kernel (the DeepSpeed4Science page's
+Evoformer attention with a mask bias and a pair bias) is timed on its own
+synthetic MSA-row shape under "biased_attention".  Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
                     [--padded] [--no-fp8]
@@ -56,6 +58,8 @@ def parse():
     ap.add_argument("--padded", action="store_true", help="also time the padded bshd layout of the same batch")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip timing the final LayerNorm / LM head / means")
+    ap.add_argument("--no-biased-attention", action="store_true",
+                    help="skip timing the biased (Evoformer MSA-row) attention kernel")
     ap.add_argument("--no-vendor-gemm", action="store_true", help="skip the hipBLASLt fc1-shape reference timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference dispatch for HBM byte counters)")
@@ -162,6 +166,61 @@ def rooflines_all(prof, fl, peaks, T: int, H: int, fp8: bool) -> dict:
             out[k] = {"bound": "hbm", "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(a / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes}
     return out
+
+
+def bench_biased_attention(enc, steps: int, dev: str, stream) -> dict:
+    """The biased attention kernel alone on the synthetic MSA-row shape
+    [1, 128, 512, 8, 64] with a mask bias and a pair bias: time per call
+    (one launch) from HIP events on the library stream, against both bounds
+    (MFMA flops 4 L^2 64 per (b, n, h); HBM bytes: q, k, v read and out
+    written once, mask and pair bias read once); the fp64 oracle is timed on
+    one row n and scaled to the call."""
+    import torch
+    from oracle import esm_oracle as O
+    from protein_language_model_amd import datagen as D
+    w = D.BIASED_ATTN_WORKLOADS["msa_row_512"]
+    bits = D.make_biased_attention_inputs(w.B, w.N, w.L, w.heads, seed=0)
+    t = {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
+         for k, v in bits.items()}
+    out = torch.empty_like(t["q"])
+
+    def call():
+        enc.biased_attention_fwd(t["q"], t["k"], t["v"], t["mask"], t["pair"], out=out, stream=stream)
+
+    for _ in range(3):
+        call()
+    n = max(10, steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    flops = 4.0 * w.B * w.N * w.heads * w.L * w.L * 64
+    nbytes = 4 * (w.B * w.N * w.L * w.heads * 64 * 2) + w.B * w.N * w.L * 2 + w.B * w.heads * w.L * w.L * 2
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    t_mfma, t_hbm = flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roof.update({"traffic": None, "flops_per_launch": flops, "bytes_per_launch": nbytes})
+    f = {k: D.bf16_bits_to_f64(v[:, :1]) if k != "pair" else D.bf16_bits_to_f64(v) for k, v in bits.items()}
+    t0 = time.perf_counter()
+    O.biased_attention(f["q"], f["k"], f["v"], [f["mask"], f["pair"]])
+    dt_row = time.perf_counter() - t0
+    del t, out
+    return {"shape": f"q, k, v, out [{w.B}, {w.N}, {w.L}, {w.heads}, 64] bf16; mask [{w.B}, {w.N}, 1, 1, {w.L}], "
+                     f"pair [{w.B}, 1, {w.heads}, {w.L}, {w.L}] bf16",
+            "ms_per_call": round(ms, 4), "calls": n, "tflops": round(tf, 1), "hbm_gbs": round(gbs, 1),
+            "roofline": roof,
+            "oracle": {"ms_per_call": round(dt_row * w.B * w.N * 1e3, 1), "kind": "oracle",
+                       "sample": f"one of the {w.B * w.N} rows n (fp64 numpy), {dt_row:.2f} s, scaled to the call"}}
 
 
 def main():
@@ -314,6 +373,10 @@ def main():
                            f"[{B},{m.hidden}] fp32",
                 "share_of_step": round(ms_h / ms, 4)}
 
+    biased = None
+    if not args.no_biased_attention:
+        biased = bench_biased_attention(enc, args.steps, dev, stream)
+
     padded = None
     if args.padded:
         S = 1024
@@ -389,6 +452,7 @@ def main():
         "ms_per_step_with_kernel_events": round(ms_instrumented, 4) if ms_instrumented else None,
         "padded": padded,
         "head": head,
+        "biased_attention": biased,
         "vendor_gemm_fc1": vendor,
         "fp8": fp8,
     }

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 6
+#define ESM_ABI_VERSION 7
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -270,6 +270,29 @@ esm_status esm_attention_fwd(esm_encoder* enc, const void* qkv, void* ctx,
                              const int32_t* cu_seqlens_dev, int32_t B, int64_t T,
                              void* workspace, size_t workspace_bytes, esm_stream_t stream);
 
+/* Biased attention ([DS4SCI] 3.2 and 5.3: the Evoformer attention kernel,
+ * which takes Q, K, V shaped [B, N, L, heads, D] and up to two additive
+ * biases, a per-key mask bias [B, N, 1, 1, L] and a pair bias
+ * [B, 1, heads, L, L] shared by the N rows).  For every (b, n, h):
+ *   out[b, n, i, h, :] = sum_j P_ij v[b, n, j, h, :],
+ *   P_ij = softmax_j( q_i . k_j / sqrt(64) + mask[b, n, j] + pair[b, h, i, j] ).
+ * q, k, v, out: bf16, contiguous [B, N, L, heads, 64], 16-byte aligned (the
+ *   head size is 64 only).  out must not overlap q, k or v.
+ * mask_bias: bf16 [B, N, L] (the [B, N, 1, 1, L] tensor) or NULL (no mask).
+ * pair_bias: bf16 [B, heads, L, L] (the [B, 1, heads, L, L] tensor) or NULL.
+ * Both biases are read as stored (e.g. -inf or a large negative value for
+ * masked keys); they need 8-byte alignment when L % 4 == 0.  A row whose
+ * scores are all -inf has no softmax and yields NaN, as the definition does.
+ * enc selects the device and the profiling timers; no workspace is used.
+ * Errors: ESM_ERR_NULL (enc NULL; q, k, v or out NULL with no size 0),
+ * ESM_ERR_SHAPE (B, N, heads < 0, L < 0 or L > 65536, or more than 2^31 - 1
+ * workgroups), ESM_ERR_UNSUPPORTED (misaligned pointer).  Any size 0 returns
+ * ESM_OK with no launch.  Asynchronous on stream. */
+esm_status esm_biased_attention_fwd(esm_encoder* enc, const void* q, const void* k, const void* v,
+                                    const void* mask_bias, const void* pair_bias, void* out,
+                                    int32_t B, int32_t N, int32_t L, int32_t heads,
+                                    esm_stream_t stream);
+
 typedef enum {
   ESM_EPI_BIAS = 0,          /* y = x W^T + b */
   ESM_EPI_BIAS_GELU = 1,     /* y = GELU(x W^T + b) */
@@ -374,7 +397,8 @@ typedef enum {
   ESM_K_SEGMENT = 0, ESM_K_EMBED = 1, ESM_K_LAYERNORM = 2, ESM_K_GEMM_QKV = 3,
   ESM_K_ATTENTION = 4, ESM_K_GEMM_OUT = 5, ESM_K_GEMM_FC1 = 6, ESM_K_GEMM_FC2 = 7,
   ESM_K_OTHER = 8, ESM_K_FP8 = 9 /* weight casts, scale updates */,
-  ESM_K_HEAD = 10 /* final LayerNorm, LM head, sequence means */, ESM_K_COUNT = 11
+  ESM_K_HEAD = 10 /* final LayerNorm, LM head, sequence means */,
+  ESM_K_BIASED_ATTENTION = 11 /* esm_biased_attention_fwd */, ESM_K_COUNT = 12
 } esm_kernel_class;
 
 /* When on, every launch is bracketed by HIP events recorded on the launch

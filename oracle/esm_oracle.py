@@ -16,6 +16,8 @@ Pages cited (title, section):
              模型概述/描述, 输入, 输出
   [TE-RU]    Russian summary of the TransformerEngine tutorial (aikraft.ru),
              section "Ключевые компоненты и Fused Kernels"
+  [DS4SCI]   "DeepSpeed4Science 深度解读以 AI 系统优化技术驱动大规模科学发现"
+             (mhpn.cn), sections 3.2 and 5.3 (biased attention only)
 
 * Encoder = stack of BERT-style bidirectional Transformer layers ([CARD] 描述;
   [TE-ESM2] 核心技术架构设计).  Each layer has self-attention, LayerNorm and two
@@ -38,6 +40,10 @@ Readings where the pages are silent (each is listed in the design notes):
   dropout; no final LayerNorm inside the stack; X0 = E[ids].  After the
   stack (head_forward): final LayerNorm, the ESM-2 masked-LM head with the
   decoder tied to the embedding, and per-sequence mean embeddings.
+
+A second, separate function, biased_attention, is the Evoformer attention of
+[DS4SCI]: softmax(q k^T / sqrt(D) + mask bias + pair bias) v per (b, n, h) on
+[B, N, L, H, D] tensors (the scale is a reading; the page does not state it).
 
 Everything is evaluated densely in float64 on bf16-valued inputs, per sequence
 and per head, with an exact max-subtracted softmax.

@@ -56,22 +56,27 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // are distinct too (key reads with a 256-byte bank sweep).
 __device__ __forceinline__ int kSwz(int r) { return (((r & 3) << 1) | ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1); }
 
-__global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
-  const int heads = a.heads;
-  const int tile = blockIdx.x / heads, head = blockIdx.x % heads;
-  if (tile >= *a.ntiles) return;
-  const int s = a.tiles[2 * tile], q0 = a.tiles[2 * tile + 1];
-  const int64_t start = a.segs[2 * s];
-  const int L = a.segs[2 * s + 1];
-  if (L <= 0) return;
+// What a workgroup adds to the scores (bit flags; 0 = the encoder's plain
+// attention).  kBias: scores become s / 8 + biases, tracked in the log2
+// domain, with rows whose keys are all -inf allowed; kMask / kPair: the
+// per-key mask bias / the pair bias is present; kVec: L % 4 == 0, so four
+// consecutive keys' biases are one aligned 8-byte load.
+enum AttnMode { kPlain = 0, kBias = 1, kMask = 2, kPair = 4, kVec = 8 };
 
+
+// One workgroup: 256 query rows from q0 of one head of one sequence of L rows.
+// Qg, Kg, Vg point at row 0 of the sequence for this head; row r of each is
+// 64 contiguous values at + r * rs.  Biased modes add maskg[c] and
+// pairg[r * L + c] to the score of (query row r, key c).  On return o holds
+// this lane's unnormalised context (dims d * 32 + 8 g + 4 lhalf + e in
+// o[d][4 g + e]) and inv the reciprocal of its softmax sum.
+template <int kMode>
+__device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg,
+                                       const bf16_t* __restrict__ Vg, const int64_t rs, const int L, const int q0,
+                                       const bf16_t* __restrict__ maskg, const bf16_t* __restrict__ pairg,
+                                       f32x16 (&o)[2], float& inv) {
   __shared__ __attribute__((aligned(1024))) bf16_t sk[2][kLT * kLdsRow];
   __shared__ __attribute__((aligned(1024))) bf16_t sv[2][kLT * kLdsRow];
-
-  const int64_t T = a.T;
-  const bf16_t* __restrict__ Qg = a.qkv + ((int64_t)(0 * heads + head) * T) * kHeadDim;
-  const bf16_t* __restrict__ Kg = a.qkv + ((int64_t)(1 * heads + head) * T) * kHeadDim;
-  const bf16_t* __restrict__ Vg = a.qkv + ((int64_t)(2 * heads + head) * T) * kHeadDim;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lhalf = lane >> 5;
@@ -81,7 +86,9 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
   const int qc = qrow < L ? qrow : L - 1;
   bf16x8 qf[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const bf16x8*)(Qg + (start + qc) * kHeadDim + kk * 16 + 8 * lhalf);
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const bf16x8*)(Qg + qc * rs + kk * 16 + 8 * lhalf);
+  const bf16_t* __restrict__ prow = nullptr;
+  if constexpr ((kMode & kPair) != 0) prow = pairg + (int64_t)qc * L;
 
   // K/V tiles go straight from global memory into LDS (global_load_lds): the
   // workgroup's 8 instructions per tensor fill 1 KB (8 rows) each; in
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
     for (int i = 0; i < kDmaPerWave; ++i) {
       int key = j * kLT + src_row[i];
       key = key < L ? key : L - 1;
-      const int64_t at = (start + key) * kHeadDim + src_col[i];
+      const int64_t at = key * rs + src_col[i];
       const uint32_t dst = (uint32_t)(buf * kLT * kLdsRow * 2 + (wave_u + kNW * i) * 1024);
       lds_dma16(Kg + at, lds_k + dst);
       lds_dma16(Vg + at, lds_v + dst);
@@ -110,7 +117,6 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
   };
 
   float m_i = -INFINITY, l_i = 0.f;
-  f32x16 o[2];
 #pragma unroll
   for (int d = 0; d < 2; ++d)
 #pragma unroll
@@ -152,14 +158,53 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
 #pragma unroll
     for (int sub = 0; sub < kSub; ++sub) {
     const int j = t * kSub + sub;   // compute tile: keys j*64 .. j*64+63, LDS rows sub*64 ..
-    if (wave_active && j < ntk) {
+    const bool active = wave_active && j < ntk;
+    // S^T for this tile: two 32-key blocks; register r of block kb is key
+    // j*64 + kb*32 + 8*(r/4) + 4*lhalf + r%4.  The MFMAs accumulate onto 0,
+    // or in the biased modes onto 8 * (mask + pair): the accumulated value is
+    // then 8 times the biased score, and the softmax below is the same.  Keys
+    // past the end read a clamped bias; their scores become -inf.
+    f32x16 st[2];
+    if (active) {
+      if constexpr ((kMode & kBias) != 0) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int key0 = j * kKT + kb * 32 + 8 * g + 4 * lhalf;
+            float b[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr ((kMode & kVec) != 0) {
+              const int key = key0 < L ? key0 : L - 4;
+              if constexpr ((kMode & kPair) != 0) {
+                const u32x2 w = *(const u32x2*)(prow + key);
+                b[0] = bflo(w[0]); b[1] = bfhi(w[0]); b[2] = bflo(w[1]); b[3] = bfhi(w[1]);
+              }
+              if constexpr ((kMode & kMask) != 0) {
+                const u32x2 w = *(const u32x2*)(maskg + key);
+                b[0] += bflo(w[0]); b[1] += bfhi(w[0]); b[2] += bflo(w[1]); b[3] += bfhi(w[1]);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int key = key0 + e < L ? key0 + e : L - 1;
+                if constexpr ((kMode & kPair) != 0) b[e] = bf2f(prow[key]);
+                if constexpr ((kMode & kMask) != 0) b[e] += bf2f(maskg[key]);
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st[kb][4 * g + e] = 8.f * b[e];
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
+      }
+    }
+    if (active) {
       const bf16_t* kt = sk[cur] + sub * kKT * kLdsRow;
-      // S^T for this tile: two 32-key blocks.
-      f32x16 st[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[kb][r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const bf16x8 kf = *(const bf16x8*)(&kt[(kb * 32 + lrow) * kLdsRow + koff[kk]]);
@@ -182,18 +227,21 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_i, mx);
-      const float alpha = exp2_fast((m_i - m_new) * kScaleLog2);
-      const float mc = m_new * kScaleLog2;
-      float rs = 0.f;
+      // Biased modes: while every key so far is -inf (masked), subtract 0, so
+      // the probabilities stay 0 instead of exp(-inf - -inf) = NaN.
+      const float m_sub = ((kMode & kBias) != 0 && m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast((m_i - m_sub) * kScaleLog2);
+      const float mc = m_sub * kScaleLog2;
+      float rs_ = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = exp2_fast(fmaf(st[kb][r], kScaleLog2, -mc));
           st[kb][r] = p;
-          rs += p;
+          rs_ += p;
         }
-      l_i = l_i * alpha + rs;
+      l_i = l_i * alpha + rs_;
       m_i = m_new;
 #pragma unroll
       for (int d = 0; d < 2; ++d)
@@ -236,7 +284,30 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
   }
 
   const float lt = l_i + __shfl_xor(l_i, 32);
-  const float inv = 1.0f / lt;
+  inv = 1.0f / lt;
+}
+
+// Encoder attention: one workgroup per (256-row query tile, head) from the
+// segment table; qkv planar [3][heads][T][64], context [T, heads * 64].
+__global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
+  const int heads = a.heads;
+  const int tile = blockIdx.x / heads, head = blockIdx.x % heads;
+  if (tile >= *a.ntiles) return;
+  const int s = a.tiles[2 * tile], q0 = a.tiles[2 * tile + 1];
+  const int64_t start = a.segs[2 * s];
+  const int L = a.segs[2 * s + 1];
+  if (L <= 0) return;
+
+  const int64_t T = a.T;
+  const bf16_t* Qg = a.qkv + ((int64_t)(0 * heads + head) * T + start) * kHeadDim;
+  const bf16_t* Kg = a.qkv + ((int64_t)(1 * heads + head) * T + start) * kHeadDim;
+  const bf16_t* Vg = a.qkv + ((int64_t)(2 * heads + head) * T + start) * kHeadDim;
+  f32x16 o[2];
+  float inv;
+  attend<kPlain>(Qg, Kg, Vg, kHeadDim, L, q0, nullptr, nullptr, o, inv);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lhalf = lane >> 5;
+  const int qrow = q0 + 32 * wave + (lane & 31);
   const int H = heads * kHeadDim;
   if (a.ctx8.y) {
     // E4M3 context for the FP8 out-projection: cast with the tensor's delayed
@@ -273,12 +344,74 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
     }
 }
 
+// Biased attention on [B, N, L, heads, 64] tensors ([DS4SCI] 3.2, 5.3): one
+// workgroup per (b, n, 256-row query tile, head), the head fastest, so with
+// 8 heads every workgroup of head h lands on the same XCD and its L2 keeps
+// that head's pair bias (shared by all n) resident.
+template <int kMode>
+__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu((kMode & kVec) ? 4 : 1, 4)))
+void k_biased_attention(BiasedAttnArgs a) {
+  const int heads = a.heads;
+  const int h = blockIdx.x % heads;
+  const int rest = blockIdx.x / heads;
+  const int tile = rest % a.qtiles;
+  const int64_t bn = rest / a.qtiles;
+  const int64_t b = bn / a.N;
+  const int L = a.L, q0 = tile * kAttnTileRows;
+  const int64_t rs = (int64_t)heads * kHeadDim;
+  const int64_t base = (bn * L * heads + h) * kHeadDim;
+  const bf16_t* maskg = (kMode & kMask) ? a.mask + bn * L : nullptr;
+  const bf16_t* pairg = (kMode & kPair) ? a.pair + (b * heads + h) * (int64_t)L * L : nullptr;
+  f32x16 o[2];
+  float inv;
+  attend<kMode>(a.q + base, a.k + base, a.v + base, rs, L, q0, maskg, pairg, o, inv);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lhalf = lane >> 5;
+  const int qrow = q0 + 32 * wave + (lane & 31);
+  if (qrow >= L) return;
+  bf16_t* dst = a.out + base + qrow * rs;
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int dim = d * 32 + 8 * gq + 4 * lhalf;
+      *(u32x2*)(dst + dim) = u32x2{pack_bf2(o[d][4 * gq] * inv, o[d][4 * gq + 1] * inv),
+                                   pack_bf2(o[d][4 * gq + 2] * inv, o[d][4 * gq + 3] * inv)};
+    }
+}
+
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.tile_cap <= 0 || a.T <= 0) return hipSuccess;
   const int64_t nblk = a.tile_cap * a.heads;
   hipLaunchKernelGGL(k_attention, dim3((unsigned)nblk), dim3(64 * kNW), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace esm
+
+namespace esm {
+
+hipError_t launch_biased_attention(const BiasedAttnArgs& a, hipStream_t st) {
+  if (a.B <= 0 || a.N <= 0 || a.L <= 0 || a.heads <= 0) return hipSuccess;
+  const int64_t nblk = (int64_t)a.B * a.N * a.qtiles * a.heads;
+  const int mode = kBias | (a.mask ? kMask : 0) | (a.pair ? kPair : 0) | (a.L % 4 == 0 ? kVec : 0);
+  const dim3 grid((unsigned)nblk), block(64 * kNW);
+  switch (mode) {
+#define ESM_BIASED_CASE(m) \
+    case m: hipLaunchKernelGGL(k_biased_attention<m>, grid, block, 0, st, a); break;
+    ESM_BIASED_CASE(kBias)
+    ESM_BIASED_CASE(kBias | kMask)
+    ESM_BIASED_CASE(kBias | kPair)
+    ESM_BIASED_CASE(kBias | kMask | kPair)
+    ESM_BIASED_CASE(kBias | kVec)
+    ESM_BIASED_CASE(kBias | kMask | kVec)
+    ESM_BIASED_CASE(kBias | kPair | kVec)
+    ESM_BIASED_CASE(kBias | kMask | kPair | kVec)
+#undef ESM_BIASED_CASE
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -189,6 +189,21 @@ struct AttnArgs {
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 
+// Biased attention on [B, N, L, heads, 64] tensors: per (b, n, h),
+// out = softmax(q k^T / 8 + mask[b, n, :] + pair[b, h, :, :]) v.
+struct BiasedAttnArgs {
+  const bf16_t* q;     // [B, N, L, heads, 64]
+  const bf16_t* k;
+  const bf16_t* v;
+  const bf16_t* mask;  // [B, N, L] or null
+  const bf16_t* pair;  // [B, heads, L, L] or null
+  bf16_t* out;         // [B, N, L, heads, 64]
+  int32_t B, N, L, heads;
+  int32_t qtiles;      // ceil(L / kAttnTileRows)
+};
+
+hipError_t launch_biased_attention(const BiasedAttnArgs& a, hipStream_t st);
+
 // Delayed-scaling bookkeeping (fp8.hip).
 struct Fp8State {
   float* act_scale;    // [layers, 4] scale used by the current step (ln1, ctx, ln2, act)

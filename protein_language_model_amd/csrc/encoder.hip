@@ -775,6 +775,32 @@ esm_status esm_attention_fwd(esm_encoder* e, const void* qkv, void* ctx, const i
   return timed(e, ESM_K_ATTENTION, st, "attention", [&] { return launch_attention(aa, st); });
 }
 
+esm_status esm_biased_attention_fwd(esm_encoder* e, const void* q, const void* k, const void* v,
+                                    const void* mask_bias, const void* pair_bias, void* out, int32_t B, int32_t N,
+                                    int32_t L, int32_t heads, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "NULL encoder");
+  if (B < 0 || N < 0 || L < 0 || heads < 0 || L > 65536)
+    return fail(ESM_ERR_SHAPE, "B %d N %d L %d heads %d", B, N, L, heads);
+  if (B == 0 || N == 0 || L == 0 || heads == 0) return ok();
+  if (!q || !k || !v || !out) return fail(ESM_ERR_NULL, "NULL argument");
+  const int32_t qtiles = (L + kAttnTileRows - 1) / kAttnTileRows;
+  if ((int64_t)B * N * qtiles * heads > INT32_MAX)
+    return fail(ESM_ERR_SHAPE, "B %d N %d L %d heads %d: more than 2^31 - 1 workgroups", B, N, L, heads);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(ESM_ERR_UNSUPPORTED, "q/k/v/out not 16-byte aligned");
+  const uintptr_t bias_align = L % 4 == 0 ? 7u : 1u;
+  if (((uintptr_t)mask_bias & bias_align) || ((uintptr_t)pair_bias & bias_align))
+    return fail(ESM_ERR_UNSUPPORTED, "bias not %d-byte aligned", (int)bias_align + 1);
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  BiasedAttnArgs a{};
+  a.q = (const bf16_t*)q; a.k = (const bf16_t*)k; a.v = (const bf16_t*)v;
+  a.mask = (const bf16_t*)mask_bias; a.pair = (const bf16_t*)pair_bias; a.out = (bf16_t*)out;
+  a.B = B; a.N = N; a.L = L; a.heads = heads; a.qtiles = qtiles;
+  hipStream_t st = (hipStream_t)stream;
+  return timed(e, ESM_K_BIASED_ATTENTION, st, "biased attention", [&] { return launch_biased_attention(a, st); });
+}
+
 esm_status esm_linear_fwd(esm_encoder* e, const void* x, const void* w, const void* b, const void* res, void* y,
                           int64_t M, int32_t N, int32_t K, int32_t epi, esm_stream_t stream) {
   g_last_error.clear();

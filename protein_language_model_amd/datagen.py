@@ -20,6 +20,11 @@ Recipe (seed s, stream k):  numpy Generator over SeedSequence([s, k]).
   stream 2      hidden states N(0, 1)  [T, H]
   stream 3      embedding table N(0, 0.02)  [vocab, H]
   stream 4      permutation of sequences (for permutation tests)
+  streams 20-24 biased attention ([B, N, L, heads, 64] tensors): q, k, v
+                N(0, 1) (streams 20, 21, 22); mask bias (stream 23): per
+                (b, n) a valid length drawn integers(ceil(3L/4), L + 1), keys
+                at or past it get the mask value (default -1e9), the rest 0;
+                pair bias N(0, 1) [B, heads, L, L] (stream 24)
   stream 1000+l weights of layer l in the order W_qkv, b_qkv, W_o, b_o, W_1,
                 b_1, W_2, b_2, each N(0, 0.02); LayerNorm gamma = 1, beta = 0
 All float draws are float64 -> float32 -> bfloat16 (round to nearest even).
@@ -40,7 +45,8 @@ import numpy as np
 __all__ = [
     "ModelShape", "Workload", "WORKLOADS", "rng", "to_bf16_bits", "bf16_bits_to_f64",
     "draw_lengths", "make_batch", "make_layer_weights", "make_embedding",
-    "make_hidden", "LAYER_WEIGHT_NAMES",
+    "make_hidden", "LAYER_WEIGHT_NAMES", "BiasedAttnShape", "BIASED_ATTN_WORKLOADS",
+    "make_biased_attention_inputs",
 ]
 
 # Order of the per-layer tensors (names follow nn.Linear's [out, in] layout).
@@ -281,3 +287,38 @@ def random_layernorm_params(H: int, seed: int, stream: int = 5) -> Dict[str, np.
 
 def permutation(B: int, seed: int = 0) -> np.ndarray:
     return rng(seed, 4).permutation(B)
+
+
+@dataclasses.dataclass(frozen=True)
+class BiasedAttnShape:
+    """Shape of one biased-attention call: q, k, v are [B, N, L, heads, 64]."""
+    name: str
+    B: int
+    N: int
+    L: int
+    heads: int
+
+
+# The Evoformer MSA row attention layout of the DeepSpeed4Science page
+# (section 5.3: Q, K, V [Batch, N_seq, N_res, Head, Dim], a residue mask bias
+# and a pair bias); the page gives no sizes, so these are synthetic: 128 MSA
+# rows of 512 residues, 8 heads of 64.
+BIASED_ATTN_WORKLOADS: Dict[str, BiasedAttnShape] = {
+    "tiny": BiasedAttnShape("tiny", 2, 3, 77, 2),
+    "msa_row_512": BiasedAttnShape("msa_row_512", 1, 128, 512, 8),
+}
+
+
+def make_biased_attention_inputs(B: int, N: int, L: int, heads: int, seed: int = 0,
+                                 mask_value: float = -1e9) -> Dict[str, np.ndarray]:
+    """bf16 bit patterns: q, k, v [B, N, L, heads, 64]; mask [B, N, 1, 1, L];
+    pair [B, 1, heads, L, L] (see the module recipe, streams 20-24)."""
+    shape = (B, N, L, heads, 64)
+    out = {}
+    for name, stream in (("q", 20), ("k", 21), ("v", 22)):
+        out[name] = to_bf16_bits(rng(seed, stream).standard_normal(shape).astype(np.float32))
+    valid = rng(seed, 23).integers(-(-3 * L // 4), L + 1, size=(B, N))
+    mask = np.where(np.arange(L)[None, None, :] >= valid[:, :, None], mask_value, 0.0)
+    out["mask"] = to_bf16_bits(mask.reshape(B, N, 1, 1, L).astype(np.float32))
+    out["pair"] = to_bf16_bits(rng(seed, 24).standard_normal((B, 1, heads, L, L)).astype(np.float32))
+    return out

@@ -25,7 +25,7 @@ EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_E4M3 = 0, 1, 2, 3
 WS_REGIONS = {"ln1": 0, "qkv": 1, "ctx": 2, "x1": 3, "ln2": 4, "act": 5, "pos": 6, "tiles": 7, "ntiles": 8, "segs": 9}
 ATTN_TILE_ROWS = 256  # ESM_ATTN_TILE_ROWS: query rows per attention workgroup
 KERNEL_CLASSES = ("segment", "embed", "layernorm", "gemm_qkv", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
-                  "other", "fp8", "head")
+                  "other", "fp8", "head", "biased_attention")
 FP8_ACT_NAMES = ("ln1", "ctx", "ln2", "act")      # activation tensors tracked per layer, in state order
 FP8_WEIGHT_NAMES = ("w_qkv", "w_out", "w_fc1", "w_fc2")
 LAYER_WEIGHT_NAMES = ("ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_out", "b_out",
@@ -83,6 +83,7 @@ SIGNATURES = {
                                   _p]),
     "esm_segment_table": (_i32, [_p, _i32, _p, _i32, _i64, _i32, _p, _sz, _p]),
     "esm_attention_fwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
+    "esm_biased_attention_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "esm_linear_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
     "esm_layernorm_fwd": (_i32, [_p, _p, _p, _p, _p, _i64, _p]),
     "esm_layernorm_e4m3_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _p]),
@@ -350,6 +351,27 @@ class Encoder:
         _call("esm_attention_fwd", self._h, _ptr(qkv), _ptr(ctx), _ptr(cu_seqlens), int(B), int(T), _ptr(workspace),
               workspace.numel(), _stream(stream))
         return ctx
+
+    def biased_attention_fwd(self, q, k, v, mask_bias=None, pair_bias=None, *, out=None, stream=None):
+        """out = softmax(q k^T / 8 + mask_bias + pair_bias) v per (b, n, h) on
+        q, k, v [B, N, L, heads, 64]; mask_bias [B, N, 1, 1, L] (or [B, N, L]),
+        pair_bias [B, 1, heads, L, L] (or [B, heads, L, L]), both optional."""
+        import torch
+        if q.dim() != 5 or q.shape[-1] != 64 or k.shape != q.shape or v.shape != q.shape:
+            raise ValueError("q, k, v must be [B, N, L, heads, 64] of one shape")
+        B, N, L, heads, _ = q.shape
+        if mask_bias is not None and mask_bias.numel() != B * N * L:
+            raise ValueError("mask_bias must be [B, N, 1, 1, L]")
+        if pair_bias is not None and pair_bias.numel() != B * heads * L * L:
+            raise ValueError("pair_bias must be [B, 1, heads, L, L]")
+        for t in (q, k, v, mask_bias, pair_bias):
+            if t is not None and t.dtype != torch.bfloat16:
+                raise TypeError("biased attention takes bf16 tensors")
+        if out is None:
+            out = torch.empty_like(q)
+        _call("esm_biased_attention_fwd", self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(mask_bias), _ptr(pair_bias),
+              _ptr(out), int(B), int(N), int(L), int(heads), _stream(stream))
+        return out
 
     def linear_fwd(self, x, w, b=None, *, residual=None, epilogue: int = EPI_BIAS, y=None, stream=None):
         import torch
