@@ -40,7 +40,6 @@ constexpr int kKT = 64;     // keys per compute tile
 constexpr int kSub = 2;     // compute tiles per LDS tile (one fill and barrier)
 constexpr int kLT = kKT * kSub;  // keys per LDS tile
 constexpr int kNW = kAttnTileRows / 32;  // waves per workgroup, 32 query rows each
-constexpr int kDmaPerWave = kLT / 8 / kNW;  // 1 KB direct loads per tensor per wave per LDS tile
 constexpr int kLdsRow = 64; // LDS row (elements): one 128-byte row per key
 constexpr float kScaleLog2 = 0.18033688011112042f;  // log2(e) / sqrt(64)
 
@@ -57,11 +56,19 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ int kSwz(int r) { return (((r & 3) << 1) | ((r >> 2) & 1)) ^ (((r >> 3) & 1) << 1); }
 
 // What a workgroup adds to the scores (bit flags; 0 = the encoder's plain
-// attention).  kBias: scores become s / 8 + biases, tracked in the log2
-// domain, with rows whose keys are all -inf allowed; kMask / kPair: the
-// per-key mask bias / the pair bias is present; kVec: L % 4 == 0, so four
-// consecutive keys' biases are one aligned 8-byte load.
-enum AttnMode { kPlain = 0, kBias = 1, kMask = 2, kPair = 4, kVec = 8 };
+// attention).  kBias: scores become s / 8 + biases, with rows whose keys are
+// all -inf allowed; kMask / kPair: the per-key mask bias / the pair bias is
+// present; kVec: L % 4 == 0, so four consecutive keys' biases are one aligned
+// 8-byte load; kLds: L % 8 == 0, and the biases of each 64-key tile are
+// staged through a wave-private LDS region by 16-byte direct loads (one
+// instruction covers 8 rows x 128 bytes instead of 32 rows x 16 bytes), with
+// 64-key K/V LDS tiles so that two workgroups still fit per CU.
+enum AttnMode { kPlain = 0, kBias = 1, kMask = 2, kPair = 4, kVec = 8, kLds = 16 };
+
+// Chunk swizzle of row r of a wave's staged pair bias (16-byte chunk c of the
+// 128-byte row is stored at c ^ kSwzB(r)): the 16 even (odd) rows read by one
+// ds_read_b64 spread over all 8 chunk positions.
+__device__ __forceinline__ int kSwzB(int r) { return (r >> 1) & 7; }
 
 
 // One workgroup: 256 query rows from q0 of one head of one sequence of L rows.
@@ -75,8 +82,16 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
                                        const bf16_t* __restrict__ Vg, const int64_t rs, const int L, const int q0,
                                        const bf16_t* __restrict__ maskg, const bf16_t* __restrict__ pairg,
                                        f32x16 (&o)[2], float& inv) {
-  __shared__ __attribute__((aligned(1024))) bf16_t sk[2][kLT * kLdsRow];
-  __shared__ __attribute__((aligned(1024))) bf16_t sv[2][kLT * kLdsRow];
+  constexpr bool kStaged = (kMode & kLds) != 0;
+  constexpr int kSubM = kStaged ? 1 : kSub;        // compute tiles per LDS tile
+  constexpr int kLTM = kKT * kSubM;                // keys per LDS tile
+  constexpr int kDmaPW = kLTM / 8 / kNW;           // 1 KB direct loads per tensor per wave per LDS tile
+  // Wave-private bias staging (kLds): 32 pair-bias rows x 64 keys (4 KB),
+  // then the tile's 64 mask values repeated 8 times (1 KB).
+  constexpr int kStageElems = 32 * 64 + 512;
+  __shared__ __attribute__((aligned(1024))) bf16_t sk[2][kLTM * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) bf16_t sv[2][kLTM * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) bf16_t sb[kStaged ? kNW : 1][kStaged ? kStageElems : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lhalf = lane >> 5;
@@ -98,21 +113,48 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
   const uint32_t lds_k = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sk[0][0];
   const uint32_t lds_v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sv[0][0];
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  int src_row[kDmaPerWave], src_col[kDmaPerWave];
+  int src_row[kDmaPW], src_col[kDmaPW];
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
+  for (int i = 0; i < kDmaPW; ++i) {
     src_row[i] = 8 * (wave + kNW * i) + (lane >> 3);
     src_col[i] = ((lane & 7) ^ kSwz(src_row[i])) * 8;
   }
   auto gload = [&](int j, int buf) {
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
-      int key = j * kLT + src_row[i];
+    for (int i = 0; i < kDmaPW; ++i) {
+      int key = j * kLTM + src_row[i];
       key = key < L ? key : L - 1;
       const int64_t at = key * rs + src_col[i];
-      const uint32_t dst = (uint32_t)(buf * kLT * kLdsRow * 2 + (wave_u + kNW * i) * 1024);
+      const uint32_t dst = (uint32_t)(buf * kLTM * kLdsRow * 2 + (wave_u + kNW * i) * 1024);
       lds_dma16(Kg + at, lds_k + dst);
       lds_dma16(Vg + at, lds_v + dst);
+    }
+  };
+  // kLds: biases of compute tile j into this wave's region.  Pair bias:
+  // instruction i, lane l fetches row 8i + l/8 of the wave's 32 query rows
+  // (clamped), logical chunk (l % 8) ^ kSwzB(row) of its 64 keys; mask: every
+  // lane fetches chunk l % 8.  With L % 8 == 0 a chunk of 8 keys lies wholly
+  // inside or wholly past the end, where it is clamped to the last chunk.
+  const uint32_t lds_b = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sb[0][0] +
+                         (kStaged ? (uint32_t)wave_u * kStageElems * 2 : 0u);
+  auto bload = [&](int j) {
+    if constexpr (kStaged) {
+      if constexpr ((kMode & kPair) != 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = 8 * i + (lane >> 3);
+          int q = q0 + 32 * wave + rr;
+          q = q < L ? q : L - 1;
+          int key = j * kKT + 8 * ((lane & 7) ^ kSwzB(rr));
+          key = key < L ? key : L - 8;
+          lds_dma16(pairg + (int64_t)q * L + key, lds_b + i * 1024);
+        }
+      }
+      if constexpr ((kMode & kMask) != 0) {
+        int key = j * kKT + 8 * (lane & 7);
+        key = key < L ? key : L - 8;
+        lds_dma16(maskg + key, lds_b + 4096);
+      }
     }
   };
 
@@ -143,21 +185,22 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
     }
 
   const int ntk = (L + kKT - 1) / kKT;   // compute tiles
-  const int ntl = (L + kLT - 1) / kLT;   // LDS tiles
+  const int ntl = (L + kLTM - 1) / kLTM; // LDS tiles
   // A wave whose 32 query rows all lie past the end of the sequence only helps
   // to stage K/V (and meets the barriers); it skips the math.
   const bool wave_active = q0 + 32 * wave < L;
   // LDS tile t is in buffer t & 1; tile t + 1 is fetched into the other
   // buffer during tile t's math and published by the barrier that ends it.
   gload(0, 0);
+  if (wave_active) bload(0);
   vm_wait_all();
   __syncthreads();
   for (int t = 0; t < ntl; ++t) {
     const int cur = t & 1;
     if (t + 1 < ntl) gload(t + 1, cur ^ 1);
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub) {
-    const int j = t * kSub + sub;   // compute tile: keys j*64 .. j*64+63, LDS rows sub*64 ..
+    for (int sub = 0; sub < kSubM; ++sub) {
+    const int j = t * kSubM + sub;  // compute tile: keys j*64 .. j*64+63, LDS rows sub*64 ..
     const bool active = wave_active && j < ntk;
     // S^T for this tile: two 32-key blocks; register r of block kb is key
     // j*64 + kb*32 + 8*(r/4) + 4*lhalf + r%4.  The MFMAs accumulate onto 0,
@@ -173,7 +216,18 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
           for (int g = 0; g < 4; ++g) {
             const int key0 = j * kKT + kb * 32 + 8 * g + 4 * lhalf;
             float b[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr ((kMode & kVec) != 0) {
+            if constexpr (kStaged) {
+              const int c = 4 * kb + g;
+              const bf16_t* sbw = &sb[wave_u][0];
+              if constexpr ((kMode & kPair) != 0) {
+                const u32x2 w = *(const u32x2*)(sbw + lrow * 64 + ((c ^ kSwzB(lrow)) * 8) + 4 * lhalf);
+                b[0] = bflo(w[0]); b[1] = bfhi(w[0]); b[2] = bflo(w[1]); b[3] = bfhi(w[1]);
+              }
+              if constexpr ((kMode & kMask) != 0) {
+                const u32x2 w = *(const u32x2*)(sbw + 2048 + c * 8 + 4 * lhalf);
+                b[0] += bflo(w[0]); b[1] += bfhi(w[0]); b[2] += bflo(w[1]); b[3] += bfhi(w[1]);
+              }
+            } else if constexpr ((kMode & kVec) != 0) {
               const int key = key0 < L ? key0 : L - 4;
               if constexpr ((kMode & kPair) != 0) {
                 const u32x2 w = *(const u32x2*)(prow + key);
@@ -194,6 +248,14 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
 #pragma unroll
             for (int e = 0; e < 4; ++e) st[kb][4 * g + e] = 8.f * b[e];
           }
+        if constexpr (kStaged) {
+          // The region is refilled with the next tile's biases once these
+          // reads have returned.
+          if (j + 1 < ntk) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            bload(j + 1);
+          }
+        }
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -349,7 +411,7 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
 // 8 heads every workgroup of head h lands on the same XCD and its L2 keeps
 // that head's pair bias (shared by all n) resident.
 template <int kMode>
-__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu((kMode & kVec) ? 4 : 1, 4)))
+__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu((kMode & (kVec | kLds)) ? 4 : 1, 4)))
 void k_biased_attention(BiasedAttnArgs a) {
   const int heads = a.heads;
   const int h = blockIdx.x % heads;
@@ -396,7 +458,8 @@ namespace esm {
 hipError_t launch_biased_attention(const BiasedAttnArgs& a, hipStream_t st) {
   if (a.B <= 0 || a.N <= 0 || a.L <= 0 || a.heads <= 0) return hipSuccess;
   const int64_t nblk = (int64_t)a.B * a.N * a.qtiles * a.heads;
-  const int mode = kBias | (a.mask ? kMask : 0) | (a.pair ? kPair : 0) | (a.L % 4 == 0 ? kVec : 0);
+  const int mode = kBias | (a.mask ? kMask : 0) | (a.pair ? kPair : 0) |
+                   ((a.mask || a.pair) && a.L % 8 == 0 ? kLds : (a.L % 4 == 0 ? kVec : 0));
   const dim3 grid((unsigned)nblk), block(64 * kNW);
   switch (mode) {
 #define ESM_BIASED_CASE(m) \
@@ -409,6 +472,9 @@ hipError_t launch_biased_attention(const BiasedAttnArgs& a, hipStream_t st) {
     ESM_BIASED_CASE(kBias | kMask | kVec)
     ESM_BIASED_CASE(kBias | kPair | kVec)
     ESM_BIASED_CASE(kBias | kMask | kPair | kVec)
+    ESM_BIASED_CASE(kBias | kMask | kLds)
+    ESM_BIASED_CASE(kBias | kPair | kLds)
+    ESM_BIASED_CASE(kBias | kMask | kPair | kLds)
 #undef ESM_BIASED_CASE
     default: return hipErrorInvalidValue;
   }
