@@ -42,6 +42,7 @@ constexpr int kLT = kKT * kSub;  // keys per LDS tile
 constexpr int kNW = kAttnTileRows / 32;  // waves per workgroup, 32 query rows each
 constexpr int kLdsRow = 64; // LDS row (elements): one 128-byte row per key
 constexpr float kScaleLog2 = 0.18033688011112042f;  // log2(e) / sqrt(64)
+constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -102,6 +103,16 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
   bf16x8 qf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = *(const bf16x8*)(Qg + qc * rs + kk * 16 + 8 * lhalf);
+  // Biased modes take q / 8 (exact: a power of two) so that the score MFMAs
+  // accumulate s / 8 onto the biases as they are; the softmax then scales by
+  // log2(e) alone.
+  constexpr float kS = (kMode & kBias) != 0 ? kLog2e : kScaleLog2;
+  if constexpr ((kMode & kBias) != 0) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kk][e] = (__bf16)((float)qf[kk][e] * 0.125f);
+  }
   const bf16_t* __restrict__ prow = nullptr;
   if constexpr ((kMode & kPair) != 0) prow = pairg + (int64_t)qc * L;
 
@@ -203,10 +214,10 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
     const int j = t * kSubM + sub;  // compute tile: keys j*64 .. j*64+63, LDS rows sub*64 ..
     const bool active = wave_active && j < ntk;
     // S^T for this tile: two 32-key blocks; register r of block kb is key
-    // j*64 + kb*32 + 8*(r/4) + 4*lhalf + r%4.  The MFMAs accumulate onto 0,
-    // or in the biased modes onto 8 * (mask + pair): the accumulated value is
-    // then 8 times the biased score, and the softmax below is the same.  Keys
-    // past the end read a clamped bias; their scores become -inf.
+    // j*64 + kb*32 + 8*(r/4) + 4*lhalf + r%4.  The MFMAs accumulate q.k onto
+    // 0, or in the biased modes (q / 8).k onto mask + pair, which is the
+    // biased score itself.  Keys past the end read a clamped bias; their
+    // scores become -inf.
     f32x16 st[2];
     if (active) {
       if constexpr ((kMode & kBias) != 0) {
@@ -246,7 +257,7 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
               }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) st[kb][4 * g + e] = 8.f * b[e];
+            for (int e = 0; e < 4; ++e) st[kb][4 * g + e] = b[e];
           }
         if constexpr (kStaged) {
           // The region is refilled with the next tile's biases once these
@@ -292,14 +303,14 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
       // Biased modes: while every key so far is -inf (masked), subtract 0, so
       // the probabilities stay 0 instead of exp(-inf - -inf) = NaN.
       const float m_sub = ((kMode & kBias) != 0 && m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast((m_i - m_sub) * kScaleLog2);
-      const float mc = m_sub * kScaleLog2;
+      const float alpha = exp2_fast((m_i - m_sub) * kS);
+      const float mc = m_sub * kS;
       float rs_ = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2_fast(fmaf(st[kb][r], kScaleLog2, -mc));
+          const float p = exp2_fast(fmaf(st[kb][r], kS, -mc));
           st[kb][r] = p;
           rs_ += p;
         }
