@@ -125,7 +125,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   constexpr int OES = OUT8 ? 1 : 2;               // output bytes per element
   constexpr int ECH = BM * BN * OES <= 2 * kStage ? WTM : 32;  // staged rows per wave per chunk
   static_assert(WTM % ECH == 0, "whole chunks");
-  constexpr int kSmem = 2 * kStage > NW * ECH * WTN * OES ? 2 * kStage : NW * ECH * WTN * OES;
+  // Residual epilogues stage the residual by direct loads one chunk ahead:
+  // two staging buffers when the tile is staged in chunks.
+  constexpr int kStageBufs = (EPI == EPI_BIAS_RESIDUAL && ECH < WTM) ? 2 : 1;
+  constexpr int kEpiBytes = kStageBufs * NW * ECH * WTN * OES;
+  static_assert(kEpiBytes <= 2 * kStage, "epilogue staging fits in the K-step stages");
+  constexpr int kSmem = 2 * kStage;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem];
 
   const int64_t M = a.M;
@@ -301,10 +306,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   }
 
   // ------------------------------------------------------------ epilogue
-  // Each wave stages its (WTM x WTN) result tile in LDS (free once every wave
-  // is past the K loop) -- all of it, or ECH-row chunks when the whole tile
-  // does not fit -- so that global memory is written (and, for the residual,
-  // read) in full rows with 16-byte lanes.  Staged rows hold CPR 16-byte
+  // Each wave stages its (WTM x WTN) result tile in its own LDS region (free
+  // once every wave is past the K loop) -- all of it, or ECH-row chunks when
+  // the whole tile does not fit -- so that global memory is written (and, for
+  // the residual, read) in full rows with 16-byte lanes.  The regions are
+  // wave-private, so after the barrier that ends the K loop the epilogue
+  // needs no further barrier.  The residual of a chunk arrives by direct
+  // loads into the staging buffer, issued one chunk ahead.  Staged rows hold CPR 16-byte
   // chunks, chunk c of row r stored at c ^ ((r / RPW) % CPR), which spreads
   // the row-per-lane accesses of the MFMA layout over the banks.  E4M3
   // operands: the accumulators are first divided by s_x s_w.  E4M3 output:
@@ -315,10 +323,34 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   constexpr int PASSES = ECH * CPR / 64;          // 16-byte transfers per lane per chunk
   constexpr int EPC = 16 / OES;                   // output elements per chunk
   __syncthreads();
-  unsigned char* stage = smem + wave * (ECH * WTN * OES);
+  auto stage_at = [&](int c0) {
+    return smem + ((c0 / ECH) % kStageBufs) * (NW * ECH * WTN * OES) + wave * (ECH * WTN * OES);
+  };
   auto soff = [&](int row, int chunk) { return row * (WTN * OES) + ((chunk ^ ((row / RPW) & (CPR - 1))) * 16); };
   const int64_t mw = m0 + wm * WTM;
   const int nw = n0 + wn * WTN;
+  // Residual rows c0 .. c0 + ECH - 1 of the wave tile into their staging
+  // buffer: one 1 KB direct load fills 1024 / (WTN * 2) rows, lane i writing
+  // physical chunk i % CPR of its row, i.e. the residual's logical chunk
+  // (i % CPR) ^ ((row / RPW) % CPR).  Rows past M are clamped (never stored).
+  auto res_load = [&](int c0) {
+    if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+      static_assert(OES == 2 && (ECH * WTN * 2) % 1024 == 0, "whole 1 KB loads of bf16 rows");
+      constexpr int RPL = 1024 / (WTN * 2);  // staged rows per direct load
+      if (nw >= N) return;
+      const uint32_t base = lds0 + (uint32_t)(((c0 / ECH) % kStageBufs) * (NW * ECH * WTN * OES) +
+                                              wave_u * (ECH * WTN * OES));
+#pragma unroll
+      for (int k = 0; k < ECH / RPL; ++k) {
+        const int row = k * RPL + lane / CPR;
+        int64_t m = mw + c0 + row;
+        m = m < M ? m : M - 1;
+        const int ch = (lane % CPR) ^ ((row / RPW) & (CPR - 1));
+        lds_dma16(a.res + m * N + nw + ch * 8, base + (uint32_t)(k * 1024));
+      }
+    }
+  };
+  res_load(0);
   const bf16_t* __restrict__ bias = a.bias;
   float dq = 1.0f;
   if constexpr (DT == kE4M3) dq = 1.0f / (a.x_scale[0] * a.w_scale[0]);
@@ -339,17 +371,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 
 #pragma unroll
   for (int c0 = 0; c0 < WTM; c0 += ECH) {
+  unsigned char* stage = stage_at(c0);
   if constexpr (EPI == EPI_BIAS_RESIDUAL) {
-#pragma unroll 4
-    for (int p = 0; p < PASSES; ++p) {
-      const int idx = p * 64 + lane, row = idx / CPR, ch = idx % CPR;
-      const int64_t m = mw + c0 + row;
-      const int n = nw + ch * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (m < M && n < N) v = *(const u32x4*)(a.res + m * N + n);
-      *(u32x4*)(stage + soff(row, ch)) = v;
-    }
-    __syncthreads();
+    // This chunk's residual has landed (and the previous chunk's stores,
+    // which read the other buffer, have been issued); fetch the next one.
+    vm_wait_all();
+    if (c0 + ECH < WTM) res_load(c0 + ECH);
   }
 
 #pragma unroll
@@ -438,7 +465,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       }
     }
   }
-  __syncthreads();
 
 #pragma unroll 4
   for (int p = 0; p < PASSES; ++p) {
@@ -458,7 +484,6 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       *(u32x4*)(a.y + m * N + n) = v;
     }
   }
-  if (c0 + ECH < WTM) __syncthreads();  // the next chunk reuses the staging region
   }
   if constexpr (OUT8) {
     __shared__ float red[NW];
