@@ -165,7 +165,8 @@ struct GemmArgs {
   const int32_t* pos;      // [M] position of each row, -1 = padding row (skipped)
   const float2* rope;      // [max_positions, 32] (cos, sin)
   int32_t max_positions;
-  // residual epilogue: rows whose pos < 0 are written as zero when zero_pad_rows
+  // set when the rows hold padding (pos < 0, a bshd batch): the residual
+  // epilogue writes such rows as zero and the rotary epilogue skips them
   int32_t zero_pad_rows;
   // EPI_BIAS_GELU_E4M3: y8 = cast(gelu(.) * y8_scale[0]), amax into *y8_amax
   uint8_t* y8;

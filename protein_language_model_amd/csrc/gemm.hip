@@ -369,6 +369,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       bcache[j][gq] = (bias && nw < N) ? *(const u32x2*)(bias + n) : u32x2{0u, 0u};
     }
 
+  // Rotary epilogue: the positions of this lane's rows (one per 32-row
+  // block), loaded together before the first block needs one.
+  [[maybe_unused]] int rpos[FM];
+  if constexpr (EPI == EPI_QKV_ROPE) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = mw + i * 32 + lrow;
+      rpos[i] = a.pos[m < M ? m : M - 1];
+    }
+  }
+
 #pragma unroll
   for (int c0 = 0; c0 < WTM; c0 += ECH) {
   unsigned char* stage = stage_at(c0);
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     const int64_t m = mw + i * 32 + lrow;
     const int64_t mc = m < M ? m : M - 1;
     if constexpr (EPI == EPI_QKV_ROPE) {
-      int p = a.pos[mc];
+      int p = rpos[i];
       p = p < 0 ? 0 : (p < a.max_positions ? p : a.max_positions - 1);
       // The wave's 64 columns are one head's q, k or v (c = 0, 1, 2): dims
       // d = 8 gq + 4 lhalf + e of this lane pair with d + 32.  Rotation
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     if (m >= M || n >= N) continue;
     const u32x4 v = *(const u32x4*)(stage + soff(row, ch));
     if constexpr (EPI == EPI_QKV_ROPE) {
-      if (a.pos[m] < 0) continue;  // padding row of a bshd batch: never attended
+      if (a.zero_pad_rows && a.pos[m] < 0) continue;  // padding row of a bshd batch: never attended
       const int heads = N / 192;
       const int head = n / 192, c = (n % 192) / 64, d = n % 64;
       *(u32x4*)(a.y + (((int64_t)c * heads + head) * M + m) * kHeadDim + d) = v;
