@@ -1,7 +1,7 @@
 """Coefficients of the GELU epilogue in gemm.hip (run once; prints C constants).
 
 GELU(z) = z Phi(z), Phi the standard normal CDF.  The kernel evaluates
-q = Phi(-a), a = min(|z|, 9), as 2^P(a) with P a degree-9 polynomial fitted to
+q = Phi(-a), a = min(|z|, 9), as 2^P(a) with P a degree-6 polynomial fitted to
 log2 Phi(-a) on [0, 9], and GELU(z) = z (1 - q) for z >= 0, z q for z < 0.
 The fit is a weighted least-squares Chebyshev fit, reweighted (Lawson) towards
 the minimax of |2^P - Phi| / max(Phi, 1e-3): absolute error where Phi is
@@ -11,7 +11,7 @@ printed bounds evaluate P in float32 by Horner's rule, as the kernel does.
 import numpy as np
 from scipy.special import log_ndtr, ndtr
 
-DEGREE, A, TAU = 9, 9.0, 1e-3
+DEGREE, A, TAU = 6, 9.0, 1e-3
 
 
 def fit(degree=DEGREE, a_max=A, tau=TAU, n=40001, iters=60):

@@ -39,7 +39,7 @@ def gelu_as_kernel(z):
 
 def test_tail_probability_bounds():
     co = kernel_coefficients()
-    assert len(co) == 10
+    assert len(co) == 7
     a = np.linspace(0.0, 9.0, 90001).astype(np.float32)
     p = np.full_like(a, co[-1])
     for ck in co[-2::-1]:
@@ -47,9 +47,9 @@ def test_tail_probability_bounds():
     q = np.exp2(p.astype(np.float64))
     phi = ndtr(-a.astype(np.float64))
     err = np.abs(q - phi)
-    assert err.max() <= 7e-8
-    assert (err / phi)[a < 4].max() <= 4e-6
-    assert (err / phi)[a < 5].max() <= 3e-4
+    assert err.max() <= 7e-7
+    assert (err / phi)[a < 4].max() <= 4e-5
+    assert (err / phi)[a < 5].max() <= 7e-4
     assert q[-1] < 2.0 ** -57   # at |z| = 9, where the kernel switches to q = 0 (Phi(-9) ~ 1.1e-19)
 
 
@@ -58,10 +58,13 @@ def test_gelu_against_exact():
     g = gelu_as_kernel(z).astype(np.float64)
     zz = f32(z).astype(np.float64)
     exact = zz * ndtr(zz)
-    # q's error (absolute 7e-8, relative 4e-6 below |z| = 4) plus two fp32 roundings
-    bound = 7e-8 * np.abs(zz) + 2.0 ** -23 * np.abs(exact)
+    # q's error (absolute 7e-7, relative 4e-5 below |z| = 4) plus two fp32 roundings
+    bound = 7e-7 * np.abs(zz) + 2.0 ** -23 * np.abs(exact)
     tail = np.abs(zz) < 4
-    assert np.all(np.abs(g - exact)[tail] <= np.maximum(bound, 4e-6 * np.abs(exact) + 2.0 ** -23 * np.abs(exact))[tail])
+    assert np.all(np.abs(g - exact)[tail] <= np.maximum(bound, 4e-5 * np.abs(exact) + 2.0 ** -23 * np.abs(exact))[tail])
+    # below half a bf16 ulp of the result wherever the result is a normal float
+    normal = np.abs(exact) > 1e-30
+    assert np.all((np.abs(g - exact) <= 2.0 ** -9 * np.abs(exact))[normal & (np.abs(zz) < 5)])
     assert np.all(np.abs(g - exact) <= bound + 1e-30)
     # the sign of the result is the sign of z (no cancellation to +0 in the
     # tail); from z = -9 down the result is -0
