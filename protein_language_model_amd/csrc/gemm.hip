@@ -436,7 +436,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       bool zero_row = false;
       if constexpr (EPI == EPI_BIAS_RESIDUAL) zero_row = a.zero_pad_rows && a.pos[mc] < 0;
       bool count_row = false;  // E4M3 output: row enters the amax (in range, not padding)
-      if constexpr (OUT8) count_row = m < M && (a.pos == nullptr || a.pos[mc] >= 0);
+      if constexpr (OUT8) count_row = m < M && (!a.zero_pad_rows || a.pos == nullptr || a.pos[mc] >= 0);
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
 #pragma unroll
