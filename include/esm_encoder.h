@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 7
+#define ESM_ABI_VERSION 8
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -292,6 +292,26 @@ esm_status esm_biased_attention_fwd(esm_encoder* enc, const void* q, const void*
                                     const void* mask_bias, const void* pair_bias, void* out,
                                     int32_t B, int32_t N, int32_t L, int32_t heads,
                                     esm_stream_t stream);
+
+/* MXFP4 quantisation (the FP4 recipe, [TE-ESM2] FP8与FP4混合精度支持, read as
+ * OCP MXFP4: E2M1 values in blocks of 32 along K, one E8M0 scale per block).
+ * Per block: e = floor(log2 max|v|) - 2, clamped to [-127, 127] (-127 for an
+ * all-zero block), scale byte e + 127, and each value v / 2^e rounded to the
+ * nearest E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6 with sign), ties to even,
+ * saturating at 6.
+ *   x      bf16 [M, K] row-major, K a positive multiple of 256, finite values
+ *          (subnormal inputs may be flushed to zero).
+ *   codes  uint8 [M, K / 2]: value 2j of a row in the low nibble of byte j,
+ *          value 2j + 1 in the high nibble (bit 3 of a nibble is the sign).
+ *   scales uint8 [K / 256][M2][8], M2 = M rounded up to even: the 8 bytes of
+ *          (K step s, row m) are the scales of blocks 8s + 0, 2, 4, 6, 1, 3, 5,
+ *          7 (the order the MXFP4 GEMM reads them in); the pad row of an odd
+ *          M holds 127.
+ * x and codes 16-byte aligned, scales 16-byte aligned.  Errors: ESM_ERR_NULL,
+ * ESM_ERR_SHAPE (M < 0, K not a positive multiple of 256),
+ * ESM_ERR_UNSUPPORTED (alignment).  M = 0 launches nothing. */
+esm_status esm_mxfp4_quantize(esm_encoder* enc, const void* x, int64_t M, int32_t K, void* codes,
+                              void* scales, esm_stream_t stream);
 
 typedef enum {
   ESM_EPI_BIAS = 0,          /* y = x W^T + b */

@@ -205,6 +205,13 @@ struct BiasedAttnArgs {
 
 hipError_t launch_biased_attention(const BiasedAttnArgs& a, hipStream_t st);
 
+// MXFP4 quantisation of x [M, K] (K % 256 == 0): codes [M, K / 2] (value 2j
+// in the low nibble of byte j), E8M0 scales [K / 256][M2][8] with M2 = M
+// rounded up to even, the 8 bytes of (K step s, row m) holding the scales of
+// blocks 8s + {0, 2, 4, 6, 1, 3, 5, 7}.
+hipError_t launch_mx_quantize(const bf16_t* x, int64_t M, int32_t K, uint8_t* codes, uint8_t* scales,
+                              hipStream_t st);
+
 // Delayed-scaling bookkeeping (fp8.hip).
 struct Fp8State {
   float* act_scale;    // [layers, 4] scale used by the current step (ln1, ctx, ln2, act)

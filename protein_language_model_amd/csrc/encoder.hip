@@ -801,6 +801,22 @@ esm_status esm_biased_attention_fwd(esm_encoder* e, const void* q, const void* k
   return timed(e, ESM_K_BIASED_ATTENTION, st, "biased attention", [&] { return launch_biased_attention(a, st); });
 }
 
+esm_status esm_mxfp4_quantize(esm_encoder* e, const void* x, int64_t M, int32_t K, void* codes, void* scales,
+                              esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "NULL encoder");
+  if (M < 0 || K <= 0 || K % 256) return fail(ESM_ERR_SHAPE, "M %lld K %d: K must be a positive multiple of 256",
+                                              (long long)M, K);
+  if (M == 0) return ok();
+  if (!x || !codes || !scales) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales))
+    return fail(ESM_ERR_UNSUPPORTED, "x/codes/scales not 16-byte aligned");
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  return timed(e, ESM_K_OTHER, (hipStream_t)stream, "mxfp4 quantize", [&] {
+    return launch_mx_quantize((const bf16_t*)x, M, K, (uint8_t*)codes, (uint8_t*)scales, (hipStream_t)stream);
+  });
+}
+
 esm_status esm_linear_fwd(esm_encoder* e, const void* x, const void* w, const void* b, const void* res, void* y,
                           int64_t M, int32_t N, int32_t K, int32_t epi, esm_stream_t stream) {
   g_last_error.clear();

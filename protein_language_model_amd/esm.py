@@ -84,6 +84,7 @@ SIGNATURES = {
     "esm_segment_table": (_i32, [_p, _i32, _p, _i32, _i64, _i32, _p, _sz, _p]),
     "esm_attention_fwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_biased_attention_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
+    "esm_mxfp4_quantize": (_i32, [_p, _p, _i64, _i32, _p, _p, _p]),
     "esm_linear_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
     "esm_layernorm_fwd": (_i32, [_p, _p, _p, _p, _p, _i64, _p]),
     "esm_layernorm_e4m3_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _p]),
@@ -372,6 +373,19 @@ class Encoder:
         _call("esm_biased_attention_fwd", self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(mask_bias), _ptr(pair_bias),
               _ptr(out), int(B), int(N), int(L), int(heads), _stream(stream))
         return out
+
+    def mxfp4_quantize(self, x, *, codes=None, scales=None, stream=None):
+        """x bf16 [M, K] -> (codes uint8 [M, K/2], scales uint8 [K/256, M2, 8]), the
+        MXFP4 layout of esm_mxfp4_quantize (M2 = M rounded up to even)."""
+        import torch
+        M, K = x.shape
+        M2 = M + (M & 1)
+        if codes is None:
+            codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        if scales is None:
+            scales = torch.empty((K // 256, M2, 8), dtype=torch.uint8, device=x.device)
+        _call("esm_mxfp4_quantize", self._h, _ptr(x), int(M), int(K), _ptr(codes), _ptr(scales), _stream(stream))
+        return codes, scales
 
     def linear_fwd(self, x, w, b=None, *, residual=None, epilogue: int = EPI_BIAS, y=None, stream=None):
         import torch
