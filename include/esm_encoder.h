@@ -339,6 +339,20 @@ esm_status esm_linear_e4m3_fwd(esm_encoder* enc, const void* x8, const float* x_
                                uint32_t* y_amax, int64_t M, int32_t N, int32_t K,
                                int32_t epilogue, esm_stream_t stream);
 
+/* MXFP4 GEMM (the FP4 recipe reading, [TE-ESM2] FP8与FP4混合精度支持):
+ *   y = epilogue(x_q . w_q^T + b),  x_q[m, k] = 2^(xs - 127) * E2M1(code)
+ * with the codes and block scales of esm_mxfp4_quantize for x [M, K] and
+ * w [N, K] (w's scale array has N rows: N is even).  Products of the
+ * dequantised values accumulate in fp32 on the scaled MFMA; y is bf16 [M, N].
+ * Epilogues ESM_EPI_BIAS, ESM_EPI_BIAS_GELU and ESM_EPI_BIAS_RESIDUAL (r may
+ * equal y).  N must be a multiple of 64 and K of 256; pointers 16-byte
+ * aligned, b 8-byte aligned.  Errors: ESM_ERR_NULL, ESM_ERR_SHAPE,
+ * ESM_ERR_UNSUPPORTED (epilogue, alignment). */
+esm_status esm_linear_mxfp4_fwd(esm_encoder* enc, const void* x_codes, const void* x_scales,
+                                const void* w_codes, const void* w_scales, const void* b,
+                                const void* residual, void* y, int64_t M, int32_t N, int32_t K,
+                                int32_t epilogue, esm_stream_t stream);
+
 /* Row LayerNorm y = (x - mean) / sqrt(var + eps) * gamma + beta over [M, H]. */
 esm_status esm_layernorm_fwd(esm_encoder* enc, const void* x, const void* gamma,
                              const void* beta, void* y, int64_t M, esm_stream_t stream);

@@ -38,6 +38,7 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 // Operand element types of the GEMM.
 constexpr int kBF16 = 0;
 constexpr int kE4M3 = 1;
+constexpr int kFP4 = 2;   // MXFP4: E2M1 codes, one E8M0 scale per 32 values along K
 constexpr float kE4M3Max = 448.0f;
 
 // Four values v * s cast to OCP E4M3 (1.4.3, bias 7, no infinity, 0x7F = NaN,
@@ -172,6 +173,10 @@ struct GemmArgs {
   uint8_t* y8;
   const float* y8_scale;
   uint32_t* y8_amax;
+  // kFP4 operands: E8M0 block scales in the esm_mxfp4_quantize layout
+  // [K / 256][rows rounded up to even][8]
+  const uint8_t* x_sc;
+  const uint8_t* w_sc;
 };
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st);

@@ -817,6 +817,31 @@ esm_status esm_mxfp4_quantize(esm_encoder* e, const void* x, int64_t M, int32_t 
   });
 }
 
+esm_status esm_linear_mxfp4_fwd(esm_encoder* e, const void* xc, const void* xs, const void* wc, const void* ws,
+                                const void* b, const void* res, void* y, int64_t M, int32_t N, int32_t K, int32_t epi,
+                                esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !xc || !xs || !wc || !ws || !y) return fail(ESM_ERR_NULL, "NULL argument");
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 256)
+    return fail(ESM_ERR_SHAPE, "M %lld N %d K %d: N must be a positive multiple of 64 and K of 256", (long long)M, N,
+                K);
+  if (epi < ESM_EPI_BIAS || epi > ESM_EPI_BIAS_RESIDUAL) return fail(ESM_ERR_UNSUPPORTED, "epilogue %d", epi);
+  if (epi == ESM_EPI_BIAS_RESIDUAL && !res) return fail(ESM_ERR_NULL, "residual is NULL");
+  if (!aligned16(xc) || !aligned16(xs) || !aligned16(wc) || !aligned16(ws) || !aligned16(y) ||
+      (res && !aligned16(res)) || (b && ((uintptr_t)b & 7u)))
+    return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer");
+  if (M == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  GemmArgs g{};
+  g.dtype = kFP4;
+  g.x = xc; g.w = wc; g.x_sc = (const uint8_t*)xs; g.w_sc = (const uint8_t*)ws;
+  g.bias = (const bf16_t*)b; g.res = (const bf16_t*)res;
+  g.y = (bf16_t*)y; g.M = M; g.N = N; g.K = K;
+  const int kind = epi == ESM_EPI_BIAS ? EPI_BIAS : (epi == ESM_EPI_BIAS_GELU ? EPI_BIAS_GELU : EPI_BIAS_RESIDUAL);
+  return timed(e, ESM_K_OTHER, (hipStream_t)stream, "mxfp4 linear",
+               [&] { return launch_gemm(kind, g, (hipStream_t)stream); });
+}
+
 esm_status esm_linear_fwd(esm_encoder* e, const void* x, const void* w, const void* b, const void* res, void* y,
                           int64_t M, int32_t N, int32_t K, int32_t epi, esm_stream_t stream) {
   g_last_error.clear();

@@ -91,14 +91,22 @@ struct Frag<kE4M3> {
   typedef i32x8 T;  // 32 E4M3 along K: one 64-wide sub-step
   static constexpr int kSub = 64;
 };
+template <>
+struct Frag<kFP4> {
+  typedef i32x8 T;  // 32 E2M1 along K (one MX block) in the low 4 registers: one 64-wide sub-step
+  static constexpr int kSub = 64;
+};
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI, int DT>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) {
   typedef typename Frag<DT>::T frag_t;
-  constexpr int ES = DT == kE4M3 ? 1 : 2;       // operand bytes per element
-  constexpr int kBK = kRowBytes / ES;           // K per step, in elements
+  // operand bytes per element = EBN / EBD: bf16 2, E4M3 1, FP4 1/2
+  constexpr int EBN = DT == kBF16 ? 2 : 1;
+  constexpr int EBD = DT == kFP4 ? 2 : 1;
+  constexpr int kBK = kRowBytes * EBD / EBN;    // K per step, in elements
   constexpr int KK = kBK / Frag<DT>::kSub;      // k sub-steps per K step
-  constexpr int FB = Frag<DT>::kSub * ES / 32;  // 16-byte chunks per lane per fragment
+  constexpr int FB = Frag<DT>::kSub * EBN / (32 * EBD);  // 16-byte chunks per lane per fragment
+  constexpr bool MX = DT == kFP4;               // block scales: 8 bytes per tile row per K step
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WTM = BM / WAVES_M;
   constexpr int WTN = BN / WAVES_N;
@@ -110,7 +118,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   constexpr int kStage = (BM + BN) * kRowBytes;  // bytes per K-step stage
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(XRB * RPI * NW == BM && WRB * RPI * NW == BN, "tile rows must split evenly over the waves");
-  static_assert(DT == kE4M3 || KK % 2 == 0, "fragment double buffering alternates over an even number of sub-steps");
+  static_assert(DT != kBF16 || KK % 2 == 0, "fragment double buffering alternates over an even number of sub-steps");
   static_assert(EPI != EPI_QKV_ROPE || (FN % 2 == 0 && WTN % 64 == 0), "rotary pairs need 64-wide wave columns");
   static_assert(EPI != EPI_BIAS_GELU_E4M3 || DT == kE4M3, "E4M3 output is built for E4M3 operands");
 
@@ -126,7 +134,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   constexpr int kStageBufs = (EPI == EPI_BIAS_RESIDUAL && ECH < WTM) ? 2 : 1;
   constexpr int kEpiBytes = kStageBufs * NW * ECH * WTN * OES;
   static_assert(kEpiBytes <= 2 * kStage, "epilogue staging fits in the K-step stages");
-  constexpr int kSmem = 2 * kStage;
+  // MXFP4: both stages' block scales (8 bytes per tile row) after the stages.
+  constexpr int kScStage = MX ? (BM + BN) * 8 : 0;
+  static_assert(!MX || (BM % 128 == 0 && BN % 128 == 0), "scale rows load in 1 KB pieces of 128 rows");
+  constexpr int kSmem = 2 * kStage + 2 * kScStage;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem];
 
   const int64_t M = a.M;
@@ -168,16 +179,37 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   for (int i = 0; i < XRB; ++i) {
     int64_t r = m0 + (int64_t)(wave + NW * i) * RPI + lr8;
     r = r < M ? r : M - 1;
-    xsrc[i] = (const unsigned char*)a.x + r * K * ES + lchunk;
+    xsrc[i] = (const unsigned char*)a.x + r * K * EBN / EBD + lchunk;
   }
 #pragma unroll
   for (int i = 0; i < WRB; ++i) {
     int r = n0 + (wave + NW * i) * RPI + lr8;
     r = r < N ? r : N - 1;
-    wsrc[i] = (const unsigned char*)a.w + (int64_t)r * K * ES + lchunk;
+    wsrc[i] = (const unsigned char*)a.w + (int64_t)r * K * EBN / EBD + lchunk;
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
+  // MXFP4 scales of K step s: the tile's x rows then w rows, 8 bytes each, in
+  // 1 KB direct loads of 128 rows (lane i: rows 2i, 2i + 1), one per wave.
+  // Rows past the scale arrays' (even) row counts are clamped to the last
+  // pair; those rows' outputs are never stored.
+  [[maybe_unused]] const int64_t M2 = M + (M & 1);
+  auto issue_scales = [&](int s, int buf) {
+    if constexpr (MX) {
+      constexpr int PX = BM / 128, PW = BN / 128;
+      static_assert(PX + PW <= NW, "one scale piece per wave");
+      if (wave_u < PX + PW) {
+        const bool isx = wave_u < PX;
+        const int piece = isx ? wave_u : wave_u - PX;
+        int64_t r = (isx ? m0 : (int64_t)n0) + piece * 128 + 2 * lane;
+        const int64_t rows2 = isx ? M2 : (int64_t)N;
+        r = r < rows2 ? r : rows2 - 2;
+        const uint8_t* src = (isx ? a.x_sc + (int64_t)s * M2 * 8 : a.w_sc + (int64_t)s * N * 8) + r * 8;
+        const uint32_t dst = lds0 + (uint32_t)(2 * kStage + buf * kScStage + (isx ? 0 : BM * 8) + piece * 1024);
+        lds_dma16(src, dst);
+      }
+    }
+  };
   auto issue_tile = [&](int kbyte, int buf) {
     const uint32_t base = lds0 + (uint32_t)(buf * kStage);
 #pragma unroll
@@ -185,6 +217,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 #pragma unroll
     for (int i = 0; i < WRB; ++i)
       lds_dma16(wsrc[i] + kbyte, base + (uint32_t)((BM + (wave_u + NW * i) * RPI) * kRowBytes));
+    issue_scales(kbyte / kRowBytes, buf);
   };
 
   // Fragment reads: row r of the tile, logical 16-byte chunk ch, stored at
@@ -195,7 +228,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   // matching k.
   const int swz = (lrow >> 1) & 7;
   auto read_frag = [&](const unsigned char* rowp, int kk) -> frag_t {
-    if constexpr (FB == 1) {
+    if constexpr (DT == kFP4) {
+      // one MX block (32 E2M1 values, 16 bytes); the MFMA reads 4 registers
+      const u32x4 v = *(const u32x4*)(rowp + (((kk * 2 + lhalf) ^ swz) * 16));
+      return __builtin_bit_cast(frag_t, __builtin_shufflevector(v, u32x4{0u, 0u, 0u, 0u}, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else if constexpr (FB == 1) {
       return *(const frag_t*)(rowp + (((kk * 2 + lhalf) ^ swz) * 16));
     } else {
       const u32x4 lo = *(const u32x4*)(rowp + (((kk * 4 + lhalf * 2) ^ swz) * 16));
@@ -220,6 +257,31 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // MXFP4 block scales of this lane's fragment rows for one K step: word
+  // lhalf of a row's 8 bytes holds the scales of blocks lhalf, 2 + lhalf,
+  // 4 + lhalf, 6 + lhalf, i.e. byte kk is the scale of sub-step kk's block.
+  [[maybe_unused]] uint32_t xsc[MX ? FM : 1], wsc[MX ? FN : 1];
+  auto load_scales = [&](int buf) {
+    if constexpr (MX) {
+      const unsigned char* sb = smem + 2 * kStage + buf * kScStage;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) xsc[i] = *(const uint32_t*)(sb + (wm * WTM + i * 32 + lrow) * 8 + 4 * lhalf);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) wsc[j] = *(const uint32_t*)(sb + (BM + wn * WTN + j * 32 + lrow) * 8 + 4 * lhalf);
+    }
+  };
+  auto mfma_step_mx = [&](const frag_t (&xf)[FM], const frag_t (&wf)[FN], int kk) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          // cbsz = blgp = 4: both operands E2M1; scale bytes shifted to byte 0
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 4, 4, 0,
+                                                                       (int)(wsc[j] >> (8 * kk)), 0,
+                                                                       (int)(xsc[i] >> (8 * kk)));
+    }
+  };
   auto mfma_step = [&](const frag_t (&xf)[FM], const frag_t (&wf)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -228,7 +290,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
         if constexpr (DT == kE4M3)
           // cbsz = blgp = 0: both operands E4M3; block scales 127 = 2^0.
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 0, 0, 0, 127, 0, 127);
-        else
+        else if constexpr (DT == kBF16)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
       }
   };
@@ -237,7 +299,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   issue_tile(0, 0);
   vm_wait_all();
   __syncthreads();
-  if constexpr (DT == kE4M3) {
+  if constexpr (DT == kFP4) {
+    // One fragment set, as for E4M3, plus the K step's block scales.
+    frag_t xf[FM], wf[FN];
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) issue_tile((kt + 1) * kRowBytes, cur ^ 1);
+      load_scales(cur);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_frags(xf, wf, cur, kk);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_step_mx(xf, wf, kk);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      vm_wait_all();
+      __syncthreads();
+    }
+  } else if constexpr (DT == kE4M3) {
     // One fragment set (8 registers per 32-byte fragment; a second set would
     // not fit beside the 128 accumulators at two waves per SIMD): the other
     // wave on the SIMD multiplies while this one waits for its LDS reads.
@@ -537,6 +617,11 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   const bool tall = r320 * 320 <= r256 * 256;
   if (a.dtype == kE4M3)
     return tall ? run<320, 256, 2, 4, EPI, kE4M3>(a, st) : run<256, 256, 2, 4, EPI, kE4M3>(a, st);
+  if constexpr (EPI == EPI_BIAS_GELU_E4M3 || EPI == EPI_QKV_ROPE) {
+    if (a.dtype == kFP4) return hipErrorInvalidValue;
+  } else {
+    if (a.dtype == kFP4) return run<256, 256, 2, 4, EPI, kFP4>(a, st);
+  }
   if constexpr (EPI == EPI_BIAS_GELU_E4M3) return hipErrorInvalidValue;
   else return tall ? run<320, 256, 2, 4, EPI, kBF16>(a, st) : run<256, 256, 2, 4, EPI, kBF16>(a, st);
 }
@@ -545,7 +630,7 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
-  const int kb = a.dtype == kE4M3 ? kRowBytes : kRowBytes / 2;
+  const int kb = a.dtype == kFP4 ? 2 * kRowBytes : (a.dtype == kE4M3 ? kRowBytes : kRowBytes / 2);
   if (a.K % kb != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_BIAS: return dispatch<EPI_BIAS>(a, st);

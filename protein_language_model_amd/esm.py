@@ -85,6 +85,7 @@ SIGNATURES = {
     "esm_attention_fwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_biased_attention_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "esm_mxfp4_quantize": (_i32, [_p, _p, _i64, _i32, _p, _p, _p]),
+    "esm_linear_mxfp4_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
     "esm_linear_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
     "esm_layernorm_fwd": (_i32, [_p, _p, _p, _p, _p, _i64, _p]),
     "esm_layernorm_e4m3_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _p]),
@@ -386,6 +387,19 @@ class Encoder:
             scales = torch.empty((K // 256, M2, 8), dtype=torch.uint8, device=x.device)
         _call("esm_mxfp4_quantize", self._h, _ptr(x), int(M), int(K), _ptr(codes), _ptr(scales), _stream(stream))
         return codes, scales
+
+    def linear_mxfp4_fwd(self, xq, wq, b=None, *, residual=None, epilogue: int = EPI_BIAS, y=None, stream=None):
+        """MXFP4 GEMM: xq = (codes [M, K/2], scales) and wq likewise, as returned
+        by mxfp4_quantize; y bf16 [M, N]."""
+        import torch
+        (xc, xs), (wc, ws) = xq, wq
+        M, K = xc.shape[0], 2 * xc.shape[1]
+        N = wc.shape[0]
+        if y is None:
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=xc.device)
+        _call("esm_linear_mxfp4_fwd", self._h, _ptr(xc), _ptr(xs), _ptr(wc), _ptr(ws), _ptr(b), _ptr(residual),
+              _ptr(y), int(M), int(N), int(K), int(epilogue), _stream(stream))
+        return y
 
     def linear_fwd(self, x, w, b=None, *, residual=None, epilogue: int = EPI_BIAS, y=None, stream=None):
         import torch

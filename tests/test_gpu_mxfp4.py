@@ -57,3 +57,29 @@ def test_mxfp4_quantize_bit_exact(enc, gu, M, K):
     want_codes, want_scales = pack_reference(ref_codes, ref_exps)
     assert np.array_equal(codes.cpu().numpy(), want_codes)
     assert np.array_equal(scales.cpu().numpy(), want_scales)
+
+
+@pytest.mark.parametrize("M,N,K,epi", [(1, 64, 256, esm.EPI_BIAS), (300, 320, 1280, esm.EPI_BIAS_GELU),
+                                       (1000, 1280, 512, esm.EPI_BIAS_RESIDUAL), (2049, 512, 1280, esm.EPI_BIAS)])
+def test_mxfp4_linear_matches_oracle(enc, gu, M, N, K, epi):
+    """MXFP4 GEMM on the library's own quantisation of x and w against the
+    oracle's quantisation and exact product: the dequantised products are
+    exact, the sums run in fp32 and y is rounded to bf16."""
+    from oracle import esm_oracle as O
+    rng = np.random.default_rng(M + N + K)
+    xb = D.to_bf16_bits((rng.standard_normal((M, K)) * np.exp2(rng.integers(-4, 4, (M, 1)))).astype(np.float32))
+    wb = D.to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    bb = D.to_bf16_bits((rng.standard_normal(N) * 0.02).astype(np.float32))
+    rb = D.to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    xq = enc.mxfp4_quantize(gu.to_dev_bf16(xb))
+    wq = enc.mxfp4_quantize(gu.to_dev_bf16(wb))
+    res = gu.to_dev_bf16(rb) if epi == esm.EPI_BIAS_RESIDUAL else None
+    got = gu.from_dev(enc.linear_mxfp4_fwd(xq, wq, gu.to_dev_bf16(bb), residual=res, epilogue=epi))
+    ref = F.mx_matmul(*F.mx_quantize(D.bf16_bits_to_f64(xb)), *F.mx_quantize(D.bf16_bits_to_f64(wb)))
+    ref = ref + D.bf16_bits_to_f64(bb)
+    if epi == esm.EPI_BIAS_GELU:
+        ref = O.gelu(ref)
+    if epi == esm.EPI_BIAS_RESIDUAL:
+        ref = ref + D.bf16_bits_to_f64(rb)
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max()
+    assert np.all(np.abs(got - ref) <= bound), np.abs(got - ref).max()
