@@ -12,7 +12,9 @@ least 10 warm-up steps, and reported under "fp8"; what follows the stack
 (final LayerNorm, masked-LM logits, per-sequence means) is timed on its own
 under "head".  The biased attention kernel (the DeepSpeed4Science page's
 Evoformer attention with a mask bias and a pair bias) is timed on its own
-synthetic MSA-row shape under "biased_attention".  Prints one JSON line.
+synthetic MSA-row shape under "biased_attention", and the MXFP4 quantiser
+and GEMM (the FP4 recipe) on the layer's four GEMM shapes under "mxfp4".
+Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
                     [--padded] [--no-fp8]
@@ -34,6 +36,7 @@ PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (vendor figure)
 PEAK_FP8_TFLOPS = 5033.2     # MI355X dense fp8 MFMA (vendor figure)
 FP8_MIN_WARMUP = 10          # delayed scales settle over the warm-up steps
 PEAK_HBM_GBS = 8000.0
+PEAK_FP4_TFLOPS = 10066.3    # MI355X dense fp4 MFMA (vendor figure)
 
 
 def layer_flops(H: int, F: int, T: int, sum_L2: int) -> dict:
@@ -60,6 +63,7 @@ def parse():
     ap.add_argument("--no-head", action="store_true", help="skip timing the final LayerNorm / LM head / means")
     ap.add_argument("--no-biased-attention", action="store_true",
                     help="skip timing the biased (Evoformer MSA-row) attention kernel")
+    ap.add_argument("--no-mxfp4", action="store_true", help="skip timing the MXFP4 GEMMs on the layer shapes")
     ap.add_argument("--no-vendor-gemm", action="store_true", help="skip the hipBLASLt fc1-shape reference timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference dispatch for HBM byte counters)")
@@ -223,6 +227,52 @@ def bench_biased_attention(enc, steps: int, dev: str, stream) -> dict:
                        "sample": f"one of the {w.B * w.N} rows n (fp64 numpy), {dt_row:.2f} s, scaled to the call"}}
 
 
+def bench_mxfp4(enc, T: int, H: int, F: int, steps: int, dev: str, stream) -> dict:
+    """The MXFP4 (FP4 recipe) quantiser and GEMM alone on the four linears'
+    shapes of one layer of this batch: bf16 activations and weights N(0, 1) /
+    N(0, 0.02), quantised by the library, GEMM with a bias epilogue; HIP
+    events on the library stream.  GEMMs against the dense fp4 MFMA peak,
+    the quantiser against HBM (bf16 read, codes and scales written)."""
+    import torch
+    out = {}
+    g = torch.Generator(device=dev).manual_seed(11)
+
+    def timeit(fn, n):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n = max(10, steps)
+    for name, N, K in (("qkv", 3 * H, H), ("out", H, H), ("fc1", F, H), ("fc2", H, F)):
+        x = torch.randn((T, K), device=dev, generator=g).to(torch.bfloat16)
+        w = (torch.randn((N, K), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        b = (torch.randn((N,), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        xq = enc.mxfp4_quantize(x, stream=stream)
+        wq = enc.mxfp4_quantize(w, stream=stream)
+        ms_q = timeit(lambda: enc.mxfp4_quantize(x, codes=xq[0], scales=xq[1], stream=stream), n)
+        ms_g = timeit(lambda: enc.linear_mxfp4_fwd(xq, wq, b, y=y, stream=stream), n)
+        fl = 2.0 * T * N * K
+        qbytes = T * K * 2 + T * K // 2 + T * K // 32
+        tf = fl / (ms_g * 1e-3) / 1e12
+        out[name] = {"gemm_us": round(ms_g * 1e3, 1), "tflops": round(tf, 1),
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP4_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_FP4_TFLOPS, 4), "traffic": None,
+                                  "flops_per_launch": fl},
+                     "quantize_us": round(ms_q * 1e3, 1),
+                     "quantize_gbs": round(qbytes / (ms_q * 1e-3) / 1e9, 1)}
+        del x, w, b, y, xq, wq
+    out["shape"] = f"T = {T} rows; x bf16 [T, K] and W bf16 [N, K] quantised to MXFP4 (E2M1, E8M0 per 32)"
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -377,6 +427,10 @@ def main():
     if not args.no_biased_attention:
         biased = bench_biased_attention(enc, args.steps, dev, stream)
 
+    mxfp4 = None
+    if not args.no_mxfp4:
+        mxfp4 = bench_mxfp4(enc, T, m.hidden, m.ffn, args.steps, dev, stream)
+
     padded = None
     if args.padded:
         S = 1024
@@ -453,6 +507,7 @@ def main():
         "padded": padded,
         "head": head,
         "biased_attention": biased,
+        "mxfp4": mxfp4,
         "vendor_gemm_fc1": vendor,
         "fp8": fp8,
     }
