@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 8
+#define ESM_ABI_VERSION 9
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -71,7 +71,7 @@ typedef enum {
   ESM_ERR_STATE = 8        /* call not valid in the handle's current state */
 } esm_status;
 
-typedef enum { ESM_PRECISION_BF16 = 0, ESM_PRECISION_FP8_DELAYED = 1 } esm_precision;
+typedef enum { ESM_PRECISION_BF16 = 0, ESM_PRECISION_FP8_DELAYED = 1, ESM_PRECISION_MXFP4 = 2 } esm_precision;
 typedef enum { ESM_LAYOUT_THD = 0, ESM_LAYOUT_BSHD = 1 } esm_layout;
 
 /* Model configuration.  Key names follow the config.json keys of [TE-ESM2]. */
@@ -181,7 +181,16 @@ esm_status esm_workspace_region(const esm_encoder* enc, int64_t max_tokens, int3
  * the bf16 weight pointers in w must still be valid, LN parameters and biases
  * are read from w.  The call is one delayed-scaling step for that layer: it
  * uses the scales fixed by earlier steps, records this step's amax of the four
- * activations and, at its end, rolls the history and sets the next scales. */
+ * activations and, at its end, rolls the history and sets the next scales.
+ *
+ * MXFP4 precision (ESM_PRECISION_MXFP4; the FP4 recipe of [TE-ESM2]
+ * FP8与FP4混合精度支持, read as OCP MXFP4, see esm_mxfp4_quantize): each linear
+ * computes x_q . W_q^T + b with x the bf16 GEMM input quantised per 32-value
+ * block on every call (no state) and W_q from esm_mxfp4_prepare_layer
+ * (ESM_ERR_STATE if never called for layer_idx); LayerNorm, attention, the
+ * residuals and every GEMM output stay in bf16/fp32.  Needs hidden_size and
+ * intermediate_size multiples of 256 and intermediate_size <= 8 hidden_size
+ * (checked at create). */
 esm_status esm_layer_fwd(esm_encoder* enc, const esm_layer_weights* w, int32_t layer_idx,
                          const void* x_in, void* x_out,
                          const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -407,14 +416,23 @@ esm_status esm_fp8_set_state(esm_encoder* enc, const esm_fp8_state* state, esm_s
  * prepared weights and per-layer precisions are kept. */
 esm_status esm_fp8_reset(esm_encoder* enc, esm_stream_t stream);
 
-/* Per-layer precision of an FP8 encoder ([TE-ESM2] FP8与FP4混合精度支持: a
- * per-layer precision setting): precision[l] (host, num_layers entries) is
- * ESM_PRECISION_FP8_DELAYED (every layer's default) or ESM_PRECISION_BF16.  A
- * bf16 layer runs the bf16 kernels, needs no prepared FP8 weights, records no
- * amax, and its FP8 state (scales, history, step count) stays as it is until
- * the layer runs FP8 again.  Waits for stream.  ESM_ERR_STATE for an encoder
- * created with bf16 precision; ESM_ERR_SHAPE when num_layers is not the
- * config's; ESM_ERR_UNSUPPORTED for another precision code. */
+/* MXFP4 weights of layer layer_idx ([TE-ESM2] FP8与FP4混合精度支持, read as
+ * OCP MXFP4): the four linear weights of w quantised per 32-value block along
+ * K (esm_mxfp4_quantize) into library-owned memory, asynchronously on stream.
+ * ESM_ERR_STATE unless the encoder was created with ESM_PRECISION_MXFP4;
+ * ESM_ERR_SHAPE for layer_idx outside [0, num_hidden_layers). */
+esm_status esm_mxfp4_prepare_layer(esm_encoder* enc, int32_t layer_idx, const esm_layer_weights* w,
+                                   esm_stream_t stream);
+
+/* Per-layer precision of an FP8 or MXFP4 encoder ([TE-ESM2] FP8与FP4混合精度支持:
+ * a per-layer precision setting): precision[l] (host, num_layers entries) is
+ * the encoder's own precision (every layer's default) or ESM_PRECISION_BF16.
+ * A bf16 layer runs the bf16 kernels and needs no prepared weights; in an FP8
+ * encoder it records no amax, and its FP8 state (scales, history, step count)
+ * stays as it is until the layer runs FP8 again.  Waits for stream.
+ * ESM_ERR_STATE for an encoder created with bf16 precision; ESM_ERR_SHAPE when
+ * num_layers is not the config's; ESM_ERR_UNSUPPORTED for another precision
+ * code. */
 esm_status esm_set_layer_precision(esm_encoder* enc, const int32_t* precision, int32_t num_layers,
                                    esm_stream_t stream);
 

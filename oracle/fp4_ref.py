@@ -81,19 +81,53 @@ def block_exponent(block) -> int:
 
 def mx_quantize(x):
     """x [rows, K] (K a multiple of 32) -> (codes uint8 [rows, K], exponents
-    int32 [rows, K // 32])."""
+    int32 [rows, K // 32]).  Every block at once: frexp writes max|v| as
+    m 2^E with m in [0.5, 1), so floor(log2 max|v|) = E - 1 exactly (the same
+    rule as block_exponent, checked against it in the tests)."""
     x = np.asarray(x, np.float64)
     rows, K = x.shape
     assert K % BLOCK == 0
     xb = x.reshape(rows, K // BLOCK, BLOCK)
-    exps = np.empty((rows, K // BLOCK), np.int32)
-    codes = np.empty((rows, K // BLOCK, BLOCK), np.uint8)
-    for r in range(rows):
-        for b in range(K // BLOCK):
-            e = block_exponent(xb[r, b])
-            exps[r, b] = e
-            codes[r, b] = e2m1_encode(xb[r, b] / 2.0 ** e)
+    amax = np.max(np.abs(xb), axis=-1)
+    _, E = np.frexp(amax)
+    exps = np.where(amax == 0.0, -127, np.clip(E - 1 - E2M1_EMAX, -127, 127)).astype(np.int32)
+    codes = e2m1_encode(xb / np.exp2(exps.astype(np.float64))[..., None])
     return codes.reshape(rows, K), exps
+
+
+def bf16_round(x) -> np.ndarray:
+    """float64 -> nearest bfloat16 value (through float32, ties to even), the
+    rounding of a bf16 tensor written by a float32 computation."""
+    f = np.ascontiguousarray(np.asarray(x, np.float64).astype(np.float32))
+    b = f.view(np.uint32).astype(np.uint64)
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(f), np.nan, out)
+
+
+def layer_forward_mxfp4(x, cu_seqlens, w, heads: int):
+    """One pre-LN layer with MXFP4 GEMMs: each linear is
+    mx(bf16(a)) . mx(W)^T + b, the GEMM input a rounded to bf16 as the layer
+    stores it and quantised per 32-value block along K, W (bf16 values)
+    likewise; everything else as in the plain fp64 layer."""
+    from . import esm_oracle as O
+    x = np.asarray(x, np.float64)
+    T, H = x.shape
+    F = w["w_fc1"].shape[0]
+
+    def lin(a, wname, bname, n_out):
+        y = mx_matmul(*mx_quantize(bf16_round(a)), *mx_quantize(w[wname]))
+        b = w.get(bname)
+        return y + (np.zeros(n_out) if b is None else b)
+
+    h1 = O.layer_norm(x, w["ln1_gamma"], w["ln1_beta"])
+    q, k, v = O.split_qkv(lin(h1, "w_qkv", "b_qkv", 3 * H), heads)
+    pos = O.positions(cu_seqlens)
+    ctx = O.attention(O.apply_rope(q, pos), O.apply_rope(k, pos), v, cu_seqlens)
+    x1 = x + lin(ctx, "w_out", "b_out", H)
+    h2 = O.layer_norm(x1, w["ln2_gamma"], w["ln2_beta"])
+    a = O.gelu(lin(h2, "w_fc1", "b_fc1", F))
+    return x1 + lin(a, "w_fc2", "b_fc2", H)
 
 
 def mx_dequantize(codes, exps) -> np.ndarray:

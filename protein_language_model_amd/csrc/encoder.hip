@@ -32,7 +32,11 @@ struct esm_encoder {
   uint8_t* w8 = nullptr;           // per layer: E4M3 w_qkv | w_out | w_fc1 | w_fc2
   size_t w8_layer = 0;             // bytes per layer
   std::vector<char> prepared;      // layer weights cast since create
-  std::vector<int32_t> layer_prec; // FP8 encoder: per-layer precision (FP8 by default, or bf16)
+  std::vector<int32_t> layer_prec; // FP8 / MXFP4 encoder: per-layer precision (the encoder's by default, or bf16)
+  // MXFP4 (precision ESM_PRECISION_MXFP4 only): per layer the codes and
+  // block scales of w_qkv | w_out | w_fc1 | w_fc2
+  uint8_t* w4 = nullptr;
+  size_t w4_layer = 0;
   // LM head: the tied decoder weight and its bias padded to vocab_pad rows
   // (a multiple of 64 GEMM columns), refilled from the caller's on each call
   bf16_t* head_w = nullptr;        // [vocab_pad, H] then [vocab_pad]
@@ -88,8 +92,15 @@ esm_status check_config(const esm_config* c) {
   if (!(c->layer_norm_eps > 0.f) || !isfinite(c->layer_norm_eps))
     return fail(ESM_ERR_SHAPE, "layer_norm_eps must be positive and finite");
   if (!(c->rope_base > 1.f) || !isfinite(c->rope_base)) return fail(ESM_ERR_SHAPE, "rope_base must be > 1");
-  if (c->precision != ESM_PRECISION_BF16 && c->precision != ESM_PRECISION_FP8_DELAYED)
+  if (c->precision != ESM_PRECISION_BF16 && c->precision != ESM_PRECISION_FP8_DELAYED &&
+      c->precision != ESM_PRECISION_MXFP4)
     return fail(ESM_ERR_UNSUPPORTED, "unknown precision %d", c->precision);
+  if (c->precision == ESM_PRECISION_MXFP4 &&
+      (c->hidden_size % 256 != 0 || c->intermediate_size % 256 != 0 || c->intermediate_size > 8 * c->hidden_size))
+    return fail(ESM_ERR_UNSUPPORTED,
+                "MXFP4 needs hidden_size (%d) and intermediate_size (%d) to be multiples of 256 (one K step) and "
+                "intermediate_size <= 8 * hidden_size (its codes are staged in the QKV region)",
+                c->hidden_size, c->intermediate_size);
   if (c->precision == ESM_PRECISION_FP8_DELAYED && (c->hidden_size % 128 != 0 || c->intermediate_size % 128 != 0))
     return fail(ESM_ERR_UNSUPPORTED,
                 "FP8 needs hidden_size (%d) and intermediate_size (%d) to be multiples of 128 (E4M3 K step)",
@@ -213,6 +224,41 @@ bool layer_fp8(const esm_encoder* e, int32_t l) {
   return is_fp8(e) && l >= 0 && (size_t)l < e->layer_prec.size() && e->layer_prec[(size_t)l] == ESM_PRECISION_FP8_DELAYED;
 }
 
+bool is_mx(const esm_encoder* e) { return e->cfg.precision == ESM_PRECISION_MXFP4; }
+// Layer l of an MXFP4 encoder runs MXFP4 unless esm_set_layer_precision chose bf16 for it.
+bool layer_mx(const esm_encoder* e, int32_t l) {
+  return is_mx(e) && l >= 0 && (size_t)l < e->layer_prec.size() && e->layer_prec[(size_t)l] == ESM_PRECISION_MXFP4;
+}
+
+// MXFP4 operand: codes [rows, K / 2] then, 256-byte aligned, the block scales
+// [K / 256][rows rounded up to even][8] (the esm_mxfp4_quantize layout).
+struct MxOff {
+  size_t codes, scales, total;
+};
+MxOff mx_operand(size_t rows, size_t K) {
+  MxOff o;
+  o.codes = 0;
+  o.scales = align256(rows * K / 2);
+  o.total = o.scales + (K / 256) * (rows + (rows & 1)) * 8;
+  return o;
+}
+// The four MXFP4 weights of one layer: offsets of w_qkv, w_out, w_fc1, w_fc2.
+struct W4Off {
+  size_t at[4], total;
+};
+W4Off w4_offsets(const esm_config& c) {
+  const size_t H = (size_t)c.hidden_size, F = (size_t)c.intermediate_size;
+  const size_t n[4] = {3 * H, H, F, H}, k[4] = {H, H, H, F};
+  W4Off o;
+  size_t at = 0;
+  for (int i = 0; i < 4; ++i) {
+    o.at[i] = at;
+    at += align256(mx_operand(n[i], k[i]).total);
+  }
+  o.total = at;
+  return o;
+}
+
 // Byte offsets of the four E4M3 weights inside one layer's block.
 struct W8Off {
   size_t qkv, out, fc1, fc2, total;
@@ -296,7 +342,8 @@ esm_status check_fp8_layer(const esm_encoder* e, int32_t l) {
   if (l < 0 || l >= e->cfg.num_hidden_layers)
     return fail(ESM_ERR_SHAPE, "layer_idx %d outside [0, num_hidden_layers = %d)", l, e->cfg.num_hidden_layers);
   if (!e->prepared[(size_t)l])
-    return fail(ESM_ERR_STATE, "FP8 weights of layer %d not prepared (esm_fp8_prepare_layer)", l);
+    return fail(ESM_ERR_STATE, "%s weights of layer %d not prepared (%s)", is_mx(e) ? "MXFP4" : "FP8", l,
+                is_mx(e) ? "esm_mxfp4_prepare_layer" : "esm_fp8_prepare_layer");
   return ok();
 }
 
@@ -313,6 +360,91 @@ esm_status run_segments(esm_encoder* e, int layout, const int32_t* lens, int32_t
   return timed(e, ESM_K_SEGMENT, st, "segment table", [&] {
     return launch_segment_table(layout, lens, B, rows, S, e->cfg.max_position_embeddings, so, st);
   });
+}
+
+// One pre-LN layer with MXFP4 GEMMs (the FP4 recipe): LayerNorm, attention
+// and every GEMM output as in the bf16 layer; each GEMM input is quantised to
+// MXFP4 right after its producer into a workspace region that is free at that
+// point (LN1 output -> ctx region, context -> LN1 region, LN2 output -> ctx
+// region, GELU output -> QKV region), and the GEMMs read layer li's prepared
+// MXFP4 weights.  Quantisation is per 32-value block of a row, so rows stay
+// independent (packed == each sequence alone, padding rows never mix in).
+esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, const bf16_t* x_in, bf16_t* x_out,
+                        int64_t rows, int32_t B, bool zero_pad_rows, void* ws, const Plan& p, hipStream_t st) {
+  const esm_config& c = e->cfg;
+  const int H = c.hidden_size, F = c.intermediate_size, heads = c.num_attention_heads;
+  bf16_t* ln1 = region<bf16_t>(ws, p, ESM_WS_LN1);
+  bf16_t* qkv = region<bf16_t>(ws, p, ESM_WS_QKV);
+  bf16_t* ctx = region<bf16_t>(ws, p, ESM_WS_CTX);
+  bf16_t* x1 = region<bf16_t>(ws, p, ESM_WS_X1);
+  bf16_t* ln2 = region<bf16_t>(ws, p, ESM_WS_LN2);
+  bf16_t* act = region<bf16_t>(ws, p, ESM_WS_ACT);
+  const int32_t* pos = region<int32_t>(ws, p, ESM_WS_POS);
+  const uint8_t* w4 = e->w4 + (size_t)li * e->w4_layer;
+  const W4Off wo = w4_offsets(c);
+  const size_t nw[4] = {(size_t)3 * H, (size_t)H, (size_t)F, (size_t)H}, kw[4] = {(size_t)H, (size_t)H, (size_t)H,
+                                                                                  (size_t)F};
+  const E4m3Out none{nullptr, nullptr, nullptr, nullptr};
+  esm_status s;
+  GemmArgs g{};
+  g.dtype = kFP4;
+  g.M = rows;
+  g.pos = pos;
+  g.rope = e->rope;
+  g.max_positions = c.max_position_embeddings;
+  g.zero_pad_rows = zero_pad_rows ? 1 : 0;
+  // quantise src [rows, K] into dst_region, then point the GEMM at it and at weight t
+  auto operands = [&](const bf16_t* src, int K, void* dst_region, int t) -> esm_status {
+    const MxOff xo = mx_operand((size_t)rows, (size_t)K);
+    uint8_t* d = (uint8_t*)dst_region;
+    esm_status q = timed(e, ESM_K_OTHER, st, "mxfp4 quantize",
+                         [&] { return launch_mx_quantize(src, rows, K, d + xo.codes, d + xo.scales, st); });
+    if (q) return q;
+    const MxOff wq = mx_operand(nw[t], kw[t]);
+    g.x = d + xo.codes;
+    g.x_sc = d + xo.scales;
+    g.w = w4 + wo.at[t] + wq.codes;
+    g.w_sc = w4 + wo.at[t] + wq.scales;
+    return ESM_OK;
+  };
+
+  s = timed(e, ESM_K_LAYERNORM, st, "layernorm 1", [&] {
+    return launch_layernorm(x_in, (const bf16_t*)w->ln1_gamma, (const bf16_t*)w->ln1_beta, ln1, rows, H,
+                            c.layer_norm_eps, none, st);
+  });
+  if (s || (s = operands(ln1, H, ctx, 0))) return s;
+  g.bias = (const bf16_t*)w->b_qkv; g.res = nullptr; g.y = qkv;
+  g.N = 3 * H; g.K = H;
+  s = timed(e, ESM_K_GEMM_QKV, st, "qkv gemm", [&] { return launch_gemm(EPI_QKV_ROPE, g, st); });
+  if (s) return s;
+
+  AttnArgs aa{};
+  aa.qkv = qkv; aa.ctx = ctx;
+  aa.ctx8 = none;
+  aa.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
+  aa.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
+  aa.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
+  aa.tile_cap = tile_cap(rows, B);
+  aa.T = rows; aa.heads = heads;
+  s = timed(e, ESM_K_ATTENTION, st, "attention", [&] { return launch_attention(aa, st); });
+  if (s || (s = operands(ctx, H, ln1, 1))) return s;
+  g.bias = (const bf16_t*)w->b_out; g.res = x_in; g.y = x1;
+  g.N = H; g.K = H;
+  s = timed(e, ESM_K_GEMM_OUT, st, "out-proj gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
+  if (s) return s;
+
+  s = timed(e, ESM_K_LAYERNORM, st, "layernorm 2", [&] {
+    return launch_layernorm(x1, (const bf16_t*)w->ln2_gamma, (const bf16_t*)w->ln2_beta, ln2, rows, H,
+                            c.layer_norm_eps, none, st);
+  });
+  if (s || (s = operands(ln2, H, ctx, 2))) return s;
+  g.bias = (const bf16_t*)w->b_fc1; g.res = nullptr; g.y = act;
+  g.N = F; g.K = H;
+  s = timed(e, ESM_K_GEMM_FC1, st, "fc1 gemm", [&] { return launch_gemm(EPI_BIAS_GELU, g, st); });
+  if (s || (s = operands(act, F, qkv, 3))) return s;
+  g.bias = (const bf16_t*)w->b_fc2; g.res = x1; g.y = x_out;
+  g.N = H; g.K = F;
+  return timed(e, ESM_K_GEMM_FC2, st, "fc2 gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
 }
 
 // One pre-LN layer on rows already described by the segment table in ws.
@@ -346,6 +478,7 @@ esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, int32_t li, con
     return fp8 ? E4m3Out{(uint8_t*)y, as + t, am + t, rows_pos} : E4m3Out{nullptr, nullptr, nullptr, nullptr};
   };
   esm_status s;
+  if (layer_mx(e, li)) return run_layer_mx(e, w, li, x_in, x_out, rows, B, zero_pad_rows, ws, p, st);
 
   s = timed(e, ESM_K_LAYERNORM, st, "layernorm 1", [&] {
     return launch_layernorm(x_in, (const bf16_t*)w->ln1_gamma, (const bf16_t*)w->ln1_beta, ln1, rows, H,
@@ -450,7 +583,9 @@ esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, 
   if (!w && nlayers > 0) return fail(ESM_ERR_NULL, "weights are NULL");
   for (int l = 0; l < nlayers; ++l) {
     if ((s = check_weights(&w[l], layer_idx >= 0 ? layer_idx : l))) return s;
-    if (layer_fp8(e, layer_idx >= 0 ? layer_idx : l) && (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l))) return s;
+    if ((layer_fp8(e, layer_idx >= 0 ? layer_idx : l) || layer_mx(e, layer_idx >= 0 ? layer_idx : l)) &&
+        (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l)))
+      return s;
   }
   if ((s = check_cu_host(e, cu_host, B, T, max_seqlen))) return s;
   if (T == 0 || B == 0) return ok();
@@ -499,7 +634,9 @@ esm_status forward_bshd(esm_encoder* e, const esm_layer_weights* w, int nlayers,
   if (!w && nlayers > 0) return fail(ESM_ERR_NULL, "weights are NULL");
   for (int l = 0; l < nlayers; ++l) {
     if ((s = check_weights(&w[l], layer_idx >= 0 ? layer_idx : l))) return s;
-    if (layer_fp8(e, layer_idx >= 0 ? layer_idx : l) && (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l))) return s;
+    if ((layer_fp8(e, layer_idx >= 0 ? layer_idx : l) || layer_mx(e, layer_idx >= 0 ? layer_idx : l)) &&
+        (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l)))
+      return s;
   }
   if (sl_host && (s = esm_check_seqlens(sl_host, B, S, e->cfg.max_position_embeddings))) return s;
   if (rows == 0) return ok();
@@ -581,6 +718,17 @@ esm_status esm_encoder_create(const esm_config* cfg, int device, esm_encoder** o
     esm_encoder_destroy(e);
     return s;
   }
+  if (is_mx(e)) {
+    const size_t L = (size_t)(cfg->num_hidden_layers > 0 ? cfg->num_hidden_layers : 1);
+    e->w4_layer = align256(w4_offsets(*cfg).total);
+    err = hipMalloc((void**)&e->w4, L * e->w4_layer);
+    if (err != hipSuccess) {
+      esm_encoder_destroy(e);
+      return hip_fail(err, "MXFP4 weights");
+    }
+    e->prepared.assign(L, 0);
+    e->layer_prec.assign(L, ESM_PRECISION_MXFP4);
+  }
   if (cfg->vocab_size <= kHeadMaxVocab) {
     e->vocab_pad = (cfg->vocab_size + 63) / 64 * 64;
     err = hipMalloc((void**)&e->head_w, (size_t)e->vocab_pad * ((size_t)cfg->hidden_size + 1) * sizeof(bf16_t));
@@ -599,6 +747,7 @@ esm_status esm_encoder_destroy(esm_encoder* e) {
   if (e->rope) (void)hipFree(e->rope);
   if (e->fp8_mem) (void)hipFree(e->fp8_mem);
   if (e->w8) (void)hipFree(e->w8);
+  if (e->w4) (void)hipFree(e->w4);
   if (e->head_w) (void)hipFree(e->head_w);
   for (hipEvent_t ev : e->pool) (void)hipEventDestroy(ev);
   delete e;
@@ -957,6 +1106,35 @@ esm_status esm_fp8_prepare_layer(esm_encoder* e, int32_t layer_idx, const esm_la
   return ok();
 }
 
+esm_status esm_mxfp4_prepare_layer(esm_encoder* e, int32_t layer_idx, const esm_layer_weights* w,
+                                   esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  if (!is_mx(e)) return fail(ESM_ERR_STATE, "encoder was not created with MXFP4 precision");
+  if (layer_idx < 0 || layer_idx >= e->cfg.num_hidden_layers)
+    return fail(ESM_ERR_SHAPE, "layer_idx %d outside [0, %d)", layer_idx, e->cfg.num_hidden_layers);
+  esm_status s = check_weights(w, layer_idx);
+  if (s) return s;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  const esm_config& c = e->cfg;
+  const int64_t H = c.hidden_size, F = c.intermediate_size;
+  const W4Off wo = w4_offsets(c);
+  uint8_t* w4 = e->w4 + (size_t)layer_idx * e->w4_layer;
+  const bf16_t* src[4] = {(const bf16_t*)w->w_qkv, (const bf16_t*)w->w_out, (const bf16_t*)w->w_fc1,
+                          (const bf16_t*)w->w_fc2};
+  const int64_t n[4] = {3 * H, H, F, H}, k[4] = {H, H, H, F};
+  for (int i = 0; i < 4; ++i) {
+    const MxOff o = mx_operand((size_t)n[i], (size_t)k[i]);
+    s = timed(e, ESM_K_OTHER, st, "mxfp4 weight", [&] {
+      return launch_mx_quantize(src[i], n[i], (int32_t)k[i], w4 + wo.at[i] + o.codes, w4 + wo.at[i] + o.scales, st);
+    });
+    if (s) return s;
+  }
+  e->prepared[(size_t)layer_idx] = 1;
+  return ok();
+}
+
 static esm_status check_state_arg(const esm_encoder* e, const esm_fp8_state* st) {
   if (!e || !st) return fail(ESM_ERR_NULL, "encoder or state is NULL");
   if (!is_fp8(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
@@ -1023,18 +1201,21 @@ esm_status esm_fp8_reset(esm_encoder* e, esm_stream_t stream) {
 esm_status esm_set_layer_precision(esm_encoder* e, const int32_t* prec, int32_t n, esm_stream_t stream) {
   g_last_error.clear();
   if (!e || !prec) return fail(ESM_ERR_NULL, "NULL argument");
-  if (!is_fp8(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
+  if (!is_fp8(e) && !is_mx(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
   if (n != e->cfg.num_hidden_layers)
     return fail(ESM_ERR_SHAPE, "%d precisions for %d layers", n, e->cfg.num_hidden_layers);
+  const int32_t own = e->cfg.precision;
   std::vector<int32_t> on((size_t)n);
   for (int32_t l = 0; l < n; ++l) {
-    if (prec[l] != ESM_PRECISION_BF16 && prec[l] != ESM_PRECISION_FP8_DELAYED)
-      return fail(ESM_ERR_UNSUPPORTED, "layer %d: precision %d", l, prec[l]);
+    if (prec[l] != ESM_PRECISION_BF16 && prec[l] != own)
+      return fail(ESM_ERR_UNSUPPORTED, "layer %d: precision %d (this encoder runs %d or bf16)", l, prec[l], own);
     on[(size_t)l] = prec[l] == ESM_PRECISION_FP8_DELAYED;
   }
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
   HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
-  HIP_TRY(hipMemcpy(e->f8.layer_on, on.data(), on.size() * sizeof(int32_t), hipMemcpyHostToDevice), "layer flags");
+  if (is_fp8(e))
+    HIP_TRY(hipMemcpy(e->f8.layer_on, on.data(), on.size() * sizeof(int32_t), hipMemcpyHostToDevice),
+            "layer flags");
   e->layer_prec.assign(prec, prec + n);
   return ok();
 }

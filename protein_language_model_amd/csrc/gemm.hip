@@ -617,7 +617,7 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   const bool tall = r320 * 320 <= r256 * 256;
   if (a.dtype == kE4M3)
     return tall ? run<320, 256, 2, 4, EPI, kE4M3>(a, st) : run<256, 256, 2, 4, EPI, kE4M3>(a, st);
-  if constexpr (EPI == EPI_BIAS_GELU_E4M3 || EPI == EPI_QKV_ROPE) {
+  if constexpr (EPI == EPI_BIAS_GELU_E4M3) {
     if (a.dtype == kFP4) return hipErrorInvalidValue;
   } else {
     if (a.dtype == kFP4) return run<256, 256, 2, 4, EPI, kFP4>(a, st);

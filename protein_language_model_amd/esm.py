@@ -19,7 +19,7 @@ LIB_PATH = os.environ.get("ESM_LIBRARY") or os.path.join(_PKG, "libesmenc.so")
 ESM_OK = 0
 STATUS_NAMES = {0: "ESM_OK", 1: "ESM_ERR_NULL", 2: "ESM_ERR_SHAPE", 3: "ESM_ERR_SEQLENS", 4: "ESM_ERR_UNSUPPORTED",
                 5: "ESM_ERR_WORKSPACE", 6: "ESM_ERR_ARCH", 7: "ESM_ERR_HIP", 8: "ESM_ERR_STATE"}
-PRECISION = {"bf16": 0, "fp8": 1}
+PRECISION = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 LAYOUT_THD, LAYOUT_BSHD = 0, 1
 EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_E4M3 = 0, 1, 2, 3
 WS_REGIONS = {"ln1": 0, "qkv": 1, "ctx": 2, "x1": 3, "ln2": 4, "act": 5, "pos": 6, "tiles": 7, "ntiles": 8, "segs": 9}
@@ -91,6 +91,7 @@ SIGNATURES = {
     "esm_layernorm_e4m3_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _p]),
     "esm_linear_e4m3_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
     "esm_fp8_prepare_layer": (_i32, [_p, _i32, ctypes.POINTER(EsmLayerWeights), _p]),
+    "esm_mxfp4_prepare_layer": (_i32, [_p, _i32, ctypes.POINTER(EsmLayerWeights), _p]),
     "esm_fp8_get_state": (_i32, [_p, ctypes.POINTER(EsmFp8State), _p]),
     "esm_fp8_set_state": (_i32, [_p, ctypes.POINTER(EsmFp8State), _p]),
     "esm_fp8_reset": (_i32, [_p, _p]),
@@ -452,6 +453,15 @@ class Encoder:
     def fp8_prepare(self, weights: Sequence[Dict], stream=None) -> None:
         for l, w in enumerate(weights):
             self.fp8_prepare_layer(l, w, stream)
+
+    # -- MXFP4 (the FP4 recipe)
+    def mxfp4_prepare_layer(self, layer_idx: int, weights, stream=None) -> None:
+        w = layer_weights_struct(weights)
+        _call("esm_mxfp4_prepare_layer", self._h, int(layer_idx), ctypes.byref(w), _stream(stream))
+
+    def mxfp4_prepare(self, weights: Sequence[Dict], stream=None) -> None:
+        for l, w in enumerate(weights):
+            self.mxfp4_prepare_layer(l, w, stream)
 
     def fp8_get_state(self, stream=None) -> Dict[str, np.ndarray]:
         L, HL = self.cfg.num_hidden_layers, self.cfg.amax_history_len

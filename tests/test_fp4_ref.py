@@ -90,3 +90,40 @@ def test_mx_matmul():
     qx2, ex2 = F.mx_quantize(x * 8.0)
     assert np.array_equal(qx2, qx) and np.array_equal(ex2, ex + 3)
     assert np.array_equal(F.mx_matmul(qx2, ex2, qw, ew), 8.0 * (x @ w.T))
+
+
+def test_vectorised_quantiser_follows_the_block_rule():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((16, 256)) * np.exp2(rng.integers(-60, 60, (16, 8)).repeat(32, axis=1))
+    x[3, 64:96] = 0.0
+    codes, exps = F.mx_quantize(x)
+    for r in range(16):
+        for b in range(8):
+            blk = x[r, 32 * b: 32 * b + 32]
+            e = F.block_exponent(blk)
+            assert exps[r, b] == e
+            assert np.array_equal(codes[r, 32 * b: 32 * b + 32], F.e2m1_encode(blk / 2.0 ** e))
+
+
+def test_bf16_round():
+    # exactly representable values stay; midpoints go to the even neighbour
+    assert F.bf16_round(1.0) == 1.0 and F.bf16_round(-3.5) == -3.5
+    assert F.bf16_round(1.0 + 2.0 ** -8) == 1.0                 # midpoint, even below
+    assert F.bf16_round(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6  # midpoint, even above
+    assert F.bf16_round(1.0 + 2.0 ** -8 + 2.0 ** -20) == 1.0 + 2.0 ** -7
+
+
+def test_mxfp4_layer_with_representable_operands_is_the_plain_layer():
+    """Zero weights in the two GEMMs that feed the residuals make the MXFP4
+    layer the identity, as the plain one (the quantised zero is exact)."""
+    from oracle import esm_oracle as O
+    rng = np.random.default_rng(9)
+    H, F_, heads = 256, 512, 4
+    w = {"ln1_gamma": np.ones(H), "ln1_beta": np.zeros(H), "ln2_gamma": np.ones(H), "ln2_beta": np.zeros(H),
+         "w_qkv": F.bf16_round(rng.standard_normal((3 * H, H)) * 0.02), "b_qkv": np.zeros(3 * H),
+         "w_out": np.zeros((H, H)), "b_out": np.zeros(H), "w_fc1": F.bf16_round(rng.standard_normal((F_, H)) * 0.02),
+         "b_fc1": np.zeros(F_), "w_fc2": np.zeros((H, F_)), "b_fc2": np.zeros(H)}
+    x = rng.standard_normal((40, H))
+    cu = np.array([0, 15, 40])
+    assert np.array_equal(F.layer_forward_mxfp4(x, cu, w, heads), x)
+    assert np.array_equal(O.layer_forward(x, cu, w, heads), x)

@@ -83,3 +83,109 @@ def test_mxfp4_linear_matches_oracle(enc, gu, M, N, K, epi):
         ref = ref + D.bf16_bits_to_f64(rb)
     bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max()
     assert np.all(np.abs(got - ref) <= bound), np.abs(got - ref).max()
+
+
+# ------------------------------------------------------------ MXFP4 layers
+
+# vs the MXFP4-emulating oracle: the library computes the quantiser inputs (LN
+# outputs, context, GELU output) in fp32 and the emulation in fp64; where the
+# two land on different sides of an E2M1 midpoint the code moves by one step
+# (up to a third of the value), and attention and the FFN carry such flips on
+# (measured 5.3e-2 on this layer).
+TOL_MX_EMU = 8e-2
+# vs the plain fp64 layer: the recipe's own error (emulation vs fp64, measured
+# 1.3e-1 here) plus 2e-2, the rule of the FP8 stack.
+TOL_MX_OVER_RECIPE = 2e-2
+
+
+@pytest.fixture(scope="module")
+def l650_mx(gu):
+    """650M-shaped single layer (hidden 1280, 20 heads, FFN 5120), MXFP4
+    encoder, three packed sequences, random LayerNorm parameters."""
+    H, F, heads = 1280, 5120, 20
+    lengths = np.array([17, 100, 333])
+    cu = D.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    enc = esm.Encoder(hidden_size=H, num_attention_heads=heads, intermediate_size=F, num_hidden_layers=1,
+                      precision="mxfp4")
+    wd, wr, _ = gu.layer_weights(H, F, layer=0, seed=3, random_ln=True)
+    enc.mxfp4_prepare([wd])
+    xb = D.make_hidden(T, H, seed=3)
+    yield {"enc": enc, "wd": wd, "wr": wr, "xb": xb, "cu": cu, "lengths": lengths, "T": T, "H": H, "heads": heads}
+    enc.close()
+
+
+def _mx_layer(t, gu, xbits, cu):
+    T = int(cu[-1])
+    return t["enc"].layer_fwd(t["wd"], gu.to_dev_bf16(xbits), gu.to_dev_i32(cu), len(cu) - 1, T,
+                              int(np.max(np.diff(cu))))
+
+
+def test_mxfp4_layer_matches_the_oracles(gu, l650_mx):
+    t = l650_mx
+    y = gu.from_dev(_mx_layer(t, gu, t["xb"], t["cu"]))
+    x = D.bf16_bits_to_f64(t["xb"])
+    emu = F.layer_forward_mxfp4(x, t["cu"], t["wr"], t["heads"])
+    from oracle import esm_oracle as O
+    ref = O.layer_forward(x, t["cu"], t["wr"], t["heads"])
+    e_emu, e_plain = gu.rel_err(y, emu), gu.rel_err(y, ref)
+    print(f"650M MXFP4 layer: rel err vs MXFP4 emulation {e_emu:.2e}, vs fp64 {e_plain:.2e}, "
+          f"emulation vs fp64 {gu.rel_err(emu, ref):.2e}")
+    assert np.isfinite(y).all()
+    assert e_emu < TOL_MX_EMU
+    assert e_plain < gu.rel_err(emu, ref) + TOL_MX_OVER_RECIPE
+
+
+def test_mxfp4_layer_packed_equals_alone(gu, l650_mx):
+    t = l650_mx
+    y = gu.bits_of(_mx_layer(t, gu, t["xb"], t["cu"]))
+    for s in range(len(t["lengths"])):
+        a, e = int(t["cu"][s]), int(t["cu"][s + 1])
+        ya = gu.bits_of(_mx_layer(t, gu, t["xb"][a:e], np.array([0, e - a])))
+        assert np.array_equal(ya, y[a:e]), s
+
+
+def test_mxfp4_layer_thd_equals_bshd_with_nan_padding(gu, l650_mx):
+    t = l650_mx
+    y = gu.bits_of(_mx_layer(t, gu, t["xb"], t["cu"]))
+    S, B = int(t["lengths"].max()), len(t["lengths"])
+    xp = np.full((B, S, t["H"]), 0x7FC0, np.uint16)            # NaN padding
+    for i in range(B):
+        xp[i, :t["lengths"][i]] = t["xb"][t["cu"][i]:t["cu"][i + 1]]
+    yp = gu.bits_of(t["enc"].layer_fwd_bshd(t["wd"], gu.to_dev_bf16(xp), gu.to_dev_i32(t["lengths"]), B, S))
+    for i in range(B):
+        L = int(t["lengths"][i])
+        assert np.array_equal(yp[i, :L], y[t["cu"][i]:t["cu"][i + 1]]), i
+        assert not np.any(yp[i, L:]), i
+
+
+def test_mxfp4_layer_precision_bf16_equals_the_bf16_encoder(gu, l650_mx):
+    t = l650_mx
+    t["enc"].set_layer_precision(["bf16"])
+    try:
+        y = gu.bits_of(_mx_layer(t, gu, t["xb"], t["cu"]))
+    finally:
+        t["enc"].set_layer_precision(["mxfp4"])
+    e16 = esm.Encoder(hidden_size=t["H"], num_attention_heads=t["heads"], intermediate_size=4 * t["H"],
+                      num_hidden_layers=1)
+    try:
+        y16 = gu.bits_of(e16.layer_fwd(t["wd"], gu.to_dev_bf16(t["xb"]), gu.to_dev_i32(t["cu"]), 3, t["T"],
+                                       int(t["lengths"].max())))
+    finally:
+        e16.close()
+    assert np.array_equal(y, y16)
+
+
+def test_mxfp4_encoder_rejects_unprepared_layers_and_bad_shapes(gu):
+    enc = esm.Encoder(hidden_size=512, num_attention_heads=8, intermediate_size=2048, num_hidden_layers=2,
+                      precision="mxfp4")
+    try:
+        w = [gu.layer_weights(512, 2048, layer=l)[0] for l in range(2)]
+        x = gu.to_dev_bf16(D.make_hidden(40, 512))
+        with pytest.raises(esm.EsmError, match="MXFP4 weights of layer 0 not prepared"):
+            enc.layer_fwd(w[0], x, gu.to_dev_i32([0, 40]), 1, 40, 40)
+    finally:
+        enc.close()
+    with pytest.raises(esm.EsmError):   # 320 is not a multiple of 256
+        esm.Encoder(hidden_size=320, num_attention_heads=5, intermediate_size=1280, num_hidden_layers=1,
+                    precision="mxfp4")
