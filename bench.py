@@ -12,8 +12,9 @@ least 10 warm-up steps, and reported under "fp8"; what follows the stack
 (final LayerNorm, masked-LM logits, per-sequence means) is timed on its own
 under "head".  The biased attention kernel (the DeepSpeed4Science page's
 Evoformer attention with a mask bias and a pair bias) is timed on its own
-synthetic MSA-row shape under "biased_attention", and the MXFP4 quantiser
-and GEMM (the FP4 recipe) on the layer's four GEMM shapes under "mxfp4".
+synthetic MSA-row shape under "biased_attention", the MXFP4 quantiser and
+GEMM (the FP4 recipe) on the layer's four GEMM shapes under "mxfp4", and the
+whole stack with MXFP4 GEMMs under "mxfp4_stack".
 Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
@@ -320,6 +321,8 @@ def main():
                           num_hidden_layers=m.layers, precision=precision)
         if precision == "fp8":
             enc.fp8_prepare(weights, stream=stream)
+        if precision == "mxfp4":
+            enc.mxfp4_prepare(weights, stream=stream)
         ws = enc.workspace(T, B)
 
         def step():
@@ -474,6 +477,20 @@ def main():
         enc8.close()
         del ws8
 
+    mx_stack = None
+    if not fp8_main and not args.no_mxfp4 and m.hidden % 256 == 0 and m.ffn % 256 == 0 and m.ffn <= 8 * m.hidden:
+        encm, wsm, msm, profm, _ = measure("mxfp4", args.warmup)
+        mx_stack = {"ms_per_step": round(msm, 4), "value": round(T / (msm * 1e-3), 1), "unit": "residues/s",
+                    "tflops": round(total_flops / (msm * 1e-3) / 1e12, 1), "speedup_vs_bf16": round(ms / msm, 3),
+                    "recipe": "MXFP4 (E2M1, E8M0 scale per 32 values along K) QKV/out/fc1/fc2 GEMMs; each GEMM "
+                              "input quantised after its producer"}
+        if profm:
+            mx_stack["kernels"] = kernel_table(profm)
+            mx_stack["rooflines"] = rooflines_all(profm, fl, {k: PEAK_FP4_TFLOPS for k in fl if k.startswith("gemm")},
+                                                  T, m.hidden, False)
+        encm.close()
+        del wsm
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, batch, emb, weights)
@@ -508,6 +525,7 @@ def main():
         "head": head,
         "biased_attention": biased,
         "mxfp4": mxfp4,
+        "mxfp4_stack": mx_stack,
         "vendor_gemm_fc1": vendor,
         "fp8": fp8,
     }
