@@ -106,17 +106,18 @@ def bf16_round(x) -> np.ndarray:
 
 
 def layer_forward_mxfp4(x, cu_seqlens, w, heads: int):
-    """One pre-LN layer with MXFP4 GEMMs: each linear is
-    mx(bf16(a)) . mx(W)^T + b, the GEMM input a rounded to bf16 as the layer
-    stores it and quantised per 32-value block along K, W (bf16 values)
-    likewise; everything else as in the plain fp64 layer."""
+    """One pre-LN layer with MXFP4 GEMMs: each linear is mx(a) . mx(W)^T + b,
+    quantised per 32-value block along K, W (bf16 values) likewise.  The
+    LayerNorm outputs are quantised as computed; the attention context and
+    the GELU output are first rounded to bf16, the tensors the layer stores
+    them in.  Everything else as in the plain fp64 layer."""
     from . import esm_oracle as O
     x = np.asarray(x, np.float64)
     T, H = x.shape
     F = w["w_fc1"].shape[0]
 
     def lin(a, wname, bname, n_out):
-        y = mx_matmul(*mx_quantize(bf16_round(a)), *mx_quantize(w[wname]))
+        y = mx_matmul(*mx_quantize(a), *mx_quantize(w[wname]))
         b = w.get(bname)
         return y + (np.zeros(n_out) if b is None else b)
 
@@ -124,10 +125,10 @@ def layer_forward_mxfp4(x, cu_seqlens, w, heads: int):
     q, k, v = O.split_qkv(lin(h1, "w_qkv", "b_qkv", 3 * H), heads)
     pos = O.positions(cu_seqlens)
     ctx = O.attention(O.apply_rope(q, pos), O.apply_rope(k, pos), v, cu_seqlens)
-    x1 = x + lin(ctx, "w_out", "b_out", H)
+    x1 = x + lin(bf16_round(ctx), "w_out", "b_out", H)
     h2 = O.layer_norm(x1, w["ln2_gamma"], w["ln2_beta"])
     a = O.gelu(lin(h2, "w_fc1", "b_fc1", F))
-    return x1 + lin(a, "w_fc2", "b_fc2", H)
+    return x1 + lin(bf16_round(a), "w_fc2", "b_fc2", H)
 
 
 def mx_dequantize(codes, exps) -> np.ndarray:

@@ -63,6 +63,36 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(const float (&v)[4], float s) {
   return r;
 }
 
+// MXFP4 (OCP microscaling, E2M1 values with one E8M0 scale per 32 values):
+// the shared exponent of a block with maximum magnitude amax,
+// e = floor(log2 amax) - 2 clamped to [-127, 127] (-127 for a zero or
+// subnormal amax), read off the float's exponent field.
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  const int E = (int)((__float_as_uint(amax) >> 23) & 0xff);
+  const int ex = E == 0 ? -127 : E - 127 - 2;
+  return ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+}
+// E2M1 code of v (already divided by the block scale 2^e): bit 3 the sign,
+// bits 2..0 the magnitude index in (0, 0.5, 1, 1.5, 2, 3, 4, 6); nearest
+// value, ties to the even mantissa, saturating at 6.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = a <= 0.25f ? 0u
+                   : a < 0.75f ? 1u
+                   : a <= 1.25f ? 2u
+                   : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u
+                   : a < 3.5f ? 5u
+                   : a <= 5.0f ? 6u
+                   : 7u;
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+// Byte offset of the scale of (row m, block b) in the MXFP4 scale layout
+// [K / 256][M2][8], blocks of a K step in the order 0, 2, 4, 6, 1, 3, 5, 7.
+__device__ __forceinline__ int64_t mx_scale_offset(int64_t m, int b, int64_t M2) {
+  return ((int64_t)(b / 8) * M2 + m) * 8 + ((b & 1) * 4 + ((b & 7) >> 1));
+}
+
 // Maximum of a non-negative per-lane value over the wave (fmaxf drops NaN).
 // Direct-to-LDS 16-byte load: lane i's 16 bytes from g land at LDS byte
 // lds_base + 16 i (lds_base must be wave-uniform; it goes through M0).  Issued
@@ -148,6 +178,10 @@ hipError_t launch_segment_mean(const bf16_t* x, const int32_t* segs, int32_t B, 
                                hipStream_t st);
 hipError_t launch_layernorm(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, bf16_t* y,
                             int64_t M, int32_t H, float eps, const E4m3Out& q, hipStream_t st);
+// LayerNorm whose output goes straight to MXFP4 (the esm_mxfp4_quantize
+// layout, H % 256 == 0): the fp32 normalised values are quantised, no bf16 row.
+hipError_t launch_layernorm_mx(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, uint8_t* codes,
+                               uint8_t* scales, int64_t M, int32_t H, float eps, hipStream_t st);
 
 enum GemmEpi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_QKV_ROPE = 3, EPI_BIAS_GELU_E4M3 = 4 };
 

@@ -137,10 +137,16 @@ constexpr int ln_rows_per_wave() { return CH <= 5 ? 2 : 1; }
 // ([BIO-ACC] 3.1 layernorm; [TE-RU] LayerNormLinear / LayerNormMLP).  With
 // OUT8 the normalised row is cast to E4M3 with the tensor's delayed scale and
 // its amax recorded, the quantiser that feeds an FP8 GEMM ([BIO-ACC] 2.1).
-template <int CH, bool OUT8>
+// With MX the normalised row goes straight to MXFP4: a block of 32 values is
+// the 4 consecutive chunks of lanes 4k .. 4k + 3, whose amax two lane
+// exchanges combine; each lane writes its 8 codes (4 bytes) and lane 4k the
+// block's scale (codes [M, H / 2], scales in the esm_mxfp4_quantize layout).
+template <int CH, bool OUT8, bool MX = false>
 __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
                                                    const bf16_t* __restrict__ beta, bf16_t* __restrict__ y,
-                                                   int64_t M, int32_t H, float eps, E4m3Out q) {
+                                                   int64_t M, int32_t H, float eps, E4m3Out q,
+                                                   uint8_t* __restrict__ mx_codes = nullptr,
+                                                   uint8_t* __restrict__ mx_scales = nullptr) {
   constexpr int RW = ln_rows_per_wave<CH, OUT8>();
   const int lane = threadIdx.x & 63;
   const int64_t row0 = (int64_t)blockIdx.x * (4 * RW) + (threadIdx.x >> 6);
@@ -232,7 +238,23 @@ __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x,
           o[2 * e] = v[i][2 * e] * rstd * bflo(g[e]) + bflo(b[e]);
           o[2 * e + 1] = v[i][2 * e + 1] * rstd * bfhi(g[e]) + bfhi(b[e]);
         }
-        if constexpr (OUT8) {
+        if constexpr (MX) {
+          float am = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(o[e]));
+          am = fmaxf(am, __shfl_xor(am, 1));
+          am = fmaxf(am, __shfl_xor(am, 2));
+          const int ex = mx_block_exponent(am);
+          const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);   // 2^-ex
+          uint32_t word = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            word |= (e2m1_code(o[2 * e] * inv) | (e2m1_code(o[2 * e + 1] * inv) << 4)) << (8 * e);
+          if (active) {
+            *(uint32_t*)(mx_codes + row * (H / 2) + c * 4) = word;
+            if ((lane & 3) == 0) mx_scales[mx_scale_offset(row, c / 4, M + (M & 1))] = (uint8_t)(ex + 127);
+          }
+        } else if constexpr (OUT8) {
           const float lo[4] = {o[0], o[1], o[2], o[3]}, hi[4] = {o[4], o[5], o[6], o[7]};
           if (count[r])
 #pragma unroll
@@ -352,6 +374,26 @@ hipError_t layernorm_ch(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta
   else if (ch <= 3) launch_ln<3, OUT8>(x, gamma, beta, y, M, H, eps, q, st);
   else if (ch <= 5) launch_ln<5, OUT8>(x, gamma, beta, y, M, H, eps, q, st);
   else if (ch <= 8) launch_ln<8, OUT8>(x, gamma, beta, y, M, H, eps, q, st);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm_mx(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, uint8_t* codes,
+                               uint8_t* scales, int64_t M, int32_t H, float eps, hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (H % 256) return hipErrorInvalidValue;
+  const E4m3Out none{nullptr, nullptr, nullptr, nullptr};
+  const int ch = (H / 8 + 63) / 64;
+  auto go = [&](auto kern, int rw) {
+    const int rows = 4 * rw;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((M + rows - 1) / rows)), dim3(256), 0, st, x, gamma, beta,
+                       (bf16_t*)nullptr, M, H, eps, none, codes, scales);
+  };
+  if (ch <= 1) go(k_layernorm<1, false, true>, ln_rows_per_wave<1, false>());
+  else if (ch <= 2) go(k_layernorm<2, false, true>, ln_rows_per_wave<2, false>());
+  else if (ch <= 3) go(k_layernorm<3, false, true>, ln_rows_per_wave<3, false>());
+  else if (ch <= 5) go(k_layernorm<5, false, true>, ln_rows_per_wave<5, false>());
+  else if (ch <= 8) go(k_layernorm<8, false, true>, ln_rows_per_wave<8, false>());
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -362,13 +362,15 @@ esm_status run_segments(esm_encoder* e, int layout, const int32_t* lens, int32_t
   });
 }
 
-// One pre-LN layer with MXFP4 GEMMs (the FP4 recipe): LayerNorm, attention
-// and every GEMM output as in the bf16 layer; each GEMM input is quantised to
-// MXFP4 right after its producer into a workspace region that is free at that
-// point (LN1 output -> ctx region, context -> LN1 region, LN2 output -> ctx
-// region, GELU output -> QKV region), and the GEMMs read layer li's prepared
-// MXFP4 weights.  Quantisation is per 32-value block of a row, so rows stay
-// independent (packed == each sequence alone, padding rows never mix in).
+// One pre-LN layer with MXFP4 GEMMs (the FP4 recipe): attention, the
+// residuals and every GEMM output as in the bf16 layer; each GEMM input goes
+// to MXFP4 in a workspace region that is free at that point: the LayerNorms
+// quantise their fp32 output themselves (LN1 -> ctx region, LN2 -> ctx
+// region), the attention context and the GELU output are quantised from
+// their bf16 tensors (context -> LN1 region, GELU output -> QKV region).  The
+// GEMMs read layer li's prepared MXFP4 weights.  Quantisation is per 32-value
+// block of a row, so rows stay independent (packed == each sequence alone,
+// padding rows never mix in).
 esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, const bf16_t* x_in, bf16_t* x_out,
                         int64_t rows, int32_t B, bool zero_pad_rows, void* ws, const Plan& p, hipStream_t st) {
   const esm_config& c = e->cfg;
@@ -377,7 +379,6 @@ esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, 
   bf16_t* qkv = region<bf16_t>(ws, p, ESM_WS_QKV);
   bf16_t* ctx = region<bf16_t>(ws, p, ESM_WS_CTX);
   bf16_t* x1 = region<bf16_t>(ws, p, ESM_WS_X1);
-  bf16_t* ln2 = region<bf16_t>(ws, p, ESM_WS_LN2);
   bf16_t* act = region<bf16_t>(ws, p, ESM_WS_ACT);
   const int32_t* pos = region<int32_t>(ws, p, ESM_WS_POS);
   const uint8_t* w4 = e->w4 + (size_t)li * e->w4_layer;
@@ -393,13 +394,16 @@ esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, 
   g.rope = e->rope;
   g.max_positions = c.max_position_embeddings;
   g.zero_pad_rows = zero_pad_rows ? 1 : 0;
-  // quantise src [rows, K] into dst_region, then point the GEMM at it and at weight t
+  // point the GEMM at the MXFP4 operand in dst_region (quantising src [rows, K]
+  // into it first unless src is null: a LayerNorm already wrote it) and at weight t
   auto operands = [&](const bf16_t* src, int K, void* dst_region, int t) -> esm_status {
     const MxOff xo = mx_operand((size_t)rows, (size_t)K);
     uint8_t* d = (uint8_t*)dst_region;
-    esm_status q = timed(e, ESM_K_OTHER, st, "mxfp4 quantize",
-                         [&] { return launch_mx_quantize(src, rows, K, d + xo.codes, d + xo.scales, st); });
-    if (q) return q;
+    if (src) {
+      esm_status q = timed(e, ESM_K_OTHER, st, "mxfp4 quantize",
+                           [&] { return launch_mx_quantize(src, rows, K, d + xo.codes, d + xo.scales, st); });
+      if (q) return q;
+    }
     const MxOff wq = mx_operand(nw[t], kw[t]);
     g.x = d + xo.codes;
     g.x_sc = d + xo.scales;
@@ -407,12 +411,18 @@ esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, 
     g.w_sc = w4 + wo.at[t] + wq.scales;
     return ESM_OK;
   };
+  // LayerNorm straight to MXFP4 in dst_region
+  auto ln_mx = [&](const bf16_t* src, const void* gamma, const void* beta, void* dst_region, const char* what) {
+    const MxOff xo = mx_operand((size_t)rows, (size_t)H);
+    uint8_t* d = (uint8_t*)dst_region;
+    return timed(e, ESM_K_LAYERNORM, st, what, [&] {
+      return launch_layernorm_mx(src, (const bf16_t*)gamma, (const bf16_t*)beta, d + xo.codes, d + xo.scales, rows,
+                                 H, c.layer_norm_eps, st);
+    });
+  };
 
-  s = timed(e, ESM_K_LAYERNORM, st, "layernorm 1", [&] {
-    return launch_layernorm(x_in, (const bf16_t*)w->ln1_gamma, (const bf16_t*)w->ln1_beta, ln1, rows, H,
-                            c.layer_norm_eps, none, st);
-  });
-  if (s || (s = operands(ln1, H, ctx, 0))) return s;
+  s = ln_mx(x_in, w->ln1_gamma, w->ln1_beta, ctx, "layernorm 1");
+  if (s || (s = operands(nullptr, H, ctx, 0))) return s;
   g.bias = (const bf16_t*)w->b_qkv; g.res = nullptr; g.y = qkv;
   g.N = 3 * H; g.K = H;
   s = timed(e, ESM_K_GEMM_QKV, st, "qkv gemm", [&] { return launch_gemm(EPI_QKV_ROPE, g, st); });
@@ -433,11 +443,8 @@ esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, 
   s = timed(e, ESM_K_GEMM_OUT, st, "out-proj gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
   if (s) return s;
 
-  s = timed(e, ESM_K_LAYERNORM, st, "layernorm 2", [&] {
-    return launch_layernorm(x1, (const bf16_t*)w->ln2_gamma, (const bf16_t*)w->ln2_beta, ln2, rows, H,
-                            c.layer_norm_eps, none, st);
-  });
-  if (s || (s = operands(ln2, H, ctx, 2))) return s;
+  s = ln_mx(x1, w->ln2_gamma, w->ln2_beta, ctx, "layernorm 2");
+  if (s || (s = operands(nullptr, H, ctx, 2))) return s;
   g.bias = (const bf16_t*)w->b_fc1; g.res = nullptr; g.y = act;
   g.N = F; g.K = H;
   s = timed(e, ESM_K_GEMM_FC1, st, "fc1 gemm", [&] { return launch_gemm(EPI_BIAS_GELU, g, st); });

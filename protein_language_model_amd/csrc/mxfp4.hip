@@ -20,21 +20,6 @@ namespace esm {
 
 namespace {
 
-// E2M1 code of v (already divided by the block scale): bit 3 the sign,
-// bits 2..0 the magnitude index in (0, 0.5, 1, 1.5, 2, 3, 4, 6).
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float a = fabsf(v);
-  uint32_t c = a <= 0.25f ? 0u
-             : a < 0.75f ? 1u
-             : a <= 1.25f ? 2u
-             : a < 1.75f ? 3u
-             : a <= 2.5f ? 4u
-             : a < 3.5f ? 5u
-             : a <= 5.0f ? 6u
-             : 7u;
-  return c | ((__float_as_uint(v) >> 28) & 8u);
-}
-
 __global__ __launch_bounds__(256) void k_mx_quantize(const bf16_t* __restrict__ x, int64_t M, int32_t K,
                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const int nb = K / 32;                     // blocks per row
@@ -44,7 +29,7 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const bf16_t* __restrict__ 
   const int64_t m = t / nb;
   const int b = (int)(t % nb);
   // scale byte of (row m, block b): K-step b / 8, position (b % 2) * 4 + (b % 8) / 2
-  uint8_t* sdst = scales + ((int64_t)(b / 8) * M2 + m) * 8 + ((b & 1) * 4 + ((b & 7) >> 1));
+  uint8_t* sdst = scales + mx_scale_offset(m, b, M2);
   if (m >= M) {          // the pad row of an odd M: scale 2^0, no codes
     *sdst = 127;
     return;
@@ -58,10 +43,7 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const bf16_t* __restrict__ 
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bflo(w[i][e])), fabsf(bfhi(w[i][e]))));
-  // floor(log2 amax) from the exponent field; a zero or subnormal amax clamps to -127.
-  const int E = (int)((__float_as_uint(amax) >> 23) & 0xff);
-  int ex = E == 0 ? -127 : E - 127 - 2;
-  ex = ex < -127 ? -127 : (ex > 127 ? 127 : ex);
+  const int ex = mx_block_exponent(amax);
   *sdst = (uint8_t)(ex + 127);
   const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);   // 2^-ex (ex <= 125 for finite input)
   u32x4 out;
