@@ -87,6 +87,22 @@ __device__ __forceinline__ uint32_t e2m1_code(float v) {
                    : 7u;
   return c | ((__float_as_uint(v) >> 28) & 8u);
 }
+// Two values of a block with exponent ex to two E2M1 codes (v0 in bits 0..3,
+// v1 in bits 4..7).  gfx950's v_cvt_scalef32_pk_fp4_f32 divides by the scale
+// and rounds to nearest even with saturation at 6 -- the rule above, checked
+// code by code against the definition (every midpoint and its neighbours,
+// saturation, signed zero) before it was used here; its scale must be a
+// normal float, so a block with ex = -127 (zero or tiny amax) takes the
+// comparison chain.
+__device__ __forceinline__ uint32_t e2m1_pair(float v0, float v1, int ex) {
+  if (ex > -127) {
+    const float X = __uint_as_float((uint32_t)(ex + 127) << 23);   // 2^ex
+    return (uint32_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v0, v1, X, 0) & 0xFFu;
+  }
+  const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);  // 2^-ex = 2^127
+  return e2m1_code(v0 * inv) | (e2m1_code(v1 * inv) << 4);
+}
+
 // Byte offset of the scale of (row m, block b) in the MXFP4 scale layout
 // [K / 256][M2][8], blocks of a K step in the order 0, 2, 4, 6, 1, 3, 5, 7.
 __device__ __forceinline__ int64_t mx_scale_offset(int64_t m, int b, int64_t M2) {

@@ -245,11 +245,9 @@ __global__ __launch_bounds__(256) void k_layernorm(const bf16_t* __restrict__ x,
           am = fmaxf(am, __shfl_xor(am, 1));
           am = fmaxf(am, __shfl_xor(am, 2));
           const int ex = mx_block_exponent(am);
-          const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);   // 2^-ex
           uint32_t word = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            word |= (e2m1_code(o[2 * e] * inv) | (e2m1_code(o[2 * e + 1] * inv) << 4)) << (8 * e);
+          for (int e = 0; e < 4; ++e) word |= e2m1_pair(o[2 * e], o[2 * e + 1], ex) << (8 * e);
           if (active) {
             *(uint32_t*)(mx_codes + row * (H / 2) + c * 4) = word;
             if ((lane & 3) == 0) mx_scales[mx_scale_offset(row, c / 4, M + (M & 1))] = (uint8_t)(ex + 127);

@@ -11,9 +11,8 @@
 //
 // One thread per block: its 32 bf16 values are one 64-byte run, so a wave
 // reads 4 KB of consecutive memory; v / X is exact (a power-of-two scaling of
-// a bf16 value), and the rounding is a chain of comparisons against the
-// midpoints between neighbouring E2M1 magnitudes, each tie resolved towards
-// the value whose mantissa bit is 0.
+// a bf16 value), and the rounding is gfx950's scaled FP4 conversion, two
+// values per instruction (see e2m1_pair).
 #include "common.h"
 
 namespace esm {
@@ -45,17 +44,13 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const bf16_t* __restrict__ 
     for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bflo(w[i][e])), fabsf(bfhi(w[i][e]))));
   const int ex = mx_block_exponent(amax);
   *sdst = (uint8_t)(ex + 127);
-  const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);   // 2^-ex (ex <= 125 for finite input)
   u32x4 out;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     // 8 values -> 8 nibbles, value 2j in the low nibble of byte j
     uint32_t word = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = e2m1_code(bflo(w[i][e]) * inv), hi = e2m1_code(bfhi(w[i][e]) * inv);
-      word |= (lo | (hi << 4)) << (8 * e);
-    }
+    for (int e = 0; e < 4; ++e) word |= e2m1_pair(bflo(w[i][e]), bfhi(w[i][e]), ex) << (8 * e);
     out[i] = word;
   }
   *(u32x4*)(codes + m * (K / 2) + b * 16) = out;
