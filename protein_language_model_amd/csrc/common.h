@@ -199,7 +199,8 @@ hipError_t launch_layernorm(const bf16_t* x, const bf16_t* gamma, const bf16_t* 
 hipError_t launch_layernorm_mx(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, uint8_t* codes,
                                uint8_t* scales, int64_t M, int32_t H, float eps, hipStream_t st);
 
-enum GemmEpi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_QKV_ROPE = 3, EPI_BIAS_GELU_E4M3 = 4 };
+enum GemmEpi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_QKV_ROPE = 3, EPI_BIAS_GELU_E4M3 = 4,
+               EPI_BIAS_GELU_MX = 5 };
 
 struct GemmArgs {
   int32_t dtype;       // kBF16 or kE4M3 operands
@@ -227,6 +228,9 @@ struct GemmArgs {
   // [K / 256][rows rounded up to even][8]
   const uint8_t* x_sc;
   const uint8_t* w_sc;
+  // EPI_BIAS_GELU_MX: y8 = MXFP4 codes [M, N / 2] of gelu(.), y_sc their
+  // block scales (the same layout, K = N)
+  uint8_t* y_sc;
 };
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st);

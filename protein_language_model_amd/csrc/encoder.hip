@@ -363,12 +363,12 @@ esm_status run_segments(esm_encoder* e, int layout, const int32_t* lens, int32_t
 }
 
 // One pre-LN layer with MXFP4 GEMMs (the FP4 recipe): attention, the
-// residuals and every GEMM output as in the bf16 layer; each GEMM input goes
-// to MXFP4 in a workspace region that is free at that point: the LayerNorms
-// quantise their fp32 output themselves (LN1 -> ctx region, LN2 -> ctx
-// region), the attention context and the GELU output are quantised from
-// their bf16 tensors (context -> LN1 region, GELU output -> QKV region).  The
-// GEMMs read layer li's prepared MXFP4 weights.  Quantisation is per 32-value
+// residuals and the QKV and residual GEMM outputs as in the bf16 layer; each
+// GEMM input goes to MXFP4 in a workspace region that is free at that point:
+// the LayerNorms quantise their fp32 output themselves (LN1 -> ctx region,
+// LN2 -> ctx region), fc1's epilogue quantises GELU(.) (-> QKV region), and
+// the attention context is quantised from its bf16 tensor (-> LN1 region).
+// The GEMMs read layer li's prepared MXFP4 weights.  Quantisation is per 32-value
 // block of a row, so rows stay independent (packed == each sequence alone,
 // padding rows never mix in).
 esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, const bf16_t* x_in, bf16_t* x_out,
@@ -379,7 +379,6 @@ esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, 
   bf16_t* qkv = region<bf16_t>(ws, p, ESM_WS_QKV);
   bf16_t* ctx = region<bf16_t>(ws, p, ESM_WS_CTX);
   bf16_t* x1 = region<bf16_t>(ws, p, ESM_WS_X1);
-  bf16_t* act = region<bf16_t>(ws, p, ESM_WS_ACT);
   const int32_t* pos = region<int32_t>(ws, p, ESM_WS_POS);
   const uint8_t* w4 = e->w4 + (size_t)li * e->w4_layer;
   const W4Off wo = w4_offsets(c);
@@ -445,10 +444,17 @@ esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, 
 
   s = ln_mx(x1, w->ln2_gamma, w->ln2_beta, ctx, "layernorm 2");
   if (s || (s = operands(nullptr, H, ctx, 2))) return s;
-  g.bias = (const bf16_t*)w->b_fc1; g.res = nullptr; g.y = act;
-  g.N = F; g.K = H;
-  s = timed(e, ESM_K_GEMM_FC1, st, "fc1 gemm", [&] { return launch_gemm(EPI_BIAS_GELU, g, st); });
-  if (s || (s = operands(act, F, qkv, 3))) return s;
+  {
+    // fc1's epilogue writes GELU(.) straight to MXFP4 in the QKV region
+    const MxOff ao = mx_operand((size_t)rows, (size_t)F);
+    g.bias = (const bf16_t*)w->b_fc1; g.res = nullptr; g.y = nullptr;
+    g.y8 = (uint8_t*)qkv + ao.codes;
+    g.y_sc = (uint8_t*)qkv + ao.scales;
+    g.N = F; g.K = H;
+    s = timed(e, ESM_K_GEMM_FC1, st, "fc1 gemm", [&] { return launch_gemm(EPI_BIAS_GELU_MX, g, st); });
+    g.y8 = nullptr; g.y_sc = nullptr;
+  }
+  if (s || (s = operands(nullptr, F, qkv, 3))) return s;
   g.bias = (const bf16_t*)w->b_fc2; g.res = x1; g.y = x_out;
   g.N = H; g.K = F;
   return timed(e, ESM_K_GEMM_FC2, st, "fc2 gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });

@@ -126,13 +126,16 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   // the whole tile at once when it fits, else 32-row chunks of every wave's
   // tile (see the epilogue).
   constexpr bool OUT8 = EPI == EPI_BIAS_GELU_E4M3;
-  constexpr int OES = OUT8 ? 1 : 2;               // output bytes per element
-  constexpr int ECH = BM * BN * OES <= 2 * kStage ? WTM : 32;  // staged rows per wave per chunk
+  constexpr bool OUTMX = EPI == EPI_BIAS_GELU_MX;
+  static_assert(!OUTMX || DT == kFP4, "MXFP4 output is built for MXFP4 operands");
+  constexpr int OES = OUT8 ? 1 : 2;               // output bytes per element (bf16, E4M3)
+  constexpr int ORB = OUTMX ? WTN / 2 : WTN * OES;  // output bytes of one row of a wave's tile
+  constexpr int ECH = BM * WAVES_N * ORB <= 2 * kStage ? WTM : 32;  // staged rows per wave per chunk
   static_assert(WTM % ECH == 0, "whole chunks");
   // Residual epilogues stage the residual by direct loads one chunk ahead:
   // two staging buffers when the tile is staged in chunks.
   constexpr int kStageBufs = (EPI == EPI_BIAS_RESIDUAL && ECH < WTM) ? 2 : 1;
-  constexpr int kEpiBytes = kStageBufs * NW * ECH * WTN * OES;
+  constexpr int kEpiBytes = kStageBufs * NW * ECH * ORB;
   static_assert(kEpiBytes <= 2 * kStage, "epilogue staging fits in the K-step stages");
   // MXFP4: both stages' block scales (8 bytes per tile row) after the stages.
   constexpr int kScStage = MX ? (BM + BN) * 8 : 0;
@@ -394,15 +397,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   // operands: the accumulators are first divided by s_x s_w.  E4M3 output:
   // the GELU values are cast with the output's scale, and their amax (before
   // the cast) is recorded.
-  constexpr int CPR = WTN * OES / 16;             // 16-byte chunks per staged row
+  constexpr int CPR = ORB / 16;                   // 16-byte chunks per staged row
   constexpr int RPW = CPR >= 16 ? 1 : 16 / CPR;   // staged rows per 256-byte bank window
   constexpr int PASSES = ECH * CPR / 64;          // 16-byte transfers per lane per chunk
-  constexpr int EPC = 16 / OES;                   // output elements per chunk
+  constexpr int EPC = 16 * WTN / ORB;             // output elements per chunk
   __syncthreads();
   auto stage_at = [&](int c0) {
-    return smem + ((c0 / ECH) % kStageBufs) * (NW * ECH * WTN * OES) + wave * (ECH * WTN * OES);
+    return smem + ((c0 / ECH) % kStageBufs) * (NW * ECH * ORB) + wave * (ECH * ORB);
   };
-  auto soff = [&](int row, int chunk) { return row * (WTN * OES) + ((chunk ^ ((row / RPW) & (CPR - 1))) * 16); };
+  auto soff = [&](int row, int chunk) { return row * ORB + ((chunk ^ ((row / RPW) & (CPR - 1))) * 16); };
   const int64_t mw = m0 + wm * WTM;
   const int nw = n0 + wn * WTN;
   // Residual rows c0 .. c0 + ECH - 1 of the wave tile into their staging
@@ -414,8 +417,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       static_assert(OES == 2 && (ECH * WTN * 2) % 1024 == 0, "whole 1 KB loads of bf16 rows");
       constexpr int RPL = 1024 / (WTN * 2);  // staged rows per direct load
       if (nw >= N) return;
-      const uint32_t base = lds0 + (uint32_t)(((c0 / ECH) % kStageBufs) * (NW * ECH * WTN * OES) +
-                                              wave_u * (ECH * WTN * OES));
+      const uint32_t base = lds0 + (uint32_t)(((c0 / ECH) % kStageBufs) * (NW * ECH * ORB) + wave_u * (ECH * ORB));
 #pragma unroll
       for (int k = 0; k < ECH / RPL; ++k) {
         const int row = k * RPL + lane / CPR;
@@ -512,6 +514,40 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
         *(u32x2*)(stage + soff(row, cl / 8) + 8 * lhalf) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
         *(u32x2*)(stage + soff(row, cl / 8 + 4) + 8 * lhalf) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
       }
+    } else if constexpr (OUTMX) {
+      // GELU straight to MXFP4: the 32 columns of block j of this row are the
+      // 16 of this lane (8 gq + 4 lhalf + e) and the 16 of lane l ^ 32; one
+      // exchange gives the block amax, each lane stages its codes (two bytes
+      // per gq, at byte 16 j + 4 gq + 2 lhalf of the staged row) and the
+      // lhalf = 0 lane writes the block's scale.
+      const int64_t M2 = M + (M & 1);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        float v[4][4];
+        float am = 0.f;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const u32x2 bb = bcache[j][gq];
+          v[gq][0] = acc[i][j][4 * gq + 0] + bflo(bb[0]);
+          v[gq][1] = acc[i][j][4 * gq + 1] + bfhi(bb[0]);
+          v[gq][2] = acc[i][j][4 * gq + 2] + bflo(bb[1]);
+          v[gq][3] = acc[i][j][4 * gq + 3] + bfhi(bb[1]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[gq][e] = gelu(v[gq][e]);
+            am = fmaxf(am, fabsf(v[gq][e]));
+          }
+        }
+        am = fmaxf(am, __shfl_xor(am, 32));
+        const int ex = mx_block_exponent(am);
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const uint32_t c2 = e2m1_pair(v[gq][0], v[gq][1], ex) | (e2m1_pair(v[gq][2], v[gq][3], ex) << 8);
+          *(uint16_t*)(stage + soff(row, j) + 4 * gq + 2 * lhalf) = (uint16_t)c2;
+        }
+        const int nb = nw + j * 32;
+        if (lhalf == 0 && m < M && nb < N) a.y_sc[mx_scale_offset(m, nb / 32, M2)] = (uint8_t)(ex + 127);
+      }
     } else {
       bool zero_row = false;
       if constexpr (EPI == EPI_BIAS_RESIDUAL) zero_row = a.zero_pad_rows && a.pos[mc] < 0;
@@ -567,6 +603,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       *(u32x4*)(a.y + (((int64_t)c * heads + head) * M + m) * kHeadDim + d) = v;
     } else if constexpr (OUT8) {
       *(u32x4*)(a.y8 + m * N + n) = v;
+    } else if constexpr (OUTMX) {
+      *(u32x4*)(a.y8 + m * (N / 2) + n / 2) = v;
     } else {
       *(u32x4*)(a.y + m * N + n) = v;
     }
@@ -615,14 +653,17 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   const int64_t r256 = ((a.M + 255) / 256 * tilesN + cus - 1) / cus;
   const int64_t r320 = ((a.M + 319) / 320 * tilesN + cus - 1) / cus;
   const bool tall = r320 * 320 <= r256 * 256;
-  if (a.dtype == kE4M3)
+  if constexpr (EPI == EPI_BIAS_GELU_MX) {
+    if (a.dtype != kFP4) return hipErrorInvalidValue;
+  } else if (a.dtype == kE4M3) {
     return tall ? run<320, 256, 2, 4, EPI, kE4M3>(a, st) : run<256, 256, 2, 4, EPI, kE4M3>(a, st);
+  }
   if constexpr (EPI == EPI_BIAS_GELU_E4M3) {
     if (a.dtype == kFP4) return hipErrorInvalidValue;
   } else {
     if (a.dtype == kFP4) return run<256, 256, 2, 4, EPI, kFP4>(a, st);
   }
-  if constexpr (EPI == EPI_BIAS_GELU_E4M3) return hipErrorInvalidValue;
+  if constexpr (EPI == EPI_BIAS_GELU_E4M3 || EPI == EPI_BIAS_GELU_MX) return hipErrorInvalidValue;
   else return tall ? run<320, 256, 2, 4, EPI, kBF16>(a, st) : run<256, 256, 2, 4, EPI, kBF16>(a, st);
 }
 
@@ -638,6 +679,7 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st) {
     case EPI_BIAS_RESIDUAL: return dispatch<EPI_BIAS_RESIDUAL>(a, st);
     case EPI_QKV_ROPE: return dispatch<EPI_QKV_ROPE>(a, st);
     case EPI_BIAS_GELU_E4M3: return dispatch<EPI_BIAS_GELU_E4M3>(a, st);
+    case EPI_BIAS_GELU_MX: return dispatch<EPI_BIAS_GELU_MX>(a, st);
   }
   return hipErrorInvalidValue;
 }
