@@ -107,10 +107,8 @@ def bf16_round(x) -> np.ndarray:
 
 def layer_forward_mxfp4(x, cu_seqlens, w, heads: int):
     """One pre-LN layer with MXFP4 GEMMs: each linear is mx(a) . mx(W)^T + b,
-    quantised per 32-value block along K, W (bf16 values) likewise.  The
-    LayerNorm and GELU outputs are quantised as computed; the attention
-    context is first rounded to bf16, the tensor the layer stores it in.
-    Everything else as in the plain fp64 layer."""
+    the input a quantised as computed, per 32-value block along K, and W (bf16
+    values) likewise.  Everything else as in the plain fp64 layer."""
     from . import esm_oracle as O
     x = np.asarray(x, np.float64)
     T, H = x.shape
@@ -125,7 +123,7 @@ def layer_forward_mxfp4(x, cu_seqlens, w, heads: int):
     q, k, v = O.split_qkv(lin(h1, "w_qkv", "b_qkv", 3 * H), heads)
     pos = O.positions(cu_seqlens)
     ctx = O.attention(O.apply_rope(q, pos), O.apply_rope(k, pos), v, cu_seqlens)
-    x1 = x + lin(bf16_round(ctx), "w_out", "b_out", H)
+    x1 = x + lin(ctx, "w_out", "b_out", H)
     h2 = O.layer_norm(x1, w["ln2_gamma"], w["ln2_beta"])
     a = O.gelu(lin(h2, "w_fc1", "b_fc1", F))
     return x1 + lin(a, "w_fc2", "b_fc2", H)

@@ -405,6 +405,32 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
     record_amax_block<kNW>(a.ctx8.amax, amax, red);
     return;
   }
+  if (a.ctx_mx) {
+    // MXFP4 context for the MXFP4 out-projection: block d of this head's 64
+    // dims is this lane's 16 (d * 32 + 8 gq + 4 lhalf + e) and the 16 of lane
+    // l ^ 32; codes of dims 8 gq + 4 lhalf + (0..3) are bytes 16 d + 4 gq +
+    // 2 lhalf (+1) of the head's 32 code bytes.
+    const int64_t M2 = T + (T & 1);
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      float am = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(o[d][r] * inv));
+      am = fmaxf(am, __shfl_xor(am, 32));
+      const int ex = mx_block_exponent(am);
+      if (qrow < L) {
+        uint8_t* dst = a.ctx_mx + (start + qrow) * (H / 2) + head * (kHeadDim / 2) + 16 * d + 2 * lhalf;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const uint32_t c2 = e2m1_pair(o[d][4 * gq] * inv, o[d][4 * gq + 1] * inv, ex) |
+                              (e2m1_pair(o[d][4 * gq + 2] * inv, o[d][4 * gq + 3] * inv, ex) << 8);
+          *(uint16_t*)(dst + 4 * gq) = (uint16_t)c2;
+        }
+        if (lhalf == 0) a.ctx_mx_sc[mx_scale_offset(start + qrow, 2 * head + d, M2)] = (uint8_t)(ex + 127);
+      }
+    }
+    return;
+  }
   if (qrow >= L) return;
   bf16_t* dst = a.ctx + (start + qrow) * H + head * kHeadDim;
 #pragma unroll

@@ -239,6 +239,8 @@ struct AttnArgs {
   const bf16_t* qkv;      // [3, heads, T, 64]
   bf16_t* ctx;            // [T, heads*64]
   E4m3Out ctx8;           // when ctx8.y is set: E4M3 context instead of ctx
+  uint8_t* ctx_mx;        // when set: MXFP4 context codes [T, H / 2] instead of ctx ...
+  uint8_t* ctx_mx_sc;     // ... and their block scales (esm_mxfp4_quantize layout, K = H)
   const int32_t* segs;    // [B, 2]
   const int32_t* tiles;   // [cap, 2]
   const int32_t* ntiles;  // [1]

@@ -362,13 +362,12 @@ esm_status run_segments(esm_encoder* e, int layout, const int32_t* lens, int32_t
   });
 }
 
-// One pre-LN layer with MXFP4 GEMMs (the FP4 recipe): attention, the
-// residuals and the QKV and residual GEMM outputs as in the bf16 layer; each
-// GEMM input goes to MXFP4 in a workspace region that is free at that point:
-// the LayerNorms quantise their fp32 output themselves (LN1 -> ctx region,
-// LN2 -> ctx region), fc1's epilogue quantises GELU(.) (-> QKV region), and
-// the attention context is quantised from its bf16 tensor (-> LN1 region).
-// The GEMMs read layer li's prepared MXFP4 weights.  Quantisation is per 32-value
+// One pre-LN layer with MXFP4 GEMMs (the FP4 recipe): the residuals and the
+// QKV and residual GEMM outputs as in the bf16 layer; each GEMM input is
+// written in MXFP4 by its producer, from fp32 values, into a workspace region
+// that is free at that point: LN1 -> ctx region, the attention context -> LN1
+// region, LN2 -> ctx region, fc1's GELU(.) -> QKV region.  The GEMMs read
+// layer li's prepared MXFP4 weights.  Quantisation is per 32-value
 // block of a row, so rows stay independent (packed == each sequence alone,
 // padding rows never mix in).
 esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, const bf16_t* x_in, bf16_t* x_out,
@@ -430,13 +429,19 @@ esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, 
   AttnArgs aa{};
   aa.qkv = qkv; aa.ctx = ctx;
   aa.ctx8 = none;
+  {
+    // the attention writes its context straight to MXFP4 in the LN1 region
+    const MxOff co = mx_operand((size_t)rows, (size_t)H);
+    aa.ctx_mx = (uint8_t*)ln1 + co.codes;
+    aa.ctx_mx_sc = (uint8_t*)ln1 + co.scales;
+  }
   aa.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
   aa.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
   aa.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
   aa.tile_cap = tile_cap(rows, B);
   aa.T = rows; aa.heads = heads;
   s = timed(e, ESM_K_ATTENTION, st, "attention", [&] { return launch_attention(aa, st); });
-  if (s || (s = operands(ctx, H, ln1, 1))) return s;
+  if (s || (s = operands(nullptr, H, ln1, 1))) return s;
   g.bias = (const bf16_t*)w->b_out; g.res = x_in; g.y = x1;
   g.N = H; g.K = H;
   s = timed(e, ESM_K_GEMM_OUT, st, "out-proj gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
