@@ -500,7 +500,7 @@ esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, int32_t li, con
 
   s = timed(e, ESM_K_LAYERNORM, st, "layernorm 1", [&] {
     return launch_layernorm(x_in, (const bf16_t*)w->ln1_gamma, (const bf16_t*)w->ln1_beta, ln1, rows, H,
-                            c.layer_norm_eps, q8(ln1, 0, pos), st);
+                            c.layer_norm_eps, q8(ln1, 0, zero_pad_rows ? pos : nullptr), st);
   });
   if (s) return s;
 
@@ -543,7 +543,7 @@ esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, int32_t li, con
 
   s = timed(e, ESM_K_LAYERNORM, st, "layernorm 2", [&] {
     return launch_layernorm(x1, (const bf16_t*)w->ln2_gamma, (const bf16_t*)w->ln2_beta, ln2, rows, H,
-                            c.layer_norm_eps, q8(ln2, 2, pos), st);
+                            c.layer_norm_eps, q8(ln2, 2, zero_pad_rows ? pos : nullptr), st);
   });
   if (s) return s;
 
