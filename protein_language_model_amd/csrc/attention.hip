@@ -30,6 +30,13 @@
 //  * Key rows past the end of the sequence are clamped to its last row (never a
 //    neighbour's row) and their scores set to -inf; query rows past the end are
 //    computed from a clamped row and not stored.
+//  * The context leaves as bf16, as E4M3 with the FP8 recipe's delayed scale
+//    and amax, or as MXFP4 codes and block scales for an MXFP4 out-projection.
+//
+// The same body (attend<mode>) serves the biased attention of the
+// DeepSpeed4Science page ([DS4SCI] 3.2, 5.3): q, k, v [B, N, L, heads, 64]
+// with a per-key mask bias and a pair bias added to the scores
+// (k_biased_attention below).
 #include "common.h"
 
 namespace esm {
