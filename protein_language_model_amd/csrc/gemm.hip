@@ -138,8 +138,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   constexpr int kEpiBytes = kStageBufs * NW * ECH * ORB;
   static_assert(kEpiBytes <= 2 * kStage, "epilogue staging fits in the K-step stages");
   // MXFP4: both stages' block scales (8 bytes per tile row) after the stages.
-  constexpr int kScStage = MX ? (BM + BN) * 8 : 0;
-  static_assert(!MX || (BM % 128 == 0 && BN % 128 == 0), "scale rows load in 1 KB pieces of 128 rows");
+  // The x rows' region is rounded up to whole 128-row pieces (rows past the
+  // tile are loaded clamped and never read).
+  constexpr int kScRowsX = (BM + 127) / 128 * 128;
+  constexpr int kScStage = MX ? (kScRowsX + BN) * 8 : 0;
+  static_assert(!MX || BN % 128 == 0, "weight scale rows load in 1 KB pieces of 128 rows");
   constexpr int kSmem = 2 * kStage + 2 * kScStage;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem];
 
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   [[maybe_unused]] const int64_t M2 = M + (M & 1);
   auto issue_scales = [&](int s, int buf) {
     if constexpr (MX) {
-      constexpr int PX = BM / 128, PW = BN / 128;
+      constexpr int PX = kScRowsX / 128, PW = BN / 128;
       static_assert(PX + PW <= NW, "one scale piece per wave");
       if (wave_u < PX + PW) {
         const bool isx = wave_u < PX;
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
         const int64_t rows2 = isx ? M2 : (int64_t)N;
         r = r < rows2 ? r : rows2 - 2;
         const uint8_t* src = (isx ? a.x_sc + (int64_t)s * M2 * 8 : a.w_sc + (int64_t)s * N * 8) + r * 8;
-        const uint32_t dst = lds0 + (uint32_t)(2 * kStage + buf * kScStage + (isx ? 0 : BM * 8) + piece * 1024);
+        const uint32_t dst = lds0 + (uint32_t)(2 * kStage + buf * kScStage + (isx ? 0 : kScRowsX * 8) + piece * 1024);
         lds_dma16(src, dst);
       }
     }
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 #pragma unroll
       for (int i = 0; i < FM; ++i) xsc[i] = *(const uint32_t*)(sb + (wm * WTM + i * 32 + lrow) * 8 + 4 * lhalf);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) wsc[j] = *(const uint32_t*)(sb + (BM + wn * WTN + j * 32 + lrow) * 8 + 4 * lhalf);
+      for (int j = 0; j < FN; ++j) wsc[j] = *(const uint32_t*)(sb + (kScRowsX + wn * WTN + j * 32 + lrow) * 8 + 4 * lhalf);
     }
   };
   auto mfma_step_mx = [&](const frag_t (&xf)[FM], const frag_t (&wf)[FN], int kk) {
@@ -661,7 +664,7 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   if constexpr (EPI == EPI_BIAS_GELU_E4M3) {
     if (a.dtype == kFP4) return hipErrorInvalidValue;
   } else {
-    if (a.dtype == kFP4) return run<256, 256, 2, 4, EPI, kFP4>(a, st);
+    if (a.dtype == kFP4) return tall ? run<320, 256, 2, 4, EPI, kFP4>(a, st) : run<256, 256, 2, 4, EPI, kFP4>(a, st);
   }
   if constexpr (EPI == EPI_BIAS_GELU_E4M3 || EPI == EPI_BIAS_GELU_MX) return hipErrorInvalidValue;
   else return tall ? run<320, 256, 2, 4, EPI, kBF16>(a, st) : run<256, 256, 2, 4, EPI, kBF16>(a, st);

@@ -189,3 +189,29 @@ def test_mxfp4_encoder_rejects_unprepared_layers_and_bad_shapes(gu):
     with pytest.raises(esm.EsmError):   # 320 is not a multiple of 256
         esm.Encoder(hidden_size=320, num_attention_heads=5, intermediate_size=1280, num_hidden_layers=1,
                     precision="mxfp4")
+
+
+@pytest.mark.parametrize("epi", [esm.EPI_BIAS_RESIDUAL, esm.EPI_BIAS_GELU])
+def test_mxfp4_linear_tall_tiles_sampled(enc, gu, epi):
+    """M = 32293, N = 1280: the GEMM takes 320-row tiles (fewer rounds of
+    workgroups); sampled rows, the last partial tile included, against the
+    oracle on the same rows (rows are independent)."""
+    from oracle import esm_oracle as O
+    M, N, K = 32293, 1280, 512
+    rng = np.random.default_rng(17)
+    xb = D.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    wb = D.to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    bb = D.to_bf16_bits((rng.standard_normal(N) * 0.02).astype(np.float32))
+    rb = D.to_bf16_bits(rng.standard_normal((M, N)).astype(np.float32))
+    res = gu.to_dev_bf16(rb) if epi == esm.EPI_BIAS_RESIDUAL else None
+    got = gu.from_dev(enc.linear_mxfp4_fwd(enc.mxfp4_quantize(gu.to_dev_bf16(xb)), enc.mxfp4_quantize(gu.to_dev_bf16(wb)),
+                                           gu.to_dev_bf16(bb), residual=res, epilogue=epi))
+    rows = np.unique(np.concatenate([np.arange(0, 640), rng.integers(0, M, 1500), np.arange(M - 400, M)]))
+    ref = F.mx_matmul(*F.mx_quantize(D.bf16_bits_to_f64(xb[rows])), *F.mx_quantize(D.bf16_bits_to_f64(wb)))
+    ref = ref + D.bf16_bits_to_f64(bb)
+    if epi == esm.EPI_BIAS_GELU:
+        ref = O.gelu(ref)
+    else:
+        ref = ref + D.bf16_bits_to_f64(rb[rows])
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-5 * np.abs(ref).max()
+    assert np.all(np.abs(got[rows] - ref) <= bound), np.abs(got[rows] - ref).max()
