@@ -41,6 +41,11 @@ Readings where the pages are silent (each is listed in the design notes):
   stack (head_forward): final LayerNorm, the ESM-2 masked-LM head with the
   decoder tied to the embedding, and per-sequence mean embeddings.
 
+attention_lse and attention_bwd give the softmax normaliser a backward pass
+keeps and the gradients of the attention with respect to q, k and v: the
+backward of the training runs the pages time ([BIO-ACC] 3.2 and 6, [CARD]
+训练性能).
+
 A second, separate function, biased_attention, is the Evoformer attention of
 [DS4SCI]: softmax(q k^T / sqrt(D) + mask bias + pair bias) v per (b, n, h) on
 [B, N, L, H, D] tensors (the scale is a reading; the page does not state it).
@@ -177,6 +182,49 @@ def attention(q, k, v, cu_seqlens, scale: float = SOFTMAX_SCALE) -> np.ndarray:
             P = attention_probs(q[a:b, n], k[a:b, n], scale)
             ctx[a:b, n] = P @ v[a:b, n]
     return ctx.reshape(T, heads * d)
+
+
+def attention_lse(q, k, cu_seqlens, scale: float = SOFTMAX_SCALE) -> np.ndarray:
+    """Natural-log softmax normaliser of every row: lse[n, t] =
+    log sum_j exp(scale q_t . k_j) over the keys j of t's sequence; q, k
+    [T, heads, 64] -> [heads, T].  Evaluated as max + log(sum exp(s - max))."""
+    T, heads, _ = q.shape
+    lse = np.zeros((heads, T), np.float64)
+    for a, b in segments(cu_seqlens):
+        for n in range(heads):
+            S = (q[a:b, n] @ k[a:b, n].T) * scale
+            m = S.max(axis=1)
+            lse[n, a:b] = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+    return lse
+
+
+def attention_bwd(q, k, v, dctx, cu_seqlens, scale: float = SOFTMAX_SCALE):
+    """Gradients of sum(dctx * attention(q, k, v)) with respect to q, k and v
+    (the backward pass of the training runs the pages time: [BIO-ACC] 3.2 and 6,
+    [CARD] 训练性能; written
+    out by the chain rule on the forward above).  Per (sequence, head), with
+    S = scale q k^T, P = softmax_rows(S), O = P v and dO the incoming gradient:
+        dv = P^T dO
+        dP = dO v^T
+        dS = P * (dP - rowsum(P * dP))          (softmax Jacobian, row by row)
+        dq = scale dS k,   dk = scale dS^T q.
+    q, k, v [T, heads, 64], dctx [T, heads * 64] -> dq, dk, dv [T, heads, 64]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    T, heads, d = q.shape
+    dO = np.asarray(dctx, np.float64).reshape(T, heads, d)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for a, b in segments(cu_seqlens):
+        for n in range(heads):
+            P = attention_probs(q[a:b, n], k[a:b, n], scale)
+            g = dO[a:b, n]
+            dv[a:b, n] = P.T @ g
+            dP = g @ v[a:b, n].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dq[a:b, n] = scale * (dS @ k[a:b, n])
+            dk[a:b, n] = scale * (dS.T @ q[a:b, n])
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------

@@ -1,0 +1,113 @@
+"""Pins of the oracle's attention backward and softmax normaliser
+(oracle/esm_oracle.py: attention_bwd, attention_lse), against things other
+than the oracle's own formulas:
+
+* central finite differences of the forward loss sum(dO * attention(q, k, v))
+  (the definition of the gradient), on tiny ragged batches;
+* exact identities of the softmax Jacobian: every row of dS sums to zero, so
+  the keys' dk of one (sequence, head) sum to zero; every row of P sums to
+  one, so the keys' dv sum to the queries' dO;
+* special cases: a one-residue sequence (P = 1: dq = dk = 0, dv = dO), equal
+  keys (uniform P), and no coupling across sequences;
+* the normaliser by a brute-force exact sum (math.fsum of exp) on tiny rows.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import esm_oracle as O
+
+D = 64
+
+
+def _inputs(lens, heads, seed):
+    rng = np.random.default_rng(seed)
+    T = sum(lens)
+    q = rng.standard_normal((T, heads, D))
+    k = rng.standard_normal((T, heads, D))
+    v = rng.standard_normal((T, heads, D))
+    g = rng.standard_normal((T, heads * D))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return q, k, v, g, cu
+
+
+def _loss(q, k, v, g, cu):
+    return float(np.sum(g * O.attention(q, k, v, cu)))
+
+
+@pytest.mark.parametrize("lens,heads,seed", [([3, 5], 2, 0), ([1, 4, 2], 1, 1), ([6], 3, 2)])
+def test_bwd_matches_finite_differences(lens, heads, seed):
+    q, k, v, g, cu = _inputs(lens, heads, seed)
+    dq, dk, dv = O.attention_bwd(q, k, v, g, cu)
+    rng = np.random.default_rng(100 + seed)
+    h = 1e-5
+    for x, dx in ((q, dq), (k, dk), (v, dv)):
+        flat = x.reshape(-1)
+        for i in rng.choice(flat.size, size=24, replace=False):
+            old = flat[i]
+            flat[i] = old + h
+            lp = _loss(q, k, v, g, cu)
+            flat[i] = old - h
+            lm = _loss(q, k, v, g, cu)
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            # central difference error O(h^2 |f'''|) plus rounding eps |f| / h
+            assert abs(fd - dx.reshape(-1)[i]) <= 1e-7 * max(1.0, abs(fd)), (i, fd, dx.reshape(-1)[i])
+
+
+def test_bwd_key_sums():
+    lens, heads = [7, 1, 12], 3
+    q, k, v, g, cu = _inputs(lens, heads, 3)
+    dq, dk, dv = O.attention_bwd(q, k, v, g, cu)
+    dO = g.reshape(-1, heads, D)
+    for a, b in O.segments(cu):
+        np.testing.assert_allclose(dk[a:b].sum(axis=0), 0.0, atol=1e-12)
+        np.testing.assert_allclose(dv[a:b].sum(axis=0), dO[a:b].sum(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_single_residue_and_equal_keys():
+    # one residue: P = [[1]], the softmax Jacobian vanishes
+    q, k, v, g, cu = _inputs([1], 2, 4)
+    dq, dk, dv = O.attention_bwd(q, k, v, g, cu)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    np.testing.assert_array_equal(dv, g.reshape(1, 2, D))
+    # all keys equal: P uniform (1 / L), so dq = scale * rowsum(dS) k = 0 and
+    # every dv[j] = mean over the queries of dO
+    L = 5
+    q, k, v, g, cu = _inputs([L], 1, 5)
+    k[:] = k[0]
+    dq, dk, dv = O.attention_bwd(q, k, v, g, cu)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-12)
+    np.testing.assert_allclose(dv[:, 0], np.repeat(g.mean(axis=0, keepdims=True), L, 0), rtol=1e-12, atol=1e-12)
+
+
+def test_bwd_no_coupling_across_sequences():
+    lens, heads = [4, 6], 2
+    q, k, v, g, cu = _inputs(lens, heads, 6)
+    base = O.attention_bwd(q, k, v, g, cu)
+    q2, k2, v2, g2 = q.copy(), k.copy(), v.copy(), g.copy()
+    rng = np.random.default_rng(7)
+    for x in (q2, k2, v2):
+        x[4:] = rng.standard_normal(x[4:].shape)
+    g2[4:] = rng.standard_normal(g2[4:].shape)
+    moved = O.attention_bwd(q2, k2, v2, g2, cu)
+    for a, b in zip(base, moved):
+        np.testing.assert_array_equal(a[:4], b[:4])
+
+
+def test_lse_brute_force():
+    lens, heads = [3, 5], 2
+    q, k, _, _, cu = _inputs(lens, heads, 8)
+    lse = O.attention_lse(q, k, cu)
+    for a, b in O.segments(cu):
+        for n in range(heads):
+            for t in range(a, b):
+                terms = [math.exp(O.SOFTMAX_SCALE * sum(q[t, n, i] * k[j, n, i] for i in range(D)))
+                         for j in range(a, b)]
+                assert abs(lse[n, t] - math.log(math.fsum(terms))) <= 1e-12 * max(1.0, abs(lse[n, t]))
+    # exp(S - lse) is the attention's P
+    a, b = 3, 8
+    S = q[a:b, 1] @ k[a:b, 1].T * O.SOFTMAX_SCALE
+    np.testing.assert_allclose(np.exp(S - lse[1, a:b, None]), O.attention_probs(q[a:b, 1], k[a:b, 1]),
+                               rtol=1e-12)
