@@ -191,6 +191,8 @@ def attention_lse(q, k, cu_seqlens, scale: float = SOFTMAX_SCALE) -> np.ndarray:
     T, heads, _ = q.shape
     lse = np.zeros((heads, T), np.float64)
     for a, b in segments(cu_seqlens):
+        if b == a:          # an empty sequence has no rows
+            continue
         for n in range(heads):
             S = (q[a:b, n] @ k[a:b, n].T) * scale
             m = S.max(axis=1)
@@ -216,6 +218,8 @@ def attention_bwd(q, k, v, dctx, cu_seqlens, scale: float = SOFTMAX_SCALE):
     dO = np.asarray(dctx, np.float64).reshape(T, heads, d)
     dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     for a, b in segments(cu_seqlens):
+        if b == a:          # an empty sequence has no rows
+            continue
         for n in range(heads):
             P = attention_probs(q[a:b, n], k[a:b, n], scale)
             g = dO[a:b, n]

@@ -111,3 +111,13 @@ def test_lse_brute_force():
     S = q[a:b, 1] @ k[a:b, 1].T * O.SOFTMAX_SCALE
     np.testing.assert_allclose(np.exp(S - lse[1, a:b, None]), O.attention_probs(q[a:b, 1], k[a:b, 1]),
                                rtol=1e-12)
+
+
+def test_empty_sequences_change_nothing():
+    """Empty sequences (zero-length segments) add no rows: the results equal
+    those of the batch without them."""
+    q, k, v, g, cu = _inputs([3, 4], 2, 9)
+    cu_e = np.array([0, 0, 3, 3, 7, 7])
+    for a, b in zip(O.attention_bwd(q, k, v, g, cu), O.attention_bwd(q, k, v, g, cu_e)):
+        np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(O.attention_lse(q, k, cu), O.attention_lse(q, k, cu_e))
