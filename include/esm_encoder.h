@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 9
+#define ESM_ABI_VERSION 10
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -279,6 +279,36 @@ esm_status esm_attention_fwd(esm_encoder* enc, const void* qkv, void* ctx,
                              const int32_t* cu_seqlens_dev, int32_t B, int64_t T,
                              void* workspace, size_t workspace_bytes, esm_stream_t stream);
 
+/* Attention with its softmax normaliser, for a backward pass: as
+ * esm_attention_fwd, and also lse[n * T + t] = log sum_j exp(q_t . k_j / 8)
+ * over the keys j of t's sequence (natural log, fp32, head-major [heads, T]).
+ * lse: device, 4-byte aligned, written for every row of every sequence.
+ * Errors as esm_attention_fwd; ESM_ERR_NULL for lse NULL. */
+esm_status esm_attention_fwd_lse(esm_encoder* enc, const void* qkv, void* ctx, float* lse,
+                                 const int32_t* cu_seqlens_dev, int32_t B, int64_t T,
+                                 void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* Attention backward (the gradient of the forward above; the pages time
+ * training, [BIO-ACC] 3.2 and 6, [CARD] 训练性能).  For each sequence and head,
+ * with S = q k^T / 8, P = exp(S - lse) and dO = the gradient of the context:
+ *   dv = P^T dO,  dP = dO v^T,  dS = P * (dP - rowsum(dO * O)),
+ *   dq = dS k / 8,  dk = dS^T q / 8.
+ * qkv:   bf16 [3, heads, T, 64], the forward's input (q and k rotated).
+ * ctx:   bf16 [T, H], the forward's context O; dctx: bf16 [T, H], dO.
+ * lse:   fp32 [heads, T] from esm_attention_fwd_lse on the same qkv.
+ * delta: fp32 [heads, T] device scratch, overwritten (rowsum(dO * O)).
+ * dqkv:  bf16 [3, heads, T, 64] out (dq, dk, dv in qkv's layout); must not
+ *        overlap the inputs.
+ * Tensors 16-byte aligned, lse and delta 4-byte aligned.  P is recomputed from
+ * lse (never stored); P and dS enter their products as bf16 with fp32
+ * accumulation.  Runs the segment table first (workspace as
+ * esm_attention_fwd).  Errors: ESM_ERR_NULL, ESM_ERR_UNSUPPORTED (alignment),
+ * ESM_ERR_SHAPE / ESM_ERR_WORKSPACE as esm_attention_fwd.  Asynchronous. */
+esm_status esm_attention_bwd(esm_encoder* enc, const void* qkv, const void* ctx, const void* dctx,
+                             const float* lse, float* delta, void* dqkv,
+                             const int32_t* cu_seqlens_dev, int32_t B, int64_t T,
+                             void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
 /* Biased attention ([DS4SCI] 3.2 and 5.3: the Evoformer attention kernel,
  * which takes Q, K, V shaped [B, N, L, heads, D] and up to two additive
  * biases, a per-key mask bias [B, N, 1, 1, L] and a pair bias
@@ -450,7 +480,8 @@ typedef enum {
   ESM_K_ATTENTION = 4, ESM_K_GEMM_OUT = 5, ESM_K_GEMM_FC1 = 6, ESM_K_GEMM_FC2 = 7,
   ESM_K_OTHER = 8, ESM_K_FP8 = 9 /* weight casts, scale updates */,
   ESM_K_HEAD = 10 /* final LayerNorm, LM head, sequence means */,
-  ESM_K_BIASED_ATTENTION = 11 /* esm_biased_attention_fwd */, ESM_K_COUNT = 12
+  ESM_K_BIASED_ATTENTION = 11 /* esm_biased_attention_fwd */,
+  ESM_K_ATTENTION_BWD = 12 /* esm_attention_bwd */, ESM_K_COUNT = 13
 } esm_kernel_class;
 
 /* When on, every launch is bracketed by HIP events recorded on the launch

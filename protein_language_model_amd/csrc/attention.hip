@@ -84,12 +84,13 @@ __device__ __forceinline__ int kSwzB(int r) { return (r >> 1) & 7; }
 // 64 contiguous values at + r * rs.  Biased modes add maskg[c] and
 // pairg[r * L + c] to the score of (query row r, key c).  On return o holds
 // this lane's unnormalised context (dims d * 32 + 8 g + 4 lhalf + e in
-// o[d][4 g + e]) and inv the reciprocal of its softmax sum.
+// o[d][4 g + e]), inv the reciprocal of its softmax sum and mrow the largest
+// raw score of its row (q.k, before the scale; the biased modes: the score).
 template <int kMode>
 __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg,
                                        const bf16_t* __restrict__ Vg, const int64_t rs, const int L, const int q0,
                                        const bf16_t* __restrict__ maskg, const bf16_t* __restrict__ pairg,
-                                       f32x16 (&o)[2], float& inv) {
+                                       f32x16 (&o)[2], float& inv, float& mrow) {
   constexpr bool kStaged = (kMode & kLds) != 0;
   constexpr int kSubM = kStaged ? 1 : kSub;        // compute tiles per LDS tile
   constexpr int kLTM = kKT * kSubM;                // keys per LDS tile
@@ -365,6 +366,7 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
 
   const float lt = l_i + __shfl_xor(l_i, 32);
   inv = 1.0f / lt;
+  mrow = m_i;
 }
 
 // Encoder attention: one workgroup per (256-row query tile, head) from the
@@ -383,12 +385,15 @@ __global__ __launch_bounds__(64 * kNW) void k_attention(AttnArgs a) {
   const bf16_t* Kg = a.qkv + ((int64_t)(1 * heads + head) * T + start) * kHeadDim;
   const bf16_t* Vg = a.qkv + ((int64_t)(2 * heads + head) * T + start) * kHeadDim;
   f32x16 o[2];
-  float inv;
-  attend<kPlain>(Qg, Kg, Vg, kHeadDim, L, q0, nullptr, nullptr, o, inv);
+  float inv, mrow;
+  attend<kPlain>(Qg, Kg, Vg, kHeadDim, L, q0, nullptr, nullptr, o, inv, mrow);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lhalf = lane >> 5;
   const int qrow = q0 + 32 * wave + (lane & 31);
   const int H = heads * kHeadDim;
+  // The softmax normaliser a backward pass takes: log sum_j exp(q.k_j / 8)
+  // = max / 8 + log(sum_j exp((q.k_j - max) / 8)).
+  if (a.lse && lhalf == 0 && qrow < L) a.lse[(int64_t)head * T + start + qrow] = mrow * 0.125f - logf(inv);
   if (a.ctx8.y) {
     // E4M3 context for the FP8 out-projection: cast with the tensor's delayed
     // scale, amax over the valid rows recorded by every lane of the wave.
@@ -469,8 +474,8 @@ void k_biased_attention(BiasedAttnArgs a) {
   const bf16_t* maskg = (kMode & kMask) ? a.mask + bn * L : nullptr;
   const bf16_t* pairg = (kMode & kPair) ? a.pair + (b * heads + h) * (int64_t)L * L : nullptr;
   f32x16 o[2];
-  float inv;
-  attend<kMode>(a.q + base, a.k + base, a.v + base, rs, L, q0, maskg, pairg, o, inv);
+  float inv, mrow;
+  attend<kMode>(a.q + base, a.k + base, a.v + base, rs, L, q0, maskg, pairg, o, inv, mrow);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, lhalf = lane >> 5;
   const int qrow = q0 + 32 * wave + (lane & 31);
@@ -486,7 +491,402 @@ void k_biased_attention(BiasedAttnArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ backward
+//
+// Gradients of the encoder attention with respect to q, k and v, from the
+// forward's context O and softmax normaliser lse, for an incoming gradient dO
+// of the context.  Per (sequence, head), with S = q k^T / 8 and
+// P = exp(S - lse):  dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D) with
+// D = rowsum(dO * O) (= rowsum(P * dP)),  dQ = dS K / 8,  dK = dS^T Q / 8.
+// P is recomputed from lse, never stored.  Three kernels:
+//  * k_attn_bwd_delta: D for every (head, row), 8 lanes per row;
+//  * k_attn_bwd_dkv: one workgroup per 256 keys of one sequence and head (8
+//    waves x 32 keys, K and V rows in registers as the MFMAs' B operand),
+//    streaming the sequence's queries in 64-row tiles of Q and dO through LDS
+//    (direct loads, double-buffered, the forward's swizzle) with their lse
+//    and D; S and dP come out query x key, so each lane owns one key and the
+//    products accumulate dV^T and dK^T in registers: no atomics;
+//  * k_attn_bwd_dq: one workgroup per 256 queries, the forward's structure
+//    with dP added: K and V tiles in LDS, S^T and dP^T key x query, and
+//    dQ^T += K^T dS^T with K^T read by the transposing LDS reads.
+// P and dS enter the second products as bf16 (fp32 accumulation), as P does
+// in the forward.
+
+struct AttnBwdPtrs {
+  const bf16_t* Q;    // row 0 of the sequence, head; row stride 64
+  const bf16_t* K;
+  const bf16_t* V;
+  const bf16_t* dO;   // row stride H
+  const float* lse;   // [L] of this head
+  const float* del;   // [L] of this head
+};
+
+__device__ __forceinline__ AttnBwdPtrs bwd_ptrs(const AttnBwdArgs& a, int head, int64_t start) {
+  const int64_t T = a.T;
+  AttnBwdPtrs p;
+  p.Q = a.qkv + ((int64_t)(0 * a.heads + head) * T + start) * kHeadDim;
+  p.K = a.qkv + ((int64_t)(1 * a.heads + head) * T + start) * kHeadDim;
+  p.V = a.qkv + ((int64_t)(2 * a.heads + head) * T + start) * kHeadDim;
+  p.dO = a.dout + start * ((int64_t)a.heads * kHeadDim) + head * kHeadDim;
+  p.lse = a.lse + (int64_t)head * T + start;
+  p.del = a.delta + (int64_t)head * T + start;
+  return p;
+}
+
+// D[head, t] = sum_d dO[t, head, d] * O[t, head, d]: 8 lanes per (t, head),
+// 16 bytes of each tensor per lane.
+__global__ __launch_bounds__(256) void k_attn_bwd_delta(AttnBwdArgs a) {
+  const int64_t g = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;
+  const int part = threadIdx.x & 7;
+  const bool live = g < a.T * a.heads;
+  const int64_t t = live ? g / a.heads : 0;
+  const int head = live ? (int)(g % a.heads) : 0;
+  float acc = 0.f;
+  if (live) {
+    const int64_t off = t * ((int64_t)a.heads * kHeadDim) + head * kHeadDim + part * 8;
+    const u32x4 o = *(const u32x4*)(a.out + off);
+    const u32x4 d = *(const u32x4*)(a.dout + off);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += bflo(o[e]) * bflo(d[e]) + bfhi(o[e]) * bfhi(d[e]);
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (live && part == 0) a.delta[(int64_t)head * a.T + t] = acc;
+}
+
+constexpr int kBT = 64;  // rows per streamed LDS tile in the backward kernels
+
+// 64 rows x 128 bytes of a row-major tensor (row stride rs elements) into a
+// swizzled LDS tile: wave w fetches rows 8w .. 8w + 7, lane l physical chunk
+// l % 8 of row 8w + l / 8, i.e. logical chunk (l % 8) ^ kSwz(row).  Rows past
+// the end of the sequence are clamped to its last row.
+__device__ __forceinline__ void tile_dma(const bf16_t* __restrict__ g, int64_t rs, int row0, int L, uint32_t lds,
+                                         int lane, int wave, int wave_u) {
+  const int r = 8 * wave + (lane >> 3);
+  int row = row0 + r;
+  row = row < L ? row : L - 1;
+  lds_dma16(g + row * rs + ((lane & 7) ^ kSwz(r)) * 8, lds + (uint32_t)wave_u * 1024u);
+}
+
+__global__ __launch_bounds__(64 * kNW) void k_attn_bwd_dkv(AttnBwdArgs a) {
+  const int heads = a.heads;
+  const int tile = blockIdx.x / heads, head = blockIdx.x % heads;
+  if (tile >= *a.ntiles) return;
+  const int s = a.tiles[2 * tile], k0 = a.tiles[2 * tile + 1];
+  const int64_t start = a.segs[2 * s];
+  const int L = a.segs[2 * s + 1];
+  if (L <= 0) return;
+  const AttnBwdPtrs p = bwd_ptrs(a, head, start);
+  const int64_t H = (int64_t)heads * kHeadDim;
+
+  __shared__ __attribute__((aligned(1024))) bf16_t sq[2][kBT * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) bf16_t sd[2][kBT * kLdsRow];
+  __shared__ __attribute__((aligned(16))) float sl[2][kBT];   // lse * log2(e); +inf past the end
+  __shared__ __attribute__((aligned(16))) float sD[2][kBT];   // D; 0 past the end
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // This lane's key (clamped): its K and V rows as the B operand, dims
+  // 16 kk + 8 lhalf .. + 7 in register kk.
+  const int key = k0 + 32 * wave + lrow;
+  const int kc = key < L ? key : L - 1;
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    kf[kk] = *(const bf16x8*)(p.K + kc * kHeadDim + kk * 16 + 8 * lhalf);
+    vf[kk] = *(const bf16x8*)(p.V + kc * kHeadDim + kk * 16 + 8 * lhalf);
+  }
+
+  const uint32_t lds_q = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sq[0][0];
+  const uint32_t lds_d = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sd[0][0];
+  auto gload = [&](int j, int buf) {
+    tile_dma(p.Q, kHeadDim, j * kBT, L, lds_q + (uint32_t)buf * kBT * kLdsRow * 2, lane, wave, wave_u);
+    tile_dma(p.dO, H, j * kBT, L, lds_d + (uint32_t)buf * kBT * kLdsRow * 2, lane, wave, wave_u);
+  };
+  auto sload = [&](int j, float& l2, float& dd) {
+    const int q = j * kBT + tid;
+    l2 = q < L ? p.lse[q] * kLog2e : INFINITY;
+    dd = q < L ? p.del[q] : 0.f;
+  };
+
+  const int g16 = lane & 15;
+  const int tr_row = g16 >> 2, tr_col = 4 * (g16 & 3);
+  const int n0_lane = 16 * ((lane >> 4) & 1);
+  int koff[4], voff[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = ((2 * kk + lhalf) ^ kSwz(lrow)) * 8;
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 4 * lhalf + tr_row + 8 * h, col = d * 32 + n0_lane + tr_col;
+      voff[d][h] = (((col >> 3) ^ kSwz(r)) * 8) + (col & 7);
+    }
+
+  f32x16 dv[2], dk[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dv[d][r] = 0.f; dk[d][r] = 0.f; }
+
+  const int ntq = (L + kBT - 1) / kBT;
+  const bool wave_active = k0 + 32 * wave < L;
+  gload(0, 0);
+  if (tid < kBT) {
+    float l2, dd;
+    sload(0, l2, dd);
+    sl[0][tid] = l2;
+    sD[0][tid] = dd;
+  }
+  vm_wait_all();
+  __syncthreads();
+  for (int t = 0; t < ntq; ++t) {
+    const int cur = t & 1;
+    float nl2 = 0.f, ndd = 0.f;
+    if (t + 1 < ntq) {
+      gload(t + 1, cur ^ 1);
+      if (tid < kBT) sload(t + 1, nl2, ndd);
+    }
+    if (wave_active) {
+      const bf16_t* qt = sq[cur];
+      const bf16_t* dt = sd[cur];
+      // S and dP, query x key: block qb holds queries qb*32 + 8*(r/4) +
+      // 4*lhalf + r%4 of this lane's key.
+      f32x16 st[2], dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { st[qb][r] = 0.f; dp[qb][r] = 0.f; }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 qa = *(const bf16x8*)(&qt[(qb * 32 + lrow) * kLdsRow + koff[kk]]);
+          st[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[kk], st[qb], 0, 0, 0);
+          const bf16x8 da = *(const bf16x8*)(&dt[(qb * 32 + lrow) * kLdsRow + koff[kk]]);
+          dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[kk], dp[qb], 0, 0, 0);
+        }
+      }
+      // P = exp2(S log2(e) / 8 - lse log2(e)); dS = P (dP - D).  Queries past
+      // the end have lse = +inf: P = 0, dS = 0.
+      bf16x8 pb[2][2], sb[2][2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int q = qb * 32 + 8 * g + 4 * lhalf;
+          const f32x4 l2 = *(const f32x4*)&sl[cur][q];
+          const f32x4 dd = *(const f32x4*)&sD[cur][q];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pr = exp2_fast(fmaf(st[qb][4 * g + e], kScaleLog2, -l2[e]));
+            st[qb][4 * g + e] = pr;
+            dp[qb][4 * g + e] = pr * (dp[qb][4 * g + e] - dd[e]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          u32x4 w, x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[e] = pack_bf2(st[qb][8 * u + 2 * e], st[qb][8 * u + 2 * e + 1]);
+            x[e] = pack_bf2(dp[qb][8 * u + 2 * e], dp[qb][8 * u + 2 * e + 1]);
+          }
+          pb[qb][u] = __builtin_bit_cast(bf16x8, w);
+          sb[qb][u] = __builtin_bit_cast(bf16x8, x);
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: the transposing reads give lane
+      // (dim d*32 + lane%32) the 8 queries qb*32 + 16u + 4*lhalf + {0..3, 8..11},
+      // the order in which pb / sb hold them.
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            const int r0 = qb * 32 + 16 * u + 4 * lhalf + tr_row;
+            const i16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(dt + r0 * kLdsRow + voff[d][0]));
+            const i16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(dt + (r0 + 8) * kLdsRow + voff[d][1]));
+            const i16x8 dv8 = __builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7);
+            dv[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, dv8), pb[qb][u], dv[d], 0, 0, 0);
+            const i16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(qt + r0 * kLdsRow + voff[d][0]));
+            const i16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(qt + (r0 + 8) * kLdsRow + voff[d][1]));
+            const i16x8 q8 = __builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7);
+            dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q8), sb[qb][u], dk[d], 0, 0, 0);
+          }
+    }
+    if (t + 1 < ntq && tid < kBT) {
+      sl[cur ^ 1][tid] = nl2;
+      sD[cur ^ 1][tid] = ndd;
+    }
+    vm_wait_all();
+    __syncthreads();
+  }
+
+  if (key >= L) return;
+  bf16_t* dkg = a.dqkv + ((int64_t)(1 * heads + head) * a.T + start + key) * kHeadDim;
+  bf16_t* dvg = a.dqkv + ((int64_t)(2 * heads + head) * a.T + start + key) * kHeadDim;
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dim = d * 32 + 8 * g + 4 * lhalf;
+      *(u32x2*)(dkg + dim) = u32x2{pack_bf2(dk[d][4 * g] * 0.125f, dk[d][4 * g + 1] * 0.125f),
+                                   pack_bf2(dk[d][4 * g + 2] * 0.125f, dk[d][4 * g + 3] * 0.125f)};
+      *(u32x2*)(dvg + dim) = u32x2{pack_bf2(dv[d][4 * g], dv[d][4 * g + 1]),
+                                   pack_bf2(dv[d][4 * g + 2], dv[d][4 * g + 3])};
+    }
+}
+
+__global__ __launch_bounds__(64 * kNW) void k_attn_bwd_dq(AttnBwdArgs a) {
+  const int heads = a.heads;
+  const int tile = blockIdx.x / heads, head = blockIdx.x % heads;
+  if (tile >= *a.ntiles) return;
+  const int s = a.tiles[2 * tile], q0 = a.tiles[2 * tile + 1];
+  const int64_t start = a.segs[2 * s];
+  const int L = a.segs[2 * s + 1];
+  if (L <= 0) return;
+  const AttnBwdPtrs p = bwd_ptrs(a, head, start);
+  const int64_t H = (int64_t)heads * kHeadDim;
+
+  __shared__ __attribute__((aligned(1024))) bf16_t sk[2][kBT * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) bf16_t sv[2][kBT * kLdsRow];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // This lane's query (clamped): q and dO rows as the B operand, its lse and D.
+  const int qrow = q0 + 32 * wave + lrow;
+  const int qc = qrow < L ? qrow : L - 1;
+  bf16x8 qf[4], df[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    qf[kk] = *(const bf16x8*)(p.Q + qc * kHeadDim + kk * 16 + 8 * lhalf);
+    df[kk] = *(const bf16x8*)(p.dO + qc * H + kk * 16 + 8 * lhalf);
+  }
+  const float l2 = p.lse[qc] * kLog2e;
+  const float dd = p.del[qc];
+
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sk[0][0];
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sv[0][0];
+  auto gload = [&](int j, int buf) {
+    tile_dma(p.K, kHeadDim, j * kBT, L, lds_k + (uint32_t)buf * kBT * kLdsRow * 2, lane, wave, wave_u);
+    tile_dma(p.V, kHeadDim, j * kBT, L, lds_v + (uint32_t)buf * kBT * kLdsRow * 2, lane, wave, wave_u);
+  };
+
+  const int g16 = lane & 15;
+  const int tr_row = g16 >> 2, tr_col = 4 * (g16 & 3);
+  const int n0_lane = 16 * ((lane >> 4) & 1);
+  int koff[4], voff[2][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) koff[kk] = ((2 * kk + lhalf) ^ kSwz(lrow)) * 8;
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 4 * lhalf + tr_row + 8 * h, col = d * 32 + n0_lane + tr_col;
+      voff[d][h] = (((col >> 3) ^ kSwz(r)) * 8) + (col & 7);
+    }
+
+  f32x16 dq[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[d][r] = 0.f;
+
+  const int ntk = (L + kBT - 1) / kBT;
+  const bool wave_active = q0 + 32 * wave < L;
+  gload(0, 0);
+  vm_wait_all();
+  __syncthreads();
+  for (int t = 0; t < ntk; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < ntk) gload(t + 1, cur ^ 1);
+    if (wave_active) {
+      const bf16_t* kt = sk[cur];
+      const bf16_t* vt = sv[cur];
+      // S^T and dP^T, key x query: block kb holds keys t*64 + kb*32 + 8*(r/4)
+      // + 4*lhalf + r%4 of this lane's query.
+      f32x16 st[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { st[kb][r] = 0.f; dp[kb][r] = 0.f; }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 ka = *(const bf16x8*)(&kt[(kb * 32 + lrow) * kLdsRow + koff[kk]]);
+          st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], st[kb], 0, 0, 0);
+          const bf16x8 va = *(const bf16x8*)(&vt[(kb * 32 + lrow) * kLdsRow + koff[kk]]);
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], dp[kb], 0, 0, 0);
+        }
+      }
+      const bool tail = (t + 1) * kBT > L;
+      bf16x8 sb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pr = exp2_fast(fmaf(st[kb][r], kScaleLog2, -l2));
+          if (tail) {
+            const int k = t * kBT + kb * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+            if (k >= L) pr = 0.f;
+          }
+          dp[kb][r] = pr * (dp[kb][r] - dd);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          u32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = pack_bf2(dp[kb][8 * u + 2 * e], dp[kb][8 * u + 2 * e + 1]);
+          sb[kb][u] = __builtin_bit_cast(bf16x8, x);
+        }
+      }
+      // dQ^T += K^T dS^T (K^T by the transposing reads, keys in the order sb holds them).
+#pragma unroll
+      for (int d = 0; d < 2; ++d)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            const int r0 = kb * 32 + 16 * u + 4 * lhalf + tr_row;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kt + r0 * kLdsRow + voff[d][0]));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(kt + (r0 + 8) * kLdsRow + voff[d][1]));
+            const i16x8 k8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            dq[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k8), sb[kb][u], dq[d], 0, 0, 0);
+          }
+    }
+    vm_wait_all();
+    __syncthreads();
+  }
+
+  if (qrow >= L) return;
+  bf16_t* dqg = a.dqkv + ((int64_t)(0 * heads + head) * a.T + start + qrow) * kHeadDim;
+#pragma unroll
+  for (int d = 0; d < 2; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dim = d * 32 + 8 * g + 4 * lhalf;
+      *(u32x2*)(dqg + dim) = u32x2{pack_bf2(dq[d][4 * g] * 0.125f, dq[d][4 * g + 1] * 0.125f),
+                                   pack_bf2(dq[d][4 * g + 2] * 0.125f, dq[d][4 * g + 3] * 0.125f)};
+    }
+}
+
 }  // namespace
+
+hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t st) {
+  if (a.tile_cap <= 0 || a.T <= 0) return hipSuccess;
+  const int64_t nd = a.T * a.heads * 8;
+  hipLaunchKernelGGL(k_attn_bwd_delta, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, st, a);
+  const int64_t nblk = a.tile_cap * a.heads;
+  hipLaunchKernelGGL(k_attn_bwd_dkv, dim3((unsigned)nblk), dim3(64 * kNW), 0, st, a);
+  hipLaunchKernelGGL(k_attn_bwd_dq, dim3((unsigned)nblk), dim3(64 * kNW), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.tile_cap <= 0 || a.T <= 0) return hipSuccess;

@@ -241,6 +241,7 @@ struct AttnArgs {
   E4m3Out ctx8;           // when ctx8.y is set: E4M3 context instead of ctx
   uint8_t* ctx_mx;        // when set: MXFP4 context codes [T, H / 2] instead of ctx ...
   uint8_t* ctx_mx_sc;     // ... and their block scales (esm_mxfp4_quantize layout, K = H)
+  float* lse;             // when set: [heads, T] softmax normaliser log sum_j exp(q.k_j / 8)
   const int32_t* segs;    // [B, 2]
   const int32_t* tiles;   // [cap, 2]
   const int32_t* ntiles;  // [1]
@@ -250,6 +251,26 @@ struct AttnArgs {
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
+// Attention backward on the encoder layout: dqkv [3, heads, T, 64] from qkv,
+// the forward's context out [T, H], its gradient dout [T, H] and lse
+// [heads, T]; delta [heads, T] is scratch (rowsum(dout * out)).
+struct AttnBwdArgs {
+  const bf16_t* qkv;
+  const bf16_t* out;
+  const bf16_t* dout;
+  const float* lse;
+  float* delta;
+  bf16_t* dqkv;
+  const int32_t* segs;    // [B, 2]
+  const int32_t* tiles;   // [cap, 2]
+  const int32_t* ntiles;  // [1]
+  int64_t tile_cap;
+  int64_t T;
+  int32_t heads;
+};
+
+hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t st);
 
 // Biased attention on [B, N, L, heads, 64] tensors: per (b, n, h),
 // out = softmax(q k^T / 8 + mask[b, n, :] + pair[b, h, :, :]) v.

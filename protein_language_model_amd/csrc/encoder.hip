@@ -942,6 +942,57 @@ esm_status esm_attention_fwd(esm_encoder* e, const void* qkv, void* ctx, const i
   return timed(e, ESM_K_ATTENTION, st, "attention", [&] { return launch_attention(aa, st); });
 }
 
+esm_status esm_attention_fwd_lse(esm_encoder* e, const void* qkv, void* ctx, float* lse, const int32_t* cu_dev,
+                                 int32_t B, int64_t T, void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !qkv || !ctx || !lse || !cu_dev) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!aligned16(qkv) || !aligned16(ctx)) return fail(ESM_ERR_UNSUPPORTED, "qkv/ctx not 16-byte aligned");
+  if ((uintptr_t)lse & 3u) return fail(ESM_ERR_UNSUPPORTED, "lse not 4-byte aligned");
+  esm_status s = check_rows(e, T, B);
+  if (s) return s;
+  if (T == 0 || B == 0) return ok();
+  Plan p;
+  if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  if ((s = run_segments(e, 0, cu_dev, B, T, 0, ws, p, st))) return s;
+  AttnArgs aa{};
+  aa.qkv = (const bf16_t*)qkv; aa.ctx = (bf16_t*)ctx; aa.lse = lse;
+  aa.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
+  aa.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
+  aa.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
+  aa.tile_cap = tile_cap(T, B);
+  aa.T = T; aa.heads = e->cfg.num_attention_heads;
+  return timed(e, ESM_K_ATTENTION, st, "attention", [&] { return launch_attention(aa, st); });
+}
+
+esm_status esm_attention_bwd(esm_encoder* e, const void* qkv, const void* ctx, const void* dctx, const float* lse,
+                             float* delta, void* dqkv, const int32_t* cu_dev, int32_t B, int64_t T, void* ws,
+                             size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !qkv || !ctx || !dctx || !lse || !delta || !dqkv || !cu_dev) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!aligned16(qkv) || !aligned16(ctx) || !aligned16(dctx) || !aligned16(dqkv))
+    return fail(ESM_ERR_UNSUPPORTED, "qkv/ctx/dctx/dqkv not 16-byte aligned");
+  if (((uintptr_t)lse & 3u) || ((uintptr_t)delta & 3u)) return fail(ESM_ERR_UNSUPPORTED, "lse/delta not 4-byte aligned");
+  esm_status s = check_rows(e, T, B);
+  if (s) return s;
+  if (T == 0 || B == 0) return ok();
+  Plan p;
+  if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  if ((s = run_segments(e, 0, cu_dev, B, T, 0, ws, p, st))) return s;
+  AttnBwdArgs a{};
+  a.qkv = (const bf16_t*)qkv; a.out = (const bf16_t*)ctx; a.dout = (const bf16_t*)dctx;
+  a.lse = lse; a.delta = delta; a.dqkv = (bf16_t*)dqkv;
+  a.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
+  a.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
+  a.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
+  a.tile_cap = tile_cap(T, B);
+  a.T = T; a.heads = e->cfg.num_attention_heads;
+  return timed(e, ESM_K_ATTENTION_BWD, st, "attention_bwd", [&] { return launch_attention_bwd(a, st); });
+}
+
 esm_status esm_biased_attention_fwd(esm_encoder* e, const void* q, const void* k, const void* v,
                                     const void* mask_bias, const void* pair_bias, void* out, int32_t B, int32_t N,
                                     int32_t L, int32_t heads, esm_stream_t stream) {

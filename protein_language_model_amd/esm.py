@@ -25,7 +25,7 @@ EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_E4M3 = 0, 1, 2, 3
 WS_REGIONS = {"ln1": 0, "qkv": 1, "ctx": 2, "x1": 3, "ln2": 4, "act": 5, "pos": 6, "tiles": 7, "ntiles": 8, "segs": 9}
 ATTN_TILE_ROWS = 256  # ESM_ATTN_TILE_ROWS: query rows per attention workgroup
 KERNEL_CLASSES = ("segment", "embed", "layernorm", "gemm_qkv", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
-                  "other", "fp8", "head", "biased_attention")
+                  "other", "fp8", "head", "biased_attention", "attention_bwd")
 FP8_ACT_NAMES = ("ln1", "ctx", "ln2", "act")      # activation tensors tracked per layer, in state order
 FP8_WEIGHT_NAMES = ("w_qkv", "w_out", "w_fc1", "w_fc2")
 LAYER_WEIGHT_NAMES = ("ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_out", "b_out",
@@ -83,6 +83,8 @@ SIGNATURES = {
                                   _p]),
     "esm_segment_table": (_i32, [_p, _i32, _p, _i32, _i64, _i32, _p, _sz, _p]),
     "esm_attention_fwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
+    "esm_attention_fwd_lse": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
+    "esm_attention_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_biased_attention_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "esm_mxfp4_quantize": (_i32, [_p, _p, _i64, _i32, _p, _p, _p]),
     "esm_linear_mxfp4_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
@@ -354,6 +356,37 @@ class Encoder:
         _call("esm_attention_fwd", self._h, _ptr(qkv), _ptr(ctx), _ptr(cu_seqlens), int(B), int(T), _ptr(workspace),
               workspace.numel(), _stream(stream))
         return ctx
+
+    def attention_fwd_lse(self, qkv, cu_seqlens, B: int, T: int, *, ctx=None, lse=None, workspace=None,
+                          stream=None):
+        """(ctx [T, H] bf16, lse [heads, T] fp32): the attention and its softmax
+        normaliser log sum_j exp(q.k_j / 8), for a backward pass."""
+        import torch
+        if ctx is None:
+            ctx = torch.empty((T, self.hidden), dtype=torch.bfloat16, device=qkv.device)
+        if lse is None:
+            lse = torch.empty((self.cfg.num_attention_heads, T), dtype=torch.float32, device=qkv.device)
+        if workspace is None:
+            workspace = self.workspace(T, B)
+        _call("esm_attention_fwd_lse", self._h, _ptr(qkv), _ptr(ctx), _ptr(lse), _ptr(cu_seqlens), int(B), int(T),
+              _ptr(workspace), workspace.numel(), _stream(stream))
+        return ctx, lse
+
+    def attention_bwd(self, qkv, ctx, dctx, lse, cu_seqlens, B: int, T: int, *, dqkv=None, delta=None,
+                      workspace=None, stream=None):
+        """dqkv [3, heads, T, 64] bf16: gradients of the attention with respect
+        to q, k, v for the context gradient dctx [T, H]; ctx and lse are the
+        forward's (attention_fwd_lse).  delta [heads, T] fp32 is scratch."""
+        import torch
+        if dqkv is None:
+            dqkv = torch.empty_like(qkv)
+        if delta is None:
+            delta = torch.empty((self.cfg.num_attention_heads, T), dtype=torch.float32, device=qkv.device)
+        if workspace is None:
+            workspace = self.workspace(T, B)
+        _call("esm_attention_bwd", self._h, _ptr(qkv), _ptr(ctx), _ptr(dctx), _ptr(lse), _ptr(delta), _ptr(dqkv),
+              _ptr(cu_seqlens), int(B), int(T), _ptr(workspace), workspace.numel(), _stream(stream))
+        return dqkv
 
     def biased_attention_fwd(self, q, k, v, mask_bias=None, pair_bias=None, *, out=None, stream=None):
         """out = softmax(q k^T / 8 + mask_bias + pair_bias) v per (b, n, h) on
