@@ -13,8 +13,9 @@ least 10 warm-up steps, and reported under "fp8"; what follows the stack
 under "head".  The biased attention kernel (the DeepSpeed4Science page's
 Evoformer attention with a mask bias and a pair bias) is timed on its own
 synthetic MSA-row shape under "biased_attention", the MXFP4 quantiser and
-GEMM (the FP4 recipe) on the layer's four GEMM shapes under "mxfp4", and the
-whole stack with MXFP4 GEMMs under "mxfp4_stack".
+GEMM (the FP4 recipe) on the layer's four GEMM shapes under "mxfp4", the
+whole stack with MXFP4 GEMMs under "mxfp4_stack", and the attention backward
+on the batch's sequences under "attention_bwd".
 Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
@@ -62,6 +63,8 @@ def parse():
     ap.add_argument("--padded", action="store_true", help="also time the padded bshd layout of the same batch")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip timing the final LayerNorm / LM head / means")
+    ap.add_argument("--no-attention-bwd", action="store_true",
+                    help="skip timing the attention backward on the batch")
     ap.add_argument("--no-biased-attention", action="store_true",
                     help="skip timing the biased (Evoformer MSA-row) attention kernel")
     ap.add_argument("--no-mxfp4", action="store_true", help="skip timing the MXFP4 GEMMs on the layer shapes")
@@ -226,6 +229,70 @@ def bench_biased_attention(enc, steps: int, dev: str, stream) -> dict:
             "roofline": roof,
             "oracle": {"ms_per_call": round(dt_row * w.B * w.N * 1e3, 1), "kind": "oracle",
                        "sample": f"one of the {w.B * w.N} rows n (fp64 numpy), {dt_row:.2f} s, scaled to the call"}}
+
+
+def bench_attention_bwd(enc, batch, cu, ws, heads: int, steps: int, dev: str, stream) -> dict:
+    """The attention backward (esm_attention_bwd: row dot, dK/dV kernel, dQ
+    kernel) on this batch's packed sequences at the layer's width: q, k, v and
+    the context gradient N(0, 1) bf16, context and lse from one
+    esm_attention_fwd_lse.  HIP events on the library stream around back-to-
+    back calls.  Algorithmic flops: 2.5x the forward's 4 * 64 * sum(L^2) per
+    head (dV, dP, dQ, dK and one S), the usual count for a backward that
+    recomputes P (the kernels form S and dP twice, once per kernel, which is
+    not counted).  The fp64 oracle is timed on the longest sequence (all
+    heads) and scaled by sum(L^2) / L_max^2."""
+    import torch
+    from oracle import esm_oracle as O
+    from protein_language_model_amd import datagen as D
+    T, B = batch.T, len(batch.lengths)
+    g = torch.Generator(device=dev).manual_seed(29)
+    qkv = torch.randn((3, heads, T, 64), generator=g, device=dev).to(torch.bfloat16)
+    dctx = torch.randn((T, heads * 64), generator=g, device=dev).to(torch.bfloat16)
+    ctx = torch.empty((T, heads * 64), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((heads, T), dtype=torch.float32, device=dev)
+    delta = torch.empty((heads, T), dtype=torch.float32, device=dev)
+    dqkv = torch.empty_like(qkv)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n = max(10, steps)
+    ms_f = timed(lambda: enc.attention_fwd_lse(qkv, cu, B, T, ctx=ctx, lse=lse, workspace=ws, stream=stream), n)
+    ms_b = timed(lambda: enc.attention_bwd(qkv, ctx, dctx, lse, cu, B, T, dqkv=dqkv, delta=delta, workspace=ws,
+                                           stream=stream), n)
+    sum_L2 = int((batch.lengths.astype(np.int64) ** 2).sum())
+    fl_f = 4.0 * 64 * heads * sum_L2
+    fl_b = 2.5 * fl_f
+    tf = fl_b / (ms_b * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "flops_per_launch": fl_b}
+    s = int(np.argmax(batch.lengths))
+    a, L = int(batch.cu_seqlens[s]), int(batch.lengths[s])
+    sl = slice(a, a + L)
+    f = D.bf16_bits_to_f64
+    host = qkv[:, :, sl].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    gq, gk, gv = (f(host[i]).transpose(1, 0, 2) for i in range(3))
+    gd = f(dctx[sl].contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+    t0 = time.perf_counter()
+    O.attention_bwd(gq, gk, gv, gd, np.array([0, L]))
+    dt = time.perf_counter() - t0
+    del qkv, dctx, ctx, lse, delta, dqkv
+    return {"what": f"esm_attention_bwd on the batch's {B} packed sequences, {heads} heads of 64; inputs N(0, 1) bf16",
+            "ms_per_call": round(ms_b, 4), "calls": n, "tflops": round(tf, 1),
+            "fwd_lse_ms_per_call": round(ms_f, 4), "fwd_tflops": round(fl_f / (ms_f * 1e-3) / 1e12, 1),
+            "bwd_over_fwd": round(ms_b / ms_f, 3), "roofline": roof,
+            "oracle": {"ms_per_call": round(dt * sum_L2 / (L * L) * 1e3, 1), "kind": "oracle",
+                       "sample": f"the longest sequence (L = {L}, all heads; fp64 numpy), {dt:.2f} s, "
+                                 f"scaled by sum(L^2) / L^2"}}
 
 
 def bench_mxfp4(enc, T: int, H: int, F: int, steps: int, dev: str, stream) -> dict:
@@ -430,6 +497,10 @@ def main():
     if not args.no_biased_attention:
         biased = bench_biased_attention(enc, args.steps, dev, stream)
 
+    attn_bwd = None
+    if not args.no_attention_bwd:
+        attn_bwd = bench_attention_bwd(enc, batch, cu, ws, m.heads, args.steps, dev, stream)
+
     mxfp4 = None
     if not args.no_mxfp4:
         mxfp4 = bench_mxfp4(enc, T, m.hidden, m.ffn, args.steps, dev, stream)
@@ -525,6 +596,7 @@ def main():
         "head": head,
         "biased_attention": biased,
         "mxfp4": mxfp4,
+        "attention_bwd": attn_bwd,
         "mxfp4_stack": mx_stack,
         "vendor_gemm_fc1": vendor,
         "fp8": fp8,

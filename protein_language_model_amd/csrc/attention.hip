@@ -500,17 +500,19 @@ void k_biased_attention(BiasedAttnArgs a) {
 // D = rowsum(dO * O) (= rowsum(P * dP)),  dQ = dS K / 8,  dK = dS^T Q / 8.
 // P is recomputed from lse, never stored.  Three kernels:
 //  * k_attn_bwd_delta: D for every (head, row), 8 lanes per row;
-//  * k_attn_bwd_dkv: one workgroup per 256 keys of one sequence and head (8
+//  * k_attn_bwd_dkv: one workgroup per 128 keys of one sequence and head (4
 //    waves x 32 keys, K and V rows in registers as the MFMAs' B operand),
 //    streaming the sequence's queries in 64-row tiles of Q and dO through LDS
 //    (direct loads, double-buffered, the forward's swizzle) with their lse
 //    and D; S and dP come out query x key, so each lane owns one key and the
 //    products accumulate dV^T and dK^T in registers: no atomics;
-//  * k_attn_bwd_dq: one workgroup per 256 queries, the forward's structure
+//  * k_attn_bwd_dq: one workgroup per 128 queries, the forward's structure
 //    with dP added: K and V tiles in LDS, S^T and dP^T key x query, and
 //    dQ^T += K^T dS^T with K^T read by the transposing LDS reads.
 // P and dS enter the second products as bf16 (fp32 accumulation), as P does
-// in the forward.
+// in the forward.  Both big kernels hold 180-220 VGPRs (two waves per SIMD),
+// so a workgroup has 4 waves and two workgroups share a CU: one's barrier
+// waits are covered by the other's math.
 
 struct AttnBwdPtrs {
   const bf16_t* Q;    // row 0 of the sequence, head; row stride 64
@@ -555,28 +557,45 @@ __global__ __launch_bounds__(256) void k_attn_bwd_delta(AttnBwdArgs a) {
   if (live && part == 0) a.delta[(int64_t)head * a.T + t] = acc;
 }
 
-constexpr int kBT = 64;  // rows per streamed LDS tile in the backward kernels
+constexpr int kBT = 64;   // rows per streamed LDS tile in the backward kernels
+constexpr int kBW = 4;    // waves per backward workgroup (32 rows each): two workgroups share a CU
+constexpr int kBParts = kAttnTileRows / (32 * kBW);  // backward workgroups per segment-table tile
 
 // 64 rows x 128 bytes of a row-major tensor (row stride rs elements) into a
-// swizzled LDS tile: wave w fetches rows 8w .. 8w + 7, lane l physical chunk
-// l % 8 of row 8w + l / 8, i.e. logical chunk (l % 8) ^ kSwz(row).  Rows past
-// the end of the sequence are clamped to its last row.
+// swizzled LDS tile: in instruction i, wave w fetches rows 8 (w + kBW i) ..
+// + 7, lane l physical chunk l % 8 of row 8 (w + kBW i) + l / 8, i.e. logical
+// chunk (l % 8) ^ kSwz(row).  Rows past the end of the sequence are clamped
+// to its last row.
 __device__ __forceinline__ void tile_dma(const bf16_t* __restrict__ g, int64_t rs, int row0, int L, uint32_t lds,
                                          int lane, int wave, int wave_u) {
-  const int r = 8 * wave + (lane >> 3);
-  int row = row0 + r;
-  row = row < L ? row : L - 1;
-  lds_dma16(g + row * rs + ((lane & 7) ^ kSwz(r)) * 8, lds + (uint32_t)wave_u * 1024u);
+#pragma unroll
+  for (int i = 0; i < 8 / kBW; ++i) {
+    const int r = 8 * (wave + kBW * i) + (lane >> 3);
+    int row = row0 + r;
+    row = row < L ? row : L - 1;
+    lds_dma16(g + row * rs + ((lane & 7) ^ kSwz(r)) * 8, lds + (uint32_t)(wave_u + kBW * i) * 1024u);
+  }
 }
 
-__global__ __launch_bounds__(64 * kNW) void k_attn_bwd_dkv(AttnBwdArgs a) {
+// Workgroup -> (segment-table tile, 32 kBW-row part of it, head), the head
+// fastest.  Returns false (for the whole workgroup) when the part starts past
+// the end of its sequence.
+__device__ __forceinline__ bool bwd_block(const AttnBwdArgs& a, int& head, int& s, int& r0) {
+  head = blockIdx.x % a.heads;
+  const int rest = blockIdx.x / a.heads;
+  const int tile = rest / kBParts, part = rest % kBParts;
+  if (tile >= *a.ntiles) return false;
+  s = a.tiles[2 * tile];
+  r0 = a.tiles[2 * tile + 1] + part * 32 * kBW;
+  return r0 < a.segs[2 * s + 1];
+}
+
+__global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_attn_bwd_dkv(AttnBwdArgs a) {
   const int heads = a.heads;
-  const int tile = blockIdx.x / heads, head = blockIdx.x % heads;
-  if (tile >= *a.ntiles) return;
-  const int s = a.tiles[2 * tile], k0 = a.tiles[2 * tile + 1];
+  int head, s, k0;
+  if (!bwd_block(a, head, s, k0)) return;
   const int64_t start = a.segs[2 * s];
   const int L = a.segs[2 * s + 1];
-  if (L <= 0) return;
   const AttnBwdPtrs p = bwd_ptrs(a, head, start);
   const int64_t H = (int64_t)heads * kHeadDim;
 
@@ -741,14 +760,12 @@ __global__ __launch_bounds__(64 * kNW) void k_attn_bwd_dkv(AttnBwdArgs a) {
     }
 }
 
-__global__ __launch_bounds__(64 * kNW) void k_attn_bwd_dq(AttnBwdArgs a) {
+__global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(3, 3))) void k_attn_bwd_dq(AttnBwdArgs a) {
   const int heads = a.heads;
-  const int tile = blockIdx.x / heads, head = blockIdx.x % heads;
-  if (tile >= *a.ntiles) return;
-  const int s = a.tiles[2 * tile], q0 = a.tiles[2 * tile + 1];
+  int head, s, q0;
+  if (!bwd_block(a, head, s, q0)) return;
   const int64_t start = a.segs[2 * s];
   const int L = a.segs[2 * s + 1];
-  if (L <= 0) return;
   const AttnBwdPtrs p = bwd_ptrs(a, head, start);
   const int64_t H = (int64_t)heads * kHeadDim;
 
@@ -882,9 +899,9 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t st) {
   if (a.tile_cap <= 0 || a.T <= 0) return hipSuccess;
   const int64_t nd = a.T * a.heads * 8;
   hipLaunchKernelGGL(k_attn_bwd_delta, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, st, a);
-  const int64_t nblk = a.tile_cap * a.heads;
-  hipLaunchKernelGGL(k_attn_bwd_dkv, dim3((unsigned)nblk), dim3(64 * kNW), 0, st, a);
-  hipLaunchKernelGGL(k_attn_bwd_dq, dim3((unsigned)nblk), dim3(64 * kNW), 0, st, a);
+  const int64_t nblk = a.tile_cap * a.heads * kBParts;
+  hipLaunchKernelGGL(k_attn_bwd_dkv, dim3((unsigned)nblk), dim3(64 * kBW), 0, st, a);
+  hipLaunchKernelGGL(k_attn_bwd_dq, dim3((unsigned)nblk), dim3(64 * kBW), 0, st, a);
   return hipGetLastError();
 }
 
