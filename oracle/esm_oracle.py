@@ -41,6 +41,7 @@ Readings where the pages are silent (each is listed in the design notes):
   stack (head_forward): final LayerNorm, the ESM-2 masked-LM head with the
   decoder tied to the embedding, and per-sequence mean embeddings.
 
+linear_bwd gives the gradients of a linear layer (dx, dW, db).
 attention_lse and attention_bwd give the softmax normaliser a backward pass
 keeps and the gradients of the attention with respect to q, k and v: the
 backward of the training runs the pages time ([BIO-ACC] 3.2 and 6, [CARD]
@@ -229,6 +230,17 @@ def attention_bwd(q, k, v, dctx, cu_seqlens, scale: float = SOFTMAX_SCALE):
             dq[a:b, n] = scale * (dS @ k[a:b, n])
             dk[a:b, n] = scale * (dS.T @ q[a:b, n])
     return dq, dk, dv
+
+
+def linear_bwd(x, w, dy):
+    """Gradients of sum(dy * (x w^T + b)) for x [M, K], w [N, K], dy [M, N]
+    (the backward of the encoder's linears, [BIO-ACC] 3.1; training timed in
+    [BIO-ACC] 3.2 and 6): dx = dy w [M, K], dw = dy^T x [N, K], db = the
+    column sums of dy [N]."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    dy = np.asarray(dy, np.float64)
+    return dy @ w, dy.T @ x, dy.sum(axis=0)
 
 
 # --------------------------------------------------------------------------

@@ -1,5 +1,5 @@
-"""Pins of the oracle's attention backward and softmax normaliser
-(oracle/esm_oracle.py: attention_bwd, attention_lse), against things other
+"""Pins of the oracle's attention backward, softmax normaliser and linear backward
+(oracle/esm_oracle.py: attention_bwd, attention_lse, linear_bwd), against things other
 than the oracle's own formulas:
 
 * central finite differences of the forward loss sum(dO * attention(q, k, v))
@@ -121,3 +121,41 @@ def test_empty_sequences_change_nothing():
     for a, b in zip(O.attention_bwd(q, k, v, g, cu), O.attention_bwd(q, k, v, g, cu_e)):
         np.testing.assert_array_equal(a, b)
     np.testing.assert_array_equal(O.attention_lse(q, k, cu), O.attention_lse(q, k, cu_e))
+
+
+# ---------------------------------------------------------------- linear backward
+
+def test_linear_bwd_matches_finite_differences():
+    """The loss sum(dy * (x w^T + b)) is linear in each of x, w, b, so central
+    differences are exact up to rounding."""
+    rng = np.random.default_rng(30)
+    M, N, K = 5, 3, 4
+    x, w, b, dy = (rng.standard_normal(s) for s in ((M, K), (N, K), (N,), (M, N)))
+    dx, dw, db = O.linear_bwd(x, w, dy)
+
+    def loss():
+        return float(np.sum(dy * (x @ w.T + b)))
+    h = 1e-3
+    for a, da in ((x, dx), (w, dw), (b, db)):
+        flat, g = a.reshape(-1), da.reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + h
+            lp = loss()
+            flat[i] = old - h
+            lm = loss()
+            flat[i] = old
+            assert abs((lp - lm) / (2 * h) - g[i]) <= 1e-9 * max(1.0, abs(g[i]))
+
+
+def test_linear_bwd_adjoint_identity():
+    """<dy, x w^T> = <dx, x> = <dw, w>: each gradient pairs with its operand to
+    the same number, which fails for a transposed or swapped operand."""
+    rng = np.random.default_rng(31)
+    M, N, K = 37, 64, 128
+    x, w, dy = (rng.standard_normal(s) for s in ((M, K), (N, K), (M, N)))
+    dx, dw, db = O.linear_bwd(x, w, dy)
+    ref = float(np.sum(dy * (x @ w.T)))
+    assert abs(float(np.sum(dx * x)) - ref) <= 1e-9 * abs(ref)
+    assert abs(float(np.sum(dw * w)) - ref) <= 1e-9 * abs(ref)
+    assert abs(float(db.sum()) - float(dy.sum())) <= 1e-9 * max(1.0, abs(float(dy.sum())))
