@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 10
+#define ESM_ABI_VERSION 11
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -393,6 +393,28 @@ esm_status esm_linear_mxfp4_fwd(esm_encoder* enc, const void* x_codes, const voi
                                 int32_t epilogue, esm_stream_t stream);
 
 /* Row LayerNorm y = (x - mean) / sqrt(var + eps) * gamma + beta over [M, H]. */
+/* Backward of a linear layer y = x W^T + b (the encoder's four linears; the
+ * pages time training, [BIO-ACC] 3.2 and 6, [CARD] 训练性能):
+ *   dx = dy W        [M, K]  (written when dx is not NULL; needs w)
+ *   dW = dy^T x      [N, K]  (written when dw is not NULL; needs x)
+ *   db = sum_m dy[m] [N]     (fp32, written when db is not NULL)
+ * x bf16 [M, K], w bf16 [N, K] (as in esm_linear_fwd), dy bf16 [M, N]; dx and
+ * dw bf16.  N and K multiples of 64, any M >= 0.  The two products run on the
+ * library's MFMA GEMM with fp32 accumulation (dW over all M rows in fp32);
+ * W^T, dy^T and x^T are written into the workspace first (rows padded with
+ * zeros to a multiple of 64), db by a fixed-order two-pass column sum, so
+ * results are deterministic.  workspace: device, 256-byte aligned, at least
+ * esm_linear_bwd_workspace_size(M, N, K) bytes, overwritten.  Outputs must not
+ * overlap inputs or workspace.  Errors: ESM_ERR_NULL, ESM_ERR_SHAPE,
+ * ESM_ERR_UNSUPPORTED (alignment: tensors 16 bytes, db 4), ESM_ERR_WORKSPACE.
+ * M = 0 launches nothing and writes nothing.  Asynchronous on stream. */
+esm_status esm_linear_bwd(esm_encoder* enc, const void* x, const void* w, const void* dy,
+                          void* dx, void* dw, float* db, int64_t M, int32_t N, int32_t K,
+                          void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* Workspace bytes esm_linear_bwd needs for these sizes (host only). */
+esm_status esm_linear_bwd_workspace_size(int64_t M, int32_t N, int32_t K, size_t* bytes);
+
 esm_status esm_layernorm_fwd(esm_encoder* enc, const void* x, const void* gamma,
                              const void* beta, void* y, int64_t M, esm_stream_t stream);
 
@@ -481,7 +503,8 @@ typedef enum {
   ESM_K_OTHER = 8, ESM_K_FP8 = 9 /* weight casts, scale updates */,
   ESM_K_HEAD = 10 /* final LayerNorm, LM head, sequence means */,
   ESM_K_BIASED_ATTENTION = 11 /* esm_biased_attention_fwd */,
-  ESM_K_ATTENTION_BWD = 12 /* esm_attention_bwd */, ESM_K_COUNT = 13
+  ESM_K_ATTENTION_BWD = 12 /* esm_attention_bwd */,
+  ESM_K_LINEAR_BWD = 13 /* esm_linear_bwd */, ESM_K_COUNT = 14
 } esm_kernel_class;
 
 /* When on, every launch is bracketed by HIP events recorded on the launch

@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libesmenc.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["encoder.hip", "elementwise.hip", "gemm.hip", "attention.hip", "fp8.hip", "mxfp4.hip"]
+SOURCES = ["encoder.hip", "elementwise.hip", "gemm.hip", "attention.hip", "fp8.hip", "mxfp4.hip", "linear_bwd.hip"]
 
 # Packed fp32 VALU forms are switched off for all device code.
 COMMON = [

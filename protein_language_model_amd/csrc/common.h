@@ -272,6 +272,13 @@ struct AttnBwdArgs {
 
 hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t st);
 
+// Linear backward helpers: out [C, Rp] = in[R, C]^T with rows R .. Rp - 1 of
+// the result zero (C, Rp multiples of 64); db[n] = sum_m dy[m, n] in fp32
+// through part [colsum_chunks(M), N] (N a multiple of 64).
+hipError_t launch_transpose_pad(const bf16_t* in, int64_t R, int32_t C, bf16_t* out, int64_t Rp, hipStream_t st);
+hipError_t launch_colsum(const bf16_t* dy, int64_t M, int32_t N, float* part, float* db, hipStream_t st);
+int64_t colsum_chunks(int64_t M);
+
 // Biased attention on [B, N, L, heads, 64] tensors: per (b, n, h),
 // out = softmax(q k^T / 8 + mask[b, n, :] + pair[b, h, :, :]) v.
 struct BiasedAttnArgs {

@@ -1080,6 +1080,78 @@ esm_status esm_linear_fwd(esm_encoder* e, const void* x, const void* w, const vo
   return timed(e, ESM_K_OTHER, (hipStream_t)stream, "linear", [&] { return launch_gemm(kind, g, (hipStream_t)stream); });
 }
 
+namespace {
+struct LinBwdPlan {
+  size_t wt, dyt, xt, part, total;
+};
+LinBwdPlan lin_bwd_plan(int64_t M, int32_t N, int32_t K) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  const int64_t M64 = (M + 63) / 64 * 64;
+  LinBwdPlan p;
+  p.wt = 0;
+  p.dyt = p.wt + up((size_t)K * N * 2);
+  p.xt = p.dyt + up((size_t)N * M64 * 2);
+  p.part = p.xt + up((size_t)K * M64 * 2);
+  p.total = p.part + up((size_t)colsum_chunks(M) * N * 4);
+  return p;
+}
+}  // namespace
+
+esm_status esm_linear_bwd_workspace_size(int64_t M, int32_t N, int32_t K, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(ESM_ERR_NULL, "NULL argument");
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64)
+    return fail(ESM_ERR_SHAPE, "M %lld N %d K %d: N and K must be positive multiples of 64", (long long)M, N, K);
+  *bytes = lin_bwd_plan(M, N, K).total;
+  return ok();
+}
+
+esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const void* dy, void* dx, void* dw, float* db,
+                          int64_t M, int32_t N, int32_t K, void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !dy || !ws) return fail(ESM_ERR_NULL, "NULL argument");
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64)
+    return fail(ESM_ERR_SHAPE, "M %lld N %d K %d: N and K must be positive multiples of 64", (long long)M, N, K);
+  if ((dx && !w) || (dw && !x)) return fail(ESM_ERR_NULL, "dx needs w, dw needs x");
+  if (!aligned16(dy) || (x && !aligned16(x)) || (w && !aligned16(w)) || (dx && !aligned16(dx)) ||
+      (dw && !aligned16(dw)) || ((uintptr_t)db & 3u) || ((uintptr_t)ws & 255u))
+    return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer (tensors 16 bytes, db 4, workspace 256)");
+  const LinBwdPlan pl = lin_bwd_plan(M, N, K);
+  if (ws_bytes < pl.total)
+    return fail(ESM_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, pl.total);
+  if (M == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  bf16_t* wt = (bf16_t*)(base + pl.wt);
+  bf16_t* dyt = (bf16_t*)(base + pl.dyt);
+  bf16_t* xt = (bf16_t*)(base + pl.xt);
+  float* part = (float*)(base + pl.part);
+  const int64_t M64 = (M + 63) / 64 * 64;
+  return timed(e, ESM_K_LINEAR_BWD, st, "linear backward", [&]() -> hipError_t {
+    hipError_t r = hipSuccess;
+    if (dx) {
+      // dx [M, K] = dy [M, N] . (W^T [K, N])^T
+      if ((r = launch_transpose_pad((const bf16_t*)w, N, K, wt, N, st))) return r;
+      GemmArgs g{};
+      g.dtype = kBF16;
+      g.x = dy; g.w = wt; g.y = (bf16_t*)dx; g.M = M; g.N = K; g.K = N;
+      if ((r = launch_gemm(EPI_BIAS, g, st))) return r;
+    }
+    if (dw) {
+      // dW [N, K] = dy^T [N, M64] . (x^T [K, M64])^T, zero columns past M
+      if ((r = launch_transpose_pad((const bf16_t*)dy, M, N, dyt, M64, st))) return r;
+      if ((r = launch_transpose_pad((const bf16_t*)x, M, K, xt, M64, st))) return r;
+      GemmArgs g{};
+      g.dtype = kBF16;
+      g.x = dyt; g.w = xt; g.y = (bf16_t*)dw; g.M = N; g.N = K; g.K = M64;
+      if ((r = launch_gemm(EPI_BIAS, g, st))) return r;
+    }
+    if (db && (r = launch_colsum((const bf16_t*)dy, M, N, part, db, st))) return r;
+    return r;
+  });
+}
+
 esm_status esm_layernorm_fwd(esm_encoder* e, const void* x, const void* gamma, const void* beta, void* y, int64_t M,
                              esm_stream_t stream) {
   g_last_error.clear();

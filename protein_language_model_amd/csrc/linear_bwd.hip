@@ -1,0 +1,131 @@
+// Helpers of the linear layers' backward for gfx950: a bf16 transpose that
+// zero-pads the rows it produces, and a deterministic column sum.
+//
+// For y = x W^T + b (x [M, K], W [N, K], y [M, N]) and an incoming gradient
+// dy, the backward is dx = dy W, dW = dy^T x and db = the column sums of dy
+// (the linears of the encoder layer; the pages time training, [BIO-ACC] 3.2
+// and 6).  dx and dW run on the library's MFMA GEMM (which computes
+// a B^T for row-major a [M', K'] and B [N', K']): dx = dy (W^T)^T and
+// dW = (dy^T) (x^T)^T, so the GEMM reads W^T [K, N], dy^T [N, M64] and
+// x^T [K, M64], written here with M rounded up to M64, a multiple of 64, and
+// the padding columns zero (they add nothing to the contraction over M).
+#include "common.h"
+
+namespace esm {
+
+namespace {
+
+// out[c, r] = in[r, c] for r < R, 0 for R <= r < Rp; in [R, C] row-major,
+// out [C, Rp].  One 256-thread workgroup per 64 x 64 tile, staged through
+// LDS with a padded row (66 halves) so that the column reads spread over
+// the banks.  C is a multiple of 64; Rp a multiple of 64 and >= R.
+__global__ __launch_bounds__(256) void k_transpose_pad(const bf16_t* __restrict__ in, int64_t R, int32_t C,
+                                                       bf16_t* __restrict__ out, int64_t Rp) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const int t = threadIdx.x;
+  {
+    // load: thread t reads 16 consecutive columns of row t / 4
+    const int r = t >> 2, c = (t & 3) * 16;
+    u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+    if (r0 + r < R) {
+      const bf16_t* src = in + (r0 + r) * C + c0 + c;
+      w0 = *(const u32x4*)src;
+      w1 = *(const u32x4*)(src + 8);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[r][c + 2 * e] = (uint16_t)(w0[e] & 0xFFFFu);
+      tile[r][c + 2 * e + 1] = (uint16_t)(w0[e] >> 16);
+      tile[r][c + 8 + 2 * e] = (uint16_t)(w1[e] & 0xFFFFu);
+      tile[r][c + 8 + 2 * e + 1] = (uint16_t)(w1[e] >> 16);
+    }
+  }
+  __syncthreads();
+  {
+    // store: thread t writes 16 consecutive rows (of in) of output row t / 4
+    const int c = t >> 2, r = (t & 3) * 16;
+    u32x4 w0, w1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w0[e] = (uint32_t)tile[r + 2 * e][c] | ((uint32_t)tile[r + 2 * e + 1][c] << 16);
+      w1[e] = (uint32_t)tile[r + 8 + 2 * e][c] | ((uint32_t)tile[r + 8 + 2 * e + 1][c] << 16);
+    }
+    bf16_t* dst = out + (int64_t)(c0 + c) * Rp + r0 + r;
+    *(u32x4*)dst = w0;
+    *(u32x4*)(dst + 8) = w1;
+  }
+}
+
+constexpr int kSumRows = 256;  // rows per partial column sum
+
+// part[chunk, n] = sum of dy[m, n] over the chunk's rows m (fp32, fixed
+// order): thread t adds 8 columns (one 16-byte load per row) of rows
+// t / 8 + 32 i, then the 32 row groups are added in LDS in a fixed tree.
+__global__ __launch_bounds__(256) void k_colsum_partial(const bf16_t* __restrict__ dy, int64_t M, int32_t N,
+                                                        float* __restrict__ part) {
+  __shared__ float red[32][65];
+  const int64_t m0 = (int64_t)blockIdx.x * kSumRows;
+  const int n0 = blockIdx.y * 64;
+  const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kSumRows / 32; ++i) {
+    const int64_t m = m0 + rg + 32 * i;
+    if (m < M) {
+      const u32x4 w = *(const u32x4*)(dy + m * N + n0 + cg * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bflo(w[e]);
+        acc[2 * e + 1] += bfhi(w[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rg][cg * 8 + e] = acc[e];
+  __syncthreads();
+  for (int s = 16; s >= 1; s >>= 1) {
+    // 64 columns x s row groups: thread t < 64 s adds row group g + s into g
+    for (int i = t; i < 64 * s; i += 256) {
+      const int g = i / 64, c = i % 64;
+      red[g][c] += red[g + s][c];
+    }
+    __syncthreads();
+  }
+  if (t < 64) part[(int64_t)blockIdx.x * N + n0 + t] = red[0][t];
+}
+
+// db[n] = sum over chunks of part[chunk, n], in chunk order.
+__global__ __launch_bounds__(256) void k_colsum_final(const float* __restrict__ part, int64_t chunks, int32_t N,
+                                                      float* __restrict__ db) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float s = 0.f;
+  for (int64_t c = 0; c < chunks; ++c) s += part[c * N + n];
+  db[n] = s;
+}
+
+}  // namespace
+
+int64_t colsum_chunks(int64_t M) { return (M + kSumRows - 1) / kSumRows; }
+
+hipError_t launch_transpose_pad(const bf16_t* in, int64_t R, int32_t C, bf16_t* out, int64_t Rp, hipStream_t st) {
+  if (C <= 0 || Rp <= 0) return hipSuccess;
+  if (C % 64 || Rp % 64 || Rp < R) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_transpose_pad, dim3((unsigned)(Rp / 64), (unsigned)(C / 64)), dim3(256), 0, st, in, R, C, out,
+                     Rp);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const bf16_t* dy, int64_t M, int32_t N, float* part, float* db, hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  if (N % 64) return hipErrorInvalidValue;
+  const int64_t chunks = colsum_chunks(M);
+  if (chunks > 0)
+    hipLaunchKernelGGL(k_colsum_partial, dim3((unsigned)chunks, (unsigned)(N / 64)), dim3(256), 0, st, dy, M, N,
+                       part);
+  hipLaunchKernelGGL(k_colsum_final, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, part, chunks, N, db);
+  return hipGetLastError();
+}
+
+}  // namespace esm

@@ -25,7 +25,7 @@ EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_E4M3 = 0, 1, 2, 3
 WS_REGIONS = {"ln1": 0, "qkv": 1, "ctx": 2, "x1": 3, "ln2": 4, "act": 5, "pos": 6, "tiles": 7, "ntiles": 8, "segs": 9}
 ATTN_TILE_ROWS = 256  # ESM_ATTN_TILE_ROWS: query rows per attention workgroup
 KERNEL_CLASSES = ("segment", "embed", "layernorm", "gemm_qkv", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
-                  "other", "fp8", "head", "biased_attention", "attention_bwd")
+                  "other", "fp8", "head", "biased_attention", "attention_bwd", "linear_bwd")
 FP8_ACT_NAMES = ("ln1", "ctx", "ln2", "act")      # activation tensors tracked per layer, in state order
 FP8_WEIGHT_NAMES = ("w_qkv", "w_out", "w_fc1", "w_fc2")
 LAYER_WEIGHT_NAMES = ("ln1_gamma", "ln1_beta", "w_qkv", "b_qkv", "w_out", "b_out",
@@ -84,6 +84,8 @@ SIGNATURES = {
     "esm_segment_table": (_i32, [_p, _i32, _p, _i32, _i64, _i32, _p, _sz, _p]),
     "esm_attention_fwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_attention_fwd_lse": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
+    "esm_linear_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _p, _sz, _p]),
+    "esm_linear_bwd_workspace_size": (_i32, [_i64, _i32, _i32, _p]),
     "esm_attention_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_biased_attention_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "esm_mxfp4_quantize": (_i32, [_p, _p, _i64, _i32, _p, _p, _p]),
@@ -387,6 +389,32 @@ class Encoder:
         _call("esm_attention_bwd", self._h, _ptr(qkv), _ptr(ctx), _ptr(dctx), _ptr(lse), _ptr(delta), _ptr(dqkv),
               _ptr(cu_seqlens), int(B), int(T), _ptr(workspace), workspace.numel(), _stream(stream))
         return dqkv
+
+    @staticmethod
+    def linear_bwd_workspace_size(M: int, N: int, K: int) -> int:
+        n = ctypes.c_size_t()
+        _call("esm_linear_bwd_workspace_size", int(M), int(N), int(K), ctypes.byref(n))
+        return int(n.value)
+
+    def linear_bwd(self, x, w, dy, *, dx=True, dw=True, db=True, workspace=None, stream=None):
+        """Backward of y = x W^T + b: returns (dx [M, K] bf16, dW [N, K] bf16,
+        db [N] fp32); pass dx/dw/db=False to skip one, or a tensor to write into."""
+        import torch
+        M, N = dy.shape
+        K = w.shape[1] if w is not None else x.shape[1]
+        dev = dy.device
+        if dx is True:
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        if dw is True:
+            dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        if db is True:
+            db = torch.empty((N,), dtype=torch.float32, device=dev)
+        dx, dw, db = (t if t is not False else None for t in (dx, dw, db))
+        if workspace is None:
+            workspace = torch.empty((self.linear_bwd_workspace_size(M, N, K),), dtype=torch.uint8, device=dev)
+        _call("esm_linear_bwd", self._h, _ptr(x), _ptr(w), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db), int(M), int(N),
+              int(K), _ptr(workspace), workspace.numel(), _stream(stream))
+        return dx, dw, db
 
     def biased_attention_fwd(self, q, k, v, mask_bias=None, pair_bias=None, *, out=None, stream=None):
         """out = softmax(q k^T / 8 + mask_bias + pair_bias) v per (b, n, h) on

@@ -1,0 +1,97 @@
+"""Parity of the linear backward (esm_linear_bwd) against the fp64 oracle
+(oracle/esm_oracle.py: linear_bwd), through the C ABI.
+
+Tolerances.  dx and dW are GEMMs of bf16 operands (exact products, fp32
+accumulation) rounded once to bf16: max|err| / max|ref| <= 4e-3, the forward
+GEMM's bound.  db is an fp32 sum of bf16 values: |err| <= 1e-5 max|ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import esm_oracle as O
+from protein_language_model_amd import datagen as D
+from protein_language_model_amd import esm
+
+pytestmark = pytest.mark.gpu
+
+TOL = 4e-3
+
+
+@pytest.fixture(scope="module")
+def gu():
+    import gpu_util
+    return gpu_util
+
+
+@pytest.fixture(scope="module")
+def enc():
+    e = esm.Encoder(hidden_size=320, num_attention_heads=5, intermediate_size=1280, num_hidden_layers=1)
+    yield e
+    e.close()
+
+
+def _bits(shape, seed, scale=1.0):
+    return D.to_bf16_bits((np.random.default_rng(seed).standard_normal(shape) * scale).astype(np.float32))
+
+
+def _case(gu, enc, M, N, K, seed=0):
+    xb, wb, gb = _bits((M, K), seed + 1), _bits((N, K), seed + 2, 0.05), _bits((M, N), seed + 3)
+    dx, dw, db = enc.linear_bwd(gu.to_dev_bf16(xb), gu.to_dev_bf16(wb), gu.to_dev_bf16(gb))
+    torch.cuda.synchronize()
+    ref = O.linear_bwd(D.bf16_bits_to_f64(xb), D.bf16_bits_to_f64(wb), D.bf16_bits_to_f64(gb))
+    return (gu.from_dev(dx), gu.from_dev(dw), db.cpu().numpy().astype(np.float64)), ref
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (63, 128, 64), (381, 960, 320), (257, 320, 1280),
+                                   (1000, 1280, 320)])
+def test_linear_bwd(gu, enc, M, N, K):
+    (dx, dw, db), (rx, rw, rb) = _case(gu, enc, M, N, K)
+    assert gu.rel_err(dx, rx) < TOL
+    assert gu.rel_err(dw, rw) < TOL
+    assert np.abs(db - rb).max() <= 1e-5 * np.abs(rb).max()
+
+
+def test_linear_bwd_partial_outputs(gu, enc):
+    """dx only, dW only, db only: each equals the full call's (bit-exact)."""
+    M, N, K = 300, 256, 192
+    xb, wb, gb = _bits((M, K), 5), _bits((N, K), 6, 0.05), _bits((M, N), 7)
+    x, w, g = (gu.to_dev_bf16(a) for a in (xb, wb, gb))
+    full = enc.linear_bwd(x, w, g)
+    dx = enc.linear_bwd(None, w, g, dw=False, db=False)[0]
+    dw = enc.linear_bwd(x, None, g, dx=False, db=False)[1]
+    db = enc.linear_bwd(x, w, g, dx=False, dw=False)[2]
+    assert np.array_equal(gu.bits_of(dx), gu.bits_of(full[0]))
+    assert np.array_equal(gu.bits_of(dw), gu.bits_of(full[1]))
+    assert torch.equal(db, full[2])
+
+
+def test_linear_bwd_650m_fc1_sampled(gu):
+    """fc1's backward at the 650M batch's T = 32293 (x [T, 1280], W1 [5120, 1280],
+    dy [T, 5120]): sampled rows of dx and dW and all of db against the oracle,
+    computed one row at a time."""
+    enc = esm.Encoder(num_hidden_layers=1)
+    try:
+        M, N, K = 32293, 5120, 1280
+        g = torch.Generator(device="cuda:0").manual_seed(40)
+        x = torch.randn((M, K), generator=g, device="cuda:0").to(torch.bfloat16)
+        w = (torch.randn((N, K), generator=g, device="cuda:0") * 0.02).to(torch.bfloat16)
+        dy = torch.randn((M, N), generator=g, device="cuda:0").to(torch.bfloat16)
+        dx, dw, db = enc.linear_bwd(x, w, dy)
+        torch.cuda.synchronize()
+    finally:
+        enc.close()
+    xf = gu.from_dev(x)
+    wf = gu.from_dev(w)
+    gf = gu.from_dev(dy)
+    dxf, dwf = gu.from_dev(dx), gu.from_dev(dw)
+    rng = np.random.default_rng(41)
+    rows = np.concatenate([[0, M - 1], rng.choice(M, 14, replace=False)])
+    for m in rows:
+        ref = O.linear_bwd(xf[m:m + 1], wf, gf[m:m + 1])[0][0]
+        assert gu.rel_err(dxf[m], ref) < TOL, m
+    for n in np.concatenate([[0, N - 1], rng.choice(N, 14, replace=False)]):
+        ref = gf[:, n] @ xf
+        assert gu.rel_err(dwf[n], ref) < TOL, n
+    rb = gf.sum(axis=0)
+    assert np.abs(db.cpu().numpy() - rb).max() <= 1e-5 * np.abs(rb).max() + 1e-3
