@@ -14,8 +14,9 @@ under "head".  The biased attention kernel (the DeepSpeed4Science page's
 Evoformer attention with a mask bias and a pair bias) is timed on its own
 synthetic MSA-row shape under "biased_attention", the MXFP4 quantiser and
 GEMM (the FP4 recipe) on the layer's four GEMM shapes under "mxfp4", the
-whole stack with MXFP4 GEMMs under "mxfp4_stack", and the attention backward
-on the batch's sequences under "attention_bwd".
+whole stack with MXFP4 GEMMs under "mxfp4_stack", the attention backward
+on the batch's sequences under "attention_bwd" and the linear backward on the
+layer's four shapes under "linear_bwd".
 Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
@@ -63,6 +64,8 @@ def parse():
     ap.add_argument("--padded", action="store_true", help="also time the padded bshd layout of the same batch")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip timing the final LayerNorm / LM head / means")
+    ap.add_argument("--no-linear-bwd", action="store_true",
+                    help="skip timing the linear backward on the layer's four shapes")
     ap.add_argument("--no-attention-bwd", action="store_true",
                     help="skip timing the attention backward on the batch")
     ap.add_argument("--no-biased-attention", action="store_true",
@@ -295,6 +298,48 @@ def bench_attention_bwd(enc, batch, cu, ws, heads: int, steps: int, dev: str, st
                                  f"scaled by sum(L^2) / L^2"}}
 
 
+def bench_linear_bwd(enc, T: int, H: int, F: int, steps: int, dev: str, stream) -> dict:
+    """esm_linear_bwd (dx, dW and db) on the layer's four linear shapes at this
+    batch's T: bf16 x, dy N(0, 1) and W N(0, 0.02); HIP events on the library
+    stream around back-to-back calls.  Algorithmic flops 4 M N K per call (the
+    two products); the transposes and the column sum are counted as time, not
+    flops."""
+    import torch
+    out = {}
+    g = torch.Generator(device=dev).manual_seed(12)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(10, steps)
+    for name, N, K in (("qkv", 3 * H, H), ("out", H, H), ("fc1", F, H), ("fc2", H, F)):
+        x = torch.randn((T, K), device=dev, generator=g).to(torch.bfloat16)
+        w = (torch.randn((N, K), device=dev, generator=g) * 0.02).to(torch.bfloat16)
+        dy = torch.randn((T, N), device=dev, generator=g).to(torch.bfloat16)
+        dx = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+        dw = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        db = torch.empty((N,), dtype=torch.float32, device=dev)
+        ws = torch.empty((enc.linear_bwd_workspace_size(T, N, K),), dtype=torch.uint8, device=dev)
+
+        def call():
+            enc.linear_bwd(x, w, dy, dx=dx, dw=dw, db=db, workspace=ws, stream=stream)
+
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        fl = 4.0 * T * N * K
+        tf = fl / (ms * 1e-3) / 1e12
+        out[name] = {"us_per_call": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                                  "flops_per_launch": fl}}
+        del x, w, dy, dx, dw, db, ws
+    return out
+
+
 def bench_mxfp4(enc, T: int, H: int, F: int, steps: int, dev: str, stream) -> dict:
     """The MXFP4 (FP4 recipe) quantiser and GEMM alone on the four linears'
     shapes of one layer of this batch: bf16 activations and weights N(0, 1) /
@@ -501,6 +546,10 @@ def main():
     if not args.no_attention_bwd:
         attn_bwd = bench_attention_bwd(enc, batch, cu, ws, m.heads, args.steps, dev, stream)
 
+    lin_bwd = None
+    if not args.no_linear_bwd:
+        lin_bwd = bench_linear_bwd(enc, T, m.hidden, m.ffn, args.steps, dev, stream)
+
     mxfp4 = None
     if not args.no_mxfp4:
         mxfp4 = bench_mxfp4(enc, T, m.hidden, m.ffn, args.steps, dev, stream)
@@ -597,6 +646,7 @@ def main():
         "biased_attention": biased,
         "mxfp4": mxfp4,
         "attention_bwd": attn_bwd,
+        "linear_bwd": lin_bwd,
         "mxfp4_stack": mx_stack,
         "vendor_gemm_fc1": vendor,
         "fp8": fp8,

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void k_transpose_pad(const bf16_t* __restrict_
   }
 }
 
-constexpr int kSumRows = 256;  // rows per partial column sum
+constexpr int kSumRows = 1024;  // rows per partial column sum
 
 // part[chunk, n] = sum of dy[m, n] over the chunk's rows m (fp32, fixed
 // order): thread t adds 8 columns (one 16-byte load per row) of rows
