@@ -109,7 +109,6 @@ __device__ __forceinline__ int64_t mx_scale_offset(int64_t m, int b, int64_t M2)
   return ((int64_t)(b / 8) * M2 + m) * 8 + ((b & 1) * 4 + ((b & 7) >> 1));
 }
 
-// Maximum of a non-negative per-lane value over the wave (fmaxf drops NaN).
 // Direct-to-LDS 16-byte load: lane i's 16 bytes from g land at LDS byte
 // lds_base + 16 i (lds_base must be wave-uniform; it goes through M0).  Issued
 // as inline assembly so the compiler keeps exact LDS wait counts for the
@@ -121,6 +120,7 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds_base) {
 }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Maximum of a non-negative per-lane value over the wave (fmaxf drops NaN).
 __device__ __forceinline__ float wave_max(float m) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
