@@ -41,7 +41,8 @@ Readings where the pages are silent (each is listed in the design notes):
   stack (head_forward): final LayerNorm, the ESM-2 masked-LM head with the
   decoder tied to the embedding, and per-sequence mean embeddings.
 
-linear_bwd gives the gradients of a linear layer (dx, dW, db).
+linear_bwd and layer_norm_bwd give the gradients of a linear layer (dx, dW,
+db) and of a LayerNorm (dx, dgamma, dbeta).
 attention_lse and attention_bwd give the softmax normaliser a backward pass
 keeps and the gradients of the attention with respect to q, k and v: the
 backward of the training runs the pages time ([BIO-ACC] 3.2 and 6, [CARD]
@@ -230,6 +231,26 @@ def attention_bwd(q, k, v, dctx, cu_seqlens, scale: float = SOFTMAX_SCALE):
             dq[a:b, n] = scale * (dS @ k[a:b, n])
             dk[a:b, n] = scale * (dS.T @ q[a:b, n])
     return dq, dk, dv
+
+
+def layer_norm_bwd(x, gamma, dy, eps: float = LN_EPS):
+    """Gradients of sum(dy * layer_norm(x, gamma, beta)) with respect to x,
+    gamma and beta (the backward of the pre-LN LayerNorms, [TE-RU] and
+    [BIO-ACC] 3.1; training timed in [BIO-ACC] 3.2 and 6).  Per row, with the
+    forward's mean mu, biased variance var, r = 1 / sqrt(var + eps),
+    xh = (x - mu) r and g = dy * gamma:
+        dx = r (g - mean(g) - xh mean(g xh)),
+        dgamma = sum over rows of dy xh,   dbeta = sum over rows of dy."""
+    x = np.asarray(x, np.float64)
+    dy = np.asarray(dy, np.float64)
+    gamma = np.asarray(gamma, np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    r = 1.0 / np.sqrt(var + eps)
+    xh = (x - mu) * r
+    g = dy * gamma
+    dx = r * (g - g.mean(axis=-1, keepdims=True) - xh * (g * xh).mean(axis=-1, keepdims=True))
+    return dx, (dy * xh).sum(axis=0), dy.sum(axis=0)
 
 
 def linear_bwd(x, w, dy):

@@ -1,5 +1,5 @@
 """Pins of the oracle's attention backward, softmax normaliser and linear backward
-(oracle/esm_oracle.py: attention_bwd, attention_lse, linear_bwd), against things other
+(oracle/esm_oracle.py: attention_bwd, attention_lse, linear_bwd, layer_norm_bwd), against things other
 than the oracle's own formulas:
 
 * central finite differences of the forward loss sum(dO * attention(q, k, v))
@@ -159,3 +159,40 @@ def test_linear_bwd_adjoint_identity():
     assert abs(float(np.sum(dx * x)) - ref) <= 1e-9 * abs(ref)
     assert abs(float(np.sum(dw * w)) - ref) <= 1e-9 * abs(ref)
     assert abs(float(db.sum()) - float(dy.sum())) <= 1e-9 * max(1.0, abs(float(dy.sum())))
+
+
+# ---------------------------------------------------------------- LayerNorm backward
+
+def test_layer_norm_bwd_matches_finite_differences():
+    rng = np.random.default_rng(32)
+    M, H = 3, 16
+    x = rng.standard_normal((M, H)) * 2 + 0.5
+    gamma, beta = rng.standard_normal(H), rng.standard_normal(H)
+    dy = rng.standard_normal((M, H))
+    dx, dg, db = O.layer_norm_bwd(x, gamma, dy)
+
+    def loss():
+        return float(np.sum(dy * O.layer_norm(x, gamma, beta)))
+    h = 1e-6
+    for a, da in ((x, dx), (gamma, dg), (beta, db)):
+        flat, g = a.reshape(-1), da.reshape(-1)
+        for i in range(flat.size):
+            old = flat[i]
+            flat[i] = old + h
+            lp = loss()
+            flat[i] = old - h
+            lm = loss()
+            flat[i] = old
+            assert abs((lp - lm) / (2 * h) - g[i]) <= 1e-7 * max(1.0, abs(g[i])), (i, g[i])
+
+
+def test_layer_norm_bwd_row_sums_and_shift():
+    """Every row of dx sums to zero (the output does not change when a constant
+    is added to a row), and dx does not change when the row is shifted."""
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((7, 64))
+    gamma, dy = rng.standard_normal(64), rng.standard_normal((7, 64))
+    dx, _, _ = O.layer_norm_bwd(x, gamma, dy)
+    np.testing.assert_allclose(dx.sum(axis=1), 0.0, atol=1e-12)
+    dx2, _, _ = O.layer_norm_bwd(x + 3.0, gamma, dy)
+    np.testing.assert_allclose(dx2, dx, rtol=1e-9, atol=1e-12)
