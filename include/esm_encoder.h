@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 11
+#define ESM_ABI_VERSION 12
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -415,6 +415,29 @@ esm_status esm_linear_bwd(esm_encoder* enc, const void* x, const void* w, const 
 /* Workspace bytes esm_linear_bwd needs for these sizes (host only). */
 esm_status esm_linear_bwd_workspace_size(int64_t M, int32_t N, int32_t K, size_t* bytes);
 
+/* Backward of the encoder's LayerNorm y = gamma (x - mu) r + beta per row of
+ * H = hidden_size values (mu the row mean, r = 1 / sqrt(var + eps) with the
+ * biased variance; the pre-LN placement of [TE-RU] and [BIO-ACC] 3.1; the
+ * pages time training, [BIO-ACC] 3.2 and 6).  With xh = (x - mu) r and
+ * g = dy gamma:
+ *   dx = r (g - mean(g) - xh mean(g xh))   bf16 [M, H]
+ *   dgamma = sum over rows of dy xh         fp32 [H]
+ *   dbeta  = sum over rows of dy            fp32 [H]
+ * mu and r are recomputed from x (fp32, as the forward).  x, dy bf16 [M, H],
+ * gamma bf16 [H]; tensors 16-byte aligned, dgamma/dbeta 4-byte aligned.
+ * workspace: device, 256-byte aligned, at least
+ * esm_layernorm_bwd_workspace_size(M, H) bytes, overwritten.  Column sums in
+ * a fixed order (deterministic).  dx must not overlap x or dy.  H must be a
+ * multiple of 64 up to 4096 (ESM_ERR_UNSUPPORTED otherwise).  Errors:
+ * ESM_ERR_NULL, ESM_ERR_SHAPE (M < 0), ESM_ERR_UNSUPPORTED, ESM_ERR_WORKSPACE.
+ * M = 0 launches nothing.  Asynchronous on stream. */
+esm_status esm_layernorm_bwd(esm_encoder* enc, const void* x, const void* gamma, const void* dy,
+                             void* dx, float* dgamma, float* dbeta, int64_t M,
+                             void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* Workspace bytes esm_layernorm_bwd needs for M rows of H values (host only). */
+esm_status esm_layernorm_bwd_workspace_size(int64_t M, int32_t H, size_t* bytes);
+
 esm_status esm_layernorm_fwd(esm_encoder* enc, const void* x, const void* gamma,
                              const void* beta, void* y, int64_t M, esm_stream_t stream);
 
@@ -504,7 +527,7 @@ typedef enum {
   ESM_K_HEAD = 10 /* final LayerNorm, LM head, sequence means */,
   ESM_K_BIASED_ATTENTION = 11 /* esm_biased_attention_fwd */,
   ESM_K_ATTENTION_BWD = 12 /* esm_attention_bwd */,
-  ESM_K_LINEAR_BWD = 13 /* esm_linear_bwd */, ESM_K_COUNT = 14
+  ESM_K_LINEAR_BWD = 13 /* esm_linear_bwd, esm_layernorm_bwd */, ESM_K_COUNT = 14
 } esm_kernel_class;
 
 /* When on, every launch is bracketed by HIP events recorded on the launch

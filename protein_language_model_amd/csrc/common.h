@@ -278,6 +278,11 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t st);
 hipError_t launch_transpose_pad(const bf16_t* in, int64_t R, int32_t C, bf16_t* out, int64_t Rp, hipStream_t st);
 hipError_t launch_colsum(const bf16_t* dy, int64_t M, int32_t N, float* part, float* db, hipStream_t st);
 int64_t colsum_chunks(int64_t M);
+// LayerNorm backward: dx [M, H] bf16, dgamma and dbeta [H] fp32; stats [2M]
+// and part [colsum_chunks(M), 2, H] fp32 are scratch.  H a multiple of 64, <= 4096.
+hipError_t launch_layernorm_bwd(const bf16_t* x, const bf16_t* gamma, const bf16_t* dy, bf16_t* dx, float* dgamma,
+                                float* dbeta, int64_t M, int32_t H, float eps, float* stats, float* part,
+                                hipStream_t st);
 
 // Biased attention on [B, N, L, heads, 64] tensors: per (b, n, h),
 // out = softmax(q k^T / 8 + mask[b, n, :] + pair[b, h, :, :]) v.

@@ -1152,6 +1152,45 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
   });
 }
 
+namespace {
+size_t ln_bwd_stats_bytes(int64_t M) { return ((size_t)M * 8 + 255) / 256 * 256; }
+size_t ln_bwd_ws_bytes(int64_t M, int32_t H) {
+  return ln_bwd_stats_bytes(M) + (size_t)colsum_chunks(M) * 2 * H * 4;
+}
+}  // namespace
+
+esm_status esm_layernorm_bwd_workspace_size(int64_t M, int32_t H, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(ESM_ERR_NULL, "NULL argument");
+  if (M < 0 || H <= 0 || H % 64 || H > 4096)
+    return fail(ESM_ERR_SHAPE, "M %lld H %d: H must be a positive multiple of 64, at most 4096", (long long)M, H);
+  *bytes = ln_bwd_ws_bytes(M, H);
+  return ok();
+}
+
+esm_status esm_layernorm_bwd(esm_encoder* e, const void* x, const void* gamma, const void* dy, void* dx,
+                             float* dgamma, float* dbeta, int64_t M, void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !x || !gamma || !dy || !dx || !dgamma || !dbeta || !ws) return fail(ESM_ERR_NULL, "NULL argument");
+  const int32_t H = e->cfg.hidden_size;
+  if (M < 0) return fail(ESM_ERR_SHAPE, "M < 0");
+  if (H % 64 || H > 4096) return fail(ESM_ERR_UNSUPPORTED, "hidden %d: the LayerNorm backward takes multiples of 64 up to 4096", H);
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(dy) || !aligned16(dx) || ((uintptr_t)dgamma & 3u) ||
+      ((uintptr_t)dbeta & 3u) || ((uintptr_t)ws & 255u))
+    return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer (tensors 16 bytes, dgamma/dbeta 4, workspace 256)");
+  const size_t need = ln_bwd_ws_bytes(M, H);
+  if (ws_bytes < need) return fail(ESM_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (M == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  float* stats = (float*)ws;
+  float* part = (float*)((char*)ws + ln_bwd_stats_bytes(M));
+  return timed(e, ESM_K_LINEAR_BWD, st, "layernorm backward", [&] {
+    return launch_layernorm_bwd((const bf16_t*)x, (const bf16_t*)gamma, (const bf16_t*)dy, (bf16_t*)dx, dgamma, dbeta,
+                                M, H, e->cfg.layer_norm_eps, stats, part, st);
+  });
+}
+
 esm_status esm_layernorm_fwd(esm_encoder* e, const void* x, const void* gamma, const void* beta, void* y, int64_t M,
                              esm_stream_t stream) {
   g_last_error.clear();

@@ -1,5 +1,6 @@
-// Helpers of the linear layers' backward for gfx950: a bf16 transpose that
-// zero-pads the rows it produces, and a deterministic column sum.
+// Backward helpers for gfx950: a bf16 transpose that zero-pads the rows it
+// produces and a deterministic column sum (the linear layers' backward), and
+// the LayerNorm backward.
 //
 // For y = x W^T + b (x [M, K], W [N, K], y [M, N]) and an incoming gradient
 // dy, the backward is dx = dy W, dW = dy^T x and db = the column sums of dy
@@ -95,19 +96,171 @@ __global__ __launch_bounds__(256) void k_colsum_partial(const bf16_t* __restrict
   if (t < 64) part[(int64_t)blockIdx.x * N + n0 + t] = red[0][t];
 }
 
-// db[n] = sum over chunks of part[chunk, n], in chunk order.
+// db[n] = sum over chunks of part[chunk * stride + n], in chunk order.
 __global__ __launch_bounds__(256) void k_colsum_final(const float* __restrict__ part, int64_t chunks, int32_t N,
-                                                      float* __restrict__ db) {
+                                                      int32_t stride, float* __restrict__ db) {
   const int n = blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
   float s = 0.f;
-  for (int64_t c = 0; c < chunks; ++c) s += part[c * N + n];
+  for (int64_t c = 0; c < chunks; ++c) s += part[c * stride + n];
   db[n] = s;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ------------------------------------------------------------ LayerNorm backward
+//
+// For y = gamma * (x - mu) r + beta per row (r = 1 / sqrt(var + eps), biased
+// variance) and an incoming gradient dy: with xh = (x - mu) r and g = dy gamma,
+// dx = r (g - mean(g) - xh mean(g xh)); dgamma and dbeta are the column sums
+// of dy xh and dy.  k_ln_bwd_rows: one wave per row (lane l holds chunks
+// l, l + 64, ... of 8 values), two-pass mean and variance in fp32 as the
+// forward takes them, dx, and the row's mu and r for the column pass;
+// k_ln_bwd_cols: per 1024-row chunk and 64 columns, the sums of dy xh and dy
+// (the layout and fixed order of k_colsum_partial); k_colsum_final adds the
+// chunks.
+
+constexpr int kLnMaxCh = 8;  // chunks of 8 per lane: H <= 4096
+
+__global__ __launch_bounds__(256) void k_ln_bwd_rows(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
+                                                     const bf16_t* __restrict__ dy, bf16_t* __restrict__ dx,
+                                                     float* __restrict__ stats, int64_t M, int32_t H, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (m >= M) return;   // whole wave: no barrier below
+  const int nch = H / 8;
+  const bf16_t* xr = x + m * H;
+  const bf16_t* gr = dy + m * H;
+  float xv[kLnMaxCh][8], gv[kLnMaxCh][8];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kLnMaxCh; ++j) {
+    const int c = lane + 64 * j;
+    if (c < nch) {
+      const u32x4 a = *(const u32x4*)(xr + 8 * c);
+      const u32x4 d = *(const u32x4*)(gr + 8 * c);
+      const u32x4 w = *(const u32x4*)(gamma + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[j][2 * e] = bflo(a[e]);
+        xv[j][2 * e + 1] = bfhi(a[e]);
+        gv[j][2 * e] = bflo(d[e]) * bflo(w[e]);
+        gv[j][2 * e + 1] = bfhi(d[e]) * bfhi(w[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += xv[j][e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { xv[j][e] = 0.f; gv[j][e] = 0.f; }
+    }
+  }
+  const float inv_h = 1.0f / (float)H;
+  const float mu = wave_sum(s) * inv_h;
+  float v = 0.f;
+#pragma unroll
+  for (int j = 0; j < kLnMaxCh; ++j)
+    if (lane + 64 * j < nch) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = xv[j][e] - mu;
+        v += t * t;
+      }
+    }
+  const float r = rsqrtf(wave_sum(v) * inv_h + eps);
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int j = 0; j < kLnMaxCh; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xv[j][e] = (xv[j][e] - mu) * r;   // xh (0 past the row: not stored)
+      s1 += gv[j][e];
+      s2 += gv[j][e] * xv[j][e];
+    }
+  const float m1 = wave_sum(s1) * inv_h, m2 = wave_sum(s2) * inv_h;
+  bf16_t* dr = dx + m * H;
+#pragma unroll
+  for (int j = 0; j < kLnMaxCh; ++j) {
+    const int c = lane + 64 * j;
+    if (c < nch) {
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = pack_bf2(r * (gv[j][2 * e] - m1 - xv[j][2 * e] * m2), r * (gv[j][2 * e + 1] - m1 - xv[j][2 * e + 1] * m2));
+      *(u32x4*)(dr + 8 * c) = o;
+    }
+  }
+  if (lane == 0) {
+    stats[2 * m] = mu;
+    stats[2 * m + 1] = r;
+  }
+}
+
+// part[chunk, 0, n] = sum of dy xh, part[chunk, 1, n] = sum of dy over the
+// chunk's rows (fp32, fixed order; the tree of k_colsum_partial).
+__global__ __launch_bounds__(256) void k_ln_bwd_cols(const bf16_t* __restrict__ x, const bf16_t* __restrict__ dy,
+                                                     const float* __restrict__ stats, int64_t M, int32_t H,
+                                                     float* __restrict__ part) {
+  __shared__ float red[2][32][65];
+  const int64_t m0 = (int64_t)blockIdx.x * kSumRows;
+  const int n0 = blockIdx.y * 64;
+  const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
+  float ag[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, ab[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kSumRows / 32; ++i) {
+    const int64_t m = m0 + rg + 32 * i;
+    if (m < M) {
+      const float mu = stats[2 * m], r = stats[2 * m + 1];
+      const u32x4 a = *(const u32x4*)(x + m * H + n0 + cg * 8);
+      const u32x4 d = *(const u32x4*)(dy + m * H + n0 + cg * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d0 = bflo(d[e]), d1 = bfhi(d[e]);
+        ag[2 * e] += d0 * ((bflo(a[e]) - mu) * r);
+        ag[2 * e + 1] += d1 * ((bfhi(a[e]) - mu) * r);
+        ab[2 * e] += d0;
+        ab[2 * e + 1] += d1;
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    red[0][rg][cg * 8 + e] = ag[e];
+    red[1][rg][cg * 8 + e] = ab[e];
+  }
+  __syncthreads();
+  for (int s = 16; s >= 1; s >>= 1) {
+    for (int i = t; i < 128 * s; i += 256) {
+      const int k = i / (64 * s), rem = i % (64 * s), g = rem / 64, c = rem % 64;
+      red[k][g][c] += red[k][g + s][c];
+    }
+    __syncthreads();
+  }
+  if (t < 128) part[((int64_t)blockIdx.x * 2 + (t >> 6)) * H + n0 + (t & 63)] = red[t >> 6][0][t & 63];
 }
 
 }  // namespace
 
 int64_t colsum_chunks(int64_t M) { return (M + kSumRows - 1) / kSumRows; }
+
+hipError_t launch_layernorm_bwd(const bf16_t* x, const bf16_t* gamma, const bf16_t* dy, bf16_t* dx, float* dgamma,
+                                float* dbeta, int64_t M, int32_t H, float eps, float* stats, float* part,
+                                hipStream_t st) {
+  if (M <= 0) return hipSuccess;
+  if (H % 64 || H / 8 > 64 * kLnMaxCh) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_ln_bwd_rows, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st, x, gamma, dy, dx, stats, M, H,
+                     eps);
+  const int64_t chunks = colsum_chunks(M);
+  hipLaunchKernelGGL(k_ln_bwd_cols, dim3((unsigned)chunks, (unsigned)(H / 64)), dim3(256), 0, st, x, dy, stats, M, H,
+                     part);
+  // part is [chunks][2][H]: dgamma from the first H of each chunk, dbeta from the second
+  const dim3 fg((unsigned)((H + 255) / 256));
+  hipLaunchKernelGGL(k_colsum_final, fg, dim3(256), 0, st, part, chunks, H, 2 * H, dgamma);
+  hipLaunchKernelGGL(k_colsum_final, fg, dim3(256), 0, st, part + H, chunks, H, 2 * H, dbeta);
+  return hipGetLastError();
+}
 
 hipError_t launch_transpose_pad(const bf16_t* in, int64_t R, int32_t C, bf16_t* out, int64_t Rp, hipStream_t st) {
   if (C <= 0 || Rp <= 0) return hipSuccess;
@@ -124,7 +277,7 @@ hipError_t launch_colsum(const bf16_t* dy, int64_t M, int32_t N, float* part, fl
   if (chunks > 0)
     hipLaunchKernelGGL(k_colsum_partial, dim3((unsigned)chunks, (unsigned)(N / 64)), dim3(256), 0, st, dy, M, N,
                        part);
-  hipLaunchKernelGGL(k_colsum_final, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, part, chunks, N, db);
+  hipLaunchKernelGGL(k_colsum_final, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, part, chunks, N, N, db);
   return hipGetLastError();
 }
 

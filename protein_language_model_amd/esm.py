@@ -86,6 +86,8 @@ SIGNATURES = {
     "esm_attention_fwd_lse": (_i32, [_p, _p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_linear_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _p, _sz, _p]),
     "esm_linear_bwd_workspace_size": (_i32, [_i64, _i32, _i32, _p]),
+    "esm_layernorm_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _p, _sz, _p]),
+    "esm_layernorm_bwd_workspace_size": (_i32, [_i64, _i32, _p]),
     "esm_attention_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_biased_attention_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "esm_mxfp4_quantize": (_i32, [_p, _p, _i64, _i32, _p, _p, _p]),
@@ -389,6 +391,26 @@ class Encoder:
         _call("esm_attention_bwd", self._h, _ptr(qkv), _ptr(ctx), _ptr(dctx), _ptr(lse), _ptr(delta), _ptr(dqkv),
               _ptr(cu_seqlens), int(B), int(T), _ptr(workspace), workspace.numel(), _stream(stream))
         return dqkv
+
+    def layernorm_bwd(self, x, gamma, dy, *, dx=None, dgamma=None, dbeta=None, workspace=None, stream=None):
+        """Backward of the LayerNorm (gamma, beta over hidden_size): returns
+        (dx [M, H] bf16, dgamma [H] fp32, dbeta [H] fp32)."""
+        import torch
+        M, H = x.shape
+        dev = x.device
+        if dx is None:
+            dx = torch.empty_like(x)
+        if dgamma is None:
+            dgamma = torch.empty((H,), dtype=torch.float32, device=dev)
+        if dbeta is None:
+            dbeta = torch.empty((H,), dtype=torch.float32, device=dev)
+        if workspace is None:
+            n = ctypes.c_size_t()
+            _call("esm_layernorm_bwd_workspace_size", int(M), int(H), ctypes.byref(n))
+            workspace = torch.empty((max(int(n.value), 1),), dtype=torch.uint8, device=dev)
+        _call("esm_layernorm_bwd", self._h, _ptr(x), _ptr(gamma), _ptr(dy), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
+              int(M), _ptr(workspace), workspace.numel(), _stream(stream))
+        return dx, dgamma, dbeta
 
     @staticmethod
     def linear_bwd_workspace_size(M: int, N: int, K: int) -> int:
