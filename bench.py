@@ -15,8 +15,9 @@ Evoformer attention with a mask bias and a pair bias) is timed on its own
 synthetic MSA-row shape under "biased_attention", the MXFP4 quantiser and
 GEMM (the FP4 recipe) on the layer's four GEMM shapes under "mxfp4", the
 whole stack with MXFP4 GEMMs under "mxfp4_stack", the attention backward
-on the batch's sequences under "attention_bwd" and the linear backward on the
-layer's four shapes under "linear_bwd".
+on the batch's sequences under "attention_bwd", the linear backward on the
+layer's four shapes under "linear_bwd" and the LayerNorm backward on [T, H]
+under "layernorm_bwd".
 Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
@@ -65,7 +66,7 @@ def parse():
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip timing the final LayerNorm / LM head / means")
     ap.add_argument("--no-linear-bwd", action="store_true",
-                    help="skip timing the linear backward on the layer's four shapes")
+                    help="skip timing the linear and LayerNorm backward on the layer's shapes")
     ap.add_argument("--no-attention-bwd", action="store_true",
                     help="skip timing the attention backward on the batch")
     ap.add_argument("--no-biased-attention", action="store_true",
@@ -340,6 +341,43 @@ def bench_linear_bwd(enc, T: int, H: int, F: int, steps: int, dev: str, stream) 
     return out
 
 
+def bench_layernorm_bwd(enc, T: int, H: int, steps: int, dev: str, stream) -> dict:
+    """esm_layernorm_bwd on [T, H] (x N(0, 1), gamma 1 + N(0, 0.04), dy N(0, 1)
+    bf16); HIP events over back-to-back calls.  HBM roofline on the
+    algorithmic bytes: x and dy read once, dx written (the column pass reads
+    x and dy a second time, which is counted as time, not bytes)."""
+    import torch
+    g = torch.Generator(device=dev).manual_seed(13)
+    x = torch.randn((T, H), device=dev, generator=g).to(torch.bfloat16)
+    gamma = (1 + 0.2 * torch.randn((H,), device=dev, generator=g)).to(torch.bfloat16)
+    dy = torch.randn((T, H), device=dev, generator=g).to(torch.bfloat16)
+    dx = torch.empty_like(x)
+    dgamma = torch.empty((H,), dtype=torch.float32, device=dev)
+    dbeta = torch.empty((H,), dtype=torch.float32, device=dev)
+    ws = torch.empty((64 << 20,), dtype=torch.uint8, device=dev)
+
+    def call():
+        enc.layernorm_bwd(x, gamma, dy, dx=dx, dgamma=dgamma, dbeta=dbeta, workspace=ws, stream=stream)
+
+    for _ in range(3):
+        call()
+    n = max(10, steps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    nbytes = 3 * T * H * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del x, gamma, dy, dx, dgamma, dbeta, ws
+    return {"shape": f"x, dy, dx [{T}, {H}] bf16; dgamma, dbeta [{H}] fp32", "us_per_call": round(ms * 1e3, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": nbytes}}
+
+
 def bench_mxfp4(enc, T: int, H: int, F: int, steps: int, dev: str, stream) -> dict:
     """The MXFP4 (FP4 recipe) quantiser and GEMM alone on the four linears'
     shapes of one layer of this batch: bf16 activations and weights N(0, 1) /
@@ -546,9 +584,10 @@ def main():
     if not args.no_attention_bwd:
         attn_bwd = bench_attention_bwd(enc, batch, cu, ws, m.heads, args.steps, dev, stream)
 
-    lin_bwd = None
+    lin_bwd = ln_bwd = None
     if not args.no_linear_bwd:
         lin_bwd = bench_linear_bwd(enc, T, m.hidden, m.ffn, args.steps, dev, stream)
+        ln_bwd = bench_layernorm_bwd(enc, T, m.hidden, args.steps, dev, stream)
 
     mxfp4 = None
     if not args.no_mxfp4:
@@ -647,6 +686,7 @@ def main():
         "mxfp4": mxfp4,
         "attention_bwd": attn_bwd,
         "linear_bwd": lin_bwd,
+        "layernorm_bwd": ln_bwd,
         "mxfp4_stack": mx_stack,
         "vendor_gemm_fc1": vendor,
         "fp8": fp8,

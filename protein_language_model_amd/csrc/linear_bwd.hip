@@ -96,6 +96,17 @@ __global__ __launch_bounds__(256) void k_colsum_partial(const bf16_t* __restrict
   if (t < 64) part[(int64_t)blockIdx.x * N + n0 + t] = red[0][t];
 }
 
+// dgamma[n] / dbeta[n] = sums over chunks of part[chunk, 0, n] / part[chunk, 1, n].
+__global__ __launch_bounds__(256) void k_ln_cols_final(const float* __restrict__ part, int64_t chunks, int32_t H,
+                                                       float* __restrict__ dgamma, float* __restrict__ dbeta) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= 2 * H) return;
+  float s = 0.f;
+  for (int64_t c = 0; c < chunks; ++c) s += part[c * 2 * H + n];
+  if (n < H) dgamma[n] = s;
+  else dbeta[n - H] = s;
+}
+
 // db[n] = sum over chunks of part[chunk * stride + n], in chunk order.
 __global__ __launch_bounds__(256) void k_colsum_final(const float* __restrict__ part, int64_t chunks, int32_t N,
                                                       int32_t stride, float* __restrict__ db) {
@@ -126,6 +137,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 constexpr int kLnMaxCh = 8;  // chunks of 8 per lane: H <= 4096
 
+// kLnMaxCh here is the number of 8-value chunks per lane (H <= 512 kLnMaxCh),
+// a template argument so that the row lives in as few registers as H needs.
+template <int kLnMaxCh>
 __global__ __launch_bounds__(256) void k_ln_bwd_rows(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
                                                      const bf16_t* __restrict__ dy, bf16_t* __restrict__ dx,
                                                      float* __restrict__ stats, int64_t M, int32_t H, float eps) {
@@ -250,15 +264,18 @@ hipError_t launch_layernorm_bwd(const bf16_t* x, const bf16_t* gamma, const bf16
                                 hipStream_t st) {
   if (M <= 0) return hipSuccess;
   if (H % 64 || H / 8 > 64 * kLnMaxCh) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_ln_bwd_rows, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st, x, gamma, dy, dx, stats, M, H,
-                     eps);
+  const int ch = (H / 8 + 63) / 64;
+  const dim3 rg((unsigned)((M + 3) / 4));
+  if (ch <= 1) hipLaunchKernelGGL(k_ln_bwd_rows<1>, rg, dim3(256), 0, st, x, gamma, dy, dx, stats, M, H, eps);
+  else if (ch <= 2) hipLaunchKernelGGL(k_ln_bwd_rows<2>, rg, dim3(256), 0, st, x, gamma, dy, dx, stats, M, H, eps);
+  else if (ch <= 3) hipLaunchKernelGGL(k_ln_bwd_rows<3>, rg, dim3(256), 0, st, x, gamma, dy, dx, stats, M, H, eps);
+  else if (ch <= 5) hipLaunchKernelGGL(k_ln_bwd_rows<5>, rg, dim3(256), 0, st, x, gamma, dy, dx, stats, M, H, eps);
+  else hipLaunchKernelGGL(k_ln_bwd_rows<8>, rg, dim3(256), 0, st, x, gamma, dy, dx, stats, M, H, eps);
   const int64_t chunks = colsum_chunks(M);
   hipLaunchKernelGGL(k_ln_bwd_cols, dim3((unsigned)chunks, (unsigned)(H / 64)), dim3(256), 0, st, x, dy, stats, M, H,
                      part);
-  // part is [chunks][2][H]: dgamma from the first H of each chunk, dbeta from the second
-  const dim3 fg((unsigned)((H + 255) / 256));
-  hipLaunchKernelGGL(k_colsum_final, fg, dim3(256), 0, st, part, chunks, H, 2 * H, dgamma);
-  hipLaunchKernelGGL(k_colsum_final, fg, dim3(256), 0, st, part + H, chunks, H, 2 * H, dbeta);
+  hipLaunchKernelGGL(k_ln_cols_final, dim3((unsigned)((2 * H + 255) / 256)), dim3(256), 0, st, part, chunks, H,
+                     dgamma, dbeta);
   return hipGetLastError();
 }
 
