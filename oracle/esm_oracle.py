@@ -42,7 +42,8 @@ Readings where the pages are silent (each is listed in the design notes):
   decoder tied to the embedding, and per-sequence mean embeddings.
 
 linear_bwd and layer_norm_bwd give the gradients of a linear layer (dx, dW,
-db) and of a LayerNorm (dx, dgamma, dbeta).
+db) and of a LayerNorm (dx, dgamma, dbeta); gelu_bwd, rope_bwd and
+qkv_rope_bwd those of GELU, of the rotary embedding and of the QKV split.
 attention_lse and attention_bwd give the softmax normaliser a backward pass
 keeps and the gradients of the attention with respect to q, k and v: the
 backward of the training runs the pages time ([BIO-ACC] 3.2 and 6, [CARD]
@@ -251,6 +252,31 @@ def layer_norm_bwd(x, gamma, dy, eps: float = LN_EPS):
     g = dy * gamma
     dx = r * (g - g.mean(axis=-1, keepdims=True) - xh * (g * xh).mean(axis=-1, keepdims=True))
     return dx, (dy * xh).sum(axis=0), dy.sum(axis=0)
+
+
+def gelu_bwd(z, dy) -> np.ndarray:
+    """dz = dy * GELU'(z) with GELU'(z) = Phi(z) + z phi(z) (the derivative of
+    the exact-erf GELU above; phi the standard normal density)."""
+    z = np.asarray(z, np.float64)
+    phi = np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+    return np.asarray(dy, np.float64) * (0.5 * (1.0 + _erf(z / math.sqrt(2.0))) + z * phi)
+
+
+def rope_bwd(du, pos, base: float = ROPE_BASE) -> np.ndarray:
+    """Gradient through apply_rope: each pair is rotated by -theta (the
+    rotation's transpose): a = a' cos + b' sin, b = b' cos - a' sin."""
+    return apply_rope(du, -np.asarray(pos, np.float64), base)
+
+
+def qkv_rope_bwd(dq, dk, dv, cu_seqlens, base: float = ROPE_BASE) -> np.ndarray:
+    """Gradient of the QKV linear's output y [T, 3H] (interleaved columns
+    192 n + 64 c + j, c = q, k, v) from the gradients of the rotated q, k
+    and of v, each [T, heads, 64]: the inverse of split_qkv after undoing the
+    rotation of q and k at every row's position."""
+    pos = positions(cu_seqlens)
+    parts = [rope_bwd(dq, pos, base), rope_bwd(dk, pos, base), np.asarray(dv, np.float64)]
+    T, heads, d = parts[0].shape
+    return np.stack(parts, axis=2).reshape(T, heads * 3 * d)
 
 
 def linear_bwd(x, w, dy):

@@ -1,5 +1,5 @@
 """Pins of the oracle's attention backward, softmax normaliser and linear backward
-(oracle/esm_oracle.py: attention_bwd, attention_lse, linear_bwd, layer_norm_bwd), against things other
+(oracle/esm_oracle.py: attention_bwd, attention_lse, linear_bwd, layer_norm_bwd, gelu_bwd, rope_bwd, qkv_rope_bwd), against things other
 than the oracle's own formulas:
 
 * central finite differences of the forward loss sum(dO * attention(q, k, v))
@@ -196,3 +196,48 @@ def test_layer_norm_bwd_row_sums_and_shift():
     np.testing.assert_allclose(dx.sum(axis=1), 0.0, atol=1e-12)
     dx2, _, _ = O.layer_norm_bwd(x + 3.0, gamma, dy)
     np.testing.assert_allclose(dx2, dx, rtol=1e-9, atol=1e-12)
+
+
+# ---------------------------------------------------------------- GELU and RoPE backward
+
+def test_gelu_bwd_finite_differences_and_closed_forms():
+    rng = np.random.default_rng(34)
+    z = np.concatenate([rng.standard_normal(40) * 3, [0.0, -8.0, 8.0, 1.0]])
+    dy = rng.standard_normal(z.size)
+    got = O.gelu_bwd(z, dy)
+    h = 1e-6
+    fd = (O.gelu(z + h) - O.gelu(z - h)) / (2 * h) * dy
+    np.testing.assert_allclose(got, fd, rtol=1e-7, atol=1e-8)
+    one = np.ones_like(z)
+    # GELU(z) - GELU(-z) = z, so GELU'(z) + GELU'(-z) = 1; GELU'(0) = 1/2
+    np.testing.assert_allclose(O.gelu_bwd(z, one) + O.gelu_bwd(-z, one), 1.0, atol=1e-14)
+    assert O.gelu_bwd(np.array([0.0]), np.array([1.0]))[0] == 0.5
+
+
+def test_rope_bwd_is_the_transpose():
+    rng = np.random.default_rng(35)
+    T, heads = 9, 3
+    pos = rng.integers(0, 1000, T)
+    u, du = rng.standard_normal((T, heads, 64)), rng.standard_normal((T, heads, 64))
+    # adjoint: <du, R u> = <R^T du, u>; orthogonal: R^T R u = u
+    lhs = float(np.sum(du * O.apply_rope(u, pos)))
+    assert abs(lhs - float(np.sum(O.rope_bwd(du, pos) * u))) <= 1e-10 * max(1.0, abs(lhs))
+    np.testing.assert_allclose(O.rope_bwd(O.apply_rope(u, pos), pos), u, atol=1e-12)
+
+
+def test_qkv_rope_bwd_adjoint_of_split_and_rotate():
+    """f(y) = (rope(q(y)), rope(k(y)), v(y)) with (q, k, v) = split_qkv(y) is
+    linear in y; its backward g satisfies <(dq, dk, dv), f(y)> = <g(dq, dk, dv), y>
+    for every y, and must undo the per-sequence positions."""
+    rng = np.random.default_rng(36)
+    lens, heads = [5, 1, 7], 2
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    pos = O.positions(cu)
+    for _ in range(3):
+        y = rng.standard_normal((T, 3 * heads * 64))
+        dq, dk, dv = (rng.standard_normal((T, heads, 64)) for _ in range(3))
+        q, k, v = O.split_qkv(y, heads)
+        lhs = float(np.sum(dq * O.apply_rope(q, pos)) + np.sum(dk * O.apply_rope(k, pos)) + np.sum(dv * v))
+        rhs = float(np.sum(O.qkv_rope_bwd(dq, dk, dv, cu) * y))
+        assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs))
