@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 12
+#define ESM_ABI_VERSION 13
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -438,6 +438,30 @@ esm_status esm_layernorm_bwd(esm_encoder* enc, const void* x, const void* gamma,
 /* Workspace bytes esm_layernorm_bwd needs for M rows of H values (host only). */
 esm_status esm_layernorm_bwd_workspace_size(int64_t M, int32_t H, size_t* bytes);
 
+/* Backward of the exact-erf GELU of fc1's epilogue ([BIO-ACC] 3.1; training
+ * timed in [BIO-ACC] 3.2 and 6): dz[i] = dy[i] (Phi(z[i]) + z[i] phi(z[i]))
+ * with Phi, phi the standard normal distribution and density.  z is the
+ * pre-activation (x W1^T + b1, e.g. from esm_linear_fwd with ESM_EPI_BIAS),
+ * dy the gradient of GELU(z); all bf16, n values, n a multiple of 8, 16-byte
+ * aligned; dz may alias dy.  Errors: ESM_ERR_NULL, ESM_ERR_SHAPE,
+ * ESM_ERR_UNSUPPORTED.  Asynchronous on stream. */
+esm_status esm_gelu_bwd(esm_encoder* enc, const void* z, const void* dy, void* dz, int64_t n,
+                        esm_stream_t stream);
+
+/* Backward of the QKV split and the rotary embedding ([TE-ESM2] 旋转位置编码集成
+ * and 权重融合技术): from dqkv, bf16 [3, heads, T, 64] (the gradients of the
+ * rotated q, k and of v, as esm_attention_bwd writes them), writes dy, bf16
+ * [T, 3H], the gradient of the fused QKV linear's output in its interleaved
+ * column order 192 n + 64 c + j: v copied, q and k turned back by each row's
+ * angle p theta_i (p the row's position in its sequence, from cu_seqlens;
+ * pairs (j, j + 32): a = a' cos + b' sin, b = b' cos - a' sin), with the
+ * forward's rotary table.  Runs the segment table first (workspace as
+ * esm_attention_fwd).  dy must not overlap dqkv.  Errors as
+ * esm_attention_fwd.  Asynchronous on stream. */
+esm_status esm_qkv_rope_bwd(esm_encoder* enc, const void* dqkv, void* dy,
+                            const int32_t* cu_seqlens_dev, int32_t B, int64_t T,
+                            void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
 esm_status esm_layernorm_fwd(esm_encoder* enc, const void* x, const void* gamma,
                              const void* beta, void* y, int64_t M, esm_stream_t stream);
 
@@ -527,7 +551,8 @@ typedef enum {
   ESM_K_HEAD = 10 /* final LayerNorm, LM head, sequence means */,
   ESM_K_BIASED_ATTENTION = 11 /* esm_biased_attention_fwd */,
   ESM_K_ATTENTION_BWD = 12 /* esm_attention_bwd */,
-  ESM_K_LINEAR_BWD = 13 /* esm_linear_bwd, esm_layernorm_bwd */, ESM_K_COUNT = 14
+  ESM_K_LINEAR_BWD = 13 /* esm_linear_bwd, esm_layernorm_bwd, esm_gelu_bwd, esm_qkv_rope_bwd */,
+  ESM_K_COUNT = 14
 } esm_kernel_class;
 
 /* When on, every launch is bracketed by HIP events recorded on the launch

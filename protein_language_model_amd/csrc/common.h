@@ -280,6 +280,12 @@ hipError_t launch_colsum(const bf16_t* dy, int64_t M, int32_t N, float* part, fl
 int64_t colsum_chunks(int64_t M);
 // LayerNorm backward: dx [M, H] bf16, dgamma and dbeta [H] fp32; stats [2M]
 // and part [colsum_chunks(M), 2, H] fp32 are scratch.  H a multiple of 64, <= 4096.
+// GELU backward: dz = dy GELU'(z), n % 8 == 0.  QKV/RoPE backward: planar
+// dqkv [3, heads, T, 64] -> dy [T, 3H] in the fused QKV linear's interleaved
+// column order, q and k rotated back by the row positions pos [T].
+hipError_t launch_gelu_bwd(const bf16_t* z, const bf16_t* dy, bf16_t* dz, int64_t n, hipStream_t st);
+hipError_t launch_qkv_rope_bwd(const bf16_t* dqkv, const int32_t* pos, const float2* rope, int32_t max_positions,
+                               int64_t T, int32_t heads, bf16_t* dy, hipStream_t st);
 hipError_t launch_layernorm_bwd(const bf16_t* x, const bf16_t* gamma, const bf16_t* dy, bf16_t* dx, float* dgamma,
                                 float* dbeta, int64_t M, int32_t H, float eps, float* stats, float* part,
                                 hipStream_t st);

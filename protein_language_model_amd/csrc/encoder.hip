@@ -1191,6 +1191,39 @@ esm_status esm_layernorm_bwd(esm_encoder* e, const void* x, const void* gamma, c
   });
 }
 
+esm_status esm_gelu_bwd(esm_encoder* e, const void* z, const void* dy, void* dz, int64_t n, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !z || !dy || !dz) return fail(ESM_ERR_NULL, "NULL argument");
+  if (n < 0 || n % 8) return fail(ESM_ERR_SHAPE, "n %lld: a non-negative multiple of 8", (long long)n);
+  if (!aligned16(z) || !aligned16(dy) || !aligned16(dz)) return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer");
+  if (n == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  return timed(e, ESM_K_LINEAR_BWD, st, "gelu backward", [&] {
+    return launch_gelu_bwd((const bf16_t*)z, (const bf16_t*)dy, (bf16_t*)dz, n, st);
+  });
+}
+
+esm_status esm_qkv_rope_bwd(esm_encoder* e, const void* dqkv, void* dy, const int32_t* cu_dev, int32_t B, int64_t T,
+                            void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !dqkv || !dy || !cu_dev) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!aligned16(dqkv) || !aligned16(dy)) return fail(ESM_ERR_UNSUPPORTED, "dqkv/dy not 16-byte aligned");
+  esm_status s = check_rows(e, T, B);
+  if (s) return s;
+  if (T == 0 || B == 0) return ok();
+  Plan p;
+  if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  if ((s = run_segments(e, 0, cu_dev, B, T, 0, ws, p, st))) return s;
+  const int32_t* pos = region<int32_t>(ws, p, ESM_WS_POS);
+  return timed(e, ESM_K_LINEAR_BWD, st, "qkv rope backward", [&] {
+    return launch_qkv_rope_bwd((const bf16_t*)dqkv, pos, e->rope, e->cfg.max_position_embeddings, T,
+                               e->cfg.num_attention_heads, (bf16_t*)dy, st);
+  });
+}
+
 esm_status esm_layernorm_fwd(esm_encoder* e, const void* x, const void* gamma, const void* beta, void* y, int64_t M,
                              esm_stream_t stream) {
   g_last_error.clear();

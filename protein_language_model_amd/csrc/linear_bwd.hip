@@ -255,9 +255,82 @@ __global__ __launch_bounds__(256) void k_ln_bwd_cols(const bf16_t* __restrict__ 
   if (t < 128) part[((int64_t)blockIdx.x * 2 + (t >> 6)) * H + n0 + (t & 63)] = red[t >> 6][0][t & 63];
 }
 
+// ------------------------------------------------------------ GELU, RoPE backward
+
+// dz = dy (Phi(z) + z phi(z)), 8 values per thread (16-byte loads); n % 8 == 0.
+__global__ __launch_bounds__(256) void k_gelu_bwd(const bf16_t* __restrict__ z, const bf16_t* __restrict__ dy,
+                                                  bf16_t* __restrict__ dz, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const u32x4 a = *(const u32x4*)(z + 8 * i);
+  const u32x4 d = *(const u32x4*)(dy + 8 * i);
+  constexpr float kRsqrt2 = 0.70710678118654752f, kRsqrt2Pi = 0.39894228040143268f;
+  auto dg = [&](float v) { return 0.5f * (1.0f + erff(v * kRsqrt2)) + v * kRsqrt2Pi * expf(-0.5f * v * v); };
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = pack_bf2(bflo(d[e]) * dg(bflo(a[e])), bfhi(d[e]) * dg(bfhi(a[e])));
+  *(u32x4*)(dz + 8 * i) = o;
+}
+
+// dy[t, 192 n + 64 c + j] from the planar gradients dqkv[c][n][t][j] of the
+// rotated q, k and of v: for c < 2 each pair (j, j + 32) turns back by the
+// row's angle (a = a' cos + b' sin, b = b' cos - a' sin), v is copied.  One
+// thread per (t, n, c, 8 pairs); positions clamped to the table as in the
+// forward epilogue.
+__global__ __launch_bounds__(256) void k_qkv_rope_bwd(const bf16_t* __restrict__ dqkv, const int32_t* __restrict__ pos,
+                                                      const float2* __restrict__ rope, int32_t max_positions,
+                                                      int64_t T, int32_t heads, bf16_t* __restrict__ dy) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= T * heads * 3 * 4) return;
+  const int i0 = 8 * (int)(g & 3);
+  const int64_t rest = g >> 2;
+  const int c = (int)(rest % 3);
+  const int n = (int)((rest / 3) % heads);
+  const int64_t t = rest / (3 * heads);
+  const bf16_t* src = dqkv + (((int64_t)c * heads + n) * T + t) * kHeadDim;
+  bf16_t* dst = dy + t * (3 * (int64_t)heads * kHeadDim) + 192 * n + 64 * c;
+  const u32x4 lo = *(const u32x4*)(src + i0);
+  const u32x4 hi = *(const u32x4*)(src + 32 + i0);
+  if (c == 2) {
+    *(u32x4*)(dst + i0) = lo;
+    *(u32x4*)(dst + 32 + i0) = hi;
+    return;
+  }
+  int p = pos[t];
+  p = p < 0 ? 0 : (p < max_positions ? p : max_positions - 1);
+  const float2* cs = rope + (int64_t)p * 32 + i0;
+  u32x4 oa, ob;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float2 c0 = cs[2 * e], c1 = cs[2 * e + 1];
+    const float a0 = bflo(lo[e]), a1 = bfhi(lo[e]), b0 = bflo(hi[e]), b1 = bfhi(hi[e]);
+    oa[e] = pack_bf2(a0 * c0.x + b0 * c0.y, a1 * c1.x + b1 * c1.y);
+    ob[e] = pack_bf2(b0 * c0.x - a0 * c0.y, b1 * c1.x - a1 * c1.y);
+  }
+  *(u32x4*)(dst + i0) = oa;
+  *(u32x4*)(dst + 32 + i0) = ob;
+}
+
 }  // namespace
 
 int64_t colsum_chunks(int64_t M) { return (M + kSumRows - 1) / kSumRows; }
+
+hipError_t launch_gelu_bwd(const bf16_t* z, const bf16_t* dy, bf16_t* dz, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(k_gelu_bwd, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, z, dy, dz, n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_rope_bwd(const bf16_t* dqkv, const int32_t* pos, const float2* rope, int32_t max_positions,
+                               int64_t T, int32_t heads, bf16_t* dy, hipStream_t st) {
+  if (T <= 0 || heads <= 0) return hipSuccess;
+  const int64_t nt = T * heads * 3 * 4;
+  hipLaunchKernelGGL(k_qkv_rope_bwd, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, st, dqkv, pos, rope,
+                     max_positions, T, heads, dy);
+  return hipGetLastError();
+}
 
 hipError_t launch_layernorm_bwd(const bf16_t* x, const bf16_t* gamma, const bf16_t* dy, bf16_t* dx, float* dgamma,
                                 float* dbeta, int64_t M, int32_t H, float eps, float* stats, float* part,

@@ -88,6 +88,8 @@ SIGNATURES = {
     "esm_linear_bwd_workspace_size": (_i32, [_i64, _i32, _i32, _p]),
     "esm_layernorm_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _p, _sz, _p]),
     "esm_layernorm_bwd_workspace_size": (_i32, [_i64, _i32, _p]),
+    "esm_gelu_bwd": (_i32, [_p, _p, _p, _p, _i64, _p]),
+    "esm_qkv_rope_bwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_attention_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_biased_attention_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
     "esm_mxfp4_quantize": (_i32, [_p, _p, _i64, _i32, _p, _p, _p]),
@@ -411,6 +413,26 @@ class Encoder:
         _call("esm_layernorm_bwd", self._h, _ptr(x), _ptr(gamma), _ptr(dy), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
               int(M), _ptr(workspace), workspace.numel(), _stream(stream))
         return dx, dgamma, dbeta
+
+    def gelu_bwd(self, z, dy, *, dz=None, stream=None):
+        """dz = dy * GELU'(z) (bf16, same shape; the element count a multiple of 8)."""
+        import torch
+        if dz is None:
+            dz = torch.empty_like(dy)
+        _call("esm_gelu_bwd", self._h, _ptr(z), _ptr(dy), _ptr(dz), int(z.numel()), _stream(stream))
+        return dz
+
+    def qkv_rope_bwd(self, dqkv, cu_seqlens, B: int, T: int, *, dy=None, workspace=None, stream=None):
+        """dy [T, 3H] (the fused QKV linear's output gradient, interleaved
+        columns) from the planar dqkv [3, heads, T, 64] of esm_attention_bwd."""
+        import torch
+        if dy is None:
+            dy = torch.empty((T, 3 * self.hidden), dtype=torch.bfloat16, device=dqkv.device)
+        if workspace is None:
+            workspace = self.workspace(T, B)
+        _call("esm_qkv_rope_bwd", self._h, _ptr(dqkv), _ptr(dy), _ptr(cu_seqlens), int(B), int(T), _ptr(workspace),
+              workspace.numel(), _stream(stream))
+        return dy
 
     @staticmethod
     def linear_bwd_workspace_size(M: int, N: int, K: int) -> int:
