@@ -43,7 +43,8 @@ Readings where the pages are silent (each is listed in the design notes):
 
 linear_bwd and layer_norm_bwd give the gradients of a linear layer (dx, dW,
 db) and of a LayerNorm (dx, dgamma, dbeta); gelu_bwd, rope_bwd and
-qkv_rope_bwd those of GELU, of the rotary embedding and of the QKV split.
+qkv_rope_bwd those of GELU, of the rotary embedding and of the QKV split;
+layer_backward chains them through one whole layer.
 attention_lse and attention_bwd give the softmax normaliser a backward pass
 keeps and the gradients of the attention with respect to q, k and v: the
 backward of the training runs the pages time ([BIO-ACC] 3.2 and 6, [CARD]
@@ -321,6 +322,31 @@ def layer_forward(x, cu_seqlens, w: Dict[str, np.ndarray], heads: int,
     if return_intermediates:
         return x2, dict(h1=h1, q=qr, k=kr, v=v, ctx=ctx, x1=x1, h2=h2, a=a)
     return x2
+
+
+def layer_backward(x, cu_seqlens, w: Dict[str, np.ndarray], heads: int, dout,
+                   eps: float = LN_EPS, base: float = ROPE_BASE):
+    """Gradients of sum(dout * layer_forward(x)) with respect to x and every
+    weight, by the chain rule through the layer's steps in reverse, each step
+    the backward above (linear_bwd, gelu_bwd, layer_norm_bwd, attention_bwd,
+    qkv_rope_bwd; the residual adds pass the gradient through).  Returns
+    (dx [T, H], {name: gradient} with the names of w)."""
+    x = np.asarray(x, np.float64)
+    dout = np.asarray(dout, np.float64)
+    T, H = x.shape
+    F = w["w_fc1"].shape[0]
+    _, im = layer_forward(x, cu_seqlens, w, heads, eps, base, return_intermediates=True)
+    z = im["h2"] @ w["w_fc1"].T + _bias(w, "b_fc1", F)
+    g = {}
+    da, g["w_fc2"], g["b_fc2"] = linear_bwd(im["a"], w["w_fc2"], dout)
+    dh2, g["w_fc1"], g["b_fc1"] = linear_bwd(im["h2"], w["w_fc1"], gelu_bwd(z, da))
+    dx1_ln, g["ln2_gamma"], g["ln2_beta"] = layer_norm_bwd(im["x1"], w["ln2_gamma"], dh2, eps)
+    dx1 = dout + dx1_ln
+    dctx, g["w_out"], g["b_out"] = linear_bwd(im["ctx"], w["w_out"], dx1)
+    dq, dk, dv = attention_bwd(im["q"], im["k"], im["v"], dctx, cu_seqlens)
+    dh1, g["w_qkv"], g["b_qkv"] = linear_bwd(im["h1"], w["w_qkv"], qkv_rope_bwd(dq, dk, dv, cu_seqlens, base))
+    dx_ln, g["ln1_gamma"], g["ln1_beta"] = layer_norm_bwd(x, w["ln1_gamma"], dh1, eps)
+    return dx1 + dx_ln, g
 
 
 def layer_forward_seqs(x, cu_seqlens, w, heads: int, seqs: Sequence[int], **kw):

@@ -241,3 +241,40 @@ def test_qkv_rope_bwd_adjoint_of_split_and_rotate():
         lhs = float(np.sum(dq * O.apply_rope(q, pos)) + np.sum(dk * O.apply_rope(k, pos)) + np.sum(dv * v))
         rhs = float(np.sum(O.qkv_rope_bwd(dq, dk, dv, cu) * y))
         assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs))
+
+
+# ---------------------------------------------------------------- whole layer
+
+def test_layer_backward_matches_finite_differences():
+    """The chained layer backward against central differences of the whole
+    layer forward (H = 128, 2 heads, F = 256, two sequences), at random
+    coordinates of x and of every weight."""
+    rng = np.random.default_rng(37)
+    H, heads, F = 128, 2, 256
+    lens = [4, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    w = {"ln1_gamma": 1 + 0.1 * rng.standard_normal(H), "ln1_beta": 0.1 * rng.standard_normal(H),
+         "w_qkv": 0.1 * rng.standard_normal((3 * H, H)), "b_qkv": 0.1 * rng.standard_normal(3 * H),
+         "w_out": 0.1 * rng.standard_normal((H, H)), "b_out": 0.1 * rng.standard_normal(H),
+         "ln2_gamma": 1 + 0.1 * rng.standard_normal(H), "ln2_beta": 0.1 * rng.standard_normal(H),
+         "w_fc1": 0.1 * rng.standard_normal((F, H)), "b_fc1": 0.1 * rng.standard_normal(F),
+         "w_fc2": 0.1 * rng.standard_normal((H, F)), "b_fc2": 0.1 * rng.standard_normal(H)}
+    x = rng.standard_normal((T, H))
+    dout = rng.standard_normal((T, H))
+    dx, g = O.layer_backward(x, cu, w, heads, dout)
+
+    def loss():
+        return float(np.sum(dout * O.layer_forward(x, cu, w, heads)))
+    h = 1e-5
+    for name, a, da in [("x", x, dx)] + [(k, w[k], g[k]) for k in w]:
+        flat, gf = a.reshape(-1), da.reshape(-1)
+        for i in rng.choice(flat.size, size=6, replace=False):
+            old = flat[i]
+            flat[i] = old + h
+            lp = loss()
+            flat[i] = old - h
+            lm = loss()
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - gf[i]) <= 1e-6 * max(1.0, abs(fd)), (name, i, fd, gf[i])
