@@ -1,0 +1,77 @@
+"""One whole encoder layer's backward through the C ABI: the backward entry
+points chained in reverse order of the forward (fc2, GELU, fc1, LN2, residual,
+out-projection, attention, QKV split/RoPE, QKV, LN1, residual), on activations
+of the layer's forward, against the oracle's layer_backward (pinned by finite
+differences of the layer forward).
+
+Saved activations: the fp64 forward's h1, rotated q and k, v, x1, h2, the fc1
+pre-activation z and a = GELU(z), each rounded to bf16 (what a bf16 forward
+keeps); the attention context and lse come from esm_attention_fwd_lse on those
+q, k, v.  The residual adds of the gradient are fp32 additions in the test.
+Tolerance: every gradient within 2e-2 (max|err| / max|ref|): a chain of about
+ten bf16 roundings (2^-9 each) of operands and results.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import esm_oracle as O
+from protein_language_model_amd import datagen as D
+from protein_language_model_amd import esm
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def gu():
+    import gpu_util
+    return gpu_util
+
+
+def test_layer_backward_chain(gu):
+    H, heads, F = 320, 5, 1280
+    lens = [17, 100, 64, 1]
+    cu = D.cu_from_lengths(lens)
+    T, B = int(cu[-1]), len(lens)
+    dev_w, w, _ = gu.layer_weights(H, F, seed=3, random_ln=True)
+    r = np.random.default_rng(90)
+    xb = D.to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+    gb = D.to_bf16_bits(r.standard_normal((T, H)).astype(np.float32))
+    x, dout = D.bf16_bits_to_f64(xb), D.bf16_bits_to_f64(gb)
+    _, im = O.layer_forward(x, cu, w, heads, return_intermediates=True)
+    z = im["h2"] @ w["w_fc1"].T + w["b_fc1"]
+
+    def dev(a):
+        return gu.to_dev_bf16(D.to_bf16_bits(np.asarray(a, np.float32)))
+
+    enc = esm.Encoder(hidden_size=H, num_attention_heads=heads, intermediate_size=F, num_hidden_layers=1)
+    try:
+        cu_d = gu.to_dev_i32(cu)
+        planar = torch.stack([dev(im[c].transpose(1, 0, 2)) for c in ("q", "k", "v")])   # [3, heads, T, 64]
+        ctx, lse = enc.attention_fwd_lse(planar, cu_d, B, T)
+        g_out = gu.to_dev_bf16(gb)
+        da, dw_fc2, db_fc2 = enc.linear_bwd(dev(im["a"]), dev_w["w_fc2"], g_out)
+        dz = enc.gelu_bwd(dev(z), da)
+        dh2, dw_fc1, db_fc1 = enc.linear_bwd(dev(im["h2"]), dev_w["w_fc1"], dz)
+        dx1_ln, dg2, dbe2 = enc.layernorm_bwd(dev(im["x1"]), dev_w["ln2_gamma"], dh2)
+        dx1 = (g_out.float() + dx1_ln.float()).to(torch.bfloat16)
+        dctx, dw_out, db_out = enc.linear_bwd(ctx, dev_w["w_out"], dx1)
+        dqkv = enc.attention_bwd(planar, ctx, dctx, lse, cu_d, B, T)
+        dy_qkv = enc.qkv_rope_bwd(dqkv, cu_d, B, T)
+        dh1, dw_qkv, db_qkv = enc.linear_bwd(dev(im["h1"]), dev_w["w_qkv"], dy_qkv)
+        dx_ln, dg1, dbe1 = enc.layernorm_bwd(gu.to_dev_bf16(xb), dev_w["ln1_gamma"], dh1)
+        dx = dx1.float() + dx_ln.float()
+        torch.cuda.synchronize()
+    finally:
+        enc.close()
+    rdx, rg = O.layer_backward(x, cu, w, heads, dout)
+    got = {"w_fc2": dw_fc2, "b_fc2": db_fc2, "w_fc1": dw_fc1, "b_fc1": db_fc1, "ln2_gamma": dg2, "ln2_beta": dbe2,
+           "w_out": dw_out, "b_out": db_out, "w_qkv": dw_qkv, "b_qkv": db_qkv, "ln1_gamma": dg1, "ln1_beta": dbe1}
+    errs = {"x": gu.rel_err(dx.cpu().numpy().astype(np.float64), rdx)}
+    for k, t in got.items():
+        v = gu.from_dev(t) if t.dtype == torch.bfloat16 else t.cpu().numpy().astype(np.float64)
+        errs[k] = gu.rel_err(v, rg[k])
+    print("layer backward chain, max|err| / max|ref|:", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert all(v < TOL for v in errs.values()), errs
