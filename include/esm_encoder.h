@@ -403,7 +403,10 @@ esm_status esm_linear_mxfp4_fwd(esm_encoder* enc, const void* x_codes, const voi
  * library's MFMA GEMM with fp32 accumulation (dW over all M rows in fp32);
  * W^T, dy^T and x^T are written into the workspace first (rows padded with
  * zeros to a multiple of 64), db by a fixed-order two-pass column sum, so
- * results are deterministic.  workspace: device, 256-byte aligned, at least
+ * results are deterministic.  The dW path runs on a stream of the encoder's own
+ * (created on first use, default priority), forked from and joined back to
+ * `stream` within the call, so the call stays ordered on `stream` alone.
+ * workspace: device, 256-byte aligned, at least
  * esm_linear_bwd_workspace_size(M, N, K) bytes, overwritten.  Outputs must not
  * overlap inputs or workspace.  Errors: ESM_ERR_NULL, ESM_ERR_SHAPE,
  * ESM_ERR_UNSUPPORTED (alignment: tensors 16 bytes, db 4), ESM_ERR_WORKSPACE.

@@ -20,6 +20,11 @@ struct esm_encoder {
   esm_config cfg;
   int device = 0;
   float2* rope = nullptr;  // [max_positions, 32]
+  // A second stream (default priority) for work that runs beside the
+  // caller's stream inside one call (the dW path of esm_linear_bwd), forked
+  // and joined with the two events; created on first use.
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
   bool profiling = false;
   std::vector<hipEvent_t> pool;
   size_t pool_used = 0;
@@ -768,6 +773,9 @@ esm_status esm_encoder_destroy(esm_encoder* e) {
   if (e->w4) (void)hipFree(e->w4);
   if (e->head_w) (void)hipFree(e->head_w);
   for (hipEvent_t ev : e->pool) (void)hipEventDestroy(ev);
+  if (e->fork) (void)hipEventDestroy(e->fork);
+  if (e->join) (void)hipEventDestroy(e->join);
+  if (e->side) (void)hipStreamDestroy(e->side);
   delete e;
   return ESM_OK;
 }
@@ -1128,8 +1136,30 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
   bf16_t* xt = (bf16_t*)(base + pl.xt);
   float* part = (float*)(base + pl.part);
   const int64_t M64 = (M + 63) / 64 * 64;
+  if (dw && !e->side) {
+    HIP_TRY(hipStreamCreateWithFlags(&e->side, hipStreamNonBlocking), "hipStreamCreateWithFlags");
+    HIP_TRY(hipEventCreateWithFlags(&e->fork, hipEventDisableTiming), "hipEventCreateWithFlags");
+    HIP_TRY(hipEventCreateWithFlags(&e->join, hipEventDisableTiming), "hipEventCreateWithFlags");
+  }
   return timed(e, ESM_K_LINEAR_BWD, st, "linear backward", [&]() -> hipError_t {
     hipError_t r = hipSuccess;
+    // The dW GEMM's output is small (N x K: tens of tiles for hundreds of
+    // compute units) with a long contraction over M, so it runs on the side
+    // stream, forked from and joined back to st, and the dx GEMM and the
+    // column sums fill the compute units it leaves idle.  The workspace
+    // regions of the two paths are disjoint.
+    if (dw) {
+      // dW [N, K] = dy^T [N, M64] . (x^T [K, M64])^T, zero columns past M
+      if ((r = hipEventRecord(e->fork, st))) return r;
+      if ((r = hipStreamWaitEvent(e->side, e->fork, 0))) return r;
+      if ((r = launch_transpose_pad((const bf16_t*)dy, M, N, dyt, M64, e->side))) return r;
+      if ((r = launch_transpose_pad((const bf16_t*)x, M, K, xt, M64, e->side))) return r;
+      GemmArgs g{};
+      g.dtype = kBF16;
+      g.x = dyt; g.w = xt; g.y = (bf16_t*)dw; g.M = N; g.N = K; g.K = M64;
+      if ((r = launch_gemm(EPI_BIAS, g, e->side))) return r;
+      if ((r = hipEventRecord(e->join, e->side))) return r;
+    }
     if (dx) {
       // dx [M, K] = dy [M, N] . (W^T [K, N])^T
       if ((r = launch_transpose_pad((const bf16_t*)w, N, K, wt, N, st))) return r;
@@ -1138,16 +1168,8 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
       g.x = dy; g.w = wt; g.y = (bf16_t*)dx; g.M = M; g.N = K; g.K = N;
       if ((r = launch_gemm(EPI_BIAS, g, st))) return r;
     }
-    if (dw) {
-      // dW [N, K] = dy^T [N, M64] . (x^T [K, M64])^T, zero columns past M
-      if ((r = launch_transpose_pad((const bf16_t*)dy, M, N, dyt, M64, st))) return r;
-      if ((r = launch_transpose_pad((const bf16_t*)x, M, K, xt, M64, st))) return r;
-      GemmArgs g{};
-      g.dtype = kBF16;
-      g.x = dyt; g.w = xt; g.y = (bf16_t*)dw; g.M = N; g.N = K; g.K = M64;
-      if ((r = launch_gemm(EPI_BIAS, g, st))) return r;
-    }
     if (db && (r = launch_colsum((const bf16_t*)dy, M, N, part, db, st))) return r;
+    if (dw && (r = hipStreamWaitEvent(st, e->join, 0))) return r;
     return r;
   });
 }
