@@ -498,8 +498,9 @@ void k_biased_attention(BiasedAttnArgs a) {
 // of the context.  Per (sequence, head), with S = q k^T / 8 and
 // P = exp(S - lse):  dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D) with
 // D = rowsum(dO * O) (= rowsum(P * dP)),  dQ = dS K / 8,  dK = dS^T Q / 8.
-// P is recomputed from lse, never stored.  Three kernels:
-//  * k_attn_bwd_delta: D for every (head, row), 8 lanes per row;
+// P is recomputed from lse, never stored.  Two kernels, dQ first:
+//  * k_attn_bwd_dq (below) also forms D for its queries from the dO row it
+//    holds and the O row, and writes it for the dK/dV kernel;
 //  * k_attn_bwd_dkv: one workgroup per 128 keys of one sequence and head (4
 //    waves x 32 keys, K and V rows in registers as the MFMAs' B operand),
 //    streaming the sequence's queries in 64-row tiles of Q and dO through LDS
@@ -519,8 +520,9 @@ struct AttnBwdPtrs {
   const bf16_t* K;
   const bf16_t* V;
   const bf16_t* dO;   // row stride H
+  const bf16_t* O;    // row stride H
   const float* lse;   // [L] of this head
-  const float* del;   // [L] of this head
+  float* del;         // [L] of this head
 };
 
 __device__ __forceinline__ AttnBwdPtrs bwd_ptrs(const AttnBwdArgs& a, int head, int64_t start) {
@@ -530,31 +532,10 @@ __device__ __forceinline__ AttnBwdPtrs bwd_ptrs(const AttnBwdArgs& a, int head, 
   p.K = a.qkv + ((int64_t)(1 * a.heads + head) * T + start) * kHeadDim;
   p.V = a.qkv + ((int64_t)(2 * a.heads + head) * T + start) * kHeadDim;
   p.dO = a.dout + start * ((int64_t)a.heads * kHeadDim) + head * kHeadDim;
+  p.O = a.out + start * ((int64_t)a.heads * kHeadDim) + head * kHeadDim;
   p.lse = a.lse + (int64_t)head * T + start;
   p.del = a.delta + (int64_t)head * T + start;
   return p;
-}
-
-// D[head, t] = sum_d dO[t, head, d] * O[t, head, d]: 8 lanes per (t, head),
-// 16 bytes of each tensor per lane.
-__global__ __launch_bounds__(256) void k_attn_bwd_delta(AttnBwdArgs a) {
-  const int64_t g = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;
-  const int part = threadIdx.x & 7;
-  const bool live = g < a.T * a.heads;
-  const int64_t t = live ? g / a.heads : 0;
-  const int head = live ? (int)(g % a.heads) : 0;
-  float acc = 0.f;
-  if (live) {
-    const int64_t off = t * ((int64_t)a.heads * kHeadDim) + head * kHeadDim + part * 8;
-    const u32x4 o = *(const u32x4*)(a.out + off);
-    const u32x4 d = *(const u32x4*)(a.dout + off);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc += bflo(o[e]) * bflo(d[e]) + bfhi(o[e]) * bfhi(d[e]);
-  }
-  acc += __shfl_xor(acc, 1);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 4);
-  if (live && part == 0) a.delta[(int64_t)head * a.T + t] = acc;
 }
 
 constexpr int kBT = 64;   // rows per streamed LDS tile in the backward kernels
@@ -786,7 +767,17 @@ __global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(3, 3))
     df[kk] = *(const bf16x8*)(p.dO + qc * H + kk * 16 + 8 * lhalf);
   }
   const float l2 = p.lse[qc] * kLog2e;
-  const float dd = p.del[qc];
+  // D = rowsum(dO * O) of this query: this lane's 32 dims, then its partner's.
+  // Written for the dK/dV kernel, which runs after this one.
+  float dpart = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const bf16x8 of = *(const bf16x8*)(p.O + qc * H + kk * 16 + 8 * lhalf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dpart += (float)df[kk][e] * (float)of[e];
+  }
+  const float dd = dpart + __shfl_xor(dpart, 32);
+  if (lhalf == 0 && qrow < L) p.del[qrow] = dd;
 
   const uint32_t lds_k = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sk[0][0];
   const uint32_t lds_v = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sv[0][0];
@@ -897,11 +888,10 @@ __global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(3, 3))
 
 hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t st) {
   if (a.tile_cap <= 0 || a.T <= 0) return hipSuccess;
-  const int64_t nd = a.T * a.heads * 8;
-  hipLaunchKernelGGL(k_attn_bwd_delta, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, st, a);
+  // dQ first: it also writes D, which the dK/dV kernel reads.
   const int64_t nblk = a.tile_cap * a.heads * kBParts;
-  hipLaunchKernelGGL(k_attn_bwd_dkv, dim3((unsigned)nblk), dim3(64 * kBW), 0, st, a);
   hipLaunchKernelGGL(k_attn_bwd_dq, dim3((unsigned)nblk), dim3(64 * kBW), 0, st, a);
+  hipLaunchKernelGGL(k_attn_bwd_dkv, dim3((unsigned)nblk), dim3(64 * kBW), 0, st, a);
   return hipGetLastError();
 }
 
