@@ -169,3 +169,46 @@ def test_missing_library_fails_loudly(tmp_path):
             mod.load_library(str(tmp_path / "nope.so"))
     finally:
         importlib.reload(esm)
+
+
+def _size(fn, *args):
+    n = ctypes.c_size_t()
+    st, msg = _status(fn, *args, ctypes.byref(n))
+    return st, msg, n.value
+
+
+def test_linear_bwd_workspace_size():
+    # W^T [K, N] bf16, dy^T [N, M64] and x^T [K, M64] bf16, db partials
+    # [ceil(M / 1024), N] fp32, each region rounded up to 256 bytes
+    M, N, K = 32293, 5120, 1280
+    M64 = (M + 63) // 64 * 64
+    up = lambda b: (b + 255) // 256 * 256
+    st, msg, n = _size("esm_linear_bwd_workspace_size", ctypes.c_int64(M), N, K)
+    assert st == 0, msg
+    assert n == up(K * N * 2) + up(N * M64 * 2) + up(K * M64 * 2) + up(-(-M // 1024) * N * 4)
+    for bad in ((M, 100, K), (M, N, 0), (-1, N, K)):
+        st, msg, _ = _size("esm_linear_bwd_workspace_size", ctypes.c_int64(bad[0]), bad[1], bad[2])
+        assert st == 2 and msg
+
+
+def test_layernorm_bwd_workspace_size():
+    # per-row mean and rstd (fp32 pairs, 256-byte rounded), then [ceil(M / 1024), 2, H] fp32
+    st, msg, n = _size("esm_layernorm_bwd_workspace_size", ctypes.c_int64(32293), 1280)
+    assert st == 0, msg
+    assert n == (32293 * 8 + 255) // 256 * 256 + 32 * 2 * 1280 * 4
+    for H in (100, 4160, 0):
+        st, msg, _ = _size("esm_layernorm_bwd_workspace_size", ctypes.c_int64(10), H)
+        assert st == 2 and msg
+
+
+def test_backward_calls_fail_cleanly_without_a_handle():
+    p = ctypes.c_void_p(16)
+    assert _status("esm_attention_fwd_lse", None, p, p, p, p, 1, ctypes.c_int64(1), p, ctypes.c_size_t(0), None)[0] == 1
+    assert _status("esm_attention_bwd", None, p, p, p, p, p, p, p, 1, ctypes.c_int64(1), p, ctypes.c_size_t(0),
+                   None)[0] == 1
+    assert _status("esm_linear_bwd", None, p, p, p, p, p, p, ctypes.c_int64(1), 64, 64, p, ctypes.c_size_t(0),
+                   None)[0] == 1
+    assert _status("esm_layernorm_bwd", None, p, p, p, p, p, p, ctypes.c_int64(1), p, ctypes.c_size_t(0),
+                   None)[0] == 1
+    assert _status("esm_gelu_bwd", None, p, p, p, ctypes.c_int64(8), None)[0] == 1
+    assert _status("esm_qkv_rope_bwd", None, p, p, p, 1, ctypes.c_int64(1), p, ctypes.c_size_t(0), None)[0] == 1
