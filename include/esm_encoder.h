@@ -400,7 +400,9 @@ esm_status esm_linear_mxfp4_fwd(esm_encoder* enc, const void* x_codes, const voi
  *   db = sum_m dy[m] [N]     (fp32, written when db is not NULL)
  * x bf16 [M, K], w bf16 [N, K] (as in esm_linear_fwd), dy bf16 [M, N]; dx and
  * dw bf16.  N and K multiples of 64, any M >= 0.  The two products run on the
- * library's MFMA GEMM with fp32 accumulation (dW over all M rows in fp32);
+ * library's MFMA GEMM with fp32 accumulation (dW over all M rows in fp32: for
+ * large M the contraction is cut into up to 16 slices whose fp32 products are
+ * summed in slice order, then rounded once);
  * W^T, dy^T and x^T are written into the workspace first (rows padded with
  * zeros to a multiple of 64), db by a fixed-order two-pass column sum, so
  * results are deterministic.  The dW path runs on a stream of the encoder's own

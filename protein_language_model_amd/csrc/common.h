@@ -200,7 +200,7 @@ hipError_t launch_layernorm_mx(const bf16_t* x, const bf16_t* gamma, const bf16_
                                uint8_t* scales, int64_t M, int32_t H, float eps, hipStream_t st);
 
 enum GemmEpi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_QKV_ROPE = 3, EPI_BIAS_GELU_E4M3 = 4,
-               EPI_BIAS_GELU_MX = 5 };
+               EPI_BIAS_GELU_MX = 5, EPI_F32_SPLIT = 6 };
 
 struct GemmArgs {
   int32_t dtype;       // kBF16 or kE4M3 operands
@@ -224,6 +224,10 @@ struct GemmArgs {
   uint8_t* y8;
   const float* y8_scale;
   uint32_t* y8_amax;
+  // EPI_F32_SPLIT (bf16 operands): K cut into ksplit equal slices; slice s's
+  // product, in fp32, goes to y32 + s * M * N (no bias); K % (64 ksplit) == 0
+  float* y32;
+  int32_t ksplit;
   // kFP4 operands: E8M0 block scales in the esm_mxfp4_quantize layout
   // [K / 256][rows rounded up to even][8]
   const uint8_t* x_sc;
@@ -278,6 +282,10 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t st);
 hipError_t launch_transpose_pad(const bf16_t* in, int64_t R, int32_t C, bf16_t* out, int64_t Rp, hipStream_t st);
 hipError_t launch_colsum(const bf16_t* dy, int64_t M, int32_t N, float* part, float* db, hipStream_t st);
 int64_t colsum_chunks(int64_t M);
+// dW GEMM of the linear backward: K slices (split-K) for M rows, and the
+// fixed-order sum of the slices' fp32 partials into bf16.
+int32_t wgrad_splits(int64_t M, int32_t N, int32_t K);
+hipError_t launch_split_reduce(const float* part, int32_t S, int64_t n, bf16_t* out, hipStream_t st);
 // LayerNorm backward: dx [M, H] bf16, dgamma and dbeta [H] fp32; stats [2M]
 // and part [colsum_chunks(M), 2, H] fp32 are scratch.  H a multiple of 64, <= 4096.
 // GELU backward: dz = dy GELU'(z), n % 8 == 0.  QKV/RoPE backward: planar

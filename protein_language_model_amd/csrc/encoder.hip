@@ -1090,17 +1090,22 @@ esm_status esm_linear_fwd(esm_encoder* e, const void* x, const void* w, const vo
 
 namespace {
 struct LinBwdPlan {
-  size_t wt, dyt, xt, part, total;
+  int32_t splits;  // K slices of the dW GEMM
+  int64_t Mp;      // rows padded to a multiple of 64 * splits
+  size_t wt, dyt, xt, part, wpart, total;
 };
 LinBwdPlan lin_bwd_plan(int64_t M, int32_t N, int32_t K) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
-  const int64_t M64 = (M + 63) / 64 * 64;
   LinBwdPlan p;
+  p.splits = wgrad_splits(M, N, K);
+  const int64_t q = 64 * (int64_t)p.splits;
+  p.Mp = (M + q - 1) / q * q;
   p.wt = 0;
   p.dyt = p.wt + up((size_t)K * N * 2);
-  p.xt = p.dyt + up((size_t)N * M64 * 2);
-  p.part = p.xt + up((size_t)K * M64 * 2);
-  p.total = p.part + up((size_t)colsum_chunks(M) * N * 4);
+  p.xt = p.dyt + up((size_t)N * p.Mp * 2);
+  p.part = p.xt + up((size_t)K * p.Mp * 2);
+  p.wpart = p.part + up((size_t)colsum_chunks(M) * N * 4);
+  p.total = p.wpart + (p.splits > 1 ? up((size_t)p.splits * N * K * 4) : 0);
   return p;
 }
 }  // namespace
@@ -1135,7 +1140,8 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
   bf16_t* dyt = (bf16_t*)(base + pl.dyt);
   bf16_t* xt = (bf16_t*)(base + pl.xt);
   float* part = (float*)(base + pl.part);
-  const int64_t M64 = (M + 63) / 64 * 64;
+  float* wpart = (float*)(base + pl.wpart);
+  const int64_t M64 = pl.Mp;
   if (dw && !e->side) {
     HIP_TRY(hipStreamCreateWithFlags(&e->side, hipStreamNonBlocking), "hipStreamCreateWithFlags");
     HIP_TRY(hipEventCreateWithFlags(&e->fork, hipEventDisableTiming), "hipEventCreateWithFlags");
@@ -1144,10 +1150,10 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
   return timed(e, ESM_K_LINEAR_BWD, st, "linear backward", [&]() -> hipError_t {
     hipError_t r = hipSuccess;
     // The dW GEMM's output is small (N x K: tens of tiles for hundreds of
-    // compute units) with a long contraction over M, so it runs on the side
-    // stream, forked from and joined back to st, and the dx GEMM and the
-    // column sums fill the compute units it leaves idle.  The workspace
-    // regions of the two paths are disjoint.
+    // compute units) with a long contraction over M: it is cut into K slices
+    // (fp32 partial products summed in slice order), and it runs on the side
+    // stream, forked from and joined back to st, beside the dx GEMM and the
+    // column sums.  The workspace regions of the two paths are disjoint.
     if (dw) {
       // dW [N, K] = dy^T [N, M64] . (x^T [K, M64])^T, zero columns past M
       if ((r = hipEventRecord(e->fork, st))) return r;
@@ -1157,7 +1163,14 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
       GemmArgs g{};
       g.dtype = kBF16;
       g.x = dyt; g.w = xt; g.y = (bf16_t*)dw; g.M = N; g.N = K; g.K = M64;
-      if ((r = launch_gemm(EPI_BIAS, g, e->side))) return r;
+      if (pl.splits > 1) {
+        // split-K: each K slice's fp32 product, then their sum in slice order
+        g.y32 = wpart; g.ksplit = pl.splits;
+        if ((r = launch_gemm(EPI_F32_SPLIT, g, e->side))) return r;
+        if ((r = launch_split_reduce(wpart, pl.splits, (int64_t)N * K, (bf16_t*)dw, e->side))) return r;
+      } else if ((r = launch_gemm(EPI_BIAS, g, e->side))) {
+        return r;
+      }
       if ((r = hipEventRecord(e->join, e->side))) return r;
     }
     if (dx) {

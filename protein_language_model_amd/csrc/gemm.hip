@@ -151,7 +151,15 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   const int tilesM = (int)((M + BM - 1) / BM);
   const int tilesN = (N + BN - 1) / BN;
   const int nb = tilesM * tilesN;
-  const int bid = blockIdx.x;
+  int bid = blockIdx.x;
+  // EPI_F32_SPLIT: workgroup = (K slice, tile), the slice slowest.
+  [[maybe_unused]] int split = 0;
+  int Kl = K;
+  if constexpr (EPI == EPI_F32_SPLIT) {
+    split = bid / nb;
+    bid = bid % nb;
+    Kl = K / a.ksplit;
+  }
   if (bid >= nb) return;
   // XCD-aware remap: hardware deals ids round-robin over the XCDs.
   const int xcd = bid % kXcds, local = bid / kXcds;
@@ -185,13 +193,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   for (int i = 0; i < XRB; ++i) {
     int64_t r = m0 + (int64_t)(wave + NW * i) * RPI + lr8;
     r = r < M ? r : M - 1;
-    xsrc[i] = (const unsigned char*)a.x + r * K * EBN / EBD + lchunk;
+    xsrc[i] = (const unsigned char*)a.x + r * K * EBN / EBD + (int64_t)split * Kl * EBN / EBD + lchunk;
   }
 #pragma unroll
   for (int i = 0; i < WRB; ++i) {
     int r = n0 + (wave + NW * i) * RPI + lr8;
     r = r < N ? r : N - 1;
-    wsrc[i] = (const unsigned char*)a.w + (int64_t)r * K * EBN / EBD + lchunk;
+    wsrc[i] = (const unsigned char*)a.w + (int64_t)r * K * EBN / EBD + (int64_t)split * Kl * EBN / EBD + lchunk;
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
@@ -301,7 +309,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       }
   };
 
-  const int nk = K / kBK;
+  const int nk = Kl / kBK;
   issue_tile(0, 0);
   vm_wait_all();
   __syncthreads();
@@ -385,6 +393,30 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  }
+
+  if constexpr (EPI == EPI_F32_SPLIT) {
+    // Split-K partial sums straight from the accumulators: register 4 gq + e
+    // of block (i, j) is row mw + 32 i + lrow, column nw + 32 j + 8 gq +
+    // 4 lhalf + e; 16-byte fp32 stores, no staging.
+    const int64_t mwf = m0 + wm * WTM;
+    const int nwf = n0 + wn * WTN;
+    float* out = a.y32 + (int64_t)split * M * N;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = mwf + i * 32 + lrow;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = nwf + j * 32 + 8 * gq + 4 * lhalf;
+          if (n < N)
+            *(f32x4*)(out + m * N + n) =
+                f32x4{acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]};
+        }
+    }
+    return;
   }
 
   // ------------------------------------------------------------ epilogue
@@ -623,7 +655,7 @@ template <int BM, int BN, int WM, int WN, int EPI, int DT>
 hipError_t run(const GemmArgs& a, hipStream_t st) {
   const int64_t tilesM = (a.M + BM - 1) / BM;
   const int64_t tilesN = (a.N + BN - 1) / BN;
-  const int64_t nb = tilesM * tilesN;
+  const int64_t nb = tilesM * tilesN * (EPI == EPI_F32_SPLIT ? a.ksplit : 1);
   hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI, DT>), dim3((unsigned)nb), dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
@@ -643,6 +675,10 @@ int device_cus() {
 
 template <int EPI>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
+  if constexpr (EPI == EPI_F32_SPLIT) {
+    if (a.dtype != kBF16 || a.ksplit < 1 || !a.y32 || a.K % (64 * a.ksplit)) return hipErrorInvalidValue;
+    return run<256, 256, 2, 4, EPI, kBF16>(a, st);
+  } else {
   // 8 waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs)
   // over 256x256 tiles (128x64 per wave), or 320x256 tiles (160x64 per wave)
   // when those need fewer rounds of workgroups over the compute units: time
@@ -668,6 +704,7 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   }
   if constexpr (EPI == EPI_BIAS_GELU_E4M3 || EPI == EPI_BIAS_GELU_MX) return hipErrorInvalidValue;
   else return tall ? run<320, 256, 2, 4, EPI, kBF16>(a, st) : run<256, 256, 2, 4, EPI, kBF16>(a, st);
+  }
 }
 
 }  // namespace
@@ -683,6 +720,7 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st) {
     case EPI_QKV_ROPE: return dispatch<EPI_QKV_ROPE>(a, st);
     case EPI_BIAS_GELU_E4M3: return dispatch<EPI_BIAS_GELU_E4M3>(a, st);
     case EPI_BIAS_GELU_MX: return dispatch<EPI_BIAS_GELU_MX>(a, st);
+    case EPI_F32_SPLIT: return dispatch<EPI_F32_SPLIT>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -255,6 +255,20 @@ __global__ __launch_bounds__(256) void k_ln_bwd_cols(const bf16_t* __restrict__ 
   if (t < 128) part[((int64_t)blockIdx.x * 2 + (t >> 6)) * H + n0 + (t & 63)] = red[t >> 6][0][t & 63];
 }
 
+// out[i] = bf16(sum over s of part[s * n + i]) in slice order (split-K
+// partial sums of the dW GEMM); 4 values per thread, n % 4 == 0.
+__global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int32_t S, int64_t n,
+                                                      bf16_t* __restrict__ out) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 acc = *(const f32x4*)(part + i);
+  for (int s = 1; s < S; ++s) {
+    const f32x4 v = *(const f32x4*)(part + (int64_t)s * n + i);
+    acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+  }
+  *(u32x2*)(out + i) = u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
+}
+
 // ------------------------------------------------------------ GELU, RoPE backward
 
 // dz = dy (Phi(z) + z phi(z)), 8 values per thread (16-byte loads); n % 8 == 0.
@@ -314,6 +328,29 @@ __global__ __launch_bounds__(256) void k_qkv_rope_bwd(const bf16_t* __restrict__
 }  // namespace
 
 int64_t colsum_chunks(int64_t M) { return (M + kSumRows - 1) / kSumRows; }
+
+int32_t wgrad_splits(int64_t M, int32_t N, int32_t K) {
+  // K slices for dW [N, K] = dy^T x (contraction over M): the count that
+  // minimises rounds of 256 x 256 tiles over 256 compute units per unit of
+  // contraction, ceil(tiles S / 256) / S, with slices of at least 1024 rows.
+  const int64_t tiles = (int64_t)((N + 255) / 256) * ((K + 255) / 256);
+  const int64_t smax = M / 1024 < 1 ? 1 : (M / 1024 > 16 ? 16 : M / 1024);
+  int32_t best = 1;
+  double best_t = 1e30;
+  for (int32_t S = 1; S <= smax; ++S) {
+    const double t = (double)((tiles * S + 255) / 256) / S;
+    if (t < best_t - 1e-12) { best_t = t; best = S; }
+  }
+  return best;
+}
+
+hipError_t launch_split_reduce(const float* part, int32_t S, int64_t n, bf16_t* out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 4 || S < 1) return hipErrorInvalidValue;
+  const int64_t nt = n / 4;
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, st, part, S, n, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_gelu_bwd(const bf16_t* z, const bf16_t* dy, bf16_t* dz, int64_t n, hipStream_t st) {
   if (n <= 0) return hipSuccess;
