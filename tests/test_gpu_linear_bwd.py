@@ -52,6 +52,17 @@ def test_linear_bwd(gu, enc, M, N, K):
     assert np.abs(db - rb).max() <= 1e-5 * np.abs(rb).max()
 
 
+@pytest.mark.parametrize("M,N,K", [(5000, 320, 192), (4097, 128, 64), (20000, 64, 1280)])
+def test_linear_bwd_split_k(gu, enc, M, N, K):
+    """Shapes whose dW GEMM is cut into K slices (few output tiles, M >= 2048):
+    ragged M padded to a multiple of 64 * slices, fp32 slice products summed
+    in order; everything against the oracle."""
+    (dx, dw, db), (rx, rw, rb) = _case(gu, enc, M, N, K, seed=M)
+    assert gu.rel_err(dx, rx) < TOL
+    assert gu.rel_err(dw, rw) < TOL
+    assert np.abs(db - rb).max() <= 1e-5 * np.abs(rb).max()
+
+
 def test_linear_bwd_partial_outputs(gu, enc):
     """dx only, dW only, db only: each equals the full call's (bit-exact)."""
     M, N, K = 300, 256, 192
