@@ -503,10 +503,11 @@ void k_biased_attention(BiasedAttnArgs a) {
 //    holds and the O row, and writes it for the dK/dV kernel;
 //  * k_attn_bwd_dkv: one workgroup per 128 keys of one sequence and head (4
 //    waves x 32 keys, K and V rows in registers as the MFMAs' B operand),
-//    streaming the sequence's queries in 64-row tiles of Q and dO through LDS
-//    (direct loads, double-buffered, the forward's swizzle) with their lse
-//    and D; S and dP come out query x key, so each lane owns one key and the
-//    products accumulate dV^T and dK^T in registers: no atomics;
+//    streaming the sequence's queries through LDS in 128-row tiles of Q and dO
+//    (two 64-row compute steps per fill; direct loads, double-buffered, the
+//    forward's swizzle) with their lse and D; S and dP come out query x key,
+//    so each lane owns one key and the products accumulate dV^T and dK^T in
+//    registers: no atomics;
 //  * k_attn_bwd_dq: one workgroup per 128 queries, the forward's structure
 //    with dP added: K and V tiles in LDS, S^T and dP^T key x query, and
 //    dQ^T += K^T dS^T with K^T read by the transposing LDS reads.
@@ -580,10 +581,13 @@ __global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(2, 2))
   const AttnBwdPtrs p = bwd_ptrs(a, head, start);
   const int64_t H = (int64_t)heads * kHeadDim;
 
-  __shared__ __attribute__((aligned(1024))) bf16_t sq[2][kBT * kLdsRow];
-  __shared__ __attribute__((aligned(1024))) bf16_t sd[2][kBT * kLdsRow];
-  __shared__ __attribute__((aligned(16))) float sl[2][kBT];   // lse * log2(e); +inf past the end
-  __shared__ __attribute__((aligned(16))) float sD[2][kBT];   // D; 0 past the end
+  // LDS tiles of 2 x 64 query rows (one fill and barrier per 128 queries,
+  // so the next tile's loads have two compute steps to land).
+  constexpr int kTR = 2 * kBT;
+  __shared__ __attribute__((aligned(1024))) bf16_t sq[2][kTR * kLdsRow];
+  __shared__ __attribute__((aligned(1024))) bf16_t sd[2][kTR * kLdsRow];
+  __shared__ __attribute__((aligned(16))) float sl[2][kTR];   // lse * log2(e); +inf past the end
+  __shared__ __attribute__((aligned(16))) float sD[2][kTR];   // D; 0 past the end
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lhalf = lane >> 5;
@@ -602,12 +606,16 @@ __global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const uint32_t lds_q = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sq[0][0];
   const uint32_t lds_d = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&sd[0][0];
-  auto gload = [&](int j, int buf) {
-    tile_dma(p.Q, kHeadDim, j * kBT, L, lds_q + (uint32_t)buf * kBT * kLdsRow * 2, lane, wave, wave_u);
-    tile_dma(p.dO, H, j * kBT, L, lds_d + (uint32_t)buf * kBT * kLdsRow * 2, lane, wave, wave_u);
+  auto gload = [&](int t, int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t off = (uint32_t)(buf * kTR + h * kBT) * kLdsRow * 2;
+      tile_dma(p.Q, kHeadDim, t * kTR + h * kBT, L, lds_q + off, lane, wave, wave_u);
+      tile_dma(p.dO, H, t * kTR + h * kBT, L, lds_d + off, lane, wave, wave_u);
+    }
   };
-  auto sload = [&](int j, float& l2, float& dd) {
-    const int q = j * kBT + tid;
+  auto sload = [&](int t, float& l2, float& dd) {
+    const int q = t * kTR + tid;
     l2 = q < L ? p.lse[q] * kLog2e : INFINITY;
     dd = q < L ? p.del[q] : 0.f;
   };
@@ -632,10 +640,11 @@ __global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int r = 0; r < 16; ++r) { dv[d][r] = 0.f; dk[d][r] = 0.f; }
 
-  const int ntq = (L + kBT - 1) / kBT;
+  const int ntq = (L + kBT - 1) / kBT;   // 64-query compute steps
+  const int ntl = (L + kTR - 1) / kTR;   // LDS tiles
   const bool wave_active = k0 + 32 * wave < L;
   gload(0, 0);
-  if (tid < kBT) {
+  if (tid < kTR) {
     float l2, dd;
     sload(0, l2, dd);
     sl[0][tid] = l2;
@@ -643,16 +652,20 @@ __global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   vm_wait_all();
   __syncthreads();
-  for (int t = 0; t < ntq; ++t) {
+  for (int t = 0; t < ntl; ++t) {
     const int cur = t & 1;
     float nl2 = 0.f, ndd = 0.f;
-    if (t + 1 < ntq) {
+    if (t + 1 < ntl) {
       gload(t + 1, cur ^ 1);
-      if (tid < kBT) sload(t + 1, nl2, ndd);
+      if (tid < kTR) sload(t + 1, nl2, ndd);
     }
-    if (wave_active) {
-      const bf16_t* qt = sq[cur];
-      const bf16_t* dt = sd[cur];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+    if (wave_active && 2 * t + sub < ntq) {
+      const bf16_t* qt = sq[cur] + sub * kBT * kLdsRow;
+      const bf16_t* dt = sd[cur] + sub * kBT * kLdsRow;
+      const float* slt = &sl[cur][sub * kBT];
+      const float* sDt = &sD[cur][sub * kBT];
       // S and dP, query x key: block qb holds queries qb*32 + 8*(r/4) +
       // 4*lhalf + r%4 of this lane's key.
       f32x16 st[2], dp[2];
@@ -676,8 +689,8 @@ __global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int q = qb * 32 + 8 * g + 4 * lhalf;
-          const f32x4 l2 = *(const f32x4*)&sl[cur][q];
-          const f32x4 dd = *(const f32x4*)&sD[cur][q];
+          const f32x4 l2 = *(const f32x4*)&slt[q];
+          const f32x4 dd = *(const f32x4*)&sDt[q];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float pr = exp2_fast(fmaf(st[qb][4 * g + e], kScaleLog2, -l2[e]));
@@ -718,7 +731,8 @@ __global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(2, 2))
             dk[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q8), sb[qb][u], dk[d], 0, 0, 0);
           }
     }
-    if (t + 1 < ntq && tid < kBT) {
+    }
+    if (t + 1 < ntl && tid < kTR) {
       sl[cur ^ 1][tid] = nl2;
       sD[cur ^ 1][tid] = ndd;
     }
