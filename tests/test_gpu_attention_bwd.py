@@ -150,3 +150,18 @@ def test_attention_bwd_650m_batch(gu):
     sum_go = np.add.reduceat(go, starts, axis=1)
     scale = np.add.reduceat(np.abs(dv), starts, axis=1).max(axis=2, keepdims=True)
     assert np.all(np.abs(sum_dv - sum_go) <= 2e-2 * scale + 1e-6)
+
+
+def test_attention_bwd_3b_heads(gu):
+    """The 3B-shaped width (40 heads of 64) on a ragged packed batch."""
+    enc = esm.Encoder(hidden_size=2560, num_attention_heads=40, intermediate_size=10240, num_hidden_layers=1)
+    try:
+        lens = [300, 1, 129, 64]
+        cu, T, q, k, v, g = _draw(lens, 40, 26)
+        _, lse, dqkv = _run(gu, enc, cu, T, q, k, v, g)
+    finally:
+        enc.close()
+    lse_r, dq_r, dk_r, dv_r = _ref(cu, q, k, v, g)
+    assert np.abs(lse - lse_r).max() <= LSE_ATOL
+    for got, ref in zip(dqkv, (dq_r, dk_r, dv_r)):
+        assert gu.rel_err(_planar_to_rows(got), ref) < TOL

@@ -106,3 +106,29 @@ def test_linear_bwd_650m_fc1_sampled(gu):
         assert gu.rel_err(dwf[n], ref) < TOL, n
     rb = gf.sum(axis=0)
     assert np.abs(db.cpu().numpy() - rb).max() <= 1e-5 * np.abs(rb).max() + 1e-3
+
+
+def test_linear_bwd_3b_fc1_sampled(gu):
+    """fc1's backward at the 3B-shaped batch's size (x [16208, 2560], W1
+    [10240, 2560], dy [16208, 10240]; the dW GEMM has 400 output tiles and
+    takes 5 K slices): sampled rows of dx and dW and all of db."""
+    enc = esm.Encoder(hidden_size=2560, num_attention_heads=40, intermediate_size=10240, num_hidden_layers=1)
+    try:
+        M, N, K = 16208, 10240, 2560
+        g = torch.Generator(device="cuda:0").manual_seed(42)
+        x = torch.randn((M, K), generator=g, device="cuda:0").to(torch.bfloat16)
+        w = (torch.randn((N, K), generator=g, device="cuda:0") * 0.02).to(torch.bfloat16)
+        dy = torch.randn((M, N), generator=g, device="cuda:0").to(torch.bfloat16)
+        dx, dw, db = enc.linear_bwd(x, w, dy)
+        torch.cuda.synchronize()
+    finally:
+        enc.close()
+    xf, wf, gf = gu.from_dev(x), gu.from_dev(w), gu.from_dev(dy)
+    dxf, dwf = gu.from_dev(dx), gu.from_dev(dw)
+    rng = np.random.default_rng(43)
+    for m in np.concatenate([[0, M - 1], rng.choice(M, 10, replace=False)]):
+        assert gu.rel_err(dxf[m], (gf[m:m + 1] @ wf)[0]) < TOL, m
+    for n in np.concatenate([[0, N - 1], rng.choice(N, 10, replace=False)]):
+        assert gu.rel_err(dwf[n], gf[:, n] @ xf) < TOL, n
+    rb = gf.sum(axis=0)
+    assert np.abs(db.cpu().numpy() - rb).max() <= 1e-5 * np.abs(rb).max() + 1e-3
