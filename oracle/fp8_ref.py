@@ -1,5 +1,5 @@
-"""FP8 reference for the ESM-2 encoder forward: E4M3 codec, per-tensor delayed
-scaling, and an FP8-emulating layer.
+"""FP8 reference for the ESM-2 encoder: E4M3 codec, per-tensor delayed
+scaling, an FP8-emulating layer, and the E5M2 codec of the gradients.
 
 TEST INFRASTRUCTURE.  Only the test suite and the benchmark's CPU-baseline leg
 use this module; it shares no code with the HIP path.
@@ -91,6 +91,55 @@ def e4m3_to_f64(codes) -> np.ndarray:
 def quantize(x, scale: float) -> np.ndarray:
     """Value of cast_e4m3(x * scale), as float64 (still scaled)."""
     return e4m3_to_f64(e4m3_encode(np.asarray(x, np.float64) * scale))
+
+
+# ---------------------------------------------------------------- E5M2
+# The HYBRID format of [BIO-ACC] 4.1 keeps E4M3 for the forward and uses E5M2
+# for gradients.  Reading: OCP E5M2, 1 sign, 5 exponent (bias 15), 2 mantissa
+# bits; exponent 0 is subnormal (m/4 * 2^-14); exponent 31 holds +-inf
+# (mantissa 0) and NaN; the largest finite value is 57344.  Casting rounds to
+# nearest, ties to even, and saturates to +-57344 (as the E4M3 cast does).
+E5M2_MAX = 57344.0
+
+
+def e5m2_decode_table() -> np.ndarray:
+    """float64 value of each of the 256 E5M2 codes."""
+    vals = np.empty(256)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 2) & 0x1F
+        m = c & 0x3
+        if e == 0x1F:
+            vals[c] = s * np.inf if m == 0 else np.nan
+        elif e == 0:
+            vals[c] = s * (m / 4.0) * 2.0 ** -14
+        else:
+            vals[c] = s * (1.0 + m / 4.0) * 2.0 ** (e - 15)
+    return vals
+
+
+_TABLE52 = e5m2_decode_table()
+_POS_CODES52 = np.arange(0x7C)          # 0 .. 57344, increasing
+_POS_VALS52 = _TABLE52[_POS_CODES52]
+
+
+def e5m2_encode(x) -> np.ndarray:
+    """Nearest E5M2 code of each value (ties to the even code), saturating at
+    +-57344; NaN -> 0x7F."""
+    x = np.asarray(x, dtype=np.float64)
+    a_sat = np.minimum(np.abs(x), E5M2_MAX)
+    sign = np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    lo = np.clip(np.searchsorted(_POS_VALS52, a_sat, side="right") - 1, 0, len(_POS_VALS52) - 1)
+    hi = np.minimum(lo + 1, len(_POS_VALS52) - 1)
+    dlo, dhi = a_sat - _POS_VALS52[lo], _POS_VALS52[hi] - a_sat
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi != lo) & ((_POS_CODES52[hi] & 1) == 0))
+    out = (np.where(pick_hi, _POS_CODES52[hi], _POS_CODES52[lo]).astype(np.uint8) | sign).astype(np.uint8)
+    out[np.isnan(x)] = 0x7F
+    return out
+
+
+def e5m2_to_f64(codes) -> np.ndarray:
+    return _TABLE52[np.asarray(codes, dtype=np.uint8)]
 
 
 class DelayedScaling:

@@ -115,3 +115,40 @@ def test_fp8_layer_first_step_uses_unit_scales():
     x, cu, w, heads = _tiny(1)
     y = F8.layer_forward_fp8(x, cu, w, heads, {n: 1.0 for n in F8.ACT_NAMES})
     assert np.isfinite(y).all()
+
+
+# ---------------------------------------------------------------- E5M2
+
+def test_e5m2_decode_table_matches_torch():
+    import torch
+    codes = torch.arange(256, dtype=torch.int16).to(torch.uint8)
+    ref = codes.view(torch.float8_e5m2).to(torch.float64).numpy()
+    got = F8.e5m2_decode_table()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(got[m], ref[m])
+    assert F8.e5m2_to_f64([0x7B])[0] == 57344.0 and F8.e5m2_to_f64([0x01])[0] == 2.0 ** -16
+    assert np.isinf(F8.e5m2_to_f64([0x7C])[0])
+
+
+def test_e5m2_encode_matches_torch_in_range_and_saturates():
+    import torch
+    # float32 inputs (exact in both; torch casts float64 through float32, which
+    # would move a value just below a midpoint onto it): every value, every
+    # midpoint and its float32 neighbours, random values
+    vals = F8.e5m2_decode_table()[:0x7C].astype(np.float32)
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
+    x = np.concatenate([vals, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf)),
+                        (np.random.default_rng(5).standard_normal(4000) * 300).astype(np.float32)])
+    x = np.concatenate([x, -x])
+    x = x[np.abs(x) <= 57344.0]
+    ref = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(F8.e5m2_encode(x.astype(np.float64)), ref)
+    # saturation (the reading): beyond the largest finite value -> +-57344
+    assert list(F8.e5m2_encode([1e6, -61440.0, 60000.0])) == [0x7B, 0xFB, 0x7B]
+    # nearest by brute force
+    r = np.random.default_rng(6).uniform(-6e4, 6e4, 500)
+    fin = F8.e5m2_decode_table()[np.r_[0:0x7C, 0x80:0xFC]]
+    best = fin[np.argmin(np.abs(np.minimum(np.abs(r), 57344.0)[:, None] * np.sign(r)[:, None] - fin[None, :]), axis=1)]
+    assert np.all(np.abs(F8.e5m2_to_f64(F8.e5m2_encode(r)) - np.clip(r, -57344, 57344))
+                  <= np.abs(best - np.clip(r, -57344, 57344)) + 0.0)
