@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 13
+#define ESM_ABI_VERSION 14
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -442,6 +442,25 @@ esm_status esm_layernorm_bwd(esm_encoder* enc, const void* x, const void* gamma,
 
 /* Workspace bytes esm_layernorm_bwd needs for M rows of H values (host only). */
 esm_status esm_layernorm_bwd_workspace_size(int64_t M, int32_t H, size_t* bytes);
+
+/* FP8 backward of the HYBRID recipe ([BIO-ACC] 4.1: E4M3 in the forward, E5M2
+ * for the gradients).  E5M2 is the OCP format (1 sign, 5 exponent bits with
+ * bias 15, 2 mantissa bits, largest finite value 57344).
+ * esm_e5m2_quantize: y8[i] = cast_e5m2(x[i] * scale[0]), round to nearest
+ * even, saturating at +-57344; the max of |x| is folded into *amax (fp32 bits,
+ * caller-initialised).  x bf16 [n], n a multiple of 8, 16-byte aligned; y8
+ * 8-byte aligned; finite inputs.
+ * esm_linear_e5m2_dgrad: dx [M, K] bf16 = (dy8 / dy_scale) . (wt8 / w_scale)^T
+ * for dy8 E5M2 [M, N] (the gradient of y = x W^T) and wt8 E4M3 [K, N] (W^T
+ * cast with its scale): the data gradient dx = dy W on the scaled MFMA with the
+ * two operands in their own FP8 formats, fp32 accumulation.  N a multiple of
+ * 128, K of 64.  Errors: ESM_ERR_NULL, ESM_ERR_SHAPE, ESM_ERR_UNSUPPORTED
+ * (alignment).  Asynchronous on stream. */
+esm_status esm_e5m2_quantize(esm_encoder* enc, const void* x, int64_t n, const float* scale, void* y8,
+                             uint32_t* amax, esm_stream_t stream);
+esm_status esm_linear_e5m2_dgrad(esm_encoder* enc, const void* dy8, const float* dy_scale, const void* wt8,
+                                 const float* w_scale, void* dx, int64_t M, int32_t N, int32_t K,
+                                 esm_stream_t stream);
 
 /* Backward of the exact-erf GELU of fc1's epilogue ([BIO-ACC] 3.1; training
  * timed in [BIO-ACC] 3.2 and 6): dz[i] = dy[i] (Phi(z[i]) + z[i] phi(z[i]))

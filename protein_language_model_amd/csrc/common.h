@@ -39,6 +39,7 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 constexpr int kBF16 = 0;
 constexpr int kE4M3 = 1;
 constexpr int kFP4 = 2;   // MXFP4: E2M1 codes, one E8M0 scale per 32 values along K
+constexpr int kE5M2X = 3; // x operand E5M2 (a gradient), w operand E4M3: the HYBRID recipe's backward GEMM
 constexpr float kE4M3Max = 448.0f;
 
 // Four values v * s cast to OCP E4M3 (1.4.3, bias 7, no infinity, 0x7F = NaN,
@@ -343,6 +344,8 @@ hipError_t launch_quantize_f32(const float* x, int64_t n, const float* scale, ui
                                hipStream_t st);
 // End of a step for layers [l0, l0 + nl): push amax into the history, new scale
 // = 448 / max(history) when that is positive and finite, clear amax.
+hipError_t launch_quantize_e5m2(const bf16_t* x, int64_t n, const float* scale, uint8_t* y, uint32_t* amax,
+                                hipStream_t st);
 hipError_t launch_scale_update(const Fp8State& s, int32_t l0, int32_t nl, hipStream_t st);
 
 }  // namespace esm

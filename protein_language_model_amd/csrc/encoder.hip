@@ -1226,6 +1226,39 @@ esm_status esm_layernorm_bwd(esm_encoder* e, const void* x, const void* gamma, c
   });
 }
 
+esm_status esm_e5m2_quantize(esm_encoder* e, const void* x, int64_t n, const float* scale, void* y8, uint32_t* amax,
+                             esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !x || !scale || !y8 || !amax) return fail(ESM_ERR_NULL, "NULL argument");
+  if (n < 0 || n % 8) return fail(ESM_ERR_SHAPE, "n %lld: a non-negative multiple of 8", (long long)n);
+  if (!aligned16(x) || ((uintptr_t)y8 & 7u) || ((uintptr_t)scale & 3u) || ((uintptr_t)amax & 3u))
+    return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer");
+  if (n == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  return timed(e, ESM_K_LINEAR_BWD, st, "e5m2 quantize", [&] {
+    return launch_quantize_e5m2((const bf16_t*)x, n, scale, (uint8_t*)y8, amax, st);
+  });
+}
+
+esm_status esm_linear_e5m2_dgrad(esm_encoder* e, const void* dy8, const float* dy_scale, const void* wt8,
+                                 const float* w_scale, void* dx, int64_t M, int32_t N, int32_t K,
+                                 esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !dy8 || !dy_scale || !wt8 || !w_scale || !dx) return fail(ESM_ERR_NULL, "NULL argument");
+  if (M < 0 || N <= 0 || K <= 0 || N % 128 || K % 64)
+    return fail(ESM_ERR_SHAPE, "M %lld N %d K %d: N a positive multiple of 128, K of 64", (long long)M, N, K);
+  if (!aligned16(dy8) || !aligned16(wt8) || !aligned16(dx)) return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer");
+  if (M == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  GemmArgs g{};
+  g.dtype = kE5M2X;
+  g.x = dy8; g.w = wt8; g.x_scale = dy_scale; g.w_scale = w_scale;
+  g.y = (bf16_t*)dx; g.M = M; g.N = K; g.K = N;
+  return timed(e, ESM_K_LINEAR_BWD, st, "e5m2 dgrad", [&] { return launch_gemm(EPI_BIAS, g, st); });
+}
+
 esm_status esm_gelu_bwd(esm_encoder* e, const void* z, const void* dy, void* dz, int64_t n, esm_stream_t stream) {
   g_last_error.clear();
   if (!e || !z || !dy || !dz) return fail(ESM_ERR_NULL, "NULL argument");

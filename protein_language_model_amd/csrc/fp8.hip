@@ -55,6 +55,39 @@ __global__ __launch_bounds__(256) void k_quantize_f32(const float* __restrict__ 
   record_amax_block<4>(amax, m, red);
 }
 
+// E5M2 cast of a bf16 gradient tensor (the HYBRID recipe): y = cast(x * s),
+// round to nearest even (gfx950's v_cvt_pk_bf8_f32) after clamping to
+// +-57344, so it saturates; amax of |x| recorded.  8 values per thread.
+__global__ __launch_bounds__(256) void k_quantize_e5m2(const bf16_t* __restrict__ x, int64_t n8,
+                                                       const float* __restrict__ scale, uint8_t* __restrict__ y,
+                                                       uint32_t* amax) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float m = 0.f;
+  if (i < n8) {
+    const u32x4 w = *(const u32x4*)(x + 8 * i);
+    const float s = scale[0];
+    constexpr float kMax = 57344.0f;
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bflo(w[e]);
+      v[2 * e + 1] = bfhi(w[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    float c[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c[e] = __builtin_amdgcn_fmed3f(v[e] * s, -kMax, kMax);
+    int lo = __builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_bf8_f32(c[4], c[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_bf8_f32(c[6], c[7], hi, true);
+    *(u32x2*)(y + 8 * i) = u32x2{(uint32_t)lo, (uint32_t)hi};
+  }
+  __shared__ float red[4];
+  record_amax_block<4>(amax, m, red);
+}
+
 // One thread per layer: its four activation tensors share the step counter.
 __global__ void k_scale_update(Fp8State s, int32_t l0, int32_t nl) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -108,6 +141,15 @@ hipError_t launch_quantize_f32(const float* x, int64_t n, const float* scale, ui
                                hipStream_t st) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_quantize_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, n, scale, y, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_e5m2(const bf16_t* x, int64_t n, const float* scale, uint8_t* y, uint32_t* amax,
+                                hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(k_quantize_e5m2, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, x, n8, scale, y, amax);
   return hipGetLastError();
 }
 

@@ -92,6 +92,8 @@ struct Frag<kE4M3> {
   static constexpr int kSub = 64;
 };
 template <>
+struct Frag<kE5M2X> : Frag<kE4M3> {};
+template <>
 struct Frag<kFP4> {
   typedef i32x8 T;  // 32 E2M1 along K (one MX block) in the low 4 registers: one 64-wide sub-step
   static constexpr int kSub = 64;
@@ -304,6 +306,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
         if constexpr (DT == kE4M3)
           // cbsz = blgp = 0: both operands E4M3; block scales 127 = 2^0.
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 0, 0, 0, 127, 0, 127);
+        else if constexpr (DT == kE5M2X)
+          // blgp = 1: operand B (the x rows) E5M2; cbsz = 0: operand A (w) E4M3.
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 0, 1, 0, 127, 0, 127);
         else if constexpr (DT == kBF16)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
       }
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       vm_wait_all();
       __syncthreads();
     }
-  } else if constexpr (DT == kE4M3) {
+  } else if constexpr (DT == kE4M3 || DT == kE5M2X) {
     // One fragment set (8 registers per 32-byte fragment; a second set would
     // not fit beside the 128 accumulators at two waves per SIMD): the other
     // wave on the SIMD multiplies while this one waits for its LDS reads.
@@ -466,7 +471,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   res_load(0);
   const bf16_t* __restrict__ bias = a.bias;
   float dq = 1.0f;
-  if constexpr (DT == kE4M3) dq = 1.0f / (a.x_scale[0] * a.w_scale[0]);
+  if constexpr (DT == kE4M3 || DT == kE5M2X) dq = 1.0f / (a.x_scale[0] * a.w_scale[0]);
   float oscale = 1.0f, amax = 0.0f;
   if constexpr (OUT8) oscale = a.y8_scale[0];
   // Bias of this lane's output columns nw + 32 j + 8 gq + 4 lhalf + 0..3,
@@ -692,6 +697,12 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   const int64_t r256 = ((a.M + 255) / 256 * tilesN + cus - 1) / cus;
   const int64_t r320 = ((a.M + 319) / 320 * tilesN + cus - 1) / cus;
   const bool tall = r320 * 320 <= r256 * 256;
+  if (a.dtype == kE5M2X) {
+    // the backward's data-gradient GEMM: plain product, bias epilogue only
+    if constexpr (EPI == EPI_BIAS)
+      return tall ? run<320, 256, 2, 4, EPI, kE5M2X>(a, st) : run<256, 256, 2, 4, EPI, kE5M2X>(a, st);
+    else return hipErrorInvalidValue;
+  }
   if constexpr (EPI == EPI_BIAS_GELU_MX) {
     if (a.dtype != kFP4) return hipErrorInvalidValue;
   } else if (a.dtype == kE4M3) {
@@ -711,7 +722,7 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
-  const int kb = a.dtype == kFP4 ? 2 * kRowBytes : (a.dtype == kE4M3 ? kRowBytes : kRowBytes / 2);
+  const int kb = a.dtype == kFP4 ? 2 * kRowBytes : (a.dtype == kE4M3 || a.dtype == kE5M2X ? kRowBytes : kRowBytes / 2);
   if (a.K % kb != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_BIAS: return dispatch<EPI_BIAS>(a, st);

@@ -89,6 +89,8 @@ SIGNATURES = {
     "esm_layernorm_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _p, _sz, _p]),
     "esm_layernorm_bwd_workspace_size": (_i32, [_i64, _i32, _p]),
     "esm_gelu_bwd": (_i32, [_p, _p, _p, _p, _i64, _p]),
+    "esm_e5m2_quantize": (_i32, [_p, _p, _i64, _p, _p, _p, _p]),
+    "esm_linear_e5m2_dgrad": (_i32, [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _p]),
     "esm_qkv_rope_bwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_attention_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_biased_attention_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
@@ -413,6 +415,28 @@ class Encoder:
         _call("esm_layernorm_bwd", self._h, _ptr(x), _ptr(gamma), _ptr(dy), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
               int(M), _ptr(workspace), workspace.numel(), _stream(stream))
         return dx, dgamma, dbeta
+
+    def e5m2_quantize(self, x, scale, *, y8=None, amax=None, stream=None):
+        """(y8 uint8 codes of cast_e5m2(x * scale[0]), amax fp32-bits int32 [1]) for bf16 x."""
+        import torch
+        if y8 is None:
+            y8 = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        if amax is None:
+            amax = torch.zeros((1,), dtype=torch.int32, device=x.device)
+        _call("esm_e5m2_quantize", self._h, _ptr(x), int(x.numel()), _ptr(scale), _ptr(y8), _ptr(amax),
+              _stream(stream))
+        return y8, amax
+
+    def linear_e5m2_dgrad(self, dy8, dy_scale, wt8, w_scale, *, dx=None, stream=None):
+        """dx [M, K] bf16 = (dy8 / dy_scale) (wt8 / w_scale)^T with dy8 E5M2 [M, N], wt8 E4M3 [K, N]."""
+        import torch
+        M, N = dy8.shape
+        K = wt8.shape[0]
+        if dx is None:
+            dx = torch.empty((M, K), dtype=torch.bfloat16, device=dy8.device)
+        _call("esm_linear_e5m2_dgrad", self._h, _ptr(dy8), _ptr(dy_scale), _ptr(wt8), _ptr(w_scale), _ptr(dx),
+              int(M), int(N), int(K), _stream(stream))
+        return dx
 
     def gelu_bwd(self, z, dy, *, dz=None, stream=None):
         """dz = dy * GELU'(z) (bf16, same shape; the element count a multiple of 8)."""
