@@ -185,8 +185,10 @@ esm_status esm_workspace_region(const esm_encoder* enc, int64_t max_tokens, int3
  *
  * MXFP4 precision (ESM_PRECISION_MXFP4; the FP4 recipe of [TE-ESM2]
  * FP8与FP4混合精度支持, read as OCP MXFP4, see esm_mxfp4_quantize): each linear
- * computes x_q . W_q^T + b with x the bf16 GEMM input quantised per 32-value
- * block on every call (no state) and W_q from esm_mxfp4_prepare_layer
+ * computes x_q . W_q^T + b with x_q the GEMM input written straight in MXFP4
+ * (32-value blocks along K) by its producer from fp32 values -- LayerNorm,
+ * the attention epilogue, fc1's GELU epilogue -- on every call (no state, no
+ * bf16 copy of the input) and W_q from esm_mxfp4_prepare_layer
  * (ESM_ERR_STATE if never called for layer_idx); LayerNorm, attention, the
  * residuals and every GEMM output stay in bf16/fp32.  Needs hidden_size and
  * intermediate_size multiples of 256 and intermediate_size <= 8 hidden_size

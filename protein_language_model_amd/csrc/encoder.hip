@@ -1154,35 +1154,47 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
     // (fp32 partial products summed in slice order), and it runs on the side
     // stream, forked from and joined back to st, beside the dx GEMM and the
     // column sums.  The workspace regions of the two paths are disjoint.
+    // Once the side stream has been forked it is joined back to st on every
+    // return, errors included, so that no work on ws or dw is left running
+    // behind the caller's stream.
+    bool forked = false;
     if (dw) {
-      // dW [N, K] = dy^T [N, M64] . (x^T [K, M64])^T, zero columns past M
       if ((r = hipEventRecord(e->fork, st))) return r;
       if ((r = hipStreamWaitEvent(e->side, e->fork, 0))) return r;
-      if ((r = launch_transpose_pad((const bf16_t*)dy, M, N, dyt, M64, e->side))) return r;
-      if ((r = launch_transpose_pad((const bf16_t*)x, M, K, xt, M64, e->side))) return r;
-      GemmArgs g{};
-      g.dtype = kBF16;
-      g.x = dyt; g.w = xt; g.y = (bf16_t*)dw; g.M = N; g.N = K; g.K = M64;
-      if (pl.splits > 1) {
-        // split-K: each K slice's fp32 product, then their sum in slice order
-        g.y32 = wpart; g.ksplit = pl.splits;
-        if ((r = launch_gemm(EPI_F32_SPLIT, g, e->side))) return r;
-        if ((r = launch_split_reduce(wpart, pl.splits, (int64_t)N * K, (bf16_t*)dw, e->side))) return r;
-      } else if ((r = launch_gemm(EPI_BIAS, g, e->side))) {
-        return r;
+      forked = true;
+      // dW [N, K] = dy^T [N, M64] . (x^T [K, M64])^T, zero columns past M
+      r = launch_transpose_pad((const bf16_t*)dy, M, N, dyt, M64, e->side);
+      if (!r) r = launch_transpose_pad((const bf16_t*)x, M, K, xt, M64, e->side);
+      if (!r) {
+        GemmArgs g{};
+        g.dtype = kBF16;
+        g.x = dyt; g.w = xt; g.y = (bf16_t*)dw; g.M = N; g.N = K; g.K = M64;
+        if (pl.splits > 1) {
+          // split-K: each K slice's fp32 product, then their sum in slice order
+          g.y32 = wpart; g.ksplit = pl.splits;
+          r = launch_gemm(EPI_F32_SPLIT, g, e->side);
+          if (!r) r = launch_split_reduce(wpart, pl.splits, (int64_t)N * K, (bf16_t*)dw, e->side);
+        } else {
+          r = launch_gemm(EPI_BIAS, g, e->side);
+        }
       }
-      if ((r = hipEventRecord(e->join, e->side))) return r;
     }
-    if (dx) {
+    if (!r && dx) {
       // dx [M, K] = dy [M, N] . (W^T [K, N])^T
-      if ((r = launch_transpose_pad((const bf16_t*)w, N, K, wt, N, st))) return r;
-      GemmArgs g{};
-      g.dtype = kBF16;
-      g.x = dy; g.w = wt; g.y = (bf16_t*)dx; g.M = M; g.N = K; g.K = N;
-      if ((r = launch_gemm(EPI_BIAS, g, st))) return r;
+      r = launch_transpose_pad((const bf16_t*)w, N, K, wt, N, st);
+      if (!r) {
+        GemmArgs g{};
+        g.dtype = kBF16;
+        g.x = dy; g.w = wt; g.y = (bf16_t*)dx; g.M = M; g.N = K; g.K = N;
+        r = launch_gemm(EPI_BIAS, g, st);
+      }
     }
-    if (db && (r = launch_colsum((const bf16_t*)dy, M, N, part, db, st))) return r;
-    if (dw && (r = hipStreamWaitEvent(st, e->join, 0))) return r;
+    if (!r && db) r = launch_colsum((const bf16_t*)dy, M, N, part, db, st);
+    if (forked) {
+      hipError_t j = hipEventRecord(e->join, e->side);
+      if (!j) j = hipStreamWaitEvent(st, e->join, 0);
+      if (!r) r = j;
+    }
     return r;
   });
 }

@@ -57,7 +57,10 @@ __global__ __launch_bounds__(256) void k_quantize_f32(const float* __restrict__ 
 
 // E5M2 cast of a bf16 gradient tensor (the HYBRID recipe): y = cast(x * s),
 // round to nearest even (gfx950's v_cvt_pk_bf8_f32) after clamping to
-// +-57344, so it saturates; amax of |x| recorded.  8 values per thread.
+// +-57344, so it saturates (infinities included); a NaN input is written as
+// the NaN code 0x7F (the clamp alone would turn it into a finite value), so
+// it reaches the GEMM that reads the codes; amax of |x| recorded (NaN left
+// out, as for the E4M3 casts).  8 values per thread.
 __global__ __launch_bounds__(256) void k_quantize_e5m2(const bf16_t* __restrict__ x, int64_t n8,
                                                        const float* __restrict__ scale, uint8_t* __restrict__ y,
                                                        uint32_t* amax) {
@@ -82,7 +85,15 @@ __global__ __launch_bounds__(256) void k_quantize_e5m2(const bf16_t* __restrict_
     lo = __builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], lo, true);
     int hi = __builtin_amdgcn_cvt_pk_bf8_f32(c[4], c[5], 0, false);
     hi = __builtin_amdgcn_cvt_pk_bf8_f32(c[6], c[7], hi, true);
-    *(u32x2*)(y + 8 * i) = u32x2{(uint32_t)lo, (uint32_t)hi};
+    uint32_t r[2] = {(uint32_t)lo, (uint32_t)hi};
+    // the sum is NaN iff a value is NaN or both infinities are present
+    const float chk = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    if (chk != chk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (v[e] != v[e]) r[e / 4] = (r[e / 4] & ~(0xFFu << (8 * (e % 4)))) | (0x7Fu << (8 * (e % 4)));
+    }
+    *(u32x2*)(y + 8 * i) = u32x2{r[0], r[1]};
   }
   __shared__ float red[4];
   record_amax_block<4>(amax, m, red);

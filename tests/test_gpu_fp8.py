@@ -25,6 +25,14 @@ TOL_FP8 = 6e-2      # per-layer max|gpu - ref| / max|ref| against the plain orac
 # GELU output) amplify that.  Measured 1.6-2.0e-2 on seeded inputs; the gate
 # is half the FP8 gate.
 TOL_EMU = 3e-2
+# The embedding-driven 33-layer stack (N(0, 0.02) embedding): in its first two
+# layers the residual stream is still tiny, so the layer output is almost all
+# FFN branch, and every E4M3 code of the LN2 output that the bf16 storage of
+# x1 moves by one step (2^-3 relative at the top of a binade) reaches the
+# output through fc1, GELU, a second cast and fc2 undiluted by the residual.
+# Measured library vs emulation: 4.4e-2 (layer 0), 3.9e-2 (layer 1), then
+# 2.0e-2 and below; on N(0, 1) inputs every layer stays within TOL_EMU.
+TOL_EMU_SMALL_RESIDUAL = 5e-2
 DEV = "cuda:0"
 
 
@@ -344,20 +352,16 @@ SPIKES = [8.0, 3.0, 5.0, 12.0, 4.0, 4.5, 6.0, 3.5, 9.0, 5.5, 4.0]
 TOL_AMAX = 1e-2   # library amax (fp32, bf16 intermediates) vs the fp64 emulation
 
 
-@pytest.mark.parametrize("history_len", [16, 4])
-def test_tiny_delayed_scaling_follows_the_oracle_state_machine(gu, history_len):
+def _follow_state_machine(gu, m, b, wd, wr, history_len, label):
     """Repeated layer steps: after every step the library's amax history,
-    step count and scales match the oracle's state machine fed the same
-    inputs, and each step's output matches the emulating oracle with the
-    scales that step used."""
-    wl = D.WORKLOADS["tiny"]
-    m = TINY8
-    b = D.make_batch(wl)
+    step count and scales match the oracle's state machine fed the amax of
+    the emulating oracle, and each step's output matches the emulating
+    oracle with the scales that step used."""
     enc = _encoder(m, history_len=history_len)
-    wd, wr, _ = gu.layer_weights(m.hidden, m.ffn, 0)
     enc.fp8_prepare_layer(0, wd)
     cu_d = gu.to_dev_i32(b.cu_seqlens)
     states = {n: F8.DelayedScaling(history_len) for n in F8.ACT_NAMES}
+    e_emu = []
     for step, spike in enumerate(SPIKES):
         x = D.bf16_bits_to_f64(D.make_hidden(b.T, m.hidden, step, 2))
         x[5, 7] = spike
@@ -370,7 +374,8 @@ def test_tiny_delayed_scaling_follows_the_oracle_state_machine(gu, history_len):
         y = enc.layer_fwd(wd, gu.to_dev_bf16(xb), cu_d, b.B, b.T, b.max_seqlen, layer_idx=0)
         emu, amax = F8.layer_forward_fp8(x, b.cu_seqlens, wr, m.heads, scales, return_amax=True)
         got = gu.from_dev(y)
-        assert gu.rel_err(got, emu) < TOL_EMU, step
+        e_emu.append(gu.rel_err(got, emu))
+        assert e_emu[-1] < TOL_EMU, step
         for n in F8.ACT_NAMES:
             states[n].record(amax[n])
         after = enc.fp8_get_state()
@@ -382,9 +387,31 @@ def test_tiny_delayed_scaling_follows_the_oracle_state_machine(gu, history_len):
             # scale = 448 / max(history), one fp32 division
             assert after["act_scale"][0, i] == np.float32(448.0) / np.max(hist[i])
     err = gu.rel_err(got, O.layer_forward(x, b.cu_seqlens, wr, m.heads))
-    print(f"tiny FP8 layer (history {history_len}) after {len(SPIKES)} steps: rel err vs fp64 {err:.2e}")
+    print(f"{label} FP8 layer (history {history_len}) after {len(SPIKES)} steps: rel err vs fp64 {err:.2e}, "
+          f"vs emulation max {max(e_emu):.2e}")
     assert 1e-4 < err < TOL_FP8
     enc.close()
+
+
+@pytest.mark.parametrize("history_len", [16, 4])
+def test_tiny_delayed_scaling_follows_the_oracle_state_machine(gu, history_len):
+    wl = D.WORKLOADS["tiny"]
+    m = TINY8
+    wd, wr, _ = gu.layer_weights(m.hidden, m.ffn, 0)
+    _follow_state_machine(gu, m, D.make_batch(wl), wd, wr, history_len, "tiny")
+
+
+def test_650m_delayed_scaling_follows_the_oracle_state_machine(gu):
+    """The same state-machine check at the 650M layer's widths (hidden 1280,
+    20 heads, FFN 5120, its seeded weights), on the first eight sequences of
+    the 650M single-layer batch (the amax are whole-tensor maxima, so the
+    oracle runs the whole sub-batch every step)."""
+    wl = D.WORKLOADS["650m_layer"]
+    m = wl.model
+    full = D.make_batch(wl)
+    b = D.make_batch(wl, lengths=full.lengths[:8])
+    wd, wr, _ = gu.layer_weights(m.hidden, m.ffn, 0)
+    _follow_state_machine(gu, m, b, wd, wr, 16, "650M")
 
 
 def test_state_round_trip_and_reset(gu):
@@ -541,9 +568,11 @@ def test_650m_fp8_stack_33_layers_teacher_forced(gu):
     embedding (N(0, 0.02)), so the output is mostly the FFN branch, which
     passes two E4M3 casts in series; there the recipe itself, computed
     exactly by the emulating oracle, is further than 6e-2 from fp64 (about
-    9e-2 at layer 0), and the bf16 storage of x1 and q, k, v moves codes of
-    the second cast.  The gate is therefore the recipe's own error plus the
-    kernel margin, and never looser than the FP8 gate."""
+    8e-2 at layer 0), and the bf16 storage of x1 and q, k, v moves codes of
+    the casts.  The gate against fp64 is therefore the recipe's own error
+    plus the kernel margin, never looser than the FP8 gate; against the
+    emulation it is TOL_EMU, and TOL_EMU_SMALL_RESIDUAL in the two layers
+    whose residual stream is still the small embedding."""
     wl = D.WORKLOADS["650m"]
     m = wl.model
     b = D.make_batch(wl)
@@ -583,4 +612,4 @@ def test_650m_fp8_stack_33_layers_teacher_forced(gu):
     print("650M FP8 stack, per layer: emulation vs fp64:", fmt(e_recipe))
     for l in range(m.layers):
         assert e_plain[l] < max(TOL_FP8, e_recipe[l] + TOL_EMU), (l, e_plain[l], e_recipe[l])
-        assert e_emu[l] < max(TOL_EMU, e_recipe[l]), (l, e_emu[l], e_recipe[l])
+        assert e_emu[l] < (TOL_EMU_SMALL_RESIDUAL if l < 2 else TOL_EMU), (l, e_emu[l], e_recipe[l])

@@ -1,6 +1,8 @@
 """Layer- and stack-level parity of the HIP path against the fp64 oracle, and
 the bit-exact index invariants (packed == alone, THD == bshd on valid rows,
 permutation, NaN padding, determinism)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -111,6 +113,72 @@ def test_bad_host_cu_seqlens_is_rejected_before_launch(gu, tiny):
     assert ei.value.status == 3
 
 
+def _bshd_stack_case(gu, m, lengths, layers, S, seed):
+    """Token ids [B, S] right-padded with out-of-range garbage ids (the
+    library clamps ids, so they are still read), and the same sequences
+    packed; returns (bshd output bits [B, S, H], THD output bits [T, H],
+    weights, embedding bits, ids [B, S])."""
+    enc = _encoder(m, layers)
+    lengths = np.asarray(lengths, np.int32)
+    B = len(lengths)
+    r = np.random.default_rng(seed)
+    ids = r.integers(0, m.vocab, (B, S)).astype(np.int32)
+    for i in range(B):
+        ids[i, lengths[i]:] = r.integers(-5, m.vocab + 40, S - lengths[i])
+    emb = D.make_embedding(m.vocab, m.hidden, seed=seed)
+    wd = [D.make_layer_weights_device(m.hidden, m.ffn, l, seed=seed) for l in range(layers)]
+    yb = enc.stack_fwd_bshd(wd, gu.to_dev_i32(lengths), B, S, token_ids=gu.to_dev_i32(ids),
+                            embedding=gu.to_dev_bf16(emb), seqlens_host=lengths)
+    packed = np.concatenate([ids[i, :lengths[i]] for i in range(B)])
+    cu = D.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    yt = enc.stack_fwd(wd, gu.to_dev_i32(cu), B, T, int(lengths.max()), token_ids=gu.to_dev_i32(packed),
+                       embedding=gu.to_dev_bf16(emb), cu_seqlens_host=cu)
+    out = gu.bits_of(yb).reshape(B, S, m.hidden), gu.bits_of(yt), wd, emb, ids
+    enc.close()
+    return out
+
+
+def test_stack_bshd_from_ids_matches_thd_and_the_oracle(gu):
+    """esm_stack_fwd_bshd from padded token ids (3 layers, hidden 320): valid
+    rows bit-equal to the packed stack, padded rows written as 0, and the
+    valid rows against the oracle's padded layers chained (free-running,
+    within the depth tolerance)."""
+    m = D.WORKLOADS["tiny"].model
+    lengths = [17, 64, 0, 100, 200, 1]
+    S, layers = 224, 3
+    yb, yt, wd, emb, ids = _bshd_stack_case(gu, m, lengths, layers, S, seed=3)
+    cu = D.cu_from_lengths(lengths)
+    for i, L in enumerate(lengths):
+        assert np.array_equal(yb[i, :L], yt[cu[i]:cu[i + 1]]), i
+        assert not np.any(yb[i, L:]), i
+    # oracle: padded rows NaN (they must never reach a valid row)
+    e0 = D.bf16_bits_to_f64(emb)
+    x = np.full((len(lengths), S, m.hidden), np.nan)
+    for i, L in enumerate(lengths):
+        x[i, :L] = e0[ids[i, :L]]
+    for l in range(layers):
+        wr = O.weights_to_f64({k: D.tensor_bits(v) for k, v in wd[l].items()})
+        x = O.layer_forward_bshd(x, lengths, wr, m.heads)
+    got = D.bf16_bits_to_f64(yb)
+    for i, L in enumerate(lengths):
+        if L:
+            assert gu.rel_err(got[i, :L], x[i, :L]) < _depth_tol(layers - 1), i
+
+
+def test_650m_stack_bshd_equals_thd_bitexact(gu):
+    """Two 650M-width layers on twelve sequences of the 650M batch padded to
+    S = 1024 (the padded benchmark's S): valid rows bit-equal to the packed
+    stack, padded rows 0."""
+    wl = D.WORKLOADS["650m"]
+    lengths = D.make_batch(wl).lengths[:12]
+    yb, yt, *_ = _bshd_stack_case(gu, dataclasses.replace(wl.model, layers=2), lengths, 2, 1024, seed=0)
+    cu = D.cu_from_lengths(lengths)
+    for i, L in enumerate(lengths):
+        assert np.array_equal(yb[i, :L], yt[cu[i]:cu[i + 1]]), i
+        assert not np.any(yb[i, L:]), i
+
+
 # ------------------------------------------------------------- 650M single layer
 
 @pytest.fixture(scope="module")
@@ -185,11 +253,17 @@ def test_650m_deterministic(gu, l650):
 
 # ------------------------------------------------------------- full stacks, sampled
 
-def _stack_free_running(gu, wl, sample_seqs):
-    """Chained esm_layer_fwd calls over the whole batch; each layer output on a
-    sample of sequences is compared with the oracle run free from the same
-    seeded inputs (sequences are independent, so the sample can be computed
-    alone).  The final output must also equal one esm_stack_fwd call."""
+def _stack_layers(gu, wl, tf_seqs, fr_seqs):
+    """Chained esm_layer_fwd calls over the whole batch from token ids; the
+    final output must equal one esm_stack_fwd call bit for bit.  Each layer's
+    output is checked on sampled sequences (sequences are independent, so a
+    sample can be computed alone) in two ways:
+      * teacher-forced (the gate): the oracle layer l is fed the library's
+        own layer-(l-1) output on the tf_seqs rows, upcast exactly, so every
+        layer is judged on its real activations;
+      * free-running (reported): the oracle runs the whole stack from the
+        same embedding on the fr_seqs rows.
+    Returns (teacher-forced errors, free-running errors) per layer."""
     m = wl.model
     enc = _encoder(m, m.layers)
     b = D.make_batch(wl)
@@ -200,19 +274,28 @@ def _stack_free_running(gu, wl, sample_seqs):
     stack = enc.stack_fwd(wd_all, cu_d, b.B, b.T, b.max_seqlen, token_ids=gu.to_dev_i32(b.ids),
                           embedding=gu.to_dev_bf16(emb), cu_seqlens_host=b.cu_seqlens, workspace=ws)
     stack_bits = gu.bits_of(stack)
-    rows = np.concatenate([np.arange(b.cu_seqlens[s], b.cu_seqlens[s + 1]) for s in sample_seqs])
-    sub_cu = D.cu_from_lengths(b.lengths[sample_seqs])
-    ref = D.bf16_bits_to_f64(emb)[b.ids[rows]]
+
+    def rows_of(seqs):
+        return (np.concatenate([np.arange(b.cu_seqlens[s], b.cu_seqlens[s + 1]) for s in seqs]),
+                D.cu_from_lengths(b.lengths[seqs]))
+
+    tf_rows, tf_cu = rows_of(tf_seqs)
+    fr_rows, fr_cu = rows_of(fr_seqs)
+    e0 = D.bf16_bits_to_f64(emb)
+    tf_in, fr_ref = e0[b.ids[tf_rows]], e0[b.ids[fr_rows]]
     cur = gu.to_dev_bf16(emb[b.ids])
-    errs = []
+    e_tf, e_fr = [], []
     for l in range(m.layers):
         cur = enc.layer_fwd(wd_all[l], cur, cu_d, b.B, b.T, b.max_seqlen, layer_idx=l, workspace=ws)
+        y = gu.from_dev(cur)
         wr = O.weights_to_f64({k: D.tensor_bits(v) for k, v in wd_all[l].items()})
-        ref = O.layer_forward(ref, sub_cu, wr, m.heads)
-        errs.append(gu.rel_err(gu.from_dev(cur)[rows], ref))
+        e_tf.append(gu.rel_err(y[tf_rows], O.layer_forward(tf_in, tf_cu, wr, m.heads)))
+        tf_in = y[tf_rows]
+        fr_ref = O.layer_forward(fr_ref, fr_cu, wr, m.heads)
+        e_fr.append(gu.rel_err(y[fr_rows], fr_ref))
     assert np.array_equal(gu.bits_of(cur), stack_bits), "stack differs from chained layer calls"
     enc.close()
-    return errs
+    return e_tf, e_fr
 
 
 def _depth_tol(l: int) -> float:
@@ -222,25 +305,38 @@ def _depth_tol(l: int) -> float:
     return TOL * float(np.sqrt(l + 1))
 
 
-def test_650m_stack_33_layers_sampled(gu):
+def _short_median_long(b):
+    order = np.argsort(b.lengths, kind="stable")
+    return sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+
+
+def test_650m_stack_33_layers_every_layer_teacher_forced(gu):
+    """cfg 650M: 87 packed sequences (T = 32293), 33 layers from token ids;
+    the per-layer gate on the shortest, median and longest (997 residues)
+    sequences."""
     wl = D.WORKLOADS["650m"]
     b = D.make_batch(wl)
-    order = np.argsort(b.lengths, kind="stable")
-    sample = sorted({int(order[0]), int(order[len(order) // 2])})
-    errs = _stack_free_running(gu, wl, sample)
-    print("650M free-running per-layer errors:", " ".join(f"{e:.1e}" for e in errs))
-    assert errs[0] < TOL
-    assert all(e < _depth_tol(l) for l, e in enumerate(errs)), errs
+    sample = _short_median_long(b)
+    assert int(b.lengths.max()) in b.lengths[sample]
+    e_tf, e_fr = _stack_layers(gu, wl, sample, sample)
+    print("650M per-layer errors, teacher-forced:", " ".join(f"{e:.1e}" for e in e_tf))
+    print("650M per-layer errors, free-running:", " ".join(f"{e:.1e}" for e in e_fr))
+    assert max(e_tf) < TOL, e_tf
+    assert all(e < _depth_tol(l) for l, e in enumerate(e_fr)), e_fr
 
 
-def test_3b_stack_36_layers_sampled(gu):
+def test_3b_stack_36_layers_every_layer_teacher_forced(gu):
+    """cfg 3B-shaped: 39 packed sequences (T = 16208), 36 layers of hidden
+    2560; the per-layer gate on the shortest and the longest (908 residues)
+    sequences, free-running reported on the shortest."""
     wl = D.WORKLOADS["3b"]
     b = D.make_batch(wl)
-    sample = [int(np.argmin(b.lengths))]
-    errs = _stack_free_running(gu, wl, sample)
-    print("3B free-running per-layer errors:", " ".join(f"{e:.1e}" for e in errs))
-    assert errs[0] < TOL
-    assert all(e < _depth_tol(l) for l, e in enumerate(errs)), errs
+    sample = sorted({int(np.argmin(b.lengths)), int(np.argmax(b.lengths))})
+    e_tf, e_fr = _stack_layers(gu, wl, sample, [int(np.argmin(b.lengths))])
+    print("3B per-layer errors, teacher-forced:", " ".join(f"{e:.1e}" for e in e_tf))
+    print("3B per-layer errors, free-running:", " ".join(f"{e:.1e}" for e in e_fr))
+    assert max(e_tf) < TOL, e_tf
+    assert all(e < _depth_tol(l) for l, e in enumerate(e_fr)), e_fr
 
 
 @pytest.mark.parametrize("name", ["650m", "3b"])

@@ -8,8 +8,9 @@ Saved activations: the fp64 forward's h1, rotated q and k, v, x1, h2, the fc1
 pre-activation z and a = GELU(z), each rounded to bf16 (what a bf16 forward
 keeps); the attention context and lse come from esm_attention_fwd_lse on those
 q, k, v.  The residual adds of the gradient are fp32 additions in the test.
-Tolerance: every gradient within 2e-2 (max|err| / max|ref|): a chain of about
-ten bf16 roundings (2^-9 each) of operands and results.
+Tolerance: every gradient within 1e-2 (max|err| / max|ref|), the forward's
+per-layer bound: a chain of about ten bf16 roundings (2^-9 each) of operands
+and results; measured at most 4.8e-3 (w_fc1) on the seeded inputs.
 """
 import numpy as np
 import pytest
@@ -21,7 +22,7 @@ from protein_language_model_amd import esm
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-2
+TOL = 1e-2
 
 
 @pytest.fixture(scope="module")
