@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 14
+#define ESM_ABI_VERSION 15
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -198,6 +198,25 @@ esm_status esm_layer_fwd(esm_encoder* enc, const esm_layer_weights* w, int32_t l
                          const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                          int32_t B, int64_t T, int32_t max_seqlen,
                          void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* Allocation-free variant of esm_layer_fwd, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, semantics and results (bit for bit)
+ * as esm_layer_fwd, without the workspace: the layer's intermediates go to a
+ * library scratch array of ESM_NOALLOC_SCRATCH_BYTES per device, held from
+ * load until the process ends.  The call allocates nothing and records no
+ * esm_profile_* timing.  A batch whose workspace (esm_workspace_size(T, B))
+ * exceeds the scratch returns ESM_ERR_WORKSPACE before any launch (at hidden
+ * 1280 / FFN 5120 that is about 2,300 rows).  Every call on one device shares
+ * that device's scratch: calls whose stream work overlaps on one device race
+ * (order them on one stream, or with events).  Nothing in the scratch needs
+ * to start at zero: every region a layer reads is written earlier in that
+ * same call. */
+#define ESM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+esm_status esm_layer_fwd_noalloc(esm_encoder* enc, const esm_layer_weights* w, int32_t layer_idx,
+                                 const void* x_in, void* x_out,
+                                 const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
+                                 int32_t B, int64_t T, int32_t max_seqlen, esm_stream_t stream);
 
 /* Embedding lookup (when token_ids != NULL: X0 = E[ids], ids clamped into
  * [0, vocab)) or the given hidden states x_in, then all num_hidden_layers

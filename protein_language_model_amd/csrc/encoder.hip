@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -46,11 +47,40 @@ struct esm_encoder {
   // (a multiple of 64 GEMM columns), refilled from the caller's on each call
   bf16_t* head_w = nullptr;        // [vocab_pad, H] then [vocab_pad]
   int32_t vocab_pad = 0;
+  // this device's copy of the file-scope scratch array (esm_layer_fwd_noalloc)
+  void* scratch = nullptr;
 };
 
 namespace {
 
 thread_local std::string g_last_error;
+
+// Device scratch of esm_layer_fwd_noalloc: a file-scope array, one copy on
+// every device the library runs on, held until the process ends.  Host code
+// never passes `scratch` itself to a kernel (in host code the name is a
+// host-side stand-in, not a device address): esm_encoder_create resolves the
+// array's address on each device once, with that device current, and every
+// use goes through that pointer.
+static __device__ __align__(256) unsigned char scratch[ESM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of `scratch` on the current device `dev` (resolved on first use).
+hipError_t scratch_on_device(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 esm_status fail(esm_status s, const char* fmt, ...) {
   char buf[512];
@@ -718,9 +748,12 @@ esm_status esm_encoder_create(const esm_config* cfg, int device, esm_encoder** o
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(ESM_ERR_ARCH, "device %d is %s; this library is built for gfx950 only", device, prop.gcnArchName);
   HIP_TRY(hipSetDevice(device), "hipSetDevice");
+  void* scr = nullptr;
+  HIP_TRY(scratch_on_device(device, &scr), "device scratch address (hipGetSymbolAddress)");
   esm_encoder* e = new esm_encoder();
   e->cfg = *cfg;
   e->device = device;
+  e->scratch = scr;
   // Rotary table: theta = p * base^(-i/32), i < 32, in fp64 then rounded
   // ([TE-ESM2] 旋转位置编码集成).
   const int P = cfg->max_position_embeddings;
@@ -803,6 +836,29 @@ esm_status esm_layer_fwd(esm_encoder* e, const esm_layer_weights* w, int32_t lay
   g_last_error.clear();
   return forward_thd(e, w, 1, layer_idx, nullptr, nullptr, x_in, x_out, cu_dev, cu_host, B, T, max_seqlen, ws,
                      ws_bytes, stream);
+}
+
+esm_status esm_layer_fwd_noalloc(esm_encoder* e, const esm_layer_weights* w, int32_t layer_idx, const void* x_in,
+                                 void* x_out, const int32_t* cu_dev, const int32_t* cu_host, int32_t B, int64_t T,
+                                 int32_t max_seqlen, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  if (!e->scratch) return fail(ESM_ERR_STATE, "device scratch not resolved");
+  if (T >= 0 && B >= 0) {
+    const size_t need = make_plan(e->cfg, T, B).total;
+    if (need > (size_t)ESM_NOALLOC_SCRATCH_BYTES)
+      return fail(ESM_ERR_WORKSPACE,
+                  "T = %lld rows, B = %d sequences need %zu bytes of scratch; the allocation-free entry has %zu "
+                  "(use esm_layer_fwd with a caller workspace)",
+                  (long long)T, B, need, (size_t)ESM_NOALLOC_SCRATCH_BYTES);
+  }
+  // no timing events: recording them may create events, which allocates
+  const bool prof = e->profiling;
+  e->profiling = false;
+  const esm_status s = forward_thd(e, w, 1, layer_idx, nullptr, nullptr, x_in, x_out, cu_dev, cu_host, B, T,
+                                   max_seqlen, e->scratch, (size_t)ESM_NOALLOC_SCRATCH_BYTES, stream);
+  e->profiling = prof;
+  return s;
 }
 
 esm_status esm_stack_fwd(esm_encoder* e, const esm_layer_weights* w, const int32_t* ids, const void* emb,

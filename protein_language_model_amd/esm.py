@@ -73,6 +73,8 @@ SIGNATURES = {
     "esm_workspace_region": (_i32, [_p, _i64, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     "esm_layer_fwd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _i32, _p, _p, _p, _p, _i32, _i64, _i32, _p, _sz,
                              _p]),
+    "esm_layer_fwd_noalloc": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _i32, _p, _p, _p, _p, _i32, _i64, _i32,
+                                     _p]),
     "esm_head_fwd": (_i32, [_p, ctypes.POINTER(EsmHeadWeights), _p, _p, _p, _p, _p, _p, _i32, _i64, _i32, _p, _sz,
                             _p]),
     "esm_stack_fwd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _p, _p, _p, _p, _p, _p, _i32, _i64, _i32, _p, _sz,
@@ -272,6 +274,16 @@ class Encoder:
         _call("esm_layer_fwd", self._h, ctypes.byref(w), int(layer_idx), _ptr(x_in), _ptr(x_out), _ptr(cu_seqlens),
               cuh.ctypes.data_as(ctypes.c_void_p) if cuh is not None else None, int(B), int(T), int(max_seqlen),
               _ptr(workspace), workspace.numel(), _stream(stream))
+        return x_out
+
+    def layer_fwd_noalloc(self, weights, x_in, cu_seqlens, B: int, T: int, max_seqlen: int, *, x_out,
+                          layer_idx: int = 0, cu_seqlens_host=None, stream=None):
+        """esm_layer_fwd_noalloc: the caller passes the output; no workspace."""
+        w = layer_weights_struct(weights)
+        cuh = _host_i32(cu_seqlens_host)
+        _call("esm_layer_fwd_noalloc", self._h, ctypes.byref(w), int(layer_idx), _ptr(x_in), _ptr(x_out),
+              _ptr(cu_seqlens), cuh.ctypes.data_as(ctypes.c_void_p) if cuh is not None else None, int(B), int(T),
+              int(max_seqlen), _stream(stream))
         return x_out
 
     def stack_fwd(self, weights: Sequence[Dict], cu_seqlens, B: int, T: int, max_seqlen: int, *, token_ids=None,

@@ -1,0 +1,65 @@
+"""The allocation-free layer entry (esm_layer_fwd_noalloc) through the C ABI:
+bit-equal to esm_layer_fwd with a caller workspace, on two calls in a row
+(the second with a smaller batch, so stale scratch contents from the first
+call would show), at the tiny and the 650M widths; batches whose workspace
+exceeds the scratch are rejected before any launch."""
+import numpy as np
+import pytest
+import torch
+
+from protein_language_model_amd import datagen as D
+from protein_language_model_amd import esm
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gu():
+    import gpu_util
+    return gpu_util
+
+
+def _two_calls(gu, m, batches, layer_seed):
+    enc = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn,
+                      num_hidden_layers=1)
+    wd, _, _ = gu.layer_weights(m.hidden, m.ffn, layer_seed)
+    for lengths in batches:
+        lengths = np.asarray(lengths, np.int32)
+        cu = D.cu_from_lengths(lengths)
+        T, B, S = int(cu[-1]), len(lengths), int(lengths.max())
+        x = gu.to_dev_bf16(D.make_hidden(T, m.hidden, seed=T))
+        cu_d = gu.to_dev_i32(cu)
+        ref = enc.layer_fwd(wd, x, cu_d, B, T, S, cu_seqlens_host=cu)
+        out = torch.full_like(x, float("nan"))
+        enc.layer_fwd_noalloc(wd, x, cu_d, B, T, S, x_out=out, cu_seqlens_host=cu)
+        assert np.array_equal(gu.bits_of(out), gu.bits_of(ref)), (m.hidden, list(lengths))
+    enc.close()
+
+
+def test_noalloc_tiny_two_calls_second_smaller(gu):
+    m = D.WORKLOADS["tiny"].model
+    _two_calls(gu, m, [[17, 64, 100, 200, 0, 300], [5, 1, 40]], 0)
+
+
+def test_noalloc_650m_width_two_calls_second_smaller(gu):
+    m = D.WORKLOADS["650m_layer"].model
+    b = D.make_batch(D.WORKLOADS["650m_layer"])
+    _two_calls(gu, m, [b.lengths[:6], b.lengths[6:8]], 1)
+
+
+def test_noalloc_rejects_a_batch_beyond_the_scratch(gu):
+    m = D.WORKLOADS["650m_layer"].model
+    enc = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn,
+                      num_hidden_layers=1)
+    wd, _, _ = gu.layer_weights(m.hidden, m.ffn, 0)
+    T = 8192
+    assert enc.workspace_size(T, 8) > 64 << 20
+    x = torch.zeros((T, m.hidden), dtype=torch.bfloat16, device="cuda:0")
+    out = torch.zeros_like(x)
+    cu = D.cu_from_lengths([1024] * 8)
+    with pytest.raises(esm.EsmError) as ei:
+        enc.layer_fwd_noalloc(wd, x, gu.to_dev_i32(cu), 8, T, 1024, x_out=out, cu_seqlens_host=cu)
+    assert ei.value.status == 5   # ESM_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert not out.any()           # nothing was launched
+    enc.close()
