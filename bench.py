@@ -2,7 +2,13 @@
 
 One step = one esm_stack_fwd call: embedding lookup plus all layers of the
 650M (33-layer, bf16) encoder over one packed THD batch of ~32768 residues
-(87 sequences, lognormal lengths, seed 0), inputs already resident in HBM.
+(87 sequences, lognormal lengths, seed 0), inputs already resident in HBM;
+the LayerNorms are folded into the QKV and fc1 linears once before timing
+(esm_prepare_layer, like the FP8 weight casts).  Beside it: the same batch
+padded to bshd [87, 1024] ("padded", the packing gain), the same stack with
+the LayerNorms as separate passes ("bf16_unfolded"), the 3B-shaped 36-layer
+stack on its own packed batch ("stack_3b"), the device's achievable bf16
+MFMA rate from a register-only probe ("mfma_peak") and memory use.
 Timing follows the TransformerEngine tutorial's protocol: warm-up steps, then
 timed steps bracketed by device synchronisation, HIP events on the library
 stream; a second pass over the same steps times every kernel launch with HIP
@@ -21,7 +27,7 @@ under "layernorm_bwd".
 Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
-                    [--padded] [--no-fp8]
+                    [--no-padded] [--no-unfolded] [--no-3b] [--no-mfma-peak] [--no-fp8]
 """
 from __future__ import annotations
 
@@ -62,7 +68,11 @@ def parse():
     ap.add_argument("--workload", default="650m", choices=["650m", "3b", "650m_fp8"])
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 leg of a bf16 workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--padded", action="store_true", help="also time the padded bshd layout of the same batch")
+    ap.add_argument("--no-padded", action="store_true", help="skip the padded bshd layout of the same batch")
+    ap.add_argument("--no-unfolded", action="store_true",
+                    help="skip the bf16 stack with the LayerNorms as separate passes")
+    ap.add_argument("--no-3b", action="store_true", help="skip the 3B-shaped 36-layer stack leg")
+    ap.add_argument("--no-mfma-peak", action="store_true", help="skip the matrix-core rate probe")
     ap.add_argument("--no-kernel-timing", action="store_true")
     ap.add_argument("--no-head", action="store_true", help="skip timing the final LayerNorm / LM head / means")
     ap.add_argument("--no-linear-bwd", action="store_true",
@@ -424,6 +434,83 @@ def bench_mxfp4(enc, T: int, H: int, F: int, steps: int, dev: str, stream) -> di
     return out
 
 
+def bench_stack_leg(name: str, steps: int, warmup: int, dev: str, stream) -> dict:
+    """Another packed workload's bf16 stack (LayerNorms folded), timed the
+    same way as the main leg: warm-up steps, then HIP events around `steps`
+    steps on the library stream."""
+    import torch
+    from protein_language_model_amd import datagen as D
+    from protein_language_model_amd import esm
+    wl = D.WORKLOADS[name]
+    m = wl.model
+    b = D.make_batch(wl)
+    emb_d = torch.from_numpy(D.make_embedding(m.vocab, m.hidden).view(np.int16)).view(torch.bfloat16).to(dev)
+    wts = [D.make_layer_weights_device(m.hidden, m.ffn, l) for l in range(m.layers)]
+    enc = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn,
+                      num_hidden_layers=m.layers)
+    enc.prepare(wts, stream=stream)
+    cu = torch.from_numpy(b.cu_seqlens).to(dev)
+    ids = torch.from_numpy(b.ids).to(dev)
+    out = torch.empty((b.T, m.hidden), dtype=torch.bfloat16, device=dev)
+    ws = enc.workspace(b.T, b.B)
+
+    def step():
+        enc.stack_fwd(wts, cu, b.B, b.T, b.max_seqlen, token_ids=ids, embedding=emb_d, x_out=out, workspace=ws,
+                      stream=stream)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    sum_L2 = int((b.lengths.astype(np.int64) ** 2).sum())
+    flops = m.layers * sum(layer_flops(m.hidden, m.ffn, b.T, sum_L2).values())
+    tf = flops / (ms * 1e-3) / 1e12
+    enc.close()
+    del ws, wts, out
+    return {"workload": f"ESM-2 {m.hidden}x{m.layers} ({name}) packed THD forward, bf16",
+            "sequences": b.B, "residues": b.T, "max_seqlen": b.max_seqlen, "sum_L2": sum_L2,
+            "hidden": m.hidden, "heads": m.heads, "ffn": m.ffn, "layers": m.layers, "steps": steps,
+            "ms_per_step": round(ms, 4), "value": round(b.T / (ms * 1e-3), 1), "unit": "residues/s",
+            "tflops": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_mfma_peak(dev: str, stream) -> dict:
+    """The library's matrix-core rate probe (bf16 32x32x16 MFMAs on changing
+    register operands, nothing else in the loop), two workgroups of four
+    waves per compute unit: the achievable bf16 MFMA rate of this device under
+    load, beside the spec peak."""
+    import torch
+    from protein_language_model_amd import esm
+    enc = esm.Encoder(hidden_size=320, num_attention_heads=5, intermediate_size=1280, num_hidden_layers=1)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(16 * cus * 2, dtype=torch.float32, device=dev)
+    iters = 20000
+    for _ in range(2):
+        enc.mfma_peak(iters, sink, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    n = 5
+    e0.record(stream)
+    flops = 0.0
+    for _ in range(n):
+        flops += enc.mfma_peak(iters, sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    enc.close()
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_spec_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "ms_per_launch": round(ms / n, 4), "launches": n,
+            "what": "bf16 v_mfma_f32_32x32x16 chains on register operands that change every instruction, "
+                    "2 workgroups x 4 waves per CU, nothing else in the loop (esm_mfma_peak)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -464,11 +551,15 @@ def main():
     fl = layer_flops(m.hidden, m.ffn, T, sum_L2)
     total_flops = m.layers * sum(fl.values())
 
-    def measure(precision: str, warmup: int):
+    def measure(precision: str, warmup: int, fold: bool = True):
         """Clean timed region (the throughput), then the same steps with every
-        launch bracketed by HIP events (per-kernel durations)."""
+        launch bracketed by HIP events (per-kernel durations).  bf16: the
+        LayerNorms are folded into the QKV and fc1 linears (esm_prepare_layer,
+        once, like the FP8 and MXFP4 weight preparation) unless fold is off."""
         enc = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn,
                           num_hidden_layers=m.layers, precision=precision)
+        if precision == "bf16" and fold:
+            enc.prepare(weights, stream=stream)
         if precision == "fp8":
             enc.fp8_prepare(weights, stream=stream)
         if precision == "mxfp4":
@@ -594,7 +685,7 @@ def main():
         mxfp4 = bench_mxfp4(enc, T, m.hidden, m.ffn, args.steps, dev, stream)
 
     padded = None
-    if args.padded:
+    if not args.no_padded:
         S = 1024
         sl = torch.from_numpy(batch.lengths).to(dev)
         ids_p = np.zeros((B, S), np.int32)
@@ -615,10 +706,37 @@ def main():
         torch.cuda.synchronize()
         ms_p = e0.elapsed_time(e1) / n_p
         padded = {"layout": f"bshd [{B}, {S}]", "ms_per_step": round(ms_p, 3), "steps": n_p,
-                  "valid_fraction": round(T / (B * S), 4), "packing_gain": round(ms_p / ms, 3)}
+                  "valid_fraction": round(T / (B * S), 4), "packing_gain": round(ms_p / ms, 3),
+                  "what": "the same sequences right-padded to S = 1024 (esm_stack_fwd_bshd, every GEMM over all "
+                          "B * S rows, attention skipping padded keys); packing_gain = padded / packed step time"}
         del ws_p, out_p
     enc.close()
     del ws
+    peak_mem = {"torch_max_allocated_bytes": int(torch.cuda.max_memory_allocated()),
+                "device_used_bytes": int(torch.cuda.mem_get_info()[1] - torch.cuda.mem_get_info()[0]),
+                "what": "torch allocator high-water mark of the run so far (weights, batch, workspaces: the bf16 "
+                        "and padded legs) and device memory in use after them (adds the library's own "
+                        "allocations: folded weights, RoPE table)"}
+
+    unfolded = None
+    if not fp8_main and not args.no_unfolded:
+        encu, wsu, msu, profu, _ = measure("bf16", args.warmup, fold=False)
+        unfolded = {"ms_per_step": round(msu, 4), "value": round(T / (msu * 1e-3), 1),
+                    "fold_gain": round(msu / ms, 4),
+                    "what": "the same bf16 stack without esm_prepare_layer: both LayerNorms as separate passes "
+                            "writing their bf16 output, plain bias epilogues"}
+        if profu:
+            unfolded["kernels"] = kernel_table(profu)
+        encu.close()
+        del wsu
+
+    stack_3b = None
+    if args.workload == "650m" and not args.no_3b:
+        stack_3b = bench_stack_leg("3b", args.steps, args.warmup, dev, stream)
+
+    mfma_peak = None
+    if not args.no_mfma_peak:
+        mfma_peak = bench_mfma_peak(dev, stream)
 
     fp8 = None
     if not fp8_main and not args.no_fp8 and m.hidden % 128 == 0 and m.ffn % 128 == 0:
@@ -680,7 +798,12 @@ def main():
         "kernels": kernels,
         "step_ms": step_stats,
         "ms_per_step_with_kernel_events": round(ms_instrumented, 4) if ms_instrumented else None,
+        "frac_measured_mfma_peak": round(tflops / mfma_peak["tflops"], 4) if mfma_peak else None,
+        "mfma_peak": mfma_peak,
+        "peak_memory": peak_mem,
         "padded": padded,
+        "bf16_unfolded": unfolded,
+        "stack_3b": stack_3b,
         "head": head,
         "biased_attention": biased,
         "mxfp4": mxfp4,

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 15
+#define ESM_ABI_VERSION 16
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -144,7 +144,10 @@ typedef enum {
   ESM_WS_POS = 6,   /* int32 [T]    position of each row in its sequence, -1 = padding */
   ESM_WS_TILES = 7, /* int32 [n, 2] attention query tiles (sequence, first row) */
   ESM_WS_NTILES = 8,/* int32 [1]    number of valid tiles */
-  ESM_WS_SEGS = 9   /* int32 [B, 2] (first row, length) of every sequence */
+  ESM_WS_SEGS = 9,  /* int32 [B, 2] (first row, length) of every sequence */
+  ESM_WS_STATS = 10 /* float2 [ceil(H / 256), T] LayerNorm statistics of a layer's input rows in
+                     * 256-column chunks (mean, sum of squared deviations), used by the layers
+                     * prepared with esm_prepare_layer */
 } esm_ws_region;
 
 /* Byte offset and size of one region inside a workspace sized for
@@ -542,6 +545,25 @@ typedef struct {
   uint32_t nonfinite;    /* sticky flag */
 } esm_fp8_state;
 
+/* bf16 encoders: folds layer layer_idx's two LayerNorms into the linears that
+ * consume them ([TE-RU] LayerNormLinear / LayerNormMLP; [BIO-ACC] 2.1, the
+ * LayerNorm fused with the projection).  With h = (x - mu) r gamma + beta,
+ * r = 1 / sqrt(var + eps), a linear of h is
+ *   h W^T + b = r (x W'^T) - r mu c + d,  W' = gamma (.) W (per input column),
+ *   c_n = sum_k W'_nk,  d_n = b_n + sum_k beta_k W_nk,
+ * so the QKV and fc1 GEMMs read the raw residual stream and apply each row's
+ * (mu, r) and the columns' (c, d) in their epilogue, and no LayerNorm output
+ * is written.  This call computes, on the device into library-owned memory,
+ * W'_qkv and W'_fc1 (bf16, the fp32 product gamma_k W_nk rounded once) and
+ * (c, d) of both (fp32 from fp64 sums).  Afterwards layer layer_idx's forward
+ * takes w_qkv, b_qkv, w_fc1, b_fc1 and the four LayerNorm vectors from this
+ * copy (the pointers in w are still checked); call again whenever any of
+ * them changes.  Layers never prepared run LayerNorm as a separate pass.
+ * Enqueued on stream.  ESM_ERR_STATE for an FP8 or MXFP4 encoder (their
+ * LayerNorms write the quantised GEMM input). */
+esm_status esm_prepare_layer(esm_encoder* enc, int32_t layer_idx, const esm_layer_weights* w,
+                             esm_stream_t stream);
+
 /* Casts layer layer_idx's four linear weights (bf16 in w) to E4M3 copies owned
  * by the library, each with scale 448 / amax(W) computed on the device.
  * Enqueued on stream; call again whenever the weights change.
@@ -599,6 +621,16 @@ typedef enum {
   ESM_K_LINEAR_BWD = 13 /* esm_linear_bwd, esm_layernorm_bwd, esm_gelu_bwd, esm_qkv_rope_bwd */,
   ESM_K_COUNT = 14
 } esm_kernel_class;
+
+/* Matrix-core rate probe, for measuring the achievable bf16 MFMA rate of the
+ * device beside the spec peak: two workgroups of four waves per compute unit,
+ * each wave issuing 16 * iters v_mfma_f32_32x32x16_bf16 on register operands
+ * that change every instruction (pseudo-random bf16 in [-2, 2)), nothing
+ * else in the loop.  *flops receives the flop count of the launch (time it
+ * with events on stream).  sink: device buffer of at least
+ * 16 * (compute units) * 2 floats; ESM_ERR_WORKSPACE if smaller. */
+esm_status esm_mfma_peak(esm_encoder* enc, int32_t iters, void* sink, size_t sink_bytes, double* flops,
+                         esm_stream_t stream);
 
 /* When on, every launch is bracketed by HIP events recorded on the launch
  * stream, and durations are summed per kernel class.  Turning it on clears the

@@ -154,6 +154,89 @@ __device__ __forceinline__ void record_amax_block(uint32_t* amax, float m, float
   }
 }
 
+// ---------------------------------------------------------------------------
+// LayerNorm row statistics in pieces ([TE-RU] LayerNormLinear / LayerNormMLP:
+// the LayerNorm belongs to the linear that consumes it).  A row of H values is
+// cut into 256-column chunks (the GEMM's column tile); a chunk's partial
+// (count, mean, sum of squared deviations M2) is built by one fixed tree:
+//   * 8 leaves of 32 values, leaf (w, h) holding the columns
+//     64 w + 32 j + 8 g + 4 h + e (j < 2, g < 4, e < 4) in that order -- the
+//     values one MFMA lane holds for one row in the GEMM epilogue;
+//   * leaves (w, 0) and (w, 1) combined, then waves ((0, 1), (2, 3)).
+// The GEMM epilogue that writes a residual stream and the standalone
+// statistics kernel both evaluate this tree with these functions, so they give
+// identical bits for identical rows.  Partials are combined by Chan et al.'s
+// pairwise update (mean and M2, no cancellation of large sums of squares).
+// Contraction is off so that every product and sum is the same IEEE
+// operation wherever the functions are inlined.
+struct LnPart {
+  float n, m, M2;
+};
+
+__device__ __forceinline__ LnPart ln_leaf(const float (&v)[32]) {
+#pragma clang fp contract(off)
+  float s = v[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) s = s + v[i];
+  const float m = s * 0.03125f;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float d = v[i] - m;
+    q = fmaf(d, d, q);
+  }
+  return LnPart{32.f, m, q};
+}
+
+// Combine partial a (columns first) with partial b; an empty side (n = 0) is
+// the identity.  Equal counts (every combine inside a chunk) take the weight
+// 1/2 without a division; it is the value the division gives.
+__device__ __forceinline__ LnPart ln_combine(LnPart a, LnPart b) {
+#pragma clang fp contract(off)
+  if (b.n == 0.f) return a;
+  if (a.n == 0.f) return b;
+  const float n = a.n + b.n;
+  const float d = b.m - a.m;
+  const float wb = a.n == b.n ? 0.5f : b.n / n;
+  const float m = a.m + d * wb;
+  const float M2 = (a.M2 + b.M2) + (d * d) * (a.n * wb);
+  return LnPart{n, m, M2};
+}
+
+// Mean and 1 / sqrt(var + eps) of a row of H <= 4096 values from its chunk
+// partials part[c * ld] = (mean, M2), c < ceil(H / 256), chunk c holding
+// n_c = min(256, H - 256 c) columns:
+//   mean = sum_c n_c mean_c / H,   M2 = sum_c (M2_c + n_c (mean_c - mean)^2).
+// All loads are issued before the first use.
+__device__ __forceinline__ float2 ln_row_stats(const float2* part, int64_t ld, int H, float eps) {
+  constexpr int kMaxChunks = 16;
+  const int chunks = (H + 255) / 256;
+  float2 p[kMaxChunks];
+  // chunks past the last re-read the last one (no branch around the loads)
+  // and are then zeroed: count 0 and M2 0, so they add nothing below
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) p[c] = part[(int64_t)(c < chunks ? c : chunks - 1) * ld];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+    if (c >= chunks) p[c] = make_float2(0.f, 0.f);
+  const float invH = 1.0f / (float)H;
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int w = H - 256 * c;
+    s = fmaf((float)(w < 0 ? 0 : (w < 256 ? w : 256)), p[c].x, s);
+  }
+  const float mean = s * invH;
+  float M2 = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int w = H - 256 * c;
+    const float d = p[c].x - mean;
+    M2 = M2 + fmaf((float)(w < 0 ? 0 : (w < 256 ? w : 256)) * d, d, p[c].y);
+  }
+  return make_float2(mean, 1.0f / sqrtf(M2 * invH + eps));
+}
+
 // Launch context handed from the host library to each launcher.
 struct Launch {
   hipStream_t stream;
@@ -178,6 +261,14 @@ hipError_t launch_segment_table(int layout, const int32_t* lens, int32_t B, int6
 
 hipError_t launch_embed(const int32_t* ids, const bf16_t* table, int32_t vocab, bf16_t* x,
                         int64_t T, int32_t H, hipStream_t st);
+// LayerNorm chunk partials [ceil(H / 256)][T] of the rows of x [T, H]; with
+// ids != nullptr the rows are first gathered from table (x = E[ids], written).
+hipError_t launch_row_stats(const int32_t* ids, const bf16_t* table, int32_t vocab, bf16_t* x, int64_t T, int32_t H,
+                            float2* stats, hipStream_t st);
+// Folded LayerNorm weight of a linear: wf [N, K] = bf16(gamma_k w_nk),
+// cd[n] = (sum_k wf_nk, b_n + sum_k beta_k w_nk); bias may be null.
+hipError_t launch_fold_weight(const bf16_t* w, const bf16_t* gamma, const bf16_t* beta, const bf16_t* bias,
+                              int32_t N, int32_t K, bf16_t* wf, float2* cd, hipStream_t st);
 
 // E4M3 output of a producer kernel: y = cast(v * scale[0]), amax of v
 // recorded into *amax.  y == nullptr selects the bf16 output instead.
@@ -200,8 +291,17 @@ hipError_t launch_layernorm(const bf16_t* x, const bf16_t* gamma, const bf16_t* 
 hipError_t launch_layernorm_mx(const bf16_t* x, const bf16_t* gamma, const bf16_t* beta, uint8_t* codes,
                                uint8_t* scales, int64_t M, int32_t H, float eps, hipStream_t st);
 
+// EPI_QKV_ROPE_LN / EPI_BIAS_GELU_LN: the rotary / GELU epilogues of a linear
+// whose input is LayerNorm(x) with the LayerNorm folded away: x (the raw
+// residual stream) is the GEMM operand, the weight is the prepared
+// W' = gamma (.) W, and output column n is
+//   r (x . W'_n) - r mu c_n + d_n,   c_n = sum_k W'_nk,  d_n = b_n + sum_k beta_k W_nk,
+// with (mu, r = 1 / sqrt(var + eps)) of each row from ln_stats.
+// EPI_RES_STATS: the residual epilogue that also writes the chunk partials of
+// the LayerNorm statistics of its output rows (stats_out).
 enum GemmEpi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_QKV_ROPE = 3, EPI_BIAS_GELU_E4M3 = 4,
-               EPI_BIAS_GELU_MX = 5, EPI_F32_SPLIT = 6 };
+               EPI_BIAS_GELU_MX = 5, EPI_F32_SPLIT = 6, EPI_QKV_ROPE_LN = 7, EPI_BIAS_GELU_LN = 8,
+               EPI_RES_STATS = 9 };
 
 struct GemmArgs {
   int32_t dtype;       // kBF16 or kE4M3 operands
@@ -236,9 +336,20 @@ struct GemmArgs {
   // EPI_BIAS_GELU_MX: y8 = MXFP4 codes [M, N / 2] of gelu(.), y_sc their
   // block scales (the same layout, K = N)
   uint8_t* y_sc;
+  // folded LayerNorm (EPI_*_LN): chunk partials [ceil(K / 256)][M] of the x
+  // rows, eps, and (c_n, d_n) per output column [N]
+  const float2* ln_stats;
+  float ln_eps;
+  const float2* ln_cd;
+  // EPI_RES_STATS: chunk partials [ceil(N / 256)][M] of the output rows
+  float2* stats_out;
 };
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st);
+// Matrix-core rate probe (k_mfma_peak): `blocks` workgroups of four waves,
+// each wave 16 * iters v_mfma_f32_32x32x16_bf16; sink [4 * blocks] floats.
+hipError_t launch_mfma_peak(int32_t iters, int32_t blocks, float* sink, hipStream_t st);
+int32_t mfma_peak_blocks();  // two workgroups per compute unit of the current device
 
 struct AttnArgs {
   const bf16_t* qkv;      // [3, heads, T, 64]

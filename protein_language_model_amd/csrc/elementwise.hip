@@ -125,6 +125,92 @@ __global__ void k_embed(const int32_t* __restrict__ ids, const bf16_t* __restric
   *(u32x4*)(x + t * H + c * 8) = *(const u32x4*)(table + (int64_t)id * H + c * 8);
 }
 
+// LayerNorm chunk partials of rows of x (optionally gathered first from the
+// embedding, X0 = E[ids]): one thread per (row, 256-column chunk, leaf), the
+// leaf's 32 values and the tree of ln_leaf / ln_combine exactly as the GEMM
+// epilogue that writes a residual stream evaluates them, so a row gives the
+// same partials whichever of the two produced them.  Eight consecutive lanes
+// hold one (row, chunk): lane bit 0 = h, bits 1..2 = w.
+__global__ __launch_bounds__(256) void k_row_stats(const int32_t* __restrict__ ids, const bf16_t* __restrict__ table,
+                                                   int32_t vocab, bf16_t* __restrict__ x, int64_t T, int32_t H,
+                                                   float2* __restrict__ stats) {
+  const int chunks = (H + 255) / 256;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int leaf = (int)(g & 7);
+  const int64_t rc = g >> 3;                 // (row, chunk), chunk fastest
+  const bool live = rc < T * chunks;
+  const int64_t t = live ? rc / chunks : 0;
+  const int c = live ? (int)(rc % chunks) : 0;
+  const int w = leaf >> 1, h = leaf & 1;
+  const int c0 = 256 * c;
+  const int cw = H - c0 < 256 ? H - c0 : 256;
+  const bool valid = live && 64 * w < cw;
+  LnPart p{0.f, 0.f, 0.f};
+  if (valid) {
+    const bf16_t* src = x + t * H;
+    if (ids) {
+      int id = ids[t];
+      id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+      src = table + (int64_t)id * H;
+    }
+    float v[32];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = c0 + 64 * w + 32 * j + 8 * q + 4 * h;
+        const u32x2 u = *(const u32x2*)(src + col);
+        if (ids) *(u32x2*)(x + t * H + col) = u;
+        v[16 * j + 4 * q + 0] = bflo(u[0]);
+        v[16 * j + 4 * q + 1] = bfhi(u[0]);
+        v[16 * j + 4 * q + 2] = bflo(u[1]);
+        v[16 * j + 4 * q + 3] = bfhi(u[1]);
+      }
+    p = ln_leaf(v);
+  }
+  // (w, 0) with (w, 1); then waves (0, 1) and (2, 3); then the two pairs.
+  // Each pair of lanes computes combine(lower, upper) identically.
+#pragma unroll
+  for (int off = 1; off <= 4; off <<= 1) {
+    LnPart o{__shfl_xor(p.n, off), __shfl_xor(p.m, off), __shfl_xor(p.M2, off)};
+    p = (leaf & off) ? ln_combine(o, p) : ln_combine(p, o);
+  }
+  if (live && leaf == 0) stats[(int64_t)c * T + t] = make_float2(p.m, p.M2);
+}
+
+// Folded LayerNorm weight of one output row n per workgroup:
+// wf[n, k] = bf16(gamma_k w[n, k]) (the product of two bf16 values is exact
+// in fp32, then one rounding), c_n = sum_k wf[n, k] and
+// d_n = b_n + sum_k beta_k w[n, k], summed in fp64 over a fixed tree.
+__global__ __launch_bounds__(256) void k_fold_weight(const bf16_t* __restrict__ w, const bf16_t* __restrict__ gamma,
+                                                     const bf16_t* __restrict__ beta, const bf16_t* __restrict__ bias,
+                                                     int32_t K, bf16_t* __restrict__ wf, float2* __restrict__ cd) {
+  const int64_t n = blockIdx.x;
+  double sc = 0.0, sd = 0.0;
+  for (int k = threadIdx.x; k < K; k += 256) {
+    const float wv = bf2f(w[n * K + k]);
+    const bf16_t f = f2bf(bf2f(gamma[k]) * wv);
+    wf[n * K + k] = f;
+    sc += (double)bf2f(f);
+    sd += (double)bf2f(beta[k]) * (double)wv;
+  }
+  __shared__ double rc[256], rd[256];
+  rc[threadIdx.x] = sc;
+  rd[threadIdx.x] = sd;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) {
+      rc[threadIdx.x] += rc[threadIdx.x + off];
+      rd[threadIdx.x] += rd[threadIdx.x + off];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double b = bias ? (double)bf2f(bias[n]) : 0.0;
+    cd[n] = make_float2((float)rc[0], (float)(rd[0] + b));
+  }
+}
+
 // Rows per wave: two for rows of up to 2560 values (all of a wave's rows are
 // loaded before the first is reduced, so their memory latencies overlap:
 // 33 -> 30 us per 650M LayerNorm), and for the E4M3 output fewer workgroups
@@ -352,6 +438,23 @@ hipError_t launch_embed(const int32_t* ids, const bf16_t* table, int32_t vocab, 
   const int64_t n = T * (H / 8);
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_embed, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ids, table, vocab, x, T, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_stats(const int32_t* ids, const bf16_t* table, int32_t vocab, bf16_t* x, int64_t T, int32_t H,
+                            float2* stats, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (H % 64) return hipErrorInvalidValue;
+  const int64_t threads = T * ((H + 255) / 256) * 8;
+  hipLaunchKernelGGL(k_row_stats, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, ids, table, vocab, x, T,
+                     H, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_weight(const bf16_t* w, const bf16_t* gamma, const bf16_t* beta, const bf16_t* bias,
+                              int32_t N, int32_t K, bf16_t* wf, float2* cd, hipStream_t st) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fold_weight, dim3((unsigned)N), dim3(256), 0, st, w, gamma, beta, bias, K, wf, cd);
   return hipGetLastError();
 }
 

@@ -49,6 +49,11 @@ struct esm_encoder {
   int32_t vocab_pad = 0;
   // this device's copy of the file-scope scratch array (esm_layer_fwd_noalloc)
   void* scratch = nullptr;
+  // bf16 precision: LayerNorms folded into the QKV and fc1 linears
+  // (esm_prepare_layer): per layer W'_qkv | W'_fc1 | (c, d) of qkv | of fc1
+  unsigned char* fold = nullptr;
+  size_t fold_layer = 0;
+  std::vector<char> folded;
 };
 
 namespace {
@@ -147,9 +152,11 @@ esm_status check_config(const esm_config* c) {
 
 // ---------------------------------------------------------------- workspace plan
 
+constexpr int kRegions = ESM_WS_STATS + 1;
+
 struct Plan {
-  size_t off[10];
-  size_t size[10];
+  size_t off[kRegions];
+  size_t size[kRegions];
   size_t total;
 };
 
@@ -161,7 +168,7 @@ Plan make_plan(const esm_config& c, int64_t T, int32_t B) {
   Plan p;
   const size_t H = (size_t)c.hidden_size, F = (size_t)c.intermediate_size;
   const size_t t = (size_t)(T > 0 ? T : 0), b = (size_t)(B > 0 ? B : 0);
-  size_t sizes[10];
+  size_t sizes[kRegions];
   sizes[ESM_WS_LN1] = t * H * 2;
   sizes[ESM_WS_QKV] = 3 * t * H * 2;
   sizes[ESM_WS_CTX] = t * H * 2;
@@ -172,8 +179,9 @@ Plan make_plan(const esm_config& c, int64_t T, int32_t B) {
   sizes[ESM_WS_TILES] = (size_t)tile_cap((int64_t)t, (int32_t)b) * 8;
   sizes[ESM_WS_NTILES] = 4;
   sizes[ESM_WS_SEGS] = b * 8;
+  sizes[ESM_WS_STATS] = (H + 255) / 256 * t * 8;
   size_t o = 0;
-  for (int i = 0; i < 10; ++i) {
+  for (int i = 0; i < kRegions; ++i) {
     p.off[i] = o;
     p.size[i] = sizes[i];
     o += align256(sizes[i]);
@@ -382,6 +390,26 @@ esm_status check_fp8_layer(const esm_encoder* e, int32_t l) {
   return ok();
 }
 
+// Folded LayerNorm weights of one layer: W'_qkv [3H, H], W'_fc1 [F, H]
+// (bf16), then (c, d) [3H] and [F] (float2).
+struct FoldOff {
+  size_t wqkv, wfc1, cdqkv, cdfc1, total;
+};
+FoldOff fold_offsets(const esm_config& c) {
+  const size_t H = (size_t)c.hidden_size, F = (size_t)c.intermediate_size;
+  FoldOff f;
+  f.wqkv = 0;
+  f.wfc1 = align256(3 * H * H * 2);
+  f.cdqkv = f.wfc1 + align256(F * H * 2);
+  f.cdfc1 = f.cdqkv + align256(3 * H * 8);
+  f.total = f.cdfc1 + align256(F * 8);
+  return f;
+}
+
+bool layer_folded(const esm_encoder* e, int32_t l) {
+  return e->cfg.precision == ESM_PRECISION_BF16 && l >= 0 && (size_t)l < e->folded.size() && e->folded[(size_t)l];
+}
+
 // ---------------------------------------------------------------- launch sequence
 
 esm_status run_segments(esm_encoder* e, int layout, const int32_t* lens, int32_t B, int64_t rows, int32_t S,
@@ -500,12 +528,90 @@ esm_status run_layer_mx(esm_encoder* e, const esm_layer_weights* w, int32_t li, 
   return timed(e, ESM_K_GEMM_FC2, st, "fc2 gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
 }
 
+// One bf16 pre-LN layer with both LayerNorms folded into the linears that
+// consume them ([TE-RU] LayerNormLinear / LayerNormMLP; [BIO-ACC] 2.1: the
+// LayerNorm, the projection and the activation in one kernel): the QKV and
+// fc1 GEMMs read the raw residual stream and layer li's prepared W' = gamma (.) W
+// and apply each row's (mean, 1/sqrt(var + eps)) and the columns' (c, d) in
+// their epilogue; the row statistics come as 256-column chunk partials,
+// written by the epilogue of the GEMM that produced the residual stream (the
+// out-projection for LN2, the previous layer's fc2 for LN1) or, for the first
+// layer of a call, by a statistics pass.  *stats_valid says whether the
+// statistics region holds the partials of x_in; on return it holds those of
+// x_out.
+esm_status run_layer_folded(esm_encoder* e, const esm_layer_weights* w, int32_t li, const bf16_t* x_in,
+                            bf16_t* x_out, int64_t rows, int32_t B, bool zero_pad_rows, void* ws, const Plan& p,
+                            bool* stats_valid, hipStream_t st) {
+  const esm_config& c = e->cfg;
+  const int H = c.hidden_size, F = c.intermediate_size, heads = c.num_attention_heads;
+  bf16_t* qkv = region<bf16_t>(ws, p, ESM_WS_QKV);
+  bf16_t* ctx = region<bf16_t>(ws, p, ESM_WS_CTX);
+  bf16_t* x1 = region<bf16_t>(ws, p, ESM_WS_X1);
+  bf16_t* act = region<bf16_t>(ws, p, ESM_WS_ACT);
+  float2* stats = region<float2>(ws, p, ESM_WS_STATS);
+  const int32_t* pos = region<int32_t>(ws, p, ESM_WS_POS);
+  const FoldOff fo = fold_offsets(c);
+  const unsigned char* fl = e->fold + (size_t)li * e->fold_layer;
+  esm_status s;
+  if (!*stats_valid) {
+    s = timed(e, ESM_K_LAYERNORM, st, "layernorm statistics", [&] {
+      return launch_row_stats(nullptr, nullptr, 0, (bf16_t*)x_in, rows, H, stats, st);
+    });
+    if (s) return s;
+    *stats_valid = true;
+  }
+  GemmArgs g{};
+  g.dtype = kBF16;
+  g.M = rows;
+  g.pos = pos;
+  g.rope = e->rope;
+  g.max_positions = c.max_position_embeddings;
+  g.zero_pad_rows = zero_pad_rows ? 1 : 0;
+  g.ln_eps = c.layer_norm_eps;
+
+  g.x = x_in; g.w = fl + fo.wqkv; g.ln_stats = stats; g.ln_cd = (const float2*)(fl + fo.cdqkv);
+  g.y = qkv; g.N = 3 * H; g.K = H;
+  s = timed(e, ESM_K_GEMM_QKV, st, "qkv gemm", [&] { return launch_gemm(EPI_QKV_ROPE_LN, g, st); });
+  if (s) return s;
+
+  AttnArgs aa{};
+  aa.qkv = qkv; aa.ctx = ctx;
+  aa.ctx8 = E4m3Out{nullptr, nullptr, nullptr, nullptr};
+  aa.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
+  aa.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
+  aa.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
+  aa.tile_cap = tile_cap(rows, B);
+  aa.T = rows; aa.heads = heads;
+  s = timed(e, ESM_K_ATTENTION, st, "attention", [&] { return launch_attention(aa, st); });
+  if (s) return s;
+
+  g.x = ctx; g.w = w->w_out; g.ln_stats = nullptr; g.ln_cd = nullptr;
+  g.bias = (const bf16_t*)w->b_out; g.res = x_in; g.y = x1; g.stats_out = stats;
+  g.N = H; g.K = H;
+  s = timed(e, ESM_K_GEMM_OUT, st, "out-proj gemm", [&] { return launch_gemm(EPI_RES_STATS, g, st); });
+  if (s) return s;
+
+  g.x = x1; g.w = fl + fo.wfc1; g.ln_stats = stats; g.ln_cd = (const float2*)(fl + fo.cdfc1);
+  g.bias = nullptr; g.res = nullptr; g.y = act; g.stats_out = nullptr;
+  g.N = F; g.K = H;
+  s = timed(e, ESM_K_GEMM_FC1, st, "fc1 gemm", [&] { return launch_gemm(EPI_BIAS_GELU_LN, g, st); });
+  if (s) return s;
+
+  g.x = act; g.w = w->w_fc2; g.ln_stats = nullptr; g.ln_cd = nullptr;
+  g.bias = (const bf16_t*)w->b_fc2; g.res = x1; g.y = x_out; g.stats_out = stats;
+  g.N = H; g.K = F;
+  return timed(e, ESM_K_GEMM_FC2, st, "fc2 gemm", [&] { return launch_gemm(EPI_RES_STATS, g, st); });
+}
+
 // One pre-LN layer on rows already described by the segment table in ws.
 // FP8: the four GEMM inputs are produced in E4M3 by their producers (LN1, the
 // attention epilogue, LN2, the fc1 epilogue) with layer li's delayed scales,
 // and the GEMMs read layer li's E4M3 weights.
 esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, int32_t li, const bf16_t* x_in, bf16_t* x_out,
-                     int64_t rows, int32_t B, bool zero_pad_rows, void* ws, const Plan& p, hipStream_t st) {
+                     int64_t rows, int32_t B, bool zero_pad_rows, void* ws, const Plan& p, bool* stats_valid,
+                     hipStream_t st) {
+  if (layer_folded(e, li)) return run_layer_folded(e, w, li, x_in, x_out, rows, B, zero_pad_rows, ws, p, stats_valid, st);
+  *stats_valid = false;
   const esm_config& c = e->cfg;
   const int H = c.hidden_size, F = c.intermediate_size, heads = c.num_attention_heads;
   bf16_t* ln1 = region<bf16_t>(ws, p, ESM_WS_LN1);
@@ -648,15 +754,23 @@ esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, 
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
   if ((s = run_segments(e, 0, cu_dev, B, T, 0, ws, p, st))) return s;
   const bf16_t* cur = (const bf16_t*)x_in;
+  bool stats_valid = false;
   if (ids) {
+    // a folded first layer takes its LayerNorm statistics from the gather
+    const bool fold0 = nlayers > 0 && layer_folded(e, layer_idx >= 0 ? layer_idx : 0);
     s = timed(e, ESM_K_EMBED, st, "embedding", [&] {
-      return launch_embed(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, T, e->cfg.hidden_size, st);
+      return fold0 ? launch_row_stats(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, T,
+                                      e->cfg.hidden_size, region<float2>(ws, p, ESM_WS_STATS), st)
+                   : launch_embed(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, T,
+                                  e->cfg.hidden_size, st);
     });
     if (s) return s;
+    stats_valid = fold0;
     cur = (const bf16_t*)x_out;
   }
   for (int l = 0; l < nlayers; ++l) {
-    if ((s = run_layer(e, &w[l], layer_idx >= 0 ? layer_idx : l, cur, (bf16_t*)x_out, T, B, false, ws, p, st)))
+    if ((s = run_layer(e, &w[l], layer_idx >= 0 ? layer_idx : l, cur, (bf16_t*)x_out, T, B, false, ws, p,
+                       &stats_valid, st)))
       return s;
     cur = (const bf16_t*)x_out;
   }
@@ -699,15 +813,23 @@ esm_status forward_bshd(esm_encoder* e, const esm_layer_weights* w, int nlayers,
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
   if ((s = run_segments(e, 1, sl_dev, B, rows, S, ws, p, st))) return s;
   const bf16_t* cur = (const bf16_t*)x_in;
+  bool stats_valid = false;
   if (ids) {
+    // a folded first layer takes its LayerNorm statistics from the gather
+    const bool fold0 = nlayers > 0 && layer_folded(e, layer_idx >= 0 ? layer_idx : 0);
     s = timed(e, ESM_K_EMBED, st, "embedding", [&] {
-      return launch_embed(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, rows, e->cfg.hidden_size, st);
+      return fold0 ? launch_row_stats(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, rows,
+                                      e->cfg.hidden_size, region<float2>(ws, p, ESM_WS_STATS), st)
+                   : launch_embed(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, rows,
+                                  e->cfg.hidden_size, st);
     });
     if (s) return s;
+    stats_valid = fold0;
     cur = (const bf16_t*)x_out;
   }
   for (int l = 0; l < nlayers; ++l) {
-    if ((s = run_layer(e, &w[l], layer_idx >= 0 ? layer_idx : l, cur, (bf16_t*)x_out, rows, B, true, ws, p, st)))
+    if ((s = run_layer(e, &w[l], layer_idx >= 0 ? layer_idx : l, cur, (bf16_t*)x_out, rows, B, true, ws, p,
+                       &stats_valid, st)))
       return s;
     cur = (const bf16_t*)x_out;
   }
@@ -805,6 +927,7 @@ esm_status esm_encoder_destroy(esm_encoder* e) {
   if (e->w8) (void)hipFree(e->w8);
   if (e->w4) (void)hipFree(e->w4);
   if (e->head_w) (void)hipFree(e->head_w);
+  if (e->fold) (void)hipFree(e->fold);
   for (hipEvent_t ev : e->pool) (void)hipEventDestroy(ev);
   if (e->fork) (void)hipEventDestroy(e->fork);
   if (e->join) (void)hipEventDestroy(e->join);
@@ -823,7 +946,7 @@ esm_status esm_workspace_size(const esm_encoder* e, int64_t max_tokens, int32_t 
 esm_status esm_workspace_region(const esm_encoder* e, int64_t max_tokens, int32_t max_seqs, int32_t r,
                                 size_t* offset, size_t* bytes) {
   if (!e || !offset || !bytes) return fail(ESM_ERR_NULL, "NULL argument");
-  if (r < 0 || r > ESM_WS_SEGS) return fail(ESM_ERR_UNSUPPORTED, "unknown region %d", r);
+  if (r < 0 || r > ESM_WS_STATS) return fail(ESM_ERR_UNSUPPORTED, "unknown region %d", r);
   const Plan p = make_plan(e->cfg, max_tokens, max_seqs);
   *offset = p.off[r];
   *bytes = p.size[r];
@@ -1455,6 +1578,42 @@ esm_status esm_fp8_prepare_layer(esm_encoder* e, int32_t layer_idx, const esm_la
   return ok();
 }
 
+esm_status esm_prepare_layer(esm_encoder* e, int32_t layer_idx, const esm_layer_weights* w, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  if (e->cfg.precision != ESM_PRECISION_BF16)
+    return fail(ESM_ERR_STATE, "esm_prepare_layer is for bf16 encoders (FP8: esm_fp8_prepare_layer, MXFP4: "
+                               "esm_mxfp4_prepare_layer)");
+  if (layer_idx < 0 || layer_idx >= e->cfg.num_hidden_layers)
+    return fail(ESM_ERR_SHAPE, "layer_idx %d outside [0, %d)", layer_idx, e->cfg.num_hidden_layers);
+  esm_status s = check_weights(w, layer_idx);
+  if (s) return s;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  const esm_config& c = e->cfg;
+  const FoldOff fo = fold_offsets(c);
+  if (!e->fold) {
+    const size_t L = (size_t)c.num_hidden_layers;
+    e->fold_layer = align256(fo.total);
+    HIP_TRY(hipMalloc((void**)&e->fold, L * e->fold_layer), "folded LayerNorm weights");
+    e->folded.assign(L, 0);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* fl = e->fold + (size_t)layer_idx * e->fold_layer;
+  const int H = c.hidden_size, F = c.intermediate_size;
+  s = timed(e, ESM_K_OTHER, st, "fold qkv", [&] {
+    return launch_fold_weight((const bf16_t*)w->w_qkv, (const bf16_t*)w->ln1_gamma, (const bf16_t*)w->ln1_beta,
+                              (const bf16_t*)w->b_qkv, 3 * H, H, (bf16_t*)(fl + fo.wqkv), (float2*)(fl + fo.cdqkv), st);
+  });
+  if (s) return s;
+  s = timed(e, ESM_K_OTHER, st, "fold fc1", [&] {
+    return launch_fold_weight((const bf16_t*)w->w_fc1, (const bf16_t*)w->ln2_gamma, (const bf16_t*)w->ln2_beta,
+                              (const bf16_t*)w->b_fc1, F, H, (bf16_t*)(fl + fo.wfc1), (float2*)(fl + fo.cdfc1), st);
+  });
+  if (s) return s;
+  e->folded[(size_t)layer_idx] = 1;
+  return ok();
+}
+
 esm_status esm_mxfp4_prepare_layer(esm_encoder* e, int32_t layer_idx, const esm_layer_weights* w,
                                    esm_stream_t stream) {
   g_last_error.clear();
@@ -1578,6 +1737,20 @@ esm_status esm_fp8_quantize(esm_encoder* e, const float* x, int64_t n, const flo
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
   return timed(e, ESM_K_FP8, (hipStream_t)stream, "e4m3 cast",
                [&] { return launch_quantize_f32(x, n, scale, (uint8_t*)y, amax, (hipStream_t)stream); });
+}
+
+esm_status esm_mfma_peak(esm_encoder* e, int32_t iters, void* sink, size_t sink_bytes, double* flops,
+                         esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !sink || !flops) return fail(ESM_ERR_NULL, "NULL argument");
+  if (iters <= 0) return fail(ESM_ERR_SHAPE, "iters %d must be positive", iters);
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  const int32_t blocks = mfma_peak_blocks();
+  if (sink_bytes < (size_t)blocks * 4 * sizeof(float))
+    return fail(ESM_ERR_WORKSPACE, "sink of %zu bytes, %zu needed", sink_bytes, (size_t)blocks * 4 * sizeof(float));
+  *flops = (double)blocks * 4 * 16 * (double)iters * 32768.0;
+  hipStream_t st = (hipStream_t)stream;
+  return timed(e, ESM_K_OTHER, st, "mfma peak", [&] { return launch_mfma_peak(iters, blocks, (float*)sink, st); });
 }
 
 esm_status esm_profile_enable(esm_encoder* e, int32_t on) {

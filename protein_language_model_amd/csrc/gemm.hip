@@ -121,8 +121,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(XRB * RPI * NW == BM && WRB * RPI * NW == BN, "tile rows must split evenly over the waves");
   static_assert(DT != kBF16 || KK % 2 == 0, "fragment double buffering alternates over an even number of sub-steps");
-  static_assert(EPI != EPI_QKV_ROPE || (FN % 2 == 0 && WTN % 64 == 0), "rotary pairs need 64-wide wave columns");
+  constexpr bool ROPE = EPI == EPI_QKV_ROPE || EPI == EPI_QKV_ROPE_LN;
+  constexpr bool RES = EPI == EPI_BIAS_RESIDUAL || EPI == EPI_RES_STATS;
+  constexpr bool FOLD = EPI == EPI_QKV_ROPE_LN || EPI == EPI_BIAS_GELU_LN;  // LayerNorm folded into the linear
+  constexpr bool STATS = EPI == EPI_RES_STATS;                              // LayerNorm partials of the output
+  static_assert(!ROPE || (FN % 2 == 0 && WTN % 64 == 0), "rotary pairs need 64-wide wave columns");
   static_assert(EPI != EPI_BIAS_GELU_E4M3 || DT == kE4M3, "E4M3 output is built for E4M3 operands");
+  static_assert(!(FOLD || STATS) || (DT == kBF16 && BN == 256), "folded LayerNorm: bf16, 256-column tiles");
 
   // Two K-step stages; after the K loop the same memory stages the output,
   // the whole tile at once when it fits, else 32-row chunks of every wave's
@@ -136,16 +141,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   static_assert(WTM % ECH == 0, "whole chunks");
   // Residual epilogues stage the residual by direct loads one chunk ahead:
   // two staging buffers when the tile is staged in chunks.
-  constexpr int kStageBufs = (EPI == EPI_BIAS_RESIDUAL && ECH < WTM) ? 2 : 1;
+  constexpr int kStageBufs = (RES && ECH < WTM) ? 2 : 1;
   constexpr int kEpiBytes = kStageBufs * NW * ECH * ORB;
   static_assert(kEpiBytes <= 2 * kStage, "epilogue staging fits in the K-step stages");
+
   // MXFP4: both stages' block scales (8 bytes per tile row) after the stages.
   // The x rows' region is rounded up to whole 128-row pieces (rows past the
   // tile are loaded clamped and never read).
   constexpr int kScRowsX = (BM + 127) / 128 * 128;
   constexpr int kScStage = MX ? (kScRowsX + BN) * 8 : 0;
   static_assert(!MX || BN % 128 == 0, "weight scale rows load in 1 KB pieces of 128 rows");
-  constexpr int kSmem = 2 * kStage + 2 * kScStage;
+  // After the stages: folded LayerNorm -- (mu, r) of every tile row and
+  // (c_n, d_n) of every tile column, written before the K loop and published
+  // by its first barrier; EPI_RES_STATS -- each wave's (mean, M2) partial of
+  // every tile row.
+  constexpr int kFoldOff = 2 * kStage + 2 * kScStage;
+  constexpr int kStatsOff = kFoldOff;
+  constexpr int kExtraBytes = FOLD ? (BM + BN) * 8 : (STATS ? WAVES_N * BM * 8 : 0);
+  constexpr int kSmem = kFoldOff + kExtraBytes;
+  static_assert(kSmem <= 160 * 1024, "LDS of one workgroup");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmem];
 
   const int64_t M = a.M;
@@ -316,8 +330,69 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 
   const int nk = Kl / kBK;
   issue_tile(0, 0);
+  if constexpr (FOLD) {
+    // Row statistics from the chunk partials of the x rows (K = the
+    // LayerNorm's width), column constants from the prepared (c, d).
+    // Thread t takes tile row t and tile column t (both loads in flight
+    // together with the first K step's tile).
+    static_assert(BM <= 64 * NW && BN <= 64 * NW, "one thread per tile row and per tile column");
+    float2* rs = (float2*)(smem + kFoldOff);
+    float2* cdl = rs + BM;
+    // Every load is unconditional (indices clamped), so none sits behind a
+    // branch that would wait for it, and all are in flight together.
+    const int64_t mr = m0 + tid;
+    const int nc = n0 + tid;
+    const float2 cdv = a.ln_cd[nc < N ? nc : N - 1];
+    const float2 st = ln_row_stats(a.ln_stats + (mr < M ? mr : M - 1), M, K, a.ln_eps);
+    if (tid < BM) rs[tid] = mr < M ? st : make_float2(0.f, 1.f);
+    if (tid < BN) cdl[tid] = nc < N ? cdv : make_float2(0.f, 0.f);
+  }
   vm_wait_all();
   __syncthreads();
+  if constexpr (FOLD) {
+    // The accumulators start at -mu_m c_n + d_n / r_m, so that after the K
+    // loop acc = x_m . W'_n - mu_m c_n + d_n / r_m and the epilogue only
+    // scales row m by r_m.  One bf16 MFMA per 32x32 block forms it: every fp32
+    // factor is split into three bf16 parts (f = f1 + f2 + f3 to 2^-24), and
+    // the 16-long contraction holds the six leading cross products of each
+    // term (lanes 0-31: k 0-7, the mu c term; lanes 32-63: k 8-15, d / r):
+    //   k:      0      1      2      3      4      5      6, 7
+    //   A[n]:  c1     c1     c2     c1     c3     c2     0   (d1 d1 d2 d1 d3 d2)
+    //   B[m]: -mu1   -mu2   -mu1   -mu3   -mu1   -mu2    0   (s1 s2 s1 s3 s1 s2, s = 1/r)
+    // bf16 x bf16 products are exact in fp32.
+    const float2* rs = (const float2*)(smem + kFoldOff);
+    const float2* cdl = rs + BM;
+    auto split3 = [](float f, __bf16 (&p)[3]) {
+      p[0] = (__bf16)f;
+      const float r1 = f - (float)p[0];
+      p[1] = (__bf16)r1;
+      p[2] = (__bf16)(r1 - (float)p[1]);
+    };
+    auto frag6 = [](const __bf16 (&u)[3], const __bf16 (&v)[3], bool second) {
+      // second = false: (u1 u1 u2 u1 u3 u2 0 0); true: (v1 v2 v1 v3 v1 v2 0 0)
+      const __bf16 z = (__bf16)0.0f;
+      return second ? bf16x8{v[0], v[1], v[0], v[2], v[0], v[1], z, z} : bf16x8{u[0], u[0], u[1], u[0], u[2], u[1], z, z};
+    };
+    bf16x8 af[FN], bfv[FM];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const float2 v = cdl[wn * WTN + 32 * j + lrow];
+      __bf16 p[3];
+      split3(lhalf ? v.y : v.x, p);
+      af[j] = frag6(p, p, false);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const float2 v = rs[wm * WTM + 32 * i + lrow];
+      __bf16 p[3];
+      split3(lhalf ? 1.0f / v.y : -v.x, p);
+      bfv[i] = frag6(p, p, true);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j], bfv[i], acc[i][j], 0, 0, 0);
+  }
   if constexpr (DT == kFP4) {
     // One fragment set, as for E4M3, plus the K step's block scales.
     frag_t xf[FM], wf[FN];
@@ -448,12 +523,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   auto soff = [&](int row, int chunk) { return row * ORB + ((chunk ^ ((row / RPW) & (CPR - 1))) * 16); };
   const int64_t mw = m0 + wm * WTM;
   const int nw = n0 + wn * WTN;
+  [[maybe_unused]] const float2* rs = (const float2*)(smem + kFoldOff);
   // Residual rows c0 .. c0 + ECH - 1 of the wave tile into their staging
   // buffer: one 1 KB direct load fills 1024 / (WTN * 2) rows, lane i writing
   // physical chunk i % CPR of its row, i.e. the residual's logical chunk
   // (i % CPR) ^ ((row / RPW) % CPR).  Rows past M are clamped (never stored).
   auto res_load = [&](int c0) {
-    if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+    if constexpr (RES) {
       static_assert(OES == 2 && (ECH * WTN * 2) % 1024 == 0, "whole 1 KB loads of bf16 rows");
       constexpr int RPL = 1024 / (WTN * 2);  // staged rows per direct load
       if (nw >= N) return;
@@ -484,13 +560,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
       const int n = nw + j * 32 + 8 * gq + 4 * lhalf;
-      bcache[j][gq] = (bias && nw < N) ? *(const u32x2*)(bias + n) : u32x2{0u, 0u};
+      bcache[j][gq] = (!FOLD && bias && nw < N) ? *(const u32x2*)(bias + n) : u32x2{0u, 0u};
     }
 
   // Rotary epilogue: the positions of this lane's rows (one per 32-row
   // block), loaded together before the first block needs one.
   [[maybe_unused]] int rpos[FM];
-  if constexpr (EPI == EPI_QKV_ROPE) {
+  if constexpr (ROPE) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int64_t m = mw + i * 32 + lrow;
@@ -501,7 +577,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 #pragma unroll
   for (int c0 = 0; c0 < WTM; c0 += ECH) {
   unsigned char* stage = stage_at(c0);
-  if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+  if constexpr (RES) {
     // This chunk's residual has landed (and the previous chunk's stores,
     // which read the other buffer, have been issued); fetch the next one.
     vm_wait_all();
@@ -513,7 +589,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     const int row = i * 32 - c0 + lrow;  // row within the staged chunk
     const int64_t m = mw + i * 32 + lrow;
     const int64_t mc = m < M ? m : M - 1;
-    if constexpr (EPI == EPI_QKV_ROPE) {
+    // folded LayerNorm: the accumulators hold (h_m . W_n^T + b_n) / r_m
+    float osc = dq;
+    if constexpr (FOLD) osc = rs[wm * WTM + i * 32 + lrow].y;
+    if constexpr (ROPE) {
       int p = rpos[i];
       p = p < 0 ? 0 : (p < a.max_positions ? p : a.max_positions - 1);
       // The wave's 64 columns are one head's q, k or v (c = 0, 1, 2): dims
@@ -535,12 +614,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
         float lo[4], hi[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          lo[e] = acc[i][0][4 * gq + e] * dq;
-          hi[e] = acc[i][1][4 * gq + e] * dq;
+          lo[e] = acc[i][0][4 * gq + e] * osc;
+          hi[e] = acc[i][1][4 * gq + e] * osc;
         }
-        const u32x2 bl = bcache[0][gq], bh = bcache[1][gq];
-        lo[0] += bflo(bl[0]); lo[1] += bfhi(bl[0]); lo[2] += bflo(bl[1]); lo[3] += bfhi(bl[1]);
-        hi[0] += bflo(bh[0]); hi[1] += bfhi(bh[0]); hi[2] += bflo(bh[1]); hi[3] += bfhi(bh[1]);
+        if constexpr (!FOLD) {
+          const u32x2 bl = bcache[0][gq], bh = bcache[1][gq];
+          lo[0] += bflo(bl[0]); lo[1] += bfhi(bl[0]); lo[2] += bflo(bl[1]); lo[3] += bfhi(bl[1]);
+          hi[0] += bflo(bh[0]); hi[1] += bfhi(bh[0]); hi[2] += bflo(bh[1]); hi[3] += bfhi(bh[1]);
+        }
         if (c < 2) {
           const float cs_[4] = {rc[gq][0].x, rc[gq][0].z, rc[gq][1].x, rc[gq][1].z};
           const float sn_[4] = {rc[gq][0].y, rc[gq][0].w, rc[gq][1].y, rc[gq][1].w};
@@ -590,7 +671,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       }
     } else {
       bool zero_row = false;
-      if constexpr (EPI == EPI_BIAS_RESIDUAL) zero_row = a.zero_pad_rows && a.pos[mc] < 0;
+      if constexpr (RES) zero_row = a.zero_pad_rows && a.pos[mc] < 0;
+      [[maybe_unused]] float sv[STATS ? 32 : 1];  // EPI_RES_STATS: this lane's 32 stored values of the row
       bool count_row = false;  // E4M3 output: row enters the amax (in range, not padding)
       if constexpr (OUT8) count_row = m < M && (!a.zero_pad_rows || a.pos == nullptr || a.pos[mc] >= 0);
 #pragma unroll
@@ -601,12 +683,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
           const int n = nw + cl;
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e] * dq;
-          {
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * gq + e] * osc;
+          if constexpr (!FOLD) {
             const u32x2 bb = bcache[j][gq];
             v[0] += bflo(bb[0]); v[1] += bfhi(bb[0]); v[2] += bflo(bb[1]); v[3] += bfhi(bb[1]);
           }
-          if constexpr (EPI == EPI_BIAS_GELU || OUT8) {
+          if constexpr (EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_LN || OUT8) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = gelu(v[e]);
           }
@@ -617,13 +699,33 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
             *(uint32_t*)(stage + soff(row, cl / 16) + (cl % 16)) = pack_e4m3x4(v, oscale);
           } else {
             unsigned char* sp = stage + soff(row, cl / 8) + 8 * lhalf;
-            if constexpr (EPI == EPI_BIAS_RESIDUAL) {
+            if constexpr (RES) {
               const u32x2 rr = *(const u32x2*)sp;
               v[0] += bflo(rr[0]); v[1] += bfhi(rr[0]); v[2] += bflo(rr[1]); v[3] += bfhi(rr[1]);
               if (zero_row) v[0] = v[1] = v[2] = v[3] = 0.f;
             }
-            *(u32x2*)sp = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+            const u32x2 packed = u32x2{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3])};
+            *(u32x2*)sp = packed;
+            if constexpr (STATS) {
+              sv[16 * j + 4 * gq + 0] = bflo(packed[0]);
+              sv[16 * j + 4 * gq + 1] = bfhi(packed[0]);
+              sv[16 * j + 4 * gq + 2] = bflo(packed[1]);
+              sv[16 * j + 4 * gq + 3] = bfhi(packed[1]);
+            }
           }
+        }
+      }
+      if constexpr (STATS) {
+        // LayerNorm partial of the 64 stored values of this row in this
+        // wave's columns: the lane's leaf, then the lane pair (lhalf 0, 1).
+        LnPart p = nw < N ? ln_leaf(sv) : LnPart{0.f, 0.f, 0.f};
+        const LnPart o{__shfl_xor(p.n, 32), __shfl_xor(p.m, 32), __shfl_xor(p.M2, 32)};
+        p = lhalf ? ln_combine(o, p) : ln_combine(p, o);
+        if (lhalf == 0) {
+          float* ex = (float*)(smem + kStatsOff);
+          const int r = wm * WTM + i * 32 + lrow;
+          ex[2 * (wn * BM + r)] = p.m;
+          ex[2 * (wn * BM + r) + 1] = p.M2;
         }
       }
     }
@@ -636,7 +738,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     const int n = nw + ch * EPC;
     if (m >= M || n >= N) continue;
     const u32x4 v = *(const u32x4*)(stage + soff(row, ch));
-    if constexpr (EPI == EPI_QKV_ROPE) {
+    if constexpr (ROPE) {
       if (a.zero_pad_rows && a.pos[m] < 0) continue;  // padding row of a bshd batch: never attended
       const int heads = N / 192;
       const int head = n / 192, c = (n % 192) / 64, d = n % 64;
@@ -653,6 +755,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   if constexpr (OUT8) {
     __shared__ float red[NW];
     record_amax_block<NW>(a.y8_amax, amax, red);
+  }
+  if constexpr (STATS) {
+    // The tile's chunk partial of every row: waves ((0, 1), (2, 3)) of the
+    // row's wave-row, written as (mean, M2) to chunk n0 / 256.  The barrier
+    // waits for the LDS writes only, not for the output stores in flight.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    const float* ex = (const float*)(smem + kStatsOff);
+    for (int r = tid; r < BM; r += 64 * NW) {
+      const int64_t m = m0 + r;
+      if (m >= M) continue;
+      LnPart w4[WAVES_N];
+#pragma unroll
+      for (int q = 0; q < WAVES_N; ++q)
+        w4[q] = n0 + q * WTN < N ? LnPart{64.f, ex[2 * (q * BM + r)], ex[2 * (q * BM + r) + 1]} : LnPart{0.f, 0.f, 0.f};
+      static_assert(!STATS || (WAVES_N == 4 && WTN == 64), "four 64-column leaves pairs per chunk");
+      const LnPart c = ln_combine(ln_combine(w4[0], w4[1]), ln_combine(w4[2], w4[3]));
+      a.stats_out[(int64_t)(n0 / 256) * M + m] = make_float2(c.m, c.M2);
+    }
   }
 }
 
@@ -683,6 +804,14 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   if constexpr (EPI == EPI_F32_SPLIT) {
     if (a.dtype != kBF16 || a.ksplit < 1 || !a.y32 || a.K % (64 * a.ksplit)) return hipErrorInvalidValue;
     return run<256, 256, 2, 4, EPI, kBF16>(a, st);
+  } else if constexpr (EPI == EPI_QKV_ROPE_LN || EPI == EPI_BIAS_GELU_LN || EPI == EPI_RES_STATS) {
+    if (a.dtype != kBF16) return hipErrorInvalidValue;
+    if (EPI == EPI_RES_STATS ? !a.stats_out : (!a.ln_stats || !a.ln_cd)) return hipErrorInvalidValue;
+    const int64_t tilesN = (a.N + 255) / 256;
+    const int64_t cus = device_cus();
+    const int64_t r256 = ((a.M + 255) / 256 * tilesN + cus - 1) / cus;
+    const int64_t r320 = ((a.M + 319) / 320 * tilesN + cus - 1) / cus;
+    return r320 * 320 <= r256 * 256 ? run<320, 256, 2, 4, EPI, kBF16>(a, st) : run<256, 256, 2, 4, EPI, kBF16>(a, st);
   } else {
   // 8 waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs)
   // over 256x256 tiles (128x64 per wave), or 320x256 tiles (160x64 per wave)
@@ -718,7 +847,54 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   }
 }
 
+// Matrix-core rate probe: each wave runs `iters` rounds of four independent
+// chains of v_mfma_f32_32x32x16_bf16 on register operands that cycle through
+// four pseudo-random sets (every MFMA sees new bits, as in a real GEMM, so the
+// clock settles where real operands put it).  Nothing but the MFMAs is in the
+// loop; one lane writes a value so the work is kept.
+__global__ __launch_bounds__(256) void k_mfma_peak(int32_t iters, float* __restrict__ sink) {
+  const uint32_t lane = threadIdx.x & 63, wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  bf16x8 av[4], bv[4];
+  uint32_t h = lane * 2654435761u + wid * 40503u + 12345u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h = h * 1664525u + 1013904223u;
+      // values in [-2, 2): sign, exponent and mantissa bits all vary
+      av[q][e] = (__bf16)((float)(int32_t)(h >> 8) * (1.0f / 4194304.0f));
+      h = h * 1664525u + 1013904223u;
+      bv[q][e] = (__bf16)((float)(int32_t)(h >> 8) * (1.0f / 4194304.0f));
+    }
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[(q + c) & 3], bv[q], acc[c], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) t += acc[c][r];
+  if (lane == 0) sink[wid] = t;
+}
+
 }  // namespace
+
+hipError_t launch_mfma_peak(int32_t iters, int32_t blocks, float* sink, hipStream_t st) {
+  if (iters <= 0 || blocks <= 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_mfma_peak, dim3((unsigned)blocks), dim3(256), 0, st, iters, sink);
+  return hipGetLastError();
+}
+
+int32_t mfma_peak_blocks() { return 2 * device_cus(); }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
@@ -732,6 +908,9 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st) {
     case EPI_BIAS_GELU_E4M3: return dispatch<EPI_BIAS_GELU_E4M3>(a, st);
     case EPI_BIAS_GELU_MX: return dispatch<EPI_BIAS_GELU_MX>(a, st);
     case EPI_F32_SPLIT: return dispatch<EPI_F32_SPLIT>(a, st);
+    case EPI_QKV_ROPE_LN: return dispatch<EPI_QKV_ROPE_LN>(a, st);
+    case EPI_BIAS_GELU_LN: return dispatch<EPI_BIAS_GELU_LN>(a, st);
+    case EPI_RES_STATS: return dispatch<EPI_RES_STATS>(a, st);
   }
   return hipErrorInvalidValue;
 }

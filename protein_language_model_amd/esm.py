@@ -22,7 +22,8 @@ STATUS_NAMES = {0: "ESM_OK", 1: "ESM_ERR_NULL", 2: "ESM_ERR_SHAPE", 3: "ESM_ERR_
 PRECISION = {"bf16": 0, "fp8": 1, "mxfp4": 2}
 LAYOUT_THD, LAYOUT_BSHD = 0, 1
 EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU_E4M3 = 0, 1, 2, 3
-WS_REGIONS = {"ln1": 0, "qkv": 1, "ctx": 2, "x1": 3, "ln2": 4, "act": 5, "pos": 6, "tiles": 7, "ntiles": 8, "segs": 9}
+WS_REGIONS = {"ln1": 0, "qkv": 1, "ctx": 2, "x1": 3, "ln2": 4, "act": 5, "pos": 6, "tiles": 7, "ntiles": 8, "segs": 9,
+              "stats": 10}
 ATTN_TILE_ROWS = 256  # ESM_ATTN_TILE_ROWS: query rows per attention workgroup
 KERNEL_CLASSES = ("segment", "embed", "layernorm", "gemm_qkv", "attention", "gemm_out", "gemm_fc1", "gemm_fc2",
                   "other", "fp8", "head", "biased_attention", "attention_bwd", "linear_bwd")
@@ -102,6 +103,7 @@ SIGNATURES = {
     "esm_layernorm_fwd": (_i32, [_p, _p, _p, _p, _p, _i64, _p]),
     "esm_layernorm_e4m3_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i64, _p]),
     "esm_linear_e4m3_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _i32, _p]),
+    "esm_prepare_layer": (_i32, [_p, _i32, ctypes.POINTER(EsmLayerWeights), _p]),
     "esm_fp8_prepare_layer": (_i32, [_p, _i32, ctypes.POINTER(EsmLayerWeights), _p]),
     "esm_mxfp4_prepare_layer": (_i32, [_p, _i32, ctypes.POINTER(EsmLayerWeights), _p]),
     "esm_fp8_get_state": (_i32, [_p, ctypes.POINTER(EsmFp8State), _p]),
@@ -109,6 +111,7 @@ SIGNATURES = {
     "esm_fp8_reset": (_i32, [_p, _p]),
     "esm_set_layer_precision": (_i32, [_p, _p, _i32, _p]),
     "esm_fp8_quantize": (_i32, [_p, _p, _i64, _p, _p, _p, _p]),
+    "esm_mfma_peak": (_i32, [_p, _i32, _p, _sz, ctypes.POINTER(ctypes.c_double), _p]),
     "esm_profile_enable": (_i32, [_p, _i32]),
     "esm_profile_read": (_i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "esm_check_cu_seqlens": (_i32, [_p, _i32, _i64, _i32, _i32]),
@@ -257,6 +260,8 @@ class Encoder:
         raw = ws[off.value: off.value + nb.value]
         if name in ("pos", "tiles", "ntiles", "segs"):
             return raw.view(torch.int32)
+        if name == "stats":
+            return raw.view(torch.float32)
         if self.cfg.precision == PRECISION["fp8"] and name in ("ln1", "ctx", "ln2", "act"):
             return raw  # E4M3 codes, row-major with the bf16 row count
         return raw.view(torch.bfloat16)
@@ -587,6 +592,14 @@ class Encoder:
         return y
 
     # -- FP8 delayed scaling
+    def prepare_layer(self, layer_idx: int, weights, stream=None) -> None:
+        w = layer_weights_struct(weights)
+        _call("esm_prepare_layer", self._h, int(layer_idx), ctypes.byref(w), _stream(stream))
+
+    def prepare(self, weights: Sequence[Dict], stream=None) -> None:
+        for l, w in enumerate(weights):
+            self.prepare_layer(l, w, stream)
+
     def fp8_prepare_layer(self, layer_idx: int, weights, stream=None) -> None:
         w = layer_weights_struct(weights)
         _call("esm_fp8_prepare_layer", self._h, int(layer_idx), ctypes.byref(w), _stream(stream))
@@ -646,6 +659,13 @@ class Encoder:
         return y, amax
 
     # -- timing
+    def mfma_peak(self, iters: int, sink, stream=None) -> float:
+        """Launch the matrix-core rate probe; returns its flop count."""
+        fl = ctypes.c_double(0.0)
+        _call("esm_mfma_peak", self._h, int(iters), _ptr(sink), sink.numel() * sink.element_size(),
+              ctypes.byref(fl), _stream(stream))
+        return fl.value
+
     def profile_enable(self, on: bool = True) -> None:
         _call("esm_profile_enable", self._h, 1 if on else 0)
 

@@ -113,7 +113,7 @@ def test_bad_host_cu_seqlens_is_rejected_before_launch(gu, tiny):
     assert ei.value.status == 3
 
 
-def _bshd_stack_case(gu, m, lengths, layers, S, seed):
+def _bshd_stack_case(gu, m, lengths, layers, S, seed, fold=False):
     """Token ids [B, S] right-padded with out-of-range garbage ids (the
     library clamps ids, so they are still read), and the same sequences
     packed; returns (bshd output bits [B, S, H], THD output bits [T, H],
@@ -127,6 +127,8 @@ def _bshd_stack_case(gu, m, lengths, layers, S, seed):
         ids[i, lengths[i]:] = r.integers(-5, m.vocab + 40, S - lengths[i])
     emb = D.make_embedding(m.vocab, m.hidden, seed=seed)
     wd = [D.make_layer_weights_device(m.hidden, m.ffn, l, seed=seed) for l in range(layers)]
+    if fold:
+        enc.prepare(wd)
     yb = enc.stack_fwd_bshd(wd, gu.to_dev_i32(lengths), B, S, token_ids=gu.to_dev_i32(ids),
                             embedding=gu.to_dev_bf16(emb), seqlens_host=lengths)
     packed = np.concatenate([ids[i, :lengths[i]] for i in range(B)])
@@ -139,7 +141,8 @@ def _bshd_stack_case(gu, m, lengths, layers, S, seed):
     return out
 
 
-def test_stack_bshd_from_ids_matches_thd_and_the_oracle(gu):
+@pytest.mark.parametrize("fold", [False, True])
+def test_stack_bshd_from_ids_matches_thd_and_the_oracle(gu, fold):
     """esm_stack_fwd_bshd from padded token ids (3 layers, hidden 320): valid
     rows bit-equal to the packed stack, padded rows written as 0, and the
     valid rows against the oracle's padded layers chained (free-running,
@@ -147,7 +150,7 @@ def test_stack_bshd_from_ids_matches_thd_and_the_oracle(gu):
     m = D.WORKLOADS["tiny"].model
     lengths = [17, 64, 0, 100, 200, 1]
     S, layers = 224, 3
-    yb, yt, wd, emb, ids = _bshd_stack_case(gu, m, lengths, layers, S, seed=3)
+    yb, yt, wd, emb, ids = _bshd_stack_case(gu, m, lengths, layers, S, seed=3, fold=fold)
     cu = D.cu_from_lengths(lengths)
     for i, L in enumerate(lengths):
         assert np.array_equal(yb[i, :L], yt[cu[i]:cu[i + 1]]), i
@@ -166,17 +169,99 @@ def test_stack_bshd_from_ids_matches_thd_and_the_oracle(gu):
             assert gu.rel_err(got[i, :L], x[i, :L]) < _depth_tol(layers - 1), i
 
 
-def test_650m_stack_bshd_equals_thd_bitexact(gu):
+@pytest.mark.parametrize("fold", [False, True])
+def test_650m_stack_bshd_equals_thd_bitexact(gu, fold):
     """Two 650M-width layers on twelve sequences of the 650M batch padded to
     S = 1024 (the padded benchmark's S): valid rows bit-equal to the packed
     stack, padded rows 0."""
     wl = D.WORKLOADS["650m"]
     lengths = D.make_batch(wl).lengths[:12]
-    yb, yt, *_ = _bshd_stack_case(gu, dataclasses.replace(wl.model, layers=2), lengths, 2, 1024, seed=0)
+    yb, yt, *_ = _bshd_stack_case(gu, dataclasses.replace(wl.model, layers=2), lengths, 2, 1024, seed=0, fold=fold)
     cu = D.cu_from_lengths(lengths)
     for i, L in enumerate(lengths):
         assert np.array_equal(yb[i, :L], yt[cu[i]:cu[i + 1]]), i
         assert not np.any(yb[i, L:]), i
+
+
+# ------------------------------------------------------------- LayerNorm folded into the linears
+
+def _chunk_stats_f64(x):
+    """Exact (fp64) 256-column chunk (mean, M2) of every row of x [T, H]."""
+    T, H = x.shape
+    out = []
+    for c0 in range(0, H, 256):
+        blk = x[:, c0:c0 + 256]
+        m = blk.mean(axis=1)
+        out.append(np.stack([m, ((blk - m[:, None]) ** 2).sum(axis=1)], axis=1))
+    return np.stack(out)          # [chunks, T, 2]
+
+
+@pytest.mark.parametrize("random_ln", [False, True])
+def test_tiny_folded_layer_matches_oracle_and_writes_exact_statistics(gu, tiny, random_ln):
+    """esm_prepare_layer folds gamma, beta into W_qkv, W_fc1: the layer against
+    the oracle (random gamma, beta included), and the LayerNorm partials its
+    fc2 epilogue leaves in the workspace (those of the output rows) against
+    fp64 chunk statistics of the output's stored values."""
+    b, m = tiny["batch"], tiny["m"]
+    enc = _encoder(m)
+    wd, wr, _ = gu.layer_weights(m.hidden, m.ffn, 4, random_ln=random_ln)
+    enc.prepare_layer(0, wd)
+    xb = D.make_hidden(b.T, m.hidden, seed=7)
+    ws = enc.workspace(b.T, b.B)
+    y = enc.layer_fwd(wd, gu.to_dev_bf16(xb), gu.to_dev_i32(b.cu_seqlens), b.B, b.T, b.max_seqlen,
+                      cu_seqlens_host=b.cu_seqlens, workspace=ws)
+    got = gu.from_dev(y)
+    err = gu.rel_err(got, O.layer_forward(D.bf16_bits_to_f64(xb), b.cu_seqlens, wr, m.heads))
+    print(f"tiny folded layer (random LN {random_ln}) rel err {err:.2e}")
+    assert err < TOL
+    st = enc.workspace_region(ws, b.T, b.B, "stats")
+    torch.cuda.synchronize()
+    chunks = (m.hidden + 255) // 256
+    st = st.cpu().numpy()[:chunks * b.T * 2].reshape(chunks, b.T, 2).astype(np.float64)
+    ref = _chunk_stats_f64(got)
+    assert np.allclose(st[..., 0], ref[..., 0], rtol=1e-5, atol=1e-6 * np.abs(got).max())
+    assert np.allclose(st[..., 1], ref[..., 1], rtol=1e-4, atol=1e-6 * ref[..., 1].max())
+    enc.close()
+
+
+def test_650m_folded_layer_matches_oracle_and_index_invariants(gu, l650):
+    """The 650M layer with folded LayerNorms: oracle gate; packed == alone,
+    THD == bshd on valid rows with NaN padding, bit for bit."""
+    b, m = l650["b"], l650["m"]
+    enc = _encoder(m)
+    enc.prepare_layer(0, l650["wd"])
+    cu = b.cu_seqlens
+    y = gu.bits_of(enc.layer_fwd(l650["wd"], gu.to_dev_bf16(b.hidden), gu.to_dev_i32(cu), b.B, b.T, b.max_seqlen))
+    err = gu.rel_err(D.bf16_bits_to_f64(y), O.layer_forward(D.bf16_bits_to_f64(b.hidden), cu, l650["wr"], m.heads))
+    print(f"650M folded layer rel err {err:.2e}")
+    assert err < TOL
+    for s in (0, int(np.argmax(b.lengths)), b.B - 1):
+        a, L = int(cu[s]), int(b.lengths[s])
+        one = enc.layer_fwd(l650["wd"], gu.to_dev_bf16(b.hidden[a:a + L]), gu.to_dev_i32([0, L]), 1, L, L)
+        assert np.array_equal(gu.bits_of(one), y[a:a + L]), s
+    sel = list(range(10))
+    lens = b.lengths[sel]
+    S = int(lens.max())
+    xb = np.full((len(sel), S, m.hidden), 0x7FC0, dtype=np.uint16)
+    for i in sel:
+        xb[i, :lens[i]] = b.hidden[cu[i]:cu[i + 1]]
+    yb = gu.bits_of(enc.layer_fwd_bshd(l650["wd"], gu.to_dev_bf16(xb), gu.to_dev_i32(lens), len(sel), S,
+                                       seqlens_host=lens)).reshape(len(sel), S, m.hidden)
+    for i in sel:
+        assert np.array_equal(yb[i, :lens[i]], y[cu[i]:cu[i + 1]]), i
+        assert not np.any(yb[i, lens[i]:]), i
+    enc.close()
+
+
+def test_prepare_is_rejected_by_quantised_encoders(gu):
+    m = D.WORKLOADS["tiny"].model
+    enc = esm.Encoder(hidden_size=256, num_attention_heads=4, intermediate_size=1024, num_hidden_layers=1,
+                      precision="fp8")
+    wd, _, _ = gu.layer_weights(256, 1024, 0)
+    with pytest.raises(esm.EsmError) as ei:
+        enc.prepare_layer(0, wd)
+    assert ei.value.status == 8   # ESM_ERR_STATE
+    enc.close()
 
 
 # ------------------------------------------------------------- 650M single layer
@@ -253,9 +338,12 @@ def test_650m_deterministic(gu, l650):
 
 # ------------------------------------------------------------- full stacks, sampled
 
-def _stack_layers(gu, wl, tf_seqs, fr_seqs):
+def _stack_layers(gu, wl, tf_seqs, fr_seqs, fold=True):
     """Chained esm_layer_fwd calls over the whole batch from token ids; the
-    final output must equal one esm_stack_fwd call bit for bit.  Each layer's
+    final output must equal one esm_stack_fwd call bit for bit (with the
+    LayerNorms folded, the chained calls take each layer's statistics from a
+    statistics pass, the stack from the previous GEMM's epilogue: the bits
+    agree only if both give the same partials).  Each layer's
     output is checked on sampled sequences (sequences are independent, so a
     sample can be computed alone) in two ways:
       * teacher-forced (the gate): the oracle layer l is fed the library's
@@ -269,6 +357,8 @@ def _stack_layers(gu, wl, tf_seqs, fr_seqs):
     b = D.make_batch(wl)
     emb = D.make_embedding(m.vocab, m.hidden)
     wd_all = [D.make_layer_weights_device(m.hidden, m.ffn, l) for l in range(m.layers)]
+    if fold:
+        enc.prepare(wd_all)
     cu_d = gu.to_dev_i32(b.cu_seqlens)
     ws = enc.workspace(b.T, b.B)
     stack = enc.stack_fwd(wd_all, cu_d, b.B, b.T, b.max_seqlen, token_ids=gu.to_dev_i32(b.ids),

@@ -19,10 +19,12 @@ def gu():
     return gpu_util
 
 
-def _two_calls(gu, m, batches, layer_seed):
+def _two_calls(gu, m, batches, layer_seed, fold=False):
     enc = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn,
                       num_hidden_layers=1)
-    wd, _, _ = gu.layer_weights(m.hidden, m.ffn, layer_seed)
+    wd, _, _ = gu.layer_weights(m.hidden, m.ffn, layer_seed, random_ln=fold)
+    if fold:
+        enc.prepare_layer(0, wd)
     for lengths in batches:
         lengths = np.asarray(lengths, np.int32)
         cu = D.cu_from_lengths(lengths)
@@ -41,10 +43,13 @@ def test_noalloc_tiny_two_calls_second_smaller(gu):
     _two_calls(gu, m, [[17, 64, 100, 200, 0, 300], [5, 1, 40]], 0)
 
 
-def test_noalloc_650m_width_two_calls_second_smaller(gu):
+@pytest.mark.parametrize("fold", [False, True])
+def test_noalloc_650m_width_two_calls_second_smaller(gu, fold):
+    """fold: the layer's LayerNorms folded into its linears (esm_prepare_layer),
+    whose statistics also live in the scratch."""
     m = D.WORKLOADS["650m_layer"].model
     b = D.make_batch(D.WORKLOADS["650m_layer"])
-    _two_calls(gu, m, [b.lengths[:6], b.lengths[6:8]], 1)
+    _two_calls(gu, m, [b.lengths[:6], b.lengths[6:8]], 1, fold)
 
 
 def test_noalloc_rejects_a_batch_beyond_the_scratch(gu):
