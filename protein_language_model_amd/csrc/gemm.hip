@@ -261,8 +261,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   // its four k sub-steps, not at once: a wave that issues all of them
   // back to back stalls at issue behind the address unit and starts its
   // MFMAs late (a loads + LDS + MFMA copy of the loop measured 8-12% faster
-  // with the loads spread so).  The last run still has a sub-step and a half
-  // to land before the barrier that ends the K step.
+  // with the loads spread so; the 650M stack's GEMMs 6-8%).  The last run
+  // still has a sub-step and a half to land before the barrier that ends the
+  // K step.  The E4M3 and MXFP4 K steps hold 2-4x the flops per byte in fewer
+  // MFMA cycles, and their loads need the whole step to land: spread over
+  // their sub-steps they measured 10-50% slower, so they go out at once.
   constexpr int kParts = DT == kBF16 ? 3 : 1;
 
   // Fragment reads: row r of the tile, logical 16-byte chunk ch, stored at
@@ -413,11 +416,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     frag_t xf[FM], wf[FN];
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < nk) issue_tile((kt + 1) * kRowBytes, cur ^ 1);
+      const bool more = kt + 1 < nk;
       load_scales(cur);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         __builtin_amdgcn_sched_barrier(0);
+        if (more && kk < kParts) issue_part((kt + 1) * kRowBytes, cur ^ 1, kk, kParts);
         load_frags(xf, wf, cur, kk);
         __builtin_amdgcn_sched_barrier(0);
         mfma_step_mx(xf, wf, kk);
@@ -433,10 +437,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     frag_t xf[FM], wf[FN];
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
-      if (kt + 1 < nk) issue_tile((kt + 1) * kRowBytes, cur ^ 1);
+      const bool more = kt + 1 < nk;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         __builtin_amdgcn_sched_barrier(0);
+        if (more && kk < kParts) issue_part((kt + 1) * kRowBytes, cur ^ 1, kk, kParts);
         load_frags(xf, wf, cur, kk);
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(xf, wf);
