@@ -94,10 +94,13 @@ def traffic_record(kernel: str, rows: int, hidden: int, ffn: int):
     on another shape (rows x hidden x ffn) than the one being measured."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    src = os.path.join(ROOT, "protein_language_model_amd", "csrc", "gemm.hip")
+    csrc = os.path.join(ROOT, "protein_language_model_amd", "csrc")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for f in ("gemm.hip", "common.h"):     # the GEMM kernel and the device helpers it inlines
+            h.update(open(os.path.join(csrc, f), "rb").read())
+        sha = h.hexdigest()
     except (OSError, ValueError):
         return None
     ent = rec.get(kernel)

@@ -30,7 +30,10 @@ def test_traffic_record_matches_source_and_shape():
     shape = (ent["rows"], ent["hidden"], ent["ffn"])
     got = b.traffic_record("gemm_fc1", *shape)
     import hashlib
-    sha = hashlib.sha256(open(os.path.join(ROOT, "protein_language_model_amd", "csrc", "gemm.hip"), "rb").read()).hexdigest()
+    h = hashlib.sha256()                # the GEMM kernel source and the device header it includes
+    for f in ("gemm.hip", "common.h"):
+        h.update(open(os.path.join(ROOT, "protein_language_model_amd", "csrc", f), "rb").read())
+    sha = h.hexdigest()
     if ent["gemm_source_sha256"] == sha:
         assert got == ent["bytes_per_launch"]
     else:
