@@ -55,6 +55,15 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// x of lanes l and l ^ 32, in some order (one VALU swap of the wave's halves:
+// whichever half moves, the two results of lane l are these two values).
+__device__ __forceinline__ void pair_halves(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  a = __builtin_bit_cast(float, (unsigned)r[0]);
+  b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
 // Chunk swizzle of LDS row r (16-byte chunk c is stored at c ^ kSwz(r)).  Over
 // any 8 consecutive rows it is a permutation (key reads: eight rows, one chunk
 // each, per 128-byte bank sweep); rows 4i..4i+3 get distinct values of bit 1..2
@@ -84,8 +93,9 @@ __device__ __forceinline__ int kSwzB(int r) { return (r >> 1) & 7; }
 // 64 contiguous values at + r * rs.  Biased modes add maskg[c] and
 // pairg[r * L + c] to the score of (query row r, key c).  On return o holds
 // this lane's unnormalised context (dims d * 32 + 8 g + 4 lhalf + e in
-// o[d][4 g + e]), inv the reciprocal of its softmax sum and mrow the largest
-// raw score of its row (q.k, before the scale; the biased modes: the score).
+// o[d][4 g + e]), inv the reciprocal of its softmax sum and mrow the maximum
+// that sum and o were taken against: a raw score of the row (q.k, before the
+// scale; the biased modes: the score) at most 8 / kS below its largest.
 template <int kMode>
 __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg,
                                        const bf16_t* __restrict__ Vg, const int64_t rs, const int L, const int q0,
@@ -283,51 +293,76 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
       }
     }
     if (active) {
+      // The matrix core and the fp32 VALU do not run at once on a SIMD (a
+      // wave's MFMAs and another wave's adds and multiplies serialise; only
+      // the exponentials overlap them), so a wave entering a run of MFMAs is
+      // given priority over the waves in their softmax.
+      __builtin_amdgcn_s_setprio(1);
       const bf16_t* kt = sk[cur] + sub * kKT * kLdsRow;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+        for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 kf = *(const bf16x8*)(&kt[(kb * 32 + lrow) * kLdsRow + koff[kk]]);
           st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], st[kb], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       if ((j + 1) * kKT > L) {
+        // Keys at or past L: key offset c of the tile (a constant per
+        // register) against this lane's limit.
+        const int lim = L - j * kKT - 4 * lhalf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = j * kKT + kb * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-            if (key >= L) st[kb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) st[kb][r] = -INFINITY;
       }
-      float mx = st[0][0];
+      // Row max and row sum in four independent chains (short dependency
+      // chains for the VALU); the chains combine in a fixed order.
+      float m4[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int c = 0; c < 4; ++c) {
+        m4[c] = st[c >> 1][8 * (c & 1)];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int r = 1; r < 8; ++r) m4[c] = fmaxf(m4[c], st[c >> 1][8 * (c & 1) + r]);
+      }
+      float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      {
+        float a, b;
+        pair_halves(mx, a, b);
+        mx = fmaxf(a, b);
+      }
       const float m_new = fmaxf(m_i, mx);
-      // Biased modes: while every key so far is -inf (masked), subtract 0, so
-      // the probabilities stay 0 instead of exp(-inf - -inf) = NaN.
-      const float m_sub = ((kMode & kBias) != 0 && m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_fast((m_i - m_sub) * kS);
-      const float mc = m_sub * kS;
-      float rs_ = 0.f;
+      // Lazy rescaling: the running maximum (and with it o and l) moves only
+      // when some row of the wave grew by more than 8 in exp2 units; until
+      // then the probabilities are taken against the older maximum and stay
+      // below 2^8.  The first tile always rescales (m_i = -inf gives +inf);
+      // rows all -inf so far (biased modes) give NaN and do not.
+      const bool grow = (m_new - m_i) * kS > 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        // Biased modes: while every key so far is -inf (masked), subtract 0,
+        // so the probabilities stay 0 instead of exp(-inf - -inf) = NaN.
+        const float m_sub = ((kMode & kBias) != 0 && m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2_fast((m_i - m_sub) * kS);
+        l_i *= alpha;
+        m_i = m_new;
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      }
+      const float mc = (((kMode & kBias) != 0 && m_i == -INFINITY) ? 0.f : m_i) * kS;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = exp2_fast(fmaf(st[kb][r], kS, -mc));
           st[kb][r] = p;
-          rs_ += p;
+          s4[2 * kb + (r >> 3)] += p;
         }
-      l_i = l_i * alpha + rs_;
-      m_i = m_new;
-#pragma unroll
-      for (int d = 0; d < 2; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      l_i += (s4[0] + s4[1]) + (s4[2] + s4[3]);
 
       // P^T as bf16 operand B: block kb, step u covers registers 8u .. 8u+7.
       bf16x8 pb[2][2];
@@ -341,13 +376,14 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
           pb[kb][u] = __builtin_bit_cast(bf16x8, w);
         }
 
+      __builtin_amdgcn_s_setprio(1);
       const bf16_t* vb = sv[cur] + sub * kKT * kLdsRow;
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int u = 0; u < 2; ++u) {
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
+          for (int d = 0; d < 2; ++d) {
             const int k0 = kb * 32 + 16 * u + 4 * lhalf;
             const bf16_t* p0 = vb + (k0 + tr_row) * kLdsRow + voff[d][0];
             const bf16_t* p1 = vb + (k0 + tr_row + 8) * kLdsRow + voff[d][1];
@@ -357,14 +393,17 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
             const i16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[kb][u], o[d], 0, 0, 0);
           }
-      }
+        }
+      __builtin_amdgcn_s_setprio(0);
     }
     }
     vm_wait_all();
     __syncthreads();
   }
 
-  const float lt = l_i + __shfl_xor(l_i, 32);
+  float la, lb;
+  pair_halves(l_i, la, lb);
+  const float lt = la + lb;
   inv = 1.0f / lt;
   mrow = m_i;
 }
