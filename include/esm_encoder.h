@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 16
+#define ESM_ABI_VERSION 17
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -195,7 +195,11 @@ esm_status esm_workspace_region(const esm_encoder* enc, int64_t max_tokens, int3
  * (ESM_ERR_STATE if never called for layer_idx); LayerNorm, attention, the
  * residuals and every GEMM output stay in bf16/fp32.  Needs hidden_size and
  * intermediate_size multiples of 256 and intermediate_size <= 8 hidden_size
- * (checked at create). */
+ * (checked at create).
+ *
+ * A quantised encoder (FP8 or MXFP4) runs each layer in the precision
+ * esm_set_layer_precision gave it -- FP8, MXFP4 or bf16, its own by default --
+ * so one stack can mix FP8 and MXFP4 layers. */
 esm_status esm_layer_fwd(esm_encoder* enc, const esm_layer_weights* w, int32_t layer_idx,
                          const void* x_in, void* x_out,
                          const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
@@ -566,12 +570,19 @@ esm_status esm_prepare_layer(esm_encoder* enc, int32_t layer_idx, const esm_laye
 
 /* Casts layer layer_idx's four linear weights (bf16 in w) to E4M3 copies owned
  * by the library, each with scale 448 / amax(W) computed on the device.
- * Enqueued on stream; call again whenever the weights change.
- * ESM_ERR_STATE for a bf16 encoder. */
+ * Enqueued on stream; call again whenever the weights change.  In an MXFP4
+ * encoder the first call creates the FP8 state and E4M3 weight store
+ * (synchronous allocation; ESM_ERR_UNSUPPORTED unless hidden_size and
+ * intermediate_size are multiples of 128).  ESM_ERR_STATE for a bf16
+ * encoder. */
 esm_status esm_fp8_prepare_layer(esm_encoder* enc, int32_t layer_idx, const esm_layer_weights* w,
                                  esm_stream_t stream);
 
-/* Copies the state into the caller's host arrays after waiting for stream. */
+/* The FP8 state functions below need an encoder holding the delayed-scaling
+ * state: an FP8 encoder, or an MXFP4 encoder given an FP8 layer (by
+ * esm_set_layer_precision or esm_fp8_prepare_layer); ESM_ERR_STATE otherwise.
+ *
+ * Copies the state into the caller's host arrays after waiting for stream. */
 esm_status esm_fp8_get_state(esm_encoder* enc, esm_fp8_state* state, esm_stream_t stream);
 
 /* Replaces the state (scales must be positive and finite; steps >= 0) after
@@ -585,20 +596,27 @@ esm_status esm_fp8_reset(esm_encoder* enc, esm_stream_t stream);
 /* MXFP4 weights of layer layer_idx ([TE-ESM2] FP8与FP4混合精度支持, read as
  * OCP MXFP4): the four linear weights of w quantised per 32-value block along
  * K (esm_mxfp4_quantize) into library-owned memory, asynchronously on stream.
- * ESM_ERR_STATE unless the encoder was created with ESM_PRECISION_MXFP4;
- * ESM_ERR_SHAPE for layer_idx outside [0, num_hidden_layers). */
+ * In an FP8 encoder the first call creates the MXFP4 weight store
+ * (synchronous allocation; ESM_ERR_UNSUPPORTED unless the MXFP4 shape rule of
+ * esm_layer_fwd holds).  ESM_ERR_STATE for a bf16 encoder; ESM_ERR_SHAPE for
+ * layer_idx outside [0, num_hidden_layers). */
 esm_status esm_mxfp4_prepare_layer(esm_encoder* enc, int32_t layer_idx, const esm_layer_weights* w,
                                    esm_stream_t stream);
 
 /* Per-layer precision of an FP8 or MXFP4 encoder ([TE-ESM2] FP8与FP4混合精度支持:
- * a per-layer precision setting): precision[l] (host, num_layers entries) is
- * the encoder's own precision (every layer's default) or ESM_PRECISION_BF16.
- * A bf16 layer runs the bf16 kernels and needs no prepared weights; in an FP8
- * encoder it records no amax, and its FP8 state (scales, history, step count)
- * stays as it is until the layer runs FP8 again.  Waits for stream.
- * ESM_ERR_STATE for an encoder created with bf16 precision; ESM_ERR_SHAPE when
- * num_layers is not the config's; ESM_ERR_UNSUPPORTED for another precision
- * code. */
+ * the encoder takes an FP8 and an FP4 recipe and a per-layer precision list):
+ * precision[l] (host, num_layers entries) is ESM_PRECISION_FP8_DELAYED,
+ * ESM_PRECISION_MXFP4 or ESM_PRECISION_BF16, in any mix; the default of every
+ * layer is the encoder's own precision.  A layer needs weights prepared in its
+ * format (esm_fp8_prepare_layer / esm_mxfp4_prepare_layer) before it runs,
+ * else the forward returns ESM_ERR_STATE; a bf16 layer runs the bf16 kernels
+ * and needs none.  Only FP8 layers record amax and step their delayed-scaling
+ * state; a layer that is not FP8 keeps its FP8 state (scales, history, step
+ * count) as it is until it runs FP8 again.  The first FP8 layer of an MXFP4
+ * encoder creates the FP8 state.  Waits for stream.  ESM_ERR_STATE for an
+ * encoder created with bf16 precision; ESM_ERR_SHAPE when num_layers is not
+ * the config's; ESM_ERR_UNSUPPORTED for another precision code or when the
+ * shape rule of a requested format (esm_layer_fwd) does not hold. */
 esm_status esm_set_layer_precision(esm_encoder* enc, const int32_t* precision, int32_t num_layers,
                                    esm_stream_t stream);
 

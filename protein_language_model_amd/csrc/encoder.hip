@@ -32,17 +32,22 @@ struct esm_encoder {
   std::vector<std::pair<int, size_t>> recs;  // (class, index of start event)
   double ms[ESM_K_COUNT] = {0};
   int64_t launches[ESM_K_COUNT] = {0};
-  // FP8 delayed scaling (precision ESM_PRECISION_FP8_DELAYED only)
+  // Quantised encoders (precision FP8 or MXFP4): per-layer precision, the
+  // encoder's own by default; FP8, MXFP4 and bf16 layers may be mixed.
+  std::vector<int32_t> layer_prec;
+  // FP8 delayed scaling: created with an FP8 encoder, or with the first FP8
+  // layer of an MXFP4 encoder
   void* fp8_mem = nullptr;         // state arrays of f8
   Fp8State f8{};
   uint8_t* w8 = nullptr;           // per layer: E4M3 w_qkv | w_out | w_fc1 | w_fc2
   size_t w8_layer = 0;             // bytes per layer
-  std::vector<char> prepared;      // layer weights cast since create
-  std::vector<int32_t> layer_prec; // FP8 / MXFP4 encoder: per-layer precision (the encoder's by default, or bf16)
-  // MXFP4 (precision ESM_PRECISION_MXFP4 only): per layer the codes and
-  // block scales of w_qkv | w_out | w_fc1 | w_fc2
+  std::vector<char> prepared8;     // E4M3 weights cast since the state was created
+  // MXFP4: per layer the codes and block scales of w_qkv | w_out | w_fc1 |
+  // w_fc2; created with an MXFP4 encoder, or with the first MXFP4 weights
+  // prepared in an FP8 encoder
   uint8_t* w4 = nullptr;
   size_t w4_layer = 0;
+  std::vector<char> prepared4;     // MXFP4 weights quantised since created
   // LM head: the tied decoder weight and its bias padded to vocab_pad rows
   // (a multiple of 64 GEMM columns), refilled from the caller's on each call
   bf16_t* head_w = nullptr;        // [vocab_pad, H] then [vocab_pad]
@@ -113,6 +118,24 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int32_t kHeadMaxVocab = 4096;  // LM head decoder rows supported
 
+// Shapes each quantised format needs (one K step of its GEMM; the MXFP4
+// activation codes are staged in the QKV region).
+esm_status check_fp8_shape(const esm_config* c) {
+  if (c->hidden_size % 128 != 0 || c->intermediate_size % 128 != 0)
+    return fail(ESM_ERR_UNSUPPORTED,
+                "FP8 needs hidden_size (%d) and intermediate_size (%d) to be multiples of 128 (E4M3 K step)",
+                c->hidden_size, c->intermediate_size);
+  return ok();
+}
+esm_status check_mx_shape(const esm_config* c) {
+  if (c->hidden_size % 256 != 0 || c->intermediate_size % 256 != 0 || c->intermediate_size > 8 * c->hidden_size)
+    return fail(ESM_ERR_UNSUPPORTED,
+                "MXFP4 needs hidden_size (%d) and intermediate_size (%d) to be multiples of 256 (one K step) and "
+                "intermediate_size <= 8 * hidden_size (its codes are staged in the QKV region)",
+                c->hidden_size, c->intermediate_size);
+  return ok();
+}
+
 esm_status check_config(const esm_config* c) {
   if (!c) return fail(ESM_ERR_NULL, "config is NULL");
   if (c->hidden_size <= 0 || c->hidden_size % 64 != 0)
@@ -135,16 +158,14 @@ esm_status check_config(const esm_config* c) {
   if (c->precision != ESM_PRECISION_BF16 && c->precision != ESM_PRECISION_FP8_DELAYED &&
       c->precision != ESM_PRECISION_MXFP4)
     return fail(ESM_ERR_UNSUPPORTED, "unknown precision %d", c->precision);
-  if (c->precision == ESM_PRECISION_MXFP4 &&
-      (c->hidden_size % 256 != 0 || c->intermediate_size % 256 != 0 || c->intermediate_size > 8 * c->hidden_size))
-    return fail(ESM_ERR_UNSUPPORTED,
-                "MXFP4 needs hidden_size (%d) and intermediate_size (%d) to be multiples of 256 (one K step) and "
-                "intermediate_size <= 8 * hidden_size (its codes are staged in the QKV region)",
-                c->hidden_size, c->intermediate_size);
-  if (c->precision == ESM_PRECISION_FP8_DELAYED && (c->hidden_size % 128 != 0 || c->intermediate_size % 128 != 0))
-    return fail(ESM_ERR_UNSUPPORTED,
-                "FP8 needs hidden_size (%d) and intermediate_size (%d) to be multiples of 128 (E4M3 K step)",
-                c->hidden_size, c->intermediate_size);
+  if (c->precision == ESM_PRECISION_MXFP4) {
+    esm_status s = check_mx_shape(c);
+    if (s) return s;
+  }
+  if (c->precision == ESM_PRECISION_FP8_DELAYED) {
+    esm_status s = check_fp8_shape(c);
+    if (s) return s;
+  }
   if (c->amax_history_len < 1 || c->amax_history_len > 1024)
     return fail(ESM_ERR_SHAPE, "amax_history_len %d outside [1, 1024]", c->amax_history_len);
   return ok();
@@ -262,16 +283,16 @@ esm_status check_ws(const esm_encoder* e, void* ws, size_t ws_bytes, int64_t row
 // ---------------------------------------------------------------- FP8 state
 
 bool is_fp8(const esm_encoder* e) { return e->cfg.precision == ESM_PRECISION_FP8_DELAYED; }
-// Layer l of an FP8 encoder runs FP8 unless esm_set_layer_precision chose bf16 for it.
-bool layer_fp8(const esm_encoder* e, int32_t l) {
-  return is_fp8(e) && l >= 0 && (size_t)l < e->layer_prec.size() && e->layer_prec[(size_t)l] == ESM_PRECISION_FP8_DELAYED;
-}
-
 bool is_mx(const esm_encoder* e) { return e->cfg.precision == ESM_PRECISION_MXFP4; }
-// Layer l of an MXFP4 encoder runs MXFP4 unless esm_set_layer_precision chose bf16 for it.
-bool layer_mx(const esm_encoder* e, int32_t l) {
-  return is_mx(e) && l >= 0 && (size_t)l < e->layer_prec.size() && e->layer_prec[(size_t)l] == ESM_PRECISION_MXFP4;
+bool is_quantised(const esm_encoder* e) { return is_fp8(e) || is_mx(e); }
+// Layer l of a quantised encoder runs the precision esm_set_layer_precision
+// gave it (the encoder's own by default).
+int32_t layer_precision(const esm_encoder* e, int32_t l) {
+  return l >= 0 && (size_t)l < e->layer_prec.size() ? e->layer_prec[(size_t)l] : ESM_PRECISION_BF16;
 }
+bool layer_fp8(const esm_encoder* e, int32_t l) { return layer_precision(e, l) == ESM_PRECISION_FP8_DELAYED; }
+bool layer_mx(const esm_encoder* e, int32_t l) { return layer_precision(e, l) == ESM_PRECISION_MXFP4; }
+
 
 // MXFP4 operand: codes [rows, K / 2] then, 256-byte aligned, the block scales
 // [K / 256][rows rounded up to even][8] (the esm_mxfp4_quantize layout).
@@ -374,19 +395,48 @@ esm_status fp8_create(esm_encoder* e) {
   e->w8_layer = align256(w8_offsets(c).total);
   const size_t L = (size_t)(c.num_hidden_layers > 0 ? c.num_hidden_layers : 1);
   HIP_TRY(hipMalloc((void**)&e->w8, L * e->w8_layer), "fp8 weights");
-  e->prepared.assign(L, 0);
-  e->layer_prec.assign(L, ESM_PRECISION_FP8_DELAYED);
-  std::vector<int32_t> on(L, 1);
+  e->prepared8.assign(L, 0);
+  std::vector<int32_t> on(L);
+  for (size_t l = 0; l < L; ++l) on[l] = layer_fp8(e, (int32_t)l);
   HIP_TRY(hipMemcpy(e->f8.layer_on, on.data(), L * sizeof(int32_t), hipMemcpyHostToDevice), "fp8 layer flags");
   return fp8_reset_state(e);
 }
 
-esm_status check_fp8_layer(const esm_encoder* e, int32_t l) {
+// The delayed-scaling state and E4M3 weight store, on first need.
+esm_status ensure_fp8(esm_encoder* e) {
+  if (e->fp8_mem) return ok();
+  esm_status s = check_fp8_shape(&e->cfg);
+  if (s) return s;
+  s = fp8_create(e);
+  if (s) {
+    if (e->fp8_mem) (void)hipFree(e->fp8_mem);
+    if (e->w8) (void)hipFree(e->w8);
+    e->fp8_mem = nullptr;
+    e->w8 = nullptr;
+  }
+  return s;
+}
+
+// The MXFP4 weight store, on first need.
+esm_status ensure_mx(esm_encoder* e) {
+  if (e->w4) return ok();
+  esm_status s = check_mx_shape(&e->cfg);
+  if (s) return s;
+  const size_t L = (size_t)(e->cfg.num_hidden_layers > 0 ? e->cfg.num_hidden_layers : 1);
+  e->w4_layer = align256(w4_offsets(e->cfg).total);
+  HIP_TRY(hipMalloc((void**)&e->w4, L * e->w4_layer), "MXFP4 weights");
+  e->prepared4.assign(L, 0);
+  return ok();
+}
+
+// A quantised layer needs its weights in its own format.
+esm_status check_quant_layer(const esm_encoder* e, int32_t l) {
   if (l < 0 || l >= e->cfg.num_hidden_layers)
     return fail(ESM_ERR_SHAPE, "layer_idx %d outside [0, num_hidden_layers = %d)", l, e->cfg.num_hidden_layers);
-  if (!e->prepared[(size_t)l])
-    return fail(ESM_ERR_STATE, "%s weights of layer %d not prepared (%s)", is_mx(e) ? "MXFP4" : "FP8", l,
-                is_mx(e) ? "esm_mxfp4_prepare_layer" : "esm_fp8_prepare_layer");
+  if (layer_fp8(e, l) && (!e->fp8_mem || !e->prepared8[(size_t)l]))
+    return fail(ESM_ERR_STATE, "FP8 weights of layer %d not prepared (esm_fp8_prepare_layer)", l);
+  if (layer_mx(e, l) && (!e->w4 || !e->prepared4[(size_t)l]))
+    return fail(ESM_ERR_STATE, "MXFP4 weights of layer %d not prepared (esm_mxfp4_prepare_layer)", l);
   return ok();
 }
 
@@ -708,7 +758,7 @@ esm_status run_layer(esm_encoder* e, const esm_layer_weights* w, int32_t li, con
 
 // FP8: the call was one step for the layers it ran; roll their histories.
 esm_status end_of_step(esm_encoder* e, int nlayers, int32_t layer_idx, hipStream_t st) {
-  if (!is_fp8(e) || nlayers == 0) return ok();
+  if (!e->fp8_mem || nlayers == 0) return ok();
   const int32_t l0 = layer_idx >= 0 ? layer_idx : 0;
   return timed(e, ESM_K_FP8, st, "fp8 scale update", [&] { return launch_scale_update(e->f8, l0, nlayers, st); });
 }
@@ -743,7 +793,7 @@ esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, 
   for (int l = 0; l < nlayers; ++l) {
     if ((s = check_weights(&w[l], layer_idx >= 0 ? layer_idx : l))) return s;
     if ((layer_fp8(e, layer_idx >= 0 ? layer_idx : l) || layer_mx(e, layer_idx >= 0 ? layer_idx : l)) &&
-        (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l)))
+        (s = check_quant_layer(e, layer_idx >= 0 ? layer_idx : l)))
       return s;
   }
   if ((s = check_cu_host(e, cu_host, B, T, max_seqlen))) return s;
@@ -802,7 +852,7 @@ esm_status forward_bshd(esm_encoder* e, const esm_layer_weights* w, int nlayers,
   for (int l = 0; l < nlayers; ++l) {
     if ((s = check_weights(&w[l], layer_idx >= 0 ? layer_idx : l))) return s;
     if ((layer_fp8(e, layer_idx >= 0 ? layer_idx : l) || layer_mx(e, layer_idx >= 0 ? layer_idx : l)) &&
-        (s = check_fp8_layer(e, layer_idx >= 0 ? layer_idx : l)))
+        (s = check_quant_layer(e, layer_idx >= 0 ? layer_idx : l)))
       return s;
   }
   if (sl_host && (s = esm_check_seqlens(sl_host, B, S, e->cfg.max_position_embeddings))) return s;
@@ -892,20 +942,11 @@ esm_status esm_encoder_create(const esm_config* cfg, int device, esm_encoder** o
     delete e;
     return hip_fail(err, "rotary table");
   }
-  if (is_fp8(e) && (s = fp8_create(e)) != ESM_OK) {
+  if (is_quantised(e))
+    e->layer_prec.assign((size_t)(cfg->num_hidden_layers > 0 ? cfg->num_hidden_layers : 1), cfg->precision);
+  if ((is_fp8(e) && (s = ensure_fp8(e)) != ESM_OK) || (is_mx(e) && (s = ensure_mx(e)) != ESM_OK)) {
     esm_encoder_destroy(e);
     return s;
-  }
-  if (is_mx(e)) {
-    const size_t L = (size_t)(cfg->num_hidden_layers > 0 ? cfg->num_hidden_layers : 1);
-    e->w4_layer = align256(w4_offsets(*cfg).total);
-    err = hipMalloc((void**)&e->w4, L * e->w4_layer);
-    if (err != hipSuccess) {
-      esm_encoder_destroy(e);
-      return hip_fail(err, "MXFP4 weights");
-    }
-    e->prepared.assign(L, 0);
-    e->layer_prec.assign(L, ESM_PRECISION_MXFP4);
   }
   if (cfg->vocab_size <= kHeadMaxVocab) {
     e->vocab_pad = (cfg->vocab_size + 63) / 64 * 64;
@@ -1549,12 +1590,13 @@ esm_status esm_linear_e4m3_fwd(esm_encoder* e, const void* x8, const float* x_sc
 esm_status esm_fp8_prepare_layer(esm_encoder* e, int32_t layer_idx, const esm_layer_weights* w, esm_stream_t stream) {
   g_last_error.clear();
   if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
-  if (!is_fp8(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
+  if (!is_quantised(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
   if (layer_idx < 0 || layer_idx >= e->cfg.num_hidden_layers)
     return fail(ESM_ERR_SHAPE, "layer_idx %d outside [0, %d)", layer_idx, e->cfg.num_hidden_layers);
   esm_status s = check_weights(w, layer_idx);
   if (s) return s;
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  if ((s = ensure_fp8(e))) return s;
   hipStream_t st = (hipStream_t)stream;
   const esm_config& c = e->cfg;
   const int64_t H = c.hidden_size, F = c.intermediate_size;
@@ -1574,7 +1616,7 @@ esm_status esm_fp8_prepare_layer(esm_encoder* e, int32_t layer_idx, const esm_la
               [&] { return launch_quantize_weight(src[i], n[i], wam + i, w8 + off[i], wsc + i, st); });
     if (s) return s;
   }
-  e->prepared[(size_t)layer_idx] = 1;
+  e->prepared8[(size_t)layer_idx] = 1;
   return ok();
 }
 
@@ -1618,12 +1660,13 @@ esm_status esm_mxfp4_prepare_layer(esm_encoder* e, int32_t layer_idx, const esm_
                                    esm_stream_t stream) {
   g_last_error.clear();
   if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
-  if (!is_mx(e)) return fail(ESM_ERR_STATE, "encoder was not created with MXFP4 precision");
+  if (!is_quantised(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
   if (layer_idx < 0 || layer_idx >= e->cfg.num_hidden_layers)
     return fail(ESM_ERR_SHAPE, "layer_idx %d outside [0, %d)", layer_idx, e->cfg.num_hidden_layers);
   esm_status s = check_weights(w, layer_idx);
   if (s) return s;
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  if ((s = ensure_mx(e))) return s;
   hipStream_t st = (hipStream_t)stream;
   const esm_config& c = e->cfg;
   const int64_t H = c.hidden_size, F = c.intermediate_size;
@@ -1639,13 +1682,13 @@ esm_status esm_mxfp4_prepare_layer(esm_encoder* e, int32_t layer_idx, const esm_
     });
     if (s) return s;
   }
-  e->prepared[(size_t)layer_idx] = 1;
+  e->prepared4[(size_t)layer_idx] = 1;
   return ok();
 }
 
 static esm_status check_state_arg(const esm_encoder* e, const esm_fp8_state* st) {
   if (!e || !st) return fail(ESM_ERR_NULL, "encoder or state is NULL");
-  if (!is_fp8(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
+  if (!e->fp8_mem) return fail(ESM_ERR_STATE, "encoder has no FP8 state (bf16, or MXFP4 with no FP8 layer)");
   if (st->num_layers != e->cfg.num_hidden_layers || st->history_len != e->cfg.amax_history_len)
     return fail(ESM_ERR_SHAPE, "state is for %d layers x history %d; the encoder has %d x %d", st->num_layers,
                 st->history_len, e->cfg.num_hidden_layers, e->cfg.amax_history_len);
@@ -1700,7 +1743,7 @@ esm_status esm_fp8_set_state(esm_encoder* e, const esm_fp8_state* st, esm_stream
 esm_status esm_fp8_reset(esm_encoder* e, esm_stream_t stream) {
   g_last_error.clear();
   if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
-  if (!is_fp8(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
+  if (!e->fp8_mem) return fail(ESM_ERR_STATE, "encoder has no FP8 state (bf16, or MXFP4 with no FP8 layer)");
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
   HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
   return fp8_reset_state(e);
@@ -1709,22 +1752,31 @@ esm_status esm_fp8_reset(esm_encoder* e, esm_stream_t stream) {
 esm_status esm_set_layer_precision(esm_encoder* e, const int32_t* prec, int32_t n, esm_stream_t stream) {
   g_last_error.clear();
   if (!e || !prec) return fail(ESM_ERR_NULL, "NULL argument");
-  if (!is_fp8(e) && !is_mx(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
+  if (!is_quantised(e)) return fail(ESM_ERR_STATE, "encoder was created with bf16 precision");
   if (n != e->cfg.num_hidden_layers)
     return fail(ESM_ERR_SHAPE, "%d precisions for %d layers", n, e->cfg.num_hidden_layers);
-  const int32_t own = e->cfg.precision;
-  std::vector<int32_t> on((size_t)n);
+  bool any8 = false, any4 = false;
   for (int32_t l = 0; l < n; ++l) {
-    if (prec[l] != ESM_PRECISION_BF16 && prec[l] != own)
-      return fail(ESM_ERR_UNSUPPORTED, "layer %d: precision %d (this encoder runs %d or bf16)", l, prec[l], own);
-    on[(size_t)l] = prec[l] == ESM_PRECISION_FP8_DELAYED;
+    if (prec[l] != ESM_PRECISION_BF16 && prec[l] != ESM_PRECISION_FP8_DELAYED && prec[l] != ESM_PRECISION_MXFP4)
+      return fail(ESM_ERR_UNSUPPORTED, "layer %d: precision %d", l, prec[l]);
+    any8 |= prec[l] == ESM_PRECISION_FP8_DELAYED;
+    any4 |= prec[l] == ESM_PRECISION_MXFP4;
   }
+  esm_status s;
+  if (any8 && (s = check_fp8_shape(&e->cfg))) return s;
+  if (any4 && (s = check_mx_shape(&e->cfg))) return s;
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
   HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
-  if (is_fp8(e))
+  e->layer_prec.assign(prec, prec + n);
+  // An FP8 layer needs the delayed-scaling state; the state's per-layer flags
+  // say which layers record amax and roll their history.
+  if (any8 && (s = ensure_fp8(e))) return s;
+  if (e->fp8_mem) {
+    std::vector<int32_t> on((size_t)n);
+    for (int32_t l = 0; l < n; ++l) on[(size_t)l] = prec[l] == ESM_PRECISION_FP8_DELAYED;
     HIP_TRY(hipMemcpy(e->f8.layer_on, on.data(), on.size() * sizeof(int32_t), hipMemcpyHostToDevice),
             "layer flags");
-  e->layer_prec.assign(prec, prec + n);
+  }
   return ok();
 }
 

@@ -643,7 +643,8 @@ class Encoder:
         _call("esm_fp8_reset", self._h, _stream(stream))
 
     def set_layer_precision(self, precisions: Sequence[str], stream=None) -> None:
-        """Per-layer precision of an FP8 encoder: "fp8" or "bf16" for every layer."""
+        """Per-layer precision of an FP8 or MXFP4 encoder: "fp8", "mxfp4" or "bf16"
+        for every layer, in any mix."""
         arr = np.ascontiguousarray(np.array([PRECISION[p] for p in precisions], np.int32))
         _call("esm_set_layer_precision", self._h, arr.ctypes.data_as(ctypes.c_void_p), len(arr), _stream(stream))
 
