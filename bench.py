@@ -22,8 +22,9 @@ synthetic MSA-row shape under "biased_attention", the MXFP4 quantiser and
 GEMM (the FP4 recipe) on the layer's four GEMM shapes under "mxfp4", the
 whole stack with MXFP4 GEMMs under "mxfp4_stack", the attention backward
 on the batch's sequences under "attention_bwd", the linear backward on the
-layer's four shapes under "linear_bwd" and the LayerNorm backward on [T, H]
-under "layernorm_bwd".
+layer's four shapes under "linear_bwd", the LayerNorm backward on [T, H]
+under "layernorm_bwd", and one 650M layer's training forward and backward
+(esm_layer_fwd_train, esm_layer_bwd) on the batch under "layer_train".
 Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
@@ -82,6 +83,8 @@ def parse():
     ap.add_argument("--no-biased-attention", action="store_true",
                     help="skip timing the biased (Evoformer MSA-row) attention kernel")
     ap.add_argument("--no-mxfp4", action="store_true", help="skip timing the MXFP4 GEMMs on the layer shapes")
+    ap.add_argument("--no-layer-train", action="store_true",
+                    help="skip one layer's training forward and backward (esm_layer_fwd_train, esm_layer_bwd)")
     ap.add_argument("--no-vendor-gemm", action="store_true", help="skip the hipBLASLt fc1-shape reference timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference dispatch for HBM byte counters)")
@@ -352,6 +355,66 @@ def bench_linear_bwd(enc, T: int, H: int, F: int, steps: int, dev: str, stream) 
                                   "flops_per_launch": fl}}
         del x, w, dy, dx, dw, db, ws
     return out
+
+
+def bench_layer_train(enc, batch, cu, weights, m, steps: int, dev: str, stream) -> dict:
+    """One layer's training forward (esm_layer_fwd_train: the forward keeping
+    the activations its backward takes) and backward (esm_layer_bwd: dx and
+    the 12 parameter gradients) on the batch, the 650M layer's widths and
+    layer 0's weights, x and dy N(0, 1) bf16; HIP events on the library stream
+    around back-to-back calls.  Algorithmic flops: the forward's (linears
+    2 T (4 H^2 + 2 H F), attention 4 H sum L^2), the backward's twice the
+    linears' and 2.5 times the attention's; a 33-layer training step is
+    projected as 33 times forward plus backward."""
+    import torch
+    T, B, H, F = batch.T, batch.B, m.hidden, m.ffn
+    g = torch.Generator(device=dev).manual_seed(13)
+    x = torch.randn((T, H), device=dev, generator=g).to(torch.bfloat16)
+    dy = torch.randn((T, H), device=dev, generator=g).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    saved = torch.empty((enc.saved_size(T),), dtype=torch.uint8, device=dev)
+    ws = enc.workspace(T, B)
+    bws = enc.layer_bwd_workspace(T, B)
+    grads = None
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(10, steps)
+
+    def fwd():
+        enc.layer_fwd_train(weights, x, cu, B, T, batch.max_seqlen, x_out=y, saved=saved, workspace=ws, stream=stream)
+
+    def bwd():
+        nonlocal grads
+        _, grads = enc.layer_bwd(weights, x, saved, dy, cu, B, T, dx=dx, grads=grads, workspace=bws, stream=stream)
+
+    res = {}
+    for name, call in (("fwd_train", fwd), ("bwd", bwd)):
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / n
+    lin = 2.0 * T * (4 * H * H + 2 * H * F)
+    att = 4.0 * H * int((batch.lengths.astype(np.int64) ** 2).sum())
+    fl_f, fl_b = lin + att, 2.0 * lin + 2.5 * att
+    tf_f = fl_f / (res["fwd_train"] * 1e-3) / 1e12
+    tf_b = fl_b / (res["bwd"] * 1e-3) / 1e12
+    per_layer = res["fwd_train"] + res["bwd"]
+    tf_t = (fl_f + fl_b) / (per_layer * 1e-3) / 1e12
+    del x, dy, y, dx, saved, ws, bws, grads
+    return {"what": "esm_layer_fwd_train then esm_layer_bwd, one 650M-width layer on the batch, inputs N(0, 1) bf16",
+            "fwd_train_ms": round(res["fwd_train"], 4), "bwd_ms": round(res["bwd"], 4),
+            "fwd_tflops": round(tf_f, 1), "bwd_tflops": round(tf_b, 1), "tflops": round(tf_t, 1),
+            "bwd_over_fwd": round(res["bwd"] / res["fwd_train"], 3),
+            "projected_33_layer_train_step_ms": round(33 * per_layer, 2),
+            "projected_residues_per_s": round(T / (33 * per_layer * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf_t, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf_t / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                         "flops_per_launch": fl_f + fl_b}}
 
 
 def bench_layernorm_bwd(enc, T: int, H: int, steps: int, dev: str, stream) -> dict:
@@ -683,6 +746,10 @@ def main():
         lin_bwd = bench_linear_bwd(enc, T, m.hidden, m.ffn, args.steps, dev, stream)
         ln_bwd = bench_layernorm_bwd(enc, T, m.hidden, args.steps, dev, stream)
 
+    layer_train = None
+    if not args.no_layer_train and m.hidden == 1280:
+        layer_train = bench_layer_train(enc, batch, cu, weights[0], m, args.steps, dev, stream)
+
     mxfp4 = None
     if not args.no_mxfp4:
         mxfp4 = bench_mxfp4(enc, T, m.hidden, m.ffn, args.steps, dev, stream)
@@ -813,6 +880,7 @@ def main():
         "attention_bwd": attn_bwd,
         "linear_bwd": lin_bwd,
         "layernorm_bwd": ln_bwd,
+        "layer_train": layer_train,
         "mxfp4_stack": mx_stack,
         "vendor_gemm_fc1": vendor,
         "fp8": fp8,

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 17
+#define ESM_ABI_VERSION 18
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -513,6 +513,82 @@ esm_status esm_gelu_bwd(esm_encoder* enc, const void* z, const void* dy, void* d
 esm_status esm_qkv_rope_bwd(esm_encoder* enc, const void* dqkv, void* dy,
                             const int32_t* cu_seqlens_dev, int32_t B, int64_t T,
                             void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* ------------------------------------------------------------ training layer
+ *
+ * One layer's forward for training and its backward from the activations the
+ * forward keeps (the pages time training: [BIO-ACC] 3.2 and 6, [CARD] 训练性能;
+ * the steps are those of the per-step backward entries above, chained in
+ * reverse order of the forward).  bf16 encoders only (ESM_ERR_UNSUPPORTED for
+ * an FP8 or MXFP4 encoder).
+ *
+ * Saved activations, one caller-owned device buffer of esm_layer_saved_size
+ * bytes (256-byte aligned); region r starts at the offset
+ * esm_layer_saved_region gives:
+ *   ESM_SAVED_H1   bf16 [T, H]              LN1 output
+ *   ESM_SAVED_QKV  bf16 [3, heads, T, 64]   rotated q, rotated k, v (planar)
+ *   ESM_SAVED_CTX  bf16 [T, H]              attention context
+ *   ESM_SAVED_LSE  fp32 [heads, T]          softmax normaliser (as esm_attention_fwd_lse)
+ *   ESM_SAVED_X1   bf16 [T, H]              residual stream after the attention block
+ *   ESM_SAVED_H2   bf16 [T, H]              LN2 output
+ *   ESM_SAVED_Z    bf16 [T, F]              fc1 output before GELU
+ *   ESM_SAVED_A    bf16 [T, F]              GELU(z), fc2's input
+ * (650M widths: 19,200 bytes per residue plus 80 of lse.) */
+typedef enum {
+  ESM_SAVED_H1 = 0, ESM_SAVED_QKV = 1, ESM_SAVED_CTX = 2, ESM_SAVED_LSE = 3, ESM_SAVED_X1 = 4,
+  ESM_SAVED_H2 = 5, ESM_SAVED_Z = 6, ESM_SAVED_A = 7, ESM_SAVED_COUNT = 8
+} esm_saved_region;
+
+/* Bytes of the saved activations of one layer for T rows (host only). */
+esm_status esm_layer_saved_size(const esm_encoder* enc, int64_t T, size_t* bytes);
+/* Offset and size of region r inside them (host only); ESM_ERR_SHAPE for r
+ * outside [0, ESM_SAVED_COUNT). */
+esm_status esm_layer_saved_region(const esm_encoder* enc, int64_t T, int32_t r, size_t* offset, size_t* bytes);
+
+/* Training forward of layer layer_idx: x_out as esm_layer_fwd computes it,
+ * except that the GELU is applied to z as stored in bf16 (the value the
+ * backward differentiates at), and the activations listed above written to
+ * saved.  Arguments and workspace (esm_workspace_size(T, B)) as
+ * esm_layer_fwd; a layer prepared by esm_prepare_layer still runs its
+ * LayerNorms as separate passes here (their outputs are saved).  The
+ * backward takes x_in again: x_out may alias x_in only if the caller keeps a
+ * copy.  ESM_ERR_WORKSPACE when saved is NULL, misaligned or smaller than
+ * esm_layer_saved_size(T).  Asynchronous on stream. */
+esm_status esm_layer_fwd_train(esm_encoder* enc, const esm_layer_weights* w, int32_t layer_idx,
+                               const void* x_in, void* x_out, const int32_t* cu_seqlens_dev,
+                               const int32_t* cu_seqlens_host, int32_t B, int64_t T, int32_t max_seqlen,
+                               void* saved, size_t saved_bytes, void* workspace, size_t workspace_bytes,
+                               esm_stream_t stream);
+
+/* Gradients of one layer's parameters: weights bf16 in the weights' own
+ * layouts ([out, in]), biases and LayerNorm vectors fp32.  All required. */
+typedef struct {
+  float* ln1_gamma; float* ln1_beta;   /* [H] */
+  void* w_qkv; float* b_qkv;           /* [3H, H], [3H] */
+  void* w_out; float* b_out;           /* [H, H], [H] */
+  float* ln2_gamma; float* ln2_beta;   /* [H] */
+  void* w_fc1; float* b_fc1;           /* [F, H], [F] */
+  void* w_fc2; float* b_fc2;           /* [H, F], [H] */
+} esm_layer_grads;
+
+/* Workspace bytes esm_layer_bwd needs for T rows in B sequences (host only). */
+esm_status esm_layer_bwd_workspace_size(const esm_encoder* enc, int64_t T, int32_t B, size_t* bytes);
+
+/* Backward of layer layer_idx from esm_layer_fwd_train's saved activations
+ * (same T, B and cu_seqlens) and its input x_in: given dy = dL/dx_out (bf16
+ * [T, H]) writes dx = dL/dx_in (bf16 [T, H]) and every parameter gradient in
+ * g.  Order: fc2 (dA, dW_fc2, db_fc2), GELU (dZ at the saved z), fc1, LN2
+ * (plus dy through the residual: dX1), out-projection, attention (from the
+ * saved lse), the QKV split and rotary embedding, the QKV linear, LN1 (plus
+ * dX1 through the residual: dx).  The residual gradients join the LayerNorm
+ * gradients in fp32 and are rounded to bf16 once.  dx may alias dy.
+ * Workspace: esm_layer_bwd_workspace_size(T, B) bytes, 256-byte aligned.
+ * Deterministic (fixed-order sums, no atomics).  Errors as esm_layer_fwd_train
+ * (ESM_ERR_NULL for a NULL gradient pointer).  Asynchronous on stream. */
+esm_status esm_layer_bwd(esm_encoder* enc, const esm_layer_weights* w, int32_t layer_idx, const void* x_in,
+                         const void* saved, size_t saved_bytes, const void* dy, void* dx, const esm_layer_grads* g,
+                         const int32_t* cu_seqlens_dev, int32_t B, int64_t T, void* workspace,
+                         size_t workspace_bytes, esm_stream_t stream);
 
 esm_status esm_layernorm_fwd(esm_encoder* enc, const void* x, const void* gamma,
                              const void* beta, void* y, int64_t M, esm_stream_t stream);

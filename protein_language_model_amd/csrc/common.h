@@ -404,10 +404,12 @@ hipError_t launch_split_reduce(const float* part, int32_t S, int64_t n, bf16_t* 
 // dqkv [3, heads, T, 64] -> dy [T, 3H] in the fused QKV linear's interleaved
 // column order, q and k rotated back by the row positions pos [T].
 hipError_t launch_gelu_bwd(const bf16_t* z, const bf16_t* dy, bf16_t* dz, int64_t n, hipStream_t st);
+// a = GELU(z) elementwise (the fc1 epilogue's GELU), bf16 in and out; n a multiple of 8
+hipError_t launch_gelu_fwd(const bf16_t* z, bf16_t* a, int64_t n, hipStream_t st);
 hipError_t launch_qkv_rope_bwd(const bf16_t* dqkv, const int32_t* pos, const float2* rope, int32_t max_positions,
                                int64_t T, int32_t heads, bf16_t* dy, hipStream_t st);
-hipError_t launch_layernorm_bwd(const bf16_t* x, const bf16_t* gamma, const bf16_t* dy, bf16_t* dx, float* dgamma,
-                                float* dbeta, int64_t M, int32_t H, float eps, float* stats, float* part,
+hipError_t launch_layernorm_bwd(const bf16_t* x, const bf16_t* gamma, const bf16_t* dy, const bf16_t* dres, bf16_t* dx,
+                                float* dgamma, float* dbeta, int64_t M, int32_t H, float eps, float* stats, float* part,
                                 hipStream_t st);
 
 // Biased attention on [B, N, L, heads, 64] tensors: per (b, n, h),

@@ -1453,8 +1453,8 @@ esm_status esm_layernorm_bwd(esm_encoder* e, const void* x, const void* gamma, c
   float* stats = (float*)ws;
   float* part = (float*)((char*)ws + ln_bwd_stats_bytes(M));
   return timed(e, ESM_K_LINEAR_BWD, st, "layernorm backward", [&] {
-    return launch_layernorm_bwd((const bf16_t*)x, (const bf16_t*)gamma, (const bf16_t*)dy, (bf16_t*)dx, dgamma, dbeta,
-                                M, H, e->cfg.layer_norm_eps, stats, part, st);
+    return launch_layernorm_bwd((const bf16_t*)x, (const bf16_t*)gamma, (const bf16_t*)dy, nullptr, (bf16_t*)dx, dgamma,
+                                dbeta, M, H, e->cfg.layer_norm_eps, stats, part, st);
   });
 }
 
@@ -1521,6 +1521,269 @@ esm_status esm_qkv_rope_bwd(esm_encoder* e, const void* dqkv, void* dy, const in
   return timed(e, ESM_K_LINEAR_BWD, st, "qkv rope backward", [&] {
     return launch_qkv_rope_bwd((const bf16_t*)dqkv, pos, e->rope, e->cfg.max_position_embeddings, T,
                                e->cfg.num_attention_heads, (bf16_t*)dy, st);
+  });
+}
+
+// ---------------------------------------------------------------- training layer
+
+namespace {
+
+// Saved activations of one layer: the regions of esm_saved_region in order,
+// each 256-byte aligned.
+struct SavedPlan {
+  size_t off[ESM_SAVED_COUNT], size[ESM_SAVED_COUNT], total;
+};
+SavedPlan saved_plan(const esm_config& c, int64_t T) {
+  const size_t t = (size_t)(T > 0 ? T : 0), H = (size_t)c.hidden_size, F = (size_t)c.intermediate_size;
+  const size_t nh = (size_t)c.num_attention_heads;
+  const size_t sz[ESM_SAVED_COUNT] = {t * H * 2, 3 * t * H * 2, t * H * 2, nh * t * 4,
+                                      t * H * 2, t * H * 2, t * F * 2, t * F * 2};
+  SavedPlan p;
+  size_t o = 0;
+  for (int i = 0; i < ESM_SAVED_COUNT; ++i) {
+    p.off[i] = o;
+    p.size[i] = sz[i];
+    o += align256(sz[i]);
+  }
+  p.total = o;
+  return p;
+}
+
+// Backward workspace: the forward plan (segment table and positions; its
+// activation regions hold the gradients of the same shapes), then delta
+// [heads, T] fp32, dA [T, F] bf16 (later the QKV output gradient [T, 3H]; sized
+// for the larger), and the linear and LayerNorm backward workspaces.
+struct BwdPlan {
+  Plan fwd;
+  size_t delta, da, lin, lin_bytes, ln, ln_bytes, total;
+};
+BwdPlan bwd_plan(const esm_config& c, int64_t T, int32_t B) {
+  BwdPlan b;
+  b.fwd = make_plan(c, T, B);
+  const int64_t t = T > 0 ? T : 0;
+  const int32_t H = c.hidden_size, F = c.intermediate_size;
+  size_t o = b.fwd.total;
+  b.delta = o;
+  o += align256((size_t)c.num_attention_heads * (size_t)t * 4);
+  b.da = o;
+  o += align256((size_t)t * (size_t)(F > 3 * H ? F : 3 * H) * 2);
+  b.lin = o;
+  b.lin_bytes = lin_bwd_plan(t, 3 * H, H).total;
+  const size_t others[3] = {lin_bwd_plan(t, H, H).total, lin_bwd_plan(t, F, H).total, lin_bwd_plan(t, H, F).total};
+  for (size_t v : others) b.lin_bytes = v > b.lin_bytes ? v : b.lin_bytes;
+  o += align256(b.lin_bytes);
+  b.ln = o;
+  b.ln_bytes = ln_bwd_ws_bytes(t, H);
+  o += align256(b.ln_bytes);
+  b.total = o;
+  return b;
+}
+
+esm_status check_train_call(const esm_encoder* e, const esm_layer_weights* w, int32_t layer_idx, int64_t T,
+                            int32_t B) {
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  if (is_quantised(e)) return fail(ESM_ERR_UNSUPPORTED, "the training layer entries run bf16 encoders");
+  esm_status s = check_rows(e, T, B);
+  if (s) return s;
+  if (layer_idx < 0 || layer_idx >= e->cfg.num_hidden_layers)
+    return fail(ESM_ERR_SHAPE, "layer_idx %d outside [0, %d)", layer_idx, e->cfg.num_hidden_layers);
+  return check_weights(w, layer_idx);
+}
+
+}  // namespace
+
+esm_status esm_layer_saved_size(const esm_encoder* e, int64_t T, size_t* bytes) {
+  g_last_error.clear();
+  if (!e || !bytes) return fail(ESM_ERR_NULL, "NULL argument");
+  if (T < 0) return fail(ESM_ERR_SHAPE, "T < 0");
+  *bytes = saved_plan(e->cfg, T).total;
+  return ok();
+}
+
+esm_status esm_layer_saved_region(const esm_encoder* e, int64_t T, int32_t r, size_t* offset, size_t* bytes) {
+  g_last_error.clear();
+  if (!e || !offset || !bytes) return fail(ESM_ERR_NULL, "NULL argument");
+  if (T < 0) return fail(ESM_ERR_SHAPE, "T < 0");
+  if (r < 0 || r >= ESM_SAVED_COUNT) return fail(ESM_ERR_SHAPE, "saved region %d outside [0, %d)", r, ESM_SAVED_COUNT);
+  const SavedPlan sp = saved_plan(e->cfg, T);
+  *offset = sp.off[r];
+  *bytes = sp.size[r];
+  return ok();
+}
+
+esm_status esm_layer_bwd_workspace_size(const esm_encoder* e, int64_t T, int32_t B, size_t* bytes) {
+  g_last_error.clear();
+  if (!e || !bytes) return fail(ESM_ERR_NULL, "NULL argument");
+  if (T < 0 || B < 0) return fail(ESM_ERR_SHAPE, "negative T or B");
+  *bytes = bwd_plan(e->cfg, T, B).total;
+  return ok();
+}
+
+esm_status esm_layer_fwd_train(esm_encoder* e, const esm_layer_weights* w, int32_t layer_idx, const void* x_in,
+                               void* x_out, const int32_t* cu_dev, const int32_t* cu_host, int32_t B, int64_t T,
+                               int32_t max_seqlen, void* saved, size_t saved_bytes, void* ws, size_t ws_bytes,
+                               esm_stream_t stream) {
+  g_last_error.clear();
+  esm_status s = check_train_call(e, w, layer_idx, T, B);
+  if (s) return s;
+  if (!x_in || !x_out || !cu_dev) return fail(ESM_ERR_NULL, "x_in, x_out or cu_seqlens_dev is NULL");
+  if (!aligned16(x_in) || !aligned16(x_out)) return fail(ESM_ERR_UNSUPPORTED, "x_in/x_out not 16-byte aligned");
+  if ((s = check_cu_host(e, cu_host, B, T, max_seqlen))) return s;
+  const SavedPlan sp = saved_plan(e->cfg, T);
+  if (!saved || ((uintptr_t)saved & 255u) || saved_bytes < sp.total)
+    return fail(ESM_ERR_WORKSPACE, "saved activations: NULL, not 256-byte aligned or %zu bytes < %zu", saved_bytes,
+                sp.total);
+  if (T == 0 || B == 0) return ok();
+  Plan p;
+  if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  if ((s = run_segments(e, 0, cu_dev, B, T, 0, ws, p, st))) return s;
+  const esm_config& c = e->cfg;
+  const int H = c.hidden_size, F = c.intermediate_size;
+  char* sv = (char*)saved;
+  bf16_t* h1 = (bf16_t*)(sv + sp.off[ESM_SAVED_H1]);
+  bf16_t* qkv = (bf16_t*)(sv + sp.off[ESM_SAVED_QKV]);
+  bf16_t* ctx = (bf16_t*)(sv + sp.off[ESM_SAVED_CTX]);
+  float* lse = (float*)(sv + sp.off[ESM_SAVED_LSE]);
+  bf16_t* x1 = (bf16_t*)(sv + sp.off[ESM_SAVED_X1]);
+  bf16_t* h2 = (bf16_t*)(sv + sp.off[ESM_SAVED_H2]);
+  bf16_t* z = (bf16_t*)(sv + sp.off[ESM_SAVED_Z]);
+  bf16_t* a = (bf16_t*)(sv + sp.off[ESM_SAVED_A]);
+  const E4m3Out none{nullptr, nullptr, nullptr, nullptr};
+
+  s = timed(e, ESM_K_LAYERNORM, st, "layernorm 1", [&] {
+    return launch_layernorm((const bf16_t*)x_in, (const bf16_t*)w->ln1_gamma, (const bf16_t*)w->ln1_beta, h1, T, H,
+                            c.layer_norm_eps, none, st);
+  });
+  if (s) return s;
+  GemmArgs g{};
+  g.dtype = kBF16;
+  g.M = T;
+  g.pos = region<int32_t>(ws, p, ESM_WS_POS);
+  g.rope = e->rope;
+  g.max_positions = c.max_position_embeddings;
+  g.x = h1; g.w = w->w_qkv; g.bias = (const bf16_t*)w->b_qkv; g.y = qkv;
+  g.N = 3 * H; g.K = H;
+  s = timed(e, ESM_K_GEMM_QKV, st, "qkv gemm", [&] { return launch_gemm(EPI_QKV_ROPE, g, st); });
+  if (s) return s;
+  AttnArgs aa{};
+  aa.qkv = qkv; aa.ctx = ctx; aa.lse = lse;
+  aa.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
+  aa.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
+  aa.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
+  aa.tile_cap = tile_cap(T, B);
+  aa.T = T; aa.heads = c.num_attention_heads;
+  s = timed(e, ESM_K_ATTENTION, st, "attention", [&] { return launch_attention(aa, st); });
+  if (s) return s;
+  g.x = ctx; g.w = w->w_out; g.bias = (const bf16_t*)w->b_out; g.res = (const bf16_t*)x_in; g.y = x1;
+  g.N = H; g.K = H;
+  s = timed(e, ESM_K_GEMM_OUT, st, "out-proj gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
+  if (s) return s;
+  s = timed(e, ESM_K_LAYERNORM, st, "layernorm 2", [&] {
+    return launch_layernorm(x1, (const bf16_t*)w->ln2_gamma, (const bf16_t*)w->ln2_beta, h2, T, H, c.layer_norm_eps,
+                            none, st);
+  });
+  if (s) return s;
+  g.x = h2; g.w = w->w_fc1; g.bias = (const bf16_t*)w->b_fc1; g.res = nullptr; g.y = z;
+  g.N = F; g.K = H;
+  s = timed(e, ESM_K_GEMM_FC1, st, "fc1 gemm", [&] { return launch_gemm(EPI_BIAS, g, st); });
+  if (s) return s;
+  s = timed(e, ESM_K_OTHER, st, "gelu", [&] { return launch_gelu_fwd(z, a, T * F, st); });
+  if (s) return s;
+  g.x = a; g.w = w->w_fc2; g.bias = (const bf16_t*)w->b_fc2; g.res = x1; g.y = (bf16_t*)x_out;
+  g.N = H; g.K = F;
+  return timed(e, ESM_K_GEMM_FC2, st, "fc2 gemm", [&] { return launch_gemm(EPI_BIAS_RESIDUAL, g, st); });
+}
+
+esm_status esm_layer_bwd(esm_encoder* e, const esm_layer_weights* w, int32_t layer_idx, const void* x_in,
+                         const void* saved, size_t saved_bytes, const void* dy, void* dx, const esm_layer_grads* gr,
+                         const int32_t* cu_dev, int32_t B, int64_t T, void* ws, size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  esm_status s = check_train_call(e, w, layer_idx, T, B);
+  if (s) return s;
+  if (!x_in || !dy || !dx || !gr || !cu_dev) return fail(ESM_ERR_NULL, "x_in, dy, dx, grads or cu_seqlens_dev is NULL");
+  void* const gw[4] = {gr->w_qkv, gr->w_out, gr->w_fc1, gr->w_fc2};
+  float* const gv[8] = {gr->ln1_gamma, gr->ln1_beta, gr->b_qkv, gr->b_out, gr->ln2_gamma, gr->ln2_beta, gr->b_fc1,
+                        gr->b_fc2};
+  for (void* q : gw)
+    if (!q) return fail(ESM_ERR_NULL, "a weight gradient pointer is NULL");
+  for (float* q : gv)
+    if (!q) return fail(ESM_ERR_NULL, "a bias or LayerNorm gradient pointer is NULL");
+  if (!aligned16(x_in) || !aligned16(dy) || !aligned16(dx)) return fail(ESM_ERR_UNSUPPORTED, "x_in/dy/dx not 16-byte aligned");
+  for (void* q : gw)
+    if (!aligned16(q)) return fail(ESM_ERR_UNSUPPORTED, "weight gradient not 16-byte aligned");
+  for (float* q : gv)
+    if ((uintptr_t)q & 3u) return fail(ESM_ERR_UNSUPPORTED, "bias/LayerNorm gradient not 4-byte aligned");
+  const SavedPlan sp = saved_plan(e->cfg, T);
+  if (!saved || ((uintptr_t)saved & 255u) || saved_bytes < sp.total)
+    return fail(ESM_ERR_WORKSPACE, "saved activations: NULL, not 256-byte aligned or %zu bytes < %zu", saved_bytes,
+                sp.total);
+  const BwdPlan bp = bwd_plan(e->cfg, T, B);
+  if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < bp.total)
+    return fail(ESM_ERR_WORKSPACE, "workspace: NULL, not 256-byte aligned or %zu bytes < %zu", ws_bytes, bp.total);
+  if (T == 0 || B == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  if ((s = run_segments(e, 0, cu_dev, B, T, 0, ws, bp.fwd, st))) return s;
+  const esm_config& c = e->cfg;
+  const int32_t H = c.hidden_size, F = c.intermediate_size;
+  const char* sv = (const char*)saved;
+  auto saved_at = [&](int r) { return (const void*)(sv + sp.off[r]); };
+  char* wb = (char*)ws;
+  const Plan& p = bp.fwd;
+  bf16_t* dz = region<bf16_t>(ws, p, ESM_WS_ACT);      // [T, F]
+  bf16_t* dh2 = region<bf16_t>(ws, p, ESM_WS_LN2);     // [T, H]
+  bf16_t* dx1 = region<bf16_t>(ws, p, ESM_WS_X1);      // [T, H]
+  bf16_t* dctx = region<bf16_t>(ws, p, ESM_WS_CTX);    // [T, H]
+  bf16_t* dqkv = region<bf16_t>(ws, p, ESM_WS_QKV);    // [3, heads, T, 64]
+  bf16_t* dh1 = region<bf16_t>(ws, p, ESM_WS_LN1);     // [T, H]
+  float* delta = (float*)(wb + bp.delta);
+  bf16_t* da = (bf16_t*)(wb + bp.da);                  // [T, F], then the QKV output gradient [T, 3H]
+  void* lin = wb + bp.lin;
+  float* ln_stats = (float*)(wb + bp.ln);
+  float* ln_part = (float*)(wb + bp.ln + ln_bwd_stats_bytes(T));
+
+  // fc2: dA = dy W_fc2, dW_fc2 = dy^T A, db_fc2
+  if ((s = esm_linear_bwd(e, saved_at(ESM_SAVED_A), w->w_fc2, dy, da, gr->w_fc2, gr->b_fc2, T, H, F, lin, bp.lin_bytes,
+                          stream)))
+    return s;
+  if ((s = esm_gelu_bwd(e, saved_at(ESM_SAVED_Z), da, dz, T * F, stream))) return s;
+  if ((s = esm_linear_bwd(e, saved_at(ESM_SAVED_H2), w->w_fc1, dz, dh2, gr->w_fc1, gr->b_fc1, T, F, H, lin,
+                          bp.lin_bytes, stream)))
+    return s;
+  // LN2, and dy through the residual: dX1 = dy + LN2'(dh2)
+  s = timed(e, ESM_K_LINEAR_BWD, st, "layernorm backward", [&] {
+    return launch_layernorm_bwd((const bf16_t*)saved_at(ESM_SAVED_X1), (const bf16_t*)w->ln2_gamma, dh2,
+                                (const bf16_t*)dy, dx1, gr->ln2_gamma, gr->ln2_beta, T, H, c.layer_norm_eps, ln_stats,
+                                ln_part, st);
+  });
+  if (s) return s;
+  if ((s = esm_linear_bwd(e, saved_at(ESM_SAVED_CTX), w->w_out, dx1, dctx, gr->w_out, gr->b_out, T, H, H, lin,
+                          bp.lin_bytes, stream)))
+    return s;
+  AttnBwdArgs ab{};
+  ab.qkv = (const bf16_t*)saved_at(ESM_SAVED_QKV); ab.out = (const bf16_t*)saved_at(ESM_SAVED_CTX);
+  ab.dout = dctx; ab.lse = (const float*)saved_at(ESM_SAVED_LSE); ab.delta = delta; ab.dqkv = dqkv;
+  ab.segs = region<int32_t>(ws, p, ESM_WS_SEGS);
+  ab.tiles = region<int32_t>(ws, p, ESM_WS_TILES);
+  ab.ntiles = region<int32_t>(ws, p, ESM_WS_NTILES);
+  ab.tile_cap = tile_cap(T, B);
+  ab.T = T; ab.heads = c.num_attention_heads;
+  if ((s = timed(e, ESM_K_ATTENTION_BWD, st, "attention_bwd", [&] { return launch_attention_bwd(ab, st); }))) return s;
+  bf16_t* dyq = da;   // dA is dead: the QKV linear's output gradient [T, 3H]
+  s = timed(e, ESM_K_LINEAR_BWD, st, "qkv rope backward", [&] {
+    return launch_qkv_rope_bwd(dqkv, region<int32_t>(ws, p, ESM_WS_POS), e->rope, c.max_position_embeddings, T,
+                               c.num_attention_heads, dyq, st);
+  });
+  if (s) return s;
+  if ((s = esm_linear_bwd(e, saved_at(ESM_SAVED_H1), w->w_qkv, dyq, dh1, gr->w_qkv, gr->b_qkv, T, 3 * H, H, lin,
+                          bp.lin_bytes, stream)))
+    return s;
+  // LN1, and dX1 through the residual: dx = dX1 + LN1'(dh1)
+  return timed(e, ESM_K_LINEAR_BWD, st, "layernorm backward", [&] {
+    return launch_layernorm_bwd((const bf16_t*)x_in, (const bf16_t*)w->ln1_gamma, dh1, dx1, (bf16_t*)dx, gr->ln1_gamma,
+                                gr->ln1_beta, T, H, c.layer_norm_eps, ln_stats, ln_part, st);
   });
 }
 

@@ -907,7 +907,27 @@ __global__ __launch_bounds__(256) void k_mfma_peak(int32_t iters, float* __restr
   if (lane == 0) sink[wid] = t;
 }
 
+// a = GELU(z), 8 values per thread: the fc1 epilogue's GELU on values a
+// training forward keeps as bf16 (its backward takes z).
+__global__ __launch_bounds__(256) void k_gelu_fwd(const bf16_t* __restrict__ z, bf16_t* __restrict__ a, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const u32x4 v = *(const u32x4*)(z + 8 * i);
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = pack_bf2(gelu(bflo(v[e])), gelu(bfhi(v[e])));
+  *(u32x4*)(a + 8 * i) = o;
+}
+
 }  // namespace
+
+hipError_t launch_gelu_fwd(const bf16_t* z, bf16_t* a, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(k_gelu_fwd, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, z, a, n8);
+  return hipGetLastError();
+}
 
 hipError_t launch_mfma_peak(int32_t iters, int32_t blocks, float* sink, hipStream_t st) {
   if (iters <= 0 || blocks <= 0) return hipErrorInvalidValue;

@@ -141,8 +141,9 @@ constexpr int kLnMaxCh = 8;  // chunks of 8 per lane: H <= 4096
 // a template argument so that the row lives in as few registers as H needs.
 template <int kLnMaxCh>
 __global__ __launch_bounds__(256) void k_ln_bwd_rows(const bf16_t* __restrict__ x, const bf16_t* __restrict__ gamma,
-                                                     const bf16_t* __restrict__ dy, bf16_t* __restrict__ dx,
-                                                     float* __restrict__ stats, int64_t M, int32_t H, float eps) {
+                                                     const bf16_t* __restrict__ dy, const bf16_t* __restrict__ dres,
+                                                     bf16_t* __restrict__ dx, float* __restrict__ stats, int64_t M,
+                                                     int32_t H, float eps) {
   const int lane = threadIdx.x & 63;
   const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (m >= M) return;   // whole wave: no barrier below
@@ -200,10 +201,20 @@ __global__ __launch_bounds__(256) void k_ln_bwd_rows(const bf16_t* __restrict__ 
   for (int j = 0; j < kLnMaxCh; ++j) {
     const int c = lane + 64 * j;
     if (c < nch) {
+      float d[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d[e] = r * (gv[j][e] - m1 - xv[j][e] * m2);
+      if (dres) {   // a residual branch's gradient joins this one, in fp32, rounded once
+        const u32x4 q = *(const u32x4*)(dres + m * H + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          d[2 * e] += bflo(q[e]);
+          d[2 * e + 1] += bfhi(q[e]);
+        }
+      }
       u32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        o[e] = pack_bf2(r * (gv[j][2 * e] - m1 - xv[j][2 * e] * m2), r * (gv[j][2 * e + 1] - m1 - xv[j][2 * e + 1] * m2));
+      for (int e = 0; e < 4; ++e) o[e] = pack_bf2(d[2 * e], d[2 * e + 1]);
       *(u32x4*)(dr + 8 * c) = o;
     }
   }
@@ -369,18 +380,18 @@ hipError_t launch_qkv_rope_bwd(const bf16_t* dqkv, const int32_t* pos, const flo
   return hipGetLastError();
 }
 
-hipError_t launch_layernorm_bwd(const bf16_t* x, const bf16_t* gamma, const bf16_t* dy, bf16_t* dx, float* dgamma,
-                                float* dbeta, int64_t M, int32_t H, float eps, float* stats, float* part,
+hipError_t launch_layernorm_bwd(const bf16_t* x, const bf16_t* gamma, const bf16_t* dy, const bf16_t* dres, bf16_t* dx,
+                                float* dgamma, float* dbeta, int64_t M, int32_t H, float eps, float* stats, float* part,
                                 hipStream_t st) {
   if (M <= 0) return hipSuccess;
   if (H % 64 || H / 8 > 64 * kLnMaxCh) return hipErrorInvalidValue;
   const int ch = (H / 8 + 63) / 64;
   const dim3 rg((unsigned)((M + 3) / 4));
-  if (ch <= 1) hipLaunchKernelGGL(k_ln_bwd_rows<1>, rg, dim3(256), 0, st, x, gamma, dy, dx, stats, M, H, eps);
-  else if (ch <= 2) hipLaunchKernelGGL(k_ln_bwd_rows<2>, rg, dim3(256), 0, st, x, gamma, dy, dx, stats, M, H, eps);
-  else if (ch <= 3) hipLaunchKernelGGL(k_ln_bwd_rows<3>, rg, dim3(256), 0, st, x, gamma, dy, dx, stats, M, H, eps);
-  else if (ch <= 5) hipLaunchKernelGGL(k_ln_bwd_rows<5>, rg, dim3(256), 0, st, x, gamma, dy, dx, stats, M, H, eps);
-  else hipLaunchKernelGGL(k_ln_bwd_rows<8>, rg, dim3(256), 0, st, x, gamma, dy, dx, stats, M, H, eps);
+  if (ch <= 1) hipLaunchKernelGGL(k_ln_bwd_rows<1>, rg, dim3(256), 0, st, x, gamma, dy, dres, dx, stats, M, H, eps);
+  else if (ch <= 2) hipLaunchKernelGGL(k_ln_bwd_rows<2>, rg, dim3(256), 0, st, x, gamma, dy, dres, dx, stats, M, H, eps);
+  else if (ch <= 3) hipLaunchKernelGGL(k_ln_bwd_rows<3>, rg, dim3(256), 0, st, x, gamma, dy, dres, dx, stats, M, H, eps);
+  else if (ch <= 5) hipLaunchKernelGGL(k_ln_bwd_rows<5>, rg, dim3(256), 0, st, x, gamma, dy, dres, dx, stats, M, H, eps);
+  else hipLaunchKernelGGL(k_ln_bwd_rows<8>, rg, dim3(256), 0, st, x, gamma, dy, dres, dx, stats, M, H, eps);
   const int64_t chunks = colsum_chunks(M);
   hipLaunchKernelGGL(k_ln_bwd_cols, dim3((unsigned)chunks, (unsigned)(H / 64)), dim3(256), 0, st, x, dy, stats, M, H,
                      part);

@@ -58,6 +58,13 @@ class EsmHeadWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in HEAD_WEIGHT_NAMES]
 
 
+class EsmLayerGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHT_NAMES]
+
+
+SAVED_REGIONS = {"h1": 0, "qkv": 1, "ctx": 2, "lse": 3, "x1": 4, "h2": 5, "z": 6, "a": 7}
+
+
 class EsmFp8State(ctypes.Structure):
     _fields_ = [
         ("num_layers", ctypes.c_int32), ("history_len", ctypes.c_int32),
@@ -112,6 +119,13 @@ SIGNATURES = {
     "esm_set_layer_precision": (_i32, [_p, _p, _i32, _p]),
     "esm_fp8_quantize": (_i32, [_p, _p, _i64, _p, _p, _p, _p]),
     "esm_mfma_peak": (_i32, [_p, _i32, _p, _sz, ctypes.POINTER(ctypes.c_double), _p]),
+    "esm_layer_saved_size": (_i32, [_p, _i64, ctypes.POINTER(_sz)]),
+    "esm_layer_saved_region": (_i32, [_p, _i64, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "esm_layer_fwd_train": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _i32, _p, _p, _p, _p, _i32, _i64, _i32, _p,
+                                   _sz, _p, _sz, _p]),
+    "esm_layer_bwd_workspace_size": (_i32, [_p, _i64, _i32, ctypes.POINTER(_sz)]),
+    "esm_layer_bwd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _i32, _p, _p, _sz, _p, _p,
+                             ctypes.POINTER(EsmLayerGrads), _p, _i32, _i64, _p, _sz, _p]),
     "esm_profile_enable": (_i32, [_p, _i32]),
     "esm_profile_read": (_i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "esm_check_cu_seqlens": (_i32, [_p, _i32, _i64, _i32, _i32]),
@@ -280,6 +294,69 @@ class Encoder:
               cuh.ctypes.data_as(ctypes.c_void_p) if cuh is not None else None, int(B), int(T), int(max_seqlen),
               _ptr(workspace), workspace.numel(), _stream(stream))
         return x_out
+
+    # -- training layer
+    def saved_size(self, T: int) -> int:
+        n = ctypes.c_size_t()
+        _call("esm_layer_saved_size", self._h, int(T), ctypes.byref(n))
+        return int(n.value)
+
+    def saved_region(self, saved, T: int, name: str):
+        """A view of one region of a layer's saved activations (esm_saved_region)."""
+        import torch
+        off, nb = ctypes.c_size_t(), ctypes.c_size_t()
+        _call("esm_layer_saved_region", self._h, int(T), SAVED_REGIONS[name], ctypes.byref(off), ctypes.byref(nb))
+        raw = saved[off.value: off.value + nb.value]
+        return raw.view(torch.float32) if name == "lse" else raw.view(torch.bfloat16)
+
+    def layer_fwd_train(self, weights, x_in, cu_seqlens, B: int, T: int, max_seqlen: int, *, x_out=None,
+                        saved=None, layer_idx: int = 0, cu_seqlens_host=None, workspace=None, stream=None):
+        """esm_layer_fwd_train: returns (x_out, saved), saved a uint8 device
+        buffer holding the activations the layer's backward takes."""
+        import torch
+        if x_out is None:
+            x_out = torch.empty_like(x_in)
+        if saved is None:
+            saved = torch.empty((max(self.saved_size(T), 256),), dtype=torch.uint8, device=x_in.device)
+        if workspace is None:
+            workspace = self.workspace(T, B)
+        w = layer_weights_struct(weights)
+        cuh = _host_i32(cu_seqlens_host)
+        _call("esm_layer_fwd_train", self._h, ctypes.byref(w), int(layer_idx), _ptr(x_in), _ptr(x_out),
+              _ptr(cu_seqlens), cuh.ctypes.data_as(ctypes.c_void_p) if cuh is not None else None, int(B), int(T),
+              int(max_seqlen), _ptr(saved), saved.numel(), _ptr(workspace), workspace.numel(), _stream(stream))
+        return x_out, saved
+
+    def layer_bwd_workspace(self, T: int, B: int):
+        import torch
+        n = ctypes.c_size_t()
+        _call("esm_layer_bwd_workspace_size", self._h, int(T), int(B), ctypes.byref(n))
+        return torch.empty((max(int(n.value), 256),), dtype=torch.uint8, device=f"cuda:{self.device}")
+
+    def layer_bwd(self, weights, x_in, saved, dy, cu_seqlens, B: int, T: int, *, dx=None, grads=None,
+                  layer_idx: int = 0, workspace=None, stream=None):
+        """esm_layer_bwd: returns (dx [T, H] bf16, grads), grads a dict of the 12
+        parameter gradients (weights bf16, biases and LayerNorm vectors fp32)."""
+        import torch
+        H, F, dev = self.cfg.hidden_size, self.cfg.intermediate_size, dy.device
+        if dx is None:
+            dx = torch.empty_like(dy)
+        if grads is None:
+            shapes = {"ln1_gamma": (H,), "ln1_beta": (H,), "w_qkv": (3 * H, H), "b_qkv": (3 * H,), "w_out": (H, H),
+                      "b_out": (H,), "ln2_gamma": (H,), "ln2_beta": (H,), "w_fc1": (F, H), "b_fc1": (F,),
+                      "w_fc2": (H, F), "b_fc2": (H,)}
+            grads = {n: torch.empty(sh, dtype=torch.bfloat16 if n.startswith("w_") else torch.float32, device=dev)
+                     for n, sh in shapes.items()}
+        if workspace is None:
+            workspace = self.layer_bwd_workspace(T, B)
+        w = layer_weights_struct(weights)
+        g = EsmLayerGrads()
+        for n in LAYER_WEIGHT_NAMES:
+            setattr(g, n, _ptr(grads[n]))
+        _call("esm_layer_bwd", self._h, ctypes.byref(w), int(layer_idx), _ptr(x_in), _ptr(saved), saved.numel(),
+              _ptr(dy), _ptr(dx), ctypes.byref(g), _ptr(cu_seqlens), int(B), int(T), _ptr(workspace),
+              workspace.numel(), _stream(stream))
+        return dx, grads
 
     def layer_fwd_noalloc(self, weights, x_in, cu_seqlens, B: int, T: int, max_seqlen: int, *, x_out,
                           layer_idx: int = 0, cu_seqlens_host=None, stream=None):

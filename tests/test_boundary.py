@@ -218,3 +218,18 @@ def test_backward_calls_fail_cleanly_without_a_handle():
                    None)[0] == 1
     assert _status("esm_gelu_bwd", None, p, p, p, ctypes.c_int64(8), None)[0] == 1
     assert _status("esm_qkv_rope_bwd", None, p, p, p, 1, ctypes.c_int64(1), p, ctypes.c_size_t(0), None)[0] == 1
+
+
+def test_training_layer_calls_fail_cleanly_without_a_handle():
+    p = ctypes.c_void_p(16)
+    n = ctypes.c_size_t()
+    off = ctypes.c_size_t()
+    assert _status("esm_layer_saved_size", None, ctypes.c_int64(10), ctypes.byref(n))[0] == 1
+    assert _status("esm_layer_saved_region", None, ctypes.c_int64(10), 0, ctypes.byref(off), ctypes.byref(n))[0] == 1
+    assert _status("esm_layer_bwd_workspace_size", None, ctypes.c_int64(10), 1, ctypes.byref(n))[0] == 1
+    w = ctypes.byref(esm.EsmLayerWeights())
+    g = ctypes.byref(esm.EsmLayerGrads())
+    assert _status("esm_layer_fwd_train", None, w, 0, p, p, p, None, 1, ctypes.c_int64(1), 1, p, ctypes.c_size_t(0),
+                   p, ctypes.c_size_t(0), None)[0] == 1
+    assert _status("esm_layer_bwd", None, w, 0, p, p, ctypes.c_size_t(0), p, p, g, p, 1, ctypes.c_int64(1), p,
+                   ctypes.c_size_t(0), None)[0] == 1
