@@ -354,6 +354,32 @@ def bench_linear_bwd(enc, T: int, H: int, F: int, steps: int, dev: str, stream) 
                                   "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
                                   "flops_per_launch": fl}}
         del x, w, dy, dx, dw, db, ws
+    # the HYBRID recipe's FP8 weight gradient on fc1's shape: E5M2 dy [T, F],
+    # E4M3 x [T, H] (codes drawn uniformly over finite values), dW [F, H]
+    f8 = torch.randint(0, 0x7B, (T, F), device=dev, generator=g, dtype=torch.int32).to(torch.uint8)
+    x8 = torch.randint(0, 0x7E, (T, H), device=dev, generator=g, dtype=torch.int32).to(torch.uint8)
+    one = torch.ones((1,), dtype=torch.float32, device=dev)
+    dw8 = torch.empty((F, H), dtype=torch.bfloat16, device=dev)
+
+    def call8():
+        enc.linear_e5m2_wgrad(f8, one, x8, one, dw=dw8, stream=stream)
+
+    for _ in range(3):
+        call8()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(n):
+        call8()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    fl = 2.0 * T * F * H
+    tf = fl / (ms * 1e-3) / 1e12
+    out["e5m2_wgrad_fc1"] = {"us_per_call": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                             "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS,
+                                          "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None,
+                                          "flops_per_launch": fl}}
+    del f8, x8, dw8
     return out
 
 

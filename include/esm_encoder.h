@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 18
+#define ESM_ABI_VERSION 19
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -489,6 +489,25 @@ esm_status esm_e5m2_quantize(esm_encoder* enc, const void* x, int64_t n, const f
 esm_status esm_linear_e5m2_dgrad(esm_encoder* enc, const void* dy8, const float* dy_scale, const void* wt8,
                                  const float* w_scale, void* dx, int64_t M, int32_t N, int32_t K,
                                  esm_stream_t stream);
+
+/* Weight gradient of the HYBRID recipe's backward ([BIO-ACC] 4.1: E5M2
+ * gradients, E4M3 activations): dW = (dy8 / s_dy)^T (x8 / s_x), dW bf16
+ * [N, K], from dy8 E5M2 codes [M, N] (esm_e5m2_quantize with scale
+ * dy_scale[0]) and x8 E4M3 codes [M, K], the linear's input as the forward
+ * cast it (scale x_scale[0]); both scales device fp32.  The contraction over
+ * the M rows runs on the scaled MFMA (E5M2 x E4M3, fp32 accumulation) after
+ * byte transposes of both operands with rows past M zero; for large M it is
+ * cut into up to 16 slices whose fp32 products are summed in slice order and
+ * dequantised once (deterministic).  N and K multiples of 64, any M >= 0.
+ * Workspace: esm_linear_e5m2_wgrad_workspace_size bytes, 256-byte aligned.
+ * ESM_ERR_NULL, ESM_ERR_SHAPE, ESM_ERR_UNSUPPORTED (alignment: tensors 16
+ * bytes, scales 4), ESM_ERR_WORKSPACE.  Asynchronous on stream. */
+esm_status esm_linear_e5m2_wgrad(esm_encoder* enc, const void* dy8, const float* dy_scale, const void* x8,
+                                 const float* x_scale, void* dw, int64_t M, int32_t N, int32_t K,
+                                 void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* Workspace bytes esm_linear_e5m2_wgrad needs for these sizes (host only). */
+esm_status esm_linear_e5m2_wgrad_workspace_size(int64_t M, int32_t N, int32_t K, size_t* bytes);
 
 /* Backward of the exact-erf GELU of fc1's epilogue ([BIO-ACC] 3.1; training
  * timed in [BIO-ACC] 3.2 and 6): dz[i] = dy[i] (Phi(z[i]) + z[i] phi(z[i]))

@@ -397,7 +397,10 @@ int64_t colsum_chunks(int64_t M);
 // dW GEMM of the linear backward: K slices (split-K) for M rows, and the
 // fixed-order sum of the slices' fp32 partials into bf16.
 int32_t wgrad_splits(int64_t M, int32_t N, int32_t K);
-hipError_t launch_split_reduce(const float* part, int32_t S, int64_t n, bf16_t* out, hipStream_t st);
+hipError_t launch_split_reduce(const float* part, int32_t S, int64_t n, bf16_t* out, hipStream_t st,
+                               const float* sa = nullptr, const float* sb = nullptr);
+// out [C, Rp] bytes = transpose of in [R, C] bytes, rows R .. Rp - 1 zero; C, Rp multiples of 64
+hipError_t launch_transpose8_pad(const uint8_t* in, int64_t R, int32_t C, uint8_t* out, int64_t Rp, hipStream_t st);
 // LayerNorm backward: dx [M, H] bf16, dgamma and dbeta [H] fp32; stats [2M]
 // and part [colsum_chunks(M), 2, H] fp32 are scratch.  H a multiple of 64, <= 4096.
 // GELU backward: dz = dy GELU'(z), n % 8 == 0.  QKV/RoPE backward: planar

@@ -1491,6 +1491,74 @@ esm_status esm_linear_e5m2_dgrad(esm_encoder* e, const void* dy8, const float* d
   return timed(e, ESM_K_LINEAR_BWD, st, "e5m2 dgrad", [&] { return launch_gemm(EPI_BIAS, g, st); });
 }
 
+namespace {
+// E5M2 weight gradient: dy^T [N, Mp] and x^T [K, Mp] as bytes (rows past M
+// zero), then, with S > 1 K slices, the slices' fp32 products [S, N, K].
+struct E5WgradPlan {
+  int32_t splits;
+  int64_t Mp;
+  size_t dyt, xt, wpart, total;
+};
+E5WgradPlan e5_wgrad_plan(int64_t M, int32_t N, int32_t K) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  E5WgradPlan p;
+  p.splits = wgrad_splits(M, N, K);
+  const int64_t q = 128 * (int64_t)p.splits;
+  p.Mp = (M + q - 1) / q * q;
+  p.dyt = 0;
+  p.xt = up((size_t)N * p.Mp);
+  p.wpart = p.xt + up((size_t)K * p.Mp);
+  p.total = p.wpart + (p.splits > 1 ? up((size_t)p.splits * N * K * 4) : 0);
+  return p;
+}
+}  // namespace
+
+esm_status esm_linear_e5m2_wgrad_workspace_size(int64_t M, int32_t N, int32_t K, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(ESM_ERR_NULL, "NULL argument");
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64)
+    return fail(ESM_ERR_SHAPE, "M %lld N %d K %d: N and K must be positive multiples of 64", (long long)M, N, K);
+  *bytes = e5_wgrad_plan(M, N, K).total;
+  return ok();
+}
+
+esm_status esm_linear_e5m2_wgrad(esm_encoder* e, const void* dy8, const float* dy_scale, const void* x8,
+                                 const float* x_scale, void* dw, int64_t M, int32_t N, int32_t K, void* ws,
+                                 size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !dy8 || !dy_scale || !x8 || !x_scale || !dw || !ws) return fail(ESM_ERR_NULL, "NULL argument");
+  if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64)
+    return fail(ESM_ERR_SHAPE, "M %lld N %d K %d: N and K must be positive multiples of 64", (long long)M, N, K);
+  if (!aligned16(dy8) || !aligned16(x8) || !aligned16(dw) || ((uintptr_t)dy_scale & 3u) || ((uintptr_t)x_scale & 3u) ||
+      ((uintptr_t)ws & 255u))
+    return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer (tensors 16 bytes, scales 4, workspace 256)");
+  const E5WgradPlan pl = e5_wgrad_plan(M, N, K);
+  if (ws_bytes < pl.total) return fail(ESM_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, pl.total);
+  if (M == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* dyt = (uint8_t*)ws + pl.dyt;
+  uint8_t* xt = (uint8_t*)ws + pl.xt;
+  float* wpart = (float*)((char*)ws + pl.wpart);
+  return timed(e, ESM_K_LINEAR_BWD, st, "e5m2 wgrad", [&]() -> hipError_t {
+    // dW [N, K] = (dy^T [N, Mp]) . (x^T [K, Mp])^T over the zero-padded rows
+    hipError_t r = launch_transpose8_pad((const uint8_t*)dy8, M, N, dyt, pl.Mp, st);
+    if (!r) r = launch_transpose8_pad((const uint8_t*)x8, M, K, xt, pl.Mp, st);
+    if (r) return r;
+    GemmArgs g{};
+    g.dtype = kE5M2X;
+    g.x = dyt; g.w = xt; g.x_scale = dy_scale; g.w_scale = x_scale;
+    g.y = (bf16_t*)dw; g.M = N; g.N = K; g.K = pl.Mp;
+    if (pl.splits > 1) {
+      g.y32 = wpart; g.ksplit = pl.splits;
+      r = launch_gemm(EPI_F32_SPLIT, g, st);
+      if (!r) r = launch_split_reduce(wpart, pl.splits, (int64_t)N * K, (bf16_t*)dw, st, dy_scale, x_scale);
+      return r;
+    }
+    return launch_gemm(EPI_BIAS, g, st);
+  });
+}
+
 esm_status esm_gelu_bwd(esm_encoder* e, const void* z, const void* dy, void* dz, int64_t n, esm_stream_t stream) {
   g_last_error.clear();
   if (!e || !z || !dy || !dz) return fail(ESM_ERR_NULL, "NULL argument");

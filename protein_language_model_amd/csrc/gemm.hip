@@ -823,7 +823,14 @@ int device_cus() {
 template <int EPI>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   if constexpr (EPI == EPI_F32_SPLIT) {
-    if (a.dtype != kBF16 || a.ksplit < 1 || !a.y32 || a.K % (64 * a.ksplit)) return hipErrorInvalidValue;
+    // split-K partial products (the backward's weight gradients): bf16, or
+    // E5M2 x E4M3 (raw products; the reduction dequantises)
+    if (a.ksplit < 1 || !a.y32) return hipErrorInvalidValue;
+    if (a.dtype == kE5M2X) {
+      if (a.K % (128 * a.ksplit)) return hipErrorInvalidValue;
+      return run<256, 256, 2, 4, EPI, kE5M2X>(a, st);
+    }
+    if (a.dtype != kBF16 || a.K % (64 * a.ksplit)) return hipErrorInvalidValue;
     return run<256, 256, 2, 4, EPI, kBF16>(a, st);
   } else if constexpr (EPI == EPI_QKV_ROPE_LN || EPI == EPI_BIAS_GELU_LN || EPI == EPI_RES_STATS) {
     if (a.dtype != kBF16) return hipErrorInvalidValue;

@@ -269,6 +269,7 @@ __global__ __launch_bounds__(256) void k_ln_bwd_cols(const bf16_t* __restrict__ 
 // out[i] = bf16(sum over s of part[s * n + i]) in slice order (split-K
 // partial sums of the dW GEMM); 4 values per thread, n % 4 == 0.
 __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ part, int32_t S, int64_t n,
+                                                      const float* __restrict__ sa, const float* __restrict__ sb,
                                                       bf16_t* __restrict__ out) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (i >= n) return;
@@ -277,7 +278,41 @@ __global__ __launch_bounds__(256) void k_split_reduce(const float* __restrict__ 
     const f32x4 v = *(const f32x4*)(part + (int64_t)s * n + i);
     acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
   }
+  if (sa) {   // FP8 operands: dequantise the sum as the GEMM epilogue does, by 1 / (s_a s_b)
+    const float dq = 1.0f / (sa[0] * sb[0]);
+    acc[0] *= dq; acc[1] *= dq; acc[2] *= dq; acc[3] *= dq;
+  }
   *(u32x2*)(out + i) = u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])};
+}
+
+// Byte transpose with zero rows past R: out[c, r] = in[r, c] for r < R, 0
+// for R <= r < Rp; 64 x 64 tiles through LDS, 16-byte loads and stores
+// (one FP8 code per byte).
+__global__ __launch_bounds__(256) void k_transpose8_pad(const uint8_t* __restrict__ in, int64_t R, int32_t C,
+                                                        uint8_t* __restrict__ out, int64_t Rp) {
+  __shared__ uint8_t tile[64][68];
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int c0 = blockIdx.y * 64;
+  const int t = threadIdx.x;
+  {
+    // load: thread t reads 16 consecutive columns of row t / 4
+    const int r = t >> 2, c = (t & 3) * 16;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (r0 + r < R) w = *(const u32x4*)(in + (r0 + r) * C + c0 + c);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) tile[r][c + e] = (uint8_t)(w[e >> 2] >> (8 * (e & 3)));
+  }
+  __syncthreads();
+  {
+    // store: thread t writes 16 consecutive rows (of in) of output row t / 4
+    const int c = t >> 2, r = (t & 3) * 16;
+    u32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)tile[r + 4 * q][c] | ((uint32_t)tile[r + 4 * q + 1][c] << 8) |
+             ((uint32_t)tile[r + 4 * q + 2][c] << 16) | ((uint32_t)tile[r + 4 * q + 3][c] << 24);
+    *(u32x4*)(out + (int64_t)(c0 + c) * Rp + r0 + r) = w;
+  }
 }
 
 // ------------------------------------------------------------ GELU, RoPE backward
@@ -355,11 +390,20 @@ int32_t wgrad_splits(int64_t M, int32_t N, int32_t K) {
   return best;
 }
 
-hipError_t launch_split_reduce(const float* part, int32_t S, int64_t n, bf16_t* out, hipStream_t st) {
+hipError_t launch_split_reduce(const float* part, int32_t S, int64_t n, bf16_t* out, hipStream_t st,
+                               const float* sa, const float* sb) {
   if (n <= 0) return hipSuccess;
-  if (n % 4 || S < 1) return hipErrorInvalidValue;
+  if (n % 4 || S < 1 || (sa == nullptr) != (sb == nullptr)) return hipErrorInvalidValue;
   const int64_t nt = n / 4;
-  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, st, part, S, n, out);
+  hipLaunchKernelGGL(k_split_reduce, dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, st, part, S, n, sa, sb, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose8_pad(const uint8_t* in, int64_t R, int32_t C, uint8_t* out, int64_t Rp, hipStream_t st) {
+  if (C <= 0 || Rp <= 0) return hipSuccess;
+  if (C % 64 || Rp % 64 || Rp < R) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_transpose8_pad, dim3((unsigned)(Rp / 64), (unsigned)(C / 64)), dim3(256), 0, st, in, R, C, out,
+                     Rp);
   return hipGetLastError();
 }
 

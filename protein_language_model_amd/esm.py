@@ -101,6 +101,8 @@ SIGNATURES = {
     "esm_gelu_bwd": (_i32, [_p, _p, _p, _p, _i64, _p]),
     "esm_e5m2_quantize": (_i32, [_p, _p, _i64, _p, _p, _p, _p]),
     "esm_linear_e5m2_dgrad": (_i32, [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _p]),
+    "esm_linear_e5m2_wgrad": (_i32, [_p, _p, _p, _p, _p, _p, _i64, _i32, _i32, _p, _sz, _p]),
+    "esm_linear_e5m2_wgrad_workspace_size": (_i32, [_i64, _i32, _i32, _p]),
     "esm_qkv_rope_bwd": (_i32, [_p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_attention_bwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_biased_attention_fwd": (_i32, [_p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p]),
@@ -531,6 +533,21 @@ class Encoder:
         _call("esm_linear_e5m2_dgrad", self._h, _ptr(dy8), _ptr(dy_scale), _ptr(wt8), _ptr(w_scale), _ptr(dx),
               int(M), int(N), int(K), _stream(stream))
         return dx
+
+    def linear_e5m2_wgrad(self, dy8, dy_scale, x8, x_scale, *, dw=None, workspace=None, stream=None):
+        """dW [N, K] bf16 = (dy8 / dy_scale)^T (x8 / x_scale) with dy8 E5M2 [M, N], x8 E4M3 [M, K]."""
+        import torch
+        M, N = dy8.shape
+        K = x8.shape[1]
+        if dw is None:
+            dw = torch.empty((N, K), dtype=torch.bfloat16, device=dy8.device)
+        if workspace is None:
+            n = ctypes.c_size_t()
+            _call("esm_linear_e5m2_wgrad_workspace_size", int(M), int(N), int(K), ctypes.byref(n))
+            workspace = torch.empty((max(int(n.value), 256),), dtype=torch.uint8, device=dy8.device)
+        _call("esm_linear_e5m2_wgrad", self._h, _ptr(dy8), _ptr(dy_scale), _ptr(x8), _ptr(x_scale), _ptr(dw),
+              int(M), int(N), int(K), _ptr(workspace), workspace.numel(), _stream(stream))
+        return dw
 
     def gelu_bwd(self, z, dy, *, dz=None, stream=None):
         """dz = dy * GELU'(z) (bf16, same shape; the element count a multiple of 8)."""

@@ -233,3 +233,19 @@ def test_training_layer_calls_fail_cleanly_without_a_handle():
                    p, ctypes.c_size_t(0), None)[0] == 1
     assert _status("esm_layer_bwd", None, w, 0, p, p, ctypes.c_size_t(0), p, p, g, p, 1, ctypes.c_int64(1), p,
                    ctypes.c_size_t(0), None)[0] == 1
+
+
+def test_e5m2_wgrad_workspace_size():
+    # dy^T [N, Mp] and x^T [K, Mp] bytes (Mp: M rounded up to 128 per K slice), then [S, N, K] fp32 slices
+    st, msg, n = _size("esm_linear_e5m2_wgrad_workspace_size", ctypes.c_int64(1000), 1280, 320)
+    assert st == 0, msg
+    assert n == 1280 * 1024 + 320 * 1024            # one slice below 2048 rows
+    st, msg, n = _size("esm_linear_e5m2_wgrad_workspace_size", ctypes.c_int64(32293), 5120, 1280)
+    assert st == 0, msg
+    up = lambda b: (b + 255) // 256 * 256             # noqa: E731
+    S = 5                                             # 100 tiles: 5 slices fill 2 rounds of 256 CUs
+    Mp = (32293 + 128 * S - 1) // (128 * S) * 128 * S
+    assert n == up(5120 * Mp) + up(1280 * Mp) + up(S * 5120 * 1280 * 4)
+    for bad in ((10, 100, 64), (10, 64, 0), (-1, 64, 64)):
+        st, msg, _ = _size("esm_linear_e5m2_wgrad_workspace_size", ctypes.c_int64(bad[0]), bad[1], bad[2])
+        assert st == 2 and msg

@@ -1,9 +1,10 @@
 """FP8 backward pieces of the HYBRID recipe through the C ABI: the E5M2 cast
 of a gradient (esm_e5m2_quantize) bit-exact against the oracle's codec
 (oracle/fp8_ref.py: e5m2_encode, with x * scale formed in float32 on both
-sides), and the E5M2 x E4M3 data-gradient GEMM (esm_linear_e5m2_dgrad)
-against the exact fp64 product of the decoded operands (bf16 output:
-max|err| / max|ref| <= 4e-3)."""
+sides), and the E5M2 x E4M3 data-gradient and weight-gradient GEMMs
+(esm_linear_e5m2_dgrad, esm_linear_e5m2_wgrad) against the exact fp64
+product of the decoded operands (bf16 output: max|err| / max|ref| <= 4e-3,
+a bf16 rounding of 2^-9 plus fp32 accumulation)."""
 import numpy as np
 import pytest
 import torch
@@ -114,3 +115,36 @@ def test_linear_e5m2_dgrad_320_row_tiles_at_the_650m_shape(gu, enc):
                                      r.choice(M, 120, replace=False)]))
     ref = (F8.e5m2_to_f64(dy8[rows]) / s_dy) @ (F8.e4m3_to_f64(wt8) / np.float64(np.float32(s_w))).T
     assert gu.rel_err(gu.from_dev(dx)[rows], ref) < 4e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 128, 64), (381, 1280, 320), (1000, 5120, 1280), (4097, 320, 1280)])
+def test_linear_e5m2_wgrad(gu, enc, M, N, K):
+    """dW = (dy8 / s_dy)^T (x8 / s_x) against the exact product of the decoded
+    operands; M = 4097 takes the split-K path (slices summed, then
+    dequantised once)."""
+    r = np.random.default_rng(M + 3 * N + K)
+    s_dy, s_x = 64.0, 448.0 / 4.0
+    dy8 = F8.e5m2_encode(r.standard_normal((M, N)) * s_dy)
+    x8 = F8.e4m3_encode(np.clip(r.standard_normal((M, K)), -4, 4) * s_x)
+    dev = "cuda:0"
+    dw = enc.linear_e5m2_wgrad(torch.from_numpy(dy8).to(dev), torch.tensor([s_dy], device=dev),
+                               torch.from_numpy(x8).to(dev), torch.tensor([s_x], dtype=torch.float32, device=dev))
+    ref = (F8.e5m2_to_f64(dy8) / s_dy).T @ (F8.e4m3_to_f64(x8) / np.float64(np.float32(s_x)))
+    assert gu.rel_err(gu.from_dev(dw), ref) < 4e-3
+
+
+def test_linear_e5m2_wgrad_at_the_650m_fc1_shape(gu, enc):
+    """fc1's weight gradient at T = 32293 (dW [5120, 1280], contraction over
+    all rows in K slices); sampled rows of dW, all columns, against the exact
+    product of the decoded operands."""
+    M, N, K = 32293, 5120, 1280
+    r = np.random.default_rng(17)
+    s_dy, s_x = 8.0, 448.0 / 4.0
+    dy8 = F8.e5m2_encode(r.standard_normal((M, N)) * s_dy)
+    x8 = F8.e4m3_encode(np.clip(r.standard_normal((M, K)), -4, 4) * s_x)
+    dev = "cuda:0"
+    dw = enc.linear_e5m2_wgrad(torch.from_numpy(dy8).to(dev), torch.tensor([s_dy], device=dev),
+                               torch.from_numpy(x8).to(dev), torch.tensor([s_x], dtype=torch.float32, device=dev))
+    rows = np.unique(np.concatenate([[0, 255, 256, 5119], r.choice(N, 60, replace=False)]))
+    ref = (F8.e5m2_to_f64(dy8[:, rows]) / s_dy).T @ (F8.e4m3_to_f64(x8) / np.float64(np.float32(s_x)))
+    assert gu.rel_err(gu.from_dev(dw)[rows], ref) < 4e-3
