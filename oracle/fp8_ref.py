@@ -143,12 +143,18 @@ def e5m2_to_f64(codes) -> np.ndarray:
 
 
 class DelayedScaling:
-    """Per-tensor delayed scaling with an amax history and the max algorithm."""
+    """Per-tensor delayed scaling with an amax history and the max algorithm.
 
-    def __init__(self, history_len: int = 16):
+    fp8_max is the largest finite value of the tensor's format: E4M3's 448 for
+    the forward's activations, E5M2's 57344 for the HYBRID recipe's gradients
+    ([BIO-ACC] 4.1: E4M3 forward, E5M2 backward), so that the scaled amax of
+    the window lands on the format's largest value."""
+
+    def __init__(self, history_len: int = 16, fp8_max: float = E4M3_MAX):
         self.history = np.zeros(history_len)
         self.pos = 0
         self.scale = 1.0
+        self.fp8_max = fp8_max
 
     def record(self, amax: float) -> None:
         """End of a step: push its amax and recompute the scale for the next."""
@@ -156,7 +162,7 @@ class DelayedScaling:
         self.pos = (self.pos + 1) % len(self.history)
         m = float(np.max(self.history))
         if m > 0 and math.isfinite(m):
-            self.scale = E4M3_MAX / m
+            self.scale = self.fp8_max / m
 
 
 def weight_scale(w) -> float:

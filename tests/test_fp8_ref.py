@@ -86,6 +86,24 @@ def test_delayed_scaling_state_machine():
     assert F8.weight_scale(np.array([0.5, -2.0])) == 224.0
 
 
+def test_delayed_scaling_of_e5m2_gradients_targets_57344():
+    """The gradient state of the HYBRID recipe: the same window rule with
+    E5M2's largest value (57344 = 1.75 * 2^15), so a window maximum of 2^k
+    gives the scale 1.75 * 2^(15 - k), exact."""
+    st = F8.DelayedScaling(history_len=2, fp8_max=F8.E5M2_MAX)
+    assert st.scale == 1.0
+    st.record(4.0)
+    assert st.scale == 14336.0                  # 57344 / 4
+    st.record(0.25)
+    assert st.scale == 14336.0                  # history [4, 0.25]
+    st.record(0.25)                             # history [0.25, 0.25]: the 4 left the window
+    assert st.scale == 229376.0                 # 57344 / 0.25
+    st.record(float("inf"))                     # non-finite: keep the scale
+    assert st.scale == 229376.0
+    # the scaled window maximum lands exactly on the format's largest value
+    assert F8.e5m2_encode(np.array([0.25 * st.scale]))[0] == 0x7B
+
+
 def _tiny(seed=0):
     r = np.random.default_rng(seed)
     H, F, heads = 128, 512, 2
