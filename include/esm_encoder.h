@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 19
+#define ESM_ABI_VERSION 20
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -687,6 +687,38 @@ esm_status esm_fp8_set_state(esm_encoder* enc, const esm_fp8_state* state, esm_s
 /* Back to the initial state (scales 1, empty histories, steps 0, flag clear);
  * prepared weights and per-layer precisions are kept. */
 esm_status esm_fp8_reset(esm_encoder* enc, esm_stream_t stream);
+
+/* Gradient scaling of the HYBRID recipe ([BIO-ACC] 4.1: E5M2 for the
+ * backward's gradients; [TE-RU] Рецепт FP8: Delayed Scaling).  Beside the
+ * forward's state each layer keeps, for four gradient tensors -- slot 0 the
+ * output gradient of the QKV linear, 1 of the out-projection, 2 of fc1, 3 of
+ * fc2 (the layer's output gradient) -- a scale (initially 1), the amax of the
+ * current backward step and a history of history_len steps, with the
+ * forward's window rule and E5M2's largest finite value: at the end of a step
+ * the step's amax enters slot steps % history_len and the scale becomes
+ * 57344 / max(history) when that is positive and finite (else it is kept; a
+ * non-finite amax sets the state's sticky flag).  esm_fp8_reset clears it with
+ * the rest of the state.  All need an encoder holding the FP8 state
+ * (ESM_ERR_STATE otherwise); layer_idx outside [0, num_hidden_layers) or slot
+ * outside [0, 4): ESM_ERR_SHAPE.
+ *
+ * esm_fp8_grad_quantize: y8 = cast_e5m2(g * scale) with the slot's current
+ * scale (g bf16, n values, a multiple of 8; y8 uint8 codes, 8-byte aligned);
+ * max |g| is folded into the slot's amax of this step; the scale used is also
+ * written to *scale_out (device fp32, may be NULL), the dy_scale that
+ * esm_linear_e5m2_dgrad and esm_linear_e5m2_wgrad take.  Asynchronous. */
+esm_status esm_fp8_grad_quantize(esm_encoder* enc, int32_t layer_idx, int32_t slot, const void* g, int64_t n,
+                                 void* y8, float* scale_out, esm_stream_t stream);
+
+/* End of layer layer_idx's backward step: rolls its four gradient histories
+ * and sets their next scales.  Asynchronous. */
+esm_status esm_fp8_grad_step(esm_encoder* enc, int32_t layer_idx, esm_stream_t stream);
+
+/* Copies the gradient state into host arrays after waiting for stream: scale
+ * [num_layers, 4], history [num_layers, 4, history_len] (ring order: step s in
+ * slot s % history_len), steps [num_layers]. */
+esm_status esm_fp8_grad_get_state(esm_encoder* enc, float* scale, float* history, int64_t* steps,
+                                  esm_stream_t stream);
 
 /* MXFP4 weights of layer layer_idx ([TE-ESM2] FP8与FP4混合精度支持, read as
  * OCP MXFP4): the four linear weights of w quantised per 32-value block along

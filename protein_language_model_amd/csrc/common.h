@@ -448,6 +448,12 @@ struct Fp8State {
   uint32_t* w_amax;    // [layers, 4]
   int32_t* layer_on;   // [layers] 1 = the layer runs FP8 (its state is updated), 0 = bf16 (state frozen)
   int32_t history_len;
+  // gradients of the HYBRID backward (E5M2): per layer the output gradients
+  // of the qkv, out-projection, fc1 and fc2 linears
+  float* g_scale;      // [layers, 4]
+  uint32_t* g_amax;    // [layers, 4] amax of the current backward step, float bits
+  float* g_history;    // [layers, 4, history_len]
+  int64_t* g_steps;    // [layers]
 };
 
 // amax of n bf16 values into *amax (which must start at 0).
@@ -460,8 +466,13 @@ hipError_t launch_quantize_f32(const float* x, int64_t n, const float* scale, ui
                                hipStream_t st);
 // End of a step for layers [l0, l0 + nl): push amax into the history, new scale
 // = 448 / max(history) when that is positive and finite, clear amax.
+// End of a backward step of layer l: the same roll for its four gradient
+// tensors with E5M2's largest value (57344).
+hipError_t launch_grad_scale_update(const Fp8State& s, int32_t l, hipStream_t st);
+// y = cast_e5m2(x * scale[0]), amax of x into *amax; scale[0] also copied to
+// *scale_out when that is not NULL.
 hipError_t launch_quantize_e5m2(const bf16_t* x, int64_t n, const float* scale, uint8_t* y, uint32_t* amax,
-                                hipStream_t st);
+                                hipStream_t st, float* scale_out = nullptr);
 hipError_t launch_scale_update(const Fp8State& s, int32_t l0, int32_t nl, hipStream_t st);
 
 }  // namespace esm

@@ -341,7 +341,8 @@ W8Off w8_offsets(const esm_config& c) {
 // Device layout of the delayed-scaling state: one allocation, 256-byte
 // aligned arrays.
 struct Fp8Layout {
-  size_t act_scale, act_amax, history, steps, flags, w_scale, w_amax, layer_on, total;
+  size_t act_scale, act_amax, history, steps, flags, w_scale, w_amax, layer_on, g_scale, g_amax, g_history, g_steps,
+      total;
 };
 Fp8Layout fp8_layout(const esm_config& c) {
   const size_t L = (size_t)(c.num_hidden_layers > 0 ? c.num_hidden_layers : 1), HL = (size_t)c.amax_history_len;
@@ -360,6 +361,10 @@ Fp8Layout fp8_layout(const esm_config& c) {
   f.w_scale = take(L * 4 * sizeof(float));
   f.w_amax = take(L * 4 * sizeof(uint32_t));
   f.layer_on = take(L * sizeof(int32_t));
+  f.g_scale = take(L * 4 * sizeof(float));
+  f.g_amax = take(L * 4 * sizeof(uint32_t));
+  f.g_history = take(L * 4 * HL * sizeof(float));
+  f.g_steps = take(L * sizeof(int64_t));
   f.total = o;
   return f;
 }
@@ -374,6 +379,10 @@ esm_status fp8_reset_state(esm_encoder* e) {
   HIP_TRY(hipMemset(e->f8.history, 0, L * 4 * HL * sizeof(float)), "fp8 reset");
   HIP_TRY(hipMemset(e->f8.steps, 0, L * sizeof(int64_t)), "fp8 reset");
   HIP_TRY(hipMemset(e->f8.flags, 0, sizeof(uint32_t)), "fp8 reset");
+  HIP_TRY(hipMemcpy(e->f8.g_scale, ones.data(), ones.size() * sizeof(float), hipMemcpyHostToDevice), "fp8 reset");
+  HIP_TRY(hipMemset(e->f8.g_amax, 0, L * 4 * sizeof(uint32_t)), "fp8 reset");
+  HIP_TRY(hipMemset(e->f8.g_history, 0, L * 4 * HL * sizeof(float)), "fp8 reset");
+  HIP_TRY(hipMemset(e->f8.g_steps, 0, L * sizeof(int64_t)), "fp8 reset");
   return ok();
 }
 
@@ -390,6 +399,10 @@ esm_status fp8_create(esm_encoder* e) {
   e->f8.w_scale = (float*)(b + f.w_scale);
   e->f8.w_amax = (uint32_t*)(b + f.w_amax);
   e->f8.layer_on = (int32_t*)(b + f.layer_on);
+  e->f8.g_scale = (float*)(b + f.g_scale);
+  e->f8.g_amax = (uint32_t*)(b + f.g_amax);
+  e->f8.g_history = (float*)(b + f.g_history);
+  e->f8.g_steps = (int64_t*)(b + f.g_steps);
   e->f8.history_len = c.amax_history_len;
   HIP_TRY(hipMemset(e->f8.w_scale, 0, f.total - f.w_scale), "fp8 state");
   e->w8_layer = align256(w8_offsets(c).total);
@@ -2078,6 +2091,53 @@ esm_status esm_fp8_reset(esm_encoder* e, esm_stream_t stream) {
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
   HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
   return fp8_reset_state(e);
+}
+
+esm_status esm_fp8_grad_quantize(esm_encoder* e, int32_t layer_idx, int32_t slot, const void* g, int64_t n, void* y8,
+                                 float* scale_out, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !g || !y8) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!e->fp8_mem) return fail(ESM_ERR_STATE, "encoder has no FP8 state (bf16, or MXFP4 with no FP8 layer)");
+  if (layer_idx < 0 || layer_idx >= e->cfg.num_hidden_layers || slot < 0 || slot > 3)
+    return fail(ESM_ERR_SHAPE, "layer_idx %d / slot %d outside [0, %d) / [0, 4)", layer_idx, slot,
+                e->cfg.num_hidden_layers);
+  if (n < 0 || n % 8) return fail(ESM_ERR_SHAPE, "n %lld: a non-negative multiple of 8", (long long)n);
+  if (!aligned16(g) || ((uintptr_t)y8 & 7u) || ((uintptr_t)scale_out & 3u))
+    return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer");
+  if (n == 0) return ok();
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  const int k = 4 * layer_idx + slot;
+  return timed(e, ESM_K_FP8, st, "e5m2 gradient cast", [&] {
+    return launch_quantize_e5m2((const bf16_t*)g, n, e->f8.g_scale + k, (uint8_t*)y8, e->f8.g_amax + k, st, scale_out);
+  });
+}
+
+esm_status esm_fp8_grad_step(esm_encoder* e, int32_t layer_idx, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  if (!e->fp8_mem) return fail(ESM_ERR_STATE, "encoder has no FP8 state (bf16, or MXFP4 with no FP8 layer)");
+  if (layer_idx < 0 || layer_idx >= e->cfg.num_hidden_layers)
+    return fail(ESM_ERR_SHAPE, "layer_idx %d outside [0, %d)", layer_idx, e->cfg.num_hidden_layers);
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  return timed(e, ESM_K_FP8, st, "gradient scale update", [&] { return launch_grad_scale_update(e->f8, layer_idx, st); });
+}
+
+esm_status esm_fp8_grad_get_state(esm_encoder* e, float* scale, float* history, int64_t* steps, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e || !scale || !history || !steps) return fail(ESM_ERR_NULL, "NULL argument");
+  if (!e->fp8_mem) return fail(ESM_ERR_STATE, "encoder has no FP8 state (bf16, or MXFP4 with no FP8 layer)");
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  HIP_TRY(hipStreamSynchronize((hipStream_t)stream), "hipStreamSynchronize");
+  const size_t L = (size_t)e->cfg.num_hidden_layers, HL = (size_t)e->cfg.amax_history_len;
+  if (L > 0) {
+    HIP_TRY(hipMemcpy(scale, e->f8.g_scale, L * 4 * sizeof(float), hipMemcpyDeviceToHost), "fp8 gradient state");
+    HIP_TRY(hipMemcpy(history, e->f8.g_history, L * 4 * HL * sizeof(float), hipMemcpyDeviceToHost),
+            "fp8 gradient state");
+    HIP_TRY(hipMemcpy(steps, e->f8.g_steps, L * sizeof(int64_t), hipMemcpyDeviceToHost), "fp8 gradient state");
+  }
+  return ok();
 }
 
 esm_status esm_set_layer_precision(esm_encoder* e, const int32_t* prec, int32_t n, esm_stream_t stream) {

@@ -63,8 +63,9 @@ __global__ __launch_bounds__(256) void k_quantize_f32(const float* __restrict__ 
 // out, as for the E4M3 casts).  8 values per thread.
 __global__ __launch_bounds__(256) void k_quantize_e5m2(const bf16_t* __restrict__ x, int64_t n8,
                                                        const float* __restrict__ scale, uint8_t* __restrict__ y,
-                                                       uint32_t* amax) {
+                                                       uint32_t* amax, float* __restrict__ scale_out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (scale_out && i == 0) scale_out[0] = scale[0];
   float m = 0.f;
   if (i < n8) {
     const u32x4 w = *(const u32x4*)(x + 8 * i);
@@ -100,20 +101,20 @@ __global__ __launch_bounds__(256) void k_quantize_e5m2(const bf16_t* __restrict_
 }
 
 // One thread per layer: its four activation tensors share the step counter.
-__global__ void k_scale_update(Fp8State s, int32_t l0, int32_t nl) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= nl) return;
-  const int l = l0 + idx;
-  if (!s.layer_on[l]) return;  // a bf16 layer: recorded nothing, its state stays as it is
-  const int HL = s.history_len;
-  const int slot = (int)(s.steps[l] % HL);
+// One layer's end of step for its four tensors: each step's amax enters
+// slot steps % HL of the tensor's history; the next scale is fmax over the
+// history's max when that is positive and finite (else the scale is kept);
+// the amax is cleared.  Returns whether a non-finite amax was recorded.
+__device__ bool roll_histories(float* scale, uint32_t* amax, float* history, int64_t* steps, int l, int HL,
+                               float fmax) {
+  const int slot = (int)(steps[l] % HL);
   bool nonfinite = false;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int k = 4 * l + t;
-    const float am = __uint_as_float(s.act_amax[k]);
+    const float am = __uint_as_float(amax[k]);
     if (!(am < __builtin_inff())) nonfinite = true;  // Inf or NaN bits
-    float* h = s.history + (int64_t)k * HL;
+    float* h = history + (int64_t)k * HL;
     h[slot] = am;
     float mx = 0.f;
     bool ok = true;
@@ -122,11 +123,25 @@ __global__ void k_scale_update(Fp8State s, int32_t l0, int32_t nl) {
       ok = ok && v < __builtin_inff() && v == v;
       mx = fmaxf(mx, v);
     }
-    if (ok && mx > 0.f) s.act_scale[k] = kE4M3Max / mx;
-    s.act_amax[k] = 0u;
+    if (ok && mx > 0.f) scale[k] = fmax / mx;
+    amax[k] = 0u;
   }
-  s.steps[l] += 1;
-  if (nonfinite) atomicOr(s.flags, 1u);
+  steps[l] += 1;
+  return nonfinite;
+}
+
+__global__ void k_scale_update(Fp8State s, int32_t l0, int32_t nl) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= nl) return;
+  const int l = l0 + idx;
+  if (!s.layer_on[l]) return;  // a bf16 layer: recorded nothing, its state stays as it is
+  if (roll_histories(s.act_scale, s.act_amax, s.history, s.steps, l, s.history_len, kE4M3Max)) atomicOr(s.flags, 1u);
+}
+
+// The gradients' end of a backward step (one layer; E5M2's largest value).
+__global__ void k_grad_scale_update(Fp8State s, int32_t l) {
+  if (threadIdx.x != 0) return;
+  if (roll_histories(s.g_scale, s.g_amax, s.g_history, s.g_steps, l, s.history_len, 57344.0f)) atomicOr(s.flags, 1u);
 }
 
 }  // namespace
@@ -156,11 +171,17 @@ hipError_t launch_quantize_f32(const float* x, int64_t n, const float* scale, ui
 }
 
 hipError_t launch_quantize_e5m2(const bf16_t* x, int64_t n, const float* scale, uint8_t* y, uint32_t* amax,
-                                hipStream_t st) {
+                                hipStream_t st, float* scale_out) {
   if (n <= 0) return hipSuccess;
   if (n % 8) return hipErrorInvalidValue;
   const int64_t n8 = n / 8;
-  hipLaunchKernelGGL(k_quantize_e5m2, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, x, n8, scale, y, amax);
+  hipLaunchKernelGGL(k_quantize_e5m2, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, x, n8, scale, y, amax,
+                     scale_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_scale_update(const Fp8State& s, int32_t l, hipStream_t st) {
+  hipLaunchKernelGGL(k_grad_scale_update, dim3(1), dim3(64), 0, st, s, l);
   return hipGetLastError();
 }
 

@@ -118,6 +118,9 @@ SIGNATURES = {
     "esm_fp8_get_state": (_i32, [_p, ctypes.POINTER(EsmFp8State), _p]),
     "esm_fp8_set_state": (_i32, [_p, ctypes.POINTER(EsmFp8State), _p]),
     "esm_fp8_reset": (_i32, [_p, _p]),
+    "esm_fp8_grad_quantize": (_i32, [_p, _i32, _i32, _p, _i64, _p, _p, _p]),
+    "esm_fp8_grad_step": (_i32, [_p, _i32, _p]),
+    "esm_fp8_grad_get_state": (_i32, [_p, _p, _p, _p, _p]),
     "esm_set_layer_precision": (_i32, [_p, _p, _i32, _p]),
     "esm_fp8_quantize": (_i32, [_p, _p, _i64, _p, _p, _p, _p]),
     "esm_mfma_peak": (_i32, [_p, _i32, _p, _sz, ctypes.POINTER(ctypes.c_double), _p]),
@@ -735,6 +738,30 @@ class Encoder:
 
     def fp8_reset(self, stream=None) -> None:
         _call("esm_fp8_reset", self._h, _stream(stream))
+
+    def fp8_grad_quantize(self, layer_idx: int, slot: int, g, *, y8=None, scale_out=None, stream=None):
+        """E5M2 codes of a gradient (bf16 g) with the slot's delayed scale;
+        returns (y8 uint8, scale_out fp32 [1] on the device: the scale used)."""
+        import torch
+        if y8 is None:
+            y8 = torch.empty(g.shape, dtype=torch.uint8, device=g.device)
+        if scale_out is None:
+            scale_out = torch.empty((1,), dtype=torch.float32, device=g.device)
+        _call("esm_fp8_grad_quantize", self._h, int(layer_idx), int(slot), _ptr(g), g.numel(), _ptr(y8),
+              _ptr(scale_out), _stream(stream))
+        return y8, scale_out
+
+    def fp8_grad_step(self, layer_idx: int, stream=None) -> None:
+        _call("esm_fp8_grad_step", self._h, int(layer_idx), _stream(stream))
+
+    def fp8_grad_get_state(self, stream=None) -> Dict[str, np.ndarray]:
+        L, HL = self.cfg.num_hidden_layers, self.cfg.amax_history_len
+        scale = np.zeros((L, 4), np.float32)
+        hist = np.zeros((L, 4, HL), np.float32)
+        steps = np.zeros((L,), np.int64)
+        _call("esm_fp8_grad_get_state", self._h, scale.ctypes.data_as(ctypes.c_void_p),
+              hist.ctypes.data_as(ctypes.c_void_p), steps.ctypes.data_as(ctypes.c_void_p), _stream(stream))
+        return {"scale": scale, "history": hist, "steps": steps}
 
     def set_layer_precision(self, precisions: Sequence[str], stream=None) -> None:
         """Per-layer precision of an FP8 or MXFP4 encoder: "fp8", "mxfp4" or "bf16"

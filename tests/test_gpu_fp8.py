@@ -613,3 +613,48 @@ def test_650m_fp8_stack_33_layers_teacher_forced(gu):
     for l in range(m.layers):
         assert e_plain[l] < max(TOL_FP8, e_recipe[l] + TOL_EMU), (l, e_plain[l], e_recipe[l])
         assert e_emu[l] < (TOL_EMU_SMALL_RESIDUAL if l < 2 else TOL_EMU), (l, e_emu[l], e_recipe[l])
+
+
+# ------------------------------------------------------------------ gradients (HYBRID)
+
+def test_gradient_delayed_scaling_follows_the_oracle(gu):
+    """The HYBRID recipe's gradient state (E5M2, 57344 / max of the window):
+    seven backward steps of two layers, each casting all four gradient
+    slots with amax spread over 2^-12 .. 2^5 and one infinite gradient
+    value; every cast bit-exact against the oracle's codec at the scale the
+    oracle's state machine gives (x * s in float32 on both sides), the scale
+    the call reports equal to it, and scales, histories and step counts
+    equal to the oracle's after every step.  The forward's state is not
+    touched; the infinite value sets the shared sticky flag and is saturated
+    in the cast."""
+    m = TINY8
+    HL, L = 4, 2
+    enc = _encoder(m, layers=L, history_len=HL)
+    r = np.random.default_rng(31)
+    orc = {(l, t): F8.DelayedScaling(HL, F8.E5M2_MAX) for l in range(L) for t in range(4)}
+    for step in range(7):
+        for l in range(L):
+            for t in range(4):
+                g = (r.standard_normal(4096) * 2.0 ** int(r.integers(-12, 6))).astype(np.float32)
+                if (step, l, t) == (4, 1, 2):
+                    g[7] = np.inf
+                gb = D.to_bf16_bits(g)
+                y8, s_used = enc.fp8_grad_quantize(l, t, gu.to_dev_bf16(gb))
+                s_ref = np.float32(orc[(l, t)].scale)
+                assert _host(s_used)[0] == s_ref, (step, l, t)
+                gf = D.bf16_bits_to_f64(gb).astype(np.float32)
+                ref = F8.e5m2_encode((gf * s_ref).astype(np.float64))
+                assert np.array_equal(_host(y8), ref), (step, l, t)
+                orc[(l, t)].record(float(np.abs(gf).max()))
+            enc.fp8_grad_step(l)
+        st = enc.fp8_grad_get_state()
+        assert list(st["steps"]) == [step + 1] * L
+        for (l, t), d in orc.items():
+            assert st["scale"][l, t] == np.float32(d.scale), (step, l, t)
+            assert np.array_equal(st["history"][l, t], d.history.astype(np.float32)), (step, l, t)
+    fst = enc.fp8_get_state()
+    assert np.all(fst["steps"] == 0) and np.all(fst["act_scale"] == 1) and fst["nonfinite"]
+    enc.fp8_reset()
+    st = enc.fp8_grad_get_state()
+    assert np.all(st["scale"] == 1) and np.all(st["steps"] == 0) and not np.any(st["history"])
+    enc.close()
