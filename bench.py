@@ -20,11 +20,13 @@ under "head".  The biased attention kernel (the DeepSpeed4Science page's
 Evoformer attention with a mask bias and a pair bias) is timed on its own
 synthetic MSA-row shape under "biased_attention", the MXFP4 quantiser and
 GEMM (the FP4 recipe) on the layer's four GEMM shapes under "mxfp4", the
-whole stack with MXFP4 GEMMs under "mxfp4_stack", the attention backward
-on the batch's sequences under "attention_bwd", the linear backward on the
-layer's four shapes under "linear_bwd", the LayerNorm backward on [T, H]
-under "layernorm_bwd", and one 650M layer's training forward and backward
-(esm_layer_fwd_train, esm_layer_bwd) on the batch under "layer_train".
+whole stack with MXFP4 GEMMs under "mxfp4_stack", the stack with FP8 and
+MXFP4 layers alternating in one encoder under "mixed_fp8_mxfp4_stack", the
+attention backward on the batch's sequences under "attention_bwd", the
+linear backward on the layer's four shapes under "linear_bwd", the
+LayerNorm backward on [T, H] under "layernorm_bwd", and one 650M layer's
+training forward and backward (esm_layer_fwd_train, esm_layer_bwd) on the
+batch under "layer_train".
 Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
@@ -643,18 +645,27 @@ def main():
     fl = layer_flops(m.hidden, m.ffn, T, sum_L2)
     total_flops = m.layers * sum(fl.values())
 
-    def measure(precision: str, warmup: int, fold: bool = True):
+    def measure(precision: str, warmup: int, fold: bool = True, layer_prec=None):
         """Clean timed region (the throughput), then the same steps with every
         launch bracketed by HIP events (per-kernel durations).  bf16: the
         LayerNorms are folded into the QKV and fc1 linears (esm_prepare_layer,
-        once, like the FP8 and MXFP4 weight preparation) unless fold is off."""
+        once, like the FP8 and MXFP4 weight preparation) unless fold is off.
+        layer_prec: per-layer precisions of a quantised encoder (each layer's
+        weights prepared in its own format)."""
         enc = esm.Encoder(hidden_size=m.hidden, num_attention_heads=m.heads, intermediate_size=m.ffn,
                           num_hidden_layers=m.layers, precision=precision)
         if precision == "bf16" and fold:
             enc.prepare(weights, stream=stream)
-        if precision == "fp8":
+        if layer_prec is not None:
+            enc.set_layer_precision(layer_prec, stream=stream)
+            for l, p in enumerate(layer_prec):
+                if p == "fp8":
+                    enc.fp8_prepare_layer(l, weights[l], stream=stream)
+                elif p == "mxfp4":
+                    enc.mxfp4_prepare_layer(l, weights[l], stream=stream)
+        elif precision == "fp8":
             enc.fp8_prepare(weights, stream=stream)
-        if precision == "mxfp4":
+        elif precision == "mxfp4":
             enc.mxfp4_prepare(weights, stream=stream)
         ws = enc.workspace(T, B)
 
@@ -864,6 +875,20 @@ def main():
         encm.close()
         del wsm
 
+    mixed = None
+    if (not fp8_main and not args.no_mxfp4 and not args.no_fp8 and m.hidden % 256 == 0 and m.ffn % 256 == 0
+            and m.ffn <= 8 * m.hidden):
+        # the per-layer precision setting: FP8 and MXFP4 layers alternating in one encoder
+        lp = ["fp8" if l % 2 == 0 else "mxfp4" for l in range(m.layers)]
+        encx, wsx, msx, profx, _ = measure("fp8", max(args.warmup, FP8_MIN_WARMUP), layer_prec=lp)
+        mixed = {"ms_per_step": round(msx, 4), "value": round(T / (msx * 1e-3), 1), "unit": "residues/s",
+                 "tflops": round(total_flops / (msx * 1e-3) / 1e12, 1), "speedup_vs_bf16": round(ms / msx, 3),
+                 "layers": "even layers FP8 (E4M3, delayed scaling), odd layers MXFP4, one encoder"}
+        if profx:
+            mixed["kernels"] = kernel_table(profx)
+        encx.close()
+        del wsx
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, batch, emb, weights)
@@ -908,6 +933,7 @@ def main():
         "layernorm_bwd": ln_bwd,
         "layer_train": layer_train,
         "mxfp4_stack": mx_stack,
+        "mixed_fp8_mxfp4_stack": mixed,
         "vendor_gemm_fc1": vendor,
         "fp8": fp8,
     }
