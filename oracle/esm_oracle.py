@@ -378,6 +378,35 @@ def stack_forward(cu_seqlens, layers: List[Dict[str, np.ndarray]], heads: int,
     return h
 
 
+def embed_backward(ids, dx0, vocab: int) -> np.ndarray:
+    """Gradient of the embedding table under X0 = E[ids]: each table row
+    collects the gradients of the residues that gathered it, zero for tokens
+    the batch does not hold."""
+    d = np.zeros((vocab, np.asarray(dx0).shape[1]))
+    np.add.at(d, np.asarray(ids, np.int64), np.asarray(dx0, np.float64))
+    return d
+
+
+def stack_backward(cu_seqlens, layers: List[Dict[str, np.ndarray]], heads: int, dout,
+                   ids=None, table=None, x=None, **kw):
+    """Gradients of sum(dout * stack_forward(...)) by the chain rule: the
+    layers' backward in reverse order, each at the input the forward gave it,
+    then the embedding's when the stack starts from token ids.  Returns
+    (gradient of the stack input X0, [per-layer gradients as layer_backward
+    names them], table gradient or None)."""
+    h = embed(ids, table) if ids is not None else np.asarray(x, np.float64)
+    inputs = []
+    for w in layers:
+        inputs.append(h)
+        h = layer_forward(h, cu_seqlens, w, heads, **kw)
+    g = np.asarray(dout, np.float64)
+    grads = [None] * len(layers)
+    for l in reversed(range(len(layers))):
+        g, grads[l] = layer_backward(inputs[l], cu_seqlens, layers[l], heads, g, **kw)
+    d_table = embed_backward(ids, g, np.asarray(table).shape[0]) if ids is not None else None
+    return g, grads, d_table
+
+
 # --------------------------------------------------------------------------
 # After the stack: final LayerNorm, masked-LM head, sequence-level embedding
 # --------------------------------------------------------------------------

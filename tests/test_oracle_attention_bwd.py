@@ -278,3 +278,79 @@ def test_layer_backward_matches_finite_differences():
             flat[i] = old
             fd = (lp - lm) / (2 * h)
             assert abs(fd - gf[i]) <= 1e-6 * max(1.0, abs(fd)), (name, i, fd, gf[i])
+
+
+# ---------------------------------------------------------------- stack
+
+def _layer_w(rng, H, F):
+    return {"ln1_gamma": 1 + 0.1 * rng.standard_normal(H), "ln1_beta": 0.1 * rng.standard_normal(H),
+            "w_qkv": 0.1 * rng.standard_normal((3 * H, H)), "b_qkv": 0.1 * rng.standard_normal(3 * H),
+            "w_out": 0.1 * rng.standard_normal((H, H)), "b_out": 0.1 * rng.standard_normal(H),
+            "ln2_gamma": 1 + 0.1 * rng.standard_normal(H), "ln2_beta": 0.1 * rng.standard_normal(H),
+            "w_fc1": 0.1 * rng.standard_normal((F, H)), "b_fc1": 0.1 * rng.standard_normal(F),
+            "w_fc2": 0.1 * rng.standard_normal((H, F)), "b_fc2": 0.1 * rng.standard_normal(H)}
+
+
+def _check_fd(loss, pairs, rng, n=4, h=1e-5, rtol=1e-6):
+    for name, a, da in pairs:
+        flat, gf = a.reshape(-1), da.reshape(-1)
+        for i in rng.choice(flat.size, size=min(n, flat.size), replace=False):
+            old = flat[i]
+            flat[i] = old + h
+            lp = loss()
+            flat[i] = old - h
+            lm = loss()
+            flat[i] = old
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - gf[i]) <= rtol * max(1.0, abs(fd)), (name, i, fd, gf[i])
+
+
+def test_stack_backward_from_ids_matches_finite_differences():
+    """Two layers on top of the embedding gather (vocab 7, token 6 absent from
+    the batch): central differences of the stack forward from token ids, at
+    random coordinates of every weight of both layers and of the table rows;
+    the absent token's table row gets exactly zero."""
+    rng = np.random.default_rng(38)
+    H, heads, F, V = 128, 2, 256, 7
+    lens = [4, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    ids = np.array([0, 3, 3, 5, 1, 2, 3])
+    table = rng.standard_normal((V, H))
+    layers = [_layer_w(rng, H, F) for _ in range(2)]
+    dout = rng.standard_normal((int(cu[-1]), H))
+    dx0, grads, dtab = O.stack_backward(cu, layers, heads, dout, ids=ids, table=table)
+    assert np.all(dtab[6] == 0) and np.all(dtab[4] == 0)
+
+    def loss():
+        return float(np.sum(dout * O.stack_forward(cu, layers, heads, ids=ids, table=table)))
+    pairs = [("table", table, dtab)]
+    for l, (w, g) in enumerate(zip(layers, grads)):
+        pairs += [(f"{k}[{l}]", w[k], g[k]) for k in w]
+    _check_fd(loss, pairs, rng, n=3)
+    # the table gradient is the sum of the input gradient over the rows of each token
+    _check_fd(loss, [("table row 3", table[3], dtab[3])], rng, n=8)
+
+
+def test_stack_backward_from_hidden_states_matches_finite_differences():
+    """Three layers from given hidden states, one-residue sequence included:
+    central differences at random coordinates of the input and of the first
+    and last layers' weights; with one layer the stack backward is the layer
+    backward."""
+    rng = np.random.default_rng(39)
+    H, heads, F = 128, 2, 256
+    lens = [1, 5, 2]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    layers = [_layer_w(rng, H, F) for _ in range(3)]
+    x = rng.standard_normal((T, H))
+    dout = rng.standard_normal((T, H))
+    dx0, grads, dtab = O.stack_backward(cu, layers, heads, dout, x=x)
+    assert dtab is None
+
+    def loss():
+        return float(np.sum(dout * O.stack_forward(cu, layers, heads, x=x)))
+    _check_fd(loss, [("x", x, dx0)] + [(f"{k}[0]", layers[0][k], grads[0][k]) for k in ("w_qkv", "ln1_gamma", "b_fc2")]
+              + [(f"{k}[2]", layers[2][k], grads[2][k]) for k in ("w_fc1", "ln2_beta", "w_out")], rng, n=4)
+    d1, g1, _ = O.stack_backward(cu, layers[:1], heads, dout, x=x)
+    d_ref, g_ref = O.layer_backward(x, cu, layers[0], heads, dout)
+    assert np.array_equal(d1, d_ref) and all(np.array_equal(g1[0][k], g_ref[k]) for k in g_ref)
