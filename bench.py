@@ -26,7 +26,8 @@ attention backward on the batch's sequences under "attention_bwd", the
 linear backward on the layer's four shapes under "linear_bwd", the
 LayerNorm backward on [T, H] under "layernorm_bwd", and one 650M layer's
 training forward and backward (esm_layer_fwd_train, esm_layer_bwd) on the
-batch under "layer_train".
+batch under "layer_train", and the whole 33-layer training step
+(esm_stack_fwd_train, esm_stack_bwd) under "stack_train".
 Prints one JSON line.
 
     python bench.py [--steps 30] [--warmup 10] [--workload 650m|3b|650m_fp8] [--no-cpu-baseline]
@@ -87,6 +88,8 @@ def parse():
     ap.add_argument("--no-mxfp4", action="store_true", help="skip timing the MXFP4 GEMMs on the layer shapes")
     ap.add_argument("--no-layer-train", action="store_true",
                     help="skip one layer's training forward and backward (esm_layer_fwd_train, esm_layer_bwd)")
+    ap.add_argument("--no-stack-train", action="store_true",
+                    help="skip the whole stack's training forward and backward (esm_stack_fwd_train, esm_stack_bwd)")
     ap.add_argument("--no-vendor-gemm", action="store_true", help="skip the hipBLASLt fc1-shape reference timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference dispatch for HBM byte counters)")
@@ -445,6 +448,65 @@ def bench_layer_train(enc, batch, cu, weights, m, steps: int, dev: str, stream) 
                          "flops_per_launch": fl_f + fl_b}}
 
 
+def bench_stack_train(enc, batch, cu, ids, emb, weights, m, steps: int, dev: str, stream) -> dict:
+    """The whole stack's training step on the batch: esm_stack_fwd_train from
+    the token ids (every layer's input and activations kept in HBM) then
+    esm_stack_bwd from dy N(0, 1) bf16 down to the embedding table's gradient;
+    HIP events on the library stream around back-to-back steps.  Algorithmic
+    flops per step: the layers' forward and backward flops of
+    bench_layer_train, times the depth (the embedding's gather and gradient
+    are not counted)."""
+    import torch
+    T, B, H, F, L = batch.T, batch.B, m.hidden, m.ffn, m.layers
+    g = torch.Generator(device=dev).manual_seed(17)
+    dy = torch.randn((T, H), device=dev, generator=g).to(torch.bfloat16)
+    y = torch.empty_like(dy)
+    dx = torch.empty_like(dy)
+    saved = torch.empty((enc.stack_saved_size(T),), dtype=torch.uint8, device=dev)
+    ws = enc.workspace(T, B)
+    bws = enc.stack_bwd_workspace(T, B)
+    grads = None
+    demb = torch.empty((m.vocab, H), dtype=torch.float32, device=dev)
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    n = max(3, steps // 10)
+
+    def fwd():
+        enc.stack_fwd_train(weights, cu, B, T, batch.max_seqlen, token_ids=ids, embedding=emb, x_out=y, saved=saved,
+                            workspace=ws, stream=stream)
+
+    def bwd():
+        nonlocal grads
+        _, grads, _ = enc.stack_bwd(weights, saved, dy, cu, B, T, dx=dx, grads=grads, token_ids=ids,
+                                    d_embedding=demb, workspace=bws, stream=stream)
+
+    fwd()
+    bwd()
+    torch.cuda.synchronize()
+    f_ms = b_ms = 0.0
+    for _ in range(n):
+        e0.record(stream)
+        fwd()
+        e1.record(stream)
+        bwd()
+        e2.record(stream)
+        torch.cuda.synchronize()
+        f_ms += e0.elapsed_time(e1) / n
+        b_ms += e1.elapsed_time(e2) / n
+    lin = 2.0 * T * (4 * H * H + 2 * H * F)
+    att = 4.0 * H * int((batch.lengths.astype(np.int64) ** 2).sum())
+    fl = L * (3.0 * lin + 3.5 * att)
+    step = f_ms + b_ms
+    tf = fl / (step * 1e-3) / 1e12
+    saved_gb = saved.numel() / 1e9
+    del dy, y, dx, saved, ws, bws, grads, demb
+    return {"what": f"esm_stack_fwd_train (from token ids) then esm_stack_bwd (to the embedding table's gradient), "
+                    f"{L} layers of the 650M widths on the batch, dy N(0, 1) bf16, {n} timed steps",
+            "fwd_train_ms": round(f_ms, 3), "bwd_ms": round(b_ms, 3), "ms_per_step": round(step, 3),
+            "residues_per_s": round(T / (step * 1e-3), 1), "tflops": round(tf, 1),
+            "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "saved_activation_gb": round(saved_gb, 2),
+            "flops_per_step": fl}
+
+
 def bench_layernorm_bwd(enc, T: int, H: int, steps: int, dev: str, stream) -> dict:
     """esm_layernorm_bwd on [T, H] (x N(0, 1), gamma 1 + N(0, 0.04), dy N(0, 1)
     bf16); HIP events over back-to-back calls.  HBM roofline on the
@@ -786,6 +848,10 @@ def main():
     layer_train = None
     if not args.no_layer_train and m.hidden == 1280:
         layer_train = bench_layer_train(enc, batch, cu, weights[0], m, args.steps, dev, stream)
+    stack_train = None
+    if not args.no_stack_train and m.hidden == 1280:
+        stack_train = bench_stack_train(enc, batch, cu, ids, emb_d, weights, m, args.steps, dev, stream)
+        torch.cuda.empty_cache()
 
     mxfp4 = None
     if not args.no_mxfp4:
@@ -932,6 +998,7 @@ def main():
         "linear_bwd": lin_bwd,
         "layernorm_bwd": ln_bwd,
         "layer_train": layer_train,
+        "stack_train": stack_train,
         "mxfp4_stack": mx_stack,
         "mixed_fp8_mxfp4_stack": mixed,
         "vendor_gemm_fc1": vendor,

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 20
+#define ESM_ABI_VERSION 21
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -552,7 +552,7 @@ esm_status esm_qkv_rope_bwd(esm_encoder* enc, const void* dqkv, void* dy,
  *   ESM_SAVED_H2   bf16 [T, H]              LN2 output
  *   ESM_SAVED_Z    bf16 [T, F]              fc1 output before GELU
  *   ESM_SAVED_A    bf16 [T, F]              GELU(z), fc2's input
- * (650M widths: 19,200 bytes per residue plus 80 of lse.) */
+ * (650M widths: 38,400 bytes per residue plus 80 of lse.) */
 typedef enum {
   ESM_SAVED_H1 = 0, ESM_SAVED_QKV = 1, ESM_SAVED_CTX = 2, ESM_SAVED_LSE = 3, ESM_SAVED_X1 = 4,
   ESM_SAVED_H2 = 5, ESM_SAVED_Z = 6, ESM_SAVED_A = 7, ESM_SAVED_COUNT = 8
@@ -608,6 +608,58 @@ esm_status esm_layer_bwd(esm_encoder* enc, const esm_layer_weights* w, int32_t l
                          const void* saved, size_t saved_bytes, const void* dy, void* dx, const esm_layer_grads* g,
                          const int32_t* cu_seqlens_dev, int32_t B, int64_t T, void* workspace,
                          size_t workspace_bytes, esm_stream_t stream);
+
+/* ------------------------------------------------------------ training stack
+ *
+ * The whole stack's training forward and backward ([BIO-ACC] 6: the training
+ * loop runs the model forward, then the loss's backward through every layer;
+ * [BIO-ACC] 3.2 PackedEsm: the stack starts from the embedding of the packed
+ * ids), built from the layer entries above: the forward keeps every layer's
+ * input and saved activations (650M widths: 41,040 bytes per residue per
+ * layer, 43.7 GB for 33 layers at T = 32,293: resident in HBM, no
+ * recomputation), the backward runs the layers' backward in reverse and then,
+ * for a stack that started from token ids, the embedding table's gradient.
+ * bf16 encoders only.
+ *
+ * Saved activations: one caller-owned device buffer of esm_stack_saved_size
+ * bytes (256-byte aligned); esm_stack_saved_layer gives, for layer l, the
+ * offset of its input X_l (bf16 [T, H]) and of its saved activations (the
+ * layout of esm_layer_saved_region). */
+esm_status esm_stack_saved_size(const esm_encoder* enc, int64_t T, size_t* bytes);
+/* ESM_ERR_SHAPE for l outside [0, num_hidden_layers). Host only. */
+esm_status esm_stack_saved_layer(const esm_encoder* enc, int64_t T, int32_t l, size_t* x_offset,
+                                 size_t* saved_offset);
+
+/* Training forward of the whole stack: x_out as esm_stack_fwd computes it
+ * through unprepared layers (each layer as esm_layer_fwd_train), from token
+ * ids and the embedding table, or from x_in when token_ids is NULL (x_in is
+ * copied into the saved buffer as X_0).  w holds num_hidden_layers weight
+ * sets; workspace esm_workspace_size(T, B).  Errors as esm_layer_fwd_train.
+ * Asynchronous on stream. */
+esm_status esm_stack_fwd_train(esm_encoder* enc, const esm_layer_weights* w, const int32_t* token_ids,
+                               const void* embedding, const void* x_in, void* x_out,
+                               const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host, int32_t B,
+                               int64_t T, int32_t max_seqlen, void* saved, size_t saved_bytes, void* workspace,
+                               size_t workspace_bytes, esm_stream_t stream);
+
+/* Workspace bytes esm_stack_bwd needs for T rows in B sequences (host only). */
+esm_status esm_stack_bwd_workspace_size(const esm_encoder* enc, int64_t T, int32_t B, size_t* bytes);
+
+/* Backward of the whole stack from esm_stack_fwd_train's saved activations
+ * (same T, B, cu_seqlens): given dy = dL/dx_out (bf16 [T, H]) writes
+ * dx = dL/dX_0 (bf16 [T, H]; may alias dy), the gradients of layer l into
+ * g[l] (num_hidden_layers entries, as esm_layer_bwd writes them), and, when
+ * token_ids is given (the forward's ids), d_embedding (fp32 [vocab, H],
+ * overwritten): row v is the sum of dX_0 over the residues whose id is v
+ * (ids clamped to [0, vocab) as the gather clamps them; zero for tokens
+ * absent from the batch).  token_ids and d_embedding are both given or both
+ * NULL (ESM_ERR_NULL otherwise); the table gradient takes vocab <= 64
+ * (ESM_ERR_UNSUPPORTED above).  Deterministic.  T = 0 or B = 0: returns
+ * without writing.  Errors as esm_layer_bwd.  Asynchronous on stream. */
+esm_status esm_stack_bwd(esm_encoder* enc, const esm_layer_weights* w, const void* saved, size_t saved_bytes,
+                         const void* dy, void* dx, const esm_layer_grads* g, const int32_t* token_ids,
+                         float* d_embedding, const int32_t* cu_seqlens_dev, int32_t B, int64_t T,
+                         void* workspace, size_t workspace_bytes, esm_stream_t stream);
 
 esm_status esm_layernorm_fwd(esm_encoder* enc, const void* x, const void* gamma,
                              const void* beta, void* y, int64_t M, esm_stream_t stream);

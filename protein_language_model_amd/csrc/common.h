@@ -394,6 +394,13 @@ hipError_t launch_attention_bwd(const AttnBwdArgs& a, hipStream_t st);
 hipError_t launch_transpose_pad(const bf16_t* in, int64_t R, int32_t C, bf16_t* out, int64_t Rp, hipStream_t st);
 hipError_t launch_colsum(const bf16_t* dy, int64_t M, int32_t N, float* part, float* db, hipStream_t st);
 int64_t colsum_chunks(int64_t M);
+// Embedding table gradient: dtable [vocab, H] fp32 = per-token sums of dx
+// [M, H] bf16 over the rows holding each token (ids clamped to [0, vocab) as
+// the gather clamps them), through part [colsum_chunks(M), vocab, H] fp32; H a
+// multiple of 64, vocab <= kEmbedBwdMaxVocab (its LDS accumulators).
+constexpr int32_t kEmbedBwdMaxVocab = 64;
+hipError_t launch_embed_bwd(const int32_t* ids, const bf16_t* dx, int64_t M, int32_t H, int32_t vocab, float* part,
+                            float* dtable, hipStream_t st);
 // dW GEMM of the linear backward: K slices (split-K) for M rows, and the
 // fixed-order sum of the slices' fp32 partials into bf16.
 int32_t wgrad_splits(int64_t M, int32_t N, int32_t K);

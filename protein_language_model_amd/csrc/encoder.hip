@@ -1868,6 +1868,166 @@ esm_status esm_layer_bwd(esm_encoder* e, const esm_layer_weights* w, int32_t lay
   });
 }
 
+namespace {
+
+// A stack's training activations: per layer, its input X_l (bf16 [T, H]) then
+// the layer's saved activations, each 256-byte aligned.
+struct StackSavedPlan {
+  SavedPlan sp;
+  size_t x_size, stride, total;
+};
+StackSavedPlan stack_saved_plan(const esm_config& c, int64_t T) {
+  StackSavedPlan q;
+  q.sp = saved_plan(c, T);
+  q.x_size = align256((size_t)(T > 0 ? T : 0) * (size_t)c.hidden_size * 2);
+  q.stride = q.x_size + q.sp.total;
+  q.total = q.stride * (size_t)c.num_hidden_layers;
+  return q;
+}
+
+// Stack backward workspace: the gradient passed between layers (bf16 [T, H]),
+// then the layer backward's workspace, which the embedding gradient's chunk
+// sums reuse once the layers are done.
+struct StackBwdPlan {
+  BwdPlan bp;
+  size_t layer, total;
+};
+StackBwdPlan stack_bwd_plan(const esm_config& c, int64_t T, int32_t B) {
+  StackBwdPlan q;
+  q.bp = bwd_plan(c, T, B);
+  const size_t t = (size_t)(T > 0 ? T : 0);
+  q.layer = align256(t * (size_t)c.hidden_size * 2);
+  const size_t emb = (size_t)colsum_chunks((int64_t)t) * (size_t)c.vocab_size * (size_t)c.hidden_size * 4;
+  q.total = q.layer + align256(q.bp.total > emb ? q.bp.total : emb);
+  return q;
+}
+
+}  // namespace
+
+esm_status esm_stack_saved_size(const esm_encoder* e, int64_t T, size_t* bytes) {
+  g_last_error.clear();
+  if (!e || !bytes) return fail(ESM_ERR_NULL, "NULL argument");
+  if (T < 0) return fail(ESM_ERR_SHAPE, "T < 0");
+  *bytes = stack_saved_plan(e->cfg, T).total;
+  return ok();
+}
+
+esm_status esm_stack_saved_layer(const esm_encoder* e, int64_t T, int32_t l, size_t* x_offset, size_t* saved_offset) {
+  g_last_error.clear();
+  if (!e || !x_offset || !saved_offset) return fail(ESM_ERR_NULL, "NULL argument");
+  if (T < 0) return fail(ESM_ERR_SHAPE, "T < 0");
+  if (l < 0 || l >= e->cfg.num_hidden_layers)
+    return fail(ESM_ERR_SHAPE, "layer %d outside [0, %d)", l, e->cfg.num_hidden_layers);
+  const StackSavedPlan q = stack_saved_plan(e->cfg, T);
+  *x_offset = q.stride * (size_t)l;
+  *saved_offset = *x_offset + q.x_size;
+  return ok();
+}
+
+esm_status esm_stack_bwd_workspace_size(const esm_encoder* e, int64_t T, int32_t B, size_t* bytes) {
+  g_last_error.clear();
+  if (!e || !bytes) return fail(ESM_ERR_NULL, "NULL argument");
+  if (T < 0 || B < 0) return fail(ESM_ERR_SHAPE, "negative T or B");
+  *bytes = stack_bwd_plan(e->cfg, T, B).total;
+  return ok();
+}
+
+esm_status esm_stack_fwd_train(esm_encoder* e, const esm_layer_weights* w, const int32_t* ids, const void* emb,
+                               const void* x_in, void* x_out, const int32_t* cu_dev, const int32_t* cu_host, int32_t B,
+                               int64_t T, int32_t max_seqlen, void* saved, size_t saved_bytes, void* ws,
+                               size_t ws_bytes, esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  if (!w) return fail(ESM_ERR_NULL, "weights are NULL");
+  const int L = e->cfg.num_hidden_layers, H = e->cfg.hidden_size;
+  esm_status s;
+  for (int l = 0; l < L; ++l)
+    if ((s = check_train_call(e, &w[l], l, T, B))) return s;
+  if (!x_out || !cu_dev) return fail(ESM_ERR_NULL, "x_out or cu_seqlens_dev is NULL");
+  if (!aligned16(x_out)) return fail(ESM_ERR_UNSUPPORTED, "x_out not 16-byte aligned");
+  if (ids) {
+    if (!emb) return fail(ESM_ERR_NULL, "token_ids given without an embedding table");
+    if (!aligned16(emb)) return fail(ESM_ERR_UNSUPPORTED, "embedding not 16-byte aligned");
+  } else {
+    if (!x_in) return fail(ESM_ERR_NULL, "x_in is NULL (and no token ids)");
+    if (!aligned16(x_in)) return fail(ESM_ERR_UNSUPPORTED, "x_in not 16-byte aligned");
+  }
+  if ((s = check_cu_host(e, cu_host, B, T, max_seqlen))) return s;
+  const StackSavedPlan q = stack_saved_plan(e->cfg, T);
+  if (!saved || ((uintptr_t)saved & 255u) || saved_bytes < q.total)
+    return fail(ESM_ERR_WORKSPACE, "saved activations: NULL, not 256-byte aligned or %zu bytes < %zu", saved_bytes,
+                q.total);
+  if (T == 0 || B == 0) return ok();
+  Plan p;
+  if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  char* sv = (char*)saved;
+  if (ids) {
+    s = timed(e, ESM_K_EMBED, st, "embedding", [&] {
+      return launch_embed(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)sv, T, H, st);
+    });
+    if (s) return s;
+  } else {
+    HIP_TRY(hipMemcpyAsync(sv, x_in, (size_t)T * H * 2, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync");
+  }
+  for (int l = 0; l < L; ++l) {
+    void* out = l + 1 < L ? (void*)(sv + q.stride * (l + 1)) : x_out;
+    if ((s = esm_layer_fwd_train(e, &w[l], l, sv + q.stride * l, out, cu_dev, cu_host, B, T, max_seqlen,
+                                 sv + q.stride * l + q.x_size, q.sp.total, ws, ws_bytes, stream)))
+      return s;
+  }
+  return ok();
+}
+
+esm_status esm_stack_bwd(esm_encoder* e, const esm_layer_weights* w, const void* saved, size_t saved_bytes,
+                         const void* dy, void* dx, const esm_layer_grads* g, const int32_t* ids, float* d_emb,
+                         const int32_t* cu_dev, int32_t B, int64_t T, void* ws, size_t ws_bytes,
+                         esm_stream_t stream) {
+  g_last_error.clear();
+  if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
+  if (!w || !g) return fail(ESM_ERR_NULL, "weights or gradients are NULL");
+  const int L = e->cfg.num_hidden_layers, H = e->cfg.hidden_size, V = e->cfg.vocab_size;
+  esm_status s;
+  for (int l = 0; l < L; ++l)
+    if ((s = check_train_call(e, &w[l], l, T, B))) return s;
+  if (!dy || !dx || !cu_dev) return fail(ESM_ERR_NULL, "dy, dx or cu_seqlens_dev is NULL");
+  if (!aligned16(dy) || !aligned16(dx)) return fail(ESM_ERR_UNSUPPORTED, "dy/dx not 16-byte aligned");
+  if ((ids == nullptr) != (d_emb == nullptr))
+    return fail(ESM_ERR_NULL, "token_ids and d_embedding go together (one of them is NULL)");
+  if (ids) {
+    if (V > kEmbedBwdMaxVocab)
+      return fail(ESM_ERR_UNSUPPORTED, "the embedding gradient takes vocab <= %d (vocab %d)", kEmbedBwdMaxVocab, V);
+    if ((uintptr_t)d_emb & 3u) return fail(ESM_ERR_UNSUPPORTED, "d_embedding not 4-byte aligned");
+  }
+  const StackSavedPlan q = stack_saved_plan(e->cfg, T);
+  if (!saved || ((uintptr_t)saved & 255u) || saved_bytes < q.total)
+    return fail(ESM_ERR_WORKSPACE, "saved activations: NULL, not 256-byte aligned or %zu bytes < %zu", saved_bytes,
+                q.total);
+  const StackBwdPlan bq = stack_bwd_plan(e->cfg, T, B);
+  if (!ws || ((uintptr_t)ws & 255u) || ws_bytes < bq.total)
+    return fail(ESM_ERR_WORKSPACE, "workspace: NULL, not 256-byte aligned or %zu bytes < %zu", ws_bytes, bq.total);
+  if (T == 0 || B == 0) return ok();
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
+  const char* sv = (const char*)saved;
+  char* gbuf = (char*)ws;   // the gradient between layers; each middle layer updates it in place
+  char* lws = (char*)ws + bq.layer;
+  const size_t lws_bytes = ws_bytes - bq.layer;
+  const void* cur = dy;
+  for (int l = L - 1; l >= 0; --l) {
+    void* out = l == 0 ? dx : (void*)gbuf;
+    if ((s = esm_layer_bwd(e, &w[l], l, sv + q.stride * l, sv + q.stride * l + q.x_size, q.sp.total, cur, out, &g[l],
+                           cu_dev, B, T, lws, lws_bytes, stream)))
+      return s;
+    cur = out;
+  }
+  if (!ids) return ok();
+  return timed(e, ESM_K_LINEAR_BWD, st, "embedding backward", [&] {
+    return launch_embed_bwd(ids, (const bf16_t*)dx, T, H, V, (float*)lws, d_emb, st);
+  });
+}
+
 esm_status esm_layernorm_fwd(esm_encoder* e, const void* x, const void* gamma, const void* beta, void* y, int64_t M,
                              esm_stream_t stream) {
   g_last_error.clear();

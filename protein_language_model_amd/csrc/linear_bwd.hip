@@ -371,6 +371,48 @@ __global__ __launch_bounds__(256) void k_qkv_rope_bwd(const bf16_t* __restrict__
   *(u32x4*)(dst + 32 + i0) = ob;
 }
 
+// ------------------------------------------------------------ embedding backward
+//
+// Under X0 = E[ids] the table gradient of token v is the sum of dX0 over the
+// residues holding v.  k_embed_bwd_partial: per 1024-row chunk and 64
+// columns, wave w walks rows w, w + 4, ... of the chunk in order and adds
+// each into its own LDS accumulator row of that row's token (one column per
+// lane, so no two lanes touch one word and the order is fixed), then the four
+// waves' accumulators are added in order into part [chunk, vocab, H];
+// k_embed_bwd_final adds the chunks in order.  Token ids are clamped to
+// [0, vocab) as the gather clamps them.
+__global__ __launch_bounds__(256) void k_embed_bwd_partial(const int32_t* __restrict__ ids,
+                                                           const bf16_t* __restrict__ dx, int64_t M, int32_t H,
+                                                           int32_t vocab, float* __restrict__ part) {
+  extern __shared__ float acc[];   // [4][vocab][64]
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * kSumRows;
+  const int n0 = blockIdx.y * 64;
+  float* mine = acc + (size_t)wv * vocab * 64 + lane;
+  for (int v = 0; v < vocab; ++v) mine[v * 64] = 0.f;
+  const int64_t mend = m0 + kSumRows < M ? m0 + kSumRows : M;
+  for (int64_t m = m0 + wv; m < mend; m += 4) {
+    int id = ids[m];
+    id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+    mine[id * 64] += bf2f(dx[m * H + n0 + lane]);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < vocab * 64; i += 256) {
+    const size_t a = (size_t)vocab * 64;
+    const float s = ((acc[i] + acc[a + i]) + acc[2 * a + i]) + acc[3 * a + i];
+    part[((int64_t)blockIdx.x * vocab + i / 64) * H + n0 + (i & 63)] = s;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_embed_bwd_final(const float* __restrict__ part, int64_t chunks, int64_t n,
+                                                         float* __restrict__ dtable) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int64_t c = 0; c < chunks; ++c) s += part[c * n + i];
+  dtable[i] = s;
+}
+
 }  // namespace
 
 int64_t colsum_chunks(int64_t M) { return (M + kSumRows - 1) / kSumRows; }
@@ -460,6 +502,19 @@ hipError_t launch_colsum(const bf16_t* dy, int64_t M, int32_t N, float* part, fl
     hipLaunchKernelGGL(k_colsum_partial, dim3((unsigned)chunks, (unsigned)(N / 64)), dim3(256), 0, st, dy, M, N,
                        part);
   hipLaunchKernelGGL(k_colsum_final, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, part, chunks, N, N, db);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed_bwd(const int32_t* ids, const bf16_t* dx, int64_t M, int32_t H, int32_t vocab, float* part,
+                            float* dtable, hipStream_t st) {
+  if (H <= 0 || vocab <= 0) return hipSuccess;
+  if (H % 64 || vocab > kEmbedBwdMaxVocab) return hipErrorInvalidValue;
+  const int64_t chunks = colsum_chunks(M);
+  if (chunks > 0)
+    hipLaunchKernelGGL(k_embed_bwd_partial, dim3((unsigned)chunks, (unsigned)(H / 64)), dim3(256),
+                       (unsigned)(4 * vocab * 64 * sizeof(float)), st, ids, dx, M, H, vocab, part);
+  const int64_t n = (int64_t)vocab * H;
+  hipLaunchKernelGGL(k_embed_bwd_final, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, chunks, n, dtable);
   return hipGetLastError();
 }
 

@@ -131,6 +131,13 @@ SIGNATURES = {
     "esm_layer_bwd_workspace_size": (_i32, [_p, _i64, _i32, ctypes.POINTER(_sz)]),
     "esm_layer_bwd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _i32, _p, _p, _sz, _p, _p,
                              ctypes.POINTER(EsmLayerGrads), _p, _i32, _i64, _p, _sz, _p]),
+    "esm_stack_saved_size": (_i32, [_p, _i64, ctypes.POINTER(_sz)]),
+    "esm_stack_saved_layer": (_i32, [_p, _i64, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
+    "esm_stack_fwd_train": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _p, _p, _p, _p, _p, _p, _i32, _i64, _i32,
+                                   _p, _sz, _p, _sz, _p]),
+    "esm_stack_bwd_workspace_size": (_i32, [_p, _i64, _i32, ctypes.POINTER(_sz)]),
+    "esm_stack_bwd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _p, _sz, _p, _p, ctypes.POINTER(EsmLayerGrads),
+                             _p, _p, _p, _i32, _i64, _p, _sz, _p]),
     "esm_profile_enable": (_i32, [_p, _i32]),
     "esm_profile_read": (_i32, [_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
     "esm_check_cu_seqlens": (_i32, [_p, _i32, _i64, _i32, _i32]),
@@ -347,11 +354,7 @@ class Encoder:
         if dx is None:
             dx = torch.empty_like(dy)
         if grads is None:
-            shapes = {"ln1_gamma": (H,), "ln1_beta": (H,), "w_qkv": (3 * H, H), "b_qkv": (3 * H,), "w_out": (H, H),
-                      "b_out": (H,), "ln2_gamma": (H,), "ln2_beta": (H,), "w_fc1": (F, H), "b_fc1": (F,),
-                      "w_fc2": (H, F), "b_fc2": (H,)}
-            grads = {n: torch.empty(sh, dtype=torch.bfloat16 if n.startswith("w_") else torch.float32, device=dev)
-                     for n, sh in shapes.items()}
+            grads = self._grad_tensors(dev)
         if workspace is None:
             workspace = self.layer_bwd_workspace(T, B)
         w = layer_weights_struct(weights)
@@ -362,6 +365,85 @@ class Encoder:
               _ptr(dy), _ptr(dx), ctypes.byref(g), _ptr(cu_seqlens), int(B), int(T), _ptr(workspace),
               workspace.numel(), _stream(stream))
         return dx, grads
+
+    def _grad_tensors(self, dev):
+        import torch
+        H, F = self.cfg.hidden_size, self.cfg.intermediate_size
+        shapes = {"ln1_gamma": (H,), "ln1_beta": (H,), "w_qkv": (3 * H, H), "b_qkv": (3 * H,), "w_out": (H, H),
+                  "b_out": (H,), "ln2_gamma": (H,), "ln2_beta": (H,), "w_fc1": (F, H), "b_fc1": (F,),
+                  "w_fc2": (H, F), "b_fc2": (H,)}
+        return {n: torch.empty(sh, dtype=torch.bfloat16 if n.startswith("w_") else torch.float32, device=dev)
+                for n, sh in shapes.items()}
+
+    def stack_saved_size(self, T: int) -> int:
+        n = ctypes.c_size_t()
+        _call("esm_stack_saved_size", self._h, int(T), ctypes.byref(n))
+        return int(n.value)
+
+    def stack_saved_layer(self, saved, T: int, l: int, name: str = None):
+        """Layer l's input X_l (name None, bf16 [T, H]) or one of its saved
+        regions (a name of SAVED_REGIONS, as saved_region returns it) inside
+        esm_stack_fwd_train's buffer."""
+        xo, so = ctypes.c_size_t(), ctypes.c_size_t()
+        _call("esm_stack_saved_layer", self._h, int(T), int(l), ctypes.byref(xo), ctypes.byref(so))
+        if name is None:
+            n = int(T) * self.hidden * 2
+            return saved[xo.value:xo.value + n].view(__import__("torch").bfloat16).view(int(T), self.hidden)
+        return self.saved_region(saved[so.value:], T, name)
+
+    def stack_fwd_train(self, weights: Sequence[Dict], cu_seqlens, B: int, T: int, max_seqlen: int, *,
+                        token_ids=None, embedding=None, x_in=None, x_out=None, saved=None, cu_seqlens_host=None,
+                        workspace=None, stream=None):
+        """esm_stack_fwd_train: returns (x_out, saved)."""
+        import torch
+        if len(weights) != self.cfg.num_hidden_layers:
+            raise ValueError(f"{len(weights)} layer weight sets for {self.cfg.num_hidden_layers} layers")
+        dev = f"cuda:{self.device}"
+        if x_out is None:
+            x_out = torch.empty((T, self.hidden), dtype=torch.bfloat16, device=dev)
+        if saved is None:
+            saved = torch.empty((max(self.stack_saved_size(T), 256),), dtype=torch.uint8, device=dev)
+        if workspace is None:
+            workspace = self.workspace(T, B)
+        arr = (EsmLayerWeights * len(weights))(*[layer_weights_struct(w) for w in weights])
+        cuh = _host_i32(cu_seqlens_host)
+        _call("esm_stack_fwd_train", self._h, arr, _ptr(token_ids), _ptr(embedding), _ptr(x_in), _ptr(x_out),
+              _ptr(cu_seqlens), cuh.ctypes.data_as(ctypes.c_void_p) if cuh is not None else None, int(B), int(T),
+              int(max_seqlen), _ptr(saved), saved.numel(), _ptr(workspace), workspace.numel(), _stream(stream))
+        return x_out, saved
+
+    def stack_bwd_workspace(self, T: int, B: int):
+        import torch
+        n = ctypes.c_size_t()
+        _call("esm_stack_bwd_workspace_size", self._h, int(T), int(B), ctypes.byref(n))
+        return torch.empty((max(int(n.value), 256),), dtype=torch.uint8, device=f"cuda:{self.device}")
+
+    def stack_bwd(self, weights: Sequence[Dict], saved, dy, cu_seqlens, B: int, T: int, *, dx=None, grads=None,
+                  token_ids=None, d_embedding=None, workspace=None, stream=None):
+        """esm_stack_bwd: returns (dx, [per-layer gradient dicts], d_embedding
+        fp32 [vocab, H] or None); d_embedding is allocated when token_ids are
+        given and it is not."""
+        import torch
+        L = self.cfg.num_hidden_layers
+        if len(weights) != L:
+            raise ValueError(f"{len(weights)} layer weight sets for {L} layers")
+        if dx is None:
+            dx = torch.empty_like(dy)
+        if grads is None:
+            grads = [self._grad_tensors(dy.device) for _ in range(L)]
+        if token_ids is not None and d_embedding is None:
+            d_embedding = torch.empty((self.cfg.vocab_size, self.hidden), dtype=torch.float32, device=dy.device)
+        if workspace is None:
+            workspace = self.stack_bwd_workspace(T, B)
+        arr = (EsmLayerWeights * L)(*[layer_weights_struct(w) for w in weights])
+        garr = (EsmLayerGrads * L)()
+        for l in range(L):
+            for n in LAYER_WEIGHT_NAMES:
+                setattr(garr[l], n, _ptr(grads[l][n]))
+        _call("esm_stack_bwd", self._h, arr, _ptr(saved), saved.numel(), _ptr(dy), _ptr(dx), garr, _ptr(token_ids),
+              _ptr(d_embedding), _ptr(cu_seqlens), int(B), int(T), _ptr(workspace), workspace.numel(),
+              _stream(stream))
+        return dx, grads, d_embedding
 
     def layer_fwd_noalloc(self, weights, x_in, cu_seqlens, B: int, T: int, max_seqlen: int, *, x_out,
                           layer_idx: int = 0, cu_seqlens_host=None, stream=None):

@@ -233,6 +233,13 @@ def test_training_layer_calls_fail_cleanly_without_a_handle():
                    p, ctypes.c_size_t(0), None)[0] == 1
     assert _status("esm_layer_bwd", None, w, 0, p, p, ctypes.c_size_t(0), p, p, g, p, 1, ctypes.c_int64(1), p,
                    ctypes.c_size_t(0), None)[0] == 1
+    assert _status("esm_stack_saved_size", None, ctypes.c_int64(10), ctypes.byref(n))[0] == 1
+    assert _status("esm_stack_saved_layer", None, ctypes.c_int64(10), 0, ctypes.byref(off), ctypes.byref(n))[0] == 1
+    assert _status("esm_stack_bwd_workspace_size", None, ctypes.c_int64(10), 1, ctypes.byref(n))[0] == 1
+    assert _status("esm_stack_fwd_train", None, w, None, None, p, p, p, None, 1, ctypes.c_int64(1), 1, p,
+                   ctypes.c_size_t(0), p, ctypes.c_size_t(0), None)[0] == 1
+    assert _status("esm_stack_bwd", None, w, p, ctypes.c_size_t(0), p, p, g, None, None, p, 1, ctypes.c_int64(1), p,
+                   ctypes.c_size_t(0), None)[0] == 1
 
 
 def test_e5m2_wgrad_workspace_size():
