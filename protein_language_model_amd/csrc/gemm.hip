@@ -51,15 +51,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // GELU(z) = z Phi(z), Phi the standard normal CDF (the exact, erf form; the
 // pages name a fused activation only).  With q = Phi(-|z|), GELU(z) is
-// z (1 - q) for z >= 0 and z q for z < 0, so the negative tail is a product
-// (no cancellation, sign kept).  q = 2^P(|z|) for |z| < 9, P a degree-6
-// polynomial fitted to log2 Phi(-a) on [0, 9] (gelu_tail_fit.py), and 0
-// beyond (Phi(-9) < 2^-62).  In fp32 |q - Phi(-|z|)| <= 6.3e-7, and relative
-// to Phi(-|z|) <= 3e-5 for |z| < 4 and <= 6e-4 for |z| < 5: below half a bf16
-// ulp of the result everywhere.  The epilogue's VALU work is not hidden behind
-// MFMAs (all waves of a tile reach it together), so the degree is the
-// smallest that keeps that margin.  GELU(+inf) = +inf, GELU(-inf) = NaN (as
-// -inf * 0), NaN stays NaN.
+// z (1 - q) for z >= 0 and z q for z < 0, i.e. max(z, 0) - |z| q in both
+// cases: one FMA, no select, and the negative tail is a product (no
+// cancellation, sign kept).  q = 2^P(t), t = min(|z|, 9), P a degree-6
+// polynomial fitted to log2 Phi(-a) on [0, 9] (gelu_tail_fit.py): beyond 9
+// the tail term is held at its value there, 9 * 2^P(9) = 2.3e-18, so
+// GELU(z) = z for z >= 9 and -2.3e-18 for z <= -9 (exactly: 0 > GELU(z) >
+// -1.1e-18).  In fp32 |q - Phi(-|z|)| <= 6.3e-7, and relative to Phi(-|z|)
+// <= 3e-5 for |z| < 4 and <= 6e-4 for |z| < 5: below half a bf16 ulp of the
+// result everywhere.  The epilogue's VALU work is not hidden behind MFMAs
+// (all waves of a tile reach it together), so the degree is the smallest that
+// keeps that margin and the form the one with fewest instructions (the
+// minimum and maximum propagate NaN: GELU(NaN) = NaN, GELU(+inf) = +inf,
+// GELU(-inf) = -2.3e-18).
 constexpr float kGeluP0 = -0.9999982118606567f;
 constexpr float kGeluP1 = -1.1511716842651367f;
 constexpr float kGeluP2 = -0.4588053524494171f;
@@ -68,15 +72,14 @@ constexpr float kGeluP4 = 0.008116660639643669f;
 constexpr float kGeluP5 = -0.0007859239703975618f;
 constexpr float kGeluP6 = 3.5450411814963445e-05f;
 __device__ __forceinline__ float gelu(float z) {
-  const float az = fabsf(z);
-  float p = fmaf(kGeluP6, az, kGeluP5);
-  p = fmaf(p, az, kGeluP4);
-  p = fmaf(p, az, kGeluP3);
-  p = fmaf(p, az, kGeluP2);
-  p = fmaf(p, az, kGeluP1);
-  p = fmaf(p, az, kGeluP0);
-  const float q = az < 9.0f ? __builtin_amdgcn_exp2f(p) : 0.0f;  // P is only fitted below 9
-  return z * (z >= 0.0f ? 1.0f - q : q);
+  const float t = __builtin_elementwise_minimum(fabsf(z), 9.0f);  // P is only fitted up to 9
+  float p = fmaf(kGeluP6, t, kGeluP5);
+  p = fmaf(p, t, kGeluP4);
+  p = fmaf(p, t, kGeluP3);
+  p = fmaf(p, t, kGeluP2);
+  p = fmaf(p, t, kGeluP1);
+  p = fmaf(p, t, kGeluP0);
+  return fmaf(-t, __builtin_amdgcn_exp2f(p), __builtin_elementwise_maximum(z, 0.0f));
 }
 
 template <int DT>

@@ -22,19 +22,19 @@ def f32(x):
 
 
 def gelu_as_kernel(z):
-    """Horner in |z| with one rounding per FMA, exp2 below |z| = 9 (0 beyond),
-    then z (1 - q) or z q."""
+    """Horner in t = min(|z|, 9) with one rounding per FMA, q = exp2 of it,
+    then max(z, 0) - t q with one rounding (NaN propagating through the
+    minimum and the maximum, as the kernel's IEEE 754-2019 forms do)."""
     z = f32(z)
     co = kernel_coefficients()
-    a = np.abs(z)
     with np.errstate(invalid="ignore", over="ignore"):
-        p = np.full_like(a, co[-1])
+        t = np.minimum(np.abs(z), np.float32(9))
+        p = np.full_like(t, co[-1])
         for ck in co[-2::-1]:
-            p = f32(p.astype(np.float64) * a + np.float64(ck))
-        q = np.where(a < 9, f32(np.exp2(p.astype(np.float64))), np.float32(0))
-    t = np.where(z >= 0, f32(np.float32(1.0) - q), q)
-    with np.errstate(invalid="ignore", over="ignore"):
-        return f32(z.astype(np.float64) * t)
+            p = f32(p.astype(np.float64) * t + np.float64(ck))
+        q = f32(np.exp2(p.astype(np.float64)))
+        relu = np.where(np.isnan(z), z, np.where(z > 0, z, np.float32(0)))
+        return f32(relu.astype(np.float64) - t.astype(np.float64) * q.astype(np.float64))
 
 
 def test_tail_probability_bounds():
@@ -67,18 +67,21 @@ def test_gelu_against_exact():
     assert np.all((np.abs(g - exact) <= 2.0 ** -9 * np.abs(exact))[normal & (np.abs(zz) < 5)])
     assert np.all(np.abs(g - exact) <= bound + 1e-30)
     # the sign of the result is the sign of z (no cancellation to +0 in the
-    # tail); from z = -9 down the result is -0
+    # tail); from z = -9 down the tail term is held at its value at 9: one
+    # negative constant within 2.5e-18 of the exact value
     inner = (zz != 0) & (np.abs(zz) < 9) & (np.abs(exact) > 1e-37)
     assert np.all(np.sign(g[inner]) == np.sign(zz[inner]))
     far = zz <= -9
-    assert np.all((g[far] == 0) & np.signbit(g[far]))
+    assert np.all(g[far] == g[far][0]) and -2.5e-18 < g[far][0] < 0
+    assert np.all(np.abs(g[far] - exact[far]) < 2.5e-18)
 
 
 def test_gelu_special_values():
     g = gelu_as_kernel(np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 1e30, -1e30, -9.5, 9.5]))
-    assert g[0] == 0 and g[1] == 0 and np.signbit(g[1])
+    tail = gelu_as_kernel(np.array([-9.0]))[0]
+    assert -2.5e-18 < tail < 0
+    assert g[0] == 0 and g[1] == 0
     assert g[2] == np.inf
-    assert np.isnan(g[3]) and np.isnan(g[4])   # -inf * Phi(-inf) = -inf * 0
+    assert g[3] == tail and np.isnan(g[4])   # -inf: the held tail value; NaN stays NaN
     assert g[5] == np.float32(1e30)
-    assert g[6] == 0 and np.signbit(g[6])
-    assert g[7] == 0 and np.signbit(g[7]) and g[8] == np.float32(9.5)
+    assert g[6] == tail and g[7] == tail and g[8] == np.float32(9.5)
