@@ -319,21 +319,24 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
             if (kb * 32 + 8 * (r >> 2) + (r & 3) >= lim) st[kb][r] = -INFINITY;
       }
       // Row max and row sum in four independent chains (short dependency
-      // chains for the VALU); the chains combine in a fixed order.
+      // chains for the VALU); the chains combine in a fixed order.  The
+      // maximum is IEEE 754-2019's (NaN propagating, no input
+      // canonicalisation), which gfx950 issues three operands at a time.
       float m4[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         m4[c] = st[c >> 1][8 * (c & 1)];
 #pragma unroll
-        for (int r = 1; r < 8; ++r) m4[c] = fmaxf(m4[c], st[c >> 1][8 * (c & 1) + r]);
+        for (int r = 1; r < 8; ++r) m4[c] = __builtin_elementwise_maximum(m4[c], st[c >> 1][8 * (c & 1) + r]);
       }
-      float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+      float mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m4[0], m4[1]),
+                                               __builtin_elementwise_maximum(m4[2], m4[3]));
       {
         float a, b;
         pair_halves(mx, a, b);
-        mx = fmaxf(a, b);
+        mx = __builtin_elementwise_maximum(a, b);
       }
-      const float m_new = fmaxf(m_i, mx);
+      const float m_new = __builtin_elementwise_maximum(m_i, mx);
       // Lazy rescaling: the running maximum (and with it o and l) moves only
       // when some row of the wave grew by more than 8 in exp2 units; until
       // then the probabilities are taken against the older maximum and stay
@@ -353,14 +356,17 @@ __device__ __forceinline__ void attend(const bf16_t* __restrict__ Qg, const bf16
           for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
       }
       const float mc = (((kMode & kBias) != 0 && m_i == -INFINITY) ? 0.f : m_i) * kS;
-      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      // each chain starts at its first probability (the same sum as from 0:
+      // probabilities are never -0)
+      float s4[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = exp2_fast(fmaf(st[kb][r], kS, -mc));
           st[kb][r] = p;
-          s4[2 * kb + (r >> 3)] += p;
+          if ((r & 7) == 0) s4[2 * kb + (r >> 3)] = p;
+          else s4[2 * kb + (r >> 3)] += p;
         }
       l_i += (s4[0] + s4[1]) + (s4[2] + s4[3]);
 
