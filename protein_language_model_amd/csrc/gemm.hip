@@ -35,6 +35,8 @@
 //    time so a row panel of x and the weight panels stay in that XCD's L2.
 #include "common.h"
 
+#include <type_traits>
+
 namespace esm {
 
 namespace {
@@ -456,22 +458,42 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     }
   } else if constexpr (FM * FN > 8) {
     // Large wave tiles (160 x 64: 160 accumulator registers): one fragment
-    // set, as for E4M3.
+    // set, as for E4M3.  The fragment addresses of each (stage, sub-step)
+    // are computed once (the 32-row blocks then differ by immediate offsets)
+    // and the loop is unrolled over the two stages, so a K step spends no
+    // vector instructions on LDS addresses.
     frag_t xf[FM], wf[FN];
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
+    const unsigned char* ax[2][KK];
+    const unsigned char* aw[2][KK];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int ch = ((kk * 2 + lhalf) ^ swz) * 16;
+        ax[b][kk] = smem + b * kStage + (wm * WTM + lrow) * kRowBytes + ch;
+        aw[b][kk] = smem + b * kStage + BM * kRowBytes + (wn * WTN + lrow) * kRowBytes + ch;
+      }
+    auto kstep = [&](int kt, auto stage) {
+      constexpr int cur = decltype(stage)::value;
       const bool more = kt + 1 < nk;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         __builtin_amdgcn_sched_barrier(0);
         if (more && kk < kParts) issue_part((kt + 1) * kRowBytes, cur ^ 1, kk, kParts);
-        load_frags(xf, wf, cur, kk);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) xf[i] = *(const frag_t*)(ax[cur][kk] + i * 32 * kRowBytes);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) wf[j] = *(const frag_t*)(aw[cur][kk] + j * 32 * kRowBytes);
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(xf, wf);
       }
       __builtin_amdgcn_sched_barrier(0);
       vm_wait_all();
       __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+      kstep(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < nk) kstep(kt + 1, std::integral_constant<int, 1>{});
     }
   } else {
   frag_t xf[2][FM], wf[2][FN];
