@@ -47,6 +47,13 @@ constexpr int kRowBytes = 128;  // bytes of each tile row per K step
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// lds_dma16 with a wave-uniform base in scalar registers and a per-lane 32-bit
+// byte offset (the instruction's saddr form).
+__device__ __forceinline__ void lds_dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -208,19 +215,25 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   // NW even).
   const int lr8 = lane >> 3;
   const int lchunk = ((lane & 7) ^ (((wave & 1) << 2) | (lane >> 4))) * 16;  // bytes
-  const unsigned char* xsrc[XRB];
-  const unsigned char* wsrc[WRB];
+  // Each operand's loads address its tile's first row (a wave-uniform base
+  // in scalar registers, advanced by a scalar add per K step) plus a 32-bit
+  // per-lane offset of at most (BM - 1) rows: no vector instructions on
+  // global addresses in the K loop.
+  const int64_t rowb = (int64_t)K * EBN / EBD;  // bytes per operand row
+  const unsigned char* const xbase = (const unsigned char*)a.x + m0 * rowb + (int64_t)split * Kl * EBN / EBD;
+  const unsigned char* const wbase = (const unsigned char*)a.w + (int64_t)n0 * rowb + (int64_t)split * Kl * EBN / EBD;
+  uint32_t xoff[XRB], woff[WRB];
 #pragma unroll
   for (int i = 0; i < XRB; ++i) {
     int64_t r = m0 + (int64_t)(wave + NW * i) * RPI + lr8;
     r = r < M ? r : M - 1;
-    xsrc[i] = (const unsigned char*)a.x + r * K * EBN / EBD + (int64_t)split * Kl * EBN / EBD + lchunk;
+    xoff[i] = (uint32_t)((r - m0) * rowb + lchunk);
   }
 #pragma unroll
   for (int i = 0; i < WRB; ++i) {
     int r = n0 + (wave + NW * i) * RPI + lr8;
     r = r < N ? r : N - 1;
-    wsrc[i] = (const unsigned char*)a.w + (int64_t)r * K * EBN / EBD + (int64_t)split * Kl * EBN / EBD + lchunk;
+    woff[i] = (uint32_t)((int64_t)(r - n0) * rowb + lchunk);
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
@@ -255,9 +268,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     for (int i = 0; i < NL; ++i) {
       if (i < p * NL / np || i >= (p + 1) * NL / np) continue;
       if (i < XRB)
-        lds_dma16(xsrc[i] + kbyte, base + (uint32_t)((wave_u + NW * i) * RPI * kRowBytes));
+        lds_dma16s(xbase + kbyte, xoff[i], base + (uint32_t)((wave_u + NW * i) * RPI * kRowBytes));
       else
-        lds_dma16(wsrc[i - XRB] + kbyte, base + (uint32_t)((BM + (wave_u + NW * (i - XRB)) * RPI) * kRowBytes));
+        lds_dma16s(wbase + kbyte, woff[i - XRB], base + (uint32_t)((BM + (wave_u + NW * (i - XRB)) * RPI) * kRowBytes));
     }
     if (p == 0) issue_scales(kbyte / kRowBytes, buf);
   };
