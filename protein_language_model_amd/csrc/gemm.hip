@@ -476,15 +476,17 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     // and the loop is unrolled over the two stages, so a K step spends no
     // vector instructions on LDS addresses.
     frag_t xf[FM], wf[FN];
-    const unsigned char* ax[2][KK];
-    const unsigned char* aw[2][KK];
+    typedef const __attribute__((address_space(3))) frag_t* lds_frag_ptr;
+    uint32_t ax[2][KK], aw[2][KK];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const int ch = ((kk * 2 + lhalf) ^ swz) * 16;
-        ax[b][kk] = smem + b * kStage + (wm * WTM + lrow) * kRowBytes + ch;
-        aw[b][kk] = smem + b * kStage + BM * kRowBytes + (wn * WTN + lrow) * kRowBytes + ch;
+        const uint32_t ch = (uint32_t)(((kk * 2 + lhalf) ^ swz) * 16);
+        ax[b][kk] = lds0 + (uint32_t)(b * kStage + (wm * WTM + lrow) * kRowBytes) + ch;
+        aw[b][kk] = lds0 + (uint32_t)(b * kStage + BM * kRowBytes + (wn * WTN + lrow) * kRowBytes) + ch;
+        // kept whole in registers (not re-derived from a shared part per step)
+        asm volatile("" : "+v"(ax[b][kk]), "+v"(aw[b][kk]));
       }
     auto kstep = [&](int kt, auto stage) {
       constexpr int cur = decltype(stage)::value;
@@ -494,9 +496,9 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
         __builtin_amdgcn_sched_barrier(0);
         if (more && kk < kParts) issue_part((kt + 1) * kRowBytes, cur ^ 1, kk, kParts);
 #pragma unroll
-        for (int i = 0; i < FM; ++i) xf[i] = *(const frag_t*)(ax[cur][kk] + i * 32 * kRowBytes);
+        for (int i = 0; i < FM; ++i) xf[i] = *(lds_frag_ptr)(uintptr_t)(ax[cur][kk] + i * 32 * kRowBytes);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) wf[j] = *(const frag_t*)(aw[cur][kk] + j * 32 * kRowBytes);
+        for (int j = 0; j < FN; ++j) wf[j] = *(lds_frag_ptr)(uintptr_t)(aw[cur][kk] + j * 32 * kRowBytes);
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(xf, wf);
       }
