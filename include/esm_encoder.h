@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 22
+#define ESM_ABI_VERSION 21
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -127,9 +127,7 @@ esm_status esm_encoder_destroy(esm_encoder* enc);
  * (T for THD, B*S for bshd) and max_seqs sequences.  The workspace is
  * caller-allocated, 256-byte aligned, and may be reused between calls once the
  * stream has passed the previous one.  Its contents after a layer call hold
- * that layer's intermediates (see esm_workspace_region).  The size includes
- * the few kilobytes esm_stack_fwd's two-group schedule needs beyond the
- * regions (a smaller workspace that holds the regions runs it as one group). */
+ * that layer's intermediates (see esm_workspace_region). */
 esm_status esm_workspace_size(const esm_encoder* enc, int64_t max_tokens, int32_t max_seqs,
                               size_t* bytes);
 
@@ -231,14 +229,7 @@ esm_status esm_layer_fwd_noalloc(esm_encoder* enc, const esm_layer_weights* w, i
  * [0, vocab)) or the given hidden states x_in, then all num_hidden_layers
  * layers in order ([BIO-ACC] 3.2 PackedEsm.forward; [TE-ESM2] 自动混合精度训练).
  * No final LayerNorm.  `w` is a HOST array of num_hidden_layers structs.
- * FP8: layer l uses state slot l; the call is one step for every layer.
- * With cu_seqlens_host given, T >= 4096 and B >= 2 (and per-kernel timing off)
- * the batch runs as two groups of whole sequences, split where the tokens
- * balance, the first on `stream` and the second on the encoder's own stream
- * (default priority), forked from and joined back to `stream` inside the
- * call: the groups' kernels fill each other's partial rounds of workgroups.
- * Rows do not interact, so the output (and the FP8 state) is the same bit for
- * bit as one group's. */
+ * FP8: layer l uses state slot l; the call is one step for every layer. */
 esm_status esm_stack_fwd(esm_encoder* enc, const esm_layer_weights* w,
                          const int32_t* token_ids, const void* embedding,
                          const void* x_in, void* x_out,

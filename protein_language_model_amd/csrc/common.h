@@ -256,9 +256,6 @@ struct SegOut {
   int64_t tile_cap;
 };
 
-// out[i] = cu[b0 + i] - cu[b0] for i = 0 .. n (the cu_seqlens of sequences b0 ..
-// b0 + n - 1 as a batch of their own)
-hipError_t launch_rebase_cu(const int32_t* cu, int32_t b0, int32_t n, int32_t* out, hipStream_t st);
 hipError_t launch_segment_table(int layout, const int32_t* lens, int32_t B, int64_t rows, int32_t S,
                                 int32_t max_positions, const SegOut& out, hipStream_t st);
 

@@ -787,7 +787,7 @@ esm_status check_cu_host(const esm_encoder* e, const int32_t* cu, int32_t B, int
 esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, int32_t layer_idx,
                        const int32_t* ids, const void* emb, const void* x_in, void* x_out, const int32_t* cu_dev,
                        const int32_t* cu_host, int32_t B, int64_t T, int32_t max_seqlen, void* ws, size_t ws_bytes,
-                       esm_stream_t stream, bool two_groups = false) {
+                       esm_stream_t stream) {
   if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
   esm_status s = check_rows(e, T, B);
   if (s) return s;
@@ -815,77 +815,28 @@ esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, 
   if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
   hipStream_t st = (hipStream_t)stream;
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
-  const int H = e->cfg.hidden_size;
-  // One group of whole sequences (rows r0 .. r0 + Tg - 1, Bg sequences whose
-  // cu_seqlens from 0 are cu_g) through the embedding and every layer, on
-  // stream sg with its own workspace.
-  auto run_group = [&](int64_t r0, int64_t Tg, int32_t Bg, const int32_t* cu_g, void* wsg, const Plan& pg,
-                       hipStream_t sg) -> esm_status {
-    esm_status q;
-    if ((q = run_segments(e, 0, cu_g, Bg, Tg, 0, wsg, pg, sg))) return q;
-    bf16_t* xo = (bf16_t*)x_out + r0 * H;
-    const bf16_t* cur = x_in ? (const bf16_t*)x_in + r0 * H : nullptr;
-    bool stats_valid = false;
-    if (ids) {
-      // a folded first layer takes its LayerNorm statistics from the gather
-      const bool fold0 = nlayers > 0 && layer_folded(e, layer_idx >= 0 ? layer_idx : 0);
-      q = timed(e, ESM_K_EMBED, sg, "embedding", [&] {
-        return fold0 ? launch_row_stats(ids + r0, (const bf16_t*)emb, e->cfg.vocab_size, xo, Tg, H,
-                                        region<float2>(wsg, pg, ESM_WS_STATS), sg)
-                     : launch_embed(ids + r0, (const bf16_t*)emb, e->cfg.vocab_size, xo, Tg, H, sg);
-      });
-      if (q) return q;
-      stats_valid = fold0;
-      cur = xo;
-    }
-    for (int l = 0; l < nlayers; ++l) {
-      if ((q = run_layer(e, &w[l], layer_idx >= 0 ? layer_idx : l, cur, xo, Tg, Bg, false, wsg, pg, &stats_valid,
-                         sg)))
-        return q;
-      cur = xo;
-    }
-    return ok();
-  };
-  // Two groups of whole sequences on two streams when the host lengths are
-  // known and the workspace holds both groups' plans: the groups share no
-  // rows, so each row's arithmetic is unchanged, while the two streams' kernels
-  // fill each other's partial last rounds of workgroups and epilogues.
-  int32_t bs = 0;
-  if (two_groups && cu_host && B >= 2 && T >= 4096 && !e->profiling && nlayers > 0) {
-    int64_t best = T;
-    for (int32_t b = 1; b < B; ++b) {
-      const int64_t d = cu_host[b] * 2 - T;
-      if ((d < 0 ? -d : d) < best) { best = d < 0 ? -d : d; bs = b; }
-    }
+  if ((s = run_segments(e, 0, cu_dev, B, T, 0, ws, p, st))) return s;
+  const bf16_t* cur = (const bf16_t*)x_in;
+  bool stats_valid = false;
+  if (ids) {
+    // a folded first layer takes its LayerNorm statistics from the gather
+    const bool fold0 = nlayers > 0 && layer_folded(e, layer_idx >= 0 ? layer_idx : 0);
+    s = timed(e, ESM_K_EMBED, st, "embedding", [&] {
+      return fold0 ? launch_row_stats(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, T,
+                                      e->cfg.hidden_size, region<float2>(ws, p, ESM_WS_STATS), st)
+                   : launch_embed(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, T,
+                                  e->cfg.hidden_size, st);
+    });
+    if (s) return s;
+    stats_valid = fold0;
+    cur = (const bf16_t*)x_out;
   }
-  if (bs > 0) {
-    const int64_t T1 = cu_host[bs], T2 = T - T1;
-    const int32_t B1 = bs, B2 = B - bs;
-    const Plan p1 = make_plan(e->cfg, T1, B1), p2 = make_plan(e->cfg, T2, B2);
-    const size_t o2 = align256(p1.total), oc = o2 + align256(p2.total), need = oc + align256((size_t)(B2 + 1) * 4);
-    if (T1 > 0 && T2 > 0 && need <= ws_bytes) {
-      if (!e->side) {
-        HIP_TRY(hipStreamCreateWithFlags(&e->side, hipStreamNonBlocking), "hipStreamCreateWithFlags");
-        HIP_TRY(hipEventCreateWithFlags(&e->fork, hipEventDisableTiming), "hipEventCreateWithFlags");
-        HIP_TRY(hipEventCreateWithFlags(&e->join, hipEventDisableTiming), "hipEventCreateWithFlags");
-      }
-      char* wb = (char*)ws;
-      int32_t* cu2 = (int32_t*)(wb + oc);
-      HIP_TRY(launch_rebase_cu(cu_dev, bs, B2, cu2, st), "rebase cu_seqlens");
-      HIP_TRY(hipEventRecord(e->fork, st), "hipEventRecord");
-      HIP_TRY(hipStreamWaitEvent(e->side, e->fork, 0), "hipStreamWaitEvent");
-      esm_status s1 = run_group(0, T1, B1, cu_dev, wb, p1, st);
-      esm_status s2 = run_group(T1, T2, B2, cu2, wb + o2, p2, e->side);
-      // joined on every return, so no work is left behind the caller's stream
-      hipError_t j = hipEventRecord(e->join, e->side);
-      if (!j) j = hipStreamWaitEvent(st, e->join, 0);
-      if (s1) return s1;
-      if (s2) return s2;
-      if (j) return hip_fail(j, "join");
-      return end_of_step(e, nlayers, layer_idx, st);
-    }
+  for (int l = 0; l < nlayers; ++l) {
+    if ((s = run_layer(e, &w[l], layer_idx >= 0 ? layer_idx : l, cur, (bf16_t*)x_out, T, B, false, ws, p,
+                       &stats_valid, st)))
+      return s;
+    cur = (const bf16_t*)x_out;
   }
-  if ((s = run_group(0, T, B, cu_dev, ws, p, st))) return s;
   return end_of_step(e, nlayers, layer_idx, st);
 }
 
@@ -1042,9 +993,7 @@ esm_status esm_encoder_destroy(esm_encoder* e) {
 esm_status esm_workspace_size(const esm_encoder* e, int64_t max_tokens, int32_t max_seqs, size_t* bytes) {
   if (!e || !bytes) return fail(ESM_ERR_NULL, "encoder or bytes is NULL");
   if (max_tokens < 0 || max_seqs < 0) return fail(ESM_ERR_SHAPE, "negative sizes");
-  // plus room for the stack's two-group schedule (a second plan's alignment
-  // and tile slack, and the second group's rebased cu_seqlens)
-  *bytes = make_plan(e->cfg, max_tokens, max_seqs).total + 8192 + align256((size_t)(max_seqs + 1) * 4);
+  *bytes = make_plan(e->cfg, max_tokens, max_seqs).total;
   return ok();
 }
 
@@ -1095,7 +1044,7 @@ esm_status esm_stack_fwd(esm_encoder* e, const esm_layer_weights* w, const int32
   g_last_error.clear();
   if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
   return forward_thd(e, w, e->cfg.num_hidden_layers, -1, ids, emb, x_in, x_out, cu_dev, cu_host, B, T, max_seqlen,
-                     ws, ws_bytes, stream, true);
+                     ws, ws_bytes, stream);
 }
 
 esm_status esm_head_fwd(esm_encoder* e, const esm_head_weights* w, const void* x, void* x_final, void* logits,
