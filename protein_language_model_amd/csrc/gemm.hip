@@ -495,10 +495,12 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       for (int kk = 0; kk < KK; ++kk) {
         __builtin_amdgcn_sched_barrier(0);
         if (more && kk < kParts) issue_part((kt + 1) * kRowBytes, cur ^ 1, kk, kParts);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) xf[i] = *(lds_frag_ptr)(uintptr_t)(ax[cur][kk] + i * 32 * kRowBytes);
+        // the weight fragments first: the sub-step's first MFMAs wait for three
+        // of the seven reads instead of six
 #pragma unroll
         for (int j = 0; j < FN; ++j) wf[j] = *(lds_frag_ptr)(uintptr_t)(aw[cur][kk] + j * 32 * kRowBytes);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) xf[i] = *(lds_frag_ptr)(uintptr_t)(ax[cur][kk] + i * 32 * kRowBytes);
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(xf, wf);
       }
