@@ -146,6 +146,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   // tile (see the epilogue).
   constexpr bool OUT8 = EPI == EPI_BIAS_GELU_E4M3;
   constexpr bool OUTMX = EPI == EPI_BIAS_GELU_MX;
+  // The feed-forward intermediate (the GELU epilogues' output) is written once
+  // and read once by the next GEMM: its stores stream past the caches
+  // (non-temporal), leaving them to the tiles' operand panels and to the next
+  // kernels' inputs.
+  constexpr bool NT_OUT = EPI == EPI_BIAS_GELU || EPI == EPI_BIAS_GELU_LN || OUT8 || OUTMX;
   static_assert(!OUTMX || DT == kFP4, "MXFP4 output is built for MXFP4 operands");
   constexpr int OES = OUT8 ? 1 : 2;               // output bytes per element (bf16, E4M3)
   constexpr int ORB = OUTMX ? WTN / 2 : WTN * OES;  // output bytes of one row of a wave's tile
@@ -807,9 +812,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       const int head = n / 192, c = (n % 192) / 64, d = n % 64;
       *(u32x4*)(a.y + (((int64_t)c * heads + head) * M + m) * kHeadDim + d) = v;
     } else if constexpr (OUT8) {
-      *(u32x4*)(a.y8 + m * N + n) = v;
+      __builtin_nontemporal_store(v, (u32x4*)(a.y8 + m * N + n));
     } else if constexpr (OUTMX) {
-      *(u32x4*)(a.y8 + m * (N / 2) + n / 2) = v;
+      __builtin_nontemporal_store(v, (u32x4*)(a.y8 + m * (N / 2) + n / 2));
+    } else if constexpr (NT_OUT) {
+      __builtin_nontemporal_store(v, (u32x4*)(a.y + m * N + n));
     } else {
       *(u32x4*)(a.y + m * N + n) = v;
     }
