@@ -31,8 +31,12 @@
 //  * Rows beyond M and weight rows beyond N are clamped on load (never read out
 //    of bounds) and skipped on store.
 //  * Workgroup ids are remapped so consecutive tiles land on one XCD (ids are
-//    dealt round-robin over the 8 XCDs), then grouped GROUP_M row-tiles at a
-//    time so a row panel of x and the weight panels stay in that XCD's L2.
+//    dealt round-robin over the 8 XCDs), then grouped a few row-tiles at a
+//    time so a row panel of x and the weight panels stay in that XCD's L2
+//    (8 row tiles; 4 when the output is at least 4x wider than the
+//    contraction, as in the first feed-forward linear, and 2 when the
+//    contraction is at least 4x the output width, as in the second; chosen
+//    by measurement on those shapes).
 #include "common.h"
 
 #include <type_traits>
@@ -41,7 +45,6 @@ namespace esm {
 
 namespace {
 
-constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kRowBytes = 128;  // bytes of each tile row per K step
 
@@ -198,10 +201,11 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   const int xcd = bid % kXcds, local = bid / kXcds;
   const int q = nb / kXcds, rem = nb % kXcds;
   const int L = xcd * q + min(xcd, rem) + local;
-  const int group = kGroupM * tilesN;
+  const int group_m = K >= 4 * N ? 2 : (N >= 4 * K ? 4 : 8);
+  const int group = group_m * tilesN;
   const int g = L / group;
-  const int first_m = g * kGroupM;
-  const int gm = min(tilesM - first_m, kGroupM);
+  const int first_m = g * group_m;
+  const int gm = min(tilesM - first_m, group_m);
   const int within = L % group;
   const int tm = first_m + within % gm;
   const int tn = within / gm;
