@@ -126,56 +126,68 @@ __global__ void k_embed(const int32_t* __restrict__ ids, const bf16_t* __restric
 }
 
 // LayerNorm chunk partials of rows of x (optionally gathered first from the
-// embedding, X0 = E[ids]): one thread per (row, 256-column chunk, leaf), the
-// leaf's 32 values and the tree of ln_leaf / ln_combine exactly as the GEMM
-// epilogue that writes a residual stream evaluates them, so a row gives the
-// same partials whichever of the two produced them.  Eight consecutive lanes
-// hold one (row, chunk): lane bit 0 = h, bits 1..2 = w.
+// embedding, X0 = E[ids]): one wave per row.  The row is read, and X0 written
+// when gathering, in 16-byte pieces (a wave covers 1 KB per instruction) and
+// staged in the wave's own LDS region; item i = 8 * chunk + leaf of the row
+// (lanes i mod 64) then takes its leaf's 32 values and the tree of ln_leaf /
+// ln_combine exactly as the GEMM epilogue that writes a residual stream
+// evaluates them, so a row gives the same partials whichever of the two
+// produced them.  Leaf bit 0 = h, bits 1..2 = w.
 __global__ __launch_bounds__(256) void k_row_stats(const int32_t* __restrict__ ids, const bf16_t* __restrict__ table,
                                                    int32_t vocab, bf16_t* __restrict__ x, int64_t T, int32_t H,
                                                    float2* __restrict__ stats) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char row_lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave;
+  if (t >= T) return;  // the whole wave; no workgroup barrier follows
+  bf16_t* row = (bf16_t*)row_lds + (int64_t)wave * H;
+  const bf16_t* src = x + t * H;
+  if (ids) {
+    int id = ids[t];
+    id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+    src = table + (int64_t)id * H;
+  }
+  for (int c = lane; c < H / 8; c += 64) {
+    const u32x4 u = *(const u32x4*)(src + 8 * c);
+    if (ids) *(u32x4*)(x + t * H + 8 * c) = u;
+    *(u32x4*)(row + 8 * c) = u;
+  }
+  // The row's LDS writes are visible to every lane of the wave.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   const int chunks = (H + 255) / 256;
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int leaf = (int)(g & 7);
-  const int64_t rc = g >> 3;                 // (row, chunk), chunk fastest
-  const bool live = rc < T * chunks;
-  const int64_t t = live ? rc / chunks : 0;
-  const int c = live ? (int)(rc % chunks) : 0;
-  const int w = leaf >> 1, h = leaf & 1;
-  const int c0 = 256 * c;
-  const int cw = H - c0 < 256 ? H - c0 : 256;
-  const bool valid = live && 64 * w < cw;
-  LnPart p{0.f, 0.f, 0.f};
-  if (valid) {
-    const bf16_t* src = x + t * H;
-    if (ids) {
-      int id = ids[t];
-      id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
-      src = table + (int64_t)id * H;
+  const int items = (chunks * 8 + 63) & ~63;  // whole waves: every lane meets the exchanges
+  for (int it = lane; it < items; it += 64) {
+    const int c = it >> 3, leaf = it & 7;
+    const int w = leaf >> 1, h = leaf & 1;
+    const int c0 = 256 * c;
+    const int cw = H - c0 < 256 ? H - c0 : 256;
+    const bool valid = c < chunks && 64 * w < cw;
+    LnPart p{0.f, 0.f, 0.f};
+    if (valid) {
+      float v[32];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x2 u = *(const u32x2*)(row + c0 + 64 * w + 32 * j + 8 * q + 4 * h);
+          v[16 * j + 4 * q + 0] = bflo(u[0]);
+          v[16 * j + 4 * q + 1] = bfhi(u[0]);
+          v[16 * j + 4 * q + 2] = bflo(u[1]);
+          v[16 * j + 4 * q + 3] = bfhi(u[1]);
+        }
+      p = ln_leaf(v);
     }
-    float v[32];
+    // (w, 0) with (w, 1); then waves (0, 1) and (2, 3); then the two pairs.
+    // Each pair of lanes computes combine(lower, upper) identically.
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = c0 + 64 * w + 32 * j + 8 * q + 4 * h;
-        const u32x2 u = *(const u32x2*)(src + col);
-        if (ids) *(u32x2*)(x + t * H + col) = u;
-        v[16 * j + 4 * q + 0] = bflo(u[0]);
-        v[16 * j + 4 * q + 1] = bfhi(u[0]);
-        v[16 * j + 4 * q + 2] = bflo(u[1]);
-        v[16 * j + 4 * q + 3] = bfhi(u[1]);
-      }
-    p = ln_leaf(v);
+    for (int off = 1; off <= 4; off <<= 1) {
+      LnPart o{__shfl_xor(p.n, off), __shfl_xor(p.m, off), __shfl_xor(p.M2, off)};
+      p = (leaf & off) ? ln_combine(o, p) : ln_combine(p, o);
+    }
+    if (leaf == 0 && c < chunks) stats[(int64_t)c * T + t] = make_float2(p.m, p.M2);
   }
-  // (w, 0) with (w, 1); then waves (0, 1) and (2, 3); then the two pairs.
-  // Each pair of lanes computes combine(lower, upper) identically.
-#pragma unroll
-  for (int off = 1; off <= 4; off <<= 1) {
-    LnPart o{__shfl_xor(p.n, off), __shfl_xor(p.m, off), __shfl_xor(p.M2, off)};
-    p = (leaf & off) ? ln_combine(o, p) : ln_combine(p, o);
-  }
-  if (live && leaf == 0) stats[(int64_t)c * T + t] = make_float2(p.m, p.M2);
 }
 
 // Folded LayerNorm weight of one output row n per workgroup:
@@ -444,10 +456,13 @@ hipError_t launch_embed(const int32_t* ids, const bf16_t* table, int32_t vocab, 
 hipError_t launch_row_stats(const int32_t* ids, const bf16_t* table, int32_t vocab, bf16_t* x, int64_t T, int32_t H,
                             float2* stats, hipStream_t st) {
   if (T <= 0) return hipSuccess;
-  if (H % 64) return hipErrorInvalidValue;
-  const int64_t threads = T * ((H + 255) / 256) * 8;
-  hipLaunchKernelGGL(k_row_stats, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, ids, table, vocab, x, T,
-                     H, stats);
+  // One wave per row, its row staged in LDS (2 H bytes per wave): four waves
+  // per workgroup up to H = 8192, one up to 32768.
+  if (H % 64 || H > 32768) return hipErrorInvalidValue;
+  const int wpb = H <= 8192 ? 4 : 1;
+  const size_t lds = (size_t)wpb * H * 2;
+  hipLaunchKernelGGL(k_row_stats, dim3((unsigned)((T + wpb - 1) / wpb)), dim3(64 * wpb), lds, st, ids, table, vocab,
+                     x, T, H, stats);
   return hipGetLastError();
 }
 
