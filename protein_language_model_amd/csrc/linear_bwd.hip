@@ -16,46 +16,64 @@ namespace esm {
 
 namespace {
 
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Chunk swizzle of the staged tile: 16-byte chunk ch of tile row r sits at
+// chunk ch ^ tp_swz(r).  It keeps each pair of chunks (2a, 2a + 1) together
+// and gives the four same-parity rows that one half-wave's transposing read
+// touches ({b, b + 2, b + 8, b + 10} + 4 h + 32 s) four different pairs, so
+// that read, like the row-wise 16-byte writes, is free of bank conflicts
+// (64 banks of 4 bytes, checked by simulating the bank map).
+__device__ __forceinline__ int tp_swz(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
+
 // out[c, r] = in[r, c] for r < R, 0 for R <= r < Rp; in [R, C] row-major,
-// out [C, Rp].  One 256-thread workgroup per 64 x 64 tile, staged through
-// LDS with a padded row (66 halves) so that the column reads spread over
-// the banks.  C is a multiple of 64; Rp a multiple of 64 and >= R.
+// out [C, Rp].  One 256-thread workgroup per 64 x 64 tile: the tile's rows go
+// to LDS as 16-byte chunks, and gfx950's transposing LDS read
+// (ds_read_b64_tr_b16: in a group of 16 lanes, lane j addresses four
+// consecutive values of row k0 + j / 4 at columns n0 + 4 (j % 4), and lane i
+// receives column n0 + i of rows k0 .. k0 + 3) hands each lane four
+// consecutive values of one output row; two reads make a 16-byte store, and
+// the four groups of a wave store 64 contiguous bytes of each of their 16
+// output rows.  C is a multiple of 64; Rp a multiple of 64 and >= R.
 __global__ __launch_bounds__(256) void k_transpose_pad(const bf16_t* __restrict__ in, int64_t R, int32_t C,
                                                        bf16_t* __restrict__ out, int64_t Rp) {
-  __shared__ uint16_t tile[64][66];
+  __shared__ __attribute__((aligned(16))) bf16_t tile[64 * 64];
   const int64_t r0 = (int64_t)blockIdx.x * 64;
   const int c0 = blockIdx.y * 64;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // thread t: chunk t % 8 of rows t / 8 and t / 8 + 32 (zeros past R), both
+  // loads in flight together
   {
-    // load: thread t reads 16 consecutive columns of row t / 4
-    const int r = t >> 2, c = (t & 3) * 16;
-    u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
-    if (r0 + r < R) {
-      const bf16_t* src = in + (r0 + r) * C + c0 + c;
-      w0 = *(const u32x4*)src;
-      w1 = *(const u32x4*)(src + 8);
+    const int ra = t >> 3, rb = ra + 32, ch = t & 7;
+    u32x4 wa = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
+    if (r0 + rb < R) {
+      wa = *(const u32x4*)(in + (r0 + ra) * C + c0 + 8 * ch);
+      wb = *(const u32x4*)(in + (r0 + rb) * C + c0 + 8 * ch);
+    } else if (r0 + ra < R) {
+      wa = *(const u32x4*)(in + (r0 + ra) * C + c0 + 8 * ch);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tile[r][c + 2 * e] = (uint16_t)(w0[e] & 0xFFFFu);
-      tile[r][c + 2 * e + 1] = (uint16_t)(w0[e] >> 16);
-      tile[r][c + 8 + 2 * e] = (uint16_t)(w1[e] & 0xFFFFu);
-      tile[r][c + 8 + 2 * e + 1] = (uint16_t)(w1[e] >> 16);
-    }
+    *(u32x4*)(tile + ra * 64 + 8 * (ch ^ tp_swz(ra))) = wa;
+    *(u32x4*)(tile + rb * 64 + 8 * (ch ^ tp_swz(rb))) = wb;
   }
   __syncthreads();
-  {
-    // store: thread t writes 16 consecutive rows (of in) of output row t / 4
-    const int c = t >> 2, r = (t & 3) * 16;
-    u32x4 w0, w1;
+  // wave w: output rows c0 + 16 w + i (i = lane % 16); group q = lane / 16 and
+  // pass s: output columns r0 + 8 (q + 4 s) .. + 7.
+  const int i = lane & 15, q = lane >> 4;
+  const int col = 16 * wave + 4 * (i & 3);  // this lane's address: tile column
+  const int64_t orow = c0 + 16 * wave + i;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      w0[e] = (uint32_t)tile[r + 2 * e][c] | ((uint32_t)tile[r + 2 * e + 1][c] << 16);
-      w1[e] = (uint32_t)tile[r + 8 + 2 * e][c] | ((uint32_t)tile[r + 8 + 2 * e + 1][c] << 16);
+  for (int s = 0; s < 2; ++s) {
+    const int k0 = 8 * (q + 4 * s);
+    i16x4 v[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = k0 + 4 * hh + (i >> 2);  // this lane's address: tile row
+      const bf16_t* p = tile + r * 64 + 8 * ((col >> 3) ^ tp_swz(r)) + (col & 7);
+      v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
     }
-    bf16_t* dst = out + (int64_t)(c0 + c) * Rp + r0 + r;
-    *(u32x4*)dst = w0;
-    *(u32x4*)(dst + 8) = w1;
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    const i16x8 w = __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    *(u32x4*)(out + orow * Rp + r0 + k0) = __builtin_bit_cast(u32x4, w);
   }
 }
 
@@ -71,14 +89,22 @@ __global__ __launch_bounds__(256) void k_colsum_partial(const bf16_t* __restrict
   const int n0 = blockIdx.y * 64;
   const int t = threadIdx.x, cg = t & 7, rg = t >> 3;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < kSumRows / 32; ++i) {
-    const int64_t m = m0 + rg + 32 * i;
-    if (m < M) {
-      const u32x4 w = *(const u32x4*)(dy + m * N + n0 + cg * 8);
+  // Eight rows' loads in flight at a time; the adds keep the row order.
+  for (int i0 = 0; i0 < kSumRows / 32; i0 += 8) {
+    u32x4 w[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += bflo(w[e]);
-        acc[2 * e + 1] += bfhi(w[e]);
+    for (int u = 0; u < 8; ++u) {
+      const int64_t m = m0 + rg + 32 * (i0 + u);
+      w[u] = m < M ? *(const u32x4*)(dy + m * N + n0 + cg * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (m0 + rg + 32 * (i0 + u) < M) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bflo(w[u][e]);
+          acc[2 * e + 1] += bfhi(w[u][e]);
+        }
       }
     }
   }
