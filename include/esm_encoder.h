@@ -431,9 +431,11 @@ esm_status esm_linear_mxfp4_fwd(esm_encoder* enc, const void* x_codes, const voi
  * library's MFMA GEMM with fp32 accumulation (dW over all M rows in fp32: for
  * large M the contraction is cut into up to 16 slices whose fp32 products are
  * summed in slice order, then rounded once);
- * W^T, dy^T and x^T are written into the workspace first (rows padded with
- * zeros to a multiple of 64), db by a fixed-order two-pass column sum, so
- * results are deterministic.  The dW path runs on a stream of the encoder's own
+ * W^T is written into the workspace first; the dW product reads dy and x as
+ * they are (contraction-major, through gfx950's transposing LDS reads), with
+ * M cut into slices of ceil(M / (64 S)) * 64 rows (rows past M count as zero);
+ * db by a fixed-order two-pass column sum, so results are deterministic.  dW
+ * needs M < 2^31 - 1024.  The dW path runs on a stream of the encoder's own
  * (created on first use, default priority), forked from and joined back to
  * `stream` within the call, so the call stays ordered on `stream` alone.
  * workspace: device, 256-byte aligned, at least

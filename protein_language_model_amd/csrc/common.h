@@ -301,7 +301,7 @@ hipError_t launch_layernorm_mx(const bf16_t* x, const bf16_t* gamma, const bf16_
 // the LayerNorm statistics of its output rows (stats_out).
 enum GemmEpi { EPI_BIAS = 0, EPI_BIAS_GELU = 1, EPI_BIAS_RESIDUAL = 2, EPI_QKV_ROPE = 3, EPI_BIAS_GELU_E4M3 = 4,
                EPI_BIAS_GELU_MX = 5, EPI_F32_SPLIT = 6, EPI_QKV_ROPE_LN = 7, EPI_BIAS_GELU_LN = 8,
-               EPI_RES_STATS = 9 };
+               EPI_RES_STATS = 9, EPI_F32_SPLIT_KM = 10 };
 
 struct GemmArgs {
   int32_t dtype;       // kBF16 or kE4M3 operands
@@ -326,7 +326,12 @@ struct GemmArgs {
   const float* y8_scale;
   uint32_t* y8_amax;
   // EPI_F32_SPLIT (bf16 operands): K cut into ksplit equal slices; slice s's
-  // product, in fp32, goes to y32 + s * M * N (no bias); K % (64 ksplit) == 0
+  // product, in fp32, goes to y32 + s * M * N (no bias); K % (64 ksplit) == 0.
+  // EPI_F32_SPLIT_KM: the same with both operands stored contraction-major,
+  // x as [K, M] and w as [K, N] row-major (a weight gradient dy^T x read from
+  // dy and x as they are); any K, the slices are Kl = K rounded up to
+  // 64 ksplit, divided by ksplit, long, and rows past K count as zero; M and
+  // N multiples of 64.
   float* y32;
   int32_t ksplit;
   // kFP4 operands: E8M0 block scales in the esm_mxfp4_quantize layout

@@ -1323,22 +1323,17 @@ esm_status esm_linear_fwd(esm_encoder* e, const void* x, const void* w, const vo
 
 namespace {
 struct LinBwdPlan {
-  int32_t splits;  // K slices of the dW GEMM
-  int64_t Mp;      // rows padded to a multiple of 64 * splits
-  size_t wt, dyt, xt, part, wpart, total;
+  int32_t splits;  // slices of the dW GEMM's contraction over M
+  size_t wt, part, wpart, total;
 };
 LinBwdPlan lin_bwd_plan(int64_t M, int32_t N, int32_t K) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   LinBwdPlan p;
   p.splits = wgrad_splits(M, N, K);
-  const int64_t q = 64 * (int64_t)p.splits;
-  p.Mp = (M + q - 1) / q * q;
   p.wt = 0;
-  p.dyt = p.wt + up((size_t)K * N * 2);
-  p.xt = p.dyt + up((size_t)N * p.Mp * 2);
-  p.part = p.xt + up((size_t)K * p.Mp * 2);
+  p.part = p.wt + up((size_t)K * N * 2);
   p.wpart = p.part + up((size_t)colsum_chunks(M) * N * 4);
-  p.total = p.wpart + (p.splits > 1 ? up((size_t)p.splits * N * K * 4) : 0);
+  p.total = p.wpart + up((size_t)p.splits * N * K * 4);
   return p;
 }
 }  // namespace
@@ -1359,6 +1354,8 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
   if (M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64)
     return fail(ESM_ERR_SHAPE, "M %lld N %d K %d: N and K must be positive multiples of 64", (long long)M, N, K);
   if ((dx && !w) || (dw && !x)) return fail(ESM_ERR_NULL, "dx needs w, dw needs x");
+  if (dw && M > (int64_t)INT32_MAX - 1024)
+    return fail(ESM_ERR_SHAPE, "M %lld: dW takes fewer than 2^31 - 1024 rows", (long long)M);
   if (!aligned16(dy) || (x && !aligned16(x)) || (w && !aligned16(w)) || (dx && !aligned16(dx)) ||
       (dw && !aligned16(dw)) || ((uintptr_t)db & 3u) || ((uintptr_t)ws & 255u))
     return fail(ESM_ERR_UNSUPPORTED, "misaligned pointer (tensors 16 bytes, db 4, workspace 256)");
@@ -1370,11 +1367,8 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
   hipStream_t st = (hipStream_t)stream;
   char* base = (char*)ws;
   bf16_t* wt = (bf16_t*)(base + pl.wt);
-  bf16_t* dyt = (bf16_t*)(base + pl.dyt);
-  bf16_t* xt = (bf16_t*)(base + pl.xt);
   float* part = (float*)(base + pl.part);
   float* wpart = (float*)(base + pl.wpart);
-  const int64_t M64 = pl.Mp;
   if (dw && !e->side) {
     HIP_TRY(hipStreamCreateWithFlags(&e->side, hipStreamNonBlocking), "hipStreamCreateWithFlags");
     HIP_TRY(hipEventCreateWithFlags(&e->fork, hipEventDisableTiming), "hipEventCreateWithFlags");
@@ -1383,10 +1377,12 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
   return timed(e, ESM_K_LINEAR_BWD, st, "linear backward", [&]() -> hipError_t {
     hipError_t r = hipSuccess;
     // The dW GEMM's output is small (N x K: tens of tiles for hundreds of
-    // compute units) with a long contraction over M: it is cut into K slices
-    // (fp32 partial products summed in slice order), and it runs on the side
+    // compute units) with a long contraction over M: it is cut into slices of
+    // M (fp32 partial products summed in slice order), and it runs on the side
     // stream, forked from and joined back to st, beside the dx GEMM and the
-    // column sums.  The workspace regions of the two paths are disjoint.
+    // column sums.  It reads dy and x as they are, contraction-major (no
+    // transposed copies).  The workspace regions of the two paths are
+    // disjoint.
     // Once the side stream has been forked it is joined back to st on every
     // return, errors included, so that no work on ws or dw is left running
     // behind the caller's stream.
@@ -1395,22 +1391,15 @@ esm_status esm_linear_bwd(esm_encoder* e, const void* x, const void* w, const vo
       if ((r = hipEventRecord(e->fork, st))) return r;
       if ((r = hipStreamWaitEvent(e->side, e->fork, 0))) return r;
       forked = true;
-      // dW [N, K] = dy^T [N, M64] . (x^T [K, M64])^T, zero columns past M
-      r = launch_transpose_pad((const bf16_t*)dy, M, N, dyt, M64, e->side);
-      if (!r) r = launch_transpose_pad((const bf16_t*)x, M, K, xt, M64, e->side);
-      if (!r) {
-        GemmArgs g{};
-        g.dtype = kBF16;
-        g.x = dyt; g.w = xt; g.y = (bf16_t*)dw; g.M = N; g.N = K; g.K = M64;
-        if (pl.splits > 1) {
-          // split-K: each K slice's fp32 product, then their sum in slice order
-          g.y32 = wpart; g.ksplit = pl.splits;
-          r = launch_gemm(EPI_F32_SPLIT, g, e->side);
-          if (!r) r = launch_split_reduce(wpart, pl.splits, (int64_t)N * K, (bf16_t*)dw, e->side);
-        } else {
-          r = launch_gemm(EPI_BIAS, g, e->side);
-        }
-      }
+      // dW [N, K] = sum over m of dy[m, n] x[m, k]: each slice of M's fp32
+      // product (slices of M rounded up to 64 * splits, divided by splits,
+      // rows past M zero), then their sum in slice order, rounded once
+      GemmArgs g{};
+      g.dtype = kBF16;
+      g.x = dy; g.w = x; g.M = N; g.N = K; g.K = (int32_t)M;
+      g.y32 = wpart; g.ksplit = pl.splits;
+      r = launch_gemm(EPI_F32_SPLIT_KM, g, e->side);
+      if (!r) r = launch_split_reduce(wpart, pl.splits, (int64_t)N * K, (bf16_t*)dw, e->side);
     }
     if (!r && dx) {
       // dx [M, K] = dy [M, N] . (W^T [K, N])^T

@@ -61,6 +61,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 512 zero bytes: the source of the contraction-major loads for rows past the
+// contraction's end (never written).
+__device__ __attribute__((aligned(16))) unsigned char g_zero_row[512];
+
 // GELU(z) = z Phi(z), Phi the standard normal CDF (the exact, erf form; the
 // pages name a fused activation only).  With q = Phi(-|z|), GELU(z) is
 // z (1 - q) for z >= 0 and z q for z < 0, i.e. max(z, 0) - |z| q in both
@@ -140,6 +146,24 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   constexpr bool RES = EPI == EPI_BIAS_RESIDUAL || EPI == EPI_RES_STATS;
   constexpr bool FOLD = EPI == EPI_QKV_ROPE_LN || EPI == EPI_BIAS_GELU_LN;  // LayerNorm folded into the linear
   constexpr bool STATS = EPI == EPI_RES_STATS;                              // LayerNorm partials of the output
+  // EPI_F32_SPLIT_KM: operands stored contraction-major (x [K, M], w [K, N]).
+  // A K step's tile of an operand is then 64 contraction rows of its 256
+  // tile columns (512 bytes each) instead of 256 rows of 64 contraction
+  // values: the same 32 KB, filled by the same 1 KB direct loads (two rows
+  // each), with 16-byte chunk c of contraction row r stored at chunk
+  // c ^ 4 (r % 4).  Fragments are read with gfx950's transposing LDS read
+  // (ds_read_b64_tr_b16: in a group of 16 lanes, lane j addresses four
+  // values of row r0 + j / 4 at columns c0 + 4 (j % 4), and lane i receives
+  // column c0 + i of rows r0 .. r0 + 3): two reads give a lane the eight
+  // contraction values of its fragment row, in the order the row-major
+  // fragments hold them, so the MFMAs see the same operands as for
+  // transposed copies of x and w.  Per half-wave read the four rows'
+  // 64-byte column bands fall on distinct banks (checked by simulating the
+  // bank map).
+  constexpr bool KMAJ = EPI == EPI_F32_SPLIT_KM;
+  constexpr bool SPLIT = EPI == EPI_F32_SPLIT || KMAJ;
+  static_assert(!KMAJ || (DT == kBF16 && BM == 256 && BN == 256 && NW == 8 && XRB == 4 && WRB == 4),
+                "contraction-major operands: bf16, 256 x 256 tiles of eight waves");
   static_assert(!ROPE || (FN % 2 == 0 && WTN % 64 == 0), "rotary pairs need 64-wide wave columns");
   static_assert(EPI != EPI_BIAS_GELU_E4M3 || DT == kE4M3, "E4M3 output is built for E4M3 operands");
   static_assert(!(FOLD || STATS) || (DT == kBF16 && BN == 256), "folded LayerNorm: bf16, 256-column tiles");
@@ -188,13 +212,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   const int tilesN = (N + BN - 1) / BN;
   const int nb = tilesM * tilesN;
   int bid = blockIdx.x;
-  // EPI_F32_SPLIT: workgroup = (K slice, tile), the slice slowest.
+  // Split-K: workgroup = (K slice, tile), the slice slowest.
   [[maybe_unused]] int split = 0;
   int Kl = K;
-  if constexpr (EPI == EPI_F32_SPLIT) {
+  if constexpr (SPLIT) {
     split = bid / nb;
     bid = bid % nb;
-    Kl = K / a.ksplit;
+    Kl = KMAJ ? (int)(((int64_t)K + 64 * a.ksplit - 1) / (64 * a.ksplit) * 64) : K / a.ksplit;
   }
   if (bid >= nb) return;
   // XCD-aware remap: hardware deals ids round-robin over the XCDs.
@@ -229,20 +253,45 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   // per-lane offset of at most (BM - 1) rows: no vector instructions on
   // global addresses in the K loop.
   const int64_t rowb = (int64_t)K * EBN / EBD;  // bytes per operand row
-  const unsigned char* const xbase = (const unsigned char*)a.x + m0 * rowb + (int64_t)split * Kl * EBN / EBD;
-  const unsigned char* const wbase = (const unsigned char*)a.w + (int64_t)n0 * rowb + (int64_t)split * Kl * EBN / EBD;
+  // contraction-major: bytes per contraction row of x ([K, M]) and of w ([K, N])
+  [[maybe_unused]] const int64_t ldxb = (int64_t)M * 2, ldwb = (int64_t)N * 2;
+  const unsigned char* const xbase =
+      KMAJ ? (const unsigned char*)a.x + (int64_t)split * Kl * ldxb + m0 * 2
+           : (const unsigned char*)a.x + m0 * rowb + (int64_t)split * Kl * EBN / EBD;
+  const unsigned char* const wbase =
+      KMAJ ? (const unsigned char*)a.w + (int64_t)split * Kl * ldwb + (int64_t)n0 * 2
+           : (const unsigned char*)a.w + (int64_t)n0 * rowb + (int64_t)split * Kl * EBN / EBD;
   uint32_t xoff[XRB], woff[WRB];
+  if constexpr (KMAJ) {
+    // Block i of a wave: contraction rows 2 (wave + NW i) and + 1 of the K
+    // step (lanes 0-31 and 32-63).  Lane i writes physical chunk i % 32 of
+    // its row, so it fetches logical chunk (i % 32) ^ 4 (row % 4): tile
+    // columns 8 c .. 8 c + 7, clamped into the operand (columns past M or N
+    // are never stored).
 #pragma unroll
-  for (int i = 0; i < XRB; ++i) {
-    int64_t r = m0 + (int64_t)(wave + NW * i) * RPI + lr8;
-    r = r < M ? r : M - 1;
-    xoff[i] = (uint32_t)((r - m0) * rowb + lchunk);
-  }
+    for (int i = 0; i < XRB; ++i) {
+      const int rr = 2 * (wave + NW * i) + (lane >> 5);
+      const int c = (lane & 31) ^ (4 * (rr & 3));
+      int64_t cx = m0 + 8 * c;
+      cx = cx < M ? cx : M - 8;
+      xoff[i] = (uint32_t)(rr * ldxb + (cx - m0) * 2);
+      int64_t cw = (int64_t)n0 + 8 * c;
+      cw = cw < N ? cw : N - 8;
+      woff[i] = (uint32_t)(rr * ldwb + (cw - n0) * 2);
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < WRB; ++i) {
-    int r = n0 + (wave + NW * i) * RPI + lr8;
-    r = r < N ? r : N - 1;
-    woff[i] = (uint32_t)((int64_t)(r - n0) * rowb + lchunk);
+    for (int i = 0; i < XRB; ++i) {
+      int64_t r = m0 + (int64_t)(wave + NW * i) * RPI + lr8;
+      r = r < M ? r : M - 1;
+      xoff[i] = (uint32_t)((r - m0) * rowb + lchunk);
+    }
+#pragma unroll
+    for (int i = 0; i < WRB; ++i) {
+      int r = n0 + (wave + NW * i) * RPI + lr8;
+      r = r < N ? r : N - 1;
+      woff[i] = (uint32_t)((int64_t)(r - n0) * rowb + lchunk);
+    }
   }
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = lds_addr(smem);
@@ -267,23 +316,42 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       }
     }
   };
-  // Part p of np of a K step's direct loads: the wave's XRB x row blocks then
-  // its WRB w row blocks, numbered 0 .. XRB + WRB - 1, split into np equal
-  // runs (the block scales go with part 0).
-  auto issue_part = [&](int kbyte, int buf, int p, int np) {
+  // Part p of np of K step kt's direct loads: the wave's XRB x row blocks
+  // then its WRB w row blocks, numbered 0 .. XRB + WRB - 1, split into np
+  // equal runs (the block scales go with part 0).
+  auto issue_part = [&](int kt, int buf, int p, int np) {
     const uint32_t base = lds0 + (uint32_t)(buf * kStage);
     constexpr int NL = XRB + WRB;
+    const int64_t xk = KMAJ ? (int64_t)kt * 64 * ldxb : (int64_t)kt * kRowBytes;
+    const int64_t wk = KMAJ ? (int64_t)kt * 64 * ldwb : (int64_t)kt * kRowBytes;
+    if constexpr (KMAJ) {
+      const int64_t g0 = (int64_t)split * Kl + (int64_t)kt * 64;  // the step's first contraction row
+      if (g0 + 64 > K) {
+        // The step reaches past the contraction's end: rows at or past K
+        // load zeros (whole-address form, one select per lane).
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          if (i < p * NL / np || i >= (p + 1) * NL / np) continue;
+          const int ib = i < XRB ? i : i - XRB;
+          const int rr = 2 * (wave_u + NW * ib) + (lane >> 5);
+          const unsigned char* src = i < XRB ? xbase + xk + xoff[ib] : wbase + wk + woff[ib];
+          if (g0 + rr >= K) src = g_zero_row + 16 * (lane & 31);
+          lds_dma16(src, base + (uint32_t)(((i < XRB ? 0 : BM) + (wave_u + NW * ib) * RPI) * kRowBytes));
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       if (i < p * NL / np || i >= (p + 1) * NL / np) continue;
       if (i < XRB)
-        lds_dma16s(xbase + kbyte, xoff[i], base + (uint32_t)((wave_u + NW * i) * RPI * kRowBytes));
+        lds_dma16s(xbase + xk, xoff[i], base + (uint32_t)((wave_u + NW * i) * RPI * kRowBytes));
       else
-        lds_dma16s(wbase + kbyte, woff[i - XRB], base + (uint32_t)((BM + (wave_u + NW * (i - XRB)) * RPI) * kRowBytes));
+        lds_dma16s(wbase + wk, woff[i - XRB], base + (uint32_t)((BM + (wave_u + NW * (i - XRB)) * RPI) * kRowBytes));
     }
-    if (p == 0) issue_scales(kbyte / kRowBytes, buf);
+    if (p == 0) issue_scales(kt, buf);
   };
-  auto issue_tile = [&](int kbyte, int buf) { issue_part(kbyte, buf, 0, 1); };
+  auto issue_tile = [&](int kt, int buf) { issue_part(kt, buf, 0, 1); };
   // bf16: a K step's loads go out in three runs, ahead of the first three of
   // its four k sub-steps, not at once: a wave that issues all of them
   // back to back stalls at issue behind the address unit and starts its
@@ -315,13 +383,38 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       return __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
   };
+  // Contraction-major fragment of tile columns R .. R + 31 at sub-step kk:
+  // lanes 16 g + i (g = 0 .. 3) take column R + 16 (g % 2) + i, contraction
+  // rows 16 kk + 8 (g / 2) + 0 .. 7 (two transposing reads of four rows);
+  // the lane's address is row 16 kk + 8 (g / 2) + i / 4 (+ 4), columns
+  // R + 16 (g % 2) + 4 (i % 4) .. + 3, whose row % 4 is i / 4.
+  [[maybe_unused]] auto read_frag_km = [&](const unsigned char* op, int R, int kk) -> frag_t {
+    if constexpr (KMAJ) {
+      const int g = lane >> 4, i16 = lane & 15;
+      const int col = R + 16 * (g & 1) + 4 * (i16 & 3);
+      const int r = 16 * kk + 8 * (g >> 1) + (i16 >> 2);
+      const unsigned char* p = op + r * (BM * 2) + (((col >> 3) ^ (4 * (i16 >> 2))) * 16) + (col & 7) * 2;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * (BM * 2)));
+      return __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      return frag_t{};
+    }
+  };
   auto load_frags = [&](frag_t (&xf)[FM], frag_t (&wf)[FN], int buf, int kk) {
     const unsigned char* sx = smem + buf * kStage;
     const unsigned char* sw = sx + BM * kRowBytes;
+    if constexpr (KMAJ) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) xf[i] = read_frag(sx + (wm * WTM + i * 32 + lrow) * kRowBytes, kk);
+      for (int i = 0; i < FM; ++i) xf[i] = read_frag_km(sx, wm * WTM + i * 32, kk);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) wf[j] = read_frag(sw + (wn * WTN + j * 32 + lrow) * kRowBytes, kk);
+      for (int j = 0; j < FN; ++j) wf[j] = read_frag_km(sw, wn * WTN + j * 32, kk);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) xf[i] = read_frag(sx + (wm * WTM + i * 32 + lrow) * kRowBytes, kk);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) wf[j] = read_frag(sw + (wn * WTN + j * 32 + lrow) * kRowBytes, kk);
+    }
   };
 
   f32x16 acc[FM][FN];
@@ -448,7 +541,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         __builtin_amdgcn_sched_barrier(0);
-        if (more && kk < kParts) issue_part((kt + 1) * kRowBytes, cur ^ 1, kk, kParts);
+        if (more && kk < kParts) issue_part(kt + 1, cur ^ 1, kk, kParts);
         load_frags(xf, wf, cur, kk);
         __builtin_amdgcn_sched_barrier(0);
         mfma_step_mx(xf, wf, kk);
@@ -468,7 +561,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         __builtin_amdgcn_sched_barrier(0);
-        if (more && kk < kParts) issue_part((kt + 1) * kRowBytes, cur ^ 1, kk, kParts);
+        if (more && kk < kParts) issue_part(kt + 1, cur ^ 1, kk, kParts);
         load_frags(xf, wf, cur, kk);
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(xf, wf);
@@ -503,7 +596,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         __builtin_amdgcn_sched_barrier(0);
-        if (more && kk < kParts) issue_part((kt + 1) * kRowBytes, cur ^ 1, kk, kParts);
+        if (more && kk < kParts) issue_part(kt + 1, cur ^ 1, kk, kParts);
         // the weight fragments first: the sub-step's first MFMAs wait for three
         // of the seven reads instead of six
 #pragma unroll
@@ -530,7 +623,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
-      if (more && kk < kParts) issue_part((kt + 1) * kRowBytes, cur ^ 1, kk, kParts);
+      if (more && kk < kParts) issue_part(kt + 1, cur ^ 1, kk, kParts);
       if (kk + 1 < KK) {
         load_frags(xf[(kk + 1) & 1], wf[(kk + 1) & 1], cur, kk + 1);
       } else if (more) {
@@ -547,7 +640,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
   }
   }
 
-  if constexpr (EPI == EPI_F32_SPLIT) {
+  if constexpr (SPLIT) {
     // Split-K partial sums straight from the accumulators: register 4 gq + e
     // of block (i, j) is row mw + 32 i + lrow, column nw + 32 j + 8 gq +
     // 4 lhalf + e; 16-byte fp32 stores, no staging.
@@ -855,7 +948,7 @@ template <int BM, int BN, int WM, int WN, int EPI, int DT>
 hipError_t run(const GemmArgs& a, hipStream_t st) {
   const int64_t tilesM = (a.M + BM - 1) / BM;
   const int64_t tilesN = (a.N + BN - 1) / BN;
-  const int64_t nb = tilesM * tilesN * (EPI == EPI_F32_SPLIT ? a.ksplit : 1);
+  const int64_t nb = tilesM * tilesN * (EPI == EPI_F32_SPLIT || EPI == EPI_F32_SPLIT_KM ? a.ksplit : 1);
   hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, EPI, DT>), dim3((unsigned)nb), dim3(64 * WM * WN), 0, st, a);
   return hipGetLastError();
 }
@@ -884,6 +977,10 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
       return run<256, 256, 2, 4, EPI, kE5M2X>(a, st);
     }
     if (a.dtype != kBF16 || a.K % (64 * a.ksplit)) return hipErrorInvalidValue;
+    return run<256, 256, 2, 4, EPI, kBF16>(a, st);
+  } else if constexpr (EPI == EPI_F32_SPLIT_KM) {
+    // contraction-major split-K products (the linears' weight gradients)
+    if (a.ksplit < 1 || !a.y32 || a.dtype != kBF16 || a.M % 64 || a.N % 64 || a.K < 0) return hipErrorInvalidValue;
     return run<256, 256, 2, 4, EPI, kBF16>(a, st);
   } else if constexpr (EPI == EPI_QKV_ROPE_LN || EPI == EPI_BIAS_GELU_LN || EPI == EPI_RES_STATS) {
     if (a.dtype != kBF16) return hipErrorInvalidValue;
@@ -1000,7 +1097,9 @@ int32_t mfma_peak_blocks() { return 2 * device_cus(); }
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;
   const int kb = a.dtype == kFP4 ? 2 * kRowBytes : (a.dtype == kE4M3 || a.dtype == kE5M2X ? kRowBytes : kRowBytes / 2);
-  if (a.K % kb != 0 || a.N % 64 != 0) return hipErrorInvalidValue;
+  // the contraction-major product takes any contraction length (rows past
+  // it load as zeros)
+  if ((epi != EPI_F32_SPLIT_KM && a.K % kb != 0) || a.N % 64 != 0) return hipErrorInvalidValue;
   switch (epi) {
     case EPI_BIAS: return dispatch<EPI_BIAS>(a, st);
     case EPI_BIAS_GELU: return dispatch<EPI_BIAS_GELU>(a, st);
@@ -1009,6 +1108,7 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st) {
     case EPI_BIAS_GELU_E4M3: return dispatch<EPI_BIAS_GELU_E4M3>(a, st);
     case EPI_BIAS_GELU_MX: return dispatch<EPI_BIAS_GELU_MX>(a, st);
     case EPI_F32_SPLIT: return dispatch<EPI_F32_SPLIT>(a, st);
+    case EPI_F32_SPLIT_KM: return dispatch<EPI_F32_SPLIT_KM>(a, st);
     case EPI_QKV_ROPE_LN: return dispatch<EPI_QKV_ROPE_LN>(a, st);
     case EPI_BIAS_GELU_LN: return dispatch<EPI_BIAS_GELU_LN>(a, st);
     case EPI_RES_STATS: return dispatch<EPI_RES_STATS>(a, st);

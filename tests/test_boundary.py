@@ -178,20 +178,19 @@ def _size(fn, *args):
 
 
 def test_linear_bwd_workspace_size():
-    # W^T [K, N] bf16, dy^T [N, Mp] and x^T [K, Mp] bf16, db partials
-    # [ceil(M / 1024), N] fp32 and the dW GEMM's S fp32 slices [S, N, K],
-    # each region rounded up to 256 bytes.  fc1's shape at T = 32293: 100
-    # tiles of 256 x 256, so S = 5 (two rounds of 250 tiles per 1/5 of the
-    # contraction) and Mp = 32293 rounded up to 64 * 5.
+    # W^T [K, N] bf16, db partials [ceil(M / 1024), N] fp32 and the dW GEMM's
+    # S fp32 slices [S, N, K] (dy and x are read in place), each region
+    # rounded up to 256 bytes.  fc1's shape at T = 32293: 100 tiles of
+    # 256 x 256, so S = 5 (two rounds of 250 tiles per 1/5 of the contraction).
     M, N, K = 32293, 5120, 1280
-    S, Mp = 5, 32320
+    S = 5
     up = lambda b: (b + 255) // 256 * 256
     st, msg, n = _size("esm_linear_bwd_workspace_size", ctypes.c_int64(M), N, K)
     assert st == 0, msg
-    assert n == up(K * N * 2) + up(N * Mp * 2) + up(K * Mp * 2) + up(-(-M // 1024) * N * 4) + up(S * N * K * 4)
-    # below 2048 rows there is one slice and no partial region
+    assert n == up(K * N * 2) + up(-(-M // 1024) * N * 4) + up(S * N * K * 4)
+    # below 2048 rows there is one slice
     st, msg, n = _size("esm_linear_bwd_workspace_size", ctypes.c_int64(1000), 64, 64)
-    assert st == 0 and n == up(64 * 64 * 2) + 2 * up(64 * 1024 * 2) + up(64 * 4)
+    assert st == 0 and n == up(64 * 64 * 2) + up(64 * 4) + up(64 * 64 * 4)
     for bad in ((M, 100, K), (M, N, 0), (-1, N, K)):
         st, msg, _ = _size("esm_linear_bwd_workspace_size", ctypes.c_int64(bad[0]), bad[1], bad[2])
         assert st == 2 and msg
