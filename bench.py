@@ -324,8 +324,8 @@ def bench_linear_bwd(enc, T: int, H: int, F: int, steps: int, dev: str, stream) 
     """esm_linear_bwd (dx, dW and db) on the layer's four linear shapes at this
     batch's T: bf16 x, dy N(0, 1) and W N(0, 0.02); HIP events on the library
     stream around back-to-back calls.  Algorithmic flops 4 M N K per call (the
-    two products); the transposes and the column sum are counted as time, not
-    flops."""
+    two products); the W^T copy, the column sum and the slice sum are counted
+    as time, not flops."""
     import torch
     out = {}
     g = torch.Generator(device=dev).manual_seed(12)
