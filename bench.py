@@ -611,8 +611,8 @@ def bench_stack_leg(name: str, steps: int, warmup: int, dev: str, stream) -> dic
     ws = enc.workspace(b.T, b.B)
 
     def step():
-        enc.stack_fwd(wts, cu, b.B, b.T, b.max_seqlen, token_ids=ids, embedding=emb_d, x_out=out, workspace=ws,
-                      stream=stream)
+        enc.stack_fwd(wts, cu, b.B, b.T, b.max_seqlen, token_ids=ids, embedding=emb_d, x_out=out,
+                      cu_seqlens_host=b.cu_seqlens, workspace=ws, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -733,7 +733,7 @@ def main():
 
         def step():
             enc.stack_fwd(weights, cu, B, T, batch.max_seqlen, token_ids=ids, embedding=emb_d, x_out=out,
-                          workspace=ws, stream=stream)
+                          cu_seqlens_host=batch.cu_seqlens, workspace=ws, stream=stream)
 
         def timed_steps(n: int, per_step: list = None) -> float:
             """Mean ms per step over n steps; per_step (if given) receives each

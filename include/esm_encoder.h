@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ESM_ABI_VERSION 21
+#define ESM_ABI_VERSION 22
 
 /* Query rows per attention workgroup (the segment table's tile size). */
 #define ESM_ATTN_TILE_ROWS 256
@@ -127,7 +127,9 @@ esm_status esm_encoder_destroy(esm_encoder* enc);
  * (T for THD, B*S for bshd) and max_seqs sequences.  The workspace is
  * caller-allocated, 256-byte aligned, and may be reused between calls once the
  * stream has passed the previous one.  Its contents after a layer call hold
- * that layer's intermediates (see esm_workspace_region). */
+ * that layer's intermediates (see esm_workspace_region).  The size includes
+ * the few kilobytes esm_stack_fwd's two-group schedule needs beyond the
+ * regions (a smaller workspace that holds the regions runs it as one group). */
 esm_status esm_workspace_size(const esm_encoder* enc, int64_t max_tokens, int32_t max_seqs,
                               size_t* bytes);
 
@@ -229,13 +231,31 @@ esm_status esm_layer_fwd_noalloc(esm_encoder* enc, const esm_layer_weights* w, i
  * [0, vocab)) or the given hidden states x_in, then all num_hidden_layers
  * layers in order ([BIO-ACC] 3.2 PackedEsm.forward; [TE-ESM2] 自动混合精度训练).
  * No final LayerNorm.  `w` is a HOST array of num_hidden_layers structs.
- * FP8: layer l uses state slot l; the call is one step for every layer. */
+ * FP8: layer l uses state slot l; the call is one step for every layer.
+ * With cu_seqlens_host given (and per-kernel timing off) the batch may run
+ * as two groups of whole sequences, split where esm_stack_split says, the
+ * first on `stream` and the second on the encoder's own stream (default
+ * priority), forked from and joined back to `stream` inside the call: one
+ * group's attention runs beside the other's GEMMs.  Rows do not interact, so
+ * the output (and the FP8 state) is the same bit for bit as one group's. */
 esm_status esm_stack_fwd(esm_encoder* enc, const esm_layer_weights* w,
                          const int32_t* token_ids, const void* embedding,
                          const void* x_in, void* x_out,
                          const int32_t* cu_seqlens_dev, const int32_t* cu_seqlens_host,
                          int32_t B, int64_t T, int32_t max_seqlen,
                          void* workspace, size_t workspace_bytes, esm_stream_t stream);
+
+/* Where esm_stack_fwd splits a batch into its two groups (host only): the
+ * sequence index b written to *split_seq (group 1 = sequences 0 .. b - 1,
+ * group 2 = b .. B - 1), or 0 when it runs one group.  A split is taken only
+ * where, for each GEMM output width of the layer (3 hidden, hidden,
+ * intermediate), the two groups' rounds of workgroups over the device's
+ * compute units (the current device's, 256 when none is visible) sum to at
+ * most the whole batch's, and among those the one with the most balanced
+ * tokens; never below 4096 rows or 2 sequences.  cu_seqlens_host [B + 1]
+ * from 0 to T.  Errors: ESM_ERR_NULL, ESM_ERR_SHAPE. */
+esm_status esm_stack_split(int32_t hidden_size, int32_t intermediate_size, const int32_t* cu_seqlens_host,
+                           int32_t B, int64_t T, int32_t* split_seq);
 
 /* Padded (bshd) variants ([TE-ESM2] 注意力掩码优化; [BIO-ACC] 3.1 bshd format).
  * x_in / x_out are [B, S, H]; row b holds a valid prefix of seqlens[b] <= S

@@ -256,6 +256,9 @@ struct SegOut {
   int64_t tile_cap;
 };
 
+// out[i] = cu[b0 + i] - cu[b0] for i = 0 .. n (the cu_seqlens of sequences b0 ..
+// b0 + n - 1 as a batch of their own)
+hipError_t launch_rebase_cu(const int32_t* cu, int32_t b0, int32_t n, int32_t* out, hipStream_t st);
 hipError_t launch_segment_table(int layout, const int32_t* lens, int32_t B, int64_t rows, int32_t S,
                                 int32_t max_positions, const SegOut& out, hipStream_t st);
 
@@ -351,6 +354,9 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st);
+// Rounds of workgroups over the current device's compute units that
+// launch_gemm runs for an M x N output (forward epilogues).
+int64_t gemm_rounds(int64_t M, int32_t N);
 // Matrix-core rate probe (k_mfma_peak): `blocks` workgroups of four waves,
 // each wave 16 * iters v_mfma_f32_32x32x16_bf16; sink [4 * blocks] floats.
 hipError_t launch_mfma_peak(int32_t iters, int32_t blocks, float* sink, hipStream_t st);

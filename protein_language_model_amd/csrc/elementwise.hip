@@ -548,4 +548,17 @@ hipError_t launch_segment_mean(const bf16_t* x, const int32_t* segs, int32_t B, 
   return hipGetLastError();
 }
 
+namespace {
+__global__ void k_rebase_cu(const int32_t* __restrict__ cu, int32_t b0, int32_t n, int32_t* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i <= n) out[i] = cu[b0 + i] - cu[b0];
+}
+}  // namespace
+
+hipError_t launch_rebase_cu(const int32_t* cu, int32_t b0, int32_t n, int32_t* out, hipStream_t st) {
+  if (n < 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_rebase_cu, dim3((unsigned)((n + 256) / 256)), dim3(256), 0, st, cu, b0, n, out);
+  return hipGetLastError();
+}
+
 }  // namespace esm

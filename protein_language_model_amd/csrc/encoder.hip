@@ -784,10 +784,43 @@ esm_status check_cu_host(const esm_encoder* e, const int32_t* cu, int32_t B, int
   return ok();
 }
 
+// Where the stack's two-group schedule splits a batch: the sequence index b
+// (group 1 = sequences 0 .. b - 1, group 2 = the rest), or 0 for one group.
+// The groups share no rows, so each row's arithmetic is unchanged, while the
+// two streams' kernels overlap (one group's attention beside the other's
+// GEMMs) and desynchronise their epilogues.  A split is taken only where
+// neither group adds rounds of workgroups to the layer's GEMMs (for each
+// output width, 3H, H and F, the groups' rounds sum to at most the whole
+// batch's): a group whose grid spills into a nearly empty extra round leaves
+// most of the chip idle, which the other stream does not fill (the
+// 3B-shaped batch, T = 16208 at width 2560, ran 9% slower split).  Among the
+// splits that qualify, the most balanced; none below 4096 rows or 2
+// sequences, or without the host lengths.
+int32_t stack_split(int32_t H, int32_t F, const int32_t* cu_host, int32_t B, int64_t T) {
+  if (!cu_host || B < 2 || T < 4096 || H <= 0 || F <= 0) return 0;
+  const int32_t widths[3] = {3 * H, H, F};
+  int64_t whole[3];
+  for (int k = 0; k < 3; ++k) whole[k] = gemm_rounds(T, widths[k]);
+  int32_t bs = 0;
+  int64_t best = T;
+  for (int32_t b = 1; b < B; ++b) {
+    const int64_t t1 = cu_host[b], t2 = T - t1;
+    if (t1 <= 0 || t2 <= 0) continue;
+    bool fits = true;
+    for (int k = 0; k < 3 && fits; ++k) fits = gemm_rounds(t1, widths[k]) + gemm_rounds(t2, widths[k]) <= whole[k];
+    const int64_t d = t1 * 2 - T;
+    if (fits && (d < 0 ? -d : d) < best) {
+      best = d < 0 ? -d : d;
+      bs = b;
+    }
+  }
+  return bs;
+}
+
 esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, int32_t layer_idx,
                        const int32_t* ids, const void* emb, const void* x_in, void* x_out, const int32_t* cu_dev,
                        const int32_t* cu_host, int32_t B, int64_t T, int32_t max_seqlen, void* ws, size_t ws_bytes,
-                       esm_stream_t stream) {
+                       esm_stream_t stream, bool two_groups = false) {
   if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
   esm_status s = check_rows(e, T, B);
   if (s) return s;
@@ -815,28 +848,70 @@ esm_status forward_thd(esm_encoder* e, const esm_layer_weights* w, int nlayers, 
   if ((s = check_ws(e, ws, ws_bytes, T, B, &p))) return s;
   hipStream_t st = (hipStream_t)stream;
   HIP_TRY(hipSetDevice(e->device), "hipSetDevice");
-  if ((s = run_segments(e, 0, cu_dev, B, T, 0, ws, p, st))) return s;
-  const bf16_t* cur = (const bf16_t*)x_in;
-  bool stats_valid = false;
-  if (ids) {
-    // a folded first layer takes its LayerNorm statistics from the gather
-    const bool fold0 = nlayers > 0 && layer_folded(e, layer_idx >= 0 ? layer_idx : 0);
-    s = timed(e, ESM_K_EMBED, st, "embedding", [&] {
-      return fold0 ? launch_row_stats(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, T,
-                                      e->cfg.hidden_size, region<float2>(ws, p, ESM_WS_STATS), st)
-                   : launch_embed(ids, (const bf16_t*)emb, e->cfg.vocab_size, (bf16_t*)x_out, T,
-                                  e->cfg.hidden_size, st);
-    });
-    if (s) return s;
-    stats_valid = fold0;
-    cur = (const bf16_t*)x_out;
+  const int H = e->cfg.hidden_size;
+  // One group of whole sequences (rows r0 .. r0 + Tg - 1, Bg sequences whose
+  // cu_seqlens from 0 are cu_g) through the embedding and every layer, on
+  // stream sg with its own workspace.
+  auto run_group = [&](int64_t r0, int64_t Tg, int32_t Bg, const int32_t* cu_g, void* wsg, const Plan& pg,
+                       hipStream_t sg) -> esm_status {
+    esm_status q;
+    if ((q = run_segments(e, 0, cu_g, Bg, Tg, 0, wsg, pg, sg))) return q;
+    bf16_t* xo = (bf16_t*)x_out + r0 * H;
+    const bf16_t* cur = x_in ? (const bf16_t*)x_in + r0 * H : nullptr;
+    bool stats_valid = false;
+    if (ids) {
+      // a folded first layer takes its LayerNorm statistics from the gather
+      const bool fold0 = nlayers > 0 && layer_folded(e, layer_idx >= 0 ? layer_idx : 0);
+      q = timed(e, ESM_K_EMBED, sg, "embedding", [&] {
+        return fold0 ? launch_row_stats(ids + r0, (const bf16_t*)emb, e->cfg.vocab_size, xo, Tg, H,
+                                        region<float2>(wsg, pg, ESM_WS_STATS), sg)
+                     : launch_embed(ids + r0, (const bf16_t*)emb, e->cfg.vocab_size, xo, Tg, H, sg);
+      });
+      if (q) return q;
+      stats_valid = fold0;
+      cur = xo;
+    }
+    for (int l = 0; l < nlayers; ++l) {
+      if ((q = run_layer(e, &w[l], layer_idx >= 0 ? layer_idx : l, cur, xo, Tg, Bg, false, wsg, pg, &stats_valid,
+                         sg)))
+        return q;
+      cur = xo;
+    }
+    return ok();
+  };
+  // Two groups of whole sequences on two streams when the host lengths are
+  // known and the workspace holds both groups' plans (stack_split).
+  const int32_t bs = (two_groups && !e->profiling && nlayers > 0)
+                         ? stack_split(e->cfg.hidden_size, e->cfg.intermediate_size, cu_host, B, T)
+                         : 0;
+  if (bs > 0) {
+    const int64_t T1 = cu_host[bs], T2 = T - T1;
+    const int32_t B1 = bs, B2 = B - bs;
+    const Plan p1 = make_plan(e->cfg, T1, B1), p2 = make_plan(e->cfg, T2, B2);
+    const size_t o2 = align256(p1.total), oc = o2 + align256(p2.total), need = oc + align256((size_t)(B2 + 1) * 4);
+    if (T1 > 0 && T2 > 0 && need <= ws_bytes) {
+      if (!e->side) {
+        HIP_TRY(hipStreamCreateWithFlags(&e->side, hipStreamNonBlocking), "hipStreamCreateWithFlags");
+        HIP_TRY(hipEventCreateWithFlags(&e->fork, hipEventDisableTiming), "hipEventCreateWithFlags");
+        HIP_TRY(hipEventCreateWithFlags(&e->join, hipEventDisableTiming), "hipEventCreateWithFlags");
+      }
+      char* wb = (char*)ws;
+      int32_t* cu2 = (int32_t*)(wb + oc);
+      HIP_TRY(launch_rebase_cu(cu_dev, bs, B2, cu2, st), "rebase cu_seqlens");
+      HIP_TRY(hipEventRecord(e->fork, st), "hipEventRecord");
+      HIP_TRY(hipStreamWaitEvent(e->side, e->fork, 0), "hipStreamWaitEvent");
+      esm_status s1 = run_group(0, T1, B1, cu_dev, wb, p1, st);
+      esm_status s2 = run_group(T1, T2, B2, cu2, wb + o2, p2, e->side);
+      // joined on every return, so no work is left behind the caller's stream
+      hipError_t j = hipEventRecord(e->join, e->side);
+      if (!j) j = hipStreamWaitEvent(st, e->join, 0);
+      if (s1) return s1;
+      if (s2) return s2;
+      if (j) return hip_fail(j, "join");
+      return end_of_step(e, nlayers, layer_idx, st);
+    }
   }
-  for (int l = 0; l < nlayers; ++l) {
-    if ((s = run_layer(e, &w[l], layer_idx >= 0 ? layer_idx : l, cur, (bf16_t*)x_out, T, B, false, ws, p,
-                       &stats_valid, st)))
-      return s;
-    cur = (const bf16_t*)x_out;
-  }
+  if ((s = run_group(0, T, B, cu_dev, ws, p, st))) return s;
   return end_of_step(e, nlayers, layer_idx, st);
 }
 
@@ -993,7 +1068,9 @@ esm_status esm_encoder_destroy(esm_encoder* e) {
 esm_status esm_workspace_size(const esm_encoder* e, int64_t max_tokens, int32_t max_seqs, size_t* bytes) {
   if (!e || !bytes) return fail(ESM_ERR_NULL, "encoder or bytes is NULL");
   if (max_tokens < 0 || max_seqs < 0) return fail(ESM_ERR_SHAPE, "negative sizes");
-  *bytes = make_plan(e->cfg, max_tokens, max_seqs).total;
+  // plus room for the stack's two-group schedule (a second plan's alignment
+  // and tile slack, and the second group's rebased cu_seqlens)
+  *bytes = make_plan(e->cfg, max_tokens, max_seqs).total + 8192 + align256((size_t)(max_seqs + 1) * 4);
   return ok();
 }
 
@@ -1044,7 +1121,18 @@ esm_status esm_stack_fwd(esm_encoder* e, const esm_layer_weights* w, const int32
   g_last_error.clear();
   if (!e) return fail(ESM_ERR_NULL, "encoder is NULL");
   return forward_thd(e, w, e->cfg.num_hidden_layers, -1, ids, emb, x_in, x_out, cu_dev, cu_host, B, T, max_seqlen,
-                     ws, ws_bytes, stream);
+                     ws, ws_bytes, stream, true);
+}
+
+esm_status esm_stack_split(int32_t hidden_size, int32_t intermediate_size, const int32_t* cu_seqlens_host, int32_t B,
+                           int64_t T, int32_t* split_seq) {
+  g_last_error.clear();
+  if (!cu_seqlens_host || !split_seq) return fail(ESM_ERR_NULL, "NULL argument");
+  if (B < 0 || T < 0 || hidden_size <= 0 || intermediate_size <= 0) return fail(ESM_ERR_SHAPE, "bad sizes");
+  if (cu_seqlens_host[0] != 0 || cu_seqlens_host[B] != T)
+    return fail(ESM_ERR_SHAPE, "cu_seqlens must run from 0 to T");
+  *split_seq = stack_split(hidden_size, intermediate_size, cu_seqlens_host, B, T);
+  return ok();
 }
 
 esm_status esm_head_fwd(esm_encoder* e, const esm_head_weights* w, const void* x, void* x_final, void* logits,

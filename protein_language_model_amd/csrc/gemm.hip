@@ -966,6 +966,23 @@ int device_cus() {
   return cus[dev];
 }
 
+// The tile shape the dispatch picks for an M x N output, 320-row tiles when
+// they need no more rows of rounds than 256-row ones (time ~ rounds x tile
+// rows; on a tie the taller tiles, fewer of them), and the rounds of
+// workgroups over the compute units it then runs.
+struct TileChoice {
+  bool tall;
+  int64_t rounds;
+};
+TileChoice tile_choice(int64_t M, int32_t N) {
+  const int64_t tilesN = (N + 255) / 256;
+  const int64_t cus = device_cus();
+  const int64_t r256 = ((M + 255) / 256 * tilesN + cus - 1) / cus;
+  const int64_t r320 = ((M + 319) / 320 * tilesN + cus - 1) / cus;
+  const bool tall = r320 * 320 <= r256 * 256;
+  return TileChoice{tall, tall ? r320 : r256};
+}
+
 template <int EPI>
 hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   if constexpr (EPI == EPI_F32_SPLIT) {
@@ -985,11 +1002,7 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   } else if constexpr (EPI == EPI_QKV_ROPE_LN || EPI == EPI_BIAS_GELU_LN || EPI == EPI_RES_STATS) {
     if (a.dtype != kBF16) return hipErrorInvalidValue;
     if (EPI == EPI_RES_STATS ? !a.stats_out : (!a.ln_stats || !a.ln_cd)) return hipErrorInvalidValue;
-    const int64_t tilesN = (a.N + 255) / 256;
-    const int64_t cus = device_cus();
-    const int64_t r256 = ((a.M + 255) / 256 * tilesN + cus - 1) / cus;
-    const int64_t r320 = ((a.M + 319) / 320 * tilesN + cus - 1) / cus;
-    return r320 * 320 <= r256 * 256 ? run<320, 256, 2, 4, EPI, kBF16>(a, st) : run<256, 256, 2, 4, EPI, kBF16>(a, st);
+    return tile_choice(a.M, a.N).tall ? run<320, 256, 2, 4, EPI, kBF16>(a, st) : run<256, 256, 2, 4, EPI, kBF16>(a, st);
   } else {
   // 8 waves (two per SIMD, so one wave's LDS reads overlap the other's MFMAs)
   // over 256x256 tiles (128x64 per wave), or 320x256 tiles (160x64 per wave)
@@ -999,11 +1012,7 @@ hipError_t dispatch(const GemmArgs& a, hipStream_t st) {
   // epilogues: N = 5120, 8 x 320 vs 10 x 256).  Each output element
   // accumulates the same K order in either shape, so results do not depend
   // on the choice.
-  const int64_t tilesN = (a.N + 255) / 256;
-  const int64_t cus = device_cus();
-  const int64_t r256 = ((a.M + 255) / 256 * tilesN + cus - 1) / cus;
-  const int64_t r320 = ((a.M + 319) / 320 * tilesN + cus - 1) / cus;
-  const bool tall = r320 * 320 <= r256 * 256;
+  const bool tall = tile_choice(a.M, a.N).tall;
   if (a.dtype == kE5M2X) {
     // the backward's data-gradient GEMM: plain product, bias epilogue only
     if constexpr (EPI == EPI_BIAS)
@@ -1093,6 +1102,8 @@ hipError_t launch_mfma_peak(int32_t iters, int32_t blocks, float* sink, hipStrea
 }
 
 int32_t mfma_peak_blocks() { return 2 * device_cus(); }
+
+int64_t gemm_rounds(int64_t M, int32_t N) { return M > 0 && N > 0 ? tile_choice(M, N).rounds : 0; }
 
 hipError_t launch_gemm(int epi, const GemmArgs& a, hipStream_t st) {
   if (a.M <= 0) return hipSuccess;

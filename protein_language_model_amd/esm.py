@@ -78,6 +78,7 @@ SIGNATURES = {
     "esm_encoder_create": (_i32, [ctypes.POINTER(EsmConfig), ctypes.c_int, ctypes.POINTER(_p)]),
     "esm_encoder_destroy": (_i32, [_p]),
     "esm_workspace_size": (_i32, [_p, _i64, _i32, ctypes.POINTER(_sz)]),
+    "esm_stack_split": (_i32, [_i32, _i32, _p, _i32, _i64, ctypes.POINTER(_i32)]),
     "esm_workspace_region": (_i32, [_p, _i64, _i32, _i32, ctypes.POINTER(_sz), ctypes.POINTER(_sz)]),
     "esm_layer_fwd": (_i32, [_p, ctypes.POINTER(EsmLayerWeights), _i32, _p, _p, _p, _p, _i32, _i64, _i32, _p, _sz,
                              _p]),
@@ -208,6 +209,16 @@ def _stream(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream
+
+
+def stack_split(hidden_size: int, intermediate_size: int, cu_seqlens_host) -> int:
+    """The sequence index where esm_stack_fwd splits this batch into its two
+    groups (0: one group); host only."""
+    cu = _host_i32(cu_seqlens_host)
+    out = ctypes.c_int32()
+    _call("esm_stack_split", int(hidden_size), int(intermediate_size), cu.ctypes.data_as(ctypes.c_void_p),
+          int(cu.size - 1), int(cu[-1]), ctypes.byref(out))
+    return int(out.value)
 
 
 def _host_i32(a) -> Optional[np.ndarray]:
