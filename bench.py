@@ -91,6 +91,9 @@ def parse():
     ap.add_argument("--no-stack-train", action="store_true",
                     help="skip the whole stack's training forward and backward (esm_stack_fwd_train, esm_stack_bwd)")
     ap.add_argument("--no-vendor-gemm", action="store_true", help="skip the hipBLASLt fc1-shape reference timing")
+    ap.add_argument("--one-group", action="store_true",
+                    help="run the stacks as one group (no host lengths, so no two-stream split): the per-kernel "
+                         "timing pass's launches, for counter runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 256 MiB device copy first (reference dispatch for HBM byte counters)")
     return ap.parse_args()
@@ -731,9 +734,11 @@ def main():
             enc.mxfp4_prepare(weights, stream=stream)
         ws = enc.workspace(T, B)
 
+        host_cu = None if args.one_group else batch.cu_seqlens
+
         def step():
             enc.stack_fwd(weights, cu, B, T, batch.max_seqlen, token_ids=ids, embedding=emb_d, x_out=out,
-                          cu_seqlens_host=batch.cu_seqlens, workspace=ws, stream=stream)
+                          cu_seqlens_host=host_cu, workspace=ws, stream=stream)
 
         def timed_steps(n: int, per_step: list = None) -> float:
             """Mean ms per step over n steps; per_step (if given) receives each
