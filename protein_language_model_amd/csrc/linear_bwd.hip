@@ -5,11 +5,11 @@
 // For y = x W^T + b (x [M, K], W [N, K], y [M, N]) and an incoming gradient
 // dy, the backward is dx = dy W, dW = dy^T x and db = the column sums of dy
 // (the linears of the encoder layer; the pages time training, [BIO-ACC] 3.2
-// and 6).  dx and dW run on the library's MFMA GEMM (which computes
-// a B^T for row-major a [M', K'] and B [N', K']): dx = dy (W^T)^T and
-// dW = (dy^T) (x^T)^T, so the GEMM reads W^T [K, N], dy^T [N, M64] and
-// x^T [K, M64], written here with M rounded up to M64, a multiple of 64, and
-// the padding columns zero (they add nothing to the contraction over M).
+// and 6).  dx and dW run on the library's MFMA GEMM (which computes a B^T for
+// row-major a [M', K'] and B [N', K']): dx = dy (W^T)^T reads W^T [K, N],
+// written here; dW reads dy and x as they are, through the GEMM's
+// contraction-major split-K mode.  The E4M3 / E5M2 weight gradient still takes
+// byte transposes of both operands (k_transpose8_pad), rows past M zero.
 #include "common.h"
 
 namespace esm {
