@@ -51,6 +51,11 @@ PEAK_FP8_TFLOPS = 5033.2     # MI355X dense fp8 MFMA (vendor figure)
 FP8_MIN_WARMUP = 10          # delayed scales settle over the warm-up steps
 PEAK_HBM_GBS = 8000.0
 PEAK_FP4_TFLOPS = 10066.3    # MI355X dense fp4 MFMA (vendor figure)
+# Exponentials per second: the transcendental unit issues a quarter of the 32
+# fp32 lanes per cycle per SIMD that make the 157.3 TFLOP/s vector peak, i.e.
+# 8 lanes per cycle (a wave-wide v_exp_f32 in 8 cycles), on 4 SIMDs x 256
+# compute units at 2.4 GHz.
+PEAK_EXP_GPS = 256 * 4 * 8 * 2.4
 
 
 def layer_flops(H: int, F: int, T: int, sum_L2: int) -> dict:
@@ -195,6 +200,12 @@ def rooflines_all(prof, fl, peaks, T: int, H: int, fp8: bool) -> dict:
             a = fl[k] / avg_s / 1e12
             out[k] = {"bound": "mfma", "achieved": round(a, 1), "peak": peak, "unit": "TFLOP/s",
                       "frac": round(a / peak, 4)}
+            if k == "attention":
+                # one exponential per score: 4 * 64 * heads * sum L^2 flops -> heads * sum L^2 exponentials
+                exps = fl[k] / 256.0
+                r = exps / avg_s / 1e9
+                out[k]["exp"] = {"bound": "alu", "achieved": round(r, 1), "peak": PEAK_EXP_GPS, "unit": "Gexp/s",
+                                 "frac": round(r / PEAK_EXP_GPS, 4), "exps_per_launch": exps}
         elif k in ("layernorm", "embed"):
             # LN: x in (bf16) + y out (bf16, or E4M3 in an FP8 encoder); embed: y out (the table is tiny)
             nbytes = (T * H * 2 + T * H * (1 if fp8 else 2)) if k == "layernorm" else T * H * 2

@@ -53,3 +53,8 @@ def test_rooflines_all_uses_each_kernels_bound():
     assert "segment" not in r
     r8 = b.rooflines_all(prof, fl, {}, 32293, 1280, True)
     assert r8["layernorm"]["bytes_per_launch"] == 3 * 32293 * 1280
+    # attention also against the exponential unit: one exponential per score, 20 heads x sum L^2
+    ex = r["attention"]["exp"]
+    assert ex["bound"] == "alu" and ex["exps_per_launch"] == 20 * 16024465
+    assert abs(ex["achieved"] - 20 * 16024465 / 0.135e-3 / 1e9) < 0.1
+    assert ex["peak"] == 256 * 4 * 8 * 2.4
