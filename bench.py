@@ -144,10 +144,12 @@ def cpu_baseline(wl, batch, emb_bits, weights_dev, budget_residues: int = 12288,
     cu = D.cu_from_lengths(batch.lengths[:n])
     x = D.bf16_bits_to_f64(emb_bits)[batch.ids[:tot]]
     ws = [O.weights_to_f64({k: D.tensor_bits(v) for k, v in weights_dev[l].items()}) for l in range(layers)]
-    threads = None
+    threads, blas = None, None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        threads = max((i.get("num_threads") or 0) for i in info) or None
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info})) or None
     except Exception:
         pass
     fp8 = wl.precision == "fp8"
@@ -166,6 +168,7 @@ def cpu_baseline(wl, batch, emb_bits, weights_dev, budget_residues: int = 12288,
         "value": tot / (per_layer * m.layers),
         "unit": "residues/s",
         "cores": threads or os.cpu_count(),
+        "blas": blas,
         "kind": "oracle",
         "sample": f"first {n} sequences ({tot} residues) of the batch through {layers} of {m.layers} layers "
                   f"({'FP8-emulating ' if fp8 else ''}fp64 numpy/scipy), {dt:.1f} s; scaled to the "
