@@ -552,9 +552,23 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
     }
   } else if constexpr (DT == kE4M3 || DT == kE5M2X) {
     // One fragment set (8 registers per 32-byte fragment; a second set would
-    // not fit beside the 128 accumulators at two waves per SIMD): the other
-    // wave on the SIMD multiplies while this one waits for its LDS reads.
+    // not fit beside the accumulators at two waves per SIMD): the other wave
+    // on the SIMD multiplies while this one waits for its LDS reads.  The
+    // LDS addresses of this lane's first x and w fragment rows, per sub-step
+    // and 16-byte half, are kept in registers and moved to the other stage by
+    // one add each per K step; the 32-row blocks are immediate offsets.
     frag_t xf[FM], wf[FN];
+    typedef const __attribute__((address_space(3))) u32x4* lds_u4_ptr;
+    uint32_t ax[KK][2], aw[KK][2];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t ch = (uint32_t)(((kk * 4 + lhalf * 2 + h) ^ swz) * 16);
+        ax[kk][h] = lds0 + (uint32_t)((wm * WTM + lrow) * kRowBytes) + ch;
+        aw[kk][h] = lds0 + (uint32_t)(BM * kRowBytes + (wn * WTN + lrow) * kRowBytes) + ch;
+      }
+    int32_t to_other = kStage;  // byte distance to the other stage
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
       const bool more = kt + 1 < nk;
@@ -562,7 +576,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       for (int kk = 0; kk < KK; ++kk) {
         __builtin_amdgcn_sched_barrier(0);
         if (more && kk < kParts) issue_part(kt + 1, cur ^ 1, kk, kParts);
-        load_frags(xf, wf, cur, kk);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const u32x4 lo = *(lds_u4_ptr)(uintptr_t)(aw[kk][0] + j * 32 * kRowBytes);
+          const u32x4 hi = *(lds_u4_ptr)(uintptr_t)(aw[kk][1] + j * 32 * kRowBytes);
+          wf[j] = __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const u32x4 lo = *(lds_u4_ptr)(uintptr_t)(ax[kk][0] + i * 32 * kRowBytes);
+          const u32x4 hi = *(lds_u4_ptr)(uintptr_t)(ax[kk][1] + i * 32 * kRowBytes);
+          xf[i] = __builtin_bit_cast(frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
         __builtin_amdgcn_sched_barrier(0);
         mfma_step(xf, wf);
       }
@@ -570,6 +595,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       // Next tile landed for every wave; every wave is done reading this one.
       vm_wait_all();
       __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          ax[kk][h] += (uint32_t)to_other;
+          aw[kk][h] += (uint32_t)to_other;
+        }
+      to_other = -to_other;
     }
   } else if constexpr (FM * FN > 8) {
     // Large wave tiles (160 x 64: 160 accumulator registers): one fragment
