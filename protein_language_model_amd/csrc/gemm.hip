@@ -532,23 +532,74 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void k_gemm(GemmArgs a) 
       for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j], bfv[i], acc[i][j], 0, 0, 0);
   }
   if constexpr (DT == kFP4) {
-    // One fragment set, as for E4M3, plus the K step's block scales.
+    // One fragment set, as for E4M3, plus the K step's block scales.  This
+    // lane's fragment-row LDS addresses per sub-step and its two scale-row
+    // addresses are kept in registers and moved to the other stage by one add
+    // each per K step (32-row blocks as immediate offsets), and each MFMA
+    // takes sub-step kk's scale byte through its scale operand select, so the
+    // loop spends no vector instructions on addresses or scale bytes.
     frag_t xf[FM], wf[FN];
+    typedef const __attribute__((address_space(3))) u32x4* lds_u4_ptr;
+    typedef const __attribute__((address_space(3))) uint32_t* lds_u1_ptr;
+    uint32_t ax[KK], aw[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint32_t ch = (uint32_t)(((kk * 2 + lhalf) ^ swz) * 16);
+      ax[kk] = lds0 + (uint32_t)((wm * WTM + lrow) * kRowBytes) + ch;
+      aw[kk] = lds0 + (uint32_t)(BM * kRowBytes + (wn * WTN + lrow) * kRowBytes) + ch;
+    }
+    uint32_t asx = lds0 + (uint32_t)(2 * kStage + (wm * WTM + lrow) * 8 + 4 * lhalf);
+    uint32_t asw = lds0 + (uint32_t)(2 * kStage + (kScRowsX + wn * WTN + lrow) * 8 + 4 * lhalf);
+    int32_t to_other = kStage, sc_to_other = kScStage;
+    auto mfma_sel = [&](int i, int j, auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      // cbsz = blgp = 4: both operands E2M1; scale byte kk of each register
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf[j], xf[i], acc[i][j], 4, 4, kk, (int)wsc[j], kk,
+                                                                   (int)xsc[i]);
+    };
+    auto sub_step = [&](int kt, int cur, bool more, auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if (more && kk < kParts) issue_part(kt + 1, cur ^ 1, kk, kParts);
+      const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        wf[j] = __builtin_bit_cast(frag_t, __builtin_shufflevector(*(lds_u4_ptr)(uintptr_t)(aw[kk] + j * 32 * kRowBytes),
+                                                                   z4, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        xf[i] = __builtin_bit_cast(frag_t, __builtin_shufflevector(*(lds_u4_ptr)(uintptr_t)(ax[kk] + i * 32 * kRowBytes),
+                                                                   z4, 0, 1, 2, 3, 4, 5, 6, 7));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mfma_sel(i, j, kkc);
+    };
+    static_assert(KK == 4, "four 64-value sub-steps per MXFP4 K step");
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1;
       const bool more = kt + 1 < nk;
-      load_scales(cur);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (more && kk < kParts) issue_part(kt + 1, cur ^ 1, kk, kParts);
-        load_frags(xf, wf, cur, kk);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_step_mx(xf, wf, kk);
-      }
+      for (int i = 0; i < FM; ++i) xsc[i] = *(lds_u1_ptr)(uintptr_t)(asx + i * 32 * 8);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) wsc[j] = *(lds_u1_ptr)(uintptr_t)(asw + j * 32 * 8);
+      sub_step(kt, cur, more, std::integral_constant<int, 0>{});
+      sub_step(kt, cur, more, std::integral_constant<int, 1>{});
+      sub_step(kt, cur, more, std::integral_constant<int, 2>{});
+      sub_step(kt, cur, more, std::integral_constant<int, 3>{});
       __builtin_amdgcn_sched_barrier(0);
       vm_wait_all();
       __syncthreads();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        ax[kk] += (uint32_t)to_other;
+        aw[kk] += (uint32_t)to_other;
+      }
+      asx += (uint32_t)sc_to_other;
+      asw += (uint32_t)sc_to_other;
+      to_other = -to_other;
+      sc_to_other = -sc_to_other;
     }
   } else if constexpr (DT == kE4M3 || DT == kE5M2X) {
     // One fragment set (8 registers per 32-byte fragment; a second set would
