@@ -891,19 +891,25 @@ __global__ __launch_bounds__(64 * kBW) __attribute__((amdgpu_waves_per_eu(3, 3))
           dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, df[kk], dp[kb], 0, 0, 0);
         }
       }
-      const bool tail = (t + 1) * kBT > L;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[kb][r] = exp2_fast(fmaf(st[kb][r], kScaleLog2, -l2));
+      if ((t + 1) * kBT > L) {
+        // Keys at or past L (a sequence's last key tile only): P = 0.  The
+        // empty asm keeps this a branch; as selects it ran on every tile.
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (t * kBT + kb * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3) >= L) st[kb][r] = 0.f;
+      }
       bf16x8 sb[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = exp2_fast(fmaf(st[kb][r], kScaleLog2, -l2));
-          if (tail) {
-            const int k = t * kBT + kb * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-            if (k >= L) pr = 0.f;
-          }
-          dp[kb][r] = pr * (dp[kb][r] - dd);
-        }
+        for (int r = 0; r < 16; ++r) dp[kb][r] = st[kb][r] * (dp[kb][r] - dd);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           u32x4 x;
